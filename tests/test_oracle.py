@@ -1,0 +1,372 @@
+"""Pins for the fp64 oracle (CPU only).
+
+Each test compares the oracle's sequential recurrence with something other
+than itself, chosen so that a plausible mistake (a dropped term, a wrong sign
+or index, a transposed operand, an exclusive readout, a missing abs or floor
+in the denominator, a wrong stabilizer) fails at least one of them:
+
+* brute force: the unrolled sums of the xLSTM post, section 3 "The Parallel
+  Dual Form", in 50-digit arithmetic, with d_qk != d_v;
+* stored fixtures written by that brute force (tests/golden);
+* the closed form of the running maximum m;
+* the quadratic parallel form H = ((Q K^T) (.) S) V with the stabilized decay
+  matrix S of the same section, evaluated with numpy matmuls;
+* the linear-attention special case (same section, last paragraph);
+* the stabilizer-shift and split/resume invariants;
+* the one-token closed form and the forget-gate limits.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import unrolled_mp
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "unrolled_small.json")
+
+
+def rel_err(x, r):
+    x = np.asarray(x, dtype=np.float64)
+    r = np.asarray(r, dtype=np.float64)
+    return float(np.max(np.abs(x - r)) / max(np.max(np.abs(r)), 1e-300))
+
+
+def tiny_case(seed, T, dqk, dv, *, fgate="sigmoid", state=False, o=True,
+              i_dist=(0.5, 1.0), f_dist=(1.0, 1.0), k_scale=1.0):
+    rng = np.random.default_rng(seed)
+    c = dict(
+        q=rng.normal(0, 1, (T, dqk)), k=rng.normal(0, 1, (T, dqk)) * k_scale,
+        v=rng.normal(0, 1, (T, dv)), i_pre=rng.normal(*i_dist, T),
+        f_pre=rng.normal(*f_dist, T),
+        o_pre=rng.normal(0, 1, (T, dv)) if o else None,
+        C0=None, n0=None, m0=None)
+    if state:
+        c["C0"] = rng.normal(0, 1, (dqk, dv))
+        c["n0"] = rng.normal(0, 1, dqk)
+        c["m0"] = float(rng.normal(0, 1))
+    return c
+
+
+def run_oracle_head(c, fgate):
+    """Oracle on a single head given as [T, d] arrays."""
+    T, dqk = c["q"].shape
+    dv = c["v"].shape[1]
+    e4 = lambda a: None if a is None else np.asarray(a)[None, None]  # noqa: E731
+    C0 = e4(c["C0"])
+    n0 = e4(c["n0"])
+    m0 = None if c["m0"] is None else np.array([[c["m0"]]])
+    return oracle.recurrent(e4(c["q"]), e4(c["k"]), e4(c["v"]), e4(c["i_pre"]),
+                            e4(c["f_pre"]), e4(c["o_pre"]), C0, n0, m0, fgate=fgate)
+
+
+def mp_to_np(x):
+    return np.array([[float(e) for e in row] for row in x]) if isinstance(x[0], list) \
+        else np.array([float(e) for e in x])
+
+
+def to_lists(c):
+    tl = lambda a: None if a is None else np.asarray(a).tolist()  # noqa: E731
+    return dict(q=tl(c["q"]), k=tl(c["k"]), v=tl(c["v"]), i_pre=tl(c["i_pre"]),
+                f_pre=tl(c["f_pre"]), o_pre=tl(c["o_pre"]), C0=tl(c["C0"]),
+                n0=tl(c["n0"]), m0=c["m0"])
+
+
+# --------------------------------------------------------------------------
+# brute force (50 digits) and the stored fixtures it wrote
+# --------------------------------------------------------------------------
+BRUTE_CASES = [
+    # seed, T, dqk, dv, fgate, state, o
+    (1, 9, 3, 4, "sigmoid", False, True),
+    (2, 10, 4, 3, "sigmoid", True, True),
+    (3, 8, 2, 5, "exp", False, False),
+    (4, 11, 3, 2, "exp", True, True),
+    (5, 12, 4, 4, "sigmoid", True, False),
+]
+
+
+@pytest.mark.parametrize("seed,T,dqk,dv,fgate,state,o", BRUTE_CASES)
+def test_recurrence_matches_unrolled_brute_force(seed, T, dqk, dv, fgate, state, o):
+    f_dist = (1.0, 1.0) if fgate == "sigmoid" else (-0.3, 0.5)
+    c = tiny_case(seed, T, dqk, dv, fgate=fgate, state=state, o=o, f_dist=f_dist)
+    h, C1, n1, m1 = run_oracle_head(c, fgate)
+    hb, Cb, nb = unrolled_mp.unrolled(**to_lists(c), fgate=fgate)
+    assert rel_err(h[0, 0], mp_to_np(hb)) < 1e-13
+    # stabilized state times e^m is the true memory
+    assert rel_err(C1[0, 0] * math.exp(m1[0, 0]), mp_to_np(Cb)) < 1e-13
+    assert rel_err(n1[0, 0] * math.exp(m1[0, 0]), mp_to_np(nb)) < 1e-13
+
+
+def test_brute_force_cases_exercise_both_denominator_branches():
+    """The cases above must contain tokens with |n.q| > 1 AND with |n.q| < 1,
+    and negative n.q with |n.q| > 1 (where the abs matters)."""
+    big = small = negbig = 0
+    for seed, T, dqk, dv, fgate, state, o in BRUTE_CASES:
+        f_dist = (1.0, 1.0) if fgate == "sigmoid" else (-0.3, 0.5)
+        c = tiny_case(seed, T, dqk, dv, fgate=fgate, state=state, o=o, f_dist=f_dist)
+        L = to_lists(c)
+        nq = unrolled_mp.retrieval_terms(L["q"], L["k"], L["v"], L["i_pre"], L["f_pre"],
+                                         L["C0"], L["n0"], L["m0"], fgate)
+        nq = [float(x) for x in nq]
+        big += sum(abs(x) > 1 for x in nq)
+        small += sum(abs(x) < 1 for x in nq)
+        negbig += sum(x < -1 for x in nq)
+    assert big > 0 and small > 0 and negbig > 0
+
+
+def test_golden_fixtures():
+    with open(GOLDEN) as fh:
+        data = json.load(fh)
+    assert data["cases"]
+    for case in data["cases"]:
+        inp = case["inputs"]
+        c = {kk: (None if inp[kk] is None else np.array(inp[kk], dtype=np.float64))
+             for kk in ("q", "k", "v", "i_pre", "f_pre", "o_pre", "C0", "n0")}
+        c["m0"] = inp["m0"]
+        h, C1, n1, m1 = run_oracle_head(c, case["fgate"])
+        exp = case["expected"]
+        assert rel_err(h[0, 0], exp["h"]) < 1e-13, case["name"]
+        assert rel_err(C1[0, 0] * math.exp(m1[0, 0]), exp["C_true"]) < 1e-13, case["name"]
+        assert rel_err(n1[0, 0] * math.exp(m1[0, 0]), exp["n_true"]) < 1e-13, case["name"]
+
+
+# --------------------------------------------------------------------------
+# the running maximum: closed form
+# --------------------------------------------------------------------------
+def np_logsigmoid(x):
+    return -np.logaddexp(0.0, -x)
+
+
+@pytest.mark.parametrize("fgate", ["sigmoid", "exp"])
+def test_stabilizer_closed_form(fgate):
+    """m_t = F_t + max(m_0, max_{j<=t}(i~_j - F_j)), F the cumulative log f."""
+    rng = np.random.default_rng(7)
+    B, H, T, d = 2, 3, 120, 4
+    q = rng.normal(0, 1, (T, B, H, d))
+    k = rng.normal(0, 1, (T, B, H, d))
+    v = rng.normal(0, 1, (T, B, H, d))
+    ip = rng.normal(-2, 3, (T, B, H))
+    fp = rng.normal(1, 2, (T, B, H)) if fgate == "sigmoid" else rng.normal(-0.2, 0.3, (T, B, H))
+    C = rng.normal(0, 1, (B, H, d, d))
+    n = rng.normal(0, 1, (B, H, d))
+    m0 = rng.normal(0, 1, (B, H))
+    m = m0.copy()
+    ms = []
+    for t in range(T):
+        _, C, n, m = oracle.step(q[t], k[t], v[t], ip[t], fp[t], None, C, n, m, fgate=fgate)
+        ms.append(m)
+    ms = np.stack(ms)
+    lf = np_logsigmoid(fp) if fgate == "sigmoid" else fp
+    F = np.cumsum(lf, axis=0)
+    closed = F + np.maximum(m0[None], np.maximum.accumulate(ip - F, axis=0))
+    assert np.max(np.abs(ms - closed)) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# the quadratic parallel form
+# --------------------------------------------------------------------------
+def quadratic_form(q, k, v, i_pre, f_pre, o_pre, C0, n0, m0, fgate):
+    """One head, [T, d] arrays.  The parallel dual form: numerator
+    ((Q K^T) (.) S) V with S_tj = (prod of f after j up to t) i_j for j <= t,
+    plus the decayed initial memory; the normalizer is the same with the
+    values replaced by ones (row sums) plus the decayed initial normalizer.
+    Everything is scaled by e^{-m_t} with m_t from the closed form, which makes
+    every exponent non-positive.
+    """
+    T = q.shape[0]
+    lf = np_logsigmoid(f_pre) if fgate == "sigmoid" else f_pre
+    F = np.cumsum(lf)
+    m0 = 0.0 if m0 is None else m0
+    m = F + np.maximum(m0, np.maximum.accumulate(i_pre - F))
+    expo = F[:, None] - F[None, :] + i_pre[None, :] - m[:, None]
+    causal = np.tril(np.ones((T, T), dtype=bool))
+    S = np.where(causal, np.exp(np.where(causal, expo, -np.inf)), 0.0)
+    W = (q @ k.T) * S
+    num = W @ v
+    nq = W.sum(axis=1)
+    g = np.exp(F + m0 - m)
+    if C0 is not None:
+        num = num + g[:, None] * (q @ C0)
+        nq = nq + g * (q @ n0)
+    den = np.maximum(np.abs(nq), np.exp(-m))
+    h = num / den[:, None]
+    if o_pre is not None:
+        h = h / (1.0 + np.exp(-o_pre))
+    w_last = S[-1]
+    C_T = (k * w_last[:, None]).T @ v
+    n_T = k.T @ w_last
+    if C0 is not None:
+        C_T = C_T + g[-1] * C0
+        n_T = n_T + g[-1] * n0
+    return h, C_T, n_T, m[-1]
+
+
+def _check_quadratic(c, fgate, tol=1e-10):
+    h, C1, n1, m1 = run_oracle_head(c, fgate)
+    hq, Cq, nq, mq = quadratic_form(c["q"], c["k"], c["v"], c["i_pre"], c["f_pre"],
+                                    c["o_pre"], c["C0"], c["n0"], c["m0"], fgate)
+    assert rel_err(h[0, 0], hq) < tol
+    assert abs(m1[0, 0] - mq) < 1e-12
+    assert rel_err(C1[0, 0], Cq) < tol
+    assert rel_err(n1[0, 0], nq) < tol
+
+
+def _head_from_config(cfg, b, hh, T=None, with_o=True):
+    inp = workloads.make_chunkwise_inputs(cfg, T=T, with_o=with_o)
+    g = lambda x: None if x is None else x[b, hh].double().numpy()  # noqa: E731
+    c = dict(q=g(inp["q"]), k=g(inp["k"]), v=g(inp["v"]), i_pre=g(inp["i_pre"]),
+             f_pre=g(inp["f_pre"]), o_pre=g(inp["o_pre"]), C0=g(inp["C0"]),
+             n0=g(inp["n0"]), m0=None if inp["m0"] is None else float(inp["m0"][b, hh]))
+    return c
+
+
+def test_quadratic_form_c0():
+    c = _head_from_config(workloads.CONFIGS["c0"], 0, 0)
+    _check_quadratic(c, "sigmoid")
+
+
+def test_quadratic_form_c1_head():
+    """One head of the c1 shape (T=2048, d=128), reduced to B=H=1."""
+    c = _head_from_config(workloads.CONFIGS["c1"], 0, 0)
+    _check_quadratic(c, "sigmoid")
+
+
+def test_quadratic_form_c2_distributions_with_state():
+    """c2's gate distributions (i~ ~ N(-2,3)) and random state, T=512."""
+    cfg = workloads.CONFIGS["c2"]
+    inp = workloads.make_chunkwise_inputs(cfg, B=1, H=1, T=512)
+    # narrow d to keep the test fast while keeping d_qk != d_v
+    c = dict(q=inp["q"][0, 0, :, :32].double().numpy(),
+             k=inp["k"][0, 0, :, :32].double().numpy(),
+             v=inp["v"][0, 0, :, :48].double().numpy(),
+             i_pre=inp["i_pre"][0, 0].double().numpy(),
+             f_pre=inp["f_pre"][0, 0].double().numpy(),
+             o_pre=inp["o_pre"][0, 0, :, :48].double().numpy(),
+             C0=inp["C0"][0, 0, :32, :48].double().numpy(),
+             n0=inp["n0"][0, 0, :32].double().numpy(), m0=float(inp["m0"][0, 0]))
+    _check_quadratic(c, "sigmoid")
+
+
+def test_quadratic_form_exp_gate_random_state():
+    c = tiny_case(21, 300, 12, 20, fgate="exp", state=True, o=True,
+                  i_dist=(0.0, 2.0), f_dist=(-0.05, 0.1))
+    _check_quadratic(c, "exp")
+
+
+# --------------------------------------------------------------------------
+# linear attention special case
+# --------------------------------------------------------------------------
+def test_reduces_to_causal_linear_attention():
+    """Exp forget gate with f~ = 0 (f = 1), i~ = 0 (i = 1), m_0 = 0, zero state,
+    no output gate, and keys scaled so that sum_s |q_t . k_s| <= 1 for every t:
+    then m stays 0, the denominator is exactly 1, and h = tril(Q K^T) V."""
+    rng = np.random.default_rng(5)
+    T, dqk, dv = 96, 8, 12
+    q = rng.normal(0, 1, (T, dqk))
+    k = rng.normal(0, 1, (T, dqk))
+    v = rng.normal(0, 1, (T, dv))
+    bound = np.max(np.cumsum(np.abs(q @ k.T) * np.tril(np.ones((T, T))), axis=1).diagonal())
+    k = k * (0.99 / max(bound, np.max(np.abs(np.tril(q @ k.T)).sum(axis=1))))
+    c = dict(q=q, k=k, v=v, i_pre=np.zeros(T), f_pre=np.zeros(T), o_pre=None,
+             C0=None, n0=None, m0=None)
+    h, C1, n1, m1 = run_oracle_head(c, "exp")
+    ref = np.tril(q @ k.T) @ v
+    assert rel_err(h[0, 0], ref) < 1e-12
+    assert m1[0, 0] == 0.0
+    assert rel_err(C1[0, 0], k.T @ v) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# invariants
+# --------------------------------------------------------------------------
+def test_stabilizer_shift_invariance():
+    """(C~ e^{-c}, n~ e^{-c}, m + c) is the same memory, so h is unchanged."""
+    c = tiny_case(31, 200, 6, 7, state=True, i_dist=(-1, 2), f_dist=(2, 1))
+    h1, C1, n1, m1 = run_oracle_head(c, "sigmoid")
+    for shift in (3.7, -5.2):
+        c2 = dict(c)
+        c2["C0"] = c["C0"] * math.exp(-shift)
+        c2["n0"] = c["n0"] * math.exp(-shift)
+        c2["m0"] = c["m0"] + shift
+        h2, C2, n2, m2 = run_oracle_head(c2, "sigmoid")
+        assert rel_err(h2, h1) < 1e-12
+        assert rel_err(C2 * np.exp(m2)[..., None, None], C1 * np.exp(m1)[..., None, None]) < 1e-12
+
+
+@pytest.mark.parametrize("split", [32, 17, 1, 63])
+def test_split_resume_is_bitwise(split):
+    """Processing T tokens in one call equals two calls with the carried
+    (C~, n~, m) state, bit for bit (same operation order)."""
+    cfg = workloads.CONFIGS["c2"]
+    inp = workloads.make_chunkwise_inputs(cfg, B=2, H=2, T=64)
+    f64 = lambda x: None if x is None else x.double().numpy()  # noqa: E731
+    a = {kk: f64(vv) for kk, vv in inp.items()}
+    d = dict(fgate="sigmoid")
+    h, C1, n1, m1 = oracle.recurrent(a["q"][..., :24], a["k"][..., :24], a["v"][..., :20],
+                                     a["i_pre"], a["f_pre"], a["o_pre"][..., :20],
+                                     a["C0"][..., :24, :20], a["n0"][..., :24], a["m0"], **d)
+    s = split
+    ha, Ca, na, ma = oracle.recurrent(a["q"][:, :, :s, :24], a["k"][:, :, :s, :24],
+                                      a["v"][:, :, :s, :20], a["i_pre"][:, :, :s],
+                                      a["f_pre"][:, :, :s], a["o_pre"][:, :, :s, :20],
+                                      a["C0"][..., :24, :20], a["n0"][..., :24], a["m0"], **d)
+    hb, Cb, nb, mb = oracle.recurrent(a["q"][:, :, s:, :24], a["k"][:, :, s:, :24],
+                                      a["v"][:, :, s:, :20], a["i_pre"][:, :, s:],
+                                      a["f_pre"][:, :, s:], a["o_pre"][:, :, s:, :20],
+                                      Ca, na, ma, **d)
+    assert np.array_equal(np.concatenate([ha, hb], axis=2), h)
+    assert np.array_equal(Cb, C1) and np.array_equal(nb, n1) and np.array_equal(mb, m1)
+
+
+def test_step_equals_recurrent_token_by_token():
+    c = tiny_case(41, 20, 5, 6, state=True)
+    h, C1, n1, m1 = run_oracle_head(c, "sigmoid")
+    C, n, m = c["C0"][None, None], c["n0"][None, None], np.array([[c["m0"]]])
+    for t in range(20):
+        ht, C, n, m = oracle.step(c["q"][t][None, None], c["k"][t][None, None],
+                                  c["v"][t][None, None], np.array([[c["i_pre"][t]]]),
+                                  np.array([[c["f_pre"][t]]]), c["o_pre"][t][None, None],
+                                  C, n, m)
+        assert np.array_equal(ht[0, 0], h[0, 0, t])
+    assert np.array_equal(C, C1) and np.array_equal(n, n1) and np.array_equal(m, m1)
+
+
+# --------------------------------------------------------------------------
+# closed forms and limits
+# --------------------------------------------------------------------------
+def test_single_token_closed_form():
+    """Zero state, one token: h = sigma(o~) e^{i~} (k.q) v / max(e^{i~}|k.q|, 1)."""
+    rng = np.random.default_rng(51)
+    for _ in range(20):
+        dqk, dv = 5, 3
+        c = dict(q=rng.normal(0, 1, (1, dqk)), k=rng.normal(0, 1, (1, dqk)),
+                 v=rng.normal(0, 1, (1, dv)), i_pre=rng.normal(0, 2, 1),
+                 f_pre=rng.normal(0, 3, 1), o_pre=rng.normal(0, 1, (1, dv)),
+                 C0=None, n0=None, m0=None)
+        h, *_ = run_oracle_head(c, "sigmoid")
+        kq = float(c["k"][0] @ c["q"][0])
+        ii = math.exp(c["i_pre"][0])
+        ref = (1 / (1 + np.exp(-c["o_pre"][0]))) * ii * kq * c["v"][0] / max(ii * abs(kq), 1.0)
+        assert rel_err(h[0, 0, 0], ref) < 1e-14
+
+
+def test_sigmoid_gate_saturated_equals_exp_gate_at_zero():
+    c = tiny_case(61, 40, 4, 5, state=True)
+    c_sig = dict(c, f_pre=np.full(40, 40.0))
+    c_exp = dict(c, f_pre=np.zeros(40))
+    h1, C1, n1, m1 = run_oracle_head(c_sig, "sigmoid")
+    h2, C2, n2, m2 = run_oracle_head(c_exp, "exp")
+    assert rel_err(h1, h2) < 1e-12 and rel_err(C1, C2) < 1e-12
+
+
+def test_output_gate_factorizes():
+    c = tiny_case(71, 30, 4, 6, state=True)
+    h1, *_ = run_oracle_head(c, "sigmoid")
+    h0, *_ = run_oracle_head(dict(c, o_pre=None), "sigmoid")
+    ref = h0[0, 0] / (1 + np.exp(-c["o_pre"]))
+    assert rel_err(h1[0, 0], ref) < 1e-14

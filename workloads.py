@@ -1,0 +1,147 @@
+"""Seeded synthetic inputs for the mLSTM cell forward pass.
+
+This module holds only input recipes: shapes, dtypes, distributions and seeds.
+It computes nothing of the method itself.  Both the HIP path's callers (tests,
+benchmark, smoke check) and the oracle's callers draw their inputs here, so the
+two sides always see the same bits.
+
+The pages train on language-model data and print no layer shapes, so the
+workloads are synthetic tensors shaped like language-model mLSTM layers:
+
+  c0  fp32, B=1, H=1, T=64, d_qk=d_v=16, chunk 16; zero initial state
+  c1  bf16 q/k/v, fp32 gates and state, B=4, H=4, T=2048, d=128, chunk 64
+  c2  bf16, B=8, H=8, T=8192, d=256, chunk 64 and 128; i~ ~ N(-2,3),
+      f~ ~ N(4,2); random initial state N(0,1)
+  c3  decode step, bf16 q/k/v, fp32 state, B=128, H=8, d=512, 256 steps;
+      initial state N(0,1); per-step gates as c0
+  c4  bf16, B=1, H=16, T=65536, d_qk=256, d_v=512, chunk 128; f~ ~ N(6,1),
+      i~ ~ N(0,2); zero initial state
+
+Recipe (every config): a CPU ``torch.Generator`` seeded with 1000 + index.
+Draw order: q, k, v, i~, f~, o~, then (if the state is random) C0, n0, m0.
+Every draw is float32 ``normal(mean, std)`` (std is the second number).
+k is multiplied by 1/sqrt(d_qk) in float32 before any cast.  For bf16 configs
+q, k, v are then rounded to bfloat16 (round to nearest even); gates, o~ and the
+state stay float32.  The forget gate goes through logsigmoid (sigmoid gate).
+For c3 the state is drawn first, then per step s = 0..S-1 the tuple
+(q, k, v, i~, f~, o~), each as one [S,B,H,...] tensor in that order.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, Optional, Tuple
+
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    name: str
+    index: int
+    dtype: str            # "f32" or "bf16": dtype of q, k, v and h
+    B: int
+    H: int
+    T: int                # tokens (for the step config: number of steps)
+    dqk: int
+    dv: int
+    chunks: Tuple[int, ...]
+    i_dist: Tuple[float, float]
+    f_dist: Tuple[float, float]
+    o_dist: Optional[Tuple[float, float]]   # None: no output gate (o = 1)
+    random_state: bool
+    fgate: str = "sigmoid"
+    kind: str = "chunkwise"                  # "chunkwise" or "step"
+
+    @property
+    def seed(self) -> int:
+        return 1000 + self.index
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    def describe(self) -> str:
+        return (f"{self.name}: {self.kind} {self.dtype} B={self.B} H={self.H} "
+                f"T={self.T} d_qk={self.dqk} d_v={self.dv} chunk={self.chunks}")
+
+
+CONFIGS: Dict[str, Config] = {
+    "c0": Config("c0", 0, "f32", 1, 1, 64, 16, 16, (16,), (0.0, 1.0), (3.0, 1.0),
+                 (0.0, 1.0), False),
+    "c1": Config("c1", 1, "bf16", 4, 4, 2048, 128, 128, (64,), (0.0, 1.0), (3.0, 1.0),
+                 (0.0, 1.0), False),
+    "c2": Config("c2", 2, "bf16", 8, 8, 8192, 256, 256, (64, 128), (-2.0, 3.0),
+                 (4.0, 2.0), (0.0, 1.0), True),
+    "c3": Config("c3", 3, "bf16", 128, 8, 256, 512, 512, (), (0.0, 1.0), (3.0, 1.0),
+                 (0.0, 1.0), True, kind="step"),
+    "c4": Config("c4", 4, "bf16", 1, 16, 65536, 256, 512, (128,), (0.0, 2.0),
+                 (6.0, 1.0), (0.0, 1.0), False),
+}
+
+
+def _normal(gen: torch.Generator, shape, mean: float, std: float) -> torch.Tensor:
+    out = torch.empty(shape, dtype=torch.float32)
+    out.normal_(mean, std, generator=gen)
+    return out
+
+
+def make_chunkwise_inputs(cfg: Config, *, B: Optional[int] = None,
+                          H: Optional[int] = None, T: Optional[int] = None,
+                          with_o: bool = True, seed: Optional[int] = None
+                          ) -> Dict[str, Optional[torch.Tensor]]:
+    """Inputs for a whole-sequence call, on the CPU.
+
+    B, H, T override the config's sizes (for reduced parity cases that keep the
+    config's distributions).  Returns a dict with q, k, v (cfg dtype), i_pre,
+    f_pre (float32 [B,H,T]), o_pre (float32 [B,H,T,dv] or None) and C0, n0, m0
+    (float32, or None for the zero state).
+    """
+    B = cfg.B if B is None else B
+    H = cfg.H if H is None else H
+    T = cfg.T if T is None else T
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(cfg.seed if seed is None else seed)
+    q = _normal(gen, (B, H, T, cfg.dqk), 0.0, 1.0)
+    k = _normal(gen, (B, H, T, cfg.dqk), 0.0, 1.0) * (1.0 / math.sqrt(cfg.dqk))
+    v = _normal(gen, (B, H, T, cfg.dv), 0.0, 1.0)
+    i_pre = _normal(gen, (B, H, T), *cfg.i_dist)
+    f_pre = _normal(gen, (B, H, T), *cfg.f_dist)
+    o_pre = _normal(gen, (B, H, T, cfg.dv), *cfg.o_dist) if (with_o and cfg.o_dist) else None
+    C0 = n0 = m0 = None
+    if cfg.random_state:
+        C0 = _normal(gen, (B, H, cfg.dqk, cfg.dv), 0.0, 1.0)
+        n0 = _normal(gen, (B, H, cfg.dqk), 0.0, 1.0)
+        m0 = _normal(gen, (B, H), 0.0, 1.0)
+    dt = cfg.torch_dtype
+    return dict(q=q.to(dt), k=k.to(dt), v=v.to(dt), i_pre=i_pre, f_pre=f_pre,
+                o_pre=o_pre, C0=C0, n0=n0, m0=m0)
+
+
+def make_step_inputs(cfg: Config, *, B: Optional[int] = None,
+                     H: Optional[int] = None, steps: Optional[int] = None,
+                     with_o: bool = True, seed: Optional[int] = None
+                     ) -> Dict[str, Optional[torch.Tensor]]:
+    """Inputs for a run of consecutive decode steps, on the CPU.
+
+    Returns C0 [B,H,dqk,dv], n0 [B,H,dqk], m0 [B,H] (float32) and per-step
+    q, k [S,B,H,dqk], v [S,B,H,dv] (cfg dtype), i_pre, f_pre [S,B,H] and
+    o_pre [S,B,H,dv] (float32, or None).
+    """
+    B = cfg.B if B is None else B
+    H = cfg.H if H is None else H
+    S = cfg.T if steps is None else steps
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(cfg.seed if seed is None else seed)
+    C0 = _normal(gen, (B, H, cfg.dqk, cfg.dv), 0.0, 1.0)
+    n0 = _normal(gen, (B, H, cfg.dqk), 0.0, 1.0)
+    m0 = _normal(gen, (B, H), 0.0, 1.0)
+    q = _normal(gen, (S, B, H, cfg.dqk), 0.0, 1.0)
+    k = _normal(gen, (S, B, H, cfg.dqk), 0.0, 1.0) * (1.0 / math.sqrt(cfg.dqk))
+    v = _normal(gen, (S, B, H, cfg.dv), 0.0, 1.0)
+    i_pre = _normal(gen, (S, B, H), *cfg.i_dist)
+    f_pre = _normal(gen, (S, B, H), *cfg.f_dist)
+    o_pre = _normal(gen, (S, B, H, cfg.dv), *cfg.o_dist) if (with_o and cfg.o_dist) else None
+    dt = cfg.torch_dtype
+    return dict(q=q.to(dt), k=k.to(dt), v=v.to(dt), i_pre=i_pre, f_pre=f_pre,
+                o_pre=o_pre, C0=C0, n0=n0, m0=m0)
