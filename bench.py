@@ -1,0 +1,241 @@
+"""Benchmark of the mLSTM forward hot path on one MI355X.
+
+One bench step is one chunkwise forward pass (mlstm_fwd_chunkwise) over the
+d=256, T=8192 workload: B=8, H=8, d_qk=d_v=256, bf16 q/k/v, fp32 gates and
+o-gate preactivation, random initial state carried in and the final state
+written out.  value = tokens/s (B*T tokens per pass).  Also reported on the
+same line: the decode step (mlstm_step) on its workload (B=128, H=8, d=512,
+256 consecutive in-place steps) as GB/s against 8 TB/s, the chunk-128
+variant, the parallel form, the roofline of the dominant kernel, and the fp64
+CPU oracle timed on a bounded sample of the chunkwise workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--chunk 64]
+                       [--skip-cpu] [--skip-step]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+
+METRIC = "mLSTM chunkwise fwd tokens/s + % bf16 MFMA peak; step GB/s % HBM peak (1 GPU)"
+
+
+def chunk_algorithmic(B, H, T, dqk, dv, L, o_bytes, state_in=True, state_out=True):
+    """Algorithmic work of one chunkwise pass.
+
+    flops: bf16 MFMA work per token-head (L+1)(d_qk+d_v) (causal halves of Q K^T
+    and P V) + 4 d_qk d_v (readout q^T C and the state update k v^T).
+    bytes: q, k, v, h (bf16), gates (2 x fp32), o-gate, plus the state in/out
+    (the minimum any implementation must move).
+    """
+    th = B * H * T
+    flops = th * ((L + 1) * (dqk + dv) + 4 * dqk * dv)
+    per_tok = (2 * dqk + dv) * 2 + dv * 2 + 8 + dv * o_bytes
+    state = B * H * (dqk * dv + dqk + 1) * 4
+    byts = th * per_tok + state * (int(state_in) + int(state_out))
+    return flops, byts
+
+
+def step_algorithmic(B, H, dqk, dv, qkv_bytes=2, o_bytes=4):
+    """Bytes one decode step must move: C~ read + write, n~ read + write, m,
+    q, k, v, gates, o-gate, h."""
+    BH = B * H
+    return BH * (2 * dqk * dv * 4 + 2 * dqk * 4 + 2 * 4 + 2 * dqk * qkv_bytes +
+                 dv * qkv_bytes + 8 + dv * o_bytes + dv * qkv_bytes)
+
+
+def time_events(fn, reps, stream):
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(reps):
+        fn()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / reps  # ms
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--chunk", type=int, default=64)
+    ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--skip-step", action="store_true")
+    ap.add_argument("--skip-extra", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: every (batch, head) is independent and this "
+              "build runs on a single MI355X; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mlstm_matrix_memory_chunkwise_amd as M
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    M.load_library()
+
+    def log(msg):
+        print(msg, file=sys.stderr, flush=True)
+
+    # ------------------------------------------------------------ chunkwise
+    cfg = workloads.CONFIGS["c2"]
+    log(f"bench: generating {cfg.describe()}")
+    inp = workloads.make_chunkwise_inputs(cfg)
+    d = {k: (None if v is None else v.to(dev)) for k, v in inp.items()}
+    B, H, T, dqk, dv = cfg.B, cfg.H, cfg.T, cfg.dqk, cfg.dv
+    h = torch.empty((B, H, T, dv), dtype=torch.bfloat16, device=dev)
+
+    def chunk_pass(L):
+        def run():
+            M.mlstm_fwd_chunkwise(d["q"], d["k"], d["v"], d["i_pre"], d["f_pre"], d["o_pre"],
+                                  d["C0"], d["n0"], d["m0"], chunk=L, out=h)
+        return run
+
+    run = chunk_pass(args.chunk)
+    log(f"bench: warmup {args.warmup}")
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    log(f"bench: timing {args.steps} steps")
+    t0 = time.perf_counter()
+    ms_events = time_events(run, args.steps, stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    flops, byts = chunk_algorithmic(B, H, T, dqk, dv, args.chunk, 4)
+    sec = ms_events / 1e3
+    tokens_per_s = B * T / sec
+    result = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"chunkwise mLSTM forward, bf16 q/k/v, fp32 gates/o-gate/state, "
+                               f"B={B} H={H} T={T} d_qk={dqk} d_v={dv} chunk={args.chunk}, "
+                               f"random initial state in, final state out",
+                   "B": B, "H": H, "T": T, "d_qk": dqk, "d_v": dv, "chunk": args.chunk},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": byts / sec / 1e9,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": byts / sec / 1e9 / HBM_PEAK_GBS,
+            "traffic": None,
+        },
+        "mfma": {"achieved_tflops": flops / sec / 1e12, "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+                 "frac": flops / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                 "algorithmic_gflop": flops / 1e9},
+        "kernel_ms": ms_events,
+        "algorithmic_bytes": byts,
+    }
+
+    if not args.skip_extra:
+        other = 128 if args.chunk == 64 else 64
+        run2 = chunk_pass(other)
+        run2()
+        torch.cuda.synchronize()
+        ms2 = time_events(run2, max(3, args.steps // 2), stream)
+        f2, b2 = chunk_algorithmic(B, H, T, dqk, dv, other, 4)
+        result[f"chunk{other}"] = {"ms": ms2, "tokens_per_s": B * T / (ms2 / 1e3),
+                                   "mfma_frac": f2 / (ms2 / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                                   "hbm_frac": b2 / (ms2 / 1e3) / 1e9 / HBM_PEAK_GBS}
+        # no output gate (gating done at block level after GroupNorm)
+        def run_noo():
+            M.mlstm_fwd_chunkwise(d["q"], d["k"], d["v"], d["i_pre"], d["f_pre"], None,
+                                  d["C0"], d["n0"], d["m0"], chunk=args.chunk, out=h)
+        run_noo()
+        torch.cuda.synchronize()
+        ms3 = time_events(run_noo, max(3, args.steps // 2), stream)
+        f3, b3 = chunk_algorithmic(B, H, T, dqk, dv, args.chunk, 0)
+        result["no_ogate"] = {"ms": ms3, "tokens_per_s": B * T / (ms3 / 1e3),
+                              "mfma_frac": f3 / (ms3 / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                              "hbm_frac": b3 / (ms3 / 1e3) / 1e9 / HBM_PEAK_GBS}
+
+    # ------------------------------------------------------------ CPU oracle
+    if not args.skip_cpu:
+        import oracle
+        nheads = int(os.environ.get("MLSTM_BENCH_CPU_HEADS", "16"))
+        sub = workloads.make_chunkwise_inputs(cfg, B=1, H=nheads)
+        thr = oracle.max_threads()
+        log(f"bench: oracle on {nheads} heads x {T} tokens, {thr} threads")
+        t0 = time.perf_counter()
+        oracle.recurrent(sub["q"], sub["k"], sub["v"], sub["i_pre"], sub["f_pre"], sub["o_pre"],
+                         sub["C0"], sub["n0"], sub["m0"])
+        cpu_s = time.perf_counter() - t0
+        # tokens/s of the full workload = (token-heads/s) / H
+        result["cpu_baseline"] = {
+            "value": nheads * T / cpu_s / H,
+            "unit": "tokens/s",
+            "cores": min(thr, nheads),
+            "kind": "oracle",
+            "sample": f"{nheads} of the {B * H} heads (B=1, H={nheads}, T={T}, same distributions "
+                      f"and seed recipe), fp64 sequential recurrence, {cpu_s:.2f} s wall; "
+                      f"tokens/s scaled as token-heads/s / H={H}",
+        }
+    del d, inp, h
+    torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ decode step
+    if not args.skip_step:
+        cfg3 = workloads.CONFIGS["c3"]
+        log(f"bench: generating {cfg3.describe()}")
+        s = workloads.make_step_inputs(cfg3)
+        ds = {k: (None if v is None else v.to(dev)) for k, v in s.items()}
+        del s
+        C, n, m = ds["C0"], ds["n0"], ds["m0"]
+        hs = torch.empty((cfg3.B, cfg3.H, cfg3.dv), dtype=torch.bfloat16, device=dev)
+        state = {"t": 0}
+
+        def step():
+            t = state["t"] % cfg3.T
+            M.mlstm_step(ds["q"][t], ds["k"][t], ds["v"][t], ds["i_pre"][t], ds["f_pre"][t],
+                         ds["o_pre"][t], C, n, m, inplace=True, out=hs)
+            state["t"] += 1
+
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        ms_step = time_events(step, cfg3.T, stream)
+        sb = step_algorithmic(cfg3.B, cfg3.H, cfg3.dqk, cfg3.dv)
+        gbs = sb / (ms_step / 1e3) / 1e9
+        result["step"] = {
+            "workload": f"decode step, bf16 q/k/v, fp32 state and o-gate, B={cfg3.B} H={cfg3.H} "
+                        f"d_qk=d_v={cfg3.dqk}, {cfg3.T} consecutive in-place steps",
+            "us_per_step": ms_step * 1e3,
+            "tokens_per_s": cfg3.B / (ms_step / 1e3),
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+            "algorithmic_bytes_per_step": sb,
+        }
+        del ds, C, n, m
+        torch.cuda.empty_cache()
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

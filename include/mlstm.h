@@ -1,0 +1,154 @@
+/*
+ * mlstm.h -- C ABI of the MI355X (gfx950) mLSTM matrix-memory cell forward pass.
+ *
+ * The method (xLSTM post, llms.blog, "xLSTM: How Exponential Gating and Matrix
+ * Memory Scale Recurrent Neural Networks"):
+ *   - section 3, "Associative Matrix Cell State": memory update
+ *     C_t = f_t C_{t-1} + i_t v_t k_t^T, normalizer n_t = f_t n_{t-1} + i_t k_t,
+ *     retrieval h~_t = C_t q_t / max(n_t^T q_t, 1), output h_t = o_t (.) h~_t,
+ *     with i_t = exp(i~_t) and f_t = exp(f~_t) or sigmoid(f~_t);
+ *   - section 2, "The Normalizer State and Numerical Stabilization": the running
+ *     maximum m_t = max(log f_t + m_{t-1}, i~_t) and the stabilized factors
+ *     exp(log f_t + m_{t-1} - m_t), exp(i~_t - m_t);
+ *   - section 3, "The Parallel Dual Form": the same outputs from the decay
+ *     matrix S and H = ((Q K^T) (.) S) V, evaluated chunk by chunk with a
+ *     carried state (chunkwise) or over the whole sequence at once (parallel).
+ *
+ * State convention.  The state is the stabilized triple (C~, n~, m) with the
+ * true memory C = C~ e^m and n = n~ e^m.  C~ is stored [d_qk][d_v] (the
+ * transpose of the page's v k^T, so the readout is q^T C~).  The output is
+ *   h_t = sigmoid(o~_t) (.) (q_t^T C~_t) / max(|n~_t . q_t|, exp(-m_t)),
+ * which equals the page's retrieval with |n^T q| in the denominator.  The
+ * final m is the value of the sequential recurrence; (C~ e^{-c}, n~ e^{-c},
+ * m + c) is the same memory, so compare states after rescaling to one m.
+ * k is expected pre-scaled by 1/sqrt(d_qk); q is used as given.
+ *
+ * Layouts.  Every tensor is dense row-major (C order) with the shapes below.
+ * B = batch, H = heads, T = tokens.  q, k: [B,H,T,d_qk]; v, o~, h:
+ * [B,H,T,d_v]; i~, f~: [B,H,T]; C~: [B,H,d_qk,d_v]; n~: [B,H,d_qk]; m: [B,H].
+ * The decode step drops the T axis.  q, k, v and h have dtype qkv_dtype; o~
+ * has o_dtype; gates and state are float32.
+ *
+ * Memory and ownership.  Every pointer is a DEVICE pointer owned by the caller
+ * and must be 16-byte aligned.  The library allocates nothing and keeps no
+ * state between calls except a per-thread error string; it is reentrant.
+ * Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ * stream); the library never synchronizes.  Argument checks run on the host
+ * before anything is enqueued; a failed check enqueues nothing.  A launch
+ * failure returns MLSTM_ERR_DEVICE; faults during execution surface at the
+ * caller's next synchronization.  NaN or Inf in the inputs propagate to the
+ * outputs without an error code.  Supported range: |m| <= 80 (exp(-m) stays
+ * finite in float32).
+ */
+#ifndef MLSTM_H
+#define MLSTM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLSTM_OK = 0,
+  MLSTM_ERR_INVALID_ARG = 1, /* NULL required pointer, bad size, misaligned or
+                                overlapping buffers, partial state, bad enum,
+                                workspace too small */
+  MLSTM_ERR_UNSUPPORTED = 2, /* valid but not implemented: d not a multiple of
+                                16 or above 512, chunk not in {16,32,64,128},
+                                T not a multiple of chunk */
+  MLSTM_ERR_DEVICE = 3       /* a HIP call or kernel launch failed */
+} mlstm_status_t;
+
+typedef enum { MLSTM_F32 = 0, MLSTM_BF16 = 1 } mlstm_dtype_t;
+
+/* Forget gate: log f = logsigmoid(f~) (sigmoid gate) or log f = f~ (exp gate). */
+typedef enum { MLSTM_FGATE_SIGMOID = 0, MLSTM_FGATE_EXP = 1 } mlstm_fgate_t;
+
+typedef struct {
+  int64_t B, H, T;    /* T is ignored by mlstm_step */
+  int64_t d_qk, d_v;  /* head dims of q/k and of v/h */
+  int32_t qkv_dtype;  /* mlstm_dtype_t of q, k, v and h */
+  int32_t o_dtype;    /* mlstm_dtype_t of o~ (ignored when o~ is NULL) */
+  int32_t fgate;      /* mlstm_fgate_t */
+  int32_t reserved;   /* must be 0 */
+} mlstm_problem_t;
+
+/*
+ * Chunkwise forward pass (section 3, "The Parallel Dual Form", evaluated one
+ * chunk of `chunk` tokens at a time: the decay matrix inside a chunk, the
+ * carried state between chunks).  Result does not depend on `chunk` beyond
+ * rounding.
+ *   q, k, v, i_pre, f_pre, h: required.
+ *   o_pre: NULL means o = 1 (no output gate).
+ *   C0, n0, m0: all NULL (zero state, m0 = 0) or all set.
+ *   C1, n1, m1: all NULL (final state not written) or all set.
+ *   State outputs must not overlap state inputs; h must not overlap any input.
+ *   workspace: device scratch of at least the size given by
+ *   mlstm_fwd_chunkwise_workspace_bytes (may be NULL when that size is 0).
+ * Returns MLSTM_OK or an error code; on error, mlstm_last_error_detail()
+ * describes it.
+ */
+mlstm_status_t mlstm_fwd_chunkwise(const mlstm_problem_t* p, int64_t chunk,
+                                   const void* q, const void* k, const void* v,
+                                   const float* i_pre, const float* f_pre,
+                                   const void* o_pre, const float* C0,
+                                   const float* n0, const float* m0, void* h,
+                                   float* C1, float* n1, float* m1,
+                                   void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+/* Workspace needed by mlstm_fwd_chunkwise for this problem (bytes). */
+mlstm_status_t mlstm_fwd_chunkwise_workspace_bytes(const mlstm_problem_t* p,
+                                                   int64_t chunk, size_t* bytes);
+
+/*
+ * Parallel (quadratic) forward pass (section 3, "The Parallel Dual Form":
+ * H = ((Q K^T) (.) S) V over the whole sequence, plus the decayed initial
+ * state).  Same arguments and rules as mlstm_fwd_chunkwise without `chunk`.
+ * Cost grows as T^2; meant for short sequences and as a cross-check.
+ */
+mlstm_status_t mlstm_fwd_parallel(const mlstm_problem_t* p, const void* q,
+                                  const void* k, const void* v,
+                                  const float* i_pre, const float* f_pre,
+                                  const void* o_pre, const float* C0,
+                                  const float* n0, const float* m0, void* h,
+                                  float* C1, float* n1, float* m1,
+                                  void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/* Workspace needed by mlstm_fwd_parallel for this problem (bytes). */
+mlstm_status_t mlstm_fwd_parallel_workspace_bytes(const mlstm_problem_t* p,
+                                                  size_t* bytes);
+
+/*
+ * One decode step for every (batch, head) (section 3, "Associative Matrix Cell
+ * State", one token; section 5's constant-memory inference: the same bytes
+ * are read and written at every step).
+ *   q, k: [B,H,d_qk]; v, o_pre, h: [B,H,d_v]; i_pre, f_pre: [B,H].
+ *   C_in, n_in, m_in: required current state.  C_out, n_out, m_out: required
+ *   new state; each may equal its input pointer exactly (in-place update) but
+ *   must not partially overlap it.  o_pre may be NULL (o = 1).
+ */
+mlstm_status_t mlstm_step(const mlstm_problem_t* p, const void* q,
+                          const void* k, const void* v, const float* i_pre,
+                          const float* f_pre, const void* o_pre,
+                          const float* C_in, const float* n_in,
+                          const float* m_in, float* C_out, float* n_out,
+                          float* m_out, void* h, void* stream);
+
+/* Static description of a status code. */
+const char* mlstm_status_string(mlstm_status_t s);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char* mlstm_last_error_detail(void);
+
+/* Library version string. */
+const char* mlstm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLSTM_H */

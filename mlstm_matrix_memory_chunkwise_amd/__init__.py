@@ -1,0 +1,277 @@
+"""mLSTM matrix-memory cell forward pass on MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libmlstm.so`` (declared in
+``include/mlstm.h``).  The functions keep the C names.  They only check and
+marshal arguments: torch supplies device memory and the current stream, and
+every step of the computation runs in the library's HIP kernels.  There is no
+fallback: if the library is missing or a call fails, an exception is raised.
+
+    h, (C1, n1, m1) = mlstm_fwd_chunkwise(q, k, v, i_pre, f_pre, o_pre,
+                                          C0, n0, m0, chunk=64)
+    h, (C1, n1, m1) = mlstm_fwd_parallel(q, k, v, i_pre, f_pre, o_pre, C0, n0, m0)
+    h, (C, n, m)    = mlstm_step(q, k, v, i_pre, f_pre, o_pre, C, n, m)
+
+Shapes: q, k [B,H,T,d_qk]; v, o_pre, h [B,H,T,d_v]; i_pre, f_pre [B,H,T];
+C [B,H,d_qk,d_v]; n [B,H,d_qk]; m [B,H] (the step drops T).  q, k, v are
+float32 or bfloat16 (h gets the same dtype); o_pre is float32 or bfloat16 or
+None; gates and state are float32.  k is expected pre-scaled by 1/sqrt(d_qk).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "mlstm_fwd_chunkwise", "mlstm_fwd_parallel", "mlstm_step",
+    "mlstm_fwd_chunkwise_workspace_bytes", "mlstm_fwd_parallel_workspace_bytes",
+    "mlstm_version", "library_path", "load_library", "MLSTMError",
+    "MLSTM_OK", "MLSTM_ERR_INVALID_ARG", "MLSTM_ERR_UNSUPPORTED", "MLSTM_ERR_DEVICE",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libmlstm.so")
+
+MLSTM_OK = 0
+MLSTM_ERR_INVALID_ARG = 1
+MLSTM_ERR_UNSUPPORTED = 2
+MLSTM_ERR_DEVICE = 3
+MLSTM_F32 = 0
+MLSTM_BF16 = 1
+MLSTM_FGATE_SIGMOID = 0
+MLSTM_FGATE_EXP = 1
+
+
+class MLSTMError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"mlstm status {status}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("T", ctypes.c_int64),
+                ("d_qk", ctypes.c_int64), ("d_v", ctypes.c_int64),
+                ("qkv_dtype", ctypes.c_int32), ("o_dtype", ctypes.c_int32),
+                ("fgate", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libmlstm.so (built in-tree by ``build.build()``); raise if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is not built; run __graft_entry__.build() "
+                           "(or python mlstm_matrix_memory_chunkwise_amd/build.py)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    PP = ctypes.POINTER(Problem)
+    seq = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.mlstm_fwd_chunkwise.argtypes = [PP, i64] + seq
+    lib.mlstm_fwd_chunkwise.restype = ctypes.c_int
+    lib.mlstm_fwd_parallel.argtypes = [PP] + seq
+    lib.mlstm_fwd_parallel.restype = ctypes.c_int
+    lib.mlstm_step.argtypes = [PP] + [vp] * 14
+    lib.mlstm_step.restype = ctypes.c_int
+    lib.mlstm_fwd_chunkwise_workspace_bytes.argtypes = [PP, i64, ctypes.POINTER(sz)]
+    lib.mlstm_fwd_chunkwise_workspace_bytes.restype = ctypes.c_int
+    lib.mlstm_fwd_parallel_workspace_bytes.argtypes = [PP, ctypes.POINTER(sz)]
+    lib.mlstm_fwd_parallel_workspace_bytes.restype = ctypes.c_int
+    lib.mlstm_status_string.argtypes = [ctypes.c_int]
+    lib.mlstm_status_string.restype = ctypes.c_char_p
+    lib.mlstm_last_error_detail.argtypes = []
+    lib.mlstm_last_error_detail.restype = ctypes.c_char_p
+    lib.mlstm_version.argtypes = []
+    lib.mlstm_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def mlstm_version() -> str:
+    return load_library().mlstm_version().decode()
+
+
+def _check(status: int):
+    if status != MLSTM_OK:
+        lib = load_library()
+        raise MLSTMError(status, lib.mlstm_last_error_detail().decode())
+
+
+_DT = {torch.float32: MLSTM_F32, torch.bfloat16: MLSTM_BF16}
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev_tensor(name, t, dtype=None, shape=None, device=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _fgate(fgate) -> int:
+    if fgate in ("sigmoid", MLSTM_FGATE_SIGMOID):
+        return MLSTM_FGATE_SIGMOID
+    if fgate in ("exp", MLSTM_FGATE_EXP):
+        return MLSTM_FGATE_EXP
+    raise ValueError(f"unknown forget gate {fgate!r}")
+
+
+def _stream_handle(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _seq_problem(q, k, v, i_pre, f_pre, o_pre, C0, n0, m0, fgate):
+    q = _dev_tensor("q", q, (torch.float32, torch.bfloat16))
+    if q.dim() != 4:
+        raise ValueError("q must be [B,H,T,d_qk]")
+    B, H, T, dqk = q.shape
+    dev = q.device
+    k = _dev_tensor("k", k, q.dtype, (B, H, T, dqk), dev)
+    v = _dev_tensor("v", v, q.dtype, None, dev)
+    if v.dim() != 4 or tuple(v.shape[:3]) != (B, H, T):
+        raise ValueError("v must be [B,H,T,d_v]")
+    dv = v.shape[3]
+    i_pre = _dev_tensor("i_pre", i_pre, torch.float32, (B, H, T), dev)
+    f_pre = _dev_tensor("f_pre", f_pre, torch.float32, (B, H, T), dev)
+    o_pre = _dev_tensor("o_pre", o_pre, (torch.float32, torch.bfloat16), (B, H, T, dv), dev)
+    C0 = _dev_tensor("C0", C0, torch.float32, (B, H, dqk, dv), dev)
+    n0 = _dev_tensor("n0", n0, torch.float32, (B, H, dqk), dev)
+    m0 = _dev_tensor("m0", m0, torch.float32, (B, H), dev)
+    p = Problem(B, H, T, dqk, dv, _DT[q.dtype],
+                _DT[o_pre.dtype] if o_pre is not None else MLSTM_F32, _fgate(fgate), 0)
+    return p, (q, k, v, i_pre, f_pre, o_pre, C0, n0, m0)
+
+
+def _outputs(p, q, out, return_state):
+    B, H, T, dqk, dv = p.B, p.H, p.T, p.d_qk, p.d_v
+    dev = q.device
+    if out is not None:
+        h = _dev_tensor("out", out, q.dtype, (B, H, T, dv), dev)
+    else:
+        h = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev)
+    if return_state:
+        C1 = torch.empty((B, H, dqk, dv), dtype=torch.float32, device=dev)
+        n1 = torch.empty((B, H, dqk), dtype=torch.float32, device=dev)
+        m1 = torch.empty((B, H), dtype=torch.float32, device=dev)
+    else:
+        C1 = n1 = m1 = None
+    return h, C1, n1, m1
+
+
+def mlstm_fwd_chunkwise_workspace_bytes(p: Problem, chunk: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().mlstm_fwd_chunkwise_workspace_bytes(ctypes.byref(p), int(chunk),
+                                                              ctypes.byref(n)))
+    return int(n.value)
+
+
+def mlstm_fwd_parallel_workspace_bytes(p: Problem) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().mlstm_fwd_parallel_workspace_bytes(ctypes.byref(p), ctypes.byref(n)))
+    return int(n.value)
+
+
+def mlstm_fwd_chunkwise(q, k, v, i_pre, f_pre, o_pre=None, C0=None, n0=None, m0=None, *,
+                        chunk: int = 64, fgate="sigmoid", return_state: bool = True,
+                        out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                        stream=None):
+    """Chunkwise forward pass.  Returns (h, (C1, n1, m1)) or (h, None)."""
+    lib = load_library()
+    p, (q, k, v, i_pre, f_pre, o_pre, C0, n0, m0) = _seq_problem(
+        q, k, v, i_pre, f_pre, o_pre, C0, n0, m0, fgate)
+    h, C1, n1, m1 = _outputs(p, q, out, return_state)
+    need = mlstm_fwd_chunkwise_workspace_bytes(p, chunk)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.mlstm_fwd_chunkwise(ctypes.byref(p), int(chunk), _ptr(q), _ptr(k), _ptr(v),
+                                   _ptr(i_pre), _ptr(f_pre), _ptr(o_pre), _ptr(C0), _ptr(n0),
+                                   _ptr(m0), _ptr(h), _ptr(C1), _ptr(n1), _ptr(m1),
+                                   _ptr(workspace), wbytes, _stream_handle(stream)))
+    return h, ((C1, n1, m1) if return_state else None)
+
+
+def mlstm_fwd_parallel(q, k, v, i_pre, f_pre, o_pre=None, C0=None, n0=None, m0=None, *,
+                       fgate="sigmoid", return_state: bool = True,
+                       out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                       stream=None):
+    """Parallel (quadratic) forward pass.  Returns (h, (C1, n1, m1)) or (h, None)."""
+    lib = load_library()
+    p, (q, k, v, i_pre, f_pre, o_pre, C0, n0, m0) = _seq_problem(
+        q, k, v, i_pre, f_pre, o_pre, C0, n0, m0, fgate)
+    h, C1, n1, m1 = _outputs(p, q, out, return_state)
+    need = mlstm_fwd_parallel_workspace_bytes(p)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check(lib.mlstm_fwd_parallel(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(i_pre),
+                                  _ptr(f_pre), _ptr(o_pre), _ptr(C0), _ptr(n0), _ptr(m0),
+                                  _ptr(h), _ptr(C1), _ptr(n1), _ptr(m1), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(),
+                                  _stream_handle(stream)))
+    return h, ((C1, n1, m1) if return_state else None)
+
+
+def mlstm_step(q, k, v, i_pre, f_pre, o_pre, C, n, m, *, fgate="sigmoid",
+               inplace: bool = False, out: Optional[torch.Tensor] = None,
+               state_out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
+               stream=None):
+    """One decode step.  Returns (h, (C', n', m')).  With inplace=True the state
+    tensors C, n, m are updated in place and returned."""
+    lib = load_library()
+    q = _dev_tensor("q", q, (torch.float32, torch.bfloat16))
+    if q.dim() != 3:
+        raise ValueError("q must be [B,H,d_qk]")
+    B, H, dqk = q.shape
+    dev = q.device
+    k = _dev_tensor("k", k, q.dtype, (B, H, dqk), dev)
+    v = _dev_tensor("v", v, q.dtype, None, dev)
+    if v.dim() != 3 or tuple(v.shape[:2]) != (B, H):
+        raise ValueError("v must be [B,H,d_v]")
+    dv = v.shape[2]
+    i_pre = _dev_tensor("i_pre", i_pre, torch.float32, (B, H), dev)
+    f_pre = _dev_tensor("f_pre", f_pre, torch.float32, (B, H), dev)
+    o_pre = _dev_tensor("o_pre", o_pre, (torch.float32, torch.bfloat16), (B, H, dv), dev)
+    C = _dev_tensor("C", C, torch.float32, (B, H, dqk, dv), dev)
+    n = _dev_tensor("n", n, torch.float32, (B, H, dqk), dev)
+    m = _dev_tensor("m", m, torch.float32, (B, H), dev)
+    if inplace:
+        C1, n1, m1 = C, n, m
+    elif state_out is not None:
+        C1 = _dev_tensor("C_out", state_out[0], torch.float32, (B, H, dqk, dv), dev)
+        n1 = _dev_tensor("n_out", state_out[1], torch.float32, (B, H, dqk), dev)
+        m1 = _dev_tensor("m_out", state_out[2], torch.float32, (B, H), dev)
+    else:
+        C1, n1, m1 = torch.empty_like(C), torch.empty_like(n), torch.empty_like(m)
+    h = (_dev_tensor("out", out, q.dtype, (B, H, dv), dev) if out is not None
+         else torch.empty((B, H, dv), dtype=q.dtype, device=dev))
+    p = Problem(B, H, 1, dqk, dv, _DT[q.dtype],
+                _DT[o_pre.dtype] if o_pre is not None else MLSTM_F32, _fgate(fgate), 0)
+    _check(lib.mlstm_step(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(i_pre), _ptr(f_pre),
+                          _ptr(o_pre), _ptr(C), _ptr(n), _ptr(m), _ptr(C1), _ptr(n1), _ptr(m1),
+                          _ptr(h), _stream_handle(stream)))
+    return h, (C1, n1, m1)

@@ -1,0 +1,276 @@
+// C ABI of the mLSTM library: argument checks, kernel selection, status codes.
+// Every check runs on the host before anything is enqueued.  No HIP call is
+// made before the checks pass, so invalid calls are rejected on hosts without
+// a GPU too.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/mlstm.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_detail[512] = "";
+
+mlstm_status_t fail(mlstm_status_t s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_detail, sizeof(g_detail), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+mlstm_status_t ok() {
+  g_detail[0] = '\0';
+  return MLSTM_OK;
+}
+
+struct Buf {
+  const char* name;
+  const void* p;
+  size_t bytes;
+};
+
+bool overlaps(const Buf& x, const Buf& y) {
+  if (!x.p || !y.p || x.bytes == 0 || y.bytes == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(x.p), a1 = a0 + x.bytes;
+  const uintptr_t b0 = reinterpret_cast<uintptr_t>(y.p), b1 = b0 + y.bytes;
+  return a0 < b1 && b0 < a1;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t dsize(int32_t dt) { return dt == MLSTM_BF16 ? 2 : 4; }
+
+mlstm_status_t check_problem(const mlstm_problem_t* p, bool need_T) {
+  if (!p) return fail(MLSTM_ERR_INVALID_ARG, "problem descriptor is NULL");
+  if (p->B <= 0 || p->H <= 0 || p->d_qk <= 0 || p->d_v <= 0 || (need_T && p->T <= 0))
+    return fail(MLSTM_ERR_INVALID_ARG, "sizes must be positive (B=%lld H=%lld T=%lld d_qk=%lld d_v=%lld)",
+                (long long)p->B, (long long)p->H, (long long)p->T, (long long)p->d_qk,
+                (long long)p->d_v);
+  if (p->qkv_dtype != MLSTM_F32 && p->qkv_dtype != MLSTM_BF16)
+    return fail(MLSTM_ERR_INVALID_ARG, "unknown qkv_dtype %d", p->qkv_dtype);
+  if (p->o_dtype != MLSTM_F32 && p->o_dtype != MLSTM_BF16)
+    return fail(MLSTM_ERR_INVALID_ARG, "unknown o_dtype %d", p->o_dtype);
+  if (p->fgate != MLSTM_FGATE_SIGMOID && p->fgate != MLSTM_FGATE_EXP)
+    return fail(MLSTM_ERR_INVALID_ARG, "unknown fgate %d", p->fgate);
+  if (p->reserved != 0) return fail(MLSTM_ERR_INVALID_ARG, "reserved field must be 0");
+  // grid-size and 32-bit index limits of the kernels
+  if (p->B * p->H > (int64_t)1 << 24)
+    return fail(MLSTM_ERR_UNSUPPORTED, "B*H=%lld exceeds 2^24", (long long)(p->B * p->H));
+  if (p->d_qk % 16 != 0 || p->d_v % 16 != 0 || p->d_qk > 512 || p->d_v > 512)
+    return fail(MLSTM_ERR_UNSUPPORTED, "d_qk=%lld d_v=%lld: need multiples of 16, at most 512",
+                (long long)p->d_qk, (long long)p->d_v);
+  if (need_T && p->T > ((int64_t)1 << 31) - 1)
+    return fail(MLSTM_ERR_UNSUPPORTED, "T=%lld exceeds 2^31-1", (long long)p->T);
+  return MLSTM_OK;
+}
+
+// Shared checks of the two whole-sequence entry points.
+mlstm_status_t check_seq(const mlstm_problem_t* p, const void* q, const void* k, const void* v,
+                         const float* i_pre, const float* f_pre, const void* o_pre,
+                         const float* C0, const float* n0, const float* m0, void* h,
+                         float* C1, float* n1, float* m1, mlstm::SeqArgs* out) {
+  mlstm_status_t s = check_problem(p, true);
+  if (s != MLSTM_OK) return s;
+  if (!q || !k || !v || !i_pre || !f_pre || !h)
+    return fail(MLSTM_ERR_INVALID_ARG, "q, k, v, i_pre, f_pre and h are required");
+  const int in_state = (C0 != nullptr) + (n0 != nullptr) + (m0 != nullptr);
+  if (in_state != 0 && in_state != 3)
+    return fail(MLSTM_ERR_INVALID_ARG, "initial state must be all of C0, n0, m0 or none");
+  const int out_state = (C1 != nullptr) + (n1 != nullptr) + (m1 != nullptr);
+  if (out_state != 0 && out_state != 3)
+    return fail(MLSTM_ERR_INVALID_ARG, "final state must be all of C1, n1, m1 or none");
+  const size_t BH = (size_t)(p->B * p->H), T = (size_t)p->T;
+  const size_t dqk = (size_t)p->d_qk, dv = (size_t)p->d_v, sq = dsize(p->qkv_dtype);
+  const Buf bufs[] = {
+      {"q", q, BH * T * dqk * sq},          {"k", k, BH * T * dqk * sq},
+      {"v", v, BH * T * dv * sq},           {"i_pre", i_pre, BH * T * 4},
+      {"f_pre", f_pre, BH * T * 4},         {"o_pre", o_pre, BH * T * dv * dsize(p->o_dtype)},
+      {"C0", C0, BH * dqk * dv * 4},        {"n0", n0, BH * dqk * 4},
+      {"m0", m0, BH * 4},                   {"h", h, BH * T * dv * sq},
+      {"C1", C1, BH * dqk * dv * 4},        {"n1", n1, BH * dqk * 4},
+      {"m1", m1, BH * 4},
+  };
+  const int nb = sizeof(bufs) / sizeof(bufs[0]);
+  for (int i = 0; i < nb; ++i)
+    if (bufs[i].p && !aligned16(bufs[i].p))
+      return fail(MLSTM_ERR_INVALID_ARG, "%s is not 16-byte aligned", bufs[i].name);
+  // outputs (h, C1, n1, m1 = indices 9..12) must not overlap any input or each other
+  for (int o = 9; o < nb; ++o)
+    for (int i = 0; i < nb; ++i)
+      if (i != o && overlaps(bufs[o], bufs[i]))
+        return fail(MLSTM_ERR_INVALID_ARG, "%s overlaps %s", bufs[o].name, bufs[i].name);
+  mlstm::SeqArgs a;
+  a.B = p->B; a.H = p->H; a.T = p->T; a.dqk = p->d_qk; a.dv = p->d_v;
+  a.qkv_bf16 = p->qkv_dtype == MLSTM_BF16;
+  a.o_mode = o_pre ? (p->o_dtype == MLSTM_BF16 ? mlstm::O_BF16 : mlstm::O_F32) : mlstm::O_NONE;
+  a.fgate_exp = p->fgate == MLSTM_FGATE_EXP;
+  a.q = q; a.k = k; a.v = v; a.i_pre = i_pre; a.f_pre = f_pre; a.o_pre = o_pre;
+  a.C0 = C0; a.n0 = n0; a.m0 = m0; a.h = h; a.C1 = C1; a.n1 = n1; a.m1 = m1;
+  *out = a;
+  return MLSTM_OK;
+}
+
+mlstm_status_t check_chunk(const mlstm_problem_t* p, int64_t chunk) {
+  if (chunk != 16 && chunk != 32 && chunk != 64 && chunk != 128)
+    return fail(MLSTM_ERR_UNSUPPORTED, "chunk=%lld: supported chunks are 16, 32, 64, 128",
+                (long long)chunk);
+  if (p->T % chunk != 0)
+    return fail(MLSTM_ERR_UNSUPPORTED, "T=%lld is not a multiple of chunk=%lld",
+                (long long)p->T, (long long)chunk);
+  return MLSTM_OK;
+}
+
+mlstm::SeqArgs problem_args(const mlstm_problem_t* p) {
+  mlstm::SeqArgs a{};
+  a.B = p->B; a.H = p->H; a.T = p->T; a.dqk = p->d_qk; a.dv = p->d_v;
+  a.qkv_bf16 = p->qkv_dtype == MLSTM_BF16;
+  return a;
+}
+
+mlstm_status_t device_status(hipError_t e, const char* what) {
+  if (e != hipSuccess)
+    return fail(MLSTM_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mlstm_version(void) { return "mlstm-gfx950 0.1.0"; }
+
+const char* mlstm_status_string(mlstm_status_t s) {
+  switch (s) {
+    case MLSTM_OK: return "ok";
+    case MLSTM_ERR_INVALID_ARG: return "invalid argument";
+    case MLSTM_ERR_UNSUPPORTED: return "unsupported problem";
+    case MLSTM_ERR_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+const char* mlstm_last_error_detail(void) { return g_detail; }
+
+mlstm_status_t mlstm_fwd_chunkwise_workspace_bytes(const mlstm_problem_t* p, int64_t chunk,
+                                                   size_t* bytes) {
+  if (!bytes) return fail(MLSTM_ERR_INVALID_ARG, "bytes is NULL");
+  mlstm_status_t s = check_problem(p, true);
+  if (s != MLSTM_OK) return s;
+  s = check_chunk(p, chunk);
+  if (s != MLSTM_OK) return s;
+  const mlstm::SeqArgs a = problem_args(p);
+  *bytes = mlstm::chunk_mfma_supported(a, chunk) ? mlstm::chunk_mfma_workspace(a, chunk) : 0;
+  return ok();
+}
+
+mlstm_status_t mlstm_fwd_chunkwise(const mlstm_problem_t* p, int64_t chunk, const void* q,
+                                   const void* k, const void* v, const float* i_pre,
+                                   const float* f_pre, const void* o_pre, const float* C0,
+                                   const float* n0, const float* m0, void* h, float* C1,
+                                   float* n1, float* m1, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  mlstm::SeqArgs a;
+  mlstm_status_t s = check_seq(p, q, k, v, i_pre, f_pre, o_pre, C0, n0, m0, h, C1, n1, m1, &a);
+  if (s != MLSTM_OK) return s;
+  s = check_chunk(p, chunk);
+  if (s != MLSTM_OK) return s;
+  const bool mfma = mlstm::chunk_mfma_supported(a, chunk);
+  const size_t need = mfma ? mlstm::chunk_mfma_workspace(a, chunk) : 0;
+  if (workspace_bytes < need || (need > 0 && !workspace))
+    return fail(MLSTM_ERR_INVALID_ARG, "workspace of %zu bytes given, %zu needed",
+                workspace_bytes, need);
+  if (need > 0 && !aligned16(workspace))
+    return fail(MLSTM_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (mfma) return device_status(mlstm::launch_chunk_mfma(a, chunk, workspace, st), "chunkwise (mfma)");
+  return device_status(mlstm::launch_chunk_valu(a, chunk, st), "chunkwise (valu)");
+}
+
+mlstm_status_t mlstm_fwd_parallel_workspace_bytes(const mlstm_problem_t* p, size_t* bytes) {
+  if (!bytes) return fail(MLSTM_ERR_INVALID_ARG, "bytes is NULL");
+  mlstm_status_t s = check_problem(p, true);
+  if (s != MLSTM_OK) return s;
+  *bytes = mlstm::parallel_workspace(problem_args(p));
+  return ok();
+}
+
+mlstm_status_t mlstm_fwd_parallel(const mlstm_problem_t* p, const void* q, const void* k,
+                                  const void* v, const float* i_pre, const float* f_pre,
+                                  const void* o_pre, const float* C0, const float* n0,
+                                  const float* m0, void* h, float* C1, float* n1, float* m1,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  mlstm::SeqArgs a;
+  mlstm_status_t s = check_seq(p, q, k, v, i_pre, f_pre, o_pre, C0, n0, m0, h, C1, n1, m1, &a);
+  if (s != MLSTM_OK) return s;
+  const size_t need = mlstm::parallel_workspace(a);
+  if (!workspace || workspace_bytes < need)
+    return fail(MLSTM_ERR_INVALID_ARG, "workspace of %zu bytes given, %zu needed",
+                workspace_bytes, need);
+  if (!aligned16(workspace)) return fail(MLSTM_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  const Buf ws{"workspace", workspace, need};
+  // the workspace must not overlap any tensor argument
+  const size_t BH = (size_t)(p->B * p->H), T = (size_t)p->T, sq = dsize(p->qkv_dtype);
+  const Buf all[] = {
+      {"q", q, BH * T * p->d_qk * sq}, {"k", k, BH * T * p->d_qk * sq},
+      {"v", v, BH * T * p->d_v * sq},  {"i_pre", i_pre, BH * T * 4},
+      {"f_pre", f_pre, BH * T * 4},    {"o_pre", o_pre, BH * T * p->d_v * dsize(p->o_dtype)},
+      {"C0", C0, BH * p->d_qk * p->d_v * 4}, {"n0", n0, BH * p->d_qk * 4}, {"m0", m0, BH * 4},
+      {"h", h, BH * T * p->d_v * sq},  {"C1", C1, BH * p->d_qk * p->d_v * 4},
+      {"n1", n1, BH * p->d_qk * 4},    {"m1", m1, BH * 4}};
+  for (const Buf& b : all)
+    if (overlaps(ws, b)) return fail(MLSTM_ERR_INVALID_ARG, "workspace overlaps %s", b.name);
+  return device_status(mlstm::launch_parallel(a, workspace, static_cast<hipStream_t>(stream)),
+                       "parallel");
+}
+
+mlstm_status_t mlstm_step(const mlstm_problem_t* p, const void* q, const void* k, const void* v,
+                          const float* i_pre, const float* f_pre, const void* o_pre,
+                          const float* C_in, const float* n_in, const float* m_in,
+                          float* C_out, float* n_out, float* m_out, void* h, void* stream) {
+  mlstm_status_t s = check_problem(p, false);
+  if (s != MLSTM_OK) return s;
+  if (!q || !k || !v || !i_pre || !f_pre || !C_in || !n_in || !m_in || !C_out || !n_out ||
+      !m_out || !h)
+    return fail(MLSTM_ERR_INVALID_ARG,
+                "q, k, v, i_pre, f_pre, C_in, n_in, m_in, C_out, n_out, m_out and h are required");
+  const size_t BH = (size_t)(p->B * p->H), dqk = (size_t)p->d_qk, dv = (size_t)p->d_v;
+  const size_t sq = dsize(p->qkv_dtype);
+  const Buf bufs[] = {
+      {"q", q, BH * dqk * sq},        {"k", k, BH * dqk * sq},
+      {"v", v, BH * dv * sq},         {"i_pre", i_pre, BH * 4},
+      {"f_pre", f_pre, BH * 4},       {"o_pre", o_pre, BH * dv * dsize(p->o_dtype)},
+      {"C_in", C_in, BH * dqk * dv * 4}, {"n_in", n_in, BH * dqk * 4},
+      {"m_in", m_in, BH * 4},         {"C_out", C_out, BH * dqk * dv * 4},
+      {"n_out", n_out, BH * dqk * 4}, {"m_out", m_out, BH * 4},
+      {"h", h, BH * dv * sq},
+  };
+  const int nb = sizeof(bufs) / sizeof(bufs[0]);
+  for (int i = 0; i < nb; ++i)
+    if (bufs[i].p && !aligned16(bufs[i].p))
+      return fail(MLSTM_ERR_INVALID_ARG, "%s is not 16-byte aligned", bufs[i].name);
+  // outputs 9..12: an output may equal its own input exactly (in place), nothing else
+  for (int o = 9; o < nb; ++o) {
+    for (int i = 0; i < nb; ++i) {
+      if (i == o || !overlaps(bufs[o], bufs[i])) continue;
+      const bool same_state = (o <= 11) && (i == o - 3) && bufs[o].p == bufs[i].p;
+      if (!same_state)
+        return fail(MLSTM_ERR_INVALID_ARG, "%s overlaps %s", bufs[o].name, bufs[i].name);
+    }
+  }
+  mlstm::StepArgs a;
+  a.B = p->B; a.H = p->H; a.dqk = p->d_qk; a.dv = p->d_v;
+  a.qkv_bf16 = p->qkv_dtype == MLSTM_BF16;
+  a.o_mode = o_pre ? (p->o_dtype == MLSTM_BF16 ? mlstm::O_BF16 : mlstm::O_F32) : mlstm::O_NONE;
+  a.fgate_exp = p->fgate == MLSTM_FGATE_EXP;
+  a.q = q; a.k = k; a.v = v; a.i_pre = i_pre; a.f_pre = f_pre; a.o_pre = o_pre;
+  a.C_in = C_in; a.n_in = n_in; a.m_in = m_in; a.C_out = C_out; a.n_out = n_out;
+  a.m_out = m_out; a.h = h;
+  return device_status(mlstm::launch_step(a, static_cast<hipStream_t>(stream)), "step");
+}
+
+}  // extern "C"

@@ -1,0 +1,71 @@
+// Launch descriptors and launcher entry points of the mLSTM kernels.
+// Only the C-ABI layer (api.hip) calls these; argument checking happens there.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mlstm {
+
+// How the output gate o~ is given: absent (o = 1), float32 or bfloat16.
+enum OGate : int { O_NONE = 0, O_F32 = 1, O_BF16 = 2 };
+
+// Whole-sequence forward (chunkwise or parallel).  All pointers are device
+// pointers; optional ones are nullptr.  Dtype codes: 0 = f32, 1 = bf16.
+struct SeqArgs {
+  int64_t B, H, T, dqk, dv;
+  int qkv_bf16;     // q, k, v, h are bfloat16 (else float32)
+  int o_mode;       // OGate: none / f32 / bf16
+  int fgate_exp;    // forget gate: 1 = exponential, 0 = sigmoid
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* i_pre;
+  const float* f_pre;
+  const void* o_pre;
+  const float* C0;  // all three null = zero state
+  const float* n0;
+  const float* m0;
+  void* h;
+  float* C1;        // all three null = not written
+  float* n1;
+  float* m1;
+};
+
+struct StepArgs {
+  int64_t B, H, dqk, dv;
+  int qkv_bf16;
+  int o_mode;
+  int fgate_exp;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* i_pre;
+  const float* f_pre;
+  const void* o_pre;
+  const float* C_in;
+  const float* n_in;
+  const float* m_in;
+  float* C_out;
+  float* n_out;
+  float* m_out;
+  void* h;
+};
+
+// Decode step: two launches (memory stream, then normalizer/max update).
+hipError_t launch_step(const StepArgs& a, hipStream_t stream);
+
+// Chunkwise forward.
+// Returns true when the bf16 MFMA kernel covers (dqk, dv, chunk).
+bool chunk_mfma_supported(const SeqArgs& a, int64_t chunk);
+size_t chunk_mfma_workspace(const SeqArgs& a, int64_t chunk);
+hipError_t launch_chunk_mfma(const SeqArgs& a, int64_t chunk, void* ws, hipStream_t stream);
+// Generic VALU chunkwise kernel (float32 path; bf16 shapes outside MFMA cover).
+hipError_t launch_chunk_valu(const SeqArgs& a, int64_t chunk, hipStream_t stream);
+
+// Parallel (quadratic) form.
+size_t parallel_workspace(const SeqArgs& a);
+hipError_t launch_parallel(const SeqArgs& a, void* ws, hipStream_t stream);
+
+}  // namespace mlstm

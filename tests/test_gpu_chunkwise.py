@@ -1,0 +1,211 @@
+"""GPU parity of the chunkwise forward pass (mlstm_fwd_chunkwise) against the
+fp64 oracle, on the five workloads (full size: the GPU runs every head, the
+oracle a fixed sample of heads) and on edge cases."""
+from __future__ import annotations
+
+import pytest
+import torch
+
+import oracle
+import workloads
+from helpers import (TOL_BF16, TOL_F32, finite, gather_heads, has_gpu, log, nan_like,
+                     sample_heads, slice_rel_err, state_errors, to_dev)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not has_gpu(), reason="needs a GPU")]
+
+
+def _M():
+    import mlstm_matrix_memory_chunkwise_amd as M
+    return M
+
+
+def run_gpu(inp, chunk, fgate="sigmoid", o_dtype=None):
+    d = to_dev(inp)
+    o = d["o_pre"]
+    if o is not None and o_dtype is not None:
+        o = o.to(o_dtype)
+    h, (C1, n1, m1) = _M().mlstm_fwd_chunkwise(d["q"], d["k"], d["v"], d["i_pre"], d["f_pre"], o,
+                                              d["C0"], d["n0"], d["m0"], chunk=chunk, fgate=fgate)
+    torch.cuda.synchronize()
+    return h, C1, n1, m1
+
+
+def run_oracle(inp, heads=None, fgate="sigmoid", o_dtype=None):
+    sel = (lambda t: t) if heads is None else (lambda t: gather_heads(t, heads))
+    g = {k: (None if v is None else sel(v)) for k, v in inp.items()}
+    if g["o_pre"] is not None and o_dtype is not None:
+        g["o_pre"] = g["o_pre"].to(o_dtype)
+    return oracle.recurrent(g["q"], g["k"], g["v"], g["i_pre"], g["f_pre"], g["o_pre"],
+                            g["C0"], g["n0"], g["m0"], fgate=fgate)
+
+
+def compare(gpu, ref, tol, heads=None, label=""):
+    h, C1, n1, m1 = gpu
+    if heads is not None:
+        h, C1, n1, m1 = (gather_heads(x, heads) for x in (h, C1, n1, m1))
+    h, C1, n1, m1 = (x.cpu() for x in (h, C1, n1, m1))
+    hr, Cr, nr, mr = ref
+    e_h = slice_rel_err(h, hr)
+    eC, en, em = state_errors(C1, n1, m1, Cr, nr, mr)
+    log(f"  {label}: h {e_h:.2e} C {eC:.2e} n {en:.2e} m {em:.2e} (tol {tol:g})")
+    assert max(e_h, eC, en, em) < tol, (e_h, eC, en, em)
+    return e_h, eC, en, em
+
+
+# ----------------------------------------------------------------- workloads
+def test_c0_fp32():
+    cfg = workloads.CONFIGS["c0"]
+    log("chunkwise c0 fp32")
+    inp = workloads.make_chunkwise_inputs(cfg)
+    compare(run_gpu(inp, 16), run_oracle(inp), TOL_F32, label="c0")
+
+
+def test_c1_bf16_full():
+    cfg = workloads.CONFIGS["c1"]
+    log("chunkwise c1 bf16 full")
+    inp = workloads.make_chunkwise_inputs(cfg)
+    compare(run_gpu(inp, 64), run_oracle(inp), TOL_BF16, label="c1")
+
+
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_c2_reduced(chunk):
+    """c2's distributions and random initial state, B=1, H=2, T=1024."""
+    cfg = workloads.CONFIGS["c2"]
+    log(f"chunkwise c2 reduced chunk={chunk}")
+    inp = workloads.make_chunkwise_inputs(cfg, B=1, H=2, T=1024)
+    compare(run_gpu(inp, chunk), run_oracle(inp), TOL_BF16, label=f"c2r L={chunk}")
+
+
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_c2_full_sampled_heads(chunk):
+    cfg = workloads.CONFIGS["c2"]
+    log(f"chunkwise c2 full chunk={chunk}: inputs")
+    inp = workloads.make_chunkwise_inputs(cfg)
+    heads = sample_heads(cfg.B, cfg.H, 6, seed=chunk)
+    log(f"chunkwise c2 full chunk={chunk}: GPU")
+    gpu = run_gpu(inp, chunk)
+    log(f"chunkwise c2 full chunk={chunk}: oracle on {len(heads)} heads")
+    compare(gpu, run_oracle(inp, heads), TOL_BF16, heads, label=f"c2 L={chunk}")
+
+
+def test_c4_full_sampled_heads():
+    cfg = workloads.CONFIGS["c4"]
+    log("chunkwise c4 full: inputs")
+    inp = workloads.make_chunkwise_inputs(cfg)
+    heads = sample_heads(cfg.B, cfg.H, 2, seed=4)
+    log("chunkwise c4 full: GPU")
+    gpu = run_gpu(inp, 128)
+    log(f"chunkwise c4 full: oracle on {len(heads)} heads")
+    compare(gpu, run_oracle(inp, heads), TOL_BF16, heads, label="c4")
+
+
+# ----------------------------------------------------------------- edge cases
+EDGE = [
+    # name, dtype, B, H, T, dqk, dv, chunk, random state, with o, fgate
+    ("one chunk", "bf16", 1, 1, 64, 64, 64, 64, True, True, "sigmoid"),
+    ("heads not multiple of 8, 2 value tiles", "bf16", 1, 3, 256, 128, 128, 64, True, True, "sigmoid"),
+    ("chunk 32", "bf16", 2, 2, 256, 64, 64, 32, True, False, "sigmoid"),
+    ("exp forget gate", "bf16", 1, 2, 512, 128, 64, 64, True, True, "exp"),
+    ("d_v not a multiple of 64 (VALU)", "bf16", 1, 2, 128, 64, 48, 32, True, True, "sigmoid"),
+    ("chunk 16 bf16 (VALU)", "bf16", 1, 2, 128, 64, 64, 16, False, True, "sigmoid"),
+    ("d_qk 512 (VALU)", "bf16", 1, 1, 64, 512, 64, 32, True, True, "sigmoid"),
+    ("fp32 chunk 128 d 32/96", "f32", 1, 2, 256, 32, 96, 128, True, True, "sigmoid"),
+    ("fp32 exp gate chunk 64", "f32", 2, 1, 128, 48, 16, 64, True, False, "exp"),
+    ("d_qk 256 d_v 512 chunk 128", "bf16", 1, 2, 512, 256, 512, 128, False, True, "sigmoid"),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[e[0] for e in EDGE])
+def test_edge_cases(case):
+    name, dtype, B, H, T, dqk, dv, chunk, rstate, with_o, fgate = case
+    log(f"chunkwise edge: {name}")
+    f_dist = (-0.05, 0.1) if fgate == "exp" else (3.0, 1.0)
+    cfg = workloads.Config("edge", 7, dtype, B, H, T, dqk, dv, (chunk,), (-1.0, 2.0), f_dist,
+                           (0.0, 1.0), rstate)
+    inp = workloads.make_chunkwise_inputs(cfg, with_o=with_o)
+    tol = TOL_F32 if dtype == "f32" else TOL_BF16
+    compare(run_gpu(inp, chunk, fgate=fgate), run_oracle(inp, fgate=fgate), tol, label=name)
+
+
+def test_bf16_output_gate():
+    cfg = workloads.CONFIGS["c2"]
+    inp = workloads.make_chunkwise_inputs(cfg, B=1, H=1, T=256)
+    log("chunkwise bf16 o")
+    compare(run_gpu(inp, 64, o_dtype=torch.bfloat16), run_oracle(inp, o_dtype=torch.bfloat16),
+            TOL_BF16, label="bf16 o")
+
+
+# ----------------------------------------------------------------- properties
+def test_split_at_chunk_boundary_is_bitwise():
+    """Two calls with the carried state equal one call, bit for bit, when the
+    split falls on a chunk boundary (same operations in the same order)."""
+    cfg = workloads.CONFIGS["c2"]
+    inp = workloads.make_chunkwise_inputs(cfg, B=1, H=8, T=512)
+    log("chunkwise split bitwise")
+    M = _M()
+    d = to_dev(inp)
+    h, (C1, n1, m1) = M.mlstm_fwd_chunkwise(d["q"], d["k"], d["v"], d["i_pre"], d["f_pre"],
+                                            d["o_pre"], d["C0"], d["n0"], d["m0"], chunk=64)
+    s = 192
+    part = lambda x: x[:, :, :s].contiguous()        # noqa: E731
+    rest = lambda x: x[:, :, s:].contiguous()        # noqa: E731
+    ha, (Ca, na, ma) = M.mlstm_fwd_chunkwise(*(part(d[k]) for k in ("q", "k", "v", "i_pre", "f_pre", "o_pre")),
+                                             d["C0"], d["n0"], d["m0"], chunk=64)
+    hb, (Cb, nb, mb) = M.mlstm_fwd_chunkwise(*(rest(d[k]) for k in ("q", "k", "v", "i_pre", "f_pre", "o_pre")),
+                                             Ca, na, ma, chunk=64)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([ha, hb], dim=2), h)
+    assert torch.equal(Cb, C1) and torch.equal(nb, n1) and torch.equal(mb, m1)
+
+
+def test_chunk_64_and_128_agree():
+    cfg = workloads.CONFIGS["c2"]
+    inp = workloads.make_chunkwise_inputs(cfg, B=1, H=8, T=1024)
+    log("chunkwise 64 vs 128")
+    a = run_gpu(inp, 64)
+    b = run_gpu(inp, 128)
+    e_h = slice_rel_err(a[0].cpu(), b[0].cpu())
+    eC, en, em = state_errors(a[1].cpu(), a[2].cpu(), a[3].cpu(), b[1].cpu(), b[2].cpu(), b[3].cpu())
+    log(f"  64 vs 128: h {e_h:.2e} C {eC:.2e}")
+    assert max(e_h, eC, en, em) < TOL_BF16
+
+
+def test_deterministic():
+    cfg = workloads.CONFIGS["c2"]
+    inp = workloads.make_chunkwise_inputs(cfg, B=1, H=8, T=512)
+    log("chunkwise determinism")
+    a = run_gpu(inp, 64)
+    b = run_gpu(inp, 64)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("dtype,chunk,dv", [("bf16", 64, 128), ("bf16", 32, 48), ("f32", 16, 32)])
+def test_every_output_written(dtype, chunk, dv):
+    """Outputs pre-filled with NaN come back finite: every element was written."""
+    cfg = workloads.Config("canary", 8, dtype, 2, 3, 4 * chunk, 64, dv, (chunk,), (0.0, 1.0),
+                           (3.0, 1.0), (0.0, 1.0), True)
+    inp = workloads.make_chunkwise_inputs(cfg)
+    log(f"chunkwise canary {dtype} chunk={chunk} dv={dv}")
+    d = to_dev(inp)
+    M = _M()
+    out = nan_like(tuple(d["v"].shape), d["q"].dtype)
+    h, (C1, n1, m1) = M.mlstm_fwd_chunkwise(d["q"], d["k"], d["v"], d["i_pre"], d["f_pre"],
+                                            d["o_pre"], d["C0"], d["n0"], d["m0"], chunk=chunk,
+                                            out=out)
+    torch.cuda.synchronize()
+    assert finite(h) and finite(C1) and finite(n1) and finite(m1)
+
+
+def test_no_state_out():
+    cfg = workloads.CONFIGS["c1"]
+    inp = workloads.make_chunkwise_inputs(cfg, B=1, H=2, T=256)
+    d = to_dev(inp)
+    M = _M()
+    h, st = M.mlstm_fwd_chunkwise(d["q"], d["k"], d["v"], d["i_pre"], d["f_pre"], d["o_pre"],
+                                  chunk=64, return_state=False)
+    torch.cuda.synchronize()
+    assert st is None
+    hr, *_ = run_oracle(inp)
+    assert slice_rel_err(h.cpu(), hr) < TOL_BF16

@@ -1,0 +1,69 @@
+"""GPU parity of the parallel (quadratic) form (mlstm_fwd_parallel) against the
+fp64 oracle."""
+from __future__ import annotations
+
+import pytest
+import torch
+
+import workloads
+from helpers import TOL_BF16, TOL_F32, has_gpu, log, slice_rel_err, state_errors, to_dev
+from test_gpu_chunkwise import run_oracle
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not has_gpu(), reason="needs a GPU")]
+
+
+def run_parallel(inp, fgate="sigmoid"):
+    import mlstm_matrix_memory_chunkwise_amd as M
+    d = to_dev(inp)
+    h, (C1, n1, m1) = M.mlstm_fwd_parallel(d["q"], d["k"], d["v"], d["i_pre"], d["f_pre"],
+                                           d["o_pre"], d["C0"], d["n0"], d["m0"], fgate=fgate)
+    torch.cuda.synchronize()
+    return h.cpu(), C1.cpu(), n1.cpu(), m1.cpu()
+
+
+def _cmp(inp, tol, label, fgate="sigmoid"):
+    h, C1, n1, m1 = run_parallel(inp, fgate)
+    hr, Cr, nr, mr = run_oracle(inp, fgate=fgate)
+    e_h = slice_rel_err(h, hr)
+    eC, en, em = state_errors(C1, n1, m1, Cr, nr, mr)
+    log(f"  {label}: h {e_h:.2e} C {eC:.2e} n {en:.2e} m {em:.2e}")
+    assert max(e_h, eC, en, em) < tol
+
+
+def test_parallel_c0_fp32():
+    log("parallel c0")
+    _cmp(workloads.make_chunkwise_inputs(workloads.CONFIGS["c0"]), TOL_F32, "c0")
+
+
+def test_parallel_c1_bf16():
+    log("parallel c1")
+    _cmp(workloads.make_chunkwise_inputs(workloads.CONFIGS["c1"]), TOL_BF16, "c1")
+
+
+def test_parallel_state_ragged_T():
+    """Random initial state, c2 distributions, T not a multiple of the 64-token
+    blocks, asymmetric dims."""
+    cfg = workloads.Config("par", 5, "bf16", 2, 2, 300, 64, 96, (), (-2.0, 3.0), (4.0, 2.0),
+                           (0.0, 1.0), True)
+    log("parallel ragged T with state")
+    _cmp(workloads.make_chunkwise_inputs(cfg), TOL_BF16, "ragged")
+
+
+def test_parallel_fp32_exp_gate():
+    cfg = workloads.Config("par32", 6, "f32", 1, 3, 130, 32, 16, (), (0.0, 1.0), (-0.05, 0.1),
+                           None, True)
+    log("parallel fp32 exp gate")
+    _cmp(workloads.make_chunkwise_inputs(cfg), TOL_F32, "fp32 exp", fgate="exp")
+
+
+def test_parallel_matches_chunkwise():
+    import mlstm_matrix_memory_chunkwise_amd as M
+    cfg = workloads.CONFIGS["c1"]
+    inp = workloads.make_chunkwise_inputs(cfg, B=1, H=4, T=512)
+    d = to_dev(inp)
+    hp, _ = M.mlstm_fwd_parallel(d["q"], d["k"], d["v"], d["i_pre"], d["f_pre"], d["o_pre"])
+    hc, _ = M.mlstm_fwd_chunkwise(d["q"], d["k"], d["v"], d["i_pre"], d["f_pre"], d["o_pre"],
+                                  chunk=64)
+    torch.cuda.synchronize()
+    assert slice_rel_err(hp.cpu(), hc.cpu()) < TOL_BF16
