@@ -29,8 +29,10 @@
  * The decode step drops the T axis.  q, k, v and h have dtype qkv_dtype; o~
  * has o_dtype; gates and state are float32.
  *
- * Memory and ownership.  Every pointer is a DEVICE pointer owned by the caller
- * and must be 16-byte aligned.  The library allocates nothing and keeps no
+ * Memory and ownership.  Every pointer is a DEVICE pointer owned by the caller.
+ * q, k, v, o~, h and C~ must be 16-byte aligned (the kernels use 16-byte
+ * vector accesses on them; mlstm_step needs this only for v and C~); every
+ * other pointer needs 4-byte alignment.  The library allocates nothing and keeps no
  * state between calls except a per-thread error string; it is reentrant.
  * Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
  * stream); the library never synchronizes.  Argument checks run on the host

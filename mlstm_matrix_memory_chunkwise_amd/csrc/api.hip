@@ -32,6 +32,7 @@ struct Buf {
   const char* name;
   const void* p;
   size_t bytes;
+  size_t align;  // alignment the kernels need (vector accesses: 16; scalars: 4)
 };
 
 bool overlaps(const Buf& x, const Buf& y) {
@@ -42,6 +43,7 @@ bool overlaps(const Buf& x, const Buf& y) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned(const Buf& b) { return (reinterpret_cast<uintptr_t>(b.p) & (b.align - 1)) == 0; }
 
 size_t dsize(int32_t dt) { return dt == MLSTM_BF16 ? 2 : 4; }
 
@@ -87,18 +89,18 @@ mlstm_status_t check_seq(const mlstm_problem_t* p, const void* q, const void* k,
   const size_t BH = (size_t)(p->B * p->H), T = (size_t)p->T;
   const size_t dqk = (size_t)p->d_qk, dv = (size_t)p->d_v, sq = dsize(p->qkv_dtype);
   const Buf bufs[] = {
-      {"q", q, BH * T * dqk * sq},          {"k", k, BH * T * dqk * sq},
-      {"v", v, BH * T * dv * sq},           {"i_pre", i_pre, BH * T * 4},
-      {"f_pre", f_pre, BH * T * 4},         {"o_pre", o_pre, BH * T * dv * dsize(p->o_dtype)},
-      {"C0", C0, BH * dqk * dv * 4},        {"n0", n0, BH * dqk * 4},
-      {"m0", m0, BH * 4},                   {"h", h, BH * T * dv * sq},
-      {"C1", C1, BH * dqk * dv * 4},        {"n1", n1, BH * dqk * 4},
-      {"m1", m1, BH * 4},
+      {"q", q, BH * T * dqk * sq, 16},      {"k", k, BH * T * dqk * sq, 16},
+      {"v", v, BH * T * dv * sq, 16},       {"i_pre", i_pre, BH * T * 4, 4},
+      {"f_pre", f_pre, BH * T * 4, 4},      {"o_pre", o_pre, BH * T * dv * dsize(p->o_dtype), 16},
+      {"C0", C0, BH * dqk * dv * 4, 16},    {"n0", n0, BH * dqk * 4, 4},
+      {"m0", m0, BH * 4, 4},                {"h", h, BH * T * dv * sq, 16},
+      {"C1", C1, BH * dqk * dv * 4, 16},    {"n1", n1, BH * dqk * 4, 4},
+      {"m1", m1, BH * 4, 4},
   };
   const int nb = sizeof(bufs) / sizeof(bufs[0]);
   for (int i = 0; i < nb; ++i)
-    if (bufs[i].p && !aligned16(bufs[i].p))
-      return fail(MLSTM_ERR_INVALID_ARG, "%s is not 16-byte aligned", bufs[i].name);
+    if (bufs[i].p && !aligned(bufs[i]))
+      return fail(MLSTM_ERR_INVALID_ARG, "%s is not %zu-byte aligned", bufs[i].name, bufs[i].align);
   // outputs (h, C1, n1, m1 = indices 9..12) must not overlap any input or each other
   for (int o = 9; o < nb; ++o)
     for (int i = 0; i < nb; ++i)
@@ -212,16 +214,18 @@ mlstm_status_t mlstm_fwd_parallel(const mlstm_problem_t* p, const void* q, const
     return fail(MLSTM_ERR_INVALID_ARG, "workspace of %zu bytes given, %zu needed",
                 workspace_bytes, need);
   if (!aligned16(workspace)) return fail(MLSTM_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
-  const Buf ws{"workspace", workspace, need};
+  const Buf ws{"workspace", workspace, need, 16};
   // the workspace must not overlap any tensor argument
   const size_t BH = (size_t)(p->B * p->H), T = (size_t)p->T, sq = dsize(p->qkv_dtype);
   const Buf all[] = {
-      {"q", q, BH * T * p->d_qk * sq}, {"k", k, BH * T * p->d_qk * sq},
-      {"v", v, BH * T * p->d_v * sq},  {"i_pre", i_pre, BH * T * 4},
-      {"f_pre", f_pre, BH * T * 4},    {"o_pre", o_pre, BH * T * p->d_v * dsize(p->o_dtype)},
-      {"C0", C0, BH * p->d_qk * p->d_v * 4}, {"n0", n0, BH * p->d_qk * 4}, {"m0", m0, BH * 4},
-      {"h", h, BH * T * p->d_v * sq},  {"C1", C1, BH * p->d_qk * p->d_v * 4},
-      {"n1", n1, BH * p->d_qk * 4},    {"m1", m1, BH * 4}};
+      {"q", q, BH * T * p->d_qk * sq, 16}, {"k", k, BH * T * p->d_qk * sq, 16},
+      {"v", v, BH * T * p->d_v * sq, 16},  {"i_pre", i_pre, BH * T * 4, 4},
+      {"f_pre", f_pre, BH * T * 4, 4},
+      {"o_pre", o_pre, BH * T * p->d_v * dsize(p->o_dtype), 16},
+      {"C0", C0, BH * p->d_qk * p->d_v * 4, 16}, {"n0", n0, BH * p->d_qk * 4, 4},
+      {"m0", m0, BH * 4, 4},               {"h", h, BH * T * p->d_v * sq, 16},
+      {"C1", C1, BH * p->d_qk * p->d_v * 4, 16}, {"n1", n1, BH * p->d_qk * 4, 4},
+      {"m1", m1, BH * 4, 4}};
   for (const Buf& b : all)
     if (overlaps(ws, b)) return fail(MLSTM_ERR_INVALID_ARG, "workspace overlaps %s", b.name);
   return device_status(mlstm::launch_parallel(a, workspace, static_cast<hipStream_t>(stream)),
@@ -241,18 +245,18 @@ mlstm_status_t mlstm_step(const mlstm_problem_t* p, const void* q, const void* k
   const size_t BH = (size_t)(p->B * p->H), dqk = (size_t)p->d_qk, dv = (size_t)p->d_v;
   const size_t sq = dsize(p->qkv_dtype);
   const Buf bufs[] = {
-      {"q", q, BH * dqk * sq},        {"k", k, BH * dqk * sq},
-      {"v", v, BH * dv * sq},         {"i_pre", i_pre, BH * 4},
-      {"f_pre", f_pre, BH * 4},       {"o_pre", o_pre, BH * dv * dsize(p->o_dtype)},
-      {"C_in", C_in, BH * dqk * dv * 4}, {"n_in", n_in, BH * dqk * 4},
-      {"m_in", m_in, BH * 4},         {"C_out", C_out, BH * dqk * dv * 4},
-      {"n_out", n_out, BH * dqk * 4}, {"m_out", m_out, BH * 4},
-      {"h", h, BH * dv * sq},
+      {"q", q, BH * dqk * sq, 4},     {"k", k, BH * dqk * sq, 4},
+      {"v", v, BH * dv * sq, 16},     {"i_pre", i_pre, BH * 4, 4},
+      {"f_pre", f_pre, BH * 4, 4},    {"o_pre", o_pre, BH * dv * dsize(p->o_dtype), 4},
+      {"C_in", C_in, BH * dqk * dv * 4, 16}, {"n_in", n_in, BH * dqk * 4, 4},
+      {"m_in", m_in, BH * 4, 4},      {"C_out", C_out, BH * dqk * dv * 4, 16},
+      {"n_out", n_out, BH * dqk * 4, 4}, {"m_out", m_out, BH * 4, 4},
+      {"h", h, BH * dv * sq, 4},
   };
   const int nb = sizeof(bufs) / sizeof(bufs[0]);
   for (int i = 0; i < nb; ++i)
-    if (bufs[i].p && !aligned16(bufs[i].p))
-      return fail(MLSTM_ERR_INVALID_ARG, "%s is not 16-byte aligned", bufs[i].name);
+    if (bufs[i].p && !aligned(bufs[i]))
+      return fail(MLSTM_ERR_INVALID_ARG, "%s is not %zu-byte aligned", bufs[i].name, bufs[i].align);
   // outputs 9..12: an output may equal its own input exactly (in place), nothing else
   for (int o = 9; o < nb; ++o) {
     for (int i = 0; i < nb; ++i) {

@@ -393,6 +393,10 @@ __global__ __launch_bounds__(NTH, MINW) void chunk_mfma_kernel(SeqArgs a) {
         pk.x = pack_bf2(pe[0], pe[1]);
         pk.y = pack_bf2(pe[2], pe[3]);
         *reinterpret_cast<uint2*>(sPV + i * C::PROW + jt * 16 + 4 * g) = pk;
+        // P V runs in 32-token k-steps: the tile right of an even diagonal
+        // tile lies in the same step and must read as zero (j > i)
+        if (jt == it && (it & 1) == 0)
+          *reinterpret_cast<uint2*>(sPV + i * C::PROW + (jt + 1) * 16 + 4 * g) = make_uint2(0u, 0u);
       }
      }
     }

@@ -1,8 +1,9 @@
 """GPU parity of the decode step (mlstm_step) against the fp64 oracle.
 
 The step computes in float32 throughout (bf16 inputs are widened exactly), so
-both dtypes are held to the float32 bound (1e-4), tighter than the 2e-2 bound
-allowed for bf16 inputs.
+the float32 state is held to the float32 bound (1e-4) for both dtypes, and a
+bf16 h to the bf16 rounding floor 2^-8 (plus 1e-4): both far tighter than the
+2e-2 allowed for bf16 inputs.
 """
 from __future__ import annotations
 
@@ -11,7 +12,7 @@ import torch
 
 import oracle
 import workloads
-from helpers import (TOL_F32, f64, gather_heads, has_gpu, log, sample_heads, slice_rel_err,
+from helpers import (TOL_BF16_ROUNDED, TOL_F32, f64, gather_heads, has_gpu, log, sample_heads, slice_rel_err,
                      state_errors, to_dev)
 
 pytestmark = [pytest.mark.gpu,
@@ -71,7 +72,8 @@ def test_step_small(dtype, inplace):
     e_h = slice_rel_err(h.permute(1, 2, 0, 3), torch.from_numpy(hr).permute(1, 2, 0, 3))
     eC, en, em = state_errors(C, n, m, Cr, nr, mr)
     log(f"  h {e_h:.2e} C {eC:.2e} n {en:.2e} m {em:.2e}")
-    assert max(e_h, eC, en, em) < TOL_F32
+    assert e_h < (TOL_F32 if dtype == "f32" else TOL_BF16_ROUNDED)
+    assert max(eC, en, em) < TOL_F32
 
 
 @pytest.mark.parametrize("dqk,dv", [(16, 16), (64, 80), (144, 32), (512, 512)])
@@ -82,7 +84,8 @@ def test_step_shapes(dqk, dv):
     hr, Cr, nr, mr = _oracle(inp, 5)
     e_h = slice_rel_err(h.permute(1, 2, 0, 3), torch.from_numpy(hr).permute(1, 2, 0, 3))
     eC, en, em = state_errors(C, n, m, Cr, nr, mr)
-    assert max(e_h, eC, en, em) < TOL_F32
+    assert e_h < TOL_BF16_ROUNDED
+    assert max(eC, en, em) < TOL_F32
 
 
 def test_step_exp_gate_no_output_gate():
@@ -101,7 +104,7 @@ def test_step_bf16_output_gate():
     h, C, n, m = _run(inp, 6, inplace=True, o_bf16=True)
     hr, Cr, nr, mr = _oracle(inp, 6, o_round_bf16=True)
     e_h = slice_rel_err(h.permute(1, 2, 0, 3), torch.from_numpy(hr).permute(1, 2, 0, 3))
-    assert e_h < TOL_F32
+    assert e_h < TOL_BF16_ROUNDED
 
 
 def test_step_full_c3_sampled_heads():
@@ -137,4 +140,5 @@ def test_step_full_c3_sampled_heads():
                         torch.from_numpy(hr[:, 0]).permute(1, 0, 2).unsqueeze(0))
     eC, en, em = state_errors(C_gpu, n_gpu, m_gpu, Cr, nr, mr)
     log(f"  c3: h {e_h:.2e} C {eC:.2e} n {en:.2e} m {em:.2e}")
-    assert max(e_h, eC, en, em) < TOL_F32
+    assert e_h < TOL_BF16_ROUNDED
+    assert max(eC, en, em) < TOL_F32
