@@ -12,26 +12,33 @@
 //   den_i = max(|g_i q_i . n~_s + sum_j D_ij (q_i . k_j)|, exp(-m_i))
 //   h_i = sigmoid(o~_i) (.) num_i / den_i
 //   C~ <- g_L C~_s + K^T diag(w) V,  n~ <- g_L n~_s + K^T w,  m <- m_L.
-// Because m is known from the gates alone, every weight is <= 1 and no online
+// m depends on the gates only, so every weight is <= 1 and no online
 // rescaling is needed (unlike softmax attention).
 //
-// Design (MI355X):
+// Design (MI355X, CDNA4):
 // * One workgroup (4 waves) per (head, 64 value columns).  It walks the chunks
 //   in order and keeps its [d_qk x 64] slice of C~ in float32 registers (each
-//   wave owns 16 columns, all d_qk rows) for the whole sequence, so the state
-//   never round-trips through HBM between chunks.  Workgroups of one head are
-//   placed on one XCD so q/k re-reads hit that XCD's L2.
-// * Five contractions per chunk, all bf16 MFMA 16x16x32 with fp32 accumulate:
-//     S^T = K Q^T (causal tiles only), readout (C~^T Q^T) with C~ taken
-//     straight from its accumulator registers, P V, and the state update
-//     K^T (w V).  The accumulator layout of the state update is arranged
-//     (rows permuted) so that each lane holds 8 consecutive d_qk rows: the
-//     readout then feeds C~ to the MFMA without any data movement.
-// * q/k are staged through LDS in 64-wide d_qk slices, double buffered, with
-//   the next slice's global loads in flight during the current slice's math.
-//   k is written twice: row-major (for Q K^T) and transposed (for K^T V, whose
-//   contraction runs over tokens).  The transposes are 8x8 register transposes
-//   done while staging.
+//   wave: 16 columns x all d_qk rows) for the whole sequence; the state never
+//   round-trips through HBM between chunks.  The workgroups of one head sit on
+//   one XCD (block id = head mod 8), so their shared q/k reads hit one L2.
+// * Four contractions per chunk on v_mfma_f32_16x16x32_bf16 (fp32 accumulate):
+//   S^T = K Q^T (causal 16x16 tiles), the readout C~^T Q^T, P V, and the state
+//   update K^T (w V).  The state update's output rows are permuted so that a
+//   lane holds 8 consecutive d_qk rows of C~: the readout then takes C~ from
+//   its accumulator registers with no data movement.
+// * Every load inside the chunk loop goes global -> LDS directly
+//   (global_load_lds_dwordx4 / _dword): q/k in 64-wide d_qk slices ("stages")
+//   into a ring of D+1 slots with D stages in flight, the value tile and the
+//   o~ tile once per chunk, and the gate preactivations.  The loads are issued
+//   from inline asm, so the compiler sees no vector-memory load in the loop and
+//   inserts no waits of its own; each wait is an explicit s_waitcnt vmcnt(n)
+//   whose n (the loads this wave issued after the awaited one) is a
+//   compile-time constant, because every load is issued unconditionally
+//   (clamped to valid addresses past the end of the sequence).
+// * All tiles stay row-major in LDS (128-byte rows, 16-byte chunks XOR-swizzled
+//   by row).  Operands that contract over tokens (K^T for the state update,
+//   V^T for P V and the update) are read with ds_read_b64_tr_b16, the gfx950
+//   LDS transpose read, instead of keeping transposed copies.
 // * The denominator uses the float32 decay-weighted row sums (before P is
 //   rounded to bf16) and the float32 n~.
 #include "common.hpp"
@@ -43,77 +50,154 @@ namespace {
 constexpr int NW = 4;       // waves per workgroup
 constexpr int NTH = 256;    // threads per workgroup
 constexpr int TV = 64;      // value columns per workgroup (16 per wave)
-constexpr int AS = 64;      // d_qk slice width
-constexpr int PAD = 8;      // bf16 row padding in LDS (bank spread)
+constexpr int AS = 64;      // d_qk slice width (one stage)
 
-template <int DQK, int L>
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+
+template <int DQK, int L, int OM>
 struct CK {
   static constexpr int NT = L / 16;                // 16-token tiles per chunk
   static constexpr int NKS = L / 32;               // 32-token MFMA k-steps
-  static constexpr int NS = DQK / AS;              // d_qk slices
+  static constexpr int NS = DQK / AS;              // stages (d_qk slices) per chunk
   static constexpr int NCT = DQK / 16;             // 16-row C~ tiles
-  static constexpr int QROW = AS + PAD;            // row stride of Q/K slices
-  static constexpr int KTROW = L + PAD;            // row stride of K^T slice
-  static constexpr int PROW = L + PAD;             // row stride of P and V^T
+  static constexpr int TILE = L * 128;             // bytes of one [L x 64] bf16 tile
+  static constexpr int DPREF = (L == 128) ? 1 : 4;
+  // look-ahead: at most one chunk, so that nothing issued for a later chunk is
+  // awaited before it is needed
+  static constexpr int D = DPREF < NS ? DPREF : NS;
+  static constexpr int NSLOT = D + 1;
+  static constexpr int VSLOT = (D <= NS - 1) ? 1 : 2;   // value tile slots
+  static constexpr int OROW = (OM == O_BF16) ? 128 : 256;   // bytes per o~ tile row
+  static constexpr int OTILE = (OM == O_NONE) ? 16 : L * OROW;
+  static constexpr int PROW = L + 8;               // padded row of P (bf16)
   static constexpr int NTILES = NT * (NT + 1) / 2; // causal 16x16 score tiles
   static constexpr int TPW = (NTILES + NW - 1) / NW;
-  static constexpr int NBLK = L * AS / 64;         // 8x8 blocks per staged slice
-  static constexpr int PBUF = (L > TV ? L : TV) * PROW;
   static constexpr int NQN = (NT + NW - 1) / NW;
+  static constexpr int NB_QK = L / 16;             // 1 KB loads per wave per stage (q + k)
+  static constexpr int NB_V = L / 32;              // 1 KB loads per wave per value tile
+  static constexpr int NB_O = (OM == O_NONE) ? 0 : L * OROW / 1024 / NW;   // per o~ tile
+  static constexpr int GH = (L > 64) ? 2 : 1;      // 64-token halves of the gates
+  static constexpr int NB_G = 2 * GH;              // 256 B gate loads per wave per chunk
+  static constexpr int NB_X = NB_O + NB_G;         // per-chunk loads after the opening stage
   static_assert(DQK % AS == 0 && NS <= NW, "d_qk must be 64, 128, 192 or 256");
   static_assert(L % 32 == 0 && L <= 128, "chunk must be 32, 64 or 128");
-  static_assert(2 * NBLK <= NTH && L <= NTH, "staging roles");
 };
 
-// Physical row of d_qk row `a` (within a 64-wide slice) in the staged K^T
-// buffer.  The state-update MFMA for C~ tile t reads rows 16t..16t+15 and its
-// output row r then holds d_qk row 32(t/2) + 8(r/4) + 4(t%2) + r%4, so a lane
-// (group g) ends up with rows 32p + 8g + 0..7 of tile pair p.
-__device__ __forceinline__ int kt_row(int a) {
-  const int p = a >> 5, rem = a & 31;
-  return 32 * p + 16 * ((rem & 7) >> 2) + 4 * (rem >> 3) + (rem & 3);
+// Byte offset of element (row, col) in a [rows x 64] bf16 tile with 128-byte
+// rows whose 16-byte chunks are XOR-swizzled by (row / 2) mod 8: the 16 rows
+// read by one MFMA fragment land on 16 distinct bank groups.
+__device__ __forceinline__ int swz(int row, int col) {
+  return row * 128 + 16 * ((col >> 3) ^ ((row >> 1) & 7)) + 2 * (col & 7);
 }
 
-__device__ __forceinline__ uint4 ld16(const bf16_t* p) { return *reinterpret_cast<const uint4*>(p); }
-__device__ __forceinline__ void st16(bf16_t* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+__device__ __forceinline__ uint4 lds_ld16(const char* base, int off) {
+  return *reinterpret_cast<const uint4*>(base + off);
+}
 
-// 8x8 transpose of bf16: in[r] holds row r (8 elements); out[e] = column e.
-__device__ __forceinline__ void transpose8x8(const uint4* in, uint4* out) {
-  const uint32_t* w = reinterpret_cast<const uint32_t*>(in);  // w[4r + d] = elems 2d, 2d+1 of row r
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    uint32_t lo[4], hi[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t A = w[4 * (2 * p) + d], Bw = w[4 * (2 * p + 1) + d];
-      lo[p] = (A & 0xffffu) | (Bw << 16);
-      hi[p] = (A >> 16) | (Bw & 0xffff0000u);
-    }
-    out[2 * d] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-    out[2 * d + 1] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+// ds_read_b64_tr_b16: within each 16-lane group, lanes 4r..4r+3 name 4
+// consecutive bf16 of "row" r (r = 0..3); lane c of the group receives
+// element c of the 16-wide concatenation of each row, for rows 0..3.
+__device__ __forceinline__ uint2 lds_tr(const char* base, int off) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(base + off));
+  return __builtin_bit_cast(uint2, v);
+}
+
+__device__ __forceinline__ bf16x8 join(uint2 lo, uint2 hi) {
+  return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
+__device__ __forceinline__ uint32_t cvt2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v;
+  v[0] = static_cast<__bf16>(lo);
+  v[1] = static_cast<__bf16>(hi);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ bf16x8 cvt8(const float* x) {
+  return __builtin_bit_cast(
+      bf16x8, make_uint4(cvt2(x[0], x[1]), cvt2(x[2], x[3]), cvt2(x[4], x[5]), cvt2(x[6], x[7])));
+}
+
+// global -> LDS loads.  Lane l's 16 (4) bytes land at lds + 16 l (4 l); the
+// LDS base goes through M0.  Issued from asm so that the compiler neither
+// tracks nor waits on them: every wait on them is explicit.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void_t*)p));
+}
+__device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(lds), "v"(gsrc) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* gsrc, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
+               :: "s"(lds), "v"(gsrc) : "memory");
+}
+
+// s_waitcnt with vmcnt = n and the other counters unconstrained (gfx9 encoding).
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Issue order of one wave (steady state).  At the top of stage y (after its
+// barrier): the loads of stage y + D (NB_QK, plus NB_V when y + D opens a
+// chunk), then, when y opens chunk c, the per-chunk loads (o~ of chunk c and
+// the gates of chunk c + 1: NB_X).  Loads of stage x were issued at the top
+// of stage x - D; when the wave waits for stage x, the loads issued after
+// them are counted below.  h stores (also vector-memory ops) are not counted,
+// which can only make a wait stricter.
+template <int NS, int D, int NBQK, int NBV, int NBX>
+__host__ __device__ constexpr int loads_after_stage(int s) {
+  int n = 0;
+  for (int k = 1; k < D; ++k) n += NBQK + (((s + k) % NS) == 0 ? NBV : 0);
+  for (int k = 1; k <= D; ++k) n += (((s - k) % NS + NS) % NS == 0) ? NBX : 0;
+  return n;
+}
+// ... and after the per-chunk loads of chunk c, at the end of chunk c.
+template <int NS, int D, int NBQK, int NBV>
+__host__ __device__ constexpr int loads_after_chunk_extras() {
+  int n = 0;
+  for (int k = 1; k < NS; ++k) n += NBQK + (((k + D) % NS) == 0 ? NBV : 0);
+  return n;
+}
+
+// Wait for the stage with slice index s (s < NS <= 4; folds to one s_waitcnt
+// once the slice loop is unrolled).
+template <int NS, int D, int NBQK, int NBV, int NBX>
+__device__ __forceinline__ void wait_stage(int s) {
+  switch (s) {
+    case 0: wait_vm<loads_after_stage<NS, D, NBQK, NBV, NBX>(0)>(); break;
+    case 1: wait_vm<loads_after_stage<NS, D, NBQK, NBV, NBX>(1 % NS)>(); break;
+    case 2: wait_vm<loads_after_stage<NS, D, NBQK, NBV, NBX>(2 % NS)>(); break;
+    default: wait_vm<loads_after_stage<NS, D, NBQK, NBV, NBX>(3 % NS)>(); break;
   }
 }
 
-template <int DQK, int L, int OM, int MINW>
-__global__ __launch_bounds__(NTH, MINW) void chunk_mfma_kernel(SeqArgs a) {
-  using C = CK<DQK, L>;
-  __shared__ __align__(16) bf16_t sQ[2][L * C::QROW];
-  __shared__ __align__(16) bf16_t sK[2][L * C::QROW];
-  __shared__ __align__(16) bf16_t sKt[2][AS * C::KTROW];
-  __shared__ __align__(16) bf16_t sPV[C::PBUF];   // V^T (chunk prologue) / P (epilogue)
-  __shared__ __align__(16) float sGate[2][5][L];  // u, M, g, w, exp(-m)  by chunk parity
+template <int DQK, int L, int OM>
+__global__ __launch_bounds__(NTH, 1) void chunk_mfma_kernel(SeqArgs a) {
+  using C = CK<DQK, L, OM>;
+  __shared__ __align__(1024) char sRing[C::NSLOT][2][C::TILE];  // [slot][q|k]
+  __shared__ __align__(1024) char sV[C::VSLOT][C::TILE];
+  __shared__ __align__(1024) char sO[C::OTILE];                 // o~ tile of the chunk
+  __shared__ __align__(256) float sGin[NW][2][64 * C::GH];      // raw gates, per wave
+  __shared__ __align__(16) bf16_t sP[L * C::PROW];
+  __shared__ __align__(16) float sGate[2][5][L];  // u, M, g, w, exp(-m) by chunk parity
   __shared__ float sRs[NW][L];
   __shared__ float sQn[L];
   __shared__ __align__(16) float sN[DQK];
-  __shared__ float sMs[2];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l16 = lane & 15;
   const int g = lane >> 4;
 
-  // ---- workgroup -> (head, value tile); the tiles of a head share an XCD
+  // ---- workgroup -> (head, value tile)
   const int nvt = static_cast<int>(a.dv / TV);
   const int64_t nhead = a.B * a.H;
   int64_t head;
@@ -132,7 +216,7 @@ __global__ __launch_bounds__(NTH, MINW) void chunk_mfma_kernel(SeqArgs a) {
   const int dv = static_cast<int>(a.dv);
   const int64_t T = a.T;
   const int nchunks = static_cast<int>(T / L);
-  const int b0w = vt * TV + wave * 16;   // first value column of this wave
+  const int b0w = vt * TV + wave * 16;
 
   const bf16_t* gq = static_cast<const bf16_t*>(a.q) + head * T * DQK;
   const bf16_t* gk = static_cast<const bf16_t*>(a.k) + head * T * DQK;
@@ -141,7 +225,7 @@ __global__ __launch_bounds__(NTH, MINW) void chunk_mfma_kernel(SeqArgs a) {
   const float* gf = a.f_pre + head * T;
   bf16_t* gh = static_cast<bf16_t*>(a.h) + head * T * dv;
 
-  // ---- state: C~ columns of this wave in registers, n~ in LDS, m in a register
+  // ---- state
   f32x4 cacc[C::NCT];
 #pragma unroll
   for (int t = 0; t < C::NCT; ++t) {
@@ -154,175 +238,191 @@ __global__ __launch_bounds__(NTH, MINW) void chunk_mfma_kernel(SeqArgs a) {
   if (tid < DQK) sN[tid] = a.C0 ? a.n0[head * DQK + tid] : 0.0f;
   float m_s = a.C0 ? a.m0[head] : 0.0f;
 
-  // ---- staging roles
-  const bool k_role = tid < C::NBLK;
-  const bool q_role = !k_role && tid < 2 * C::NBLK;
-  const int sblk = k_role ? tid : tid - C::NBLK;
-  const int s_jb = sblk / (AS / 8), s_ab = sblk % (AS / 8);
-  const bf16_t* s_src = k_role ? gk : gq;
-  uint4 pre[8];  // next slice (8 rows x 8 d_qk columns)
-  auto load_slice = [&](int c, int s) {
-    if (k_role || q_role) {
-      const bf16_t* src = s_src + (static_cast<int64_t>(c) * L + 8 * s_jb) * DQK + s * AS + 8 * s_ab;
+  // ---- stage loads (global -> LDS).  Lane l of a 1 KB load writes bytes
+  // 16l..16l+15 of its destination: row 8G + l/8 of the tile, physical chunk
+  // l%8, which holds logical chunk (l%8) ^ ((row/2)%8).
+  const int ld_r = lane >> 3, ld_pc = lane & 7;
+  auto issue_stage = [&](int x) {
+    const int cx = x / C::NS, sx = x % C::NS;
+    const int cc = cx < nchunks ? cx : nchunks - 1;    // past the end: harmless re-read
+    char* slot = sRing[x % C::NSLOT][0];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) pre[r] = ld16(src + r * DQK);
+    for (int m = 0; m < C::NB_QK; ++m) {
+      const int G = wave * C::NB_QK + m;               // 0 .. L/4-1
+      const int mat = G / (L / 8);                      // 0 = q, 1 = k
+      const int Gr = G % (L / 8);
+      const int row = 8 * Gr + ld_r;
+      const int lc = ld_pc ^ ((row >> 1) & 7);
+      const bf16_t* src = (mat ? gk : gq) + (static_cast<int64_t>(cc) * L + row) * DQK + sx * AS + 8 * lc;
+      dma16(src, lds_addr(slot + mat * C::TILE + Gr * 1024));
+    }
+    if (sx == 0) {
+#pragma unroll
+      for (int m = 0; m < C::NB_V; ++m) {
+        const int Gr = wave * C::NB_V + m;             // 0 .. L/8-1
+        const int row = 8 * Gr + ld_r;
+        const int lc = ld_pc ^ ((row >> 1) & 7);
+        const bf16_t* src = gv + (static_cast<int64_t>(cc) * L + row) * dv + 8 * lc;
+        dma16(src, lds_addr(sV[cx % C::VSLOT] + Gr * 1024));
+      }
     }
   };
-  auto store_slice = [&](int buf) {
-    if (k_role || q_role) {
-      bf16_t* dst = (k_role ? sK[buf] : sQ[buf]) + 8 * s_jb * C::QROW + 8 * s_ab;
+  // Per-chunk loads: the o~ tile of chunk c (rows of 64 values; 16-byte
+  // chunks swizzled by row) and this wave's copy of the gates of chunk c + 1.
+  auto issue_chunk_extras = [&](int c) {
+    if (OM != O_NONE) {
+      constexpr int RPI = 1024 / C::OROW;               // o~ rows per 1 KB load
+      constexpr int NCH = C::OROW / 16;                 // 16-byte chunks per row
 #pragma unroll
-      for (int r = 0; r < 8; ++r) st16(dst + r * C::QROW, pre[r]);
+      for (int m = 0; m < C::NB_O; ++m) {
+        const int G = wave * C::NB_O + m;
+        const int row = RPI * G + lane / NCH;
+        const int pc = lane % NCH;
+        const int lc = (OM == O_F32) ? (pc ^ (row & 15)) : (pc ^ ((row >> 1) & 7));
+        const int64_t r = head * T + static_cast<int64_t>(c) * L + row;
+        const char* src = (OM == O_F32)
+            ? reinterpret_cast<const char*>(static_cast<const float*>(a.o_pre) + r * dv + vt * TV + 4 * lc)
+            : reinterpret_cast<const char*>(static_cast<const bf16_t*>(a.o_pre) + r * dv + vt * TV + 8 * lc);
+        dma16(src, lds_addr(sO + G * 1024));
+      }
     }
-    if (k_role) {
-      uint4 col[8];
-      transpose8x8(pre, col);
+    const int cn = (c + 1 < nchunks) ? c + 1 : nchunks - 1;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) st16(sKt[buf] + kt_row(8 * s_ab + e) * C::KTROW + 8 * s_jb, col[e]);
+    for (int h2 = 0; h2 < C::GH; ++h2) {
+      const int64_t j = static_cast<int64_t>(cn) * L + (lane + 64 * h2) % L;
+      dma4(gi + j, lds_addr(&sGin[wave][0][64 * h2]));
+      dma4(gf + j, lds_addr(&sGin[wave][1][64 * h2]));
     }
   };
-  // V tile: thread t < L owns an 8x8 block (8 tokens x 8 columns)
-  const bool v_role = tid < L;
-  const int v_jb = tid >> 3, v_cb = tid & 7;
-  uint4 pv[8];
-  auto load_v = [&](int c) {
-    if (v_role) {
-      const bf16_t* src = gv + (static_cast<int64_t>(c) * L + 8 * v_jb) * dv + 8 * v_cb;
+
+  // Gate scan of one chunk (gates in this wave's sGin copy) given the carried
+  // m.  Every wave computes it (no wait on another wave); wave 0 publishes the
+  // per-token values.  Returns the m after the chunk's last token.
+  auto scan_gates = [&](int par, float ms) {
+    float pgi[2], pgf[2], lf[2], bcum[2], u[2], Mx[2];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) pv[r] = ld16(src + static_cast<int64_t>(r) * dv);
+    for (int h2 = 0; h2 < 2; ++h2) {
+      pgi[h2] = (h2 < C::GH) ? sGin[wave][0][lane + 64 * h2] : 0.0f;
+      pgf[h2] = (h2 < C::GH) ? sGin[wave][1][lane + 64 * h2] : 0.0f;
     }
-  };
-  float pgi[2], pgf[2];  // wave 0: gate preactivations of tokens lane, lane + 64
-  auto load_gates = [&](int c) {
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int j = lane + 64 * h2;
+      lf[h2] = (j < L && (h2 == 0 || L > 64)) ? log_forget(pgf[h2], a.fgate_exp) : 0.0f;
+    }
+    bcum[0] = wave_incl_sum(lf[0], lane);
+    u[0] = (lane < L) ? pgi[0] - bcum[0] : -INFINITY;
+    Mx[0] = fmaxf(ms, wave_incl_max(u[0], lane));
+    if (L > 64) {
+      bcum[1] = wave_incl_sum(lf[1], lane) + __shfl(bcum[0], 63, 64);
+      u[1] = pgi[1] - bcum[1];
+      Mx[1] = fmaxf(__shfl(Mx[0], 63, 64), wave_incl_max(u[1], lane));
+    } else {
+      bcum[1] = u[1] = Mx[1] = 0.0f;
+    }
+    const float Mlast = __shfl(L > 64 ? Mx[1] : Mx[0], (L - 1) & 63, 64);
+    const float blast = __shfl(L > 64 ? bcum[1] : bcum[0], (L - 1) & 63, 64);
     if (wave == 0) {
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const int j = lane + 64 * h2;
-        pgi[h2] = (j < L) ? gi[static_cast<int64_t>(c) * L + j] : 0.0f;
-        pgf[h2] = (j < L) ? gf[static_cast<int64_t>(c) * L + j] : 0.0f;
-      }
-    }
-  };
-
-  load_gates(0);
-  load_v(0);
-  load_slice(0, 0);
-
-  f32x4 outT[C::NT];
-  f32x4 sacc[C::TPW];
-  uint4 Vf[C::NKS];
-  bf16x8 wVf[C::NKS];
-  float nnew = 0.0f;
-
-  for (int c = 0; c < nchunks; ++c) {
-    const int par = c & 1;
-    // ================= prologue: gates, V^T fragments
-    if (wave == 0) {
-      float lf[2], bcum[2], u[2], Mx[2];
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const int j = lane + 64 * h2;
-        lf[h2] = (j < L) ? log_forget(pgf[h2], a.fgate_exp) : 0.0f;
-      }
-      bcum[0] = wave_incl_sum(lf[0], lane);
-      u[0] = (lane < L) ? pgi[0] - bcum[0] : -INFINITY;
-      Mx[0] = fmaxf(m_s, wave_incl_max(u[0], lane));
-      if (L > 64) {
-        bcum[1] = wave_incl_sum(lf[1], lane) + __shfl(bcum[0], 63, 64);
-        u[1] = pgi[1] - bcum[1];
-        Mx[1] = fmaxf(__shfl(Mx[0], 63, 64), wave_incl_max(u[1], lane));
-      }
-      const float Mlast = (L > 64) ? __shfl(Mx[1], (L - 1) & 63, 64) : __shfl(Mx[0], (L - 1) & 63, 64);
-      const float blast = (L > 64) ? __shfl(bcum[1], (L - 1) & 63, 64) : __shfl(bcum[0], (L - 1) & 63, 64);
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         const int j = lane + 64 * h2;
         if (j < L) {
           sGate[par][0][j] = u[h2];
           sGate[par][1][j] = Mx[h2];
-          sGate[par][2][j] = __expf(m_s - Mx[h2]);
+          sGate[par][2][j] = __expf(ms - Mx[h2]);
           sGate[par][3][j] = __expf(u[h2] - Mlast);
           sGate[par][4][j] = __expf(-(bcum[h2] + Mx[h2]));
         }
       }
-      if (lane == 0) sMs[par] = blast + Mlast;
     }
-    if (v_role) {
-      uint4 col[8];
-      transpose8x8(pv, col);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) st16(sPV + (8 * v_cb + e) * C::PROW + 8 * v_jb, col[e]);
-    }
-    if (c + 1 < nchunks) {
-      load_gates(c + 1);
-      load_v(c + 1);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int ks = 0; ks < C::NKS; ++ks) {
-      Vf[ks] = ld16(sPV + (wave * 16 + l16) * C::PROW + 32 * ks + 8 * g);
-      const float4 w0 = *reinterpret_cast<const float4*>(&sGate[par][3][32 * ks + 8 * g]);
-      const float4 w1 = *reinterpret_cast<const float4*>(&sGate[par][3][32 * ks + 8 * g + 4]);
-      float x[8];
-      x[0] = bf_lo(Vf[ks].x) * w0.x; x[1] = bf_hi(Vf[ks].x) * w0.y;
-      x[2] = bf_lo(Vf[ks].y) * w0.z; x[3] = bf_hi(Vf[ks].y) * w0.w;
-      x[4] = bf_lo(Vf[ks].z) * w1.x; x[5] = bf_hi(Vf[ks].z) * w1.y;
-      x[6] = bf_lo(Vf[ks].w) * w1.z; x[7] = bf_hi(Vf[ks].w) * w1.w;
-      wVf[ks] = to_bf16x8(x);
-    }
-    const float gL = sGate[par][2][L - 1];
+    return blast + Mlast;
+  };
 
+  // ---- prologue: stages 0 .. D-1 in flight, gates of chunk 0 scanned
 #pragma unroll
-    for (int it = 0; it < C::NT; ++it) outT[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int x = 0; x < C::D; ++x) issue_stage(x);
 #pragma unroll
-    for (int k = 0; k < C::TPW; ++k) sacc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float qnp[C::NQN];
-#pragma unroll
-    for (int k = 0; k < C::NQN; ++k) qnp[k] = 0.0f;
-    float4 oreg[C::NT];
+  for (int h2 = 0; h2 < C::GH; ++h2) {
+    dma4(gi + (lane + 64 * h2) % L, lds_addr(&sGin[wave][0][64 * h2]));
+    dma4(gf + (lane + 64 * h2) % L, lds_addr(&sGin[wave][1][64 * h2]));
+  }
+  wait_vm<0>();
+  float m_next = scan_gates(0, m_s);   // m after chunk 0
 
-    // ================= d_qk slices
+  f32x4 outT[C::NT];
+  f32x4 sacc[C::TPW];
+  bf16x8 Vf[C::NKS];
+  bf16x8 wVf[C::NKS];
+  float nn[C::NS];
+  float qnp[C::NQN];
+
+  for (int c = 0; c < nchunks; ++c) {
+    const int par = c & 1;
+    float gL = 0.0f;
+
 #pragma unroll
     for (int s = 0; s < C::NS; ++s) {
-      const int buf = (c * C::NS + s) & 1;
-      store_slice(buf);
-      if (s + 1 < C::NS) load_slice(c, s + 1);
-      else if (c + 1 < nchunks) load_slice(c + 1, 0);
-      if (s == C::NS - 1 && OM != O_NONE) {
-#pragma unroll
-        for (int it = 0; it < C::NT; ++it) {
-          const int64_t row = head * T + static_cast<int64_t>(c) * L + it * 16 + l16;
-          if (OM == O_F32) {
-            oreg[it] = *reinterpret_cast<const float4*>(static_cast<const float*>(a.o_pre) + row * dv + b0w + 4 * g);
-          } else {
-            const uint2 u2 = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(a.o_pre) + row * dv + b0w + 4 * g);
-            oreg[it] = make_float4(bf_lo(u2.x), bf_hi(u2.x), bf_lo(u2.y), bf_hi(u2.y));
-          }
-        }
-      }
+      const int x = c * C::NS + s;
+      // ---- wait for this stage's LDS loads, then make them visible
+      if (x < C::D) wait_vm<0>();
+      else wait_stage<C::NS, C::D, C::NB_QK, C::NB_V, C::NB_X>(s);
       __syncthreads();
+      issue_stage(x + C::D);
+      if (s == 0) issue_chunk_extras(c);
+      const char* Qb = sRing[x % C::NSLOT][0];
+      const char* Kb = sRing[x % C::NSLOT][1];
 
-      const bf16_t* Qb = sQ[buf];
-      const bf16_t* Kb = sK[buf];
-      const bf16_t* Ktb = sKt[buf];
+      if (s == 0) {
+        // V^T fragments of this wave's 16 columns: lane (g, c) gets the
+        // values of column c for tokens 32ks + 8g + 0..7
+        const char* Vb = sV[c % C::VSLOT];
+        const int vr = l16 >> 2, vq = l16 & 3;
+#pragma unroll
+        for (int ks = 0; ks < C::NKS; ++ks) {
+          const int col = wave * 16 + 4 * vq;
+          const uint2 lo = lds_tr(Vb, swz(32 * ks + 8 * g + vr, col));
+          const uint2 hi = lds_tr(Vb, swz(32 * ks + 8 * g + 4 + vr, col));
+          Vf[ks] = join(lo, hi);
+          const float4 w0 = *reinterpret_cast<const float4*>(&sGate[par][3][32 * ks + 8 * g]);
+          const float4 w1 = *reinterpret_cast<const float4*>(&sGate[par][3][32 * ks + 8 * g + 4]);
+          float xw[8];
+          xw[0] = bf_lo(lo.x) * w0.x; xw[1] = bf_hi(lo.x) * w0.y;
+          xw[2] = bf_lo(lo.y) * w0.z; xw[3] = bf_hi(lo.y) * w0.w;
+          xw[4] = bf_lo(hi.x) * w1.x; xw[5] = bf_hi(hi.x) * w1.y;
+          xw[6] = bf_lo(hi.y) * w1.z; xw[7] = bf_hi(hi.y) * w1.w;
+          wVf[ks] = cvt8(xw);
+        }
+#pragma unroll
+        for (int it = 0; it < C::NT; ++it) outT[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < C::TPW; ++k) sacc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < C::NQN; ++k) qnp[k] = 0.0f;
+      }
+      gL = sGate[par][2][L - 1];
+
+      // ---- readout, n~ . q and score tiles for the slice's two 32-row k-steps
 #pragma unroll
       for (int p = 0; p < AS / 32; ++p) {
-        const int P = s * (AS / 32) + p;   // C~ tile pair index
+        const int P = s * (AS / 32) + p;   // C~ tile pair
         float ca[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           ca[e] = cacc[2 * P][e];
           ca[4 + e] = cacc[2 * P + 1][e];
         }
-        const bf16x8 A_C = to_bf16x8(ca);
-        const float4 n0v = *reinterpret_cast<const float4*>(&sN[32 * P + 8 * g]);
-        const float4 n1v = *reinterpret_cast<const float4*>(&sN[32 * P + 8 * g + 4]);
+        const bf16x8 A_C = cvt8(ca);
         uint4 Qf[C::NT];
 #pragma unroll
         for (int it = 0; it < C::NT; ++it) {
-          Qf[it] = ld16(Qb + (it * 16 + l16) * C::QROW + 32 * p + 8 * g);
+          Qf[it] = lds_ld16(Qb, swz(it * 16 + l16, 32 * p + 8 * g));
           outT[it] = mfma16x16x32(A_C, as_bf16x8(Qf[it]), outT[it]);
+        }
+#pragma unroll
+        for (int it = 0; it < C::NT; ++it) {
           if (it % NW == wave) {
+            const float4 n0v = *reinterpret_cast<const float4*>(&sN[32 * P + 8 * g]);
+            const float4 n1v = *reinterpret_cast<const float4*>(&sN[32 * P + 8 * g + 4]);
             qnp[it / NW] += bf_lo(Qf[it].x) * n0v.x + bf_hi(Qf[it].x) * n0v.y +
                             bf_lo(Qf[it].y) * n0v.z + bf_hi(Qf[it].y) * n0v.w +
                             bf_lo(Qf[it].z) * n1v.x + bf_hi(Qf[it].z) * n1v.y +
@@ -335,70 +435,79 @@ __global__ __launch_bounds__(NTH, MINW) void chunk_mfma_kernel(SeqArgs a) {
           for (int jt = 0; jt <= it; ++jt) {
             const int n = it * (it + 1) / 2 + jt;
             if (n % NW == wave) {
-              const uint4 Kf = ld16(Kb + (jt * 16 + l16) * C::QROW + 32 * p + 8 * g);
+              const uint4 Kf = lds_ld16(Kb, swz(jt * 16 + l16, 32 * p + 8 * g));
               sacc[n / NW] = mfma16x16x32(as_bf16x8(Kf), as_bf16x8(Qf[it]), sacc[n / NW]);
             }
           }
         }
       }
-      // state update of this slice's rows (after their readout above)
+
+      // ---- state update of the slice's rows (after their readout above).
+      // A fragment of C~ tile t: lane (g, c) holds k_j[a] for tokens
+      // 32ks+8g+0..7 and d_qk row a = 32(t/2) + 8(c/4) + 4(t%2) + c%4.
+      float npart = 0.0f;
 #pragma unroll
-      for (int tl = 0; tl < AS / 16; ++tl) {
-        const int t = s * (AS / 16) + tl;
-        cacc[t] *= gL;
+      for (int tl = 0; tl < AS / 16; ++tl) cacc[s * (AS / 16) + tl] *= gL;
+      const int kr = l16 >> 2, kq = l16 & 3;
 #pragma unroll
-        for (int ks = 0; ks < C::NKS; ++ks) {
-          const uint4 Af = ld16(Ktb + (16 * tl + l16) * C::KTROW + 32 * ks + 8 * g);
-          cacc[t] = mfma16x16x32(as_bf16x8(Af), wVf[ks], cacc[t]);
+      for (int ks = 0; ks < C::NKS; ++ks) {
+#pragma unroll
+        for (int tl = 0; tl < AS / 16; ++tl) {
+          const int col = 32 * (tl >> 1) + 8 * kq + 4 * (tl & 1);
+          const uint2 lo = lds_tr(Kb, swz(32 * ks + 8 * g + kr, col));
+          const uint2 hi = lds_tr(Kb, swz(32 * ks + 8 * g + 4 + kr, col));
+          const int t = s * (AS / 16) + tl;
+          cacc[t] = mfma16x16x32(join(lo, hi), wVf[ks], cacc[t]);
+          if (tl == wave) {
+            // n~ rows of this tile: sum_j w_j k_j[a] over this lane's 8 tokens
+            const float4 w0 = *reinterpret_cast<const float4*>(&sGate[par][3][32 * ks + 8 * g]);
+            const float4 w1 = *reinterpret_cast<const float4*>(&sGate[par][3][32 * ks + 8 * g + 4]);
+            npart += bf_lo(lo.x) * w0.x + bf_hi(lo.x) * w0.y + bf_lo(lo.y) * w0.z + bf_hi(lo.y) * w0.w +
+                     bf_lo(hi.x) * w1.x + bf_hi(hi.x) * w1.y + bf_lo(hi.y) * w1.z + bf_hi(hi.y) * w1.w;
+          }
         }
       }
-      // n~ update for this slice's rows: wave (s % NW), lane = row in slice
-      if (wave == s % NW) {
-        float acc = gL * sN[s * AS + lane];
-        const bf16_t* kr = Ktb + kt_row(lane) * C::KTROW;
-#pragma unroll
-        for (int j = 0; j < L; j += 8) {
-          const uint4 k8 = ld16(kr + j);
-          const float4 w0 = *reinterpret_cast<const float4*>(&sGate[par][3][j]);
-          const float4 w1 = *reinterpret_cast<const float4*>(&sGate[par][3][j + 4]);
-          acc += bf_lo(k8.x) * w0.x + bf_hi(k8.x) * w0.y + bf_lo(k8.y) * w0.z + bf_hi(k8.y) * w0.w +
-                 bf_lo(k8.z) * w1.x + bf_hi(k8.z) * w1.y + bf_lo(k8.w) * w1.z + bf_hi(k8.w) * w1.w;
-        }
-        nnew = acc;
-      }
+      npart += __shfl_xor(npart, 16, 64);
+      npart += __shfl_xor(npart, 32, 64);
+      nn[s] = npart;
     }
 
-    // ================= epilogue: P = S (.) D, row sums, P V, output
+    // ================= end of chunk: this chunk's o~ and the next chunk's
+    // gates have landed (each wave waits for its own loads; the barrier below
+    // publishes the o~ tile), then the epilogue
+    wait_vm<loads_after_chunk_extras<C::NS, C::D, C::NB_QK, C::NB_V>()>();
+    const float m_cur = m_next;
+    m_next = scan_gates(par ^ 1, m_cur);
+
     float rsp[C::NT];
 #pragma unroll
     for (int it = 0; it < C::NT; ++it) rsp[it] = 0.0f;
 #pragma unroll
     for (int it = 0; it < C::NT; ++it) {
 #pragma unroll
-     for (int jt = 0; jt <= it; ++jt) {
-      const int n = it * (it + 1) / 2 + jt;
-      if (n % NW == wave) {
-        const int i = it * 16 + l16;
-        const float Mi = sGate[par][1][i];
-        const float4 uj = *reinterpret_cast<const float4*>(&sGate[par][0][jt * 16 + 4 * g]);
-        float pe[4];
-        const float ujv[4] = {uj.x, uj.y, uj.z, uj.w};
+      for (int jt = 0; jt <= it; ++jt) {
+        const int n = it * (it + 1) / 2 + jt;
+        if (n % NW == wave) {
+          const int i = it * 16 + l16;
+          const float Mi = sGate[par][1][i];
+          const float4 uj = *reinterpret_cast<const float4*>(&sGate[par][0][jt * 16 + 4 * g]);
+          const float ujv[4] = {uj.x, uj.y, uj.z, uj.w};
+          float pe[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = jt * 16 + 4 * g + e;
-          pe[e] = (j <= i) ? sacc[n / NW][e] * __expf(ujv[e] - Mi) : 0.0f;
+          for (int e = 0; e < 4; ++e) {
+            const int j = jt * 16 + 4 * g + e;
+            const float pv = sacc[n / NW][e] * __expf(ujv[e] - Mi);
+            pe[e] = (jt < it || j <= i) ? pv : 0.0f;
+          }
+          rsp[it] += (pe[0] + pe[1]) + (pe[2] + pe[3]);
+          *reinterpret_cast<uint2*>(sP + i * C::PROW + jt * 16 + 4 * g) =
+              make_uint2(cvt2(pe[0], pe[1]), cvt2(pe[2], pe[3]));
+          // P V runs in 32-token k-steps: the tile right of an even diagonal
+          // tile lies in the same step and must read as zero (j > i)
+          if (jt == it && (it & 1) == 0)
+            *reinterpret_cast<uint2*>(sP + i * C::PROW + (jt + 1) * 16 + 4 * g) = make_uint2(0u, 0u);
         }
-        rsp[it] += (pe[0] + pe[1]) + (pe[2] + pe[3]);
-        uint2 pk;
-        pk.x = pack_bf2(pe[0], pe[1]);
-        pk.y = pack_bf2(pe[2], pe[3]);
-        *reinterpret_cast<uint2*>(sPV + i * C::PROW + jt * 16 + 4 * g) = pk;
-        // P V runs in 32-token k-steps: the tile right of an even diagonal
-        // tile lies in the same step and must read as zero (j > i)
-        if (jt == it && (it & 1) == 0)
-          *reinterpret_cast<uint2*>(sPV + i * C::PROW + (jt + 1) * 16 + 4 * g) = make_uint2(0u, 0u);
       }
-     }
     }
 #pragma unroll
     for (int it = 0; it < C::NT; ++it) {
@@ -414,7 +523,14 @@ __global__ __launch_bounds__(NTH, MINW) void chunk_mfma_kernel(SeqArgs a) {
       }
     }
     __syncthreads();
-    if (wave < C::NS) sN[wave * AS + lane] = nnew;
+    // n~ for the next chunk: wave w owns the rows of tile w of every slice
+    if (g == 0) {
+#pragma unroll
+      for (int s = 0; s < C::NS; ++s) {
+        const int arow = s * AS + 32 * (wave >> 1) + 8 * (l16 >> 2) + 4 * (wave & 1) + (l16 & 3);
+        sN[arow] = gL * sN[arow] + nn[s];
+      }
+    }
 
 #pragma unroll
     for (int it = 0; it < C::NT; ++it) {
@@ -424,30 +540,37 @@ __global__ __launch_bounds__(NTH, MINW) void chunk_mfma_kernel(SeqArgs a) {
 #pragma unroll
       for (int ks = 0; ks < C::NKS; ++ks) {
         if (32 * ks <= it * 16 + 15) {
-          const uint4 Pf = ld16(sPV + i * C::PROW + 32 * ks + 8 * g);
-          o = mfma16x16x32(as_bf16x8(Vf[ks]), as_bf16x8(Pf), o);
+          const uint4 Pf = *reinterpret_cast<const uint4*>(sP + i * C::PROW + 32 * ks + 8 * g);
+          o = mfma16x16x32(Vf[ks], as_bf16x8(Pf), o);
         }
       }
       const float rs = (sRs[0][i] + sRs[1][i]) + (sRs[2][i] + sRs[3][i]);
       const float den = fmaxf(fabsf(gi_ * sQn[i] + rs), sGate[par][4][i]);
-      const float inv = 1.0f / den;
+      const float inv = __builtin_amdgcn_rcpf(den);
       float hv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) hv[e] = o[e] * inv;
       if (OM != O_NONE) {
-        hv[0] *= sigmoidf_(oreg[it].x);
-        hv[1] *= sigmoidf_(oreg[it].y);
-        hv[2] *= sigmoidf_(oreg[it].z);
-        hv[3] *= sigmoidf_(oreg[it].w);
+        float ov[4];
+        if (OM == O_F32) {
+          const float4 o4 = *reinterpret_cast<const float4*>(
+              sO + i * 256 + 16 * ((wave * 4 + g) ^ (i & 15)));
+          ov[0] = o4.x; ov[1] = o4.y; ov[2] = o4.z; ov[3] = o4.w;
+        } else {
+          const uint2 o2 = *reinterpret_cast<const uint2*>(sO + swz(i, wave * 16 + 4 * g));
+          ov[0] = bf_lo(o2.x); ov[1] = bf_hi(o2.x); ov[2] = bf_lo(o2.y); ov[3] = bf_hi(o2.y);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hv[e] *= __builtin_amdgcn_rcpf(1.0f + __expf(-ov[e]));
       }
-      uint2 pk;
-      pk.x = pack_bf2(hv[0], hv[1]);
-      pk.y = pack_bf2(hv[2], hv[3]);
-      *reinterpret_cast<uint2*>(gh + (static_cast<int64_t>(c) * L + i) * dv + b0w + 4 * g) = pk;
+      *reinterpret_cast<uint2*>(gh + (static_cast<int64_t>(c) * L + i) * dv + b0w + 4 * g) =
+          make_uint2(cvt2(hv[0], hv[1]), cvt2(hv[2], hv[3]));
     }
-    m_s = sMs[par];
-    __syncthreads();
+    m_s = m_cur;
   }
+  // no LDS load may still be in flight when the workgroup ends
+  wait_vm<0>();
+  __syncthreads();
 
   // ---- final state
   if (a.C1) {
@@ -469,8 +592,7 @@ __global__ __launch_bounds__(NTH, MINW) void chunk_mfma_kernel(SeqArgs a) {
 template <int DQK, int L, int OM>
 hipError_t launch_shape(const SeqArgs& a, hipStream_t stream) {
   const unsigned nwg = static_cast<unsigned>(a.B * a.H * (a.dv / TV));
-  constexpr int MINW = 1;  // one 4-wave workgroup per CU: up to 512 registers per lane
-  chunk_mfma_kernel<DQK, L, OM, MINW><<<dim3(nwg), dim3(NTH), 0, stream>>>(a);
+  chunk_mfma_kernel<DQK, L, OM><<<dim3(nwg), dim3(NTH), 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -479,7 +601,9 @@ hipError_t launch_L(const SeqArgs& a, int64_t chunk, hipStream_t stream) {
   switch (chunk) {
     case 32: return launch_shape<DQK, 32, OM>(a, stream);
     case 64: return launch_shape<DQK, 64, OM>(a, stream);
-    default: return launch_shape<DQK, 128, OM>(a, stream);
+    default:
+      if constexpr (DQK >= 128) return launch_shape<DQK, 128, OM>(a, stream);
+      return hipErrorInvalidValue;
   }
 }
 
@@ -495,8 +619,10 @@ hipError_t launch_D(const SeqArgs& a, int64_t chunk, hipStream_t stream) {
 }  // namespace
 
 bool chunk_mfma_supported(const SeqArgs& a, int64_t chunk) {
+  // chunk 128 with d_qk 64 would need more LDS than a CU has (one look-ahead
+  // stage cannot share its value slot); it takes the VALU kernel instead
   return a.qkv_bf16 && (a.dqk == 64 || a.dqk == 128 || a.dqk == 256) && a.dv % TV == 0 &&
-         (chunk == 32 || chunk == 64 || chunk == 128) && a.T % chunk == 0;
+         (chunk == 32 || chunk == 64 || (chunk == 128 && a.dqk >= 128)) && a.T % chunk == 0;
 }
 
 size_t chunk_mfma_workspace(const SeqArgs&, int64_t) { return 0; }
