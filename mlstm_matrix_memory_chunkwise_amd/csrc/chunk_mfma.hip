@@ -41,6 +41,8 @@
 //   LDS transpose read, instead of keeping transposed copies.
 // * The denominator uses the float32 decay-weighted row sums (before P is
 //   rounded to bf16) and the float32 n~.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -178,13 +180,30 @@ __device__ __forceinline__ void wait_stage(int s) {
   }
 }
 
+template <int W>
+using wave_c = std::integral_constant<int, W>;
+
+// Runs f with the (wave-uniform) wave index as a compile-time constant, so that
+// per-wave work splits fold into straight-line code instead of branches.
+template <typename F>
+__device__ __forceinline__ void for_wave(int wave, F&& f) {
+  switch (wave) {
+    case 0: f(wave_c<0>{}); break;
+    case 1: f(wave_c<1>{}); break;
+    case 2: f(wave_c<2>{}); break;
+    default: f(wave_c<3>{}); break;
+  }
+}
+
 template <int DQK, int L, int OM>
 __global__ __launch_bounds__(NTH, 1) void chunk_mfma_kernel(SeqArgs a) {
   using C = CK<DQK, L, OM>;
   __shared__ __align__(1024) char sRing[C::NSLOT][2][C::TILE];  // [slot][q|k]
   __shared__ __align__(1024) char sV[C::VSLOT][C::TILE];
   __shared__ __align__(1024) char sO[C::OTILE];                 // o~ tile of the chunk
-  __shared__ __align__(256) float sGin[NW][2][64 * C::GH];      // raw gates, per wave
+  // raw gates [chunk parity][i~ | f~]; every wave loads the same values here
+  // (identical writes) so that all waves issue the same number of loads
+  __shared__ __align__(256) float sGin[2][2][64 * C::GH];
   __shared__ __align__(16) bf16_t sP[L * C::PROW];
   __shared__ __align__(16) float sGate[2][5][L];  // u, M, g, w, exp(-m) by chunk parity
   __shared__ float sRs[NW][L];
@@ -242,33 +261,41 @@ __global__ __launch_bounds__(NTH, 1) void chunk_mfma_kernel(SeqArgs a) {
   // 16l..16l+15 of its destination: row 8G + l/8 of the tile, physical chunk
   // l%8, which holds logical chunk (l%8) ^ ((row/2)%8).
   const int ld_r = lane >> 3, ld_pc = lane & 7;
+  // per-lane element offsets of this wave's stage loads inside one chunk/slice
+  int qk_off[C::NB_QK], v_off[C::NB_V];
+#pragma unroll
+  for (int m = 0; m < C::NB_QK; ++m) {
+    const int Gr = (wave * C::NB_QK + m) % (L / 8);
+    const int row = 8 * Gr + ld_r;
+    qk_off[m] = row * DQK + 8 * (ld_pc ^ ((row >> 1) & 7));
+  }
+#pragma unroll
+  for (int m = 0; m < C::NB_V; ++m) {
+    const int row = 8 * (wave * C::NB_V + m) + ld_r;
+    v_off[m] = row * dv + 8 * (ld_pc ^ ((row >> 1) & 7));
+  }
   auto issue_stage = [&](int x) {
     const int cx = x / C::NS, sx = x % C::NS;
     const int cc = cx < nchunks ? cx : nchunks - 1;    // past the end: harmless re-read
     char* slot = sRing[x % C::NSLOT][0];
+    const int64_t base = static_cast<int64_t>(cc) * L * DQK + sx * AS;
 #pragma unroll
     for (int m = 0; m < C::NB_QK; ++m) {
       const int G = wave * C::NB_QK + m;               // 0 .. L/4-1
       const int mat = G / (L / 8);                      // 0 = q, 1 = k
       const int Gr = G % (L / 8);
-      const int row = 8 * Gr + ld_r;
-      const int lc = ld_pc ^ ((row >> 1) & 7);
-      const bf16_t* src = (mat ? gk : gq) + (static_cast<int64_t>(cc) * L + row) * DQK + sx * AS + 8 * lc;
-      dma16(src, lds_addr(slot + mat * C::TILE + Gr * 1024));
+      dma16((mat ? gk : gq) + base + qk_off[m], lds_addr(slot + mat * C::TILE + Gr * 1024));
     }
     if (sx == 0) {
+      const int64_t vbase = static_cast<int64_t>(cc) * L * dv;
 #pragma unroll
-      for (int m = 0; m < C::NB_V; ++m) {
-        const int Gr = wave * C::NB_V + m;             // 0 .. L/8-1
-        const int row = 8 * Gr + ld_r;
-        const int lc = ld_pc ^ ((row >> 1) & 7);
-        const bf16_t* src = gv + (static_cast<int64_t>(cc) * L + row) * dv + 8 * lc;
-        dma16(src, lds_addr(sV[cx % C::VSLOT] + Gr * 1024));
-      }
+      for (int m = 0; m < C::NB_V; ++m)
+        dma16(gv + vbase + v_off[m], lds_addr(sV[cx % C::VSLOT] + (wave * C::NB_V + m) * 1024));
     }
   };
   // Per-chunk loads: the o~ tile of chunk c (rows of 64 values; 16-byte
-  // chunks swizzled by row) and this wave's copy of the gates of chunk c + 1.
+  // chunks swizzled by row) and this wave's copy of the gates of chunk c + 2
+  // (two chunks ahead, so that waiting for them never waits for a stage).
   auto issue_chunk_extras = [&](int c) {
     if (OM != O_NONE) {
       constexpr int RPI = 1024 / C::OROW;               // o~ rows per 1 KB load
@@ -286,24 +313,24 @@ __global__ __launch_bounds__(NTH, 1) void chunk_mfma_kernel(SeqArgs a) {
         dma16(src, lds_addr(sO + G * 1024));
       }
     }
-    const int cn = (c + 1 < nchunks) ? c + 1 : nchunks - 1;
+    const int cn = (c + 2 < nchunks) ? c + 2 : nchunks - 1;
 #pragma unroll
     for (int h2 = 0; h2 < C::GH; ++h2) {
       const int64_t j = static_cast<int64_t>(cn) * L + (lane + 64 * h2) % L;
-      dma4(gi + j, lds_addr(&sGin[wave][0][64 * h2]));
-      dma4(gf + j, lds_addr(&sGin[wave][1][64 * h2]));
+      dma4(gi + j, lds_addr(&sGin[c & 1][0][64 * h2]));
+      dma4(gf + j, lds_addr(&sGin[c & 1][1][64 * h2]));
     }
   };
 
-  // Gate scan of one chunk (gates in this wave's sGin copy) given the carried
-  // m.  Every wave computes it (no wait on another wave); wave 0 publishes the
-  // per-token values.  Returns the m after the chunk's last token.
+  // Gate scan of one chunk (its gates in the staging buffer of parity `par`)
+  // given the carried m; run by wave 0, which publishes the per-token
+  // values.  Returns the m after the chunk's last token.
   auto scan_gates = [&](int par, float ms) {
     float pgi[2], pgf[2], lf[2], bcum[2], u[2], Mx[2];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
-      pgi[h2] = (h2 < C::GH) ? sGin[wave][0][lane + 64 * h2] : 0.0f;
-      pgf[h2] = (h2 < C::GH) ? sGin[wave][1][lane + 64 * h2] : 0.0f;
+      pgi[h2] = (h2 < C::GH) ? sGin[par][0][lane + 64 * h2] : 0.0f;
+      pgf[h2] = (h2 < C::GH) ? sGin[par][1][lane + 64 * h2] : 0.0f;
     }
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
@@ -322,7 +349,7 @@ __global__ __launch_bounds__(NTH, 1) void chunk_mfma_kernel(SeqArgs a) {
     }
     const float Mlast = __shfl(L > 64 ? Mx[1] : Mx[0], (L - 1) & 63, 64);
     const float blast = __shfl(L > 64 ? bcum[1] : bcum[0], (L - 1) & 63, 64);
-    if (wave == 0) {
+    {
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         const int j = lane + 64 * h2;
@@ -343,11 +370,20 @@ __global__ __launch_bounds__(NTH, 1) void chunk_mfma_kernel(SeqArgs a) {
   for (int x = 0; x < C::D; ++x) issue_stage(x);
 #pragma unroll
   for (int h2 = 0; h2 < C::GH; ++h2) {
-    dma4(gi + (lane + 64 * h2) % L, lds_addr(&sGin[wave][0][64 * h2]));
-    dma4(gf + (lane + 64 * h2) % L, lds_addr(&sGin[wave][1][64 * h2]));
+    const int j0 = (lane + 64 * h2) % L;
+    const int j1 = (nchunks > 1 ? L : 0) + j0;
+    dma4(gi + j0, lds_addr(&sGin[0][0][64 * h2]));
+    dma4(gf + j0, lds_addr(&sGin[0][1][64 * h2]));
+    dma4(gi + j1, lds_addr(&sGin[1][0][64 * h2]));
+    dma4(gf + j1, lds_addr(&sGin[1][1][64 * h2]));
   }
   wait_vm<0>();
-  float m_next = scan_gates(0, m_s);   // m after chunk 0
+  float m_next = 0.0f;                 // m after the current chunk (wave 0)
+  if (wave == 0) m_next = scan_gates(0, m_s);
+  __syncthreads();   // chunk 0's gate values are read by every wave below
+  // C~ = sig * cacc: the decay g_L of each chunk is folded into sig (a scalar)
+  // instead of rescaling every accumulator; see the state update below.
+  float sig = 1.0f;
 
   f32x4 outT[C::NT];
   f32x4 sacc[C::TPW];
@@ -358,7 +394,13 @@ __global__ __launch_bounds__(NTH, 1) void chunk_mfma_kernel(SeqArgs a) {
 
   for (int c = 0; c < nchunks; ++c) {
     const int par = c & 1;
-    float gL = 0.0f;
+    const float gL = sGate[par][2][L - 1];
+    // Lazy scaling: C~_new = g_L C~ + K^T(wV) = sig' (cacc + K^T((w / sig') V))
+    // with sig' = g_L sig.  When sig' gets tiny the chunk instead applies
+    // g_L sig to the accumulators (after their readout) and resets sig' = 1.
+    const bool renorm = gL * sig < 0x1p-64f;
+    const float sig_new = renorm ? 1.0f : gL * sig;
+    const float wscale = 1.0f / sig_new;
 
 #pragma unroll
     for (int s = 0; s < C::NS; ++s) {
@@ -386,10 +428,10 @@ __global__ __launch_bounds__(NTH, 1) void chunk_mfma_kernel(SeqArgs a) {
           const float4 w0 = *reinterpret_cast<const float4*>(&sGate[par][3][32 * ks + 8 * g]);
           const float4 w1 = *reinterpret_cast<const float4*>(&sGate[par][3][32 * ks + 8 * g + 4]);
           float xw[8];
-          xw[0] = bf_lo(lo.x) * w0.x; xw[1] = bf_hi(lo.x) * w0.y;
-          xw[2] = bf_lo(lo.y) * w0.z; xw[3] = bf_hi(lo.y) * w0.w;
-          xw[4] = bf_lo(hi.x) * w1.x; xw[5] = bf_hi(hi.x) * w1.y;
-          xw[6] = bf_lo(hi.y) * w1.z; xw[7] = bf_hi(hi.y) * w1.w;
+          xw[0] = bf_lo(lo.x) * (w0.x * wscale); xw[1] = bf_hi(lo.x) * (w0.y * wscale);
+          xw[2] = bf_lo(lo.y) * (w0.z * wscale); xw[3] = bf_hi(lo.y) * (w0.w * wscale);
+          xw[4] = bf_lo(hi.x) * (w1.x * wscale); xw[5] = bf_hi(hi.x) * (w1.y * wscale);
+          xw[6] = bf_lo(hi.y) * (w1.z * wscale); xw[7] = bf_hi(hi.y) * (w1.w * wscale);
           wVf[ks] = cvt8(xw);
         }
 #pragma unroll
@@ -399,7 +441,6 @@ __global__ __launch_bounds__(NTH, 1) void chunk_mfma_kernel(SeqArgs a) {
 #pragma unroll
         for (int k = 0; k < C::NQN; ++k) qnp[k] = 0.0f;
       }
-      gL = sGate[par][2][L - 1];
 
       // ---- readout, n~ . q and score tiles for the slice's two 32-row k-steps
 #pragma unroll
@@ -418,55 +459,62 @@ __global__ __launch_bounds__(NTH, 1) void chunk_mfma_kernel(SeqArgs a) {
           Qf[it] = lds_ld16(Qb, swz(it * 16 + l16, 32 * p + 8 * g));
           outT[it] = mfma16x16x32(A_C, as_bf16x8(Qf[it]), outT[it]);
         }
+        for_wave(wave, [&](auto Wc) {
+          constexpr int W = decltype(Wc)::value;
+          // n~ . q for the query tiles of this wave, and its causal score tiles
+          const float4 n0v = *reinterpret_cast<const float4*>(&sN[32 * P + 8 * g]);
+          const float4 n1v = *reinterpret_cast<const float4*>(&sN[32 * P + 8 * g + 4]);
 #pragma unroll
-        for (int it = 0; it < C::NT; ++it) {
-          if (it % NW == wave) {
-            const float4 n0v = *reinterpret_cast<const float4*>(&sN[32 * P + 8 * g]);
-            const float4 n1v = *reinterpret_cast<const float4*>(&sN[32 * P + 8 * g + 4]);
-            qnp[it / NW] += bf_lo(Qf[it].x) * n0v.x + bf_hi(Qf[it].x) * n0v.y +
-                            bf_lo(Qf[it].y) * n0v.z + bf_hi(Qf[it].y) * n0v.w +
-                            bf_lo(Qf[it].z) * n1v.x + bf_hi(Qf[it].z) * n1v.y +
-                            bf_lo(Qf[it].w) * n1v.z + bf_hi(Qf[it].w) * n1v.w;
-          }
-        }
+          for (int it = 0; it < C::NT; ++it) {
+            if (it % NW == W) {
+              qnp[it / NW] += bf_lo(Qf[it].x) * n0v.x + bf_hi(Qf[it].x) * n0v.y +
+                              bf_lo(Qf[it].y) * n0v.z + bf_hi(Qf[it].y) * n0v.w +
+                              bf_lo(Qf[it].z) * n1v.x + bf_hi(Qf[it].z) * n1v.y +
+                              bf_lo(Qf[it].w) * n1v.z + bf_hi(Qf[it].w) * n1v.w;
+            }
 #pragma unroll
-        for (int it = 0; it < C::NT; ++it) {
-#pragma unroll
-          for (int jt = 0; jt <= it; ++jt) {
-            const int n = it * (it + 1) / 2 + jt;
-            if (n % NW == wave) {
-              const uint4 Kf = lds_ld16(Kb, swz(jt * 16 + l16, 32 * p + 8 * g));
-              sacc[n / NW] = mfma16x16x32(as_bf16x8(Kf), as_bf16x8(Qf[it]), sacc[n / NW]);
+            for (int jt = 0; jt <= it; ++jt) {
+              const int n = it * (it + 1) / 2 + jt;
+              if (n % NW == W) {
+                const uint4 Kf = lds_ld16(Kb, swz(jt * 16 + l16, 32 * p + 8 * g));
+                sacc[n / NW] = mfma16x16x32(as_bf16x8(Kf), as_bf16x8(Qf[it]), sacc[n / NW]);
+              }
             }
           }
-        }
+        });
       }
 
       // ---- state update of the slice's rows (after their readout above).
       // A fragment of C~ tile t: lane (g, c) holds k_j[a] for tokens
       // 32ks+8g+0..7 and d_qk row a = 32(t/2) + 8(c/4) + 4(t%2) + c%4.
       float npart = 0.0f;
+      if (renorm) {
+        const float f = gL * sig;
 #pragma unroll
-      for (int tl = 0; tl < AS / 16; ++tl) cacc[s * (AS / 16) + tl] *= gL;
+        for (int tl = 0; tl < AS / 16; ++tl) cacc[s * (AS / 16) + tl] *= f;
+      }
       const int kr = l16 >> 2, kq = l16 & 3;
+      for_wave(wave, [&](auto Wc) {
+        constexpr int W = decltype(Wc)::value;
 #pragma unroll
-      for (int ks = 0; ks < C::NKS; ++ks) {
+        for (int ks = 0; ks < C::NKS; ++ks) {
 #pragma unroll
-        for (int tl = 0; tl < AS / 16; ++tl) {
-          const int col = 32 * (tl >> 1) + 8 * kq + 4 * (tl & 1);
-          const uint2 lo = lds_tr(Kb, swz(32 * ks + 8 * g + kr, col));
-          const uint2 hi = lds_tr(Kb, swz(32 * ks + 8 * g + 4 + kr, col));
-          const int t = s * (AS / 16) + tl;
-          cacc[t] = mfma16x16x32(join(lo, hi), wVf[ks], cacc[t]);
-          if (tl == wave) {
-            // n~ rows of this tile: sum_j w_j k_j[a] over this lane's 8 tokens
-            const float4 w0 = *reinterpret_cast<const float4*>(&sGate[par][3][32 * ks + 8 * g]);
-            const float4 w1 = *reinterpret_cast<const float4*>(&sGate[par][3][32 * ks + 8 * g + 4]);
-            npart += bf_lo(lo.x) * w0.x + bf_hi(lo.x) * w0.y + bf_lo(lo.y) * w0.z + bf_hi(lo.y) * w0.w +
-                     bf_lo(hi.x) * w1.x + bf_hi(hi.x) * w1.y + bf_lo(hi.y) * w1.z + bf_hi(hi.y) * w1.w;
+          for (int tl = 0; tl < AS / 16; ++tl) {
+            const int col = 32 * (tl >> 1) + 8 * kq + 4 * (tl & 1);
+            const uint2 lo = lds_tr(Kb, swz(32 * ks + 8 * g + kr, col));
+            const uint2 hi = lds_tr(Kb, swz(32 * ks + 8 * g + 4 + kr, col));
+            const int t = s * (AS / 16) + tl;
+            cacc[t] = mfma16x16x32(join(lo, hi), wVf[ks], cacc[t]);
+            if (tl == W) {
+              // n~ rows of tile W: sum_j w_j k_j[a] over this lane's 8 tokens
+              const float4 w0 = *reinterpret_cast<const float4*>(&sGate[par][3][32 * ks + 8 * g]);
+              const float4 w1 = *reinterpret_cast<const float4*>(&sGate[par][3][32 * ks + 8 * g + 4]);
+              npart += bf_lo(lo.x) * w0.x + bf_hi(lo.x) * w0.y + bf_lo(lo.y) * w0.z + bf_hi(lo.y) * w0.w +
+                       bf_lo(hi.x) * w1.x + bf_hi(hi.x) * w1.y + bf_lo(hi.y) * w1.z + bf_hi(hi.y) * w1.w;
+            }
           }
         }
-      }
+      });
       npart += __shfl_xor(npart, 16, 64);
       npart += __shfl_xor(npart, 32, 64);
       nn[s] = npart;
@@ -475,19 +523,21 @@ __global__ __launch_bounds__(NTH, 1) void chunk_mfma_kernel(SeqArgs a) {
     // ================= end of chunk: this chunk's o~ and the next chunk's
     // gates have landed (each wave waits for its own loads; the barrier below
     // publishes the o~ tile), then the epilogue
-    wait_vm<loads_after_chunk_extras<C::NS, C::D, C::NB_QK, C::NB_V>()>();
+    wait_vm<C::NB_G + loads_after_chunk_extras<C::NS, C::D, C::NB_QK, C::NB_V>()>();
     const float m_cur = m_next;
-    m_next = scan_gates(par ^ 1, m_cur);
+    if (wave == 0) m_next = scan_gates(par ^ 1, m_cur);
 
     float rsp[C::NT];
 #pragma unroll
     for (int it = 0; it < C::NT; ++it) rsp[it] = 0.0f;
+    for_wave(wave, [&](auto Wc) {
+     constexpr int W = decltype(Wc)::value;
 #pragma unroll
-    for (int it = 0; it < C::NT; ++it) {
+     for (int it = 0; it < C::NT; ++it) {
 #pragma unroll
       for (int jt = 0; jt <= it; ++jt) {
         const int n = it * (it + 1) / 2 + jt;
-        if (n % NW == wave) {
+        if (n % NW == W) {
           const int i = it * 16 + l16;
           const float Mi = sGate[par][1][i];
           const float4 uj = *reinterpret_cast<const float4*>(&sGate[par][0][jt * 16 + 4 * g]);
@@ -508,20 +558,21 @@ __global__ __launch_bounds__(NTH, 1) void chunk_mfma_kernel(SeqArgs a) {
             *reinterpret_cast<uint2*>(sP + i * C::PROW + (jt + 1) * 16 + 4 * g) = make_uint2(0u, 0u);
         }
       }
-    }
+     }
 #pragma unroll
-    for (int it = 0; it < C::NT; ++it) {
-      float r = rsp[it];
-      r += __shfl_xor(r, 16, 64);
-      r += __shfl_xor(r, 32, 64);
-      if (g == 0) sRs[wave][it * 16 + l16] = r;
-      if (it % NW == wave) {
-        float qv = qnp[it / NW];
-        qv += __shfl_xor(qv, 16, 64);
-        qv += __shfl_xor(qv, 32, 64);
-        if (g == 0) sQn[it * 16 + l16] = qv;
-      }
-    }
+     for (int it = 0; it < C::NT; ++it) {
+       float r = rsp[it];
+       r += __shfl_xor(r, 16, 64);
+       r += __shfl_xor(r, 32, 64);
+       if (g == 0) sRs[W][it * 16 + l16] = r;
+       if (it % NW == W) {
+         float qv = qnp[it / NW];
+         qv += __shfl_xor(qv, 16, 64);
+         qv += __shfl_xor(qv, 32, 64);
+         if (g == 0) sQn[it * 16 + l16] = qv;
+       }
+     }
+    });
     __syncthreads();
     // n~ for the next chunk: wave w owns the rows of tile w of every slice
     if (g == 0) {
@@ -536,7 +587,7 @@ __global__ __launch_bounds__(NTH, 1) void chunk_mfma_kernel(SeqArgs a) {
     for (int it = 0; it < C::NT; ++it) {
       const int i = it * 16 + l16;
       const float gi_ = sGate[par][2][i];
-      f32x4 o = outT[it] * gi_;
+      f32x4 o = outT[it] * (gi_ * sig);   // the readout saw C~_s / sig
 #pragma unroll
       for (int ks = 0; ks < C::NKS; ++ks) {
         if (32 * ks <= it * 16 + 15) {
@@ -567,6 +618,7 @@ __global__ __launch_bounds__(NTH, 1) void chunk_mfma_kernel(SeqArgs a) {
           make_uint2(cvt2(hv[0], hv[1]), cvt2(hv[2], hv[3]));
     }
     m_s = m_cur;
+    sig = sig_new;
   }
   // no LDS load may still be in flight when the workgroup ends
   wait_vm<0>();
@@ -579,7 +631,7 @@ __global__ __launch_bounds__(NTH, 1) void chunk_mfma_kernel(SeqArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int arow = 32 * (t >> 1) + 8 * g + 4 * (t & 1) + e;
-        a.C1[(head * DQK + arow) * dv + b0w + l16] = cacc[t][e];
+        a.C1[(head * DQK + arow) * dv + b0w + l16] = cacc[t][e] * sig;
       }
     }
     if (vt == 0) {
@@ -628,6 +680,7 @@ bool chunk_mfma_supported(const SeqArgs& a, int64_t chunk) {
 size_t chunk_mfma_workspace(const SeqArgs&, int64_t) { return 0; }
 
 hipError_t launch_chunk_mfma(const SeqArgs& a, int64_t chunk, void*, hipStream_t stream) {
+  if (chunk_mfma8_supported(a, chunk)) return launch_chunk_mfma8(a, stream);
   switch (a.o_mode) {
     case O_F32: return launch_D<O_F32>(a, chunk, stream);
     case O_BF16: return launch_D<O_BF16>(a, chunk, stream);

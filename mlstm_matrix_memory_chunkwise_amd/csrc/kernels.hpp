@@ -61,6 +61,10 @@ hipError_t launch_step(const StepArgs& a, hipStream_t stream);
 bool chunk_mfma_supported(const SeqArgs& a, int64_t chunk);
 size_t chunk_mfma_workspace(const SeqArgs& a, int64_t chunk);
 hipError_t launch_chunk_mfma(const SeqArgs& a, int64_t chunk, void* ws, hipStream_t stream);
+// Chunk-64 variant with 8 waves per workgroup (two per SIMD); launch_chunk_mfma
+// routes to it when it covers the shape.
+bool chunk_mfma8_supported(const SeqArgs& a, int64_t chunk);
+hipError_t launch_chunk_mfma8(const SeqArgs& a, hipStream_t stream);
 // Generic VALU chunkwise kernel (float32 path; bf16 shapes outside MFMA cover).
 hipError_t launch_chunk_valu(const SeqArgs& a, int64_t chunk, hipStream_t stream);
 

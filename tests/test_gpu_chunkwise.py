@@ -113,6 +113,9 @@ EDGE = [
     ("fp32 chunk 128 d 32/96", "f32", 1, 2, 256, 32, 96, 128, True, True, "sigmoid"),
     ("fp32 exp gate chunk 64", "f32", 2, 1, 128, 48, 16, 64, True, False, "exp"),
     ("d_qk 256 d_v 512 chunk 128", "bf16", 1, 2, 512, 256, 512, 128, False, True, "sigmoid"),
+    # input-gate spikes: the running maximum jumps by tens, so whole chunks of
+    # decay underflow to zero and the state's scale is reset
+    ("input-gate spikes", "bf16", 1, 2, 1024, 128, 64, 64, True, True, "sigmoid"),
 ]
 
 
@@ -121,7 +124,8 @@ def test_edge_cases(case):
     name, dtype, B, H, T, dqk, dv, chunk, rstate, with_o, fgate = case
     log(f"chunkwise edge: {name}")
     f_dist = (-0.05, 0.1) if fgate == "exp" else (3.0, 1.0)
-    cfg = workloads.Config("edge", 7, dtype, B, H, T, dqk, dv, (chunk,), (-1.0, 2.0), f_dist,
+    i_dist = (0.0, 15.0) if name == "input-gate spikes" else (-1.0, 2.0)
+    cfg = workloads.Config("edge", 7, dtype, B, H, T, dqk, dv, (chunk,), i_dist, f_dist,
                            (0.0, 1.0), rstate)
     inp = workloads.make_chunkwise_inputs(cfg, with_o=with_o)
     tol = TOL_F32 if dtype == "f32" else TOL_BF16
@@ -137,26 +141,46 @@ def test_bf16_output_gate():
 
 
 # ----------------------------------------------------------------- properties
-def test_split_at_chunk_boundary_is_bitwise():
-    """Two calls with the carried state equal one call, bit for bit, when the
-    split falls on a chunk boundary (same operations in the same order)."""
-    cfg = workloads.CONFIGS["c2"]
-    inp = workloads.make_chunkwise_inputs(cfg, B=1, H=8, T=512)
-    log("chunkwise split bitwise")
+def _split_run(inp, chunk, s):
     M = _M()
     d = to_dev(inp)
     h, (C1, n1, m1) = M.mlstm_fwd_chunkwise(d["q"], d["k"], d["v"], d["i_pre"], d["f_pre"],
-                                            d["o_pre"], d["C0"], d["n0"], d["m0"], chunk=64)
-    s = 192
+                                            d["o_pre"], d["C0"], d["n0"], d["m0"], chunk=chunk)
     part = lambda x: x[:, :, :s].contiguous()        # noqa: E731
     rest = lambda x: x[:, :, s:].contiguous()        # noqa: E731
-    ha, (Ca, na, ma) = M.mlstm_fwd_chunkwise(*(part(d[k]) for k in ("q", "k", "v", "i_pre", "f_pre", "o_pre")),
-                                             d["C0"], d["n0"], d["m0"], chunk=64)
-    hb, (Cb, nb, mb) = M.mlstm_fwd_chunkwise(*(rest(d[k]) for k in ("q", "k", "v", "i_pre", "f_pre", "o_pre")),
-                                             Ca, na, ma, chunk=64)
+    names = ("q", "k", "v", "i_pre", "f_pre", "o_pre")
+    ha, (Ca, na, ma) = M.mlstm_fwd_chunkwise(*(part(d[k]) for k in names),
+                                             d["C0"], d["n0"], d["m0"], chunk=chunk)
+    hb, (Cb, nb, mb) = M.mlstm_fwd_chunkwise(*(rest(d[k]) for k in names), Ca, na, ma, chunk=chunk)
     torch.cuda.synchronize()
-    assert torch.equal(torch.cat([ha, hb], dim=2), h)
-    assert torch.equal(Cb, C1) and torch.equal(nb, n1) and torch.equal(mb, m1)
+    return (h, C1, n1, m1), (torch.cat([ha, hb], dim=2), Cb, nb, mb)
+
+
+def test_split_at_chunk_boundary_is_bitwise_fp32():
+    """Float32 path: two calls with the carried state equal one call, bit for
+    bit, when the split falls on a chunk boundary (same operations in the
+    same order, the state kept in float32 either way)."""
+    cfg = workloads.Config("split32", 3, "f32", 1, 2, 256, 32, 48, (32,), (-1.0, 2.0), (3.0, 1.0),
+                           (0.0, 1.0), True)
+    inp = workloads.make_chunkwise_inputs(cfg)
+    log("chunkwise split bitwise (fp32)")
+    one, two = _split_run(inp, 32, 96)
+    for x, y in zip(one, two):
+        assert torch.equal(x, y)
+
+
+def test_split_at_chunk_boundary_bf16():
+    """bf16 MFMA path: two calls with the carried state agree with one call.
+    Not bit for bit: inside one call the state is carried as (scale, scaled
+    accumulator) and crossing the call boundary rounds it to C~ once."""
+    cfg = workloads.CONFIGS["c2"]
+    inp = workloads.make_chunkwise_inputs(cfg, B=1, H=8, T=512)
+    log("chunkwise split (bf16)")
+    (h, C1, n1, m1), (h2, C2, n2, m2) = _split_run(inp, 64, 192)
+    e_h = slice_rel_err(h2.cpu(), h.cpu())
+    eC, en, em = state_errors(C2.cpu(), n2.cpu(), m2.cpu(), C1.cpu(), n1.cpu(), m1.cpu())
+    log(f"  split vs one pass: h {e_h:.2e} C {eC:.2e} n {en:.2e} m {em:.2e}")
+    assert max(e_h, eC, en, em) < TOL_BF16
 
 
 def test_chunk_64_and_128_agree():
