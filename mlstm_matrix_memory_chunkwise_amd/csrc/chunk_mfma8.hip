@@ -62,30 +62,6 @@ struct C8 {
   static_assert(DQK % AS == 0 && NS <= 4, "d_qk must be 64, 128, 192 or 256");
 };
 
-// see chunk_mfma.hip: loads this wave issued after the stage with slice s
-template <int NS, int D, int NBQK, int NBV, int NBX>
-__host__ __device__ constexpr int loads_after_stage(int s) {
-  int n = 0;
-  for (int k = 1; k < D; ++k) n += NBQK + (((s + k) % NS) == 0 ? NBV : 0);
-  for (int k = 1; k <= D; ++k) n += (((s - k) % NS + NS) % NS == 0) ? NBX : 0;
-  return n;
-}
-template <int NS, int D, int NBQK, int NBV>
-__host__ __device__ constexpr int loads_after_chunk_extras() {
-  int n = 0;
-  for (int k = 1; k < NS; ++k) n += NBQK + (((k + D) % NS) == 0 ? NBV : 0);
-  return n;
-}
-template <int NS, int D, int NBQK, int NBV, int NBX>
-__device__ __forceinline__ void wait_stage(int s) {
-  switch (s) {
-    case 0: wait_vm<loads_after_stage<NS, D, NBQK, NBV, NBX>(0)>(); break;
-    case 1: wait_vm<loads_after_stage<NS, D, NBQK, NBV, NBX>(1 % NS)>(); break;
-    case 2: wait_vm<loads_after_stage<NS, D, NBQK, NBV, NBX>(2 % NS)>(); break;
-    default: wait_vm<loads_after_stage<NS, D, NBQK, NBV, NBX>(3 % NS)>(); break;
-  }
-}
-
 template <int DQK, int OM>
 __global__ __launch_bounds__(NTH, 1) void chunk_mfma8_kernel(SeqArgs a) {
   using C = C8<DQK, OM>;
@@ -95,10 +71,12 @@ __global__ __launch_bounds__(NTH, 1) void chunk_mfma8_kernel(SeqArgs a) {
   __shared__ __align__(16) bf16_t sP[L * PROW];
   __shared__ __align__(16) float sSx[NTILES][64][4];          // score partials
   __shared__ __align__(16) float sOx[4][NT][64][4];           // readout partials
-  __shared__ __align__(16) float sGate[2][5][L];
+  // per chunk parity: u, M, g, w, exp(-m), w / sig'
+  __shared__ __align__(16) float sGate[2][6][L];
   __shared__ float sRs[NW][L];
   __shared__ float sQn[2][L];
   __shared__ __align__(16) float sN[DQK];
+  __shared__ float sNp[DQK];   // n~ increments over the chunk's second k-step
   __shared__ __align__(256) float sGin[2][2][64];
 
   const int tid = threadIdx.x;
@@ -199,19 +177,26 @@ __global__ __launch_bounds__(NTH, 1) void chunk_mfma8_kernel(SeqArgs a) {
     dma4(gf + static_cast<int64_t>(cn) * L + lane, lds_addr(&sGin[c & 1][1][0]));
   };
 
-  // gate scan of one chunk (wave 0), DPP scans; returns m after the chunk
-  auto scan_gates = [&](int par, float ms) {
+  // Gate scan of one chunk (wave 0), DPP scans; returns m after the chunk.
+  // sg is the state scale before the chunk; the update weights are stored
+  // already divided by the scale after it (the same expression as the loop).
+  auto scan_gates = [&](int par, float ms, float sg) {
     const float lf = log_forget_fast(sGin[par][1][lane], a.fgate_exp);
     const float bcum = scan_add(lf);
     const float u = sGin[par][0][lane] - bcum;
     const float Mx = fmaxf(ms, scan_max(u));
     const float ML = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, Mx), L - 1));
     const float bL = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bcum), L - 1));
+    const float gv = __expf(ms - Mx);
+    const float wv = __expf(u - ML);
+    const float gLn = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gv), L - 1));
+    const float sg_new = gLn * sg < 0x1p-64f ? 1.0f : gLn * sg;
     sGate[par][0][lane] = u;
     sGate[par][1][lane] = Mx;
-    sGate[par][2][lane] = __expf(ms - Mx);
-    sGate[par][3][lane] = __expf(u - ML);
+    sGate[par][2][lane] = gv;
+    sGate[par][3][lane] = wv;
     sGate[par][4][lane] = __expf(-(bcum + Mx));
+    sGate[par][5][lane] = wv * (1.0f / sg_new);
     return bL + ML;
   };
 
@@ -224,7 +209,7 @@ __global__ __launch_bounds__(NTH, 1) void chunk_mfma8_kernel(SeqArgs a) {
   dma4(gf + (nchunks > 1 ? L : 0) + lane, lds_addr(&sGin[1][1][0]));
   wait_vm<0>();
   float m_next = 0.0f;
-  if (wave == 0) m_next = scan_gates(0, m_s);
+  if (wave == 0) m_next = scan_gates(0, m_s, 1.0f);
   __syncthreads();
   float sig = 1.0f;   // C~ = sig * cacc
 
@@ -240,7 +225,6 @@ __global__ __launch_bounds__(NTH, 1) void chunk_mfma8_kernel(SeqArgs a) {
     const float gL = sGate[par][2][L - 1];
     const bool renorm = gL * sig < 0x1p-64f;
     const float sig_new = renorm ? 1.0f : gL * sig;
-    const float wscale = 1.0f / sig_new;
 
 #pragma unroll
     for (int s = 0; s < C::NS; ++s) {
@@ -262,13 +246,13 @@ __global__ __launch_bounds__(NTH, 1) void chunk_mfma8_kernel(SeqArgs a) {
           const uint2 lo = lds_tr(Vb, swz(32 * ks + 8 * g + vr, col));
           const uint2 hi = lds_tr(Vb, swz(32 * ks + 8 * g + 4 + vr, col));
           Vf[ks] = join(lo, hi);
-          const float4 w0 = *reinterpret_cast<const float4*>(&sGate[par][3][32 * ks + 8 * g]);
-          const float4 w1 = *reinterpret_cast<const float4*>(&sGate[par][3][32 * ks + 8 * g + 4]);
+          const float4 w0 = *reinterpret_cast<const float4*>(&sGate[par][5][32 * ks + 8 * g]);
+          const float4 w1 = *reinterpret_cast<const float4*>(&sGate[par][5][32 * ks + 8 * g + 4]);
           float xw[8];
-          xw[0] = bf_lo(lo.x) * (w0.x * wscale); xw[1] = bf_hi(lo.x) * (w0.y * wscale);
-          xw[2] = bf_lo(lo.y) * (w0.z * wscale); xw[3] = bf_hi(lo.y) * (w0.w * wscale);
-          xw[4] = bf_lo(hi.x) * (w1.x * wscale); xw[5] = bf_hi(hi.x) * (w1.y * wscale);
-          xw[6] = bf_lo(hi.y) * (w1.z * wscale); xw[7] = bf_hi(hi.y) * (w1.w * wscale);
+          xw[0] = bf_lo(lo.x) * w0.x; xw[1] = bf_hi(lo.x) * w0.y;
+          xw[2] = bf_lo(lo.y) * w0.z; xw[3] = bf_hi(lo.y) * w0.w;
+          xw[4] = bf_lo(hi.x) * w1.x; xw[5] = bf_hi(hi.x) * w1.y;
+          xw[6] = bf_lo(hi.y) * w1.z; xw[7] = bf_hi(hi.y) * w1.w;
           wVf[ks] = cvt8(xw);
         }
 #pragma unroll
@@ -317,7 +301,9 @@ __global__ __launch_bounds__(NTH, 1) void chunk_mfma8_kernel(SeqArgs a) {
         }
       });
 
-      // ---- state update of this wave's 32 rows; n~ partial for tile (W&1)
+      // ---- state update of this wave's 32 rows.  n~ increment: the four
+      // waves of a half split its 2 row tiles x 2 token k-steps (tile W & 1,
+      // k-step (W & 3) / 2); the two k-step partials of a row meet in LDS.
       if (renorm) {
         const float f = gL * sig;
         cacc[s][0] *= f;
@@ -336,7 +322,7 @@ __global__ __launch_bounds__(NTH, 1) void chunk_mfma8_kernel(SeqArgs a) {
             const uint2 lo = lds_tr(Kb, swz(32 * ks + 8 * g + kr, col));
             const uint2 hi = lds_tr(Kb, swz(32 * ks + 8 * g + 4 + kr, col));
             cacc[s][e2] = mfma16x16x32(join(lo, hi), wVf[ks], cacc[s][e2]);
-            if ((W & 3) < 2 && e2 == (W & 1)) {
+            if (e2 == (W & 1) && ks == ((W & 3) >> 1)) {
               const float4 w0 = *reinterpret_cast<const float4*>(&sGate[par][3][32 * ks + 8 * g]);
               const float4 w1 = *reinterpret_cast<const float4*>(&sGate[par][3][32 * ks + 8 * g + 4]);
               npart += bf_lo(lo.x) * w0.x + bf_hi(lo.x) * w0.y + bf_lo(lo.y) * w0.z + bf_hi(lo.y) * w0.w +
@@ -351,10 +337,16 @@ __global__ __launch_bounds__(NTH, 1) void chunk_mfma8_kernel(SeqArgs a) {
     // ================= end of chunk
     wait_vm<C::NB_G + loads_after_chunk_extras<C::NS, C::D, C::NB_QK, C::NB_V>()>();
     const float m_cur = m_next;
-    if (wave == 0) m_next = scan_gates(par ^ 1, m_cur);
+    if (wave == 0) m_next = scan_gates(par ^ 1, m_cur, sig_new);
 
-    // partial sums out: q.n~, score tiles finished by the other half, readout
-    // tiles finished by the other half (query tile it is finished by half it/2)
+    // partial sums out: q.n~, n~ increments of the second k-step, score tiles
+    // finished by the other half, readout tiles finished by the other half
+    // (query tile it is finished by half it/2)
+    if (cg >= 2 && g == 0) {
+#pragma unroll
+      for (int s = 0; s < C::NS; ++s)
+        sNp[s * AS + 32 * hh + 8 * (l16 >> 2) + 4 * (cg & 1) + (l16 & 3)] = nn[s];
+    }
     {
       const float qv = sum_groups(qnp);
       if (g == 0) sQn[hh][cg * 16 + l16] = qv;
@@ -372,12 +364,13 @@ __global__ __launch_bounds__(NTH, 1) void chunk_mfma8_kernel(SeqArgs a) {
     });
     __syncthreads();
 
-    // n~ of the next chunk (waves with cg < 2 own tile 2 hh + cg of each slice)
+    // n~ of the next chunk (waves with cg < 2 finish the rows of tile 2 hh + cg
+    // of each slice: first k-step here, second from LDS)
     if (cg < 2 && g == 0) {
 #pragma unroll
       for (int s = 0; s < C::NS; ++s) {
         const int arow = s * AS + 32 * hh + 8 * (l16 >> 2) + 4 * cg + (l16 & 3);
-        sN[arow] = gL * sN[arow] + nn[s];
+        sN[arow] = gL * sN[arow] + (nn[s] + sNp[arow]);
       }
     }
     // finish this wave's score tiles: P = S (.) D, row sums

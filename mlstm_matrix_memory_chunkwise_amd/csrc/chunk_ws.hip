@@ -1,0 +1,627 @@
+// Fused chunkwise mLSTM forward, bf16 MFMA, chunk 64, d_qk 256: a state group
+// and an intra-chunk group of waves, software-pipelined by one chunk.
+//
+// Method: xLSTM post (llms.blog), section 3 "The Parallel Dual Form" inside
+// chunks of 64 tokens, the state of "Associative Matrix Cell State" carried
+// between chunks, the running maximum of section 2 "The Normalizer State and
+// Numerical Stabilization".  The chunk algebra is the one of chunk_mfma.hip:
+//   u_j = i~_j - b_j,  M_i = max(m_s, max_{j<=i} u_j),  m_i = b_i + M_i
+//   D_ij = exp(u_j - M_i),  g_i = exp(m_s - M_i),  w_j = exp(u_j - M_L)
+//   h_i = sigmoid(o~_i) (.) (g_i q_i^T C~_s + sum_j D_ij (q_i.k_j) v_j)
+//         / max(|g_i q_i.n~_s + sum_j D_ij (q_i.k_j)|, exp(-m_i))
+//   C~ <- g_L C~ + K^T diag(w) V,  n~ <- g_L n~ + K^T w.
+//
+// Of the chunk's work only the state update feeds the next chunk; the score
+// tiles, P, P V and the output do not.  The workgroup (8 waves, one (head, 64
+// value columns) pair) therefore splits by role, one wave of each role per
+// SIMD:
+// * state waves 0..3 (16 value columns each) keep C~ in registers and, per
+//   64-row d_qk slice ("stage"), run the readout C~^T Q^T and the update
+//   K^T (w V) on MFMA, plus q.n~ and the n~ increment; at the end of a chunk
+//   they leave the scaled readout g_i sig C~^T q_i and q.n~ in LDS;
+// * intra waves 4..7 run the causal score tiles S^T = K Q^T of the current
+//   chunk stage by stage and, during the stages of chunk c, finish chunk c-1:
+//   P = S (.) D at stage 0, then P V, the denominator, the output gate and
+//   the h store at stages 1 and 2.
+// The VALU-heavy finishing of one chunk thus overlaps the MFMA-heavy state
+// work of the next on every SIMD, and no wave waits for a chunk epilogue.
+//
+// Loads are as in chunk_mfma.hip: every loop load is a global->LDS DMA
+// issued from asm, shared by all 8 waves (each issues the same count), with
+// compile-time vmcnt waits; q/k come in 64-wide d_qk slices through a ring of
+// D+1 slots, v once per chunk, the o~ tile once per chunk into one of two
+// slots, the gates two chunks ahead.
+#include "common.hpp"
+#include "kernels.hpp"
+#include "mfma_util.hpp"
+
+namespace mlstm {
+namespace {
+
+using namespace mk;
+
+constexpr int NW = 8;
+constexpr int NTH = 512;
+constexpr int TV = 64;         // value columns per workgroup
+constexpr int AS = 64;         // d_qk slice (stage) width
+constexpr int L = 64;          // chunk
+constexpr int NT = L / 16;     // 16-token tiles
+constexpr int NKS = L / 32;    // 32-token k-steps
+constexpr int TILE = L * 128;  // one [64 x 64] bf16 tile
+constexpr int PROW = L + 8;
+constexpr int DQK = 256;
+constexpr int NS = DQK / AS;   // stages per chunk
+constexpr int NCT = DQK / 16;  // 16-row C~ tiles per state wave
+constexpr int D = 3;           // stages in flight
+constexpr int NSLOT = D + 1;
+// Only the intra waves (NWL of them) issue and await the global->LDS loads:
+// issuing can stall while the memory system is saturated, and the state
+// waves are the critical path.  The barrier after each wait publishes the
+// landed data to the state waves.
+constexpr int NWL = 4;
+constexpr int NB_QK = 2 * TILE / 1024 / NWL;   // 1 KB loads per loading wave per stage
+constexpr int NB_V = TILE / 1024 / NWL;
+constexpr int NB_G = 2;
+static_assert(NS == 4 && D <= NS - 1, "one value slot needs the look-ahead inside a chunk");
+
+template <int OM>
+struct CO {
+  static constexpr int OROW = (OM == O_BF16) ? 128 : 256;
+  static constexpr int OTILE = (OM == O_NONE) ? 16 : L * OROW;
+  static constexpr int NB_O = (OM == O_NONE) ? 0 : L * OROW / 1024 / NWL;
+  static constexpr int NB_X = NB_O + NB_G;
+};
+
+template <int OM>
+__global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
+  using C = CO<OM>;
+  __shared__ __align__(1024) char sRing[NSLOT][2][TILE];   // [slot][q|k]
+  __shared__ __align__(1024) char sV[TILE];
+  __shared__ __align__(1024) char sO[2][C::OTILE];         // o~ by chunk parity
+  __shared__ __align__(16) float sR[4][NT][64][4];         // scaled readout
+  __shared__ __align__(16) bf16_t sP[L * PROW];
+  // per chunk mod 3: u, M, g, w, exp(-m), w / sig'
+  __shared__ __align__(16) float sGate[3][6][L];
+  __shared__ float sQn[L];
+  __shared__ __align__(16) float sN[DQK];
+  // n~ and w as bf16 (high, remainder) pairs for the v_dot2 products
+  __shared__ __align__(16) uint16_t sNb[2][DQK];
+  __shared__ __align__(16) uint16_t sWb[3][2][L];
+  __shared__ __align__(256) float sGin[2][2][64];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l16 = lane & 15;
+  const int g = lane >> 4;
+  const bool state_wave = wave < 4;
+  const int cg = wave & 3;   // column group of either role
+
+  const int nvt = static_cast<int>(a.dv / TV);
+  const int64_t nhead = a.B * a.H;
+  int64_t head;
+  int vt;
+  {
+    const int64_t w = blockIdx.x;
+    if (nhead % 8 == 0) {
+      const int64_t grp = w / (8 * nvt), r = w % (8 * nvt);
+      vt = static_cast<int>(r / 8);
+      head = grp * 8 + r % 8;
+    } else {
+      head = w / nvt;
+      vt = static_cast<int>(w % nvt);
+    }
+  }
+  const int dv = static_cast<int>(a.dv);
+  const int64_t T = a.T;
+  const int nchunks = static_cast<int>(T / L);
+  const int b0w = vt * TV + cg * 16;
+
+  const bf16_t* gq = static_cast<const bf16_t*>(a.q) + head * T * DQK;
+  const bf16_t* gk = static_cast<const bf16_t*>(a.k) + head * T * DQK;
+  const bf16_t* gv = static_cast<const bf16_t*>(a.v) + head * T * dv + vt * TV;
+  const float* gi = a.i_pre + head * T;
+  const float* gf = a.f_pre + head * T;
+  bf16_t* gh = static_cast<bf16_t*>(a.h) + head * T * dv + b0w + 4 * g;
+
+  if (tid < DQK) {
+    const float n = a.C0 ? a.n0[head * DQK + tid] : 0.0f;
+    sN[tid] = n;
+    split_bf16(n, sNb[0][tid], sNb[1][tid]);
+  }
+  float m_s = a.C0 ? a.m0[head] : 0.0f;
+
+  // ---- loads (intra waves; lw = 0..3 is the loading wave's index)
+  const int lw = cg;
+  const int ld_r = lane >> 3, ld_pc = lane & 7;
+  int qk_off[NB_QK];
+#pragma unroll
+  for (int m = 0; m < NB_QK; ++m) {
+    const int Gr = (lw * NB_QK + m) % (L / 8);
+    const int row = 8 * Gr + ld_r;
+    qk_off[m] = row * DQK + 8 * (ld_pc ^ ((row >> 1) & 7));
+  }
+  int v_off[NB_V];
+#pragma unroll
+  for (int m = 0; m < NB_V; ++m) {
+    const int row = 8 * (lw * NB_V + m) + ld_r;
+    v_off[m] = row * dv + 8 * (ld_pc ^ ((row >> 1) & 7));
+  }
+  auto issue_stage = [&](int x) {
+    const int cx = x / NS, sx = x % NS;
+    const int cc = cx < nchunks ? cx : nchunks - 1;    // past the end: harmless re-read
+    char* slot = sRing[x % NSLOT][0];
+    const int64_t base = static_cast<int64_t>(cc) * L * DQK + sx * AS;
+#pragma unroll
+    for (int m = 0; m < NB_QK; ++m) {
+      const int G = lw * NB_QK + m;
+      const int mat = G / (L / 8);
+      dma16((mat ? gk : gq) + base + qk_off[m], lds_addr(slot + mat * TILE + (G % (L / 8)) * 1024));
+    }
+    if (sx == 0) {
+#pragma unroll
+      for (int m = 0; m < NB_V; ++m)
+        dma16(gv + static_cast<int64_t>(cc) * L * dv + v_off[m], lds_addr(sV + (lw * NB_V + m) * 1024));
+    }
+  };
+  auto issue_chunk_extras = [&](int c) {
+    if (OM != O_NONE) {
+      constexpr int RPI = 1024 / C::OROW;
+      constexpr int NCH = C::OROW / 16;
+#pragma unroll
+      for (int m = 0; m < C::NB_O; ++m) {
+        const int G = lw * C::NB_O + m;
+        const int row = RPI * G + lane / NCH;
+        const int pc = lane % NCH;
+        const int lc = (OM == O_F32) ? (pc ^ (row & 15)) : (pc ^ ((row >> 1) & 7));
+        const int64_t r = head * T + static_cast<int64_t>(c) * L + row;
+        const char* src = (OM == O_F32)
+            ? reinterpret_cast<const char*>(static_cast<const float*>(a.o_pre) + r * dv + vt * TV + 4 * lc)
+            : reinterpret_cast<const char*>(static_cast<const bf16_t*>(a.o_pre) + r * dv + vt * TV + 8 * lc);
+        dma16(src, lds_addr(sO[c & 1] + G * 1024));
+      }
+    }
+    const int cn = (c + 2 < nchunks) ? c + 2 : nchunks - 1;
+    dma4(gi + static_cast<int64_t>(cn) * L + lane, lds_addr(&sGin[c & 1][0][0]));
+    dma4(gf + static_cast<int64_t>(cn) * L + lane, lds_addr(&sGin[c & 1][1][0]));
+  };
+
+  // Gate scan of one chunk (wave 0) from raw gates gin into sGate[gb].  ms is
+  // m before the chunk, sg the state scale before it; returns m after it.
+  auto scan_gates = [&](int gin, int gb, float ms, float sg) {
+    const float lf = log_forget_fast(sGin[gin][1][lane], a.fgate_exp);
+    const float bcum = scan_add(lf);
+    const float u = sGin[gin][0][lane] - bcum;
+    const float Mx = fmaxf(ms, scan_max(u));
+    const float ML = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, Mx), L - 1));
+    const float bL = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bcum), L - 1));
+    const float gv_ = __expf(ms - Mx);
+    const float wv = __expf(u - ML);
+    const float gLn = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gv_), L - 1));
+    const float sg_new = gLn * sg < 0x1p-64f ? 1.0f : gLn * sg;
+    sGate[gb][0][lane] = u;
+    sGate[gb][1][lane] = Mx;
+    sGate[gb][2][lane] = gv_;
+    sGate[gb][3][lane] = wv;
+    split_bf16(wv, sWb[gb][0][lane], sWb[gb][1][lane]);
+    sGate[gb][4][lane] = __expf(-(bcum + Mx));
+    sGate[gb][5][lane] = wv * (1.0f / sg_new);
+    return bL + ML;
+  };
+
+  // ---- prologue
+  if (!state_wave) {
+#pragma unroll
+    for (int x = 0; x < D; ++x) issue_stage(x);
+    dma4(gi + lane, lds_addr(&sGin[0][0][0]));
+    dma4(gf + lane, lds_addr(&sGin[0][1][0]));
+    dma4(gi + (nchunks > 1 ? L : 0) + lane, lds_addr(&sGin[1][0][0]));
+    dma4(gf + (nchunks > 1 ? L : 0) + lane, lds_addr(&sGin[1][1][0]));
+    wait_vm<0>();
+  }
+  __syncthreads();
+  float m_n1 = 0.0f;   // m after the current chunk (wave 0)
+  if (wave == 0) m_n1 = scan_gates(0, 0, m_s, 1.0f);
+  __syncthreads();
+
+  const int vr = l16 >> 2, vq = l16 & 3;
+  const int kr = l16 >> 2, kq = l16 & 3;
+
+  // Everything below is written without branches on the wave index: the
+  // per-wave choices are uniform offsets, so that each stage is one basic
+  // block in which the compiler can overlap LDS latency with MFMA work.
+
+  // P tiles right of the even diagonal tiles, (0, 1) and (2, 3), lie inside
+  // the 32-token k-steps of P V and must read as zero; nothing else writes
+  // them, so they are cleared once.
+  for (int e = tid; e < 2 * 16 * 4; e += NTH) {
+    const int blk = e >> 6, r = (e >> 2) & 15, q = e & 3;   // tile, row, 4-column group
+    const int row = 32 * blk + r, col = 32 * blk + 16 + 4 * q;
+    *reinterpret_cast<uint2*>(sP + row * PROW + col) = make_uint2(0u, 0u);
+  }
+
+  // Intra wave W owns the causal score tiles n = it (it + 1) / 2 + jt with
+  // n = W mod 4: three for W < 2, two for W >= 2 (whose third slot repeats
+  // the second: identical P writes, and its row sum is never read).
+  int slot_it[3], slot_jt[3];
+  {
+    const int W = cg;
+    slot_it[0] = W == 0 ? 0 : W == 1 ? 1 : W == 2 ? 1 : 2;
+    slot_jt[0] = W == 0 ? 0 : W == 1 ? 0 : W == 2 ? 1 : 0;
+    slot_it[1] = W == 0 ? 2 : W == 1 ? 2 : 3;
+    slot_jt[1] = W == 0 ? 1 : W == 1 ? 2 : W == 2 ? 0 : 1;
+    slot_it[2] = W == 0 ? 3 : W == 1 ? 3 : slot_it[1];
+    slot_jt[2] = W == 0 ? 2 : W == 1 ? 3 : slot_jt[1];
+  }
+  // row sums of P by (wave, slot): query tile it collects the slots below
+  __shared__ float sRs[4][3][16];
+  auto row_sum = [&](int it, int i16) {
+    switch (it) {
+      case 0: return sRs[0][0][i16];
+      case 1: return sRs[1][0][i16] + sRs[2][0][i16];
+      case 2: return (sRs[0][1][i16] + sRs[1][1][i16]) + sRs[3][0][i16];
+      default: return (sRs[0][2][i16] + sRs[1][2][i16]) + (sRs[2][1][i16] + sRs[3][1][i16]);
+    }
+  };
+
+  // P = S (.) D for this wave's tiles of the chunk whose scores are in sp
+  // (gates in gb), and their row sums
+  auto finish_p = [&](const f32x4* sp, int gb) {
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const int it = slot_it[k], jt = slot_jt[k];
+      const int i = it * 16 + l16;
+      const float Mi = sGate[gb][1][i];
+      const float4 uj = *reinterpret_cast<const float4*>(&sGate[gb][0][jt * 16 + 4 * g]);
+      const float ujv[4] = {uj.x, uj.y, uj.z, uj.w};
+      float pe[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = jt * 16 + 4 * g + e;
+        const float pv = sp[k][e] * __expf(ujv[e] - Mi);
+        pe[e] = (j <= i) ? pv : 0.0f;
+      }
+      *reinterpret_cast<uint2*>(sP + i * PROW + jt * 16 + 4 * g) =
+          make_uint2(cvt2(pe[0], pe[1]), cvt2(pe[2], pe[3]));
+      sRs[cg][k][l16] = sum_groups((pe[0] + pe[1]) + (pe[2] + pe[3]));
+    }
+  };
+  // h of query tiles it0, it0 + 1 of chunk cp (gates gb, o~ slot ob)
+  auto finish_out = [&](const bf16x8* vfr, int it0, int cp, int gb, int ob) {
+#pragma unroll
+    for (int it = it0; it < it0 + 2; ++it) {
+      const int i = it * 16 + l16;
+      f32x4 o = *reinterpret_cast<const f32x4*>(&sR[cg][it][lane][0]);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        if (32 * ks <= it * 16 + 15) {
+          const uint4 Pf = *reinterpret_cast<const uint4*>(sP + i * PROW + 32 * ks + 8 * g);
+          o = mfma16x16x32(vfr[ks], as_bf16x8(Pf), o);
+        }
+      }
+      const float rs = row_sum(it, l16);
+      const float den = fmaxf(fabsf(sGate[gb][2][i] * sQn[i] + rs), sGate[gb][4][i]);
+      const float inv = __builtin_amdgcn_rcpf(den);
+      float hv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) hv[e] = o[e] * inv;
+      if (OM != O_NONE) {
+        float ov[4];
+        if (OM == O_F32) {
+          const float4 o4 = *reinterpret_cast<const float4*>(sO[ob] + i * 256 + 16 * ((cg * 4 + g) ^ (i & 15)));
+          ov[0] = o4.x; ov[1] = o4.y; ov[2] = o4.z; ov[3] = o4.w;
+        } else {
+          const uint2 o2 = *reinterpret_cast<const uint2*>(sO[ob] + swz(i, cg * 16 + 4 * g));
+          ov[0] = bf_lo(o2.x); ov[1] = bf_hi(o2.x); ov[2] = bf_lo(o2.y); ov[3] = bf_hi(o2.y);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hv[e] *= sigmoid_fast(ov[e]);
+      }
+      *reinterpret_cast<uint2*>(gh + (static_cast<int64_t>(cp) * L + i) * dv) =
+          make_uint2(cvt2(hv[0], hv[1]), cvt2(hv[2], hv[3]));
+    }
+  };
+  // value fragments (V^T, this wave's 16 columns) of the chunk in sV
+  auto load_vf = [&](bf16x8* dst, uint2* raw) {
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int col = cg * 16 + 4 * vq;
+      raw[2 * ks] = lds_tr(sV, swz(32 * ks + 8 * g + vr, col));
+      raw[2 * ks + 1] = lds_tr(sV, swz(32 * ks + 8 * g + 4 + vr, col));
+      dst[ks] = join(raw[2 * ks], raw[2 * ks + 1]);
+    }
+  };
+
+  // Both roles run the same stage sequence (same barriers, same loads and
+  // waits); each role has its own loop so that its registers are its own.
+  // the intra waves wait for the stage's loads before the barrier and issue
+  // the loads D stages ahead after it
+  auto stage_top_intra = [&](int c, int s) {
+    const int x = c * NS + s;
+    if (x < D) wait_vm<0>();
+    else wait_stage<NS, D, NB_QK, NB_V, C::NB_X>(s);
+    __syncthreads();
+    issue_stage(x + D);
+    if (s == 0) issue_chunk_extras(c);
+    return x % NSLOT;
+  };
+  auto stage_top_state = [&](int c, int s) {
+    __syncthreads();
+    return (c * NS + s) % NSLOT;
+  };
+
+  if (state_wave) {
+    const int W = cg;
+    // C~ of this wave's 16 columns: tile t holds rows 32 (t/2) + 8 g + 4 (t%2) + e
+    f32x4 cacc[NCT];
+#pragma unroll
+    for (int t = 0; t < NCT; ++t) cacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (a.C0) {
+#pragma unroll
+      for (int t = 0; t < NCT; ++t) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int arow = 32 * (t >> 1) + 8 * g + 4 * (t & 1) + e;
+          cacc[t][e] = a.C0[(head * DQK + arow) * dv + b0w + l16];
+        }
+      }
+    }
+    // n~ rows of this wave's tile of a slice (four lanes store the same value)
+    const int nrow = 32 * (W >> 1) + 8 * (l16 >> 2) + 4 * (W & 1) + (l16 & 3);
+    const int ncol = 32 * (W >> 1) + 8 * kq + 4 * (W & 1);   // its K^T fragment column
+    float sig = 1.0f;    // C~ = sig * cacc
+    float gL_prev = 1.0f;   // with nn = 0: the update before chunk 0 keeps n~
+    f32x4 outT[NT];
+    bf16x8 wVf[NKS];
+    float nn[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) nn[s] = 0.0f;
+    float qnp = 0.0f;
+    int gb = 0, gbn = 1;   // gate buffers of chunks c, c + 1
+    for (int c = 0; c < nchunks; ++c) {
+      const float gL = sGate[gb][2][L - 1];
+      const bool renorm = gL * sig < 0x1p-64f;
+      const float sig_new = renorm ? 1.0f : gL * sig;
+      const float fscale = renorm ? gL * sig : 1.0f;   // exact 1 unless renormalising
+      float m_n2 = 0.0f;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int slot = stage_top_state(c, s);
+        const char* Qb = sRing[slot][0];
+        const char* Kb = sRing[slot][1];
+        if (s == 0) {
+          uint2 raw[2 * NKS];
+          bf16x8 vtmp[NKS];
+          load_vf(vtmp, raw);
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) {
+            const float4 w0 = *reinterpret_cast<const float4*>(&sGate[gb][5][32 * ks + 8 * g]);
+            const float4 w1 = *reinterpret_cast<const float4*>(&sGate[gb][5][32 * ks + 8 * g + 4]);
+            const uint2 lo = raw[2 * ks], hi = raw[2 * ks + 1];
+            float xw[8];
+            xw[0] = bf_lo(lo.x) * w0.x; xw[1] = bf_hi(lo.x) * w0.y;
+            xw[2] = bf_lo(lo.y) * w0.z; xw[3] = bf_hi(lo.y) * w0.w;
+            xw[4] = bf_lo(hi.x) * w1.x; xw[5] = bf_hi(hi.x) * w1.y;
+            xw[6] = bf_lo(hi.y) * w1.z; xw[7] = bf_hi(hi.y) * w1.w;
+            wVf[ks] = cvt8(xw);
+          }
+#pragma unroll
+          for (int it = 0; it < NT; ++it) outT[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+          qnp = 0.0f;
+        }
+        // ---- the stage's LDS reads are issued ahead of the arithmetic that
+        // consumes them (reads return in order, so each MFMA waits only for
+        // its own operands): Q and K fragments, then the readout MFMAs, then
+        // the small operands of q.n~ and the n~ increment (reusing the Q
+        // registers), then the update MFMAs and the dot products
+        uint4 Qf[2][NT];
+        uint2 Klo[NKS][AS / 16], Khi[NKS][AS / 16];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+#pragma unroll
+          for (int it = 0; it < NT; ++it) Qf[p][it] = lds_ld16(Qb, swz(it * 16 + l16, 32 * p + 8 * g));
+        }
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+          for (int tl = 0; tl < AS / 16; ++tl) {
+            const int col = 32 * (tl >> 1) + 8 * kq + 4 * (tl & 1);
+            Klo[ks][tl] = lds_tr(Kb, swz(32 * ks + 8 * g + kr, col));
+            Khi[ks][tl] = lds_tr(Kb, swz(32 * ks + 8 * g + 4 + kr, col));
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // readout: query tiles x the slice's two 32-row k-steps
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const int P = 2 * s + p;
+          float ca[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            ca[e] = cacc[2 * P][e];
+            ca[4 + e] = cacc[2 * P + 1][e];
+          }
+          const bf16x8 A_C = cvt8(ca);
+#pragma unroll
+          for (int it = 0; it < NT; ++it) outT[it] = mfma16x16x32(A_C, as_bf16x8(Qf[p][it]), outT[it]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        uint4 Qn[2], nh[2], nl[2];
+        uint2 Nlo[NKS], Nhi[NKS];
+        uint4 wh[NKS], wl[NKS];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const int P = 2 * s + p;
+          Qn[p] = lds_ld16(Qb, W * 2048 + swz(l16, 32 * p + 8 * g));
+          nh[p] = *reinterpret_cast<const uint4*>(&sNb[0][32 * P + 8 * g]);
+          nl[p] = *reinterpret_cast<const uint4*>(&sNb[1][32 * P + 8 * g]);
+        }
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          Nlo[ks] = lds_tr(Kb, swz(32 * ks + 8 * g + kr, ncol));
+          Nhi[ks] = lds_tr(Kb, swz(32 * ks + 8 * g + 4 + kr, ncol));
+          wh[ks] = *reinterpret_cast<const uint4*>(&sWb[gb][0][32 * ks + 8 * g]);
+          wl[ks] = *reinterpret_cast<const uint4*>(&sWb[gb][1][32 * ks + 8 * g]);
+        }
+        // n~ rows of the previous slice: every state wave has finished
+        // reading them (q.n~) before this stage's barrier
+        const int sp_ = (s + NS - 1) % NS;
+        const int nprow = sp_ * AS + nrow;
+        const float nprev = sN[nprow];
+        __builtin_amdgcn_sched_barrier(0);
+        // state update of the slice's rows (after their readout)
+#pragma unroll
+        for (int tl = 0; tl < AS / 16; ++tl) cacc[s * (AS / 16) + tl] *= fscale;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+          for (int tl = 0; tl < AS / 16; ++tl) {
+            const int t = s * (AS / 16) + tl;
+            cacc[t] = mfma16x16x32(join(Klo[ks][tl], Khi[ks][tl]), wVf[ks], cacc[t]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // q.n~ for query tile W, the n~ update of the previous slice and the
+        // n~ increment of this wave's tile of the slice
+#pragma unroll
+        for (int p = 0; p < 2; ++p) qnp = dot8_split(Qn[p], nh[p], nl[p], qnp);
+        {
+          const float nnew = (s > 0 ? gL : gL_prev) * nprev + nn[sp_];
+          sN[nprow] = nnew;
+          split_bf16(nnew, sNb[0][nprow], sNb[1][nprow]);
+        }
+        float npart = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const uint4 kk = make_uint4(Nlo[ks].x, Nlo[ks].y, Nhi[ks].x, Nhi[ks].y);
+          npart = dot8_split(kk, wh[ks], wl[ks], npart);
+        }
+        nn[s] = sum_groups(npart);
+        if (s == NS - 1) {
+          // scaled readout and q.n~ for the intra waves
+#pragma unroll
+          for (int it = 0; it < NT; ++it) {
+            const float gi_ = sGate[gb][2][it * 16 + l16];
+            *reinterpret_cast<f32x4*>(&sR[W][it][lane][0]) = outT[it] * (gi_ * sig);
+          }
+          sQn[W * 16 + l16] = sum_groups(qnp);
+        }
+        // gates of the next chunk (staged two chunks ahead)
+        if (s == 1 && wave == 0) m_n2 = scan_gates((c + 1) & 1, gbn, m_n1, sig_new);
+      }
+      m_s = m_n1;
+      m_n1 = m_n2;
+      sig = sig_new;
+      gL_prev = gL;
+      gb = gbn;
+      gbn = (gbn == 2) ? 0 : gbn + 1;
+    }
+    // ---- drain
+    {
+      const int arow = (NS - 1) * AS + nrow;
+      const float nnew = gL_prev * sN[arow] + nn[NS - 1];
+      sN[arow] = nnew;
+      split_bf16(nnew, sNb[0][arow], sNb[1][arow]);
+    }
+    __syncthreads();
+    __syncthreads();
+    if (a.C1) {
+#pragma unroll
+      for (int t = 0; t < NCT; ++t) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int arow = 32 * (t >> 1) + 8 * g + 4 * (t & 1) + e;
+          a.C1[(head * DQK + arow) * dv + b0w + l16] = cacc[t][e] * sig;
+        }
+      }
+      if (vt == 0) {
+        if (tid < DQK) a.n1[head * DQK + tid] = sN[tid];
+        if (tid == 0) a.m1[head] = m_s;
+      }
+    }
+  } else {
+    // this wave's score-tile slots as uniform LDS offsets of the Q and K rows
+    int qoff[3], koff[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      qoff[k] = slot_it[k] * 2048;
+      koff[k] = slot_jt[k] * 2048;
+    }
+    // score tiles of the current and the previous chunk, value fragments
+    // of both
+    f32x4 sacc[3], sprev[3];
+    bf16x8 Vf[NKS], Vp[NKS];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) sacc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    int gb = 0, gbp = 2;   // gate buffers of chunks c, c - 1
+    for (int c = 0; c < nchunks; ++c) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int slot = stage_top_intra(c, s);
+        const char* Qb = sRing[slot][0];
+        const char* Kb = sRing[slot][1];
+        if (s == 0) {
+#pragma unroll
+          for (int k = 0; k < 3; ++k) {
+            sprev[k] = sacc[k];
+            sacc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) Vp[ks] = Vf[ks];
+          uint2 raw[2 * NKS];
+          load_vf(Vf, raw);
+        }
+        // score tiles over the slice (operands first, see the state role)
+        uint4 Qf[2][3], Kf[2][3];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+#pragma unroll
+          for (int k = 0; k < 3; ++k) {
+            Qf[p][k] = lds_ld16(Qb, qoff[k] + swz(l16, 32 * p + 8 * g));
+            Kf[p][k] = lds_ld16(Kb, koff[k] + swz(l16, 32 * p + 8 * g));
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+#pragma unroll
+          for (int k = 0; k < 3; ++k)
+            sacc[k] = mfma16x16x32(as_bf16x8(Kf[p][k]), as_bf16x8(Qf[p][k]), sacc[k]);
+        }
+        // finishing of the previous chunk (in chunk 0 the P pass works on
+        // zeros and its results are never read)
+        if (s == 0) finish_p(sprev, gbp);
+        if (s == 1 || s == 2) {
+          if (c > 0) finish_out(Vp, 2 * (s - 1), c - 1, gbp, (c - 1) & 1);
+        }
+      }
+      gbp = gb;
+      gb = (gb == 2) ? 0 : gb + 1;
+    }
+    // ---- drain: finish the last chunk
+    wait_vm<0>();
+    __syncthreads();
+    finish_p(sacc, gbp);
+    __syncthreads();
+    finish_out(Vf, 0, nchunks - 1, gbp, (nchunks - 1) & 1);
+    finish_out(Vf, 2, nchunks - 1, gbp, (nchunks - 1) & 1);
+  }
+}
+
+}  // namespace
+
+bool chunk_ws_supported(const SeqArgs& a, int64_t chunk) {
+  return a.qkv_bf16 && a.dqk == DQK && a.dv % TV == 0 && chunk == L && a.T % L == 0;
+}
+
+hipError_t launch_chunk_ws(const SeqArgs& a, hipStream_t stream) {
+  const unsigned nwg = static_cast<unsigned>(a.B * a.H * (a.dv / TV));
+  switch (a.o_mode) {
+    case O_F32: chunk_ws_kernel<O_F32><<<dim3(nwg), dim3(NTH), 0, stream>>>(a); break;
+    case O_BF16: chunk_ws_kernel<O_BF16><<<dim3(nwg), dim3(NTH), 0, stream>>>(a); break;
+    default: chunk_ws_kernel<O_NONE><<<dim3(nwg), dim3(NTH), 0, stream>>>(a); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mlstm

@@ -65,6 +65,10 @@ hipError_t launch_chunk_mfma(const SeqArgs& a, int64_t chunk, void* ws, hipStrea
 // routes to it when it covers the shape.
 bool chunk_mfma8_supported(const SeqArgs& a, int64_t chunk);
 hipError_t launch_chunk_mfma8(const SeqArgs& a, hipStream_t stream);
+// Chunk-64, d_qk-256 variant with state and intra-chunk wave groups pipelined
+// by one chunk; launch_chunk_mfma routes to it first.
+bool chunk_ws_supported(const SeqArgs& a, int64_t chunk);
+hipError_t launch_chunk_ws(const SeqArgs& a, hipStream_t stream);
 // Generic VALU chunkwise kernel (float32 path; bf16 shapes outside MFMA cover).
 hipError_t launch_chunk_valu(const SeqArgs& a, int64_t chunk, hipStream_t stream);
 

@@ -71,6 +71,39 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// ---- explicit wait counts for the stage ring.  Issue order of one wave: at
+// the top of stage y (after its barrier) the loads of stage y + D (NBQK, plus
+// NBV when y + D opens a chunk), then, when y opens chunk c, the per-chunk
+// loads (NBX).  Loads of stage x were issued at the top of stage x - D; the
+// loads issued after them when the wave waits for stage x (slice s) are
+// counted here.  Vector-memory stores are not counted, which can only make a
+// wait stricter.
+template <int NS, int D, int NBQK, int NBV, int NBX>
+__host__ __device__ constexpr int loads_after_stage(int s) {
+  int n = 0;
+  for (int k = 1; k < D; ++k) n += NBQK + (((s + k) % NS) == 0 ? NBV : 0);
+  for (int k = 1; k <= D; ++k) n += (((s - k) % NS + NS) % NS == 0) ? NBX : 0;
+  return n;
+}
+// ... and after the per-chunk loads of chunk c, at the end of chunk c.
+template <int NS, int D, int NBQK, int NBV>
+__host__ __device__ constexpr int loads_after_chunk_extras() {
+  int n = 0;
+  for (int k = 1; k < NS; ++k) n += NBQK + (((k + D) % NS) == 0 ? NBV : 0);
+  return n;
+}
+// Wait for the stage with slice index s (folds to one s_waitcnt once the
+// slice loop is unrolled).
+template <int NS, int D, int NBQK, int NBV, int NBX>
+__device__ __forceinline__ void wait_stage(int s) {
+  switch (s) {
+    case 0: wait_vm<loads_after_stage<NS, D, NBQK, NBV, NBX>(0)>(); break;
+    case 1: wait_vm<loads_after_stage<NS, D, NBQK, NBV, NBX>(1 % NS)>(); break;
+    case 2: wait_vm<loads_after_stage<NS, D, NBQK, NBV, NBX>(2 % NS)>(); break;
+    default: wait_vm<loads_after_stage<NS, D, NBQK, NBV, NBX>(3 % NS)>(); break;
+  }
+}
+
 template <int W>
 using wave_c = std::integral_constant<int, W>;
 
@@ -138,6 +171,26 @@ __device__ __forceinline__ float sum_groups(float x) {
   const auto r32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
   const uint32_t b0 = r32[0], b1 = r32[1];
   return __uint_as_float(b0) + __uint_as_float(b1);
+}
+
+// ---- bf16 pair dot products (v_dot2_f32_bf16: products exact, fp32 sums)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+// sum over 8 bf16 pairs of a . (bh + bl), where bh + bl is a float split into
+// a bf16 high part and a bf16 remainder (about 16 significant bits)
+__device__ __forceinline__ float dot8_split(uint4 a, uint4 bh, uint4 bl, float c) {
+  c = dot2(a.x, bh.x, c); c = dot2(a.y, bh.y, c); c = dot2(a.z, bh.z, c); c = dot2(a.w, bh.w, c);
+  c = dot2(a.x, bl.x, c); c = dot2(a.y, bl.y, c); c = dot2(a.z, bl.z, c); c = dot2(a.w, bl.w, c);
+  return c;
+}
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi), as bf16 bit patterns
+__device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
+  const __bf16 h = static_cast<__bf16>(x);
+  const __bf16 l = static_cast<__bf16>(x - static_cast<float>(h));
+  hi = __builtin_bit_cast(uint16_t, h);
+  lo = __builtin_bit_cast(uint16_t, l);
 }
 
 // log(sigmoid(x)) = min(x, 0) - log(1 + exp(-|x|)), with the hardware exp/log
