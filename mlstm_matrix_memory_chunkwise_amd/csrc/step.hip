@@ -75,13 +75,25 @@ __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, float4 v) {
 constexpr int kThreads = 256;
 constexpr int kUnroll = 8;
 
-// CT column threads (4 floats each) x (256 / CT) row groups.
+// C~ is touched exactly once per step: stream it past the caches.
+__device__ __forceinline__ float4 ld_stream(const float* p) {
+  const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  return make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void st_stream(float* p, float4 v) {
+  const f32x4 x = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(p));
+}
+
+// CT column threads (4 floats each) x (256 / CT) row groups.  Dynamic LDS:
+// w k and q as float32 for all d_qk rows (2 d_qk floats).
 template <typename TQ, int OM, int CT>
 __global__ __launch_bounds__(kThreads) void step_stream_kernel(StepArgs a) {
   constexpr int R = kThreads / CT;   // row groups
   constexpr int CB = 4 * CT;         // columns per workgroup
   __shared__ float s_red[R][CB];
   __shared__ float s_qn[kThreads / 64];
+  extern __shared__ float s_dyn[];   // [0, dqk): w k_r, [dqk, 2 dqk): q_r
 
   const int tid = threadIdx.x;
   const int ct = tid % CT;
@@ -91,66 +103,76 @@ __global__ __launch_bounds__(kThreads) void step_stream_kernel(StepArgs a) {
   const int dv = static_cast<int>(a.dv);
   const int col = blockIdx.y * CB + 4 * ct;
   const bool col_ok = col < dv;
+  float* s_kw = s_dyn;
+  float* s_q = s_dyn + dqk;
 
   const TQ* q = static_cast<const TQ*>(a.q) + bh * dqk;
   const TQ* k = static_cast<const TQ*>(a.k) + bh * dqk;
   const TQ* v = static_cast<const TQ*>(a.v) + bh * dv;
   const float* n_in = a.n_in + bh * dqk;
+  const float* Cin = a.C_in + bh * static_cast<int64_t>(dqk) * dv + col;
+  float* Cout = a.C_out + bh * static_cast<int64_t>(dqk) * dv + col;
   const StepScalars sc = step_scalars(a.i_pre[bh], a.f_pre[bh], a.m_in[bh], a.fgate_exp);
 
-  // n~' . q over all rows (every workgroup of the head needs it; cheap).
+  // the first batch of C~ rows is in flight while the row vectors are staged
+  float4 c[kUnroll];
+  const bool full_first = col_ok && (kUnroll - 1) * R + rg < dqk;
+  if (full_first) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) c[u] = ld_stream(Cin + static_cast<int64_t>(rg + u * R) * dv);
+  }
+
+  // w k and q into LDS; n~' . q over all rows (every workgroup of the head
+  // needs it)
   float qn = 0.0f;
   for (int r = tid; r < dqk; r += kThreads) {
-    float nn = sc.g * n_in[r] + sc.w * to_f32(k[r]);
-    qn += nn * to_f32(q[r]);
+    const float kw = sc.w * to_f32(k[r]);
+    const float qr = to_f32(q[r]);
+    s_kw[r] = kw;
+    s_q[r] = qr;
+    qn += (sc.g * n_in[r] + kw) * qr;
   }
   qn = wave_sum(qn);
   if ((tid & 63) == 0) s_qn[tid >> 6] = qn;
+  __syncthreads();
 
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   if (col_ok) {
     const float4 v4 = load4<TQ>(v + col);
-    const float* Cin = a.C_in + bh * static_cast<int64_t>(dqk) * dv + col;
-    float* Cout = a.C_out + bh * static_cast<int64_t>(dqk) * dv + col;
-    int r0 = rg;
-    // main body: kUnroll independent 16-byte loads in flight per thread
-    for (; r0 + (kUnroll - 1) * R < dqk; r0 += kUnroll * R) {
-      float4 c[kUnroll];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u)
-        c[u] = *reinterpret_cast<const float4*>(Cin + static_cast<int64_t>(r0 + u * R) * dv);
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int r = r0 + u * R;
-        const float kw = sc.w * to_f32(k[r]);
-        const float qr = to_f32(q[r]);
-        float4 cn;
-        cn.x = sc.g * c[u].x + kw * v4.x;
-        cn.y = sc.g * c[u].y + kw * v4.y;
-        cn.z = sc.g * c[u].z + kw * v4.z;
-        cn.w = sc.g * c[u].w + kw * v4.w;
-        *reinterpret_cast<float4*>(Cout + static_cast<int64_t>(r) * dv) = cn;
-        acc.x += qr * cn.x;
-        acc.y += qr * cn.y;
-        acc.z += qr * cn.z;
-        acc.w += qr * cn.w;
-      }
-    }
-    for (; r0 < dqk; r0 += R) {
-      const float4 c = *reinterpret_cast<const float4*>(Cin + static_cast<int64_t>(r0) * dv);
-      const float kw = sc.w * to_f32(k[r0]);
-      const float qr = to_f32(q[r0]);
+    auto update = [&](int r, float4 cv) {
+      const float kw = s_kw[r];
+      const float qr = s_q[r];
       float4 cn;
-      cn.x = sc.g * c.x + kw * v4.x;
-      cn.y = sc.g * c.y + kw * v4.y;
-      cn.z = sc.g * c.z + kw * v4.z;
-      cn.w = sc.g * c.w + kw * v4.w;
-      *reinterpret_cast<float4*>(Cout + static_cast<int64_t>(r0) * dv) = cn;
+      cn.x = sc.g * cv.x + kw * v4.x;
+      cn.y = sc.g * cv.y + kw * v4.y;
+      cn.z = sc.g * cv.z + kw * v4.z;
+      cn.w = sc.g * cv.w + kw * v4.w;
+      st_stream(Cout + static_cast<int64_t>(r) * dv, cn);
       acc.x += qr * cn.x;
       acc.y += qr * cn.y;
       acc.z += qr * cn.z;
       acc.w += qr * cn.w;
+    };
+    int r0 = rg;
+    if (full_first) {
+      // steady state: kUnroll independent 16-byte loads in flight per thread
+      for (;;) {
+        const int rn = r0 + kUnroll * R;
+        const bool more = rn + (kUnroll - 1) * R < dqk;
+        float4 cnext[kUnroll];
+        if (more) {
+#pragma unroll
+          for (int u = 0; u < kUnroll; ++u) cnext[u] = ld_stream(Cin + static_cast<int64_t>(rn + u * R) * dv);
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) update(r0 + u * R, c[u]);
+        r0 = rn;
+        if (!more) break;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) c[u] = cnext[u];
+      }
     }
+    for (; r0 < dqk; r0 += R) update(r0, ld_stream(Cin + static_cast<int64_t>(r0) * dv));
   }
   s_red[rg][4 * ct + 0] = acc.x;
   s_red[rg][4 * ct + 1] = acc.y;
@@ -160,8 +182,8 @@ __global__ __launch_bounds__(kThreads) void step_stream_kernel(StepArgs a) {
 
   // Column sums over the R row groups; thread t < CB finishes column t.
   if (tid < CB) {
-    const int c = blockIdx.y * CB + tid;
-    if (c < dv) {
+    const int cc = blockIdx.y * CB + tid;
+    if (cc < dv) {
       float num = 0.0f;
 #pragma unroll 8
       for (int r = 0; r < R; ++r) num += s_red[r][tid];
@@ -170,9 +192,9 @@ __global__ __launch_bounds__(kThreads) void step_stream_kernel(StepArgs a) {
       for (int w = 0; w < kThreads / 64; ++w) qn_all += s_qn[w];
       const float den = fmaxf(fabsf(qn_all), __expf(-sc.m_new));
       float gate = 1.0f;
-      if (OM == O_F32) gate = sigmoidf_(static_cast<const float*>(a.o_pre)[bh * dv + c]);
-      if (OM == O_BF16) gate = sigmoidf_(bf2f(static_cast<const bf16_t*>(a.o_pre)[bh * dv + c]));
-      static_cast<TQ*>(a.h)[bh * dv + c] = from_f32<TQ>(gate * num / den);
+      if (OM == O_F32) gate = sigmoidf_(static_cast<const float*>(a.o_pre)[bh * dv + cc]);
+      if (OM == O_BF16) gate = sigmoidf_(bf2f(static_cast<const bf16_t*>(a.o_pre)[bh * dv + cc]));
+      static_cast<TQ*>(a.h)[bh * dv + cc] = from_f32<TQ>(gate * num / den);
     }
   }
 }
@@ -196,11 +218,12 @@ hipError_t launch_typed(const StepArgs& a, hipStream_t stream) {
   while (ct > ctmax) ct >>= 1;
   const int cb = 4 * ct;
   dim3 grid(static_cast<unsigned>(BH), static_cast<unsigned>((a.dv + cb - 1) / cb));
+  const size_t lds = 2 * static_cast<size_t>(a.dqk) * sizeof(float);
   switch (ct) {
-    case 32: step_stream_kernel<TQ, OM, 32><<<grid, kThreads, 0, stream>>>(a); break;
-    case 16: step_stream_kernel<TQ, OM, 16><<<grid, kThreads, 0, stream>>>(a); break;
-    case 8: step_stream_kernel<TQ, OM, 8><<<grid, kThreads, 0, stream>>>(a); break;
-    default: step_stream_kernel<TQ, OM, 4><<<grid, kThreads, 0, stream>>>(a); break;
+    case 32: step_stream_kernel<TQ, OM, 32><<<grid, kThreads, lds, stream>>>(a); break;
+    case 16: step_stream_kernel<TQ, OM, 16><<<grid, kThreads, lds, stream>>>(a); break;
+    case 8: step_stream_kernel<TQ, OM, 8><<<grid, kThreads, lds, stream>>>(a); break;
+    default: step_stream_kernel<TQ, OM, 4><<<grid, kThreads, lds, stream>>>(a); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
