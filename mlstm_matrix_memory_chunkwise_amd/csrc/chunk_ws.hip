@@ -161,7 +161,7 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
     if (sx == 0) {
 #pragma unroll
       for (int m = 0; m < NB_V; ++m)
-        dma16(gv + static_cast<int64_t>(cc) * L * dv + v_off[m], lds_addr(sV + (lw * NB_V + m) * 1024));
+        dma16_nt(gv + static_cast<int64_t>(cc) * L * dv + v_off[m], lds_addr(sV + (lw * NB_V + m) * 1024));
     }
   };
   auto issue_chunk_extras = [&](int c) {
@@ -178,7 +178,7 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
         const char* src = (OM == O_F32)
             ? reinterpret_cast<const char*>(static_cast<const float*>(a.o_pre) + r * dv + vt * TV + 4 * lc)
             : reinterpret_cast<const char*>(static_cast<const bf16_t*>(a.o_pre) + r * dv + vt * TV + 8 * lc);
-        dma16(src, lds_addr(sO[c & 1] + G * 1024));
+        dma16_nt(src, lds_addr(sO[c & 1] + G * 1024));
       }
     }
     const int cn = (c + 2 < nchunks) ? c + 2 : nchunks - 1;
@@ -317,8 +317,7 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) hv[e] *= sigmoid_fast(ov[e]);
       }
-      *reinterpret_cast<uint2*>(gh + (static_cast<int64_t>(cp) * L + i) * dv) =
-          make_uint2(cvt2(hv[0], hv[1]), cvt2(hv[2], hv[3]));
+      st8_nt(gh + (static_cast<int64_t>(cp) * L + i) * dv, cvt2(hv[0], hv[1]), cvt2(hv[2], hv[3]));
     }
   };
   // value fragments (V^T, this wave's 16 columns) of the chunk in sV

@@ -59,9 +59,21 @@ __device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
                :: "s"(lds), "v"(gsrc) : "memory");
 }
+// the same, for data read once (streamed past the caches)
+__device__ __forceinline__ void dma16_nt(const void* gsrc, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt"
+               :: "s"(lds), "v"(gsrc) : "memory");
+}
 __device__ __forceinline__ void dma4(const void* gsrc, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
                :: "s"(lds), "v"(gsrc) : "memory");
+}
+
+// 8-byte store of data written once
+__device__ __forceinline__ void st8_nt(void* p, uint32_t lo, uint32_t hi) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 v = {lo, hi};
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
 }
 
 // s_waitcnt with vmcnt = n and the other counters unconstrained (gfx9 encoding).
