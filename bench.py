@@ -10,11 +10,20 @@ variant, the parallel form, the roofline of the dominant kernel, and the fp64
 CPU oracle timed on a bounded sample of the chunkwise workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--chunk 64]
-                       [--skip-cpu] [--skip-step]
+                       [--skip-cpu] [--skip-step] [--skip-extra]
+       python bench.py --profile-workload   (one chunkwise pass, one decode
+           step and a 1 GiB copy, for rocprofv3 counter runs; prints nothing)
+
+roofline.traffic is the HBM traffic per launch of the dominant kernel from
+the committed counter summary (profiles/hbm_traffic.txt: FETCH_SIZE and
+WRITE_SIZE of the kernel, scaled by what the same counters read for a copy of
+known size); it is null when the kernel sources changed since the counters
+were taken (their SHA-256 is recorded with the counters).
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -54,6 +63,69 @@ def step_algorithmic(B, H, dqk, dv, qkv_bytes=2, o_bytes=4):
                  dv * qkv_bytes + 8 + dv * o_bytes + dv * qkv_bytes)
 
 
+# sources whose kernels the HBM counters describe
+KERNEL_SOURCES = {
+    "chunkwise": ["chunk_ws.hip", "mfma_util.hpp", "common.hpp", "kernels.hpp"],
+    "step": ["step.hip", "common.hpp", "kernels.hpp"],
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+
+
+def kernel_sources_sha(which):
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mlstm_matrix_memory_chunkwise_amd", "csrc")
+    for f in KERNEL_SOURCES[which]:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(which):
+    """Calibrated HBM bytes per launch from profiles/hbm_traffic.txt, or None
+    when absent or taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            kv = dict(line.split(":", 1) for line in fh if ":" in line and not line.startswith("#"))
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get(f"{which}_sources_sha256") != kernel_sources_sha(which):
+        return None
+    try:
+        return float(kv[f"{which}_calibrated_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def profile_workload():
+    """One launch of each measured kernel plus a copy of known size."""
+    import torch
+
+    import mlstm_matrix_memory_chunkwise_amd as M
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    M.load_library()
+    cfg = workloads.CONFIGS["c2"]
+    d = {k: (None if v is None else v.to(dev)) for k, v in workloads.make_chunkwise_inputs(cfg).items()}
+    h = torch.empty((cfg.B, cfg.H, cfg.T, cfg.dv), dtype=torch.bfloat16, device=dev)
+    M.mlstm_fwd_chunkwise(d["q"], d["k"], d["v"], d["i_pre"], d["f_pre"], d["o_pre"],
+                          d["C0"], d["n0"], d["m0"], chunk=64, out=h)
+    torch.cuda.synchronize()
+    del d, h
+    cfg3 = workloads.CONFIGS["c3"]
+    s = {k: (None if v is None else v.to(dev)) for k, v in workloads.make_step_inputs(cfg3).items()}
+    M.mlstm_step(s["q"][0], s["k"][0], s["v"][0], s["i_pre"][0], s["f_pre"][0], s["o_pre"][0],
+                 s["C0"], s["n0"], s["m0"], inplace=True)
+    torch.cuda.synchronize()
+    del s
+    x = torch.ones(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+    y = torch.empty_like(x)
+    y.copy_(x)
+    torch.cuda.synchronize()
+
+
 def time_events(fn, reps, stream):
     import torch
     start = torch.cuda.Event(enable_timing=True)
@@ -75,11 +147,15 @@ def main():
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--skip-step", action="store_true")
     ap.add_argument("--skip-extra", action="store_true")
+    ap.add_argument("--profile-workload", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: every (batch, head) is independent and this "
               "build runs on a single MI355X; run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.profile_workload:
+        profile_workload()
+        return
 
     import torch
 
@@ -144,7 +220,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": byts / sec / 1e9 / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": measured_traffic("chunkwise") if args.chunk == 64 else None,
         },
         "mfma": {"achieved_tflops": flops / sec / 1e12, "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
                  "frac": flops / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS,
@@ -178,7 +254,7 @@ def main():
     # ------------------------------------------------------------ CPU oracle
     if not args.skip_cpu:
         import oracle
-        nheads = int(os.environ.get("MLSTM_BENCH_CPU_HEADS", "16"))
+        nheads = int(os.environ.get("MLSTM_BENCH_CPU_HEADS", "32"))
         sub = workloads.make_chunkwise_inputs(cfg, B=1, H=nheads)
         thr = oracle.max_threads()
         log(f"bench: oracle on {nheads} heads x {T} tokens, {thr} threads")
@@ -228,7 +304,7 @@ def main():
             "us_per_step": ms_step * 1e3,
             "tokens_per_s": cfg3.B / (ms_step / 1e3),
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic("step")},
             "algorithmic_bytes_per_step": sb,
         }
         del ds, C, n, m
