@@ -41,23 +41,19 @@
 //   LDS transpose read, instead of keeping transposed copies.
 // * The denominator uses the float32 decay-weighted row sums (before P is
 //   rounded to bf16) and the float32 n~.
-#include <type_traits>
-
 #include "common.hpp"
 #include "kernels.hpp"
+#include "mfma_util.hpp"
 
 namespace mlstm {
 namespace {
+
+using namespace mk;
 
 constexpr int NW = 4;       // waves per workgroup
 constexpr int NTH = 256;    // threads per workgroup
 constexpr int TV = 64;      // value columns per workgroup (16 per wave)
 constexpr int AS = 64;      // d_qk slice width (one stage)
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
 template <int DQK, int L, int OM>
 struct CK {
@@ -87,113 +83,6 @@ struct CK {
   static_assert(DQK % AS == 0 && NS <= NW, "d_qk must be 64, 128, 192 or 256");
   static_assert(L % 32 == 0 && L <= 128, "chunk must be 32, 64 or 128");
 };
-
-// Byte offset of element (row, col) in a [rows x 64] bf16 tile with 128-byte
-// rows whose 16-byte chunks are XOR-swizzled by (row / 2) mod 8: the 16 rows
-// read by one MFMA fragment land on 16 distinct bank groups.
-__device__ __forceinline__ int swz(int row, int col) {
-  return row * 128 + 16 * ((col >> 3) ^ ((row >> 1) & 7)) + 2 * (col & 7);
-}
-
-__device__ __forceinline__ uint4 lds_ld16(const char* base, int off) {
-  return *reinterpret_cast<const uint4*>(base + off);
-}
-
-// ds_read_b64_tr_b16: within each 16-lane group, lanes 4r..4r+3 name 4
-// consecutive bf16 of "row" r (r = 0..3); lane c of the group receives
-// element c of the 16-wide concatenation of each row, for rows 0..3.
-__device__ __forceinline__ uint2 lds_tr(const char* base, int off) {
-  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(base + off));
-  return __builtin_bit_cast(uint2, v);
-}
-
-__device__ __forceinline__ bf16x8 join(uint2 lo, uint2 hi) {
-  return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-}
-
-__device__ __forceinline__ uint32_t cvt2(float lo, float hi) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  bf16x2 v;
-  v[0] = static_cast<__bf16>(lo);
-  v[1] = static_cast<__bf16>(hi);
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-__device__ __forceinline__ bf16x8 cvt8(const float* x) {
-  return __builtin_bit_cast(
-      bf16x8, make_uint4(cvt2(x[0], x[1]), cvt2(x[2], x[3]), cvt2(x[4], x[5]), cvt2(x[6], x[7])));
-}
-
-// global -> LDS loads.  Lane l's 16 (4) bytes land at lds + 16 l (4 l); the
-// LDS base goes through M0.  Issued from asm so that the compiler neither
-// tracks nor waits on them: every wait on them is explicit.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void_t*)p));
-}
-__device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-               :: "s"(lds), "v"(gsrc) : "memory");
-}
-__device__ __forceinline__ void dma4(const void* gsrc, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
-               :: "s"(lds), "v"(gsrc) : "memory");
-}
-
-// s_waitcnt with vmcnt = n and the other counters unconstrained (gfx9 encoding).
-template <int n>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(n >= 0 && n < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Issue order of one wave (steady state).  At the top of stage y (after its
-// barrier): the loads of stage y + D (NB_QK, plus NB_V when y + D opens a
-// chunk), then, when y opens chunk c, the per-chunk loads (o~ of chunk c and
-// the gates of chunk c + 1: NB_X).  Loads of stage x were issued at the top
-// of stage x - D; when the wave waits for stage x, the loads issued after
-// them are counted below.  h stores (also vector-memory ops) are not counted,
-// which can only make a wait stricter.
-template <int NS, int D, int NBQK, int NBV, int NBX>
-__host__ __device__ constexpr int loads_after_stage(int s) {
-  int n = 0;
-  for (int k = 1; k < D; ++k) n += NBQK + (((s + k) % NS) == 0 ? NBV : 0);
-  for (int k = 1; k <= D; ++k) n += (((s - k) % NS + NS) % NS == 0) ? NBX : 0;
-  return n;
-}
-// ... and after the per-chunk loads of chunk c, at the end of chunk c.
-template <int NS, int D, int NBQK, int NBV>
-__host__ __device__ constexpr int loads_after_chunk_extras() {
-  int n = 0;
-  for (int k = 1; k < NS; ++k) n += NBQK + (((k + D) % NS) == 0 ? NBV : 0);
-  return n;
-}
-
-// Wait for the stage with slice index s (s < NS <= 4; folds to one s_waitcnt
-// once the slice loop is unrolled).
-template <int NS, int D, int NBQK, int NBV, int NBX>
-__device__ __forceinline__ void wait_stage(int s) {
-  switch (s) {
-    case 0: wait_vm<loads_after_stage<NS, D, NBQK, NBV, NBX>(0)>(); break;
-    case 1: wait_vm<loads_after_stage<NS, D, NBQK, NBV, NBX>(1 % NS)>(); break;
-    case 2: wait_vm<loads_after_stage<NS, D, NBQK, NBV, NBX>(2 % NS)>(); break;
-    default: wait_vm<loads_after_stage<NS, D, NBQK, NBV, NBX>(3 % NS)>(); break;
-  }
-}
-
-template <int W>
-using wave_c = std::integral_constant<int, W>;
-
-// Runs f with the (wave-uniform) wave index as a compile-time constant, so that
-// per-wave work splits fold into straight-line code instead of branches.
-template <typename F>
-__device__ __forceinline__ void for_wave(int wave, F&& f) {
-  switch (wave) {
-    case 0: f(wave_c<0>{}); break;
-    case 1: f(wave_c<1>{}); break;
-    case 2: f(wave_c<2>{}); break;
-    default: f(wave_c<3>{}); break;
-  }
-}
 
 template <int DQK, int L, int OM>
 __global__ __launch_bounds__(NTH, 1) void chunk_mfma_kernel(SeqArgs a) {
@@ -452,14 +341,17 @@ __global__ __launch_bounds__(NTH, 1) void chunk_mfma_kernel(SeqArgs a) {
           ca[e] = cacc[2 * P][e];
           ca[4 + e] = cacc[2 * P + 1][e];
         }
-        const bf16x8 A_C = cvt8(ca);
+        // C~ as a (high, remainder) pair of bf16 operands (see cvt8_split)
+        bf16x8 A_hi, A_lo;
+        cvt8_split(ca, A_hi, A_lo);
         uint4 Qf[C::NT];
 #pragma unroll
         for (int it = 0; it < C::NT; ++it) {
           Qf[it] = lds_ld16(Qb, swz(it * 16 + l16, 32 * p + 8 * g));
-          outT[it] = mfma16x16x32(A_C, as_bf16x8(Qf[it]), outT[it]);
+          outT[it] = mfma16x16x32(A_hi, as_bf16x8(Qf[it]), outT[it]);
+          outT[it] = mfma16x16x32(A_lo, as_bf16x8(Qf[it]), outT[it]);
         }
-        for_wave(wave, [&](auto Wc) {
+        for_wave<NW>(wave, [&](auto Wc) {
           constexpr int W = decltype(Wc)::value;
           // n~ . q for the query tiles of this wave, and its causal score tiles
           const float4 n0v = *reinterpret_cast<const float4*>(&sN[32 * P + 8 * g]);
@@ -494,7 +386,7 @@ __global__ __launch_bounds__(NTH, 1) void chunk_mfma_kernel(SeqArgs a) {
         for (int tl = 0; tl < AS / 16; ++tl) cacc[s * (AS / 16) + tl] *= f;
       }
       const int kr = l16 >> 2, kq = l16 & 3;
-      for_wave(wave, [&](auto Wc) {
+      for_wave<NW>(wave, [&](auto Wc) {
         constexpr int W = decltype(Wc)::value;
 #pragma unroll
         for (int ks = 0; ks < C::NKS; ++ks) {
@@ -530,7 +422,7 @@ __global__ __launch_bounds__(NTH, 1) void chunk_mfma_kernel(SeqArgs a) {
     float rsp[C::NT];
 #pragma unroll
     for (int it = 0; it < C::NT; ++it) rsp[it] = 0.0f;
-    for_wave(wave, [&](auto Wc) {
+    for_wave<NW>(wave, [&](auto Wc) {
      constexpr int W = decltype(Wc)::value;
 #pragma unroll
      for (int it = 0; it < C::NT; ++it) {

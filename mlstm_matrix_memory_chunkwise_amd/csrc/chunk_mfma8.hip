@@ -270,12 +270,15 @@ __global__ __launch_bounds__(NTH, 1) void chunk_mfma8_kernel(SeqArgs a) {
         ca[e] = cacc[s][0][e];
         ca[4 + e] = cacc[s][1][e];
       }
-      const bf16x8 A_C = cvt8(ca);
+      // C~ as a (high, remainder) pair of bf16 operands (see cvt8_split)
+      bf16x8 A_hi, A_lo;
+      cvt8_split(ca, A_hi, A_lo);
       uint4 Qf[NT];
 #pragma unroll
       for (int it = 0; it < NT; ++it) {
         Qf[it] = lds_ld16(Qb, swz(it * 16 + l16, 32 * hh + 8 * g));
-        outT[it] = mfma16x16x32(A_C, as_bf16x8(Qf[it]), outT[it]);
+        outT[it] = mfma16x16x32(A_hi, as_bf16x8(Qf[it]), outT[it]);
+        outT[it] = mfma16x16x32(A_lo, as_bf16x8(Qf[it]), outT[it]);
       }
       const float4 n0v = *reinterpret_cast<const float4*>(&sN[32 * P + 8 * g]);
       const float4 n1v = *reinterpret_cast<const float4*>(&sN[32 * P + 8 * g + 4]);

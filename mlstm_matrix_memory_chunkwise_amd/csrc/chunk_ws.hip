@@ -84,9 +84,6 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
   __shared__ __align__(16) float sGate[3][6][L];
   __shared__ float sQn[L];
   __shared__ __align__(16) float sN[DQK];
-  // n~ and w as bf16 (high, remainder) pairs for the v_dot2 products
-  __shared__ __align__(16) uint16_t sNb[2][DQK];
-  __shared__ __align__(16) uint16_t sWb[3][2][L];
   __shared__ __align__(256) float sGin[2][2][64];
 
   const int tid = threadIdx.x;
@@ -124,11 +121,7 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
   const float* gf = a.f_pre + head * T;
   bf16_t* gh = static_cast<bf16_t*>(a.h) + head * T * dv + b0w + 4 * g;
 
-  if (tid < DQK) {
-    const float n = a.C0 ? a.n0[head * DQK + tid] : 0.0f;
-    sN[tid] = n;
-    split_bf16(n, sNb[0][tid], sNb[1][tid]);
-  }
+  if (tid < DQK) sN[tid] = a.C0 ? a.n0[head * DQK + tid] : 0.0f;
   float m_s = a.C0 ? a.m0[head] : 0.0f;
 
   // ---- loads (intra waves; lw = 0..3 is the loading wave's index)
@@ -203,7 +196,6 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
     sGate[gb][1][lane] = Mx;
     sGate[gb][2][lane] = gv_;
     sGate[gb][3][lane] = wv;
-    split_bf16(wv, sWb[gb][0][lane], sWb[gb][1][lane]);
     sGate[gb][4][lane] = __expf(-(bcum + Mx));
     sGate[gb][5][lane] = wv * (1.0f / sg_new);
     return bL + ML;
@@ -440,27 +432,38 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
             ca[e] = cacc[2 * P][e];
             ca[4 + e] = cacc[2 * P + 1][e];
           }
-          const bf16x8 A_C = cvt8(ca);
+          // C~ enters as a (high, remainder) pair of bf16 operands: rounding
+          // it to bf16 alone costs up to ~2% of h where the carried and the
+          // in-chunk terms cancel
+          bf16x8 A_hi, A_lo;
+          cvt8_split(ca, A_hi, A_lo);
 #pragma unroll
-          for (int it = 0; it < NT; ++it) outT[it] = mfma16x16x32(A_C, as_bf16x8(Qf[p][it]), outT[it]);
+          for (int it = 0; it < NT; ++it) {
+            outT[it] = mfma16x16x32(A_hi, as_bf16x8(Qf[p][it]), outT[it]);
+            outT[it] = mfma16x16x32(A_lo, as_bf16x8(Qf[p][it]), outT[it]);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
-        uint4 Qn[2], nh[2], nl[2];
+        // (the dot products below are float32 FMAs: v_dot2_f32_bf16 on
+        // (high, remainder) splits of n~ and w was measurably less accurate
+        // where the denominator cancels)
+        uint4 Qn[2];
+        float4 nv[2][2];
         uint2 Nlo[NKS], Nhi[NKS];
-        uint4 wh[NKS], wl[NKS];
+        float4 wv[NKS][2];
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
           const int P = 2 * s + p;
           Qn[p] = lds_ld16(Qb, W * 2048 + swz(l16, 32 * p + 8 * g));
-          nh[p] = *reinterpret_cast<const uint4*>(&sNb[0][32 * P + 8 * g]);
-          nl[p] = *reinterpret_cast<const uint4*>(&sNb[1][32 * P + 8 * g]);
+          nv[p][0] = *reinterpret_cast<const float4*>(&sN[32 * P + 8 * g]);
+          nv[p][1] = *reinterpret_cast<const float4*>(&sN[32 * P + 8 * g + 4]);
         }
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
           Nlo[ks] = lds_tr(Kb, swz(32 * ks + 8 * g + kr, ncol));
           Nhi[ks] = lds_tr(Kb, swz(32 * ks + 8 * g + 4 + kr, ncol));
-          wh[ks] = *reinterpret_cast<const uint4*>(&sWb[gb][0][32 * ks + 8 * g]);
-          wl[ks] = *reinterpret_cast<const uint4*>(&sWb[gb][1][32 * ks + 8 * g]);
+          wv[ks][0] = *reinterpret_cast<const float4*>(&sGate[gb][3][32 * ks + 8 * g]);
+          wv[ks][1] = *reinterpret_cast<const float4*>(&sGate[gb][3][32 * ks + 8 * g + 4]);
         }
         // n~ rows of the previous slice: every state wave has finished
         // reading them (q.n~) before this stage's barrier
@@ -483,17 +486,20 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
         // q.n~ for query tile W, the n~ update of the previous slice and the
         // n~ increment of this wave's tile of the slice
 #pragma unroll
-        for (int p = 0; p < 2; ++p) qnp = dot8_split(Qn[p], nh[p], nl[p], qnp);
-        {
-          const float nnew = (s > 0 ? gL : gL_prev) * nprev + nn[sp_];
-          sN[nprow] = nnew;
-          split_bf16(nnew, sNb[0][nprow], sNb[1][nprow]);
+        for (int p = 0; p < 2; ++p) {
+          const uint4 q = Qn[p];
+          const float4 n0v = nv[p][0], n1v = nv[p][1];
+          qnp += bf_lo(q.x) * n0v.x + bf_hi(q.x) * n0v.y + bf_lo(q.y) * n0v.z + bf_hi(q.y) * n0v.w +
+                 bf_lo(q.z) * n1v.x + bf_hi(q.z) * n1v.y + bf_lo(q.w) * n1v.z + bf_hi(q.w) * n1v.w;
         }
+        sN[nprow] = (s > 0 ? gL : gL_prev) * nprev + nn[sp_];
         float npart = 0.0f;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-          const uint4 kk = make_uint4(Nlo[ks].x, Nlo[ks].y, Nhi[ks].x, Nhi[ks].y);
-          npart = dot8_split(kk, wh[ks], wl[ks], npart);
+          const uint2 lo = Nlo[ks], hi = Nhi[ks];
+          const float4 w0 = wv[ks][0], w1 = wv[ks][1];
+          npart += bf_lo(lo.x) * w0.x + bf_hi(lo.x) * w0.y + bf_lo(lo.y) * w0.z + bf_hi(lo.y) * w0.w +
+                   bf_lo(hi.x) * w1.x + bf_hi(hi.x) * w1.y + bf_lo(hi.y) * w1.z + bf_hi(hi.y) * w1.w;
         }
         nn[s] = sum_groups(npart);
         if (s == NS - 1) {
@@ -518,9 +524,7 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
     // ---- drain
     {
       const int arow = (NS - 1) * AS + nrow;
-      const float nnew = gL_prev * sN[arow] + nn[NS - 1];
-      sN[arow] = nnew;
-      split_bf16(nnew, sNb[0][arow], sNb[1][arow]);
+      sN[arow] = gL_prev * sN[arow] + nn[NS - 1];
     }
     __syncthreads();
     __syncthreads();

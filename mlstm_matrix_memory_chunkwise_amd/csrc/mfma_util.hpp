@@ -49,6 +49,20 @@ __device__ __forceinline__ bf16x8 cvt8(const float* x) {
       bf16x8, make_uint4(cvt2(x[0], x[1]), cvt2(x[2], x[3]), cvt2(x[4], x[5]), cvt2(x[6], x[7])));
 }
 
+// 8 floats -> (hi, lo) bf16 operands with hi = bf16(x) and lo = bf16(x - hi):
+// hi + lo carries about 16 significant bits, so two MFMAs with (hi, lo)
+// contract a float32 operand nearly exactly.
+__device__ __forceinline__ void cvt8_split(const float* x, bf16x8& hi, bf16x8& lo) {
+  hi = cvt8(x);
+  const uint4 h = __builtin_bit_cast(uint4, hi);
+  float r[8];
+  r[0] = x[0] - bf_lo(h.x); r[1] = x[1] - bf_hi(h.x);
+  r[2] = x[2] - bf_lo(h.y); r[3] = x[3] - bf_hi(h.y);
+  r[4] = x[4] - bf_lo(h.z); r[5] = x[5] - bf_hi(h.z);
+  r[6] = x[6] - bf_lo(h.w); r[7] = x[7] - bf_hi(h.w);
+  lo = cvt8(r);
+}
+
 // global -> LDS loads.  Lane l's 16 (4) bytes land at lds + 16 l (4 l); the
 // LDS base goes through M0.  Issued from asm so that the compiler neither
 // tracks nor waits on them: every wait on them is an explicit vmcnt wait.
@@ -183,26 +197,6 @@ __device__ __forceinline__ float sum_groups(float x) {
   const auto r32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
   const uint32_t b0 = r32[0], b1 = r32[1];
   return __uint_as_float(b0) + __uint_as_float(b1);
-}
-
-// ---- bf16 pair dot products (v_dot2_f32_bf16: products exact, fp32 sums)
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
-}
-// sum over 8 bf16 pairs of a . (bh + bl), where bh + bl is a float split into
-// a bf16 high part and a bf16 remainder (about 16 significant bits)
-__device__ __forceinline__ float dot8_split(uint4 a, uint4 bh, uint4 bl, float c) {
-  c = dot2(a.x, bh.x, c); c = dot2(a.y, bh.y, c); c = dot2(a.z, bh.z, c); c = dot2(a.w, bh.w, c);
-  c = dot2(a.x, bl.x, c); c = dot2(a.y, bl.y, c); c = dot2(a.z, bl.z, c); c = dot2(a.w, bl.w, c);
-  return c;
-}
-// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi), as bf16 bit patterns
-__device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
-  const __bf16 h = static_cast<__bf16>(x);
-  const __bf16 l = static_cast<__bf16>(x - static_cast<float>(h));
-  hi = __builtin_bit_cast(uint16_t, h);
-  lo = __builtin_bit_cast(uint16_t, l);
 }
 
 // log(sigmoid(x)) = min(x, 0) - log(1 + exp(-|x|)), with the hardware exp/log

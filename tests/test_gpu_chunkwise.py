@@ -116,6 +116,14 @@ EDGE = [
     # input-gate spikes: the running maximum jumps by tens, so whole chunks of
     # decay underflow to zero and the state's scale is reset
     ("input-gate spikes", "bf16", 1, 2, 1024, 128, 64, 64, True, True, "sigmoid"),
+    # d_qk 256 at chunk 64: the kernel with state and intra-chunk wave roles
+    ("d_qk 256: one chunk", "bf16", 1, 1, 64, 256, 64, 64, True, True, "sigmoid"),
+    ("d_qk 256: two chunks", "bf16", 1, 2, 128, 256, 64, 64, True, True, "sigmoid"),
+    ("d_qk 256: no o-gate, zero state, 6 heads, 2 value tiles", "bf16", 2, 3, 384, 256, 128, 64,
+     False, False, "sigmoid"),
+    ("d_qk 256: exp forget gate", "bf16", 1, 2, 512, 256, 64, 64, True, True, "exp"),
+    ("d_qk 256: input-gate spikes", "bf16", 1, 2, 1024, 256, 64, 64, True, True, "sigmoid"),
+    ("d_qk 256: d_v 512", "bf16", 1, 1, 256, 256, 512, 64, True, True, "sigmoid"),
 ]
 
 
@@ -124,7 +132,7 @@ def test_edge_cases(case):
     name, dtype, B, H, T, dqk, dv, chunk, rstate, with_o, fgate = case
     log(f"chunkwise edge: {name}")
     f_dist = (-0.05, 0.1) if fgate == "exp" else (3.0, 1.0)
-    i_dist = (0.0, 15.0) if name == "input-gate spikes" else (-1.0, 2.0)
+    i_dist = (0.0, 15.0) if name.endswith("input-gate spikes") else (-1.0, 2.0)
     cfg = workloads.Config("edge", 7, dtype, B, H, T, dqk, dv, (chunk,), i_dist, f_dist,
                            (0.0, 1.0), rstate)
     inp = workloads.make_chunkwise_inputs(cfg, with_o=with_o)
@@ -205,13 +213,14 @@ def test_deterministic():
         assert torch.equal(x, y)
 
 
-@pytest.mark.parametrize("dtype,chunk,dv", [("bf16", 64, 128), ("bf16", 32, 48), ("f32", 16, 32)])
-def test_every_output_written(dtype, chunk, dv):
+@pytest.mark.parametrize("dtype,chunk,dqk,dv", [("bf16", 64, 64, 128), ("bf16", 64, 256, 128),
+                                                ("bf16", 32, 64, 48), ("f32", 16, 64, 32)])
+def test_every_output_written(dtype, chunk, dqk, dv):
     """Outputs pre-filled with NaN come back finite: every element was written."""
-    cfg = workloads.Config("canary", 8, dtype, 2, 3, 4 * chunk, 64, dv, (chunk,), (0.0, 1.0),
+    cfg = workloads.Config("canary", 8, dtype, 2, 3, 4 * chunk, dqk, dv, (chunk,), (0.0, 1.0),
                            (3.0, 1.0), (0.0, 1.0), True)
     inp = workloads.make_chunkwise_inputs(cfg)
-    log(f"chunkwise canary {dtype} chunk={chunk} dv={dv}")
+    log(f"chunkwise canary {dtype} chunk={chunk} dqk={dqk} dv={dv}")
     d = to_dev(inp)
     M = _M()
     out = nan_like(tuple(d["v"].shape), d["q"].dtype)
