@@ -234,14 +234,17 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
 
   // Intra wave W owns the causal score tiles n = it (it + 1) / 2 + jt with
   // n = W mod 4: three for W < 2, two for W >= 2 (whose third slot repeats
-  // the second: identical P writes, and its row sum is never read).
+  // the second: identical P writes, and its row sum is never read).  Slot 0
+  // is tile (qt, 0) with qt = 0, 1, 3, 2 for W = 0..3 (wave 2 takes its
+  // tiles in the order 6, 2), so that the four waves' first slots cover the
+  // four query tiles.
   int slot_it[3], slot_jt[3];
   {
     const int W = cg;
-    slot_it[0] = W == 0 ? 0 : W == 1 ? 1 : W == 2 ? 1 : 2;
-    slot_jt[0] = W == 0 ? 0 : W == 1 ? 0 : W == 2 ? 1 : 0;
-    slot_it[1] = W == 0 ? 2 : W == 1 ? 2 : 3;
-    slot_jt[1] = W == 0 ? 1 : W == 1 ? 2 : W == 2 ? 0 : 1;
+    slot_it[0] = W == 0 ? 0 : W == 1 ? 1 : W == 2 ? 3 : 2;
+    slot_jt[0] = 0;
+    slot_it[1] = W == 0 ? 2 : W == 1 ? 2 : W == 2 ? 1 : 3;
+    slot_jt[1] = W == 0 ? 1 : W == 1 ? 2 : 1;
     slot_it[2] = W == 0 ? 3 : W == 1 ? 3 : slot_it[1];
     slot_jt[2] = W == 0 ? 2 : W == 1 ? 3 : slot_jt[1];
   }
@@ -250,9 +253,9 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
   auto row_sum = [&](int it, int i16) {
     switch (it) {
       case 0: return sRs[0][0][i16];
-      case 1: return sRs[1][0][i16] + sRs[2][0][i16];
+      case 1: return sRs[1][0][i16] + sRs[2][1][i16];
       case 2: return (sRs[0][1][i16] + sRs[1][1][i16]) + sRs[3][0][i16];
-      default: return (sRs[0][2][i16] + sRs[1][2][i16]) + (sRs[2][1][i16] + sRs[3][1][i16]);
+      default: return (sRs[0][2][i16] + sRs[1][2][i16]) + (sRs[2][0][i16] + sRs[3][1][i16]);
     }
   };
 
@@ -357,23 +360,14 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
         }
       }
     }
-    // n~ rows of this wave's tile of a slice (four lanes store the same value)
-    const int nrow = 32 * (W >> 1) + 8 * (l16 >> 2) + 4 * (W & 1) + (l16 & 3);
-    const int ncol = 32 * (W >> 1) + 8 * kq + 4 * (W & 1);   // its K^T fragment column
     float sig = 1.0f;    // C~ = sig * cacc
-    float gL_prev = 1.0f;   // with nn = 0: the update before chunk 0 keeps n~
     f32x4 outT[NT];
     bf16x8 wVf[NKS];
-    float nn[NS];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) nn[s] = 0.0f;
-    float qnp = 0.0f;
     int gb = 0, gbn = 1;   // gate buffers of chunks c, c + 1
     for (int c = 0; c < nchunks; ++c) {
       const float gL = sGate[gb][2][L - 1];
       const bool renorm = gL * sig < 0x1p-64f;
       const float sig_new = renorm ? 1.0f : gL * sig;
-      const float fscale = renorm ? gL * sig : 1.0f;   // exact 1 unless renormalising
       float m_n2 = 0.0f;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
@@ -398,13 +392,11 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
           }
 #pragma unroll
           for (int it = 0; it < NT; ++it) outT[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-          qnp = 0.0f;
         }
         // ---- the stage's LDS reads are issued ahead of the arithmetic that
         // consumes them (reads return in order, so each MFMA waits only for
         // its own operands): Q and K fragments, then the readout MFMAs, then
-        // the small operands of q.n~ and the n~ increment (reusing the Q
-        // registers), then the update MFMAs and the dot products
+        // the update MFMAs
         uint4 Qf[2][NT];
         uint2 Klo[NKS][AS / 16], Khi[NKS][AS / 16];
 #pragma unroll
@@ -444,36 +436,13 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
           }
         }
         __builtin_amdgcn_sched_barrier(0);
-        // (the dot products below are float32 FMAs: v_dot2_f32_bf16 on
-        // (high, remainder) splits of n~ and w was measurably less accurate
-        // where the denominator cancels)
-        uint4 Qn[2];
-        float4 nv[2][2];
-        uint2 Nlo[NKS], Nhi[NKS];
-        float4 wv[NKS][2];
+        // state update of the slice's rows (after their readout); the
+        // renormalisation (rare) scales them first
+        if (renorm) {
+          const float f = gL * sig;
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          const int P = 2 * s + p;
-          Qn[p] = lds_ld16(Qb, W * 2048 + swz(l16, 32 * p + 8 * g));
-          nv[p][0] = *reinterpret_cast<const float4*>(&sN[32 * P + 8 * g]);
-          nv[p][1] = *reinterpret_cast<const float4*>(&sN[32 * P + 8 * g + 4]);
+          for (int tl = 0; tl < AS / 16; ++tl) cacc[s * (AS / 16) + tl] *= f;
         }
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          Nlo[ks] = lds_tr(Kb, swz(32 * ks + 8 * g + kr, ncol));
-          Nhi[ks] = lds_tr(Kb, swz(32 * ks + 8 * g + 4 + kr, ncol));
-          wv[ks][0] = *reinterpret_cast<const float4*>(&sGate[gb][3][32 * ks + 8 * g]);
-          wv[ks][1] = *reinterpret_cast<const float4*>(&sGate[gb][3][32 * ks + 8 * g + 4]);
-        }
-        // n~ rows of the previous slice: every state wave has finished
-        // reading them (q.n~) before this stage's barrier
-        const int sp_ = (s + NS - 1) % NS;
-        const int nprow = sp_ * AS + nrow;
-        const float nprev = sN[nprow];
-        __builtin_amdgcn_sched_barrier(0);
-        // state update of the slice's rows (after their readout)
-#pragma unroll
-        for (int tl = 0; tl < AS / 16; ++tl) cacc[s * (AS / 16) + tl] *= fscale;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
@@ -482,34 +451,13 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
             cacc[t] = mfma16x16x32(join(Klo[ks][tl], Khi[ks][tl]), wVf[ks], cacc[t]);
           }
         }
-        __builtin_amdgcn_sched_barrier(0);
-        // q.n~ for query tile W, the n~ update of the previous slice and the
-        // n~ increment of this wave's tile of the slice
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          const uint4 q = Qn[p];
-          const float4 n0v = nv[p][0], n1v = nv[p][1];
-          qnp += bf_lo(q.x) * n0v.x + bf_hi(q.x) * n0v.y + bf_lo(q.y) * n0v.z + bf_hi(q.y) * n0v.w +
-                 bf_lo(q.z) * n1v.x + bf_hi(q.z) * n1v.y + bf_lo(q.w) * n1v.z + bf_hi(q.w) * n1v.w;
-        }
-        sN[nprow] = (s > 0 ? gL : gL_prev) * nprev + nn[sp_];
-        float npart = 0.0f;
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const uint2 lo = Nlo[ks], hi = Nhi[ks];
-          const float4 w0 = wv[ks][0], w1 = wv[ks][1];
-          npart += bf_lo(lo.x) * w0.x + bf_hi(lo.x) * w0.y + bf_lo(lo.y) * w0.z + bf_hi(lo.y) * w0.w +
-                   bf_lo(hi.x) * w1.x + bf_hi(hi.x) * w1.y + bf_lo(hi.y) * w1.z + bf_hi(hi.y) * w1.w;
-        }
-        nn[s] = sum_groups(npart);
         if (s == NS - 1) {
-          // scaled readout and q.n~ for the intra waves
+          // scaled readout for the intra waves
 #pragma unroll
           for (int it = 0; it < NT; ++it) {
             const float gi_ = sGate[gb][2][it * 16 + l16];
             *reinterpret_cast<f32x4*>(&sR[W][it][lane][0]) = outT[it] * (gi_ * sig);
           }
-          sQn[W * 16 + l16] = sum_groups(qnp);
         }
         // gates of the next chunk (staged two chunks ahead)
         if (s == 1 && wave == 0) m_n2 = scan_gates((c + 1) & 1, gbn, m_n1, sig_new);
@@ -517,15 +465,10 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
       m_s = m_n1;
       m_n1 = m_n2;
       sig = sig_new;
-      gL_prev = gL;
       gb = gbn;
       gbn = (gbn == 2) ? 0 : gbn + 1;
     }
     // ---- drain
-    {
-      const int arow = (NS - 1) * AS + nrow;
-      sN[arow] = gL_prev * sN[arow] + nn[NS - 1];
-    }
     __syncthreads();
     __syncthreads();
     if (a.C1) {
@@ -543,6 +486,7 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
       }
     }
   } else {
+    const int W = cg;
     // this wave's score-tile slots as uniform LDS offsets of the Q and K rows
     int qoff[3], koff[3];
 #pragma unroll
@@ -550,6 +494,17 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
       qoff[k] = slot_it[k] * 2048;
       koff[k] = slot_jt[k] * 2048;
     }
+    // q.n~ of query tile qt, from the Q fragments of slot 0
+    const int qt = slot_it[0];
+    // n~ increments: this wave covers the rows of tile W of every slice
+    // (four lanes store the same value)
+    const int nrow = 32 * (W >> 1) + 8 * (l16 >> 2) + 4 * (W & 1) + (l16 & 3);
+    const int ncol = 32 * (W >> 1) + 8 * kq + 4 * (W & 1);   // its K^T fragment column
+    float nn[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) nn[s] = 0.0f;
+    float qnp = 0.0f;
+    float gL_prev = 1.0f;   // with nn = 0: the update before chunk 0 keeps n~
     // score tiles of the current and the previous chunk, value fragments
     // of both
     f32x4 sacc[3], sprev[3];
@@ -558,6 +513,8 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
     for (int k = 0; k < 3; ++k) sacc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
     int gb = 0, gbp = 2;   // gate buffers of chunks c, c - 1
     for (int c = 0; c < nchunks; ++c) {
+      // (wave-uniform: kept in a scalar register)
+      const float gL = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sGate[gb][2][L - 1])));
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const int slot = stage_top_intra(c, s);
@@ -573,6 +530,7 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
           for (int ks = 0; ks < NKS; ++ks) Vp[ks] = Vf[ks];
           uint2 raw[2 * NKS];
           load_vf(Vf, raw);
+          qnp = 0.0f;
         }
         // score tiles over the slice (operands first, see the state role)
         uint4 Qf[2][3], Kf[2][3];
@@ -591,18 +549,69 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
           for (int k = 0; k < 3; ++k)
             sacc[k] = mfma16x16x32(as_bf16x8(Kf[p][k]), as_bf16x8(Qf[p][k]), sacc[k]);
         }
+        // operands of q.n~ and of the n~ increment (float32 FMAs below:
+        // v_dot2_f32_bf16 on (high, remainder) splits of n~ and w was
+        // measurably less accurate where the denominator cancels)
+        float4 nv[2][2];
+        uint2 Nlo[NKS], Nhi[NKS];
+        float4 wv[NKS][2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const int P = 2 * s + p;
+          nv[p][0] = *reinterpret_cast<const float4*>(&sN[32 * P + 8 * g]);
+          nv[p][1] = *reinterpret_cast<const float4*>(&sN[32 * P + 8 * g + 4]);
+        }
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          Nlo[ks] = lds_tr(Kb, swz(32 * ks + 8 * g + kr, ncol));
+          Nhi[ks] = lds_tr(Kb, swz(32 * ks + 8 * g + 4 + kr, ncol));
+          wv[ks][0] = *reinterpret_cast<const float4*>(&sGate[gb][3][32 * ks + 8 * g]);
+          wv[ks][1] = *reinterpret_cast<const float4*>(&sGate[gb][3][32 * ks + 8 * g + 4]);
+        }
+        // n~ rows of the previous slice: every intra wave has finished
+        // reading them (q.n~) before this stage's barrier
+        const int sp_ = (s + NS - 1) % NS;
+        const int nprow = sp_ * AS + nrow;
+        const float nprev = sN[nprow];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const uint4 q = Qf[p][0];
+          const float4 n0v = nv[p][0], n1v = nv[p][1];
+          qnp += bf_lo(q.x) * n0v.x + bf_hi(q.x) * n0v.y + bf_lo(q.y) * n0v.z + bf_hi(q.y) * n0v.w +
+                 bf_lo(q.z) * n1v.x + bf_hi(q.z) * n1v.y + bf_lo(q.w) * n1v.z + bf_hi(q.w) * n1v.w;
+        }
+        sN[nprow] = (s > 0 ? gL : gL_prev) * nprev + nn[sp_];
+        float npart = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const uint2 lo = Nlo[ks], hi = Nhi[ks];
+          const float4 w0 = wv[ks][0], w1 = wv[ks][1];
+          npart += bf_lo(lo.x) * w0.x + bf_hi(lo.x) * w0.y + bf_lo(lo.y) * w0.z + bf_hi(lo.y) * w0.w +
+                   bf_lo(hi.x) * w1.x + bf_hi(hi.x) * w1.y + bf_lo(hi.y) * w1.z + bf_hi(hi.y) * w1.w;
+        }
+        nn[s] = sum_groups(npart);
+        __builtin_amdgcn_sched_barrier(0);
         // finishing of the previous chunk (in chunk 0 the P pass works on
         // zeros and its results are never read)
         if (s == 0) finish_p(sprev, gbp);
         if (s == 1 || s == 2) {
           if (c > 0) finish_out(Vp, 2 * (s - 1), c - 1, gbp, (c - 1) & 1);
         }
+        // this chunk's q.n~ of query tile qt, read from stage 1 of the next
+        // chunk on (after the previous chunk's outputs are done)
+        if (s == NS - 1) sQn[qt * 16 + l16] = sum_groups(qnp);
       }
+      gL_prev = gL;
       gbp = gb;
       gb = (gb == 2) ? 0 : gb + 1;
     }
-    // ---- drain: finish the last chunk
+    // ---- drain: finish the last chunk (and the n~ rows of its last slice)
     wait_vm<0>();
+    {
+      const int arow = (NS - 1) * AS + nrow;
+      sN[arow] = gL_prev * sN[arow] + nn[NS - 1];
+    }
     __syncthreads();
     finish_p(sacc, gbp);
     __syncthreads();
