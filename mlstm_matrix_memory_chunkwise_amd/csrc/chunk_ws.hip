@@ -17,20 +17,21 @@
 // SIMD:
 // * state waves 0..3 (16 value columns each) keep C~ in registers and, per
 //   64-row d_qk slice ("stage"), run the readout C~^T Q^T and the update
-//   K^T (w V) on MFMA, plus q.n~ and the n~ increment; at the end of a chunk
-//   they leave the scaled readout g_i sig C~^T q_i and q.n~ in LDS;
+//   K^T (w V) on MFMA; at the end of a chunk they leave the scaled readout
+//   g_i sig C~^T q_i in LDS.  They also issue and await every global->LDS
+//   load (their stages are the shorter ones);
 // * intra waves 4..7 run the causal score tiles S^T = K Q^T of the current
-//   chunk stage by stage and, during the stages of chunk c, finish chunk c-1:
-//   P = S (.) D at stage 0, then P V, the denominator, the output gate and
-//   the h store at stages 1 and 2.
+//   chunk stage by stage, q.n~ and the n~ increment K^T w (MFMAs with the
+//   vector split into three bf16 terms), and, during the stages of chunk c,
+//   finish chunk c-1: P = S (.) D at stage 0, then P V, the denominator, the
+//   output gate and the h store at stages 1 and 2.
 // The VALU-heavy finishing of one chunk thus overlaps the MFMA-heavy state
 // work of the next on every SIMD, and no wave waits for a chunk epilogue.
 //
-// Loads are as in chunk_mfma.hip: every loop load is a global->LDS DMA
-// issued from asm, shared by all 8 waves (each issues the same count), with
-// compile-time vmcnt waits; q/k come in 64-wide d_qk slices through a ring of
-// D+1 slots, v once per chunk, the o~ tile once per chunk into one of two
-// slots, the gates two chunks ahead.
+// Loads are global->LDS DMAs issued from asm, with compile-time vmcnt
+// waits; q/k come in 64-wide d_qk slices through a ring of D+1 slots, v once
+// per chunk, the o~ tile once per chunk into one of two slots, the gates two
+// chunks ahead.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mfma_util.hpp"
@@ -54,10 +55,11 @@ constexpr int NS = DQK / AS;   // stages per chunk
 constexpr int NCT = DQK / 16;  // 16-row C~ tiles per state wave
 constexpr int D = 3;           // stages in flight
 constexpr int NSLOT = D + 1;
-// Only the intra waves (NWL of them) issue and await the global->LDS loads:
-// issuing can stall while the memory system is saturated, and the state
-// waves are the critical path.  The barrier after each wait publishes the
-// landed data to the state waves.
+// One role (NWL waves) issues and awaits all global->LDS loads: issuing
+// stalls while the address units are busy, so the role with slack in its
+// stages takes them (the state waves: the intra waves' stages are longer).
+// The barrier after each wait publishes the landed data to the other role.
+constexpr bool STATE_LOADS = true;
 constexpr int NWL = 4;
 constexpr int NB_QK = 2 * TILE / 1024 / NWL;   // 1 KB loads per loading wave per stage
 constexpr int NB_V = TILE / 1024 / NWL;
@@ -80,10 +82,14 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
   __shared__ __align__(1024) char sO[2][C::OTILE];         // o~ by chunk parity
   __shared__ __align__(16) float sR[4][NT][64][4];         // scaled readout
   __shared__ __align__(16) bf16_t sP[L * PROW];
-  // per chunk mod 3: u, M, g, w, exp(-m), w / sig'
-  __shared__ __align__(16) float sGate[3][6][L];
+  // per chunk mod 3: u, M, g, exp(-m), w / sig'
+  __shared__ __align__(16) float sGate[3][5][L];
   __shared__ float sQn[L];
   __shared__ __align__(16) float sN[DQK];
+  // n~ and w (per chunk mod 3) as three bf16 terms (high, middle, low) and a
+  // row of zeros: the A operands of the normaliser MFMAs
+  __shared__ __align__(16) bf16_t sNs[4][DQK];
+  __shared__ __align__(16) bf16_t sWs[3][4][L];
   __shared__ __align__(256) float sGin[2][2][64];
 
   const int tid = threadIdx.x;
@@ -121,10 +127,16 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
   const float* gf = a.f_pre + head * T;
   bf16_t* gh = static_cast<bf16_t*>(a.h) + head * T * dv + b0w + 4 * g;
 
-  if (tid < DQK) sN[tid] = a.C0 ? a.n0[head * DQK + tid] : 0.0f;
+  if (tid < DQK) {
+    const float n0 = a.C0 ? a.n0[head * DQK + tid] : 0.0f;
+    sN[tid] = n0;
+    split3_bf16(n0, sNs[0][tid], sNs[1][tid], sNs[2][tid]);
+    sNs[3][tid] = 0;
+  }
+  if (tid < 3 * L) sWs[tid / L][3][tid % L] = 0;
   float m_s = a.C0 ? a.m0[head] : 0.0f;
 
-  // ---- loads (intra waves; lw = 0..3 is the loading wave's index)
+  // ---- loads (the loading role; lw = 0..3 is the loading wave's index)
   const int lw = cg;
   const int ld_r = lane >> 3, ld_pc = lane & 7;
   int qk_off[NB_QK];
@@ -195,14 +207,15 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
     sGate[gb][0][lane] = u;
     sGate[gb][1][lane] = Mx;
     sGate[gb][2][lane] = gv_;
-    sGate[gb][3][lane] = wv;
-    sGate[gb][4][lane] = __expf(-(bcum + Mx));
-    sGate[gb][5][lane] = wv * (1.0f / sg_new);
+    split3_bf16(wv, sWs[gb][0][lane], sWs[gb][1][lane], sWs[gb][2][lane]);
+    sGate[gb][3][lane] = __expf(-(bcum + Mx));
+    sGate[gb][4][lane] = wv * (1.0f / sg_new);
     return bL + ML;
   };
 
   // ---- prologue
-  if (!state_wave) {
+  const bool load_wave = state_wave == STATE_LOADS;
+  if (load_wave) {
 #pragma unroll
     for (int x = 0; x < D; ++x) issue_stage(x);
     dma4(gi + lane, lds_addr(&sGin[0][0][0]));
@@ -295,7 +308,7 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
         }
       }
       const float rs = row_sum(it, l16);
-      const float den = fmaxf(fabsf(sGate[gb][2][i] * sQn[i] + rs), sGate[gb][4][i]);
+      const float den = fmaxf(fabsf(sGate[gb][2][i] * sQn[i] + rs), sGate[gb][3][i]);
       const float inv = __builtin_amdgcn_rcpf(den);
       float hv[4];
 #pragma unroll
@@ -326,11 +339,11 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
     }
   };
 
-  // Both roles run the same stage sequence (same barriers, same loads and
-  // waits); each role has its own loop so that its registers are its own.
-  // the intra waves wait for the stage's loads before the barrier and issue
-  // the loads D stages ahead after it
-  auto stage_top_intra = [&](int c, int s) {
+  // Both roles run the same stage sequence (same barriers); each role has
+  // its own loop so that its registers are its own.  The loading role waits
+  // for the stage's loads before the barrier and issues the loads D stages
+  // ahead after it.
+  auto stage_top_load = [&](int c, int s) {
     const int x = c * NS + s;
     if (x < D) wait_vm<0>();
     else wait_stage<NS, D, NB_QK, NB_V, C::NB_X>(s);
@@ -339,9 +352,15 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
     if (s == 0) issue_chunk_extras(c);
     return x % NSLOT;
   };
-  auto stage_top_state = [&](int c, int s) {
+  auto stage_top_wait = [&](int c, int s) {
     __syncthreads();
     return (c * NS + s) % NSLOT;
+  };
+  auto stage_top_state = [&](int c, int s) {
+    return STATE_LOADS ? stage_top_load(c, s) : stage_top_wait(c, s);
+  };
+  auto stage_top_intra = [&](int c, int s) {
+    return STATE_LOADS ? stage_top_wait(c, s) : stage_top_load(c, s);
   };
 
   if (state_wave) {
@@ -380,8 +399,8 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
           load_vf(vtmp, raw);
 #pragma unroll
           for (int ks = 0; ks < NKS; ++ks) {
-            const float4 w0 = *reinterpret_cast<const float4*>(&sGate[gb][5][32 * ks + 8 * g]);
-            const float4 w1 = *reinterpret_cast<const float4*>(&sGate[gb][5][32 * ks + 8 * g + 4]);
+            const float4 w0 = *reinterpret_cast<const float4*>(&sGate[gb][4][32 * ks + 8 * g]);
+            const float4 w1 = *reinterpret_cast<const float4*>(&sGate[gb][4][32 * ks + 8 * g + 4]);
             const uint2 lo = raw[2 * ks], hi = raw[2 * ks + 1];
             float xw[8];
             xw[0] = bf_lo(lo.x) * w0.x; xw[1] = bf_hi(lo.x) * w0.y;
@@ -469,6 +488,7 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
       gbn = (gbn == 2) ? 0 : gbn + 1;
     }
     // ---- drain
+    if (STATE_LOADS) wait_vm<0>();
     __syncthreads();
     __syncthreads();
     if (a.C1) {
@@ -497,13 +517,14 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
     // q.n~ of query tile qt, from the Q fragments of slot 0
     const int qt = slot_it[0];
     // n~ increments: this wave covers the rows of tile W of every slice
-    // (four lanes store the same value)
+    // (every lane of a 16-lane column holds the same value)
     const int nrow = 32 * (W >> 1) + 8 * (l16 >> 2) + 4 * (W & 1) + (l16 & 3);
     const int ncol = 32 * (W >> 1) + 8 * kq + 4 * (W & 1);   // its K^T fragment column
     float nn[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) nn[s] = 0.0f;
-    float qnp = 0.0f;
+    f32x4 qn = f32x4{0.f, 0.f, 0.f, 0.f};
+    uint4 Wx[NKS];   // w terms of the current chunk (A operand, see below)
     float gL_prev = 1.0f;   // with nn = 0: the update before chunk 0 keeps n~
     // score tiles of the current and the previous chunk, value fragments
     // of both
@@ -530,7 +551,10 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
           for (int ks = 0; ks < NKS; ++ks) Vp[ks] = Vf[ks];
           uint2 raw[2 * NKS];
           load_vf(Vf, raw);
-          qnp = 0.0f;
+          qn = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks)
+            Wx[ks] = *reinterpret_cast<const uint4*>(&sWs[gb][l16 & 3][32 * ks + 8 * g]);
         }
         // score tiles over the slice (operands first, see the state role)
         uint4 Qf[2][3], Kf[2][3];
@@ -549,24 +573,21 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
           for (int k = 0; k < 3; ++k)
             sacc[k] = mfma16x16x32(as_bf16x8(Kf[p][k]), as_bf16x8(Qf[p][k]), sacc[k]);
         }
-        // operands of q.n~ and of the n~ increment (float32 FMAs below:
-        // v_dot2_f32_bf16 on (high, remainder) splits of n~ and w was
-        // measurably less accurate where the denominator cancels)
-        float4 nv[2][2];
-        uint2 Nlo[NKS], Nhi[NKS];
-        float4 wv[NKS][2];
+        // q.n~ and the n~ increment as MFMAs whose A operand holds the
+        // vector (n~, w) split into three bf16 terms, in rows 4r, 4r+1,
+        // 4r+2 (row 4r+3 is zero): with B = the Q fragment, D[4r+e][c] is
+        // term e of q_c . n~; with B = the K^T fragment of the update, term e
+        // of sum_j w_j K[j][row c].  Summing the terms gives the float32
+        // product to about 24 significant bits of the vector.
+        uint4 Nx[2];
+        uint2 Klo[NKS], Khi[NKS];
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          const int P = 2 * s + p;
-          nv[p][0] = *reinterpret_cast<const float4*>(&sN[32 * P + 8 * g]);
-          nv[p][1] = *reinterpret_cast<const float4*>(&sN[32 * P + 8 * g + 4]);
-        }
+        for (int p = 0; p < 2; ++p)
+          Nx[p] = *reinterpret_cast<const uint4*>(&sNs[l16 & 3][32 * (2 * s + p) + 8 * g]);
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-          Nlo[ks] = lds_tr(Kb, swz(32 * ks + 8 * g + kr, ncol));
-          Nhi[ks] = lds_tr(Kb, swz(32 * ks + 8 * g + 4 + kr, ncol));
-          wv[ks][0] = *reinterpret_cast<const float4*>(&sGate[gb][3][32 * ks + 8 * g]);
-          wv[ks][1] = *reinterpret_cast<const float4*>(&sGate[gb][3][32 * ks + 8 * g + 4]);
+          Klo[ks] = lds_tr(Kb, swz(32 * ks + 8 * g + kr, ncol));
+          Khi[ks] = lds_tr(Kb, swz(32 * ks + 8 * g + 4 + kr, ncol));
         }
         // n~ rows of the previous slice: every intra wave has finished
         // reading them (q.n~) before this stage's barrier
@@ -575,22 +596,16 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
         const float nprev = sN[nprow];
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          const uint4 q = Qf[p][0];
-          const float4 n0v = nv[p][0], n1v = nv[p][1];
-          qnp += bf_lo(q.x) * n0v.x + bf_hi(q.x) * n0v.y + bf_lo(q.y) * n0v.z + bf_hi(q.y) * n0v.w +
-                 bf_lo(q.z) * n1v.x + bf_hi(q.z) * n1v.y + bf_lo(q.w) * n1v.z + bf_hi(q.w) * n1v.w;
-        }
-        sN[nprow] = (s > 0 ? gL : gL_prev) * nprev + nn[sp_];
-        float npart = 0.0f;
+        for (int p = 0; p < 2; ++p) qn = mfma16x16x32(as_bf16x8(Nx[p]), as_bf16x8(Qf[p][0]), qn);
+        f32x4 ni = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const uint2 lo = Nlo[ks], hi = Nhi[ks];
-          const float4 w0 = wv[ks][0], w1 = wv[ks][1];
-          npart += bf_lo(lo.x) * w0.x + bf_hi(lo.x) * w0.y + bf_lo(lo.y) * w0.z + bf_hi(lo.y) * w0.w +
-                   bf_lo(hi.x) * w1.x + bf_hi(hi.x) * w1.y + bf_lo(hi.y) * w1.z + bf_hi(hi.y) * w1.w;
+        for (int ks = 0; ks < NKS; ++ks) ni = mfma16x16x32(as_bf16x8(Wx[ks]), join(Klo[ks], Khi[ks]), ni);
+        {
+          const float nv = (s > 0 ? gL : gL_prev) * nprev + nn[sp_];
+          sN[nprow] = nv;
+          split3_bf16(nv, sNs[0][nprow], sNs[1][nprow], sNs[2][nprow]);
         }
-        nn[s] = sum_groups(npart);
+        nn[s] = (ni[0] + ni[1]) + ni[2];
         __builtin_amdgcn_sched_barrier(0);
         // finishing of the previous chunk (in chunk 0 the P pass works on
         // zeros and its results are never read)
@@ -600,17 +615,17 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
         }
         // this chunk's q.n~ of query tile qt, read from stage 1 of the next
         // chunk on (after the previous chunk's outputs are done)
-        if (s == NS - 1) sQn[qt * 16 + l16] = sum_groups(qnp);
+        if (s == NS - 1) sQn[qt * 16 + l16] = (qn[0] + qn[1]) + qn[2];
       }
       gL_prev = gL;
       gbp = gb;
       gb = (gb == 2) ? 0 : gb + 1;
     }
     // ---- drain: finish the last chunk (and the n~ rows of its last slice)
-    wait_vm<0>();
+    if (!STATE_LOADS) wait_vm<0>();
     {
       const int arow = (NS - 1) * AS + nrow;
-      sN[arow] = gL_prev * sN[arow] + nn[NS - 1];
+      sN[arow] = gL_prev * sN[arow] + nn[NS - 1];   // (its bf16 terms are not read again)
     }
     __syncthreads();
     finish_p(sacc, gbp);

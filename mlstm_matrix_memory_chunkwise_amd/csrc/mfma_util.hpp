@@ -63,6 +63,18 @@ __device__ __forceinline__ void cvt8_split(const float* x, bf16x8& hi, bf16x8& l
   lo = cvt8(r);
 }
 
+// x -> three bf16 (storage bits) whose sum is x to about 24 significant
+// bits: hi = bf16(x), mid = bf16(x - hi), lo = bf16(x - hi - mid) (each
+// difference is exact in float32)
+__device__ __forceinline__ void split3_bf16(float x, bf16_t& hi, bf16_t& mid, bf16_t& lo) {
+  const uint32_t h = cvt2(x, 0.0f);
+  const float r1 = x - bf_lo(h);
+  const uint32_t m = cvt2(r1, 0.0f);
+  hi = static_cast<bf16_t>(h);
+  mid = static_cast<bf16_t>(m);
+  lo = static_cast<bf16_t>(cvt2(r1 - bf_lo(m), 0.0f));
+}
+
 // global -> LDS loads.  Lane l's 16 (4) bytes land at lds + 16 l (4 l); the
 // LDS base goes through M0.  Issued from asm so that the compiler neither
 // tracks nor waits on them: every wait on them is an explicit vmcnt wait.
