@@ -16,15 +16,17 @@
 // value columns) pair) therefore splits by role, one wave of each role per
 // SIMD:
 // * state waves 0..3 (16 value columns each) keep C~ in registers and, per
-//   64-row d_qk slice ("stage"), run the readout C~^T Q^T and the update
-//   K^T (w V) on MFMA; at the end of a chunk they leave the scaled readout
-//   g_i sig C~^T q_i in LDS.  They also issue and await every global->LDS
-//   load (their stages are the shorter ones);
-// * intra waves 4..7 run the causal score tiles S^T = K Q^T of the current
-//   chunk stage by stage, q.n~ and the n~ increment K^T w (MFMAs with the
-//   vector split into three bf16 terms), and, during the stages of chunk c,
-//   finish chunk c-1: P = S (.) D at stage 0, then P V, the denominator, the
-//   output gate and the h store at stages 1 and 2.
+//   64-row d_qk slice ("stage"), run the readout C~^T Q^T, the update
+//   K^T (w V) and the transposed score tiles S^T = K Q^T of key tile W
+//   against every query tile on MFMA; at the end of a chunk they leave the
+//   scaled readout g_i sig C~^T q_i and P = S (.) D (query tiles 0, 1; tiles
+//   2, 3 at stage 0 of the next chunk) in LDS;
+// * intra waves 4..7 compute q.n~ and the n~ increment K^T w (MFMAs with
+//   the vector split into three bf16 terms), issue and await every
+//   global->LDS load, and, during the stages of chunk c, finish chunk c-1:
+//   P V of query tiles 0, 1 at stage 1, their h and P V of tiles 2, 3 at
+//   stage 2, the denominators of tiles 2, 3 at stage 3 and their h at stage
+//   0 of chunk c+1.
 // The VALU-heavy finishing of one chunk thus overlaps the MFMA-heavy state
 // work of the next on every SIMD, and no wave waits for a chunk epilogue.
 //
@@ -55,11 +57,11 @@ constexpr int NS = DQK / AS;   // stages per chunk
 constexpr int NCT = DQK / 16;  // 16-row C~ tiles per state wave
 constexpr int D = 3;           // stages in flight
 constexpr int NSLOT = D + 1;
-// One role (NWL waves) issues and awaits all global->LDS loads: issuing
-// stalls while the address units are busy, so the role with slack in its
-// stages takes them (the state waves: the intra waves' stages are longer).
-// The barrier after each wait publishes the landed data to the other role.
-constexpr bool STATE_LOADS = true;
+// One role (NWL waves) issues and awaits all global->LDS loads (issuing
+// stalls while the address units are busy); the barrier after each wait
+// publishes the landed data to the other role.  The intra waves take them:
+// the state waves have the longer stages and the higher register count.
+constexpr bool STATE_LOADS = false;
 constexpr int NWL = 4;
 constexpr int NB_QK = 2 * TILE / 1024 / NWL;   // 1 KB loads per loading wave per stage
 constexpr int NB_V = TILE / 1024 / NWL;
@@ -236,97 +238,105 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
   // per-wave choices are uniform offsets, so that each stage is one basic
   // block in which the compiler can overlap LDS latency with MFMA work.
 
-  // P tiles right of the even diagonal tiles, (0, 1) and (2, 3), lie inside
-  // the 32-token k-steps of P V and must read as zero; nothing else writes
-  // them, so they are cleared once.
-  for (int e = tid; e < 2 * 16 * 4; e += NTH) {
-    const int blk = e >> 6, r = (e >> 2) & 15, q = e & 3;   // tile, row, 4-column group
-    const int row = 32 * blk + r, col = 32 * blk + 16 + 4 * q;
-    *reinterpret_cast<uint2*>(sP + row * PROW + col) = make_uint2(0u, 0u);
-  }
-
-  // Intra wave W owns the causal score tiles n = it (it + 1) / 2 + jt with
-  // n = W mod 4: three for W < 2, two for W >= 2 (whose third slot repeats
-  // the second: identical P writes, and its row sum is never read).  Slot 0
-  // is tile (qt, 0) with qt = 0, 1, 3, 2 for W = 0..3 (wave 2 takes its
-  // tiles in the order 6, 2), so that the four waves' first slots cover the
-  // four query tiles.
-  int slot_it[3], slot_jt[3];
-  {
-    const int W = cg;
-    slot_it[0] = W == 0 ? 0 : W == 1 ? 1 : W == 2 ? 3 : 2;
-    slot_jt[0] = 0;
-    slot_it[1] = W == 0 ? 2 : W == 1 ? 2 : W == 2 ? 1 : 3;
-    slot_jt[1] = W == 0 ? 1 : W == 1 ? 2 : 1;
-    slot_it[2] = W == 0 ? 3 : W == 1 ? 3 : slot_it[1];
-    slot_jt[2] = W == 0 ? 2 : W == 1 ? 3 : slot_jt[1];
-  }
-  // row sums of P by (wave, slot): query tile it collects the slots below
-  __shared__ float sRs[4][3][16];
-  auto row_sum = [&](int it, int i16) {
-    switch (it) {
-      case 0: return sRs[0][0][i16];
-      case 1: return sRs[1][0][i16] + sRs[2][1][i16];
-      case 2: return (sRs[0][1][i16] + sRs[1][1][i16]) + sRs[3][0][i16];
-      default: return (sRs[0][2][i16] + sRs[1][2][i16]) + (sRs[2][0][i16] + sRs[3][1][i16]);
-    }
+  // row sums of P by (chunk parity, key tile, query tile)
+  __shared__ float sRs[2][NT][NT][16];
+  auto row_sum = [&](int par, int it, int i16) {
+    float r = sRs[par][0][it][i16];
+#pragma unroll
+    for (int jt = 1; jt < NT; ++jt)
+      if (jt <= it) r += sRs[par][jt][it][i16];
+    return r;
   };
 
-  // P = S (.) D for this wave's tiles of the chunk whose scores are in sp
-  // (gates in gb), and their row sums
-  auto finish_p = [&](const f32x4* sp, int gb) {
+  // P = S (.) D of key tile jt and query tiles it0, it0 + 1 of the chunk
+  // whose transposed scores are in sp[0..1], and their row sums; tiles above
+  // the diagonal come out as zeros.  The gate operands (from buffer gb) are
+  // read first, so that their LDS latency can be hidden.
+  struct POp {
+    float Mi[2];
+    float uj[4];
+  };
+  auto p_load = [&](int it0, int jt, int gb, POp& x) {
+    const float4 uj = *reinterpret_cast<const float4*>(&sGate[gb][0][jt * 16 + 4 * g]);
+    x.uj[0] = uj.x; x.uj[1] = uj.y; x.uj[2] = uj.z; x.uj[3] = uj.w;
 #pragma unroll
-    for (int k = 0; k < 3; ++k) {
-      const int it = slot_it[k], jt = slot_jt[k];
+    for (int r = 0; r < 2; ++r) x.Mi[r] = sGate[gb][1][(it0 + r) * 16 + l16];
+  };
+  auto finish_p = [&](const f32x4* sp, int it0, int jt, int par, const POp& x) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int it = it0 + r;
       const int i = it * 16 + l16;
-      const float Mi = sGate[gb][1][i];
-      const float4 uj = *reinterpret_cast<const float4*>(&sGate[gb][0][jt * 16 + 4 * g]);
-      const float ujv[4] = {uj.x, uj.y, uj.z, uj.w};
       float pe[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int j = jt * 16 + 4 * g + e;
-        const float pv = sp[k][e] * __expf(ujv[e] - Mi);
+        const float pv = sp[r][e] * __expf(x.uj[e] - x.Mi[r]);
         pe[e] = (j <= i) ? pv : 0.0f;
       }
       *reinterpret_cast<uint2*>(sP + i * PROW + jt * 16 + 4 * g) =
           make_uint2(cvt2(pe[0], pe[1]), cvt2(pe[2], pe[3]));
-      sRs[cg][k][l16] = sum_groups((pe[0] + pe[1]) + (pe[2] + pe[3]));
+      sRs[par][jt][it][l16] = sum_groups((pe[0] + pe[1]) + (pe[2] + pe[3]));
     }
   };
-  // h of query tiles it0, it0 + 1 of chunk cp (gates gb, o~ slot ob)
-  auto finish_out = [&](const bf16x8* vfr, int it0, int cp, int gb, int ob) {
+  // P V of query tiles it0, it0 + 1 onto their scaled readout
+  auto pv_tiles = [&](const bf16x8* vfr, int it0, f32x4* o) {
 #pragma unroll
-    for (int it = it0; it < it0 + 2; ++it) {
+    for (int r = 0; r < 2; ++r) {
+      const int it = it0 + r;
       const int i = it * 16 + l16;
-      f32x4 o = *reinterpret_cast<const f32x4*>(&sR[cg][it][lane][0]);
+      o[r] = *reinterpret_cast<const f32x4*>(&sR[cg][it][lane][0]);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         if (32 * ks <= it * 16 + 15) {
           const uint4 Pf = *reinterpret_cast<const uint4*>(sP + i * PROW + 32 * ks + 8 * g);
-          o = mfma16x16x32(vfr[ks], as_bf16x8(Pf), o);
+          o[r] = mfma16x16x32(vfr[ks], as_bf16x8(Pf), o[r]);
         }
       }
-      const float rs = row_sum(it, l16);
+    }
+  };
+  // h of query tiles it0, it0 + 1 of chunk cp in two steps: the reciprocal
+  // denominators and the o~ values (gates gb, o~ slot ob), then h from the
+  // numerators o
+  struct HOp {
+    float inv[2];
+    float ov[2][4];
+  };
+  auto h_prep = [&](int it0, int cp, int gb, int ob, HOp& x) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int it = it0 + r;
+      const int i = it * 16 + l16;
+      const float rs = row_sum(cp & 1, it, l16);
       const float den = fmaxf(fabsf(sGate[gb][2][i] * sQn[i] + rs), sGate[gb][3][i]);
-      const float inv = __builtin_amdgcn_rcpf(den);
+      x.inv[r] = __builtin_amdgcn_rcpf(den);
+      if (OM == O_F32) {
+        const float4 o4 = *reinterpret_cast<const float4*>(sO[ob] + i * 256 + 16 * ((cg * 4 + g) ^ (i & 15)));
+        x.ov[r][0] = o4.x; x.ov[r][1] = o4.y; x.ov[r][2] = o4.z; x.ov[r][3] = o4.w;
+      } else if (OM == O_BF16) {
+        const uint2 o2 = *reinterpret_cast<const uint2*>(sO[ob] + swz(i, cg * 16 + 4 * g));
+        x.ov[r][0] = bf_lo(o2.x); x.ov[r][1] = bf_hi(o2.x); x.ov[r][2] = bf_lo(o2.y); x.ov[r][3] = bf_hi(o2.y);
+      }
+    }
+  };
+  auto h_store = [&](const f32x4* o, const HOp& x, int it0, int cp) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int i = (it0 + r) * 16 + l16;
       float hv[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) hv[e] = o[e] * inv;
+      for (int e = 0; e < 4; ++e) hv[e] = o[r][e] * x.inv[r];
       if (OM != O_NONE) {
-        float ov[4];
-        if (OM == O_F32) {
-          const float4 o4 = *reinterpret_cast<const float4*>(sO[ob] + i * 256 + 16 * ((cg * 4 + g) ^ (i & 15)));
-          ov[0] = o4.x; ov[1] = o4.y; ov[2] = o4.z; ov[3] = o4.w;
-        } else {
-          const uint2 o2 = *reinterpret_cast<const uint2*>(sO[ob] + swz(i, cg * 16 + 4 * g));
-          ov[0] = bf_lo(o2.x); ov[1] = bf_hi(o2.x); ov[2] = bf_lo(o2.y); ov[3] = bf_hi(o2.y);
-        }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) hv[e] *= sigmoid_fast(ov[e]);
+        for (int e = 0; e < 4; ++e) hv[e] *= sigmoid_fast(x.ov[r][e]);
       }
       st8_nt(gh + (static_cast<int64_t>(cp) * L + i) * dv, cvt2(hv[0], hv[1]), cvt2(hv[2], hv[3]));
     }
+  };
+  auto h_tiles = [&](const f32x4* o, int it0, int cp, int gb, int ob) {
+    HOp x;
+    h_prep(it0, cp, gb, ob, x);
+    h_store(o, x, it0, cp);
   };
   // value fragments (V^T, this wave's 16 columns) of the chunk in sV
   auto load_vf = [&](bf16x8* dst, uint2* raw) {
@@ -382,7 +392,9 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
     float sig = 1.0f;    // C~ = sig * cacc
     f32x4 outT[NT];
     bf16x8 wVf[NKS];
-    int gb = 0, gbn = 1;   // gate buffers of chunks c, c + 1
+    // transposed score tiles S^T = K Q^T of key tile W and every query tile
+    f32x4 sacc[NT], sp23[2];
+    int gb = 0, gbn = 1, gbp = 2;   // gate buffers of chunks c, c + 1, c - 1
     for (int c = 0; c < nchunks; ++c) {
       const float gL = sGate[gb][2][L - 1];
       const bool renorm = gL * sig < 0x1p-64f;
@@ -410,18 +422,31 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
             wVf[ks] = cvt8(xw);
           }
 #pragma unroll
-          for (int it = 0; it < NT; ++it) outT[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int it = 0; it < NT; ++it) {
+            outT[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+            sacc[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
         }
         // ---- the stage's LDS reads are issued ahead of the arithmetic that
         // consumes them (reads return in order, so each MFMA waits only for
-        // its own operands): Q and K fragments, then the readout MFMAs, then
-        // the update MFMAs
-        uint4 Qf[2][NT];
+        // its own operands): Q and K fragments, then the score and readout
+        // MFMAs, then the update MFMAs
+        uint4 Qf[2][NT], Kf[2];
         uint2 Klo[NKS][AS / 16], Khi[NKS][AS / 16];
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
 #pragma unroll
           for (int it = 0; it < NT; ++it) Qf[p][it] = lds_ld16(Qb, swz(it * 16 + l16, 32 * p + 8 * g));
+          Kf[p] = lds_ld16(Kb, W * 2048 + swz(l16, 32 * p + 8 * g));
+        }
+        // gate operands of this stage's P pass and scaled readout
+        POp pop;
+        float gi4[NT];
+        if (s == 0) p_load(2, W, gbp, pop);
+        if (s == NS - 1) {
+          p_load(0, W, gb, pop);
+#pragma unroll
+          for (int it = 0; it < NT; ++it) gi4[it] = sGate[gb][2][it * 16 + l16];
         }
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
@@ -433,6 +458,14 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
           }
         }
         __builtin_amdgcn_sched_barrier(0);
+        // score tiles over the slice first (P at the last stage waits only
+        // for them; above-diagonal tiles are included and masked with P)
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+#pragma unroll
+          for (int it = 0; it < NT; ++it)
+            sacc[it] = mfma16x16x32(as_bf16x8(Kf[p]), as_bf16x8(Qf[p][it]), sacc[it]);
+        }
         // readout: query tiles x the slice's two 32-row k-steps
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
@@ -473,10 +506,17 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
         if (s == NS - 1) {
           // scaled readout for the intra waves
 #pragma unroll
-          for (int it = 0; it < NT; ++it) {
-            const float gi_ = sGate[gb][2][it * 16 + l16];
-            *reinterpret_cast<f32x4*>(&sR[W][it][lane][0]) = outT[it] * (gi_ * sig);
-          }
+          for (int it = 0; it < NT; ++it)
+            *reinterpret_cast<f32x4*>(&sR[W][it][lane][0]) = outT[it] * (gi4[it] * sig);
+        }
+        // P of the chunk: query tiles 0, 1 at the last stage (read from
+        // stage 1 of the next chunk on), tiles 2, 3 at stage 0 of the next
+        // chunk (read from its stage 2 on)
+        if (s == 0 && c > 0) finish_p(sp23, 2, W, (c - 1) & 1, pop);
+        if (s == NS - 1) {
+          finish_p(sacc, 0, W, c & 1, pop);
+          sp23[0] = sacc[2];
+          sp23[1] = sacc[3];
         }
         // gates of the next chunk (staged two chunks ahead)
         if (s == 1 && wave == 0) m_n2 = scan_gates((c + 1) & 1, gbn, m_n1, sig_new);
@@ -484,12 +524,18 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
       m_s = m_n1;
       m_n1 = m_n2;
       sig = sig_new;
+      gbp = gb;
       gb = gbn;
       gbn = (gbn == 2) ? 0 : gbn + 1;
     }
-    // ---- drain
+    // ---- drain: P of the last chunk's query tiles 2, 3
     if (STATE_LOADS) wait_vm<0>();
     __syncthreads();
+    {
+      POp pop;
+      p_load(2, W, gbp, pop);
+      finish_p(sp23, 2, W, (nchunks - 1) & 1, pop);
+    }
     __syncthreads();
     if (a.C1) {
 #pragma unroll
@@ -507,31 +553,23 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
     }
   } else {
     const int W = cg;
-    // this wave's score-tile slots as uniform LDS offsets of the Q and K rows
-    int qoff[3], koff[3];
-#pragma unroll
-    for (int k = 0; k < 3; ++k) {
-      qoff[k] = slot_it[k] * 2048;
-      koff[k] = slot_jt[k] * 2048;
-    }
-    // q.n~ of query tile qt, from the Q fragments of slot 0
-    const int qt = slot_it[0];
+    // q.n~ of query tile qt = W
+    const int qt = W;
     // n~ increments: this wave covers the rows of tile W of every slice
     // (every lane of a 16-lane column holds the same value)
     const int nrow = 32 * (W >> 1) + 8 * (l16 >> 2) + 4 * (W & 1) + (l16 & 3);
     const int ncol = 32 * (W >> 1) + 8 * kq + 4 * (W & 1);   // its K^T fragment column
-    float nn[NS];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) nn[s] = 0.0f;
+    // MFMA results are consumed one stage after their issue: the n~
+    // increment of the previous slice, q.n~ of the previous chunk, the
+    // numerators of two query tiles of chunk c - 1
+    f32x4 niP = f32x4{0.f, 0.f, 0.f, 0.f};
     f32x4 qn = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 oacc[2];
+    HOp hx;
     uint4 Wx[NKS];   // w terms of the current chunk (A operand, see below)
-    float gL_prev = 1.0f;   // with nn = 0: the update before chunk 0 keeps n~
-    // score tiles of the current and the previous chunk, value fragments
-    // of both
-    f32x4 sacc[3], sprev[3];
+    float gL_prev = 1.0f;   // with niP = 0: the update before chunk 0 keeps n~
+    // value fragments of the current and the previous chunk
     bf16x8 Vf[NKS], Vp[NKS];
-#pragma unroll
-    for (int k = 0; k < 3; ++k) sacc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
     int gb = 0, gbp = 2;   // gate buffers of chunks c, c - 1
     for (int c = 0; c < nchunks; ++c) {
       // (wave-uniform: kept in a scalar register)
@@ -543,36 +581,20 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
         const char* Kb = sRing[slot][1];
         if (s == 0) {
 #pragma unroll
-          for (int k = 0; k < 3; ++k) {
-            sprev[k] = sacc[k];
-            sacc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-          }
-#pragma unroll
           for (int ks = 0; ks < NKS; ++ks) Vp[ks] = Vf[ks];
           uint2 raw[2 * NKS];
           load_vf(Vf, raw);
+          // q.n~ of chunk c - 1 (its outputs are finished from stage 2 on)
+          if (c > 0) sQn[qt * 16 + l16] = (qn[0] + qn[1]) + qn[2];
           qn = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int ks = 0; ks < NKS; ++ks)
             Wx[ks] = *reinterpret_cast<const uint4*>(&sWs[gb][l16 & 3][32 * ks + 8 * g]);
         }
-        // score tiles over the slice (operands first, see the state role)
-        uint4 Qf[2][3], Kf[2][3];
+        // Q fragments of query tile qt over the slice
+        uint4 Qf[2];
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-#pragma unroll
-          for (int k = 0; k < 3; ++k) {
-            Qf[p][k] = lds_ld16(Qb, qoff[k] + swz(l16, 32 * p + 8 * g));
-            Kf[p][k] = lds_ld16(Kb, koff[k] + swz(l16, 32 * p + 8 * g));
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-#pragma unroll
-          for (int k = 0; k < 3; ++k)
-            sacc[k] = mfma16x16x32(as_bf16x8(Kf[p][k]), as_bf16x8(Qf[p][k]), sacc[k]);
-        }
+        for (int p = 0; p < 2; ++p) Qf[p] = lds_ld16(Qb, qt * 2048 + swz(l16, 32 * p + 8 * g));
         // q.n~ and the n~ increment as MFMAs whose A operand holds the
         // vector (n~, w) split into three bf16 terms, in rows 4r, 4r+1,
         // 4r+2 (row 4r+3 is zero): with B = the Q fragment, D[4r+e][c] is
@@ -596,42 +618,50 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
         const float nprev = sN[nprow];
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int p = 0; p < 2; ++p) qn = mfma16x16x32(as_bf16x8(Nx[p]), as_bf16x8(Qf[p][0]), qn);
+        for (int p = 0; p < 2; ++p) qn = mfma16x16x32(as_bf16x8(Nx[p]), as_bf16x8(Qf[p]), qn);
         f32x4 ni = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) ni = mfma16x16x32(as_bf16x8(Wx[ks]), join(Klo[ks], Khi[ks]), ni);
         {
-          const float nv = (s > 0 ? gL : gL_prev) * nprev + nn[sp_];
+          const float nv = (s > 0 ? gL : gL_prev) * nprev + ((niP[0] + niP[1]) + niP[2]);
           sN[nprow] = nv;
           split3_bf16(nv, sNs[0][nprow], sNs[1][nprow], sNs[2][nprow]);
         }
-        nn[s] = (ni[0] + ni[1]) + ni[2];
+        niP = ni;
         __builtin_amdgcn_sched_barrier(0);
-        // finishing of the previous chunk (in chunk 0 the P pass works on
-        // zeros and its results are never read)
-        if (s == 0) finish_p(sprev, gbp);
-        if (s == 1 || s == 2) {
-          if (c > 0) finish_out(Vp, 2 * (s - 1), c - 1, gbp, (c - 1) & 1);
+        // finishing of chunk c - 1: P V of query tiles 0, 1 at stage 1, their
+        // h and P V of tiles 2, 3 at stage 2, the operands of their h at
+        // stage 3 and the h itself at stage 0 of the next chunk
+        if (s == 0 && c > 1) h_store(oacc, hx, 2, c - 2);
+        if (c > 0) {
+          if (s == 1) pv_tiles(Vp, 0, oacc);
+          if (s == 2) {
+            h_tiles(oacc, 0, c - 1, gbp, (c - 1) & 1);
+            pv_tiles(Vp, 2, oacc);
+          }
+          if (s == 3) h_prep(2, c - 1, gbp, (c - 1) & 1, hx);
         }
-        // this chunk's q.n~ of query tile qt, read from stage 1 of the next
-        // chunk on (after the previous chunk's outputs are done)
-        if (s == NS - 1) sQn[qt * 16 + l16] = (qn[0] + qn[1]) + qn[2];
       }
       gL_prev = gL;
       gbp = gb;
       gb = (gb == 2) ? 0 : gb + 1;
     }
-    // ---- drain: finish the last chunk (and the n~ rows of its last slice)
+    // ---- drain: finish the last two chunks (and the n~ rows of the last
+    // slice)
     if (!STATE_LOADS) wait_vm<0>();
+    if (nchunks > 1) h_store(oacc, hx, 2, nchunks - 2);
     {
       const int arow = (NS - 1) * AS + nrow;
-      sN[arow] = gL_prev * sN[arow] + nn[NS - 1];   // (its bf16 terms are not read again)
+      sN[arow] = gL_prev * sN[arow] + ((niP[0] + niP[1]) + niP[2]);   // (its bf16 terms are not read again)
     }
     __syncthreads();
-    finish_p(sacc, gbp);
+    sQn[qt * 16 + l16] = (qn[0] + qn[1]) + qn[2];
     __syncthreads();
-    finish_out(Vf, 0, nchunks - 1, gbp, (nchunks - 1) & 1);
-    finish_out(Vf, 2, nchunks - 1, gbp, (nchunks - 1) & 1);
+#pragma unroll
+    for (int it0 = 0; it0 < NT; it0 += 2) {
+      pv_tiles(Vf, it0, oacc);
+      h_tiles(oacc, it0, nchunks - 1, gbp, (nchunks - 1) & 1);
+    }
   }
 }
 
