@@ -193,26 +193,46 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
     dma4(gf + static_cast<int64_t>(cn) * L + lane, lds_addr(&sGin[c & 1][1][0]));
   };
 
-  // Gate scan of one chunk (wave 0) from raw gates gin into sGate[gb].  ms is
-  // m before the chunk, sg the state scale before it; returns m after it.
+  // Gate scan of one chunk from raw gates gin into sGate[gb], in four parts
+  // (part k runs at stage k of the previous chunk, so that no stage carries
+  // the whole dependency chain).  ms is m before the chunk, sg the state
+  // scale before it; the last part returns m after it.
+  struct GScan {
+    float xi, lf, bcum, u, Mx, ML, bL;
+  };
+  auto scan_part = [&](int part, int gin, int gb, float ms, float sg, GScan& x) {
+    float m_after = 0.0f;
+    if (part == 0) {
+      x.xi = sGin[gin][0][lane];
+      x.lf = log_forget_fast(sGin[gin][1][lane], a.fgate_exp);
+    } else if (part == 1) {
+      x.bcum = scan_add(x.lf);
+      x.u = x.xi - x.bcum;
+    } else if (part == 2) {
+      x.Mx = fmaxf(ms, scan_max(x.u));
+      x.ML = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x.Mx), L - 1));
+      x.bL = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x.bcum), L - 1));
+    } else {
+      const float gv_ = __expf(ms - x.Mx);
+      const float wv = __expf(x.u - x.ML);
+      const float gLn = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gv_), L - 1));
+      const float sg_new = gLn * sg < 0x1p-64f ? 1.0f : gLn * sg;
+      sGate[gb][0][lane] = x.u;
+      sGate[gb][1][lane] = x.Mx;
+      sGate[gb][2][lane] = gv_;
+      split3_bf16(wv, sWs[gb][0][lane], sWs[gb][1][lane], sWs[gb][2][lane]);
+      sGate[gb][3][lane] = __expf(-(x.bcum + x.Mx));
+      sGate[gb][4][lane] = wv * __builtin_amdgcn_rcpf(sg_new);
+      m_after = x.bL + x.ML;
+    }
+    return m_after;
+  };
   auto scan_gates = [&](int gin, int gb, float ms, float sg) {
-    const float lf = log_forget_fast(sGin[gin][1][lane], a.fgate_exp);
-    const float bcum = scan_add(lf);
-    const float u = sGin[gin][0][lane] - bcum;
-    const float Mx = fmaxf(ms, scan_max(u));
-    const float ML = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, Mx), L - 1));
-    const float bL = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bcum), L - 1));
-    const float gv_ = __expf(ms - Mx);
-    const float wv = __expf(u - ML);
-    const float gLn = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gv_), L - 1));
-    const float sg_new = gLn * sg < 0x1p-64f ? 1.0f : gLn * sg;
-    sGate[gb][0][lane] = u;
-    sGate[gb][1][lane] = Mx;
-    sGate[gb][2][lane] = gv_;
-    split3_bf16(wv, sWs[gb][0][lane], sWs[gb][1][lane], sWs[gb][2][lane]);
-    sGate[gb][3][lane] = __expf(-(bcum + Mx));
-    sGate[gb][4][lane] = wv * (1.0f / sg_new);
-    return bL + ML;
+    GScan x;
+    float m_after = 0.0f;
+#pragma unroll
+    for (int part = 0; part < 4; ++part) m_after = scan_part(part, gin, gb, ms, sg, x);
+    return m_after;
   };
 
   // ---- prologue
@@ -227,8 +247,10 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
     wait_vm<0>();
   }
   __syncthreads();
-  float m_n1 = 0.0f;   // m after the current chunk (wave 0)
-  if (wave == 0) m_n1 = scan_gates(0, 0, m_s, 1.0f);
+  // the gate scans run on state wave 0 (SCAN_WAVE)
+  constexpr int SCAN_WAVE = 0;
+  float m_n1 = 0.0f;   // m after the current chunk (scan wave)
+  if (wave == SCAN_WAVE) m_n1 = scan_gates(0, 0, m_s, 1.0f);
   __syncthreads();
 
   const int vr = l16 >> 2, vq = l16 & 3;
@@ -396,13 +418,20 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
     f32x4 sacc[NT], sp23[2];
     int gb = 0, gbn = 1, gbp = 2;   // gate buffers of chunks c, c + 1, c - 1
     for (int c = 0; c < nchunks; ++c) {
-      const float gL = sGate[gb][2][L - 1];
-      const bool renorm = gL * sig < 0x1p-64f;
-      const float sig_new = renorm ? 1.0f : gL * sig;
+      // the chunk's gates are read after the first stage's barrier (the
+      // scan that writes them ends one stage earlier)
+      float gL = 0.0f, sig_new = 0.0f;
+      bool renorm = false;
       float m_n2 = 0.0f;
+      GScan gsc;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const int slot = stage_top_state(c, s);
+        if (s == 0) {
+          gL = sGate[gb][2][L - 1];
+          renorm = gL * sig < 0x1p-64f;
+          sig_new = renorm ? 1.0f : gL * sig;
+        }
         const char* Qb = sRing[slot][0];
         const char* Kb = sRing[slot][1];
         if (s == 0) {
@@ -518,8 +547,11 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
           sp23[0] = sacc[2];
           sp23[1] = sacc[3];
         }
-        // gates of the next chunk (staged two chunks ahead)
-        if (s == 1 && wave == 0) m_n2 = scan_gates((c + 1) & 1, gbn, m_n1, sig_new);
+        // gate scan of the next chunk, a quarter per stage
+        if (wave == SCAN_WAVE) {
+          const float mp = scan_part(s, (c + 1) & 1, gbn, m_n1, sig_new, gsc);
+          if (s == NS - 1) m_n2 = mp;
+        }
       }
       m_s = m_n1;
       m_n1 = m_n2;
@@ -573,10 +605,15 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
     int gb = 0, gbp = 2;   // gate buffers of chunks c, c - 1
     for (int c = 0; c < nchunks; ++c) {
       // (wave-uniform: kept in a scalar register)
-      const float gL = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sGate[gb][2][L - 1])));
+      // (read after the first stage's barrier, as in the state role)
+      float gL = 0.0f;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const int slot = stage_top_intra(c, s);
+        if (s == 0) {
+          // (wave-uniform: kept in a scalar register)
+          gL = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sGate[gb][2][L - 1])));
+        }
         const char* Qb = sRing[slot][0];
         const char* Kb = sRing[slot][1];
         if (s == 0) {
