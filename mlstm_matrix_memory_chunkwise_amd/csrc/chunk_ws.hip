@@ -194,7 +194,7 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
   };
 
   // Gate scan of one chunk from raw gates gin into sGate[gb], in four parts
-  // (part k runs at stage k of the previous chunk, so that no stage carries
+  // (spread over the stages of the previous chunk, so that no stage carries
   // the whole dependency chain).  ms is m before the chunk, sg the state
   // scale before it; the last part returns m after it.
   struct GScan {
@@ -301,13 +301,17 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
       sRs[par][jt][it][l16] = sum_groups((pe[0] + pe[1]) + (pe[2] + pe[3]));
     }
   };
-  // P V of query tiles it0, it0 + 1 onto their scaled readout
-  auto pv_tiles = [&](const bf16x8* vfr, int it0, f32x4* o) {
+  // P V of query tiles it0, it0 + 1 onto their scaled readout, in two steps
+  // (the readout can be read a stage before the products)
+  auto pv_init = [&](int it0, f32x4* o) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) o[r] = *reinterpret_cast<const f32x4*>(&sR[cg][it0 + r][lane][0]);
+  };
+  auto pv_mma = [&](const bf16x8* vfr, int it0, f32x4* o) {
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int it = it0 + r;
       const int i = it * 16 + l16;
-      o[r] = *reinterpret_cast<const f32x4*>(&sR[cg][it][lane][0]);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         if (32 * ks <= it * 16 + 15) {
@@ -316,6 +320,10 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
         }
       }
     }
+  };
+  auto pv_tiles = [&](const bf16x8* vfr, int it0, f32x4* o) {
+    pv_init(it0, o);
+    pv_mma(vfr, it0, o);
   };
   // h of query tiles it0, it0 + 1 of chunk cp in two steps: the reciprocal
   // denominators and the o~ values (gates gb, o~ slot ob), then h from the
@@ -547,10 +555,15 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
           sp23[0] = sacc[2];
           sp23[1] = sacc[3];
         }
-        // gate scan of the next chunk, a quarter per stage
+        // gate scan of the next chunk: part 0 at stage 0, parts 1 and 2 at
+        // stage 1, part 3 at stage 2 (the last stage carries the P pass)
         if (wave == SCAN_WAVE) {
-          const float mp = scan_part(s, (c + 1) & 1, gbn, m_n1, sig_new, gsc);
-          if (s == NS - 1) m_n2 = mp;
+          if (s == 0) scan_part(0, (c + 1) & 1, gbn, m_n1, sig_new, gsc);
+          if (s == 1) {
+            scan_part(1, (c + 1) & 1, gbn, m_n1, sig_new, gsc);
+            scan_part(2, (c + 1) & 1, gbn, m_n1, sig_new, gsc);
+          }
+          if (s == 2) m_n2 = scan_part(3, (c + 1) & 1, gbn, m_n1, sig_new, gsc);
         }
       }
       m_s = m_n1;
@@ -667,16 +680,19 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
         niP = ni;
         __builtin_amdgcn_sched_barrier(0);
         // finishing of chunk c - 1: P V of query tiles 0, 1 at stage 1, their
-        // h and P V of tiles 2, 3 at stage 2, the operands of their h at
-        // stage 3 and the h itself at stage 0 of the next chunk
+        // h at stage 2, P V of tiles 2, 3 and the operands of their h at
+        // stage 3, and that h at stage 0 of the next chunk
         if (s == 0 && c > 1) h_store(oacc, hx, 2, c - 2);
         if (c > 0) {
           if (s == 1) pv_tiles(Vp, 0, oacc);
           if (s == 2) {
             h_tiles(oacc, 0, c - 1, gbp, (c - 1) & 1);
-            pv_tiles(Vp, 2, oacc);
+            pv_init(2, oacc);   // (the state waves rewrite the readout at stage 3)
           }
-          if (s == 3) h_prep(2, c - 1, gbp, (c - 1) & 1, hx);
+          if (s == 3) {
+            pv_mma(Vp, 2, oacc);
+            h_prep(2, c - 1, gbp, (c - 1) & 1, hx);
+          }
         }
       }
       gL_prev = gL;
