@@ -16,6 +16,12 @@ unrolled-sum form evaluated in 50-digit arithmetic (``unrolled_mp``), against
 a numpy fp64 evaluation of the quadratic parallel form, against causal linear
 attention, against the closed form of the stabilizer, and against the
 split/resume and stabilizer-shift invariants.
+
+The gradient of the forward pass (``backward``) lives in
+``mlstm_oracle_bwd.c``: reverse mode through the recurrence in true units.
+Parity status: pinned, against central finite differences of the forward
+recurrence, the closed form of one token, the closed form of causal linear
+attention, and planted mistakes (``tests/test_oracle_bwd.py``).
 """
 from __future__ import annotations
 
@@ -28,6 +34,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "mlstm_oracle.c")
+_SRC_BWD = os.path.join(_HERE, "mlstm_oracle_bwd.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 FGATE_SIGMOID = 0
@@ -43,20 +50,24 @@ def build() -> str:
     library travels to other hosts).
     """
     cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
-           "-Wall", "-Wextra", "-o", _LIB + ".tmp", _SRC, "-lm"]
+           "-Wall", "-Wextra", "-o", _LIB + ".tmp", _SRC, _SRC_BWD, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(_LIB + ".tmp", _LIB)
     return _LIB
 
 
-def build_variant(src_text: str, out_path: str) -> str:
+def build_variant(src_text: str, out_path: str, bwd_text: Optional[str] = None) -> str:
     """Compile an edited copy of the oracle source (used by the test that
-    plants mistakes in the oracle to show that its pins catch them)."""
+    plants mistakes in the oracle to show that its pins catch them).
+    ``bwd_text`` replaces the gradient source the same way (default: as is)."""
     src = out_path + ".c"
     with open(src, "w") as fh:
         fh.write(src_text)
+    src_b = out_path + "_bwd.c"
+    with open(src_b, "w") as fh:
+        fh.write(bwd_source_text() if bwd_text is None else bwd_text)
     subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
-                    "-o", out_path, src, "-lm"], check=True)
+                    "-o", out_path, src, src_b, "-lm"], check=True)
     return out_path
 
 
@@ -65,11 +76,17 @@ def source_text() -> str:
         return fh.read()
 
 
+def bwd_source_text() -> str:
+    with open(_SRC_BWD) as fh:
+        return fh.read()
+
+
 def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+    if (not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)
+            or os.path.getmtime(_LIB) < os.path.getmtime(_SRC_BWD)):
         build()
     _lib = load_library(_LIB)
     return _lib
@@ -88,6 +105,8 @@ def load_library(path: str):
     lib.oracle_step.restype = None
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ctypes.c_int
+    lib.oracle_backward.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int] + [P] * 21 + [ctypes.c_int]
+    lib.oracle_backward.restype = None
     return lib
 
 
@@ -172,3 +191,37 @@ def step(q, k, v, i_pre, f_pre, o_pre, C, n, m, fgate="sigmoid",
                     _ptr(i_pre), _ptr(f_pre), _ptr(o_pre), _ptr(C), _ptr(n),
                     _ptr(m), _ptr(h), int(nthreads))
     return h, C, n, m
+
+
+def backward(q, k, v, i_pre, f_pre, o_pre, C0, n0, m0, dh, dC1=None, dn1=None,
+             fgate="sigmoid", nthreads: int = 0, lib=None):
+    """Gradient of L = sum dh . h + e^{-m_T} (<dC1, C_T> + <dn1, n_T>) (see
+    ``mlstm_oracle_bwd.c``) with respect to every input of the forward pass.
+
+    Shapes as in ``recurrent``; dh like v; dC1 [B,H,dqk,dv], dn1 [B,H,dqk] or
+    both None.  Returns a dict of float64 arrays: dq, dk, dv, di, df, do (None
+    without o~), dC0, dn0, dm0 (the initial-state gradients in its stored
+    scale; computed for the zero state too).
+    """
+    lib = lib or _load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    i_pre, f_pre, o_pre = _f64(i_pre), _f64(f_pre), _f64(o_pre)
+    C0, n0, m0 = _f64(C0), _f64(n0), _f64(m0)
+    dh, dC1, dn1 = _f64(dh), _f64(dC1), _f64(dn1)
+    if (C0 is None) != (n0 is None) or (C0 is None) != (m0 is None):
+        raise ValueError("initial state must be given whole or not at all")
+    if (dC1 is None) != (dn1 is None):
+        raise ValueError("final-state gradient must be given whole or not at all")
+    B, H, T, dqk = q.shape
+    dv = v.shape[-1]
+    assert dh.shape == (B, H, T, dv)
+    out = dict(dq=np.empty((B, H, T, dqk)), dk=np.empty((B, H, T, dqk)),
+               dv=np.empty((B, H, T, dv)), di=np.empty((B, H, T)), df=np.empty((B, H, T)),
+               do=None if o_pre is None else np.empty((B, H, T, dv)),
+               dC0=np.empty((B, H, dqk, dv)), dn0=np.empty((B, H, dqk)), dm0=np.empty((B, H)))
+    lib.oracle_backward(B, H, T, dqk, dv, fgate_code(fgate), _ptr(q), _ptr(k), _ptr(v),
+                        _ptr(i_pre), _ptr(f_pre), _ptr(o_pre), _ptr(C0), _ptr(n0), _ptr(m0),
+                        _ptr(dh), _ptr(dC1), _ptr(dn1), _ptr(out["dq"]), _ptr(out["dk"]),
+                        _ptr(out["dv"]), _ptr(out["di"]), _ptr(out["df"]), _ptr(out["do"]),
+                        _ptr(out["dC0"]), _ptr(out["dn0"]), _ptr(out["dm0"]), int(nthreads))
+    return out
