@@ -140,6 +140,52 @@ mlstm_status_t mlstm_step(const mlstm_problem_t* p, const void* q,
                           const float* m_in, float* C_out, float* n_out,
                           float* m_out, void* h, void* stream);
 
+/*
+ * Chunkwise backward pass: the gradient of the forward pass of
+ * mlstm_fwd_chunkwise (same problem and inputs) for the scalar
+ *   L = sum_t dh_t . h_t + e^{-m_T} (<dC1, C_T> + <dn1, n_T>),
+ * where h is the forward output, C_T = C~_T e^{m_T} and n_T = n~_T e^{m_T} the
+ * true final memory and m_T the final running maximum (held constant): dC1,
+ * dn1 are gradients of the final memory in the scale of the stored final
+ * state.  The pages print no gradient; this is the derivative of the
+ * forward pass of section 3, "Associative Matrix Cell State" and "The
+ * Parallel Dual Form", with the gates of section 2.
+ *   q..m0: as for mlstm_fwd_chunkwise (C0, n0, m0 all NULL or all set).
+ *   h: the forward output of the same call, [B,H,T,d_v], qkv_dtype.
+ *   dh: [B,H,T,d_v], qkv_dtype.  dC1 [B,H,d_qk,d_v], dn1 [B,H,d_qk]: both
+ *   NULL (zero) or both set.
+ *   Outputs, all float32: dq, dk [B,H,T,d_qk]; dv [B,H,T,d_v]; di, df
+ *   [B,H,T] (gradients of the preactivations i~, f~); d_o [B,H,T,d_v]
+ *   (required exactly when o_pre is given); dC0 [B,H,d_qk,d_v], dn0
+ *   [B,H,d_qk], dm0 [B,H] (may each be NULL): the initial-state gradients in
+ *   its stored scale, dC0 = e^{m0} dL/dC_0, dn0 = e^{m0} dL/dn_0, and dm0 the
+ *   derivative through the factor e^{m0} (zero without an initial state).
+ *   Outputs must not overlap inputs or each other.
+ *   workspace: device scratch of at least
+ *   mlstm_bwd_chunkwise_workspace_bytes (it holds the state at every chunk
+ *   boundary and per-column-block partial sums: about
+ *   B*H*(T/chunk+1)*d_qk*d_v*4 + 2*(d_v/32)*B*H*T*d_qk*4 bytes), 16-byte
+ *   aligned, not overlapping any argument.
+ * Supported: chunk 16 or 32 (T a multiple of it) and d_qk <= 256; otherwise
+ * MLSTM_ERR_UNSUPPORTED.  The result does not depend on chunk beyond
+ * rounding.
+ */
+mlstm_status_t mlstm_bwd_chunkwise(const mlstm_problem_t* p, int64_t chunk,
+                                   const void* q, const void* k, const void* v,
+                                   const float* i_pre, const float* f_pre,
+                                   const void* o_pre, const float* C0,
+                                   const float* n0, const float* m0,
+                                   const void* h, const void* dh,
+                                   const float* dC1, const float* dn1,
+                                   float* dq, float* dk, float* dv, float* di,
+                                   float* df, float* d_o, float* dC0,
+                                   float* dn0, float* dm0, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/* Workspace needed by mlstm_bwd_chunkwise for this problem (bytes). */
+mlstm_status_t mlstm_bwd_chunkwise_workspace_bytes(const mlstm_problem_t* p,
+                                                   int64_t chunk, size_t* bytes);
+
 /* Static description of a status code. */
 const char* mlstm_status_string(mlstm_status_t s);
 

@@ -25,7 +25,8 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = [
-    "mlstm_fwd_chunkwise", "mlstm_fwd_parallel", "mlstm_step",
+    "mlstm_fwd_chunkwise", "mlstm_fwd_parallel", "mlstm_step", "mlstm_bwd_chunkwise",
+    "mlstm_bwd_chunkwise_workspace_bytes",
     "mlstm_fwd_chunkwise_workspace_bytes", "mlstm_fwd_parallel_workspace_bytes",
     "mlstm_version", "library_path", "load_library", "MLSTMError",
     "MLSTM_OK", "MLSTM_ERR_INVALID_ARG", "MLSTM_ERR_UNSUPPORTED", "MLSTM_ERR_DEVICE",
@@ -87,6 +88,10 @@ def load_library():
     lib.mlstm_fwd_chunkwise_workspace_bytes.restype = ctypes.c_int
     lib.mlstm_fwd_parallel_workspace_bytes.argtypes = [PP, ctypes.POINTER(sz)]
     lib.mlstm_fwd_parallel_workspace_bytes.restype = ctypes.c_int
+    lib.mlstm_bwd_chunkwise.argtypes = [PP, i64] + [vp] * 23 + [sz, vp]
+    lib.mlstm_bwd_chunkwise.restype = ctypes.c_int
+    lib.mlstm_bwd_chunkwise_workspace_bytes.argtypes = [PP, i64, ctypes.POINTER(sz)]
+    lib.mlstm_bwd_chunkwise_workspace_bytes.restype = ctypes.c_int
     lib.mlstm_status_string.argtypes = [ctypes.c_int]
     lib.mlstm_status_string.restype = ctypes.c_char_p
     lib.mlstm_last_error_detail.argtypes = []
@@ -234,6 +239,53 @@ def mlstm_fwd_parallel(q, k, v, i_pre, f_pre, o_pre=None, C0=None, n0=None, m0=N
                                   workspace.numel() * workspace.element_size(),
                                   _stream_handle(stream)))
     return h, ((C1, n1, m1) if return_state else None)
+
+
+def mlstm_bwd_chunkwise_workspace_bytes(p: Problem, chunk: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().mlstm_bwd_chunkwise_workspace_bytes(ctypes.byref(p), int(chunk),
+                                                              ctypes.byref(n)))
+    return int(n.value)
+
+
+def mlstm_bwd_chunkwise(q, k, v, i_pre, f_pre, o_pre, C0, n0, m0, h, dh, dC1=None, dn1=None, *,
+                        chunk: int = 32, fgate="sigmoid", workspace: Optional[torch.Tensor] = None,
+                        stream=None):
+    """Chunkwise backward pass (see mlstm_bwd_chunkwise in include/mlstm.h).
+
+    h is the forward output of the same inputs; dh its gradient (same dtype);
+    dC1, dn1 the gradient of the final memory in the stored final scale, or
+    None.  Returns a dict of float32 tensors dq, dk, dv, di, df, do (None
+    without o_pre), dC0, dn0, dm0.
+    """
+    lib = load_library()
+    p, (q, k, v, i_pre, f_pre, o_pre, C0, n0, m0) = _seq_problem(
+        q, k, v, i_pre, f_pre, o_pre, C0, n0, m0, fgate)
+    B, H, T, dqk, dv = p.B, p.H, p.T, p.d_qk, p.d_v
+    dev = q.device
+    h = _dev_tensor("h", h, q.dtype, (B, H, T, dv), dev)
+    dh = _dev_tensor("dh", dh, q.dtype, (B, H, T, dv), dev)
+    dC1 = _dev_tensor("dC1", dC1, torch.float32, (B, H, dqk, dv), dev)
+    dn1 = _dev_tensor("dn1", dn1, torch.float32, (B, H, dqk), dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = dict(dq=torch.empty((B, H, T, dqk), **f32), dk=torch.empty((B, H, T, dqk), **f32),
+             dv=torch.empty((B, H, T, dv), **f32), di=torch.empty((B, H, T), **f32),
+             df=torch.empty((B, H, T), **f32),
+             do=None if o_pre is None else torch.empty((B, H, T, dv), **f32),
+             dC0=torch.empty((B, H, dqk, dv), **f32), dn0=torch.empty((B, H, dqk), **f32),
+             dm0=torch.empty((B, H), **f32))
+    need = mlstm_bwd_chunkwise_workspace_bytes(p, chunk)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _check(lib.mlstm_bwd_chunkwise(ctypes.byref(p), int(chunk), _ptr(q), _ptr(k), _ptr(v),
+                                   _ptr(i_pre), _ptr(f_pre), _ptr(o_pre), _ptr(C0), _ptr(n0),
+                                   _ptr(m0), _ptr(h), _ptr(dh), _ptr(dC1), _ptr(dn1),
+                                   _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["di"]),
+                                   _ptr(g["df"]), _ptr(g["do"]), _ptr(g["dC0"]), _ptr(g["dn0"]),
+                                   _ptr(g["dm0"]), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(),
+                                   _stream_handle(stream)))
+    return g
 
 
 def mlstm_step(q, k, v, i_pre, f_pre, o_pre, C, n, m, *, fgate="sigmoid",

@@ -134,6 +134,31 @@ mlstm::SeqArgs problem_args(const mlstm_problem_t* p) {
   return a;
 }
 
+// Shapes the backward pass covers.
+mlstm_status_t check_bwd_shape(const mlstm_problem_t* p, int64_t chunk) {
+  if (chunk != 16 && chunk != 32)
+    return fail(MLSTM_ERR_UNSUPPORTED, "backward: chunk=%lld: supported chunks are 16, 32",
+                (long long)chunk);
+  if (p->T % chunk != 0)
+    return fail(MLSTM_ERR_UNSUPPORTED, "T=%lld is not a multiple of chunk=%lld",
+                (long long)p->T, (long long)chunk);
+  const int64_t tv = p->d_v % 32 == 0 ? 32 : 16;
+  if (p->d_qk > 256 || p->d_qk % (256 / tv) != 0)
+    return fail(MLSTM_ERR_UNSUPPORTED,
+                "backward: d_qk=%lld: need at most 256 and a multiple of %lld (d_v=%lld)",
+                (long long)p->d_qk, (long long)(256 / tv), (long long)p->d_v);
+  return MLSTM_OK;
+}
+
+mlstm::BwdArgs bwd_problem_args(const mlstm_problem_t* p, int64_t chunk) {
+  mlstm::BwdArgs a{};
+  a.B = p->B; a.H = p->H; a.T = p->T; a.dqk = p->d_qk; a.dv = p->d_v;
+  a.qkv_bf16 = p->qkv_dtype == MLSTM_BF16;
+  a.fgate_exp = p->fgate == MLSTM_FGATE_EXP;
+  a.L = static_cast<int>(chunk);
+  return a;
+}
+
 mlstm_status_t device_status(hipError_t e, const char* what) {
   if (e != hipSuccess)
     return fail(MLSTM_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
@@ -191,6 +216,82 @@ mlstm_status_t mlstm_fwd_chunkwise(const mlstm_problem_t* p, int64_t chunk, cons
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (mfma) return device_status(mlstm::launch_chunk_mfma(a, chunk, workspace, st), "chunkwise (mfma)");
   return device_status(mlstm::launch_chunk_valu(a, chunk, st), "chunkwise (valu)");
+}
+
+mlstm_status_t mlstm_bwd_chunkwise_workspace_bytes(const mlstm_problem_t* p, int64_t chunk,
+                                                   size_t* bytes) {
+  if (!bytes) return fail(MLSTM_ERR_INVALID_ARG, "bytes is NULL");
+  mlstm_status_t s = check_problem(p, true);
+  if (s != MLSTM_OK) return s;
+  s = check_bwd_shape(p, chunk);
+  if (s != MLSTM_OK) return s;
+  *bytes = mlstm::bwd_workspace(bwd_problem_args(p, chunk), nullptr);
+  return ok();
+}
+
+mlstm_status_t mlstm_bwd_chunkwise(const mlstm_problem_t* p, int64_t chunk, const void* q,
+                                   const void* k, const void* v, const float* i_pre,
+                                   const float* f_pre, const void* o_pre, const float* C0,
+                                   const float* n0, const float* m0, const void* h,
+                                   const void* dh, const float* dC1, const float* dn1,
+                                   float* dq, float* dk, float* dv, float* di, float* df,
+                                   float* d_o, float* dC0, float* dn0, float* dm0,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  mlstm_status_t s = check_problem(p, true);
+  if (s != MLSTM_OK) return s;
+  s = check_bwd_shape(p, chunk);
+  if (s != MLSTM_OK) return s;
+  if (!q || !k || !v || !i_pre || !f_pre || !h || !dh || !dq || !dk || !dv || !di || !df)
+    return fail(MLSTM_ERR_INVALID_ARG,
+                "q, k, v, i_pre, f_pre, h, dh, dq, dk, dv, di and df are required");
+  const int in_state = (C0 != nullptr) + (n0 != nullptr) + (m0 != nullptr);
+  if (in_state != 0 && in_state != 3)
+    return fail(MLSTM_ERR_INVALID_ARG, "initial state must be all of C0, n0, m0 or none");
+  if ((dC1 != nullptr) != (dn1 != nullptr))
+    return fail(MLSTM_ERR_INVALID_ARG, "final-state gradient must be both of dC1, dn1 or none");
+  if ((o_pre != nullptr) != (d_o != nullptr))
+    return fail(MLSTM_ERR_INVALID_ARG, "d_o is required exactly when o_pre is given");
+  const size_t BH = (size_t)(p->B * p->H), T = (size_t)p->T;
+  const size_t dqk = (size_t)p->d_qk, dvv = (size_t)p->d_v, sq = dsize(p->qkv_dtype);
+  const Buf bufs[] = {
+      {"q", q, BH * T * dqk * sq, 4},       {"k", k, BH * T * dqk * sq, 4},
+      {"v", v, BH * T * dvv * sq, 4},       {"i_pre", i_pre, BH * T * 4, 4},
+      {"f_pre", f_pre, BH * T * 4, 4},      {"o_pre", o_pre, BH * T * dvv * dsize(p->o_dtype), 4},
+      {"C0", C0, BH * dqk * dvv * 4, 4},    {"n0", n0, BH * dqk * 4, 4},
+      {"m0", m0, BH * 4, 4},                {"h", h, BH * T * dvv * sq, 4},
+      {"dh", dh, BH * T * dvv * sq, 4},     {"dC1", dC1, BH * dqk * dvv * 4, 4},
+      {"dn1", dn1, BH * dqk * 4, 4},
+      // outputs from here (index 13 on)
+      {"dq", dq, BH * T * dqk * 4, 4},      {"dk", dk, BH * T * dqk * 4, 4},
+      {"dv", dv, BH * T * dvv * 4, 4},      {"di", di, BH * T * 4, 4},
+      {"df", df, BH * T * 4, 4},            {"d_o", d_o, BH * T * dvv * 4, 4},
+      {"dC0", dC0, BH * dqk * dvv * 4, 4},  {"dn0", dn0, BH * dqk * 4, 4},
+      {"dm0", dm0, BH * 4, 4},
+  };
+  const int nb = sizeof(bufs) / sizeof(bufs[0]);
+  for (int i = 0; i < nb; ++i)
+    if (bufs[i].p && !aligned(bufs[i]))
+      return fail(MLSTM_ERR_INVALID_ARG, "%s is not %zu-byte aligned", bufs[i].name, bufs[i].align);
+  for (int o = 13; o < nb; ++o)
+    for (int i = 0; i < nb; ++i)
+      if (i != o && overlaps(bufs[o], bufs[i]))
+        return fail(MLSTM_ERR_INVALID_ARG, "%s overlaps %s", bufs[o].name, bufs[i].name);
+  mlstm::BwdArgs a = bwd_problem_args(p, chunk);
+  const size_t need = mlstm::bwd_workspace(a, nullptr);
+  if (!workspace || workspace_bytes < need)
+    return fail(MLSTM_ERR_INVALID_ARG, "workspace of %zu bytes given, %zu needed", workspace_bytes,
+                need);
+  if (!aligned16(workspace)) return fail(MLSTM_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  const Buf ws{"workspace", workspace, need, 16};
+  for (int i = 0; i < nb; ++i)
+    if (overlaps(ws, bufs[i])) return fail(MLSTM_ERR_INVALID_ARG, "workspace overlaps %s", bufs[i].name);
+  a.o_mode = o_pre ? (p->o_dtype == MLSTM_BF16 ? mlstm::O_BF16 : mlstm::O_F32) : mlstm::O_NONE;
+  a.q = q; a.k = k; a.v = v; a.i_pre = i_pre; a.f_pre = f_pre; a.o_pre = o_pre;
+  a.C0 = C0; a.n0 = n0; a.m0 = m0; a.h = h; a.dh = dh; a.dC1 = dC1; a.dn1 = dn1;
+  a.d_q = dq; a.d_k = dk; a.d_v = dv; a.d_i = di; a.d_f = df; a.d_o = d_o;
+  a.dC0 = dC0; a.dn0 = dn0; a.dm0 = dm0;
+  return device_status(mlstm::launch_bwd(a, workspace, static_cast<hipStream_t>(stream)),
+                       "chunkwise backward");
 }
 
 mlstm_status_t mlstm_fwd_parallel_workspace_bytes(const mlstm_problem_t* p, size_t* bytes) {

@@ -1,0 +1,490 @@
+// Chunkwise backward pass of the mLSTM cell (gfx950): gradients of h (and of
+// the final memory) with respect to q, k, v, i~, f~, o~ and the initial state.
+//
+// Method: the forward pass of the xLSTM post (llms.blog), section 3
+// "Associative Matrix Cell State" and "The Parallel Dual Form", with the
+// running maximum of section 2 "The Normalizer State and Numerical
+// Stabilization".  The pages print no gradient; the one evaluated here is
+// the derivative of that forward pass, written in the chunk variables of the
+// forward kernels.  Within a chunk of L tokens starting from the stored state
+// (C~_s, n~_s, m_s), with u_j, M_i, m_i, D_ij, g_i, w_j as in the forward:
+//
+//   den_i  = max(|g_i q_i.n~_s + sum_j D_ij (q_i.k_j)|, exp(-m_i))
+//   r_i    = sigmoid(o~_i) (.) dh_i / den_i
+//   dnq_i  = -(dh_i . h_i) / den_i * sign(.)   where |.| >= exp(-m_i), else 0
+//   W_ij   = D_ij (r_i . v_j + dnq_i)                     (j <= i)
+//   dq_i   = sum_j W_ij k_j + g_i (C~_s r_i + dnq_i n~_s)
+//   dk_j   = sum_i W_ij q_i + w_j (dC_e v_j + dn_e)
+//   dv_j   = sum_i D_ij (q_i.k_j) r_i + w_j dC_e^T k_j
+//   do~_i  = dh_i (.) h_i (.) (1 - sigmoid(o~_i))
+//   dC_s   = g_L dC_e + sum_i g_i q_i r_i^T,   dn_s = g_L dn_e + sum_i g_i dnq_i q_i
+//
+// where dC, dn are the gradients of the memory in the scale of the stored
+// state at the chunk boundary (dC = e^{m} dL/dC_true).  Every factor is the
+// forward's own stabilized one, so nothing overflows.  Summing the token
+// contributions gives two identities used for the gates:
+//   di~_t = k_t . dk_t,
+//   d(log f_t) = sum_{t'>=t} (q_t'.dq_t' - k_t'.dk_t') + <dC1, C~_T> + <dn1, n~_T>.
+//
+// Passes (all on the launch stream, sharing one workspace):
+//   1. beta_t = dh_t . h_t per token;
+//   2. a forward state pass that stores (C~, n~, m) at every chunk boundary;
+//   3. a reverse pass over the chunks per (head, 32 or 16 value columns): it
+//      carries dC in registers and writes dv, do~ and per-column-block
+//      partial sums of dq and dk;
+//   4. per token: the sums of the partials, di~ and q.dq - k.dk;
+//   5. per head: the reverse prefix sum that gives df~, and dm0.
+// All arithmetic is float32 on the vector ALUs; this is the first, simple
+// form of the backward pass.
+#include "common.hpp"
+#include "kernels.hpp"
+#include "mfma_util.hpp"
+
+namespace mlstm {
+namespace {
+
+constexpr int NTB = 256;   // threads per workgroup
+
+template <typename T>
+__device__ __forceinline__ float ld(const void* p, int64_t i) {
+  return to_f32<T>(static_cast<const T*>(p)[i]);
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+__device__ __forceinline__ float block_sum(float x, float* red) {
+  x = wave_sum(x);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wave] = x;
+  __syncthreads();
+  float s = 0.0f;
+#pragma unroll
+  for (int w = 0; w < NTB / 64; ++w) s += red[w];
+  return s;
+}
+
+// ---- pass 1: beta_t = dh_t . h_t (one wave per token)
+template <typename T>
+__global__ __launch_bounds__(NTB) void bwd_beta_kernel(BwdArgs a) {
+  const int64_t tok = static_cast<int64_t>(blockIdx.x) * (NTB / 64) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (tok >= a.B * a.H * a.T) return;
+  float s = 0.0f;
+  for (int64_t b = lane; b < a.dv; b += 64) s += ld<T>(a.dh, tok * a.dv + b) * ld<T>(a.h, tok * a.dv + b);
+  s = wave_sum(s);
+  if (lane == 0) a.ws_beta[tok] = s;
+}
+
+// Gate scan of one chunk of L <= 64 tokens by wave 0 into LDS: per token j,
+// u_j = i~_j - b_j (b: in-chunk prefix sum of log f), M_j = max(ms, max u),
+// m_j = b_j + M_j, g_j = exp(ms - M_j), w_j = exp(u_j - M_L).  Returns nothing;
+// every wave reads the arrays after the next barrier.
+struct GateLds {
+  float u[64], M[64], m[64], g[64], w[64], lfv[64];
+};
+
+template <int L>
+__device__ __forceinline__ void gate_scan(const BwdArgs& a, int64_t tok0, float ms, GateLds& G) {
+  const int lane = threadIdx.x & 63;
+  const bool in = lane < L;
+  const float fpre = in ? a.f_pre[tok0 + lane] : 0.0f;
+  const float lf = in ? (a.fgate_exp ? fpre : log_sigmoid(fpre)) : 0.0f;
+  const float bc = mk::scan_add(lf);
+  const float u = in ? a.i_pre[tok0 + lane] - bc : -INFINITY;
+  const float Mx = fmaxf(ms, mk::scan_max(u));
+  const float ML = __shfl(Mx, L - 1, 64);
+  if (in) {
+    G.u[lane] = u;
+    G.M[lane] = Mx;
+    G.m[lane] = bc + Mx;
+    G.g[lane] = __expf(ms - Mx);
+    G.w[lane] = __expf(u - ML);
+    G.lfv[lane] = lf;
+  }
+}
+
+// ---- pass 2: chunk-boundary states.  Workgroup = (head, TV value columns);
+// thread t owns column t % TV of rows t / TV + (NTB / TV) r of C~.
+template <typename T, int TV, int L>
+__global__ __launch_bounds__(NTB) void bwd_states_kernel(BwdArgs a) {
+  constexpr int RSTEP = NTB / TV;
+  __shared__ float sK[L * 256];
+  __shared__ float sWV[L * TV];
+  __shared__ GateLds G;
+  __shared__ float sMs;
+  const int tid = threadIdx.x;
+  const int ncb = static_cast<int>(a.dv / TV);
+  const int64_t bh = blockIdx.x / ncb;
+  const int cb = blockIdx.x % ncb;
+  const int dqk = static_cast<int>(a.dqk), dv = static_cast<int>(a.dv);
+  const int ne = dqk / RSTEP;                    // owned rows (<= 256 / RSTEP)
+  const int b = tid % TV, r0 = tid / TV;
+  const int64_t nT = a.T;
+  const int nc = static_cast<int>(nT / L);
+  float C[256 / RSTEP];
+  float n[256 / RSTEP];
+  float m = a.C0 ? a.m0[bh] : 0.0f;
+  for (int r = 0; r < ne; ++r) {
+    const int row = r0 + RSTEP * r;
+    C[r] = a.C0 ? a.C0[(bh * dqk + row) * dv + cb * TV + b] : 0.0f;
+    n[r] = a.C0 ? a.n0[bh * dqk + row] : 0.0f;
+  }
+  const int64_t nb = static_cast<int64_t>(nc + 1);
+  for (int c = 0; c <= nc; ++c) {
+    // stored state at boundary c (before chunk c; c = nc: the final state)
+    float* wsC = a.ws_C + ((bh * nb + c) * dqk) * dv + cb * TV + b;
+    for (int r = 0; r < ne; ++r) {
+      const int row = r0 + RSTEP * r;
+      wsC[static_cast<int64_t>(row) * dv] = C[r];
+      if (cb == 0 && b == 0) a.ws_n[(bh * nb + c) * dqk + row] = n[r];
+    }
+    if (cb == 0 && tid == 0) a.ws_m[bh * nb + c] = m;
+    if (c == nc) break;
+    const int64_t tok0 = bh * nT + static_cast<int64_t>(c) * L;
+    __syncthreads();
+    if (tid < 64) gate_scan<L>(a, tok0, m, G);
+    for (int e = tid; e < L * dqk; e += NTB) sK[e] = ld<T>(a.k, tok0 * dqk + e);
+    __syncthreads();
+    for (int e = tid; e < L * TV; e += NTB) {
+      const int j = e / TV, bb = e % TV;
+      sWV[e] = G.w[j] * ld<T>(a.v, (tok0 + j) * dv + cb * TV + bb);
+    }
+    if (tid == 0) sMs = G.m[L - 1];
+    __syncthreads();
+    const float gL = G.g[L - 1];
+    for (int r = 0; r < ne; ++r) {
+      const int row = r0 + RSTEP * r;
+      float acc = gL * C[r], accn = gL * n[r];
+#pragma unroll 8
+      for (int j = 0; j < L; ++j) {
+        const float kv = sK[j * dqk + row];
+        acc += kv * sWV[j * TV + b];
+        accn += kv * G.w[j];
+      }
+      C[r] = acc;
+      n[r] = accn;
+    }
+    m = sMs;
+  }
+}
+
+// ---- pass 3: reverse over the chunks.
+template <typename T, typename TO, int TV, int L>
+__global__ __launch_bounds__(NTB) void bwd_rev_kernel(BwdArgs a) {
+  constexpr int RSTEP = NTB / TV;
+  constexpr int TP = TV + 1;   // padded row of the [d_qk][TV] tiles
+  __shared__ float sQ[L * 256];
+  __shared__ float sKt[L * 256];
+  __shared__ float sX[256 * TP];       // C~_s, then dC_e (own columns)
+  __shared__ float sV[L * TV];
+  __shared__ float sR[L * TV];
+  __shared__ float sS[L * L];          // q_i . k_j
+  __shared__ float sDm[L * L];         // D_ij, zero above the diagonal
+  __shared__ float sW[L * L];
+  __shared__ float sN[256];            // n~_s
+  __shared__ float sDn[256];           // dn_e, then dn_s
+  __shared__ float sQn[L], sDen[L], sDnq[L], sBeta[L];
+  __shared__ GateLds G;
+  __shared__ float sRed[NTB / 64];
+  const int tid = threadIdx.x;
+  const int ncb = static_cast<int>(a.dv / TV);
+  const int64_t bh = blockIdx.x / ncb;
+  const int cb = blockIdx.x % ncb;
+  const bool lead = cb == 0;           // adds the terms shared by all column blocks
+  const int dqk = static_cast<int>(a.dqk), dv = static_cast<int>(a.dv);
+  const int ne = dqk / RSTEP;
+  const int b = tid % TV, r0 = tid / TV;
+  const int64_t nT = a.T;
+  const int nc = static_cast<int>(nT / L);
+  const int64_t nb = static_cast<int64_t>(nc + 1);
+  // carried dC (own columns, this thread's rows) and dn (all rows, in LDS)
+  float dC[256 / RSTEP];
+  {
+    const float* src = a.dC1 ? a.dC1 + (bh * dqk) * dv + cb * TV + b : nullptr;
+    for (int r = 0; r < ne; ++r) dC[r] = src ? src[static_cast<int64_t>(r0 + RSTEP * r) * dv] : 0.0f;
+    for (int e = tid; e < dqk; e += NTB) sDn[e] = a.dn1 ? a.dn1[bh * dqk + e] : 0.0f;
+  }
+  for (int c = nc - 1; c >= 0; --c) {
+    const int64_t tok0 = bh * nT + static_cast<int64_t>(c) * L;
+    const float ms = a.ws_m[bh * nb + c];
+    __syncthreads();
+    // ---- loads
+    if (tid < 64) gate_scan<L>(a, tok0, ms, G);
+    for (int e = tid; e < L * dqk; e += NTB) {
+      sQ[e] = ld<T>(a.q, tok0 * dqk + e);
+      sKt[e] = ld<T>(a.k, tok0 * dqk + e);
+    }
+    for (int e = tid; e < L * TV; e += NTB) {
+      const int j = e / TV, bb = e % TV;
+      sV[e] = ld<T>(a.v, (tok0 + j) * dv + cb * TV + bb);
+    }
+    {
+      const float* Cs = a.ws_C + ((bh * nb + c) * dqk) * dv + cb * TV;
+      for (int e = tid; e < dqk * TV; e += NTB) {
+        const int row = e / TV, bb = e % TV;
+        sX[row * TP + bb] = Cs[static_cast<int64_t>(row) * dv + bb];
+      }
+    }
+    for (int e = tid; e < dqk; e += NTB) sN[e] = a.ws_n[(bh * nb + c) * dqk + e];
+    for (int e = tid; e < L; e += NTB) sBeta[e] = a.ws_beta[tok0 + e];
+    __syncthreads();
+    // ---- scores, q.n~_s and the decay matrix
+    for (int e = tid; e < L * L; e += NTB) {
+      const int i = e / L, j = e % L;
+      float s = 0.0f;
+      for (int x = 0; x < dqk; ++x) s += sQ[i * dqk + x] * sKt[j * dqk + x];
+      sS[e] = s;
+      sDm[e] = j <= i ? __expf(G.u[j] - G.M[i]) : 0.0f;
+    }
+    for (int i = tid; i < L; i += NTB) {
+      float s = 0.0f;
+      for (int x = 0; x < dqk; ++x) s += sQ[i * dqk + x] * sN[x];
+      sQn[i] = s;
+    }
+    __syncthreads();
+    // ---- denominators and the normalizer gradient per token
+    for (int i = tid; i < L; i += NTB) {
+      float nq = G.g[i] * sQn[i];
+      for (int j = 0; j <= i; ++j) nq += sDm[i * L + j] * sS[i * L + j];
+      const float floor_ = __expf(-G.m[i]);
+      const float den = fmaxf(fabsf(nq), floor_);
+      sDen[i] = den;
+      sDnq[i] = fabsf(nq) >= floor_ ? (nq >= 0.0f ? -sBeta[i] / den : sBeta[i] / den) : 0.0f;
+    }
+    __syncthreads();
+    // ---- r = sigmoid(o~) dh / den, and do~ (own columns)
+    for (int e = tid; e < L * TV; e += NTB) {
+      const int i = e / TV, bb = e % TV;
+      const int64_t gi = (tok0 + i) * dv + cb * TV + bb;
+      const float dh = ld<T>(a.dh, gi);
+      float gate = 1.0f;
+      if (a.o_pre) {
+        gate = mk::sigmoid_fast(ld<TO>(a.o_pre, gi));
+        a.d_o[gi] = dh * ld<T>(a.h, gi) * (1.0f - gate);
+      }
+      sR[e] = gate * dh / sDen[i];
+    }
+    __syncthreads();
+    // ---- W = D (.) (r.v + dnq)
+    for (int e = tid; e < L * L; e += NTB) {
+      const int i = e / L, j = e % L;
+      float rv = lead ? sDnq[i] : 0.0f;
+      for (int bb = 0; bb < TV; ++bb) rv += sR[i * TV + bb] * sV[j * TV + bb];
+      sW[e] = sDm[e] * rv;
+    }
+    __syncthreads();
+    // ---- dq partial: sum_j W_ij k_j + g_i (C~_s r_i + dnq_i n~_s)
+    {
+      float* out = a.ws_dq + ((static_cast<int64_t>(cb) * a.B * a.H + bh) * nT + static_cast<int64_t>(c) * L) * dqk;
+      for (int e = tid; e < L * dqk; e += NTB) {
+        const int i = e / dqk, x = e % dqk;
+        float s = 0.0f;
+        for (int j = 0; j <= i; ++j) s += sW[i * L + j] * sKt[j * dqk + x];
+        float cr = lead ? sDnq[i] * sN[x] : 0.0f;
+        for (int bb = 0; bb < TV; ++bb) cr += sX[x * TP + bb] * sR[i * TV + bb];
+        out[e] = s + G.g[i] * cr;
+      }
+    }
+    __syncthreads();
+    // ---- the carried gradient dC_e into LDS (replaces C~_s)
+    for (int r = 0; r < ne; ++r) sX[(r0 + RSTEP * r) * TP + b] = dC[r];
+    __syncthreads();
+    // ---- dk partial: sum_i W_ij q_i + w_j (dC_e v_j + dn_e)
+    {
+      float* out = a.ws_dk + ((static_cast<int64_t>(cb) * a.B * a.H + bh) * nT + static_cast<int64_t>(c) * L) * dqk;
+      for (int e = tid; e < L * dqk; e += NTB) {
+        const int j = e / dqk, x = e % dqk;
+        float s = 0.0f;
+        for (int i = j; i < L; ++i) s += sW[i * L + j] * sQ[i * dqk + x];
+        float cv = lead ? sDn[x] : 0.0f;
+        for (int bb = 0; bb < TV; ++bb) cv += sX[x * TP + bb] * sV[j * TV + bb];
+        out[e] = s + G.w[j] * cv;
+      }
+    }
+    // ---- dv: sum_i D_ij (q_i.k_j) r_i + w_j dC_e^T k_j (own columns)
+    for (int e = tid; e < L * TV; e += NTB) {
+      const int j = e / TV, bb = e % TV;
+      float s = 0.0f;
+      for (int i = j; i < L; ++i) s += sDm[i * L + j] * sS[i * L + j] * sR[i * TV + bb];
+      float ck = 0.0f;
+      for (int x = 0; x < dqk; ++x) ck += sX[x * TP + bb] * sKt[j * dqk + x];
+      a.d_v[(tok0 + j) * dv + cb * TV + bb] = s + G.w[j] * ck;
+    }
+    // ---- dC_s = g_L dC_e + sum_i g_i q_i r_i^T (this thread's entries)
+    const float gL = G.g[L - 1];
+    for (int r = 0; r < ne; ++r) {
+      const int row = r0 + RSTEP * r;
+      float s = gL * dC[r];
+      for (int i = 0; i < L; ++i) s += G.g[i] * sQ[i * dqk + row] * sR[i * TV + b];
+      dC[r] = s;
+    }
+    __syncthreads();   // every read of sDn (dk) is done
+    // ---- dn_s = g_L dn_e + sum_i g_i dnq_i q_i
+    for (int x = tid; x < dqk; x += NTB) {
+      float s = gL * sDn[x];
+      for (int i = 0; i < L; ++i) s += G.g[i] * sDnq[i] * sQ[i * dqk + x];
+      sDn[x] = s;
+    }
+  }
+  // ---- initial state: gradients in its stored scale, and dm0's share
+  __syncthreads();
+  float part = 0.0f;
+  for (int r = 0; r < ne; ++r) {
+    const int row = r0 + RSTEP * r;
+    const int64_t gi = (bh * dqk + row) * dv + cb * TV + b;
+    if (a.dC0) a.dC0[gi] = dC[r];
+    if (a.C0) part += dC[r] * a.C0[gi];
+  }
+  if (lead) {
+    for (int x = tid; x < dqk; x += NTB) {
+      if (a.dn0) a.dn0[bh * dqk + x] = sDn[x];
+      if (a.C0) part += sDn[x] * a.n0[bh * dqk + x];
+    }
+  }
+  part = block_sum(part, sRed);
+  if (tid == 0) a.ws_dm0[static_cast<int64_t>(cb) * a.B * a.H + bh] = part;
+}
+
+// ---- pass 4: per token, the partial sums of dq and dk, di~ and q.dq - k.dk
+// (one wave per token)
+template <typename T>
+__global__ __launch_bounds__(NTB) void bwd_tok_kernel(BwdArgs a, int ncb) {
+  const int64_t ntok = a.B * a.H * a.T;
+  const int64_t tok = static_cast<int64_t>(blockIdx.x) * (NTB / 64) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (tok >= ntok) return;
+  const int64_t dqk = a.dqk;
+  float kdk = 0.0f, qdq = 0.0f;
+  for (int64_t x = lane; x < dqk; x += 64) {
+    float sq = 0.0f, sk = 0.0f;
+    for (int p = 0; p < ncb; ++p) {
+      sq += a.ws_dq[(static_cast<int64_t>(p) * ntok + tok) * dqk + x];
+      sk += a.ws_dk[(static_cast<int64_t>(p) * ntok + tok) * dqk + x];
+    }
+    a.d_q[tok * dqk + x] = sq;
+    a.d_k[tok * dqk + x] = sk;
+    qdq += ld<T>(a.q, tok * dqk + x) * sq;
+    kdk += ld<T>(a.k, tok * dqk + x) * sk;
+  }
+  qdq = wave_sum(qdq);
+  kdk = wave_sum(kdk);
+  if (lane == 0) {
+    a.d_i[tok] = kdk;
+    a.ws_s[tok] = qdq - kdk;
+  }
+}
+
+// ---- pass 5: per head, d(log f_t) = sum_{t'>=t} s_t' + <dC1, C~_T> + <dn1, n~_T>
+// (a reverse prefix sum over blocks of T / NTB tokens), df~ and dm0.
+__global__ __launch_bounds__(NTB) void bwd_head_kernel(BwdArgs a, int ncb, int nc) {
+  __shared__ float sRed[NTB / 64];
+  __shared__ float sBlk[NTB];
+  const int tid = threadIdx.x;
+  const int64_t bh = blockIdx.x;
+  const int64_t T = a.T, dqk = a.dqk, dv = a.dv;
+  const int64_t nb = nc + 1;
+  // constant term from the final-state gradient
+  float kend = 0.0f;
+  if (a.dC1) {
+    const float* CT = a.ws_C + (bh * nb + nc) * dqk * dv;
+    for (int64_t e = tid; e < dqk * dv; e += NTB) kend += a.dC1[bh * dqk * dv + e] * CT[e];
+    for (int64_t e = tid; e < dqk; e += NTB) kend += a.dn1[bh * dqk + e] * a.ws_n[(bh * nb + nc) * dqk + e];
+  }
+  kend = block_sum(kend, sRed);
+  // reverse prefix sum: thread t owns tokens [t * per, (t + 1) * per)
+  const int64_t per = (T + NTB - 1) / NTB;
+  const int64_t t0 = tid * per, t1 = (t0 + per < T) ? t0 + per : T;
+  float own = 0.0f;
+  for (int64_t t = t0; t < t1; ++t) own += a.ws_s[bh * T + t];
+  sBlk[tid] = own;
+  __syncthreads();
+  float after = kend;   // sum over the blocks after this thread's
+  for (int u = tid + 1; u < NTB; ++u) after += sBlk[u];
+  for (int64_t t = t1 - 1; t >= t0; --t) {
+    after += a.ws_s[bh * T + t];
+    const float fpre = a.f_pre[bh * T + t];
+    a.d_f[bh * T + t] = a.fgate_exp ? after : after * (1.0f - mk::sigmoid_fast(fpre));
+  }
+  if (a.dm0 && tid == 0) {
+    float s = 0.0f;
+    for (int p = 0; p < ncb; ++p) s += a.ws_dm0[static_cast<int64_t>(p) * a.B * a.H + bh];
+    a.dm0[bh] = s;
+  }
+}
+
+template <typename T, typename TO, int TV, int L>
+hipError_t launch_typed(const BwdArgs& a, hipStream_t st) {
+  const int64_t ntok = a.B * a.H * a.T;
+  const int ncb = static_cast<int>(a.dv / TV);
+  const int nc = static_cast<int>(a.T / L);
+  const unsigned tok_blocks = static_cast<unsigned>((ntok + NTB / 64 - 1) / (NTB / 64));
+  const unsigned wgs = static_cast<unsigned>(a.B * a.H * ncb);
+  bwd_beta_kernel<T><<<tok_blocks, NTB, 0, st>>>(a);
+  bwd_states_kernel<T, TV, L><<<wgs, NTB, 0, st>>>(a);
+  bwd_rev_kernel<T, TO, TV, L><<<wgs, NTB, 0, st>>>(a);
+  bwd_tok_kernel<T><<<tok_blocks, NTB, 0, st>>>(a, ncb);
+  bwd_head_kernel<<<static_cast<unsigned>(a.B * a.H), NTB, 0, st>>>(a, ncb, nc);
+  return hipGetLastError();
+}
+
+template <typename T, typename TO>
+hipError_t launch_dt(const BwdArgs& a, hipStream_t st) {
+  const int TV = bwd_tile_columns(a);
+  if (a.L == 16) return TV == 32 ? launch_typed<T, TO, 32, 16>(a, st) : launch_typed<T, TO, 16, 16>(a, st);
+  return TV == 32 ? launch_typed<T, TO, 32, 32>(a, st) : launch_typed<T, TO, 16, 32>(a, st);
+}
+
+size_t round_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+}  // namespace
+
+int bwd_tile_columns(const BwdArgs& a) { return a.dv % 32 == 0 ? 32 : 16; }
+
+bool bwd_supported(const BwdArgs& a) {
+  const int TV = a.dv % 32 == 0 ? 32 : 16;
+  return (a.L == 16 || a.L == 32) && a.T % a.L == 0 && a.dqk <= 256 && a.dqk % (NTB / TV) == 0 &&
+         a.dv % 16 == 0;
+}
+
+// Workspace layout: ws_C, ws_n, ws_m, ws_beta, ws_dq, ws_dk, ws_s, ws_dm0.
+size_t bwd_workspace(const BwdArgs& a, size_t offsets[8]) {
+  const size_t BH = static_cast<size_t>(a.B * a.H), T = static_cast<size_t>(a.T);
+  const size_t nb = static_cast<size_t>(a.T / a.L) + 1, dqk = static_cast<size_t>(a.dqk);
+  const size_t dv = static_cast<size_t>(a.dv);
+  const size_t ncb = dv / static_cast<size_t>(a.dv % 32 == 0 ? 32 : 16);
+  const size_t sizes[8] = {BH * nb * dqk * dv * 4, BH * nb * dqk * 4, BH * nb * 4, BH * T * 4,
+                           ncb * BH * T * dqk * 4, ncb * BH * T * dqk * 4, BH * T * 4, ncb * BH * 4};
+  size_t off = 0;
+  for (int i = 0; i < 8; ++i) {
+    if (offsets) offsets[i] = off;
+    off += round_up(sizes[i]);
+  }
+  return off;
+}
+
+hipError_t launch_bwd(BwdArgs a, void* ws, hipStream_t st) {
+  size_t off[8];
+  bwd_workspace(a, off);
+  char* base = static_cast<char*>(ws);
+  a.ws_C = reinterpret_cast<float*>(base + off[0]);
+  a.ws_n = reinterpret_cast<float*>(base + off[1]);
+  a.ws_m = reinterpret_cast<float*>(base + off[2]);
+  a.ws_beta = reinterpret_cast<float*>(base + off[3]);
+  a.ws_dq = reinterpret_cast<float*>(base + off[4]);
+  a.ws_dk = reinterpret_cast<float*>(base + off[5]);
+  a.ws_s = reinterpret_cast<float*>(base + off[6]);
+  a.ws_dm0 = reinterpret_cast<float*>(base + off[7]);
+  if (a.qkv_bf16) {
+    if (a.o_mode == O_BF16) return launch_dt<bf16_t, bf16_t>(a, st);
+    return launch_dt<bf16_t, float>(a, st);
+  }
+  if (a.o_mode == O_BF16) return launch_dt<float, bf16_t>(a, st);
+  return launch_dt<float, float>(a, st);
+}
+
+}  // namespace mlstm

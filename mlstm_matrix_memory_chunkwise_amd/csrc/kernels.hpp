@@ -72,6 +72,49 @@ hipError_t launch_chunk_ws(const SeqArgs& a, hipStream_t stream);
 // Generic VALU chunkwise kernel (float32 path; bf16 shapes outside MFMA cover).
 hipError_t launch_chunk_valu(const SeqArgs& a, int64_t chunk, hipStream_t stream);
 
+// Chunkwise backward pass.  Gradients are float32; d_o is written only when
+// o_pre is given; dC0, dn0, dm0 may be null; dC1/dn1 null = zero.
+struct BwdArgs {
+  int64_t B, H, T, dqk, dv;
+  int qkv_bf16, o_mode, fgate_exp;
+  int L;            // chunk (16 or 32)
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* i_pre;
+  const float* f_pre;
+  const void* o_pre;
+  const float* C0;
+  const float* n0;
+  const float* m0;
+  const void* h;    // forward output (qkv dtype)
+  const void* dh;   // gradient of h (qkv dtype)
+  const float* dC1;
+  const float* dn1;
+  float* d_q;
+  float* d_k;
+  float* d_v;
+  float* d_i;
+  float* d_f;
+  float* d_o;
+  float* dC0;
+  float* dn0;
+  float* dm0;
+  // workspace pieces (set by launch_bwd)
+  float* ws_C;
+  float* ws_n;
+  float* ws_m;
+  float* ws_beta;
+  float* ws_dq;
+  float* ws_dk;
+  float* ws_s;
+  float* ws_dm0;
+};
+bool bwd_supported(const BwdArgs& a);
+int bwd_tile_columns(const BwdArgs& a);
+size_t bwd_workspace(const BwdArgs& a, size_t offsets[8]);
+hipError_t launch_bwd(BwdArgs a, void* ws, hipStream_t stream);
+
 // Parallel (quadratic) form.
 size_t parallel_workspace(const SeqArgs& a);
 hipError_t launch_parallel(const SeqArgs& a, void* ws, hipStream_t stream);

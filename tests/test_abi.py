@@ -190,3 +190,52 @@ def test_python_binding_refuses_host_tensors():
     q = torch.zeros(1, 1, 16, 16)
     with pytest.raises(ValueError):
         M.mlstm_fwd_chunkwise(q, q, q, torch.zeros(1, 1, 16), torch.zeros(1, 1, 16), chunk=16)
+
+
+BWD_NAMES = ["q", "k", "v", "i", "f", "o", "C0", "n0", "m0", "h", "dh", "dC1", "dn1",
+             "dq", "dk", "dv", "di", "df", "do", "dC0", "dn0", "dm0"]
+
+
+def bwd_call(lib, p, chunk=16, ws_bytes=1 << 40, **over):
+    vals = dict(zip(BWD_NAMES, ptrs(len(BWD_NAMES))))
+    for n in ("o", "C0", "n0", "m0", "dC1", "dn1", "do", "dC0", "dn0", "dm0"):
+        vals[n] = None
+    vals.update(over)
+    ws = over.get("ws", ctypes.c_void_p(FAKE + 60 * (1 << 30)))
+    r = lib.mlstm_bwd_chunkwise(ctypes.byref(p), chunk, *(vals[n] for n in BWD_NAMES), ws,
+                                ws_bytes, None)
+    return r, lib.mlstm_last_error_detail().decode()
+
+
+def test_bwd_rejects_missing_pointers(lib):
+    for name in ("q", "k", "v", "i", "f", "h", "dh", "dq", "dk", "dv", "di", "df"):
+        r, det = bwd_call(lib, P(), **{name: None})
+        assert r == M.MLSTM_ERR_INVALID_ARG, (name, det)
+
+
+def test_bwd_pairing_rules(lib):
+    r, det = bwd_call(lib, P(), o=ctypes.c_void_p(FAKE + 30 * (1 << 30)))
+    assert r == M.MLSTM_ERR_INVALID_ARG and "d_o" in det
+    r, det = bwd_call(lib, P(), dC1=ctypes.c_void_p(FAKE + 30 * (1 << 30)))
+    assert r == M.MLSTM_ERR_INVALID_ARG and "final-state gradient" in det
+    r, det = bwd_call(lib, P(), C0=ctypes.c_void_p(FAKE + 30 * (1 << 30)))
+    assert r == M.MLSTM_ERR_INVALID_ARG and "initial state" in det
+
+
+def test_bwd_unsupported(lib):
+    assert bwd_call(lib, P(), chunk=64)[0] == M.MLSTM_ERR_UNSUPPORTED
+    assert bwd_call(lib, P(T=40))[0] == M.MLSTM_ERR_UNSUPPORTED
+    assert bwd_call(lib, P(dqk=512, dv=32))[0] == M.MLSTM_ERR_UNSUPPORTED
+    assert bwd_call(lib, P(dqk=272, dv=48))[0] == M.MLSTM_ERR_UNSUPPORTED
+
+
+def test_bwd_workspace(lib):
+    n = ctypes.c_size_t(0)
+    p = P(B=2, H=3, T=64, dqk=16, dv=16)
+    assert lib.mlstm_bwd_chunkwise_workspace_bytes(ctypes.byref(p), 16, ctypes.byref(n)) == 0
+    # the stored boundary states and the per-column-block partials dominate
+    assert n.value >= 2 * 3 * (64 // 16 + 1) * 16 * 16 * 4 + 2 * 1 * 2 * 3 * 64 * 16 * 4
+    r, det = bwd_call(lib, p, ws_bytes=n.value - 1)
+    assert r == M.MLSTM_ERR_INVALID_ARG and "workspace" in det
+    r, det = bwd_call(lib, p, ws=ctypes.c_void_p(FAKE + 64))   # inside q
+    assert r == M.MLSTM_ERR_INVALID_ARG and "overlaps" in det
