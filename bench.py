@@ -35,6 +35,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+FP32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector, TFLOP/s
 
 METRIC = "mLSTM chunkwise fwd tokens/s + % bf16 MFMA peak; step GB/s % HBM peak (1 GPU)"
 
@@ -52,6 +53,24 @@ def chunk_algorithmic(B, H, T, dqk, dv, L, o_bytes, state_in=True, state_out=Tru
     per_tok = (2 * dqk + dv) * 2 + dv * 2 + 8 + dv * o_bytes
     state = B * H * (dqk * dv + dqk + 1) * 4
     byts = th * per_tok + state * (int(state_in) + int(state_out))
+    return flops, byts
+
+
+def bwd_algorithmic(B, H, T, dqk, dv, L, o_bytes):
+    """Algorithmic work of one chunkwise backward pass.
+
+    flops per token-head: the causal halves of Q K^T, W K, W^T Q (3 (L+1) d_qk)
+    and of R V^T, (D S)^T R (2 (L+1) d_v), plus five d_qk x d_v products: the
+    state recomputed forward (K^T V), C~_s r, dC v, dC^T k and the state
+    gradient Q^T R (10 d_qk d_v).
+    bytes: q, k, v, h, dh (bf16), gates, o-gate in; dq, dk, dv, do (float32),
+    di, df out; the state and its gradient in and out once.
+    """
+    th = B * H * T
+    flops = th * (3 * (L + 1) * dqk + 2 * (L + 1) * dv + 10 * dqk * dv)
+    per_tok = (2 * dqk + 3 * dv) * 2 + 8 + dv * o_bytes + (2 * dqk + 2 * dv) * 4 + 8
+    state = B * H * (dqk * dv + dqk + 1) * 4
+    byts = th * per_tok + 4 * state
     return flops, byts
 
 
@@ -149,6 +168,7 @@ def main():
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--skip-step", action="store_true")
     ap.add_argument("--skip-extra", action="store_true")
+    ap.add_argument("--skip-bwd", action="store_true")
     ap.add_argument("--profile-workload", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -266,6 +286,41 @@ def main():
         result["no_ogate"] = {"ms": ms3, "tokens_per_s": B * T / (ms3 / 1e3),
                               "mfma_frac": f3 / (ms3 / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                               "hbm_frac": b3 / (ms3 / 1e3) / 1e9 / HBM_PEAK_GBS}
+
+    # ------------------------------------------------------------ backward
+    if not args.skip_bwd:
+        gen = torch.Generator(device="cpu").manual_seed(cfg.seed + 1)
+        dh = torch.randn((B, H, T, dv), generator=gen).to(torch.bfloat16).to(dev)
+        dC1 = torch.randn((B, H, dqk, dv), generator=gen).to(dev)
+        dn1 = torch.randn((B, H, dqk), generator=gen).to(dev)
+        run()   # h of these inputs
+        torch.cuda.synchronize()
+        bchunk = 16
+        wsb = torch.empty(M.mlstm_bwd_chunkwise_workspace_bytes(
+            M.Problem(B, H, T, dqk, dv, 1, 0, 0, 0), bchunk), dtype=torch.uint8, device=dev)
+
+        def run_bwd():
+            M.mlstm_bwd_chunkwise(d["q"], d["k"], d["v"], d["i_pre"], d["f_pre"], d["o_pre"],
+                                  d["C0"], d["n0"], d["m0"], h, dh, dC1, dn1, chunk=bchunk,
+                                  workspace=wsb)
+
+        run_bwd()
+        torch.cuda.synchronize()
+        ms_b = time_events(run_bwd, max(3, args.steps // 4), stream)
+        fb, bb = bwd_algorithmic(B, H, T, dqk, dv, bchunk, 4)
+        result["backward"] = {
+            "workload": f"chunkwise backward of the same pass (bf16 q/k/v/h/dh, f32 o-gate, state "
+                        f"in, final-state gradient in), chunk {bchunk}; float32 gradients out",
+            "ms": ms_b,
+            "tokens_per_s": B * T / (ms_b / 1e3),
+            "algorithmic_gflop": fb / 1e9,
+            "algorithmic_bytes": bb,
+            "hbm_frac": bb / (ms_b / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "fp32_valu_frac": fb / (ms_b / 1e3) / 1e12 / FP32_VALU_PEAK_TFLOPS,
+            "workspace_bytes": wsb.numel(),
+        }
+        del dh, dC1, dn1, wsb
+        torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ CPU oracle
     if not args.skip_cpu:

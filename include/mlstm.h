@@ -165,7 +165,8 @@ mlstm_status_t mlstm_step(const mlstm_problem_t* p, const void* q,
  *   mlstm_bwd_chunkwise_workspace_bytes (it holds the state at every chunk
  *   boundary and per-column-block partial sums: about
  *   B*H*(T/chunk+1)*d_qk*d_v*4 + 2*(d_v/32)*B*H*T*d_qk*4 bytes), 16-byte
- *   aligned, not overlapping any argument.
+ *   aligned, not overlapping any argument.  q, k and v must be 16-byte
+ *   aligned; every other pointer 4-byte aligned.  q, k and v must be 16-byte aligned.
  * Supported: chunk 16 or 32 (T a multiple of it) and d_qk <= 256; otherwise
  * MLSTM_ERR_UNSUPPORTED.  The result does not depend on chunk beyond
  * rounding.

@@ -254,8 +254,8 @@ mlstm_status_t mlstm_bwd_chunkwise(const mlstm_problem_t* p, int64_t chunk, cons
   const size_t BH = (size_t)(p->B * p->H), T = (size_t)p->T;
   const size_t dqk = (size_t)p->d_qk, dvv = (size_t)p->d_v, sq = dsize(p->qkv_dtype);
   const Buf bufs[] = {
-      {"q", q, BH * T * dqk * sq, 4},       {"k", k, BH * T * dqk * sq, 4},
-      {"v", v, BH * T * dvv * sq, 4},       {"i_pre", i_pre, BH * T * 4, 4},
+      {"q", q, BH * T * dqk * sq, 16},      {"k", k, BH * T * dqk * sq, 16},
+      {"v", v, BH * T * dvv * sq, 16},      {"i_pre", i_pre, BH * T * 4, 4},
       {"f_pre", f_pre, BH * T * 4, 4},      {"o_pre", o_pre, BH * T * dvv * dsize(p->o_dtype), 4},
       {"C0", C0, BH * dqk * dvv * 4, 4},    {"n0", n0, BH * dqk * 4, 4},
       {"m0", m0, BH * 4, 4},                {"h", h, BH * T * dvv * sq, 4},

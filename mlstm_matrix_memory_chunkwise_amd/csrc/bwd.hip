@@ -50,6 +50,60 @@ __device__ __forceinline__ float ld(const void* p, int64_t i) {
   return to_f32<T>(static_cast<const T*>(p)[i]);
 }
 
+// Copy of an R x NC tile (row-major source of element type S, leading
+// dimension ld elements, first element at src[base]) into LDS as float32 with
+// row stride dst_ld, by 16-byte vector loads: all of a thread's loads are
+// issued before any is converted, so their latencies overlap.  NC must be a
+// multiple of 8 (bf16) / 4 (float32) and every row 16-byte aligned.
+template <typename S, int MAXE>
+__device__ __forceinline__ void load_tile(float* dst, int dst_ld, const void* src, int64_t base,
+                                          int64_t ld, int R, int NC) {
+  constexpr int VE = 16 / static_cast<int>(sizeof(S));
+  constexpr int MAXV = (MAXE / VE + NTB - 1) / NTB;
+  const int per_row = NC / VE;
+  const int nv = R * per_row;
+  uint4 buf[MAXV];
+#pragma unroll
+  for (int k = 0; k < MAXV; ++k) {
+    const int e = static_cast<int>(threadIdx.x) + k * NTB;
+    if (e < nv) {
+      const int r = e / per_row, c = (e % per_row) * VE;
+      buf[k] = *reinterpret_cast<const uint4*>(static_cast<const S*>(src) + base + r * ld + c);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < MAXV; ++k) {
+    const int e = static_cast<int>(threadIdx.x) + k * NTB;
+    if (e < nv) {
+      const int r = e / per_row, c = (e % per_row) * VE;
+      float* d = dst + r * dst_ld + c;
+      if (sizeof(S) == 2) {
+        d[0] = bf_lo(buf[k].x); d[1] = bf_hi(buf[k].x); d[2] = bf_lo(buf[k].y); d[3] = bf_hi(buf[k].y);
+        d[4] = bf_lo(buf[k].z); d[5] = bf_hi(buf[k].z); d[6] = bf_lo(buf[k].w); d[7] = bf_hi(buf[k].w);
+      } else {
+        d[0] = __uint_as_float(buf[k].x); d[1] = __uint_as_float(buf[k].y);
+        d[2] = __uint_as_float(buf[k].z); d[3] = __uint_as_float(buf[k].w);
+      }
+    }
+  }
+}
+
+// sum_{x < n} a[x sa] b[x sb] with four partial sums, so that the LDS reads
+// of several terms are in flight at once.
+__device__ __forceinline__ float dot4(const float* a, int sa, const float* b, int sb, int n) {
+  float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+  int x = 0;
+#pragma unroll 2
+  for (; x + 4 <= n; x += 4) {
+    s0 += a[x * sa] * b[x * sb];
+    s1 += a[(x + 1) * sa] * b[(x + 1) * sb];
+    s2 += a[(x + 2) * sa] * b[(x + 2) * sb];
+    s3 += a[(x + 3) * sa] * b[(x + 3) * sb];
+  }
+  for (; x < n; ++x) s0 += a[x * sa] * b[x * sb];
+  return (s0 + s1) + (s2 + s3);
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
@@ -148,12 +202,10 @@ __global__ __launch_bounds__(NTB) void bwd_states_kernel(BwdArgs a) {
     const int64_t tok0 = bh * nT + static_cast<int64_t>(c) * L;
     __syncthreads();
     if (tid < 64) gate_scan<L>(a, tok0, m, G);
-    for (int e = tid; e < L * dqk; e += NTB) sK[e] = ld<T>(a.k, tok0 * dqk + e);
+    load_tile<T, L * 256>(sK, dqk, a.k, tok0 * dqk, dqk, L, dqk);
+    load_tile<T, L * TV>(sWV, TV, a.v, tok0 * dv + cb * TV, dv, L, TV);
     __syncthreads();
-    for (int e = tid; e < L * TV; e += NTB) {
-      const int j = e / TV, bb = e % TV;
-      sWV[e] = G.w[j] * ld<T>(a.v, (tok0 + j) * dv + cb * TV + bb);
-    }
+    for (int e = tid; e < L * TV; e += NTB) sWV[e] *= G.w[e / TV];
     if (tid == 0) sMs = G.m[L - 1];
     __syncthreads();
     const float gL = G.g[L - 1];
@@ -177,15 +229,19 @@ __global__ __launch_bounds__(NTB) void bwd_states_kernel(BwdArgs a) {
 template <typename T, typename TO, int TV, int L>
 __global__ __launch_bounds__(NTB) void bwd_rev_kernel(BwdArgs a) {
   constexpr int RSTEP = NTB / TV;
-  constexpr int TP = TV + 1;   // padded row of the [d_qk][TV] tiles
-  __shared__ float sQ[L * 256];
-  __shared__ float sKt[L * 256];
+  // LDS rows are padded by one float so that lanes walking a column (token
+  // index across lanes) hit distinct banks
+  constexpr int TP = TV + 1;   // [d_qk][TV] tiles
+  constexpr int LP = L + 1;    // [L][L] tiles
+  __shared__ float sQ[L * 257];
+  __shared__ float sKt[L * 257];
   __shared__ float sX[256 * TP];       // C~_s, then dC_e (own columns)
-  __shared__ float sV[L * TV];
-  __shared__ float sR[L * TV];
-  __shared__ float sS[L * L];          // q_i . k_j
-  __shared__ float sDm[L * L];         // D_ij, zero above the diagonal
-  __shared__ float sW[L * L];
+  __shared__ float sV[L * TP];
+  __shared__ float sR[L * TP];
+  __shared__ float sS[L * LP];         // q_i . k_j
+  __shared__ float sDm[L * LP];        // D_ij, zero above the diagonal
+  __shared__ float sW[L * LP];
+  __shared__ float sRg[L * TP];        // g_i r_i
   __shared__ float sN[256];            // n~_s
   __shared__ float sDn[256];           // dn_e, then dn_s
   __shared__ float sQn[L], sDen[L], sDnq[L], sBeta[L];
@@ -197,6 +253,7 @@ __global__ __launch_bounds__(NTB) void bwd_rev_kernel(BwdArgs a) {
   const int cb = blockIdx.x % ncb;
   const bool lead = cb == 0;           // adds the terms shared by all column blocks
   const int dqk = static_cast<int>(a.dqk), dv = static_cast<int>(a.dv);
+  const int QP = dqk + 1;              // padded row of the [L][d_qk] tiles
   const int ne = dqk / RSTEP;
   const int b = tid % TV, r0 = tid / TV;
   const int64_t nT = a.T;
@@ -215,42 +272,28 @@ __global__ __launch_bounds__(NTB) void bwd_rev_kernel(BwdArgs a) {
     __syncthreads();
     // ---- loads
     if (tid < 64) gate_scan<L>(a, tok0, ms, G);
-    for (int e = tid; e < L * dqk; e += NTB) {
-      sQ[e] = ld<T>(a.q, tok0 * dqk + e);
-      sKt[e] = ld<T>(a.k, tok0 * dqk + e);
-    }
-    for (int e = tid; e < L * TV; e += NTB) {
-      const int j = e / TV, bb = e % TV;
-      sV[e] = ld<T>(a.v, (tok0 + j) * dv + cb * TV + bb);
-    }
-    {
-      const float* Cs = a.ws_C + ((bh * nb + c) * dqk) * dv + cb * TV;
-      for (int e = tid; e < dqk * TV; e += NTB) {
-        const int row = e / TV, bb = e % TV;
-        sX[row * TP + bb] = Cs[static_cast<int64_t>(row) * dv + bb];
-      }
-    }
+    load_tile<T, L * 256>(sQ, QP, a.q, tok0 * dqk, dqk, L, dqk);
+    load_tile<T, L * 256>(sKt, QP, a.k, tok0 * dqk, dqk, L, dqk);
+    load_tile<T, L * TV>(sV, TP, a.v, tok0 * dv + cb * TV, dv, L, TV);
+    load_tile<float, 256 * TV>(sX, TP, a.ws_C, ((bh * nb + c) * dqk) * dv + cb * TV, dv, dqk, TV);
     for (int e = tid; e < dqk; e += NTB) sN[e] = a.ws_n[(bh * nb + c) * dqk + e];
     for (int e = tid; e < L; e += NTB) sBeta[e] = a.ws_beta[tok0 + e];
     __syncthreads();
     // ---- scores, q.n~_s and the decay matrix
     for (int e = tid; e < L * L; e += NTB) {
       const int i = e / L, j = e % L;
-      float s = 0.0f;
-      for (int x = 0; x < dqk; ++x) s += sQ[i * dqk + x] * sKt[j * dqk + x];
-      sS[e] = s;
-      sDm[e] = j <= i ? __expf(G.u[j] - G.M[i]) : 0.0f;
+      sS[i * LP + j] = dot4(sQ + i * QP, 1, sKt + j * QP, 1, dqk);
+      sDm[i * LP + j] = j <= i ? __expf(G.u[j] - G.M[i]) : 0.0f;
     }
     for (int i = tid; i < L; i += NTB) {
-      float s = 0.0f;
-      for (int x = 0; x < dqk; ++x) s += sQ[i * dqk + x] * sN[x];
-      sQn[i] = s;
+      sQn[i] = dot4(sQ + i * QP, 1, sN, 1, dqk);
     }
     __syncthreads();
     // ---- denominators and the normalizer gradient per token
     for (int i = tid; i < L; i += NTB) {
       float nq = G.g[i] * sQn[i];
-      for (int j = 0; j <= i; ++j) nq += sDm[i * L + j] * sS[i * L + j];
+#pragma unroll 8
+      for (int j = 0; j <= i; ++j) nq += sDm[i * LP + j] * sS[i * LP + j];
       const float floor_ = __expf(-G.m[i]);
       const float den = fmaxf(fabsf(nq), floor_);
       sDen[i] = den;
@@ -267,26 +310,28 @@ __global__ __launch_bounds__(NTB) void bwd_rev_kernel(BwdArgs a) {
         gate = mk::sigmoid_fast(ld<TO>(a.o_pre, gi));
         a.d_o[gi] = dh * ld<T>(a.h, gi) * (1.0f - gate);
       }
-      sR[e] = gate * dh / sDen[i];
+      sR[i * TP + bb] = gate * dh / sDen[i];
     }
     __syncthreads();
     // ---- W = D (.) (r.v + dnq)
     for (int e = tid; e < L * L; e += NTB) {
       const int i = e / L, j = e % L;
-      float rv = lead ? sDnq[i] : 0.0f;
-      for (int bb = 0; bb < TV; ++bb) rv += sR[i * TV + bb] * sV[j * TV + bb];
-      sW[e] = sDm[e] * rv;
+      const float rv = (lead ? sDnq[i] : 0.0f) + dot4(sR + i * TP, 1, sV + j * TP, 1, TV);
+      sW[i * LP + j] = sDm[i * LP + j] * rv;
     }
+    __syncthreads();
+    // (D (.) S replaces S: only dv reads it from here on)
+    for (int e = tid; e < L * L; e += NTB) sS[(e / L) * LP + e % L] *= sDm[(e / L) * LP + e % L];
+    // r scaled by g, for the state gradient
+    for (int e = tid; e < L * TV; e += NTB) sRg[(e / TV) * TP + e % TV] = G.g[e / TV] * sR[(e / TV) * TP + e % TV];
     __syncthreads();
     // ---- dq partial: sum_j W_ij k_j + g_i (C~_s r_i + dnq_i n~_s)
     {
       float* out = a.ws_dq + ((static_cast<int64_t>(cb) * a.B * a.H + bh) * nT + static_cast<int64_t>(c) * L) * dqk;
       for (int e = tid; e < L * dqk; e += NTB) {
         const int i = e / dqk, x = e % dqk;
-        float s = 0.0f;
-        for (int j = 0; j <= i; ++j) s += sW[i * L + j] * sKt[j * dqk + x];
-        float cr = lead ? sDnq[i] * sN[x] : 0.0f;
-        for (int bb = 0; bb < TV; ++bb) cr += sX[x * TP + bb] * sR[i * TV + bb];
+        const float s = dot4(sW + i * LP, 1, sKt + x, QP, i + 1);
+        const float cr = (lead ? sDnq[i] * sN[x] : 0.0f) + dot4(sX + x * TP, 1, sR + i * TP, 1, TV);
         out[e] = s + G.g[i] * cr;
       }
     }
@@ -299,35 +344,30 @@ __global__ __launch_bounds__(NTB) void bwd_rev_kernel(BwdArgs a) {
       float* out = a.ws_dk + ((static_cast<int64_t>(cb) * a.B * a.H + bh) * nT + static_cast<int64_t>(c) * L) * dqk;
       for (int e = tid; e < L * dqk; e += NTB) {
         const int j = e / dqk, x = e % dqk;
-        float s = 0.0f;
-        for (int i = j; i < L; ++i) s += sW[i * L + j] * sQ[i * dqk + x];
-        float cv = lead ? sDn[x] : 0.0f;
-        for (int bb = 0; bb < TV; ++bb) cv += sX[x * TP + bb] * sV[j * TV + bb];
+        const float s = dot4(sW + j * LP + j, LP, sQ + j * QP + x, QP, L - j);
+        const float cv = (lead ? sDn[x] : 0.0f) + dot4(sX + x * TP, 1, sV + j * TP, 1, TV);
         out[e] = s + G.w[j] * cv;
       }
     }
     // ---- dv: sum_i D_ij (q_i.k_j) r_i + w_j dC_e^T k_j (own columns)
     for (int e = tid; e < L * TV; e += NTB) {
       const int j = e / TV, bb = e % TV;
-      float s = 0.0f;
-      for (int i = j; i < L; ++i) s += sDm[i * L + j] * sS[i * L + j] * sR[i * TV + bb];
-      float ck = 0.0f;
-      for (int x = 0; x < dqk; ++x) ck += sX[x * TP + bb] * sKt[j * dqk + x];
+      const float s = dot4(sS + j * LP + j, LP, sR + j * TP + bb, TP, L - j);   // sS holds D (.) S
+      const float ck = dot4(sX + bb, TP, sKt + j * QP, 1, dqk);
       a.d_v[(tok0 + j) * dv + cb * TV + bb] = s + G.w[j] * ck;
     }
     // ---- dC_s = g_L dC_e + sum_i g_i q_i r_i^T (this thread's entries)
     const float gL = G.g[L - 1];
     for (int r = 0; r < ne; ++r) {
       const int row = r0 + RSTEP * r;
-      float s = gL * dC[r];
-      for (int i = 0; i < L; ++i) s += G.g[i] * sQ[i * dqk + row] * sR[i * TV + b];
-      dC[r] = s;
+      dC[r] = gL * dC[r] + dot4(sQ + row, QP, sRg + b, TP, L);
     }
     __syncthreads();   // every read of sDn (dk) is done
     // ---- dn_s = g_L dn_e + sum_i g_i dnq_i q_i
     for (int x = tid; x < dqk; x += NTB) {
       float s = gL * sDn[x];
-      for (int i = 0; i < L; ++i) s += G.g[i] * sDnq[i] * sQ[i * dqk + x];
+#pragma unroll 8
+      for (int i = 0; i < L; ++i) s += G.g[i] * sDnq[i] * sQ[i * QP + x];
       sDn[x] = s;
     }
   }
