@@ -136,12 +136,20 @@ mlstm::SeqArgs problem_args(const mlstm_problem_t* p) {
 
 // Shapes the backward pass covers.
 mlstm_status_t check_bwd_shape(const mlstm_problem_t* p, int64_t chunk) {
-  if (chunk != 16 && chunk != 32)
-    return fail(MLSTM_ERR_UNSUPPORTED, "backward: chunk=%lld: supported chunks are 16, 32",
+  if (chunk != 16 && chunk != 32 && chunk != 64)
+    return fail(MLSTM_ERR_UNSUPPORTED, "backward: chunk=%lld: supported chunks are 16, 32, 64",
                 (long long)chunk);
   if (p->T % chunk != 0)
     return fail(MLSTM_ERR_UNSUPPORTED, "T=%lld is not a multiple of chunk=%lld",
                 (long long)p->T, (long long)chunk);
+  if (chunk == 64) {
+    if (p->qkv_dtype != MLSTM_BF16 || p->d_v % 64 != 0 ||
+        (p->d_qk != 64 && p->d_qk != 128 && p->d_qk != 256))
+      return fail(MLSTM_ERR_UNSUPPORTED,
+                  "backward chunk 64 needs bf16 q/k/v, d_v a multiple of 64 and d_qk 64, 128 "
+                  "or 256 (got d_qk=%lld, d_v=%lld)", (long long)p->d_qk, (long long)p->d_v);
+    return MLSTM_OK;
+  }
   const int64_t tv = p->d_v % 32 == 0 ? 32 : 16;
   if (p->d_qk > 256 || p->d_qk % (256 / tv) != 0)
     return fail(MLSTM_ERR_UNSUPPORTED,
@@ -253,19 +261,21 @@ mlstm_status_t mlstm_bwd_chunkwise(const mlstm_problem_t* p, int64_t chunk, cons
     return fail(MLSTM_ERR_INVALID_ARG, "d_o is required exactly when o_pre is given");
   const size_t BH = (size_t)(p->B * p->H), T = (size_t)p->T;
   const size_t dqk = (size_t)p->d_qk, dvv = (size_t)p->d_v, sq = dsize(p->qkv_dtype);
+  // chunk 64 reads and writes the [.., d_v] arrays 16 bytes at a time
+  const size_t va = chunk == 64 ? 16 : 4;
   const Buf bufs[] = {
       {"q", q, BH * T * dqk * sq, 16},      {"k", k, BH * T * dqk * sq, 16},
       {"v", v, BH * T * dvv * sq, 16},      {"i_pre", i_pre, BH * T * 4, 4},
-      {"f_pre", f_pre, BH * T * 4, 4},      {"o_pre", o_pre, BH * T * dvv * dsize(p->o_dtype), 4},
-      {"C0", C0, BH * dqk * dvv * 4, 4},    {"n0", n0, BH * dqk * 4, 4},
-      {"m0", m0, BH * 4, 4},                {"h", h, BH * T * dvv * sq, 4},
-      {"dh", dh, BH * T * dvv * sq, 4},     {"dC1", dC1, BH * dqk * dvv * 4, 4},
+      {"f_pre", f_pre, BH * T * 4, 4},      {"o_pre", o_pre, BH * T * dvv * dsize(p->o_dtype), va},
+      {"C0", C0, BH * dqk * dvv * 4, va},   {"n0", n0, BH * dqk * 4, 4},
+      {"m0", m0, BH * 4, 4},                {"h", h, BH * T * dvv * sq, va},
+      {"dh", dh, BH * T * dvv * sq, va},    {"dC1", dC1, BH * dqk * dvv * 4, va},
       {"dn1", dn1, BH * dqk * 4, 4},
       // outputs from here (index 13 on)
       {"dq", dq, BH * T * dqk * 4, 4},      {"dk", dk, BH * T * dqk * 4, 4},
-      {"dv", dv, BH * T * dvv * 4, 4},      {"di", di, BH * T * 4, 4},
-      {"df", df, BH * T * 4, 4},            {"d_o", d_o, BH * T * dvv * 4, 4},
-      {"dC0", dC0, BH * dqk * dvv * 4, 4},  {"dn0", dn0, BH * dqk * 4, 4},
+      {"dv", dv, BH * T * dvv * 4, va},     {"di", di, BH * T * 4, 4},
+      {"df", df, BH * T * 4, 4},            {"d_o", d_o, BH * T * dvv * 4, va},
+      {"dC0", dC0, BH * dqk * dvv * 4, va}, {"dn0", dn0, BH * dqk * 4, 4},
       {"dm0", dm0, BH * 4, 4},
   };
   const int nb = sizeof(bufs) / sizeof(bufs[0]);

@@ -472,8 +472,26 @@ hipError_t launch_typed(const BwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Chunk 64 (bf16 q, k, v): the state pass on the vector ALUs, the reverse
+// pass on MFMA (bwd_mfma.hip) with 64 value columns per workgroup.
+template <typename T>
+hipError_t launch_mfma(const BwdArgs& a, hipStream_t st) {
+  const int64_t ntok = a.B * a.H * a.T;
+  const int ncb = static_cast<int>(a.dv / 64);
+  const int nc = static_cast<int>(a.T / 64);
+  const unsigned tok_blocks = static_cast<unsigned>((ntok + NTB / 64 - 1) / (NTB / 64));
+  bwd_beta_kernel<T><<<tok_blocks, NTB, 0, st>>>(a);
+  bwd_states_kernel<T, 32, 64><<<static_cast<unsigned>(a.B * a.H * (a.dv / 32)), NTB, 0, st>>>(a);
+  const hipError_t e = launch_bwd_rev_mfma(a, st);
+  if (e != hipSuccess) return e;
+  bwd_tok_kernel<T><<<tok_blocks, NTB, 0, st>>>(a, ncb);
+  bwd_head_kernel<<<static_cast<unsigned>(a.B * a.H), NTB, 0, st>>>(a, ncb, nc);
+  return hipGetLastError();
+}
+
 template <typename T, typename TO>
 hipError_t launch_dt(const BwdArgs& a, hipStream_t st) {
+  if (a.L == 64) return launch_mfma<T>(a, st);
   const int TV = bwd_tile_columns(a);
   if (a.L == 16) return TV == 32 ? launch_typed<T, TO, 32, 16>(a, st) : launch_typed<T, TO, 16, 16>(a, st);
   return TV == 32 ? launch_typed<T, TO, 32, 32>(a, st) : launch_typed<T, TO, 16, 32>(a, st);
@@ -483,9 +501,13 @@ size_t round_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 }  // namespace
 
-int bwd_tile_columns(const BwdArgs& a) { return a.dv % 32 == 0 ? 32 : 16; }
+int bwd_tile_columns(const BwdArgs& a) {
+  if (a.L == 64) return 64;
+  return a.dv % 32 == 0 ? 32 : 16;
+}
 
 bool bwd_supported(const BwdArgs& a) {
+  if (a.L == 64) return bwd_mfma_supported(a);
   const int TV = a.dv % 32 == 0 ? 32 : 16;
   return (a.L == 16 || a.L == 32) && a.T % a.L == 0 && a.dqk <= 256 && a.dqk % (NTB / TV) == 0 &&
          a.dv % 16 == 0;
@@ -496,7 +518,7 @@ size_t bwd_workspace(const BwdArgs& a, size_t offsets[8]) {
   const size_t BH = static_cast<size_t>(a.B * a.H), T = static_cast<size_t>(a.T);
   const size_t nb = static_cast<size_t>(a.T / a.L) + 1, dqk = static_cast<size_t>(a.dqk);
   const size_t dv = static_cast<size_t>(a.dv);
-  const size_t ncb = dv / static_cast<size_t>(a.dv % 32 == 0 ? 32 : 16);
+  const size_t ncb = dv / static_cast<size_t>(bwd_tile_columns(a));
   const size_t sizes[8] = {BH * nb * dqk * dv * 4, BH * nb * dqk * 4, BH * nb * 4, BH * T * 4,
                            ncb * BH * T * dqk * 4, ncb * BH * T * dqk * 4, BH * T * 4, ncb * BH * 4};
   size_t off = 0;

@@ -1,0 +1,492 @@
+// Reverse pass of the chunkwise backward on bf16 MFMA (gfx950): chunk 64,
+// 64 value columns per workgroup, d_qk in {64, 128, 256}, bf16 q/k/v/h/dh.
+//
+// The same gradient as the float32 reverse pass in bwd.hip (the derivative of
+// the forward pass of the xLSTM post, llms.blog, section 3 "Associative
+// Matrix Cell State" and "The Parallel Dual Form", with the running maximum of
+// section 2 "The Normalizer State and Numerical Stabilization"), with every
+// matrix product on 16x16x32 MFMAs.  Per chunk of 64 tokens, with the stored
+// state (C~_s, n~_s, m_s) and the carried memory gradient dC:
+//
+//   S^T = K Q^T,  DS = D (.) S            (masked, bf16 in LDS; row sums fp32)
+//   r = sigmoid(o~) dh / den,  g r,  w V (bf16 in LDS)
+//   W = D (.) (R V^T + dnq)               (bf16 in LDS)
+//   dq^T = K^T W^T + C~_s (g R)^T  (+ g dnq n~_s)
+//   dk^T = Q^T W + dC (w V)^T      (+ w dn)
+//   dv^T = R^T DS + w (dC^T K^T)
+//   dC^T <- g_L dC^T + (g R)^T Q
+//
+// Operands are read from swizzled [rows][64] bf16 LDS tiles either as row
+// fragments (8 consecutive columns, ds_read_b128) or as transposed column
+// fragments (8 consecutive rows, two ds_read_b64_tr_b16), both in natural
+// index order.  The memory gradient is carried transposed (dC^T tiles, one
+// 16-column block per wave), which makes its bf16 copy for the products a run
+// of 4 consecutive columns per lane.  The products round their operands to
+// bf16 (accumulation stays float32); q, k, v are exact.
+#include "common.hpp"
+#include "kernels.hpp"
+#include "mfma_util.hpp"
+
+namespace mlstm {
+namespace {
+
+using namespace mk;
+
+constexpr int NT4 = 256;           // 4 waves
+constexpr int LC = 64;             // chunk
+constexpr int TVC = 64;            // value columns per workgroup
+constexpr int TB = 64 * 128;       // bytes of a [64][64] bf16 tile
+
+__device__ __forceinline__ bf16x8 rowfrag(const char* t, int r, int c) {
+  return as_bf16x8(lds_ld16(t, swz(r, c)));
+}
+// X[l16][8g + e] = M[k0 + 8g + e][m0 + l16] of the tile M at t
+__device__ __forceinline__ bf16x8 colfrag(const char* t, int k0, int m0, int g, int kr, int kq) {
+  return join(lds_tr(t, swz(k0 + 8 * g + kr, m0 + 4 * kq)), lds_tr(t, swz(k0 + 8 * g + 4 + kr, m0 + 4 * kq)));
+}
+// the 64-column tile of a wide [64][DK] matrix holding column c
+__device__ __forceinline__ const char* wide(const char* base, int c) { return base + (c >> 6) * TB; }
+
+struct Gate64 {
+  float u[LC], M[LC], m[LC], g[LC], w[LC];
+};
+
+__device__ __forceinline__ void gate_scan64(const BwdArgs& a, int64_t tok0, float ms, Gate64& G) {
+  const int lane = threadIdx.x & 63;
+  const float fpre = a.f_pre[tok0 + lane];
+  const float lf = a.fgate_exp ? fpre : log_sigmoid(fpre);
+  const float bc = scan_add(lf);
+  const float u = a.i_pre[tok0 + lane] - bc;
+  const float Mx = fmaxf(ms, scan_max(u));
+  const float ML = __shfl(Mx, LC - 1, 64);
+  G.u[lane] = u;
+  G.M[lane] = Mx;
+  G.m[lane] = bc + Mx;
+  G.g[lane] = __expf(ms - Mx);
+  G.w[lane] = __expf(u - ML);
+}
+
+__device__ __forceinline__ uint32_t pk2(float a, float b) { return cvt2(a, b); }
+
+template <int DK, typename TO>
+__global__ __launch_bounds__(NT4, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
+  constexpr int NXT = DK / 16;      // 16-row tiles of x (d_qk)
+  constexpr int XPW = NXT / 4;      // x tiles per wave in the dq / dk products
+  constexpr int NQT = DK / 64;
+  __shared__ __align__(1024) char sQ[NQT * TB];
+  __shared__ __align__(1024) char sK[NQT * TB];
+  __shared__ __align__(1024) char sV[TB];
+  __shared__ __align__(1024) char sWV[TB];
+  __shared__ __align__(1024) char sR[TB];
+  __shared__ __align__(1024) char sGR[TB];
+  __shared__ __align__(1024) char sW[TB];
+  __shared__ __align__(1024) char sDS[TB];
+  __shared__ __align__(1024) char sCX[DK * 128];   // [DK][64]: C~_s, then dC
+  __shared__ float sN[DK], sDn[DK];
+  __shared__ float sRs[4][LC];
+  __shared__ float sQn[LC], sDen[LC], sDnq[LC], sBeta[LC];
+  __shared__ Gate64 G;
+  __shared__ float sRed[4];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+  const int kr = l16 >> 2, kq = l16 & 3;
+  const int ncb = static_cast<int>(a.dv / TVC);
+  const int64_t bh = blockIdx.x / ncb;
+  const int cb = blockIdx.x % ncb;
+  const bool lead = cb == 0;
+  const int dv = static_cast<int>(a.dv);
+  const int64_t T = a.T;
+  const int nc = static_cast<int>(T / LC);
+  const int64_t nb = nc + 1;
+  const int64_t BH = a.B * a.H;
+  const int c0 = cb * TVC;
+
+  // carried dC^T: tile xt holds dC^T[b = 16 wave + 4 g + e][x = 16 xt + l16]
+  f32x4 dCt[NXT];
+#pragma unroll
+  for (int xt = 0; xt < NXT; ++xt) {
+    dCt[xt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (a.dC1) {
+      const float4 v4 = *reinterpret_cast<const float4*>(
+          a.dC1 + (bh * DK + xt * 16 + l16) * dv + c0 + wave * 16 + 4 * g);
+      dCt[xt] = f32x4{v4.x, v4.y, v4.z, v4.w};
+    }
+  }
+  for (int x = tid; x < DK; x += NT4) sDn[x] = a.dn1 ? a.dn1[bh * DK + x] : 0.0f;
+
+  for (int c = nc - 1; c >= 0; --c) {
+    const int64_t tok0 = bh * T + static_cast<int64_t>(c) * LC;
+    const float ms = a.ws_m[bh * nb + c];
+    __syncthreads();
+    // ---- loads: gates, Q, K, V (own columns), C~_s (own columns, to bf16), n~_s, beta
+    if (wave == 0) gate_scan64(a, tok0, ms, G);
+    {
+      const bf16_t* q = static_cast<const bf16_t*>(a.q) + tok0 * DK;
+      const bf16_t* k = static_cast<const bf16_t*>(a.k) + tok0 * DK;
+#pragma unroll
+      for (int p = 0; p < LC * DK / 8 / NT4; ++p) {
+        const int e = tid + p * NT4;
+        const int r = e / (DK / 8), cc = (e % (DK / 8)) * 8;
+        const uint4 vq = *reinterpret_cast<const uint4*>(q + r * DK + cc);
+        const uint4 vk = *reinterpret_cast<const uint4*>(k + r * DK + cc);
+        *reinterpret_cast<uint4*>(sQ + (cc >> 6) * TB + swz(r, cc & 63)) = vq;
+        *reinterpret_cast<uint4*>(sK + (cc >> 6) * TB + swz(r, cc & 63)) = vk;
+      }
+      const bf16_t* v = static_cast<const bf16_t*>(a.v) + tok0 * dv + c0;
+#pragma unroll
+      for (int p = 0; p < LC * TVC / 8 / NT4; ++p) {
+        const int e = tid + p * NT4;
+        const int r = e >> 3, cc = (e & 7) * 8;
+        *reinterpret_cast<uint4*>(sV + swz(r, cc)) = *reinterpret_cast<const uint4*>(v + static_cast<int64_t>(r) * dv + cc);
+      }
+      const float* Cs = a.ws_C + ((bh * nb + c) * DK) * dv + c0;
+#pragma unroll
+      for (int p = 0; p < DK * TVC / 8 / NT4; ++p) {
+        const int e = tid + p * NT4;
+        const int r = e >> 3, cc = (e & 7) * 8;
+        const float4 x0 = *reinterpret_cast<const float4*>(Cs + static_cast<int64_t>(r) * dv + cc);
+        const float4 x1 = *reinterpret_cast<const float4*>(Cs + static_cast<int64_t>(r) * dv + cc + 4);
+        *reinterpret_cast<uint4*>(sCX + swz(r, cc)) =
+            make_uint4(pk2(x0.x, x0.y), pk2(x0.z, x0.w), pk2(x1.x, x1.y), pk2(x1.z, x1.w));
+      }
+    }
+    for (int x = tid; x < DK; x += NT4) sN[x] = a.ws_n[(bh * nb + c) * DK + x];
+    if (tid < LC) sBeta[tid] = a.ws_beta[tok0 + tid];
+    __syncthreads();
+
+    // ---- S^T = K Q^T for key tile jt = wave; DS = D (.) S to LDS; row sums
+    {
+      f32x4 acc[4];
+#pragma unroll
+      for (int it = 0; it < 4; ++it) acc[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < DK / 32; ++ks) {
+        const int x0 = 32 * ks;
+        const bf16x8 A = rowfrag(wide(sK, x0), wave * 16 + l16, (x0 & 63) + 8 * g);
+#pragma unroll
+        for (int it = 0; it < 4; ++it)
+          acc[it] = mfma16x16x32(A, rowfrag(wide(sQ, x0), it * 16 + l16, (x0 & 63) + 8 * g), acc[it]);
+      }
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int i = it * 16 + l16;
+        const float Mi = G.M[i];
+        float ds[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = wave * 16 + 4 * g + e;
+          ds[e] = j <= i ? __expf(G.u[j] - Mi) * acc[it][e] : 0.0f;
+        }
+        *reinterpret_cast<uint2*>(sDS + swz(i, wave * 16 + 4 * g)) = make_uint2(pk2(ds[0], ds[1]), pk2(ds[2], ds[3]));
+        const float rs = sum_groups((ds[0] + ds[1]) + (ds[2] + ds[3]));
+        if (g == 0) sRs[wave][i] = rs;
+      }
+    }
+    // q . n~_s (four threads per token)
+    {
+      const int i = tid >> 2, qq = tid & 3;
+      float s = 0.0f;
+#pragma unroll
+      for (int x8 = qq * (DK / 4); x8 < (qq + 1) * (DK / 4); x8 += 8) {
+        const uint4 v8 = lds_ld16(wide(sQ, x8), swz(i, x8 & 63));
+        s += bf_lo(v8.x) * sN[x8] + bf_hi(v8.x) * sN[x8 + 1] + bf_lo(v8.y) * sN[x8 + 2] +
+             bf_hi(v8.y) * sN[x8 + 3] + bf_lo(v8.z) * sN[x8 + 4] + bf_hi(v8.z) * sN[x8 + 5] +
+             bf_lo(v8.w) * sN[x8 + 6] + bf_hi(v8.w) * sN[x8 + 7];
+      }
+      s += __shfl_xor(s, 1, 64);
+      s += __shfl_xor(s, 2, 64);
+      if (qq == 0) sQn[i] = s;
+    }
+    __syncthreads();
+    // ---- denominators and the normalizer gradient
+    if (tid < LC) {
+      const int i = tid;
+      const float nq = G.g[i] * sQn[i] + ((sRs[0][i] + sRs[1][i]) + (sRs[2][i] + sRs[3][i]));
+      const float floor_ = __expf(-G.m[i]);
+      const float den = fmaxf(fabsf(nq), floor_);
+      sDen[i] = den;
+      sDnq[i] = fabsf(nq) >= floor_ ? (nq >= 0.0f ? -sBeta[i] / den : sBeta[i] / den) : 0.0f;
+    }
+    __syncthreads();
+    // ---- r, g r, w V (bf16 to LDS) and do~ (16 columns per thread)
+    {
+      const int i = tid >> 2, b0 = (tid & 3) * 16;
+      const int64_t gi = (tok0 + i) * dv + c0 + b0;
+      const float inv = 1.0f / sDen[i];
+      const float gi_ = G.g[i], wi = G.w[i];
+      const bf16_t* dh = static_cast<const bf16_t*>(a.dh) + gi;
+      uint32_t rp[8], gp[8], wp[8];
+#pragma unroll
+      for (int h8 = 0; h8 < 2; ++h8) {
+        const uint4 d8 = *reinterpret_cast<const uint4*>(dh + 8 * h8);
+        const uint4 v8 = lds_ld16(sV, swz(i, b0 + 8 * h8));
+        float dhv[8] = {bf_lo(d8.x), bf_hi(d8.x), bf_lo(d8.y), bf_hi(d8.y),
+                        bf_lo(d8.z), bf_hi(d8.z), bf_lo(d8.w), bf_hi(d8.w)};
+        float vv[8] = {bf_lo(v8.x), bf_hi(v8.x), bf_lo(v8.y), bf_hi(v8.y),
+                       bf_lo(v8.z), bf_hi(v8.z), bf_lo(v8.w), bf_hi(v8.w)};
+        float gate[8];
+        if (a.o_pre) {
+          const uint4 h8v = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(a.h) + gi + 8 * h8);
+          const float hv[8] = {bf_lo(h8v.x), bf_hi(h8v.x), bf_lo(h8v.y), bf_hi(h8v.y),
+                               bf_lo(h8v.z), bf_hi(h8v.z), bf_lo(h8v.w), bf_hi(h8v.w)};
+          float ov[8];
+          if (sizeof(TO) == 4) {
+            const float4 o0 = *reinterpret_cast<const float4*>(static_cast<const float*>(a.o_pre) + gi + 8 * h8);
+            const float4 o1 = *reinterpret_cast<const float4*>(static_cast<const float*>(a.o_pre) + gi + 8 * h8 + 4);
+            ov[0] = o0.x; ov[1] = o0.y; ov[2] = o0.z; ov[3] = o0.w;
+            ov[4] = o1.x; ov[5] = o1.y; ov[6] = o1.z; ov[7] = o1.w;
+          } else {
+            const uint4 o8 = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(a.o_pre) + gi + 8 * h8);
+            ov[0] = bf_lo(o8.x); ov[1] = bf_hi(o8.x); ov[2] = bf_lo(o8.y); ov[3] = bf_hi(o8.y);
+            ov[4] = bf_lo(o8.z); ov[5] = bf_hi(o8.z); ov[6] = bf_lo(o8.w); ov[7] = bf_hi(o8.w);
+          }
+          float dov[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            gate[e] = sigmoid_fast(ov[e]);
+            dov[e] = dhv[e] * hv[e] * (1.0f - gate[e]);
+          }
+          float* dO = a.d_o + gi + 8 * h8;
+          *reinterpret_cast<float4*>(dO) = make_float4(dov[0], dov[1], dov[2], dov[3]);
+          *reinterpret_cast<float4*>(dO + 4) = make_float4(dov[4], dov[5], dov[6], dov[7]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) gate[e] = 1.0f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const float r0 = gate[e] * dhv[e] * inv, r1 = gate[e + 1] * dhv[e + 1] * inv;
+          rp[4 * h8 + e / 2] = pk2(r0, r1);
+          gp[4 * h8 + e / 2] = pk2(gi_ * r0, gi_ * r1);
+          wp[4 * h8 + e / 2] = pk2(wi * vv[e], wi * vv[e + 1]);
+        }
+      }
+#pragma unroll
+      for (int h8 = 0; h8 < 2; ++h8) {
+        *reinterpret_cast<uint4*>(sR + swz(i, b0 + 8 * h8)) = make_uint4(rp[4 * h8], rp[4 * h8 + 1], rp[4 * h8 + 2], rp[4 * h8 + 3]);
+        *reinterpret_cast<uint4*>(sGR + swz(i, b0 + 8 * h8)) = make_uint4(gp[4 * h8], gp[4 * h8 + 1], gp[4 * h8 + 2], gp[4 * h8 + 3]);
+        *reinterpret_cast<uint4*>(sWV + swz(i, b0 + 8 * h8)) = make_uint4(wp[4 * h8], wp[4 * h8 + 1], wp[4 * h8 + 2], wp[4 * h8 + 3]);
+      }
+    }
+    __syncthreads();
+    // ---- W = D (.) (R V^T + dnq): (R V^T)^T = V R^T for key tile jt = wave
+    {
+      f32x4 acc[4];
+#pragma unroll
+      for (int it = 0; it < 4; ++it) acc[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < TVC / 32; ++ks) {
+        const bf16x8 A = rowfrag(sV, wave * 16 + l16, 32 * ks + 8 * g);
+#pragma unroll
+        for (int it = 0; it < 4; ++it)
+          acc[it] = mfma16x16x32(A, rowfrag(sR, it * 16 + l16, 32 * ks + 8 * g), acc[it]);
+      }
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int i = it * 16 + l16;
+        const float Mi = G.M[i], dq_ = lead ? sDnq[i] : 0.0f;
+        float wv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = wave * 16 + 4 * g + e;
+          wv[e] = j <= i ? __expf(G.u[j] - Mi) * (acc[it][e] + dq_) : 0.0f;
+        }
+        *reinterpret_cast<uint2*>(sW + swz(i, wave * 16 + 4 * g)) = make_uint2(pk2(wv[0], wv[1]), pk2(wv[2], wv[3]));
+      }
+    }
+    __syncthreads();
+    // ---- dq^T = K^T W^T + C~_s (g R)^T (+ g dnq n~_s): x tiles of this wave x query tiles
+    {
+      f32x4 acc[XPW][4];
+#pragma unroll
+      for (int p = 0; p < XPW; ++p)
+#pragma unroll
+        for (int it = 0; it < 4; ++it) acc[p][it] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        bf16x8 Bw[4], Bg[4];
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          Bw[it] = rowfrag(sW, it * 16 + l16, 32 * ks + 8 * g);
+          Bg[it] = rowfrag(sGR, it * 16 + l16, 32 * ks + 8 * g);
+        }
+#pragma unroll
+        for (int p = 0; p < XPW; ++p) {
+          const int xt = wave * XPW + p;
+          const bf16x8 Ak = colfrag(wide(sK, xt * 16), 32 * ks, (xt * 16) & 63, g, kr, kq);
+          const bf16x8 Ac = rowfrag(sCX, xt * 16 + l16, 32 * ks + 8 * g);
+#pragma unroll
+          for (int it = 0; it < 4; ++it) {
+            acc[p][it] = mfma16x16x32(Ak, Bw[it], acc[p][it]);
+            acc[p][it] = mfma16x16x32(Ac, Bg[it], acc[p][it]);
+          }
+        }
+      }
+      float* out = a.ws_dq + ((static_cast<int64_t>(cb) * BH + bh) * T + static_cast<int64_t>(c) * LC) * DK;
+#pragma unroll
+      for (int p = 0; p < XPW; ++p) {
+        const int x0 = (wave * XPW + p) * 16 + 4 * g;
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const int i = it * 16 + l16;
+          const float f = lead ? G.g[i] * sDnq[i] : 0.0f;
+          *reinterpret_cast<float4*>(out + i * DK + x0) =
+              make_float4(acc[p][it][0] + f * sN[x0], acc[p][it][1] + f * sN[x0 + 1],
+                          acc[p][it][2] + f * sN[x0 + 2], acc[p][it][3] + f * sN[x0 + 3]);
+        }
+      }
+    }
+    __syncthreads();   // C~_s is no longer read
+    // ---- dC (carried, float32) to LDS as bf16 [x][b]
+#pragma unroll
+    for (int xt = 0; xt < NXT; ++xt)
+      *reinterpret_cast<uint2*>(sCX + swz(xt * 16 + l16, wave * 16 + 4 * g)) =
+          make_uint2(pk2(dCt[xt][0], dCt[xt][1]), pk2(dCt[xt][2], dCt[xt][3]));
+    __syncthreads();
+    // ---- dk^T = Q^T W + dC (w V)^T (+ w dn)
+    {
+      f32x4 acc[XPW][4];
+#pragma unroll
+      for (int p = 0; p < XPW; ++p)
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) acc[p][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        bf16x8 Bw[4], Bv[4];
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+          Bw[jt] = colfrag(sW, 32 * ks, jt * 16, g, kr, kq);
+          Bv[jt] = rowfrag(sWV, jt * 16 + l16, 32 * ks + 8 * g);
+        }
+#pragma unroll
+        for (int p = 0; p < XPW; ++p) {
+          const int xt = wave * XPW + p;
+          const bf16x8 Aq = colfrag(wide(sQ, xt * 16), 32 * ks, (xt * 16) & 63, g, kr, kq);
+          const bf16x8 Ac = rowfrag(sCX, xt * 16 + l16, 32 * ks + 8 * g);
+#pragma unroll
+          for (int jt = 0; jt < 4; ++jt) {
+            acc[p][jt] = mfma16x16x32(Aq, Bw[jt], acc[p][jt]);
+            acc[p][jt] = mfma16x16x32(Ac, Bv[jt], acc[p][jt]);
+          }
+        }
+      }
+      float* out = a.ws_dk + ((static_cast<int64_t>(cb) * BH + bh) * T + static_cast<int64_t>(c) * LC) * DK;
+#pragma unroll
+      for (int p = 0; p < XPW; ++p) {
+        const int x0 = (wave * XPW + p) * 16 + 4 * g;
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+          const int j = jt * 16 + l16;
+          const float f = lead ? G.w[j] : 0.0f;
+          *reinterpret_cast<float4*>(out + j * DK + x0) =
+              make_float4(acc[p][jt][0] + f * sDn[x0], acc[p][jt][1] + f * sDn[x0 + 1],
+                          acc[p][jt][2] + f * sDn[x0 + 2], acc[p][jt][3] + f * sDn[x0 + 3]);
+        }
+      }
+    }
+    // ---- dv^T = R^T DS + w (dC^T K^T) for value tile bt = wave
+    {
+      f32x4 accA[4], accB[4];
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        accA[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        accB[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 Ar = colfrag(sR, 32 * ks, wave * 16, g, kr, kq);
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) accA[jt] = mfma16x16x32(Ar, colfrag(sDS, 32 * ks, jt * 16, g, kr, kq), accA[jt]);
+      }
+#pragma unroll
+      for (int ks = 0; ks < DK / 32; ++ks) {
+        const int x0 = 32 * ks;
+        const bf16x8 Ac = colfrag(sCX, x0, wave * 16, g, kr, kq);
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt)
+          accB[jt] = mfma16x16x32(Ac, rowfrag(wide(sK, x0), jt * 16 + l16, (x0 & 63) + 8 * g), accB[jt]);
+      }
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        const int j = jt * 16 + l16;
+        const float wj = G.w[j];
+        *reinterpret_cast<float4*>(a.d_v + (tok0 + j) * dv + c0 + wave * 16 + 4 * g) =
+            make_float4(accA[jt][0] + wj * accB[jt][0], accA[jt][1] + wj * accB[jt][1],
+                        accA[jt][2] + wj * accB[jt][2], accA[jt][3] + wj * accB[jt][3]);
+      }
+    }
+    // ---- dC^T <- g_L dC^T + (g R)^T Q
+    {
+      const float gL = G.g[LC - 1];
+#pragma unroll
+      for (int xt = 0; xt < NXT; ++xt) dCt[xt] *= gL;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 Ag = colfrag(sGR, 32 * ks, wave * 16, g, kr, kq);
+#pragma unroll
+        for (int xt = 0; xt < NXT; ++xt)
+          dCt[xt] = mfma16x16x32(Ag, colfrag(wide(sQ, xt * 16), 32 * ks, (xt * 16) & 63, g, kr, kq), dCt[xt]);
+      }
+    }
+    __syncthreads();   // every read of sDn (dk) is done
+    // ---- dn <- g_L dn + sum_i g_i dnq_i q_i
+    for (int x = tid; x < DK; x += NT4) {
+      float s = G.g[LC - 1] * sDn[x];
+      const char* qt = wide(sQ, x);
+      for (int i = 0; i < LC; ++i) {
+        const bf16_t qv = *reinterpret_cast<const bf16_t*>(qt + swz(i, x & 63));
+        s += G.g[i] * sDnq[i] * bf2f(qv);
+      }
+      sDn[x] = s;
+    }
+  }
+  // ---- the initial state's gradients and dm0's share
+  __syncthreads();
+  float part = 0.0f;
+#pragma unroll
+  for (int xt = 0; xt < NXT; ++xt) {
+    const int64_t gi = (bh * DK + xt * 16 + l16) * dv + c0 + wave * 16 + 4 * g;
+    if (a.dC0) *reinterpret_cast<float4*>(a.dC0 + gi) = make_float4(dCt[xt][0], dCt[xt][1], dCt[xt][2], dCt[xt][3]);
+    if (a.C0) {
+      const float4 c4 = *reinterpret_cast<const float4*>(a.C0 + gi);
+      part += (dCt[xt][0] * c4.x + dCt[xt][1] * c4.y) + (dCt[xt][2] * c4.z + dCt[xt][3] * c4.w);
+    }
+  }
+  if (lead) {
+    for (int x = tid; x < DK; x += NT4) {
+      if (a.dn0) a.dn0[bh * DK + x] = sDn[x];
+      if (a.C0) part += sDn[x] * a.n0[bh * DK + x];
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
+  if (lane == 0) sRed[wave] = part;
+  __syncthreads();
+  if (tid == 0) a.ws_dm0[static_cast<int64_t>(cb) * BH + bh] = (sRed[0] + sRed[1]) + (sRed[2] + sRed[3]);
+}
+
+template <int DK>
+hipError_t launch_dk(const BwdArgs& a, hipStream_t st) {
+  const unsigned wgs = static_cast<unsigned>(a.B * a.H * (a.dv / TVC));
+  if (a.o_mode == O_BF16) bwd_rev_mfma_kernel<DK, bf16_t><<<wgs, NT4, 0, st>>>(a);
+  else bwd_rev_mfma_kernel<DK, float><<<wgs, NT4, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool bwd_mfma_supported(const BwdArgs& a) {
+  return a.qkv_bf16 && a.L == LC && a.T % LC == 0 && a.dv % TVC == 0 &&
+         (a.dqk == 64 || a.dqk == 128 || a.dqk == 256);
+}
+
+hipError_t launch_bwd_rev_mfma(const BwdArgs& a, hipStream_t st) {
+  switch (a.dqk) {
+    case 64: return launch_dk<64>(a, st);
+    case 128: return launch_dk<128>(a, st);
+    default: return launch_dk<256>(a, st);
+  }
+}
+
+}  // namespace mlstm

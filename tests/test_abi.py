@@ -223,10 +223,27 @@ def test_bwd_pairing_rules(lib):
 
 
 def test_bwd_unsupported(lib):
+    # chunk 64 is the MFMA path: bf16 q/k/v, d_v % 64 == 0, d_qk in {64, 128, 256}
     assert bwd_call(lib, P(), chunk=64)[0] == M.MLSTM_ERR_UNSUPPORTED
+    assert bwd_call(lib, P(dqk=64, dv=64), chunk=64)[0] == M.MLSTM_ERR_UNSUPPORTED
+    assert bwd_call(lib, P(dqk=96, dv=64, qkv=1), chunk=64)[0] == M.MLSTM_ERR_UNSUPPORTED
+    assert bwd_call(lib, P(dqk=64, dv=32, qkv=1), chunk=64)[0] == M.MLSTM_ERR_UNSUPPORTED
+    assert bwd_call(lib, P(T=96, dqk=64, dv=64, qkv=1), chunk=64)[0] == M.MLSTM_ERR_UNSUPPORTED
+    assert bwd_call(lib, P(), chunk=128)[0] == M.MLSTM_ERR_UNSUPPORTED
     assert bwd_call(lib, P(T=40))[0] == M.MLSTM_ERR_UNSUPPORTED
     assert bwd_call(lib, P(dqk=512, dv=32))[0] == M.MLSTM_ERR_UNSUPPORTED
     assert bwd_call(lib, P(dqk=272, dv=48))[0] == M.MLSTM_ERR_UNSUPPORTED
+
+
+def test_bwd_chunk64_alignment(lib):
+    """Chunk 64 moves the [.., d_v] arrays in 16-byte pieces: 4-byte
+    aligned dh is rejected there (and accepted by chunk 32)."""
+    p = P(dqk=64, dv=64, qkv=1)
+    odd = ctypes.c_void_p(FAKE + 10 * (1 << 30) + 4)
+    r, det = bwd_call(lib, p, chunk=64, dh=odd)
+    assert r == M.MLSTM_ERR_INVALID_ARG and "dh" in det and "aligned" in det
+    r, det = bwd_call(lib, p, chunk=32, dh=odd, ws_bytes=0)
+    assert r == M.MLSTM_ERR_INVALID_ARG and "workspace" in det
 
 
 def test_bwd_workspace(lib):

@@ -91,6 +91,11 @@ CASES = [
     ("bf16 d128 chunk 32", torch.bfloat16, 1, 2, 256, 128, 128, 32, "sigmoid", True, torch.float32, True, True),
     ("bf16 d256 chunk 32 bf16 o", torch.bfloat16, 1, 2, 256, 256, 256, 32, "sigmoid", True, torch.bfloat16, True, True),
     ("bf16 d256/512 chunk 16", torch.bfloat16, 1, 1, 128, 256, 512, 16, "sigmoid", True, torch.float32, True, False),
+    # chunk 64: the reverse pass on MFMA (bf16 operands, float32 accumulation)
+    ("bf16 d64 chunk 64", torch.bfloat16, 1, 2, 256, 64, 64, 64, "sigmoid", True, torch.float32, True, True),
+    ("bf16 d128/192 chunk 64 exp gate bf16 o", torch.bfloat16, 2, 1, 192, 128, 192, 64, "exp", True, torch.bfloat16, False, True),
+    ("bf16 d256 chunk 64 no o", torch.bfloat16, 1, 2, 256, 256, 256, 64, "sigmoid", False, None, True, False),
+    ("bf16 d256/128 chunk 64 single chunk", torch.bfloat16, 1, 3, 64, 256, 128, 64, "sigmoid", True, torch.float32, True, True),
 ]
 
 
@@ -114,15 +119,24 @@ def test_bwd_chunk_independent():
         assert slice_rel_err(g16[k], g32[k]) < 1e-5, k
 
 
-def test_bwd_c2_sampled_heads():
+@pytest.fixture(scope="module")
+def c2_case():
     """The measured workload's shape (B=8, H=8, T=8192, d=256, bf16, f32 o-gate,
-    random state in, final-state gradient), chunk 32: the GPU computes every
-    head, the oracle two sampled heads."""
+    random state in, final-state gradient), with the oracle's gradients of two
+    sampled heads."""
     log("bwd c2 full: inputs")
     inp, gin = make_inputs(2, torch.bfloat16, 8, 8, 8192, 256, 256)
-    log("bwd c2 full: GPU")
-    g = run_gpu(inp, gin, 32, "sigmoid", torch.float32)
     heads = sample_heads(8, 8, 2, seed=5)
     log(f"bwd c2 full: oracle on heads {heads}")
     r = run_oracle(inp, gin, "sigmoid", torch.float32, heads=heads)
-    compare(g, r, TOL_BF16, "c2 sampled", True, heads=heads)
+    return inp, gin, heads, r
+
+
+@pytest.mark.parametrize("chunk", [32, 64])
+def test_bwd_c2_sampled_heads(c2_case, chunk):
+    """The GPU computes every head of the measured workload, the oracle two
+    sampled heads (chunk 32: the float32 reverse pass; chunk 64: MFMA)."""
+    inp, gin, heads, r = c2_case
+    log(f"bwd c2 full: GPU chunk {chunk}")
+    g = run_gpu(inp, gin, chunk, "sigmoid", torch.float32)
+    compare(g, r, TOL_BF16, f"c2 sampled chunk {chunk}", True, heads=heads)
