@@ -472,8 +472,8 @@ hipError_t launch_typed(const BwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Chunk 64 (bf16 q, k, v): the state pass on the vector ALUs, the reverse
-// pass on MFMA (bwd_mfma.hip) with 64 value columns per workgroup.
+// Chunk 64 (bf16 q, k, v): the state and reverse passes on MFMA
+// (bwd_mfma.hip) with 64 value columns per workgroup.
 template <typename T>
 hipError_t launch_mfma(const BwdArgs& a, hipStream_t st) {
   const int64_t ntok = a.B * a.H * a.T;
@@ -481,8 +481,9 @@ hipError_t launch_mfma(const BwdArgs& a, hipStream_t st) {
   const int nc = static_cast<int>(a.T / 64);
   const unsigned tok_blocks = static_cast<unsigned>((ntok + NTB / 64 - 1) / (NTB / 64));
   bwd_beta_kernel<T><<<tok_blocks, NTB, 0, st>>>(a);
-  bwd_states_kernel<T, 32, 64><<<static_cast<unsigned>(a.B * a.H * (a.dv / 32)), NTB, 0, st>>>(a);
-  const hipError_t e = launch_bwd_rev_mfma(a, st);
+  hipError_t e = launch_bwd_states_mfma(a, st);
+  if (e != hipSuccess) return e;
+  e = launch_bwd_rev_mfma(a, st);
   if (e != hipSuccess) return e;
   bwd_tok_kernel<T><<<tok_blocks, NTB, 0, st>>>(a, ncb);
   bwd_head_kernel<<<static_cast<unsigned>(a.B * a.H), NTB, 0, st>>>(a, ncb, nc);

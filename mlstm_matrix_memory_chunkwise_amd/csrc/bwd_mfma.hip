@@ -466,6 +466,146 @@ __global__ __launch_bounds__(NT4, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
   if (tid == 0) a.ws_dm0[static_cast<int64_t>(cb) * BH + bh] = (sRed[0] + sRed[1]) + (sRed[2] + sRed[3]);
 }
 
+// Chunk-boundary states for the reverse pass: (C~, n~, m) before every chunk
+// and after the last, C~_{c+1} = g_L C~_c + K^T (w (.) V) and
+// n~_{c+1} = g_L n~_c + K^T w.  Workgroup = (head, 64 value columns); the
+// state is carried transposed in float32 registers (wave w: value columns
+// 16 w..16 w + 15, all d_qk rows), w (.) V enters the MFMAs as a bf16 hi/lo
+// pair (about 16 significant bits; k is exact), n~ is a float32 sum on the
+// vector ALUs (column block 0 only, which also writes n~ and m).  The next
+// chunk's k and v are loaded into registers while the current one is used.
+template <int DK>
+__global__ __launch_bounds__(NT4, 1) void bwd_states_mfma_kernel(BwdArgs a) {
+  constexpr int NXT = DK / 16;
+  constexpr int NQT = DK / 64;
+  constexpr int KV = LC * DK / 8 / NT4;   // 16-byte pieces of k per thread
+  __shared__ __align__(1024) char sK[NQT * TB];
+  __shared__ __align__(1024) char sWH[TB];
+  __shared__ __align__(1024) char sWL[TB];
+  __shared__ Gate64 G;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, l16 = threadIdx.x & 15, g = (threadIdx.x & 63) >> 4;
+  const int kr = l16 >> 2, kq = l16 & 3;
+  const int ncb = static_cast<int>(a.dv / TVC);
+  const int64_t bh = blockIdx.x / ncb;
+  const int cb = blockIdx.x % ncb;
+  const int dv = static_cast<int>(a.dv);
+  const int64_t T = a.T;
+  const int nc = static_cast<int>(T / LC);
+  const int64_t nb = nc + 1;
+  const int c0 = cb * TVC;
+  const bool lead = cb == 0;
+
+  f32x4 Ct[NXT];
+#pragma unroll
+  for (int xt = 0; xt < NXT; ++xt) {
+    Ct[xt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (a.C0) {
+      const float4 v4 = *reinterpret_cast<const float4*>(
+          a.C0 + (bh * DK + xt * 16 + l16) * dv + c0 + wave * 16 + 4 * g);
+      Ct[xt] = f32x4{v4.x, v4.y, v4.z, v4.w};
+    }
+  }
+  float n = (a.C0 && tid < DK) ? a.n0[bh * DK + tid] : 0.0f;
+  float m = a.C0 ? a.m0[bh] : 0.0f;
+
+  // register prefetch of a chunk's k (KV pieces) and v (rows tid / 4,
+  // columns 16 (tid % 4) ..)
+  uint4 kb[KV], vb[2];
+  auto fetch = [&](int c) {
+    const int64_t tok0 = bh * T + static_cast<int64_t>(c) * LC;
+    const bf16_t* k = static_cast<const bf16_t*>(a.k) + tok0 * DK;
+#pragma unroll
+    for (int p = 0; p < KV; ++p) {
+      const int e = tid + p * NT4;
+      kb[p] = *reinterpret_cast<const uint4*>(k + (e / (DK / 8)) * DK + (e % (DK / 8)) * 8);
+    }
+    const bf16_t* v = static_cast<const bf16_t*>(a.v) + (tok0 + (tid >> 2)) * dv + c0 + (tid & 3) * 16;
+    vb[0] = *reinterpret_cast<const uint4*>(v);
+    vb[1] = *reinterpret_cast<const uint4*>(v + 8);
+  };
+  if (nc > 0) fetch(0);
+
+  for (int c = 0; c <= nc; ++c) {
+    // the stored state at boundary c
+    float* wsC = a.ws_C + (bh * nb + c) * DK * dv + c0 + wave * 16 + 4 * g;
+#pragma unroll
+    for (int xt = 0; xt < NXT; ++xt)
+      *reinterpret_cast<float4*>(wsC + static_cast<int64_t>(xt * 16 + l16) * dv) =
+          make_float4(Ct[xt][0], Ct[xt][1], Ct[xt][2], Ct[xt][3]);
+    if (lead) {
+      if (tid < DK) a.ws_n[(bh * nb + c) * DK + tid] = n;
+      if (tid == 0) a.ws_m[bh * nb + c] = m;
+    }
+    if (c == nc) break;
+    const int64_t tok0 = bh * T + static_cast<int64_t>(c) * LC;
+    __syncthreads();   // the previous chunk's reads of sK, sWH, sWL and G are done
+    if (wave == 0) gate_scan64(a, tok0, m, G);
+#pragma unroll
+    for (int p = 0; p < KV; ++p) {
+      const int e = tid + p * NT4;
+      const int cc = (e % (DK / 8)) * 8;
+      *reinterpret_cast<uint4*>(sK + (cc >> 6) * TB + swz(e / (DK / 8), cc & 63)) = kb[p];
+    }
+    const uint4 v0 = vb[0], v1 = vb[1];
+    if (c + 1 < nc) fetch(c + 1);
+    __syncthreads();
+    {
+      const int j = tid >> 2, b0 = (tid & 3) * 16;
+      const float wj = G.w[j];
+      const float x[16] = {bf_lo(v0.x), bf_hi(v0.x), bf_lo(v0.y), bf_hi(v0.y), bf_lo(v0.z), bf_hi(v0.z),
+                           bf_lo(v0.w), bf_hi(v0.w), bf_lo(v1.x), bf_hi(v1.x), bf_lo(v1.y), bf_hi(v1.y),
+                           bf_lo(v1.z), bf_hi(v1.z), bf_lo(v1.w), bf_hi(v1.w)};
+      uint32_t hp[8], lp[8];
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        const float y0 = wj * x[e], y1 = wj * x[e + 1];
+        const uint32_t h2 = pk2(y0, y1);
+        hp[e / 2] = h2;
+        lp[e / 2] = pk2(y0 - bf_lo(h2), y1 - bf_hi(h2));
+      }
+#pragma unroll
+      for (int h8 = 0; h8 < 2; ++h8) {
+        *reinterpret_cast<uint4*>(sWH + swz(j, b0 + 8 * h8)) = make_uint4(hp[4 * h8], hp[4 * h8 + 1], hp[4 * h8 + 2], hp[4 * h8 + 3]);
+        *reinterpret_cast<uint4*>(sWL + swz(j, b0 + 8 * h8)) = make_uint4(lp[4 * h8], lp[4 * h8 + 1], lp[4 * h8 + 2], lp[4 * h8 + 3]);
+      }
+    }
+    const float gL = G.g[LC - 1];
+    if (lead && tid < DK) {
+      const char* kt = wide(sK, tid);
+      float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll 8
+      for (int j = 0; j < LC; j += 2) {
+        s0 += G.w[j] * bf2f(*reinterpret_cast<const bf16_t*>(kt + swz(j, tid & 63)));
+        s1 += G.w[j + 1] * bf2f(*reinterpret_cast<const bf16_t*>(kt + swz(j + 1, tid & 63)));
+      }
+      n = gL * n + (s0 + s1);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int xt = 0; xt < NXT; ++xt) Ct[xt] *= gL;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 Ah = colfrag(sWH, 32 * ks, wave * 16, g, kr, kq);
+      const bf16x8 Al = colfrag(sWL, 32 * ks, wave * 16, g, kr, kq);
+#pragma unroll
+      for (int xt = 0; xt < NXT; ++xt) {
+        const bf16x8 Bk = colfrag(wide(sK, xt * 16), 32 * ks, (xt * 16) & 63, g, kr, kq);
+        Ct[xt] = mfma16x16x32(Ah, Bk, Ct[xt]);
+        Ct[xt] = mfma16x16x32(Al, Bk, Ct[xt]);
+      }
+    }
+    m = G.m[LC - 1];
+  }
+}
+
+template <int DK>
+hipError_t launch_states_dk(const BwdArgs& a, hipStream_t st) {
+  bwd_states_mfma_kernel<DK><<<static_cast<unsigned>(a.B * a.H * (a.dv / TVC)), NT4, 0, st>>>(a);
+  return hipGetLastError();
+}
+
 template <int DK>
 hipError_t launch_dk(const BwdArgs& a, hipStream_t st) {
   const unsigned wgs = static_cast<unsigned>(a.B * a.H * (a.dv / TVC));
@@ -479,6 +619,14 @@ hipError_t launch_dk(const BwdArgs& a, hipStream_t st) {
 bool bwd_mfma_supported(const BwdArgs& a) {
   return a.qkv_bf16 && a.L == LC && a.T % LC == 0 && a.dv % TVC == 0 &&
          (a.dqk == 64 || a.dqk == 128 || a.dqk == 256);
+}
+
+hipError_t launch_bwd_states_mfma(const BwdArgs& a, hipStream_t st) {
+  switch (a.dqk) {
+    case 64: return launch_states_dk<64>(a, st);
+    case 128: return launch_states_dk<128>(a, st);
+    default: return launch_states_dk<256>(a, st);
+  }
 }
 
 hipError_t launch_bwd_rev_mfma(const BwdArgs& a, hipStream_t st) {

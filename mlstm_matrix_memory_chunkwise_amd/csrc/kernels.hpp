@@ -114,8 +114,9 @@ bool bwd_supported(const BwdArgs& a);
 int bwd_tile_columns(const BwdArgs& a);
 size_t bwd_workspace(const BwdArgs& a, size_t offsets[8]);
 hipError_t launch_bwd(BwdArgs a, void* ws, hipStream_t stream);
-// Reverse pass on MFMA: bf16 q/k/v, chunk 64, d_v % 64 == 0, d_qk in {64, 128, 256}.
+// State and reverse passes on MFMA: bf16 q/k/v, chunk 64, d_v % 64 == 0, d_qk in {64, 128, 256}.
 bool bwd_mfma_supported(const BwdArgs& a);
+hipError_t launch_bwd_states_mfma(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_rev_mfma(const BwdArgs& a, hipStream_t stream);
 
 // Parallel (quadratic) form.
