@@ -466,33 +466,52 @@ __global__ __launch_bounds__(NT4, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
   if (tid == 0) a.ws_dm0[static_cast<int64_t>(cb) * BH + bh] = (sRed[0] + sRed[1]) + (sRed[2] + sRed[3]);
 }
 
+// Direct global -> LDS load of one chunk's k ([64][DK] bf16) into swizzled
+// [64 x 64] tiles: each wave instruction fills 8 rows of one tile (lane l:
+// row 8 rg + l / 8, 16-byte slot l % 8, which holds the global column piece
+// slot ^ ((row / 2) % 8)).  Waves 0..3 issue DK / 32 instructions each.
+template <int DK>
+__device__ __forceinline__ void dma_k_chunk(const BwdArgs& a, int64_t tok0, int wave, int lane, char* dst) {
+  constexpr int PER_WAVE = DK / 32;   // (DK / 64 tiles) x (8 row groups) / 4 waves
+  const bf16_t* k = static_cast<const bf16_t*>(a.k) + tok0 * DK;
+#pragma unroll
+  for (int q = 0; q < PER_WAVE; ++q) {
+    const int R = wave * PER_WAVE + q;
+    const int qt = R >> 3, rg = R & 7;
+    const int row = rg * 8 + (lane >> 3), slot = lane & 7;
+    const bf16_t* src = k + static_cast<int64_t>(row) * DK + qt * 64 + 8 * (slot ^ ((row >> 1) & 7));
+    dma16(src, static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(
+                   static_cast<int>(lds_addr(dst + qt * TB + rg * 1024)))));
+  }
+}
+
 // Chunk-boundary states for the reverse pass: (C~, n~, m) before every chunk
 // and after the last, C~_{c+1} = g_L C~_c + K^T (w (.) V) and
 // n~_{c+1} = g_L n~_c + K^T w.  Workgroup = (head, 64 value columns); the
 // state is carried transposed in float32 registers (wave w: value columns
 // 16 w..16 w + 15, all d_qk rows), w (.) V enters the MFMAs as a bf16 hi/lo
 // pair (about 16 significant bits; k is exact), n~ is a float32 sum on the
-// vector ALUs (column block 0 only, which also writes n~ and m).  The next
-// chunk's k and v are loaded into registers while the current one is used.
+// vector ALUs (column block 0 only, which also writes n~ and m).  k of the
+// next chunk streams into the other half of a double-buffered LDS tile while
+// the current one is used; v of the next chunk is held in registers.
 template <int DK>
 __global__ __launch_bounds__(NT4, 1) void bwd_states_mfma_kernel(BwdArgs a) {
   constexpr int NXT = DK / 16;
   constexpr int NQT = DK / 64;
-  constexpr int KV = LC * DK / 8 / NT4;   // 16-byte pieces of k per thread
-  __shared__ __align__(1024) char sK[NQT * TB];
+  __shared__ __align__(1024) char sK[2][NQT * TB];
   __shared__ __align__(1024) char sWH[TB];
   __shared__ __align__(1024) char sWL[TB];
   __shared__ Gate64 G;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, l16 = threadIdx.x & 15, g = (threadIdx.x & 63) >> 4;
+  const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const int kr = l16 >> 2, kq = l16 & 3;
   const int ncb = static_cast<int>(a.dv / TVC);
   const int64_t bh = blockIdx.x / ncb;
   const int cb = blockIdx.x % ncb;
   const int dv = static_cast<int>(a.dv);
   const int64_t T = a.T;
-  const int nc = static_cast<int>(T / LC);
+  const int nc = static_cast<int>(T / LC);   // >= 1
   const int64_t nb = nc + 1;
   const int c0 = cb * TVC;
   const bool lead = cb == 0;
@@ -510,24 +529,17 @@ __global__ __launch_bounds__(NT4, 1) void bwd_states_mfma_kernel(BwdArgs a) {
   float n = (a.C0 && tid < DK) ? a.n0[bh * DK + tid] : 0.0f;
   float m = a.C0 ? a.m0[bh] : 0.0f;
 
-  // register prefetch of a chunk's k (KV pieces) and v (rows tid / 4,
-  // columns 16 (tid % 4) ..)
-  uint4 kb[KV], vb[2];
-  auto fetch = [&](int c) {
-    const int64_t tok0 = bh * T + static_cast<int64_t>(c) * LC;
-    const bf16_t* k = static_cast<const bf16_t*>(a.k) + tok0 * DK;
-#pragma unroll
-    for (int p = 0; p < KV; ++p) {
-      const int e = tid + p * NT4;
-      kb[p] = *reinterpret_cast<const uint4*>(k + (e / (DK / 8)) * DK + (e % (DK / 8)) * 8);
-    }
-    const bf16_t* v = static_cast<const bf16_t*>(a.v) + (tok0 + (tid >> 2)) * dv + c0 + (tid & 3) * 16;
-    vb[0] = *reinterpret_cast<const uint4*>(v);
-    vb[1] = *reinterpret_cast<const uint4*>(v + 8);
-  };
-  if (nc > 0) fetch(0);
+  // v rows tid / 4, columns c0 + 16 (tid % 4) .. + 15 of a chunk
+  const bf16_t* vrow = static_cast<const bf16_t*>(a.v) + (bh * T + (tid >> 2)) * dv + c0 + (tid & 3) * 16;
+  uint4 nv0 = *reinterpret_cast<const uint4*>(vrow);
+  uint4 nv1 = *reinterpret_cast<const uint4*>(vrow + 8);
+  dma_k_chunk<DK>(a, bh * T, wave, lane, sK[0]);
 
   for (int c = 0; c <= nc; ++c) {
+    // every load issued so far (k of chunk c, v) has landed; the previous
+    // chunk's reads of sK[(c + 1) & 1], sWH, sWL and G are done
+    wait_vm<0>();
+    __syncthreads();
     // the stored state at boundary c
     float* wsC = a.ws_C + (bh * nb + c) * DK * dv + c0 + wave * 16 + 4 * g;
 #pragma unroll
@@ -540,16 +552,14 @@ __global__ __launch_bounds__(NT4, 1) void bwd_states_mfma_kernel(BwdArgs a) {
     }
     if (c == nc) break;
     const int64_t tok0 = bh * T + static_cast<int64_t>(c) * LC;
-    __syncthreads();   // the previous chunk's reads of sK, sWH, sWL and G are done
+    const char* kc = sK[c & 1];
+    if (c + 1 < nc) dma_k_chunk<DK>(a, tok0 + LC, wave, lane, sK[(c + 1) & 1]);
     if (wave == 0) gate_scan64(a, tok0, m, G);
-#pragma unroll
-    for (int p = 0; p < KV; ++p) {
-      const int e = tid + p * NT4;
-      const int cc = (e % (DK / 8)) * 8;
-      *reinterpret_cast<uint4*>(sK + (cc >> 6) * TB + swz(e / (DK / 8), cc & 63)) = kb[p];
+    const uint4 v0 = nv0, v1 = nv1;
+    if (c + 1 < nc) {
+      nv0 = *reinterpret_cast<const uint4*>(vrow + static_cast<int64_t>(c + 1) * LC * dv);
+      nv1 = *reinterpret_cast<const uint4*>(vrow + static_cast<int64_t>(c + 1) * LC * dv + 8);
     }
-    const uint4 v0 = vb[0], v1 = vb[1];
-    if (c + 1 < nc) fetch(c + 1);
     __syncthreads();
     {
       const int j = tid >> 2, b0 = (tid & 3) * 16;
@@ -573,7 +583,7 @@ __global__ __launch_bounds__(NT4, 1) void bwd_states_mfma_kernel(BwdArgs a) {
     }
     const float gL = G.g[LC - 1];
     if (lead && tid < DK) {
-      const char* kt = wide(sK, tid);
+      const char* kt = wide(kc, tid);
       float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll 8
       for (int j = 0; j < LC; j += 2) {
@@ -591,7 +601,7 @@ __global__ __launch_bounds__(NT4, 1) void bwd_states_mfma_kernel(BwdArgs a) {
       const bf16x8 Al = colfrag(sWL, 32 * ks, wave * 16, g, kr, kq);
 #pragma unroll
       for (int xt = 0; xt < NXT; ++xt) {
-        const bf16x8 Bk = colfrag(wide(sK, xt * 16), 32 * ks, (xt * 16) & 63, g, kr, kq);
+        const bf16x8 Bk = colfrag(wide(kc, xt * 16), 32 * ks, (xt * 16) & 63, g, kr, kq);
         Ct[xt] = mfma16x16x32(Ah, Bk, Ct[xt]);
         Ct[xt] = mfma16x16x32(Al, Bk, Ct[xt]);
       }
