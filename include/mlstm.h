@@ -191,6 +191,52 @@ mlstm_status_t mlstm_bwd_chunkwise(const mlstm_problem_t* p, int64_t chunk,
 mlstm_status_t mlstm_bwd_chunkwise_workspace_bytes(const mlstm_problem_t* p,
                                                    int64_t chunk, size_t* bytes);
 
+/* ---- Block operations around the cell -------------------------------------
+ * The mLSTM block of the xLSTM post (llms.blog), section 4 "xLSTM Block
+ * Architecture and Residual Stacking", "mLSTM Block Structure": a causal
+ * depthwise convolution on the paths that feed the cell (item 3), and the
+ * per-head normalization of the cell output with the output gate (item 5).
+ * Both are bound by HBM bandwidth; all pointers are device pointers owned by
+ * the caller, calls are asynchronous on `stream` (NULL: the null stream) and
+ * every argument check runs on the host before anything is enqueued.
+ */
+
+/* Per-head group normalization with output gate:
+ *   y[b,hd,t,:] = sigmoid(o_pre) * (gamma[hd] * (h - mean) / sqrt(var + eps)
+ *                 + beta[hd])
+ * with mean and biased variance over the d_v features of one (b, hd, t).
+ *   h:     [B,H,T,d_v] in h_dtype (the cell output computed with o_pre NULL,
+ *          i.e. without its own gate).
+ *   o_pre: [B,H,T,d_v] in o_dtype, or NULL (no gate).
+ *   gamma, beta: [H,d_v] float32, or NULL (1 and 0).
+ *   eps:   added to the variance, >= 0 and finite.
+ *   y:     [B,H,T,d_v] in h_dtype.  y may be h itself (in place); otherwise
+ *          it must not overlap any input.
+ * Supported: d_v a multiple of 4, at most 1024; h, o_pre, y, gamma and beta
+ * 16-byte aligned (8-byte for bf16 h/y/o_pre).  Arithmetic is float32. */
+mlstm_status_t mlstm_groupnorm_ogate(int64_t B, int64_t H, int64_t T, int64_t d_v,
+                                     mlstm_dtype_t h_dtype, mlstm_dtype_t o_dtype,
+                                     const void* h, const void* o_pre,
+                                     const float* gamma, const float* beta, float eps,
+                                     void* y, void* stream);
+
+/* Causal depthwise convolution over the token axis:
+ *   y[b,t,c] = bias[c] + sum_{s<K} w[c,s] x[b, t-K+1+s, c]
+ * (w[c,K-1] multiplies the current token).  Inputs before t = 0 come from
+ * state_in.
+ *   x, y:      [B,T,C] in dtype (channels last), 16-byte aligned.
+ *   w:         [C,K] float32;  bias: [C] float32 or NULL (0).
+ *   state_in:  [B,K-1,C] float32, the K-1 inputs before x[:,0] oldest first,
+ *              or NULL (zeros).
+ *   state_out: [B,K-1,C] float32 or NULL: the last K-1 inputs of
+ *              (state_in, x), to continue with the next segment.
+ * No output may overlap an input or the other output.  Supported: 1 <= K <= 8,
+ * C a multiple of 8 (bf16) or 4 (float32).  Arithmetic is float32. */
+mlstm_status_t mlstm_causal_conv1d(int64_t B, int64_t T, int64_t C, int64_t K,
+                                   mlstm_dtype_t dtype, const void* x, const float* w,
+                                   const float* bias, const float* state_in, void* y,
+                                   float* state_out, void* stream);
+
 /* Static description of a status code. */
 const char* mlstm_status_string(mlstm_status_t s);
 

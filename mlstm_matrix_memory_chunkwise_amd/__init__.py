@@ -10,6 +10,8 @@ fallback: if the library is missing or a call fails, an exception is raised.
                                           C0, n0, m0, chunk=64)
     h, (C1, n1, m1) = mlstm_fwd_parallel(q, k, v, i_pre, f_pre, o_pre, C0, n0, m0)
     h, (C, n, m)    = mlstm_step(q, k, v, i_pre, f_pre, o_pre, C, n, m)
+    y               = mlstm_groupnorm_ogate(h, o_pre, gamma, beta, eps=1e-5)
+    y, state        = mlstm_causal_conv1d(x, w, bias, state)
 
 Shapes: q, k [B,H,T,d_qk]; v, o_pre, h [B,H,T,d_v]; i_pre, f_pre [B,H,T];
 C [B,H,d_qk,d_v]; n [B,H,d_qk]; m [B,H] (the step drops T).  q, k, v are
@@ -26,7 +28,7 @@ import torch
 
 __all__ = [
     "mlstm_fwd_chunkwise", "mlstm_fwd_parallel", "mlstm_step", "mlstm_bwd_chunkwise",
-    "mlstm_bwd_chunkwise_workspace_bytes",
+    "mlstm_bwd_chunkwise_workspace_bytes", "mlstm_groupnorm_ogate", "mlstm_causal_conv1d",
     "mlstm_fwd_chunkwise_workspace_bytes", "mlstm_fwd_parallel_workspace_bytes",
     "mlstm_version", "library_path", "load_library", "MLSTMError",
     "MLSTM_OK", "MLSTM_ERR_INVALID_ARG", "MLSTM_ERR_UNSUPPORTED", "MLSTM_ERR_DEVICE",
@@ -92,6 +94,12 @@ def load_library():
     lib.mlstm_bwd_chunkwise.restype = ctypes.c_int
     lib.mlstm_bwd_chunkwise_workspace_bytes.argtypes = [PP, i64, ctypes.POINTER(sz)]
     lib.mlstm_bwd_chunkwise_workspace_bytes.restype = ctypes.c_int
+    lib.mlstm_groupnorm_ogate.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                                          vp, vp, vp, vp, ctypes.c_float, vp, vp]
+    lib.mlstm_groupnorm_ogate.restype = ctypes.c_int
+    lib.mlstm_causal_conv1d.argtypes = [i64, i64, i64, i64, ctypes.c_int, vp, vp, vp, vp, vp,
+                                        vp, vp]
+    lib.mlstm_causal_conv1d.restype = ctypes.c_int
     lib.mlstm_status_string.argtypes = [ctypes.c_int]
     lib.mlstm_status_string.restype = ctypes.c_char_p
     lib.mlstm_last_error_detail.argtypes = []
@@ -327,3 +335,53 @@ def mlstm_step(q, k, v, i_pre, f_pre, o_pre, C, n, m, *, fgate="sigmoid",
                           _ptr(o_pre), _ptr(C), _ptr(n), _ptr(m), _ptr(C1), _ptr(n1), _ptr(m1),
                           _ptr(h), _stream_handle(stream)))
     return h, (C1, n1, m1)
+
+
+def mlstm_groupnorm_ogate(h, o_pre=None, gamma=None, beta=None, eps: float = 1e-5, *,
+                          out: Optional[torch.Tensor] = None, stream=None):
+    """Per-head group normalization of the cell output with the output gate
+    (see mlstm_groupnorm_ogate in include/mlstm.h).  h [B,H,T,d_v] float32 or
+    bfloat16; o_pre like h (float32 or bfloat16) or None; gamma, beta [H,d_v]
+    float32 or None.  Returns y with h's dtype (``out`` may be h: in place)."""
+    lib = load_library()
+    h = _dev_tensor("h", h, (torch.float32, torch.bfloat16))
+    if h.dim() != 4:
+        raise ValueError("h must be [B,H,T,d_v]")
+    B, H, T, dv = h.shape
+    dev = h.device
+    o_pre = _dev_tensor("o_pre", o_pre, (torch.float32, torch.bfloat16), (B, H, T, dv), dev)
+    gamma = _dev_tensor("gamma", gamma, torch.float32, (H, dv), dev)
+    beta = _dev_tensor("beta", beta, torch.float32, (H, dv), dev)
+    y = (torch.empty_like(h) if out is None
+         else _dev_tensor("out", out, h.dtype, (B, H, T, dv), dev))
+    odt = _DT[o_pre.dtype] if o_pre is not None else MLSTM_F32
+    _check(lib.mlstm_groupnorm_ogate(B, H, T, dv, _DT[h.dtype], odt, _ptr(h), _ptr(o_pre),
+                                     _ptr(gamma), _ptr(beta), float(eps), _ptr(y),
+                                     _stream_handle(stream)))
+    return y
+
+
+def mlstm_causal_conv1d(x, w, bias=None, state=None, *, return_state: bool = True,
+                        out: Optional[torch.Tensor] = None, stream=None):
+    """Causal depthwise convolution over the token axis (see
+    mlstm_causal_conv1d in include/mlstm.h).  x [B,T,C] float32 or bfloat16;
+    w [C,K] float32; bias [C] float32 or None; state [B,K-1,C] float32 (the
+    K-1 inputs before x[:,0]) or None.  Returns (y, new state) or (y, None)."""
+    lib = load_library()
+    x = _dev_tensor("x", x, (torch.float32, torch.bfloat16))
+    if x.dim() != 3:
+        raise ValueError("x must be [B,T,C]")
+    B, T, C = x.shape
+    dev = x.device
+    w = _dev_tensor("w", w, torch.float32, None, dev)
+    if w.dim() != 2 or w.shape[0] != C:
+        raise ValueError(f"w must be [C={C},K]")
+    K = w.shape[1]
+    bias = _dev_tensor("bias", bias, torch.float32, (C,), dev)
+    state = _dev_tensor("state", state, torch.float32, (B, K - 1, C), dev)
+    y = (torch.empty_like(x) if out is None
+         else _dev_tensor("out", out, x.dtype, (B, T, C), dev))
+    st_out = torch.empty((B, K - 1, C), dtype=torch.float32, device=dev) if return_state else None
+    _check(lib.mlstm_causal_conv1d(B, T, C, K, _DT[x.dtype], _ptr(x), _ptr(w), _ptr(bias),
+                                   _ptr(state), _ptr(y), _ptr(st_out), _stream_handle(stream)))
+    return y, st_out

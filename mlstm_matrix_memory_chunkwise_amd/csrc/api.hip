@@ -304,6 +304,82 @@ mlstm_status_t mlstm_bwd_chunkwise(const mlstm_problem_t* p, int64_t chunk, cons
                        "chunkwise backward");
 }
 
+mlstm_status_t mlstm_groupnorm_ogate(int64_t B, int64_t H, int64_t T, int64_t d_v,
+                                     mlstm_dtype_t h_dtype, mlstm_dtype_t o_dtype,
+                                     const void* h, const void* o_pre,
+                                     const float* gamma, const float* beta, float eps,
+                                     void* y, void* stream) {
+  if (B <= 0 || H <= 0 || T <= 0 || d_v <= 0)
+    return fail(MLSTM_ERR_INVALID_ARG, "sizes must be positive (B=%lld H=%lld T=%lld d_v=%lld)",
+                (long long)B, (long long)H, (long long)T, (long long)d_v);
+  if ((h_dtype != MLSTM_F32 && h_dtype != MLSTM_BF16) || (o_dtype != MLSTM_F32 && o_dtype != MLSTM_BF16))
+    return fail(MLSTM_ERR_INVALID_ARG, "unknown dtype (h %d, o %d)", h_dtype, o_dtype);
+  if (!h || !y) return fail(MLSTM_ERR_INVALID_ARG, "h and y are required");
+  if (!(eps >= 0.0f) || eps == __builtin_inff())
+    return fail(MLSTM_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (d_v % 4 != 0 || d_v > 1024)
+    return fail(MLSTM_ERR_UNSUPPORTED, "d_v=%lld: need a multiple of 4, at most 1024", (long long)d_v);
+  if (B * H * T > ((int64_t)1 << 40))
+    return fail(MLSTM_ERR_UNSUPPORTED, "B*H*T=%lld too large", (long long)(B * H * T));
+  const size_t n = (size_t)(B * H * T * d_v), sh = dsize(h_dtype), so = dsize(o_dtype);
+  const Buf bufs[] = {
+      {"h", h, n * sh, 2 * sh},     {"o_pre", o_pre, n * so, 2 * so},
+      {"gamma", gamma, (size_t)(H * d_v) * 4, 16}, {"beta", beta, (size_t)(H * d_v) * 4, 16},
+      {"y", y, n * sh, 2 * sh},
+  };
+  for (const Buf& b : bufs)
+    if (b.p && !aligned(b))
+      return fail(MLSTM_ERR_INVALID_ARG, "%s is not %zu-byte aligned", b.name, b.align);
+  for (int i = 1; i < 4; ++i)
+    if (overlaps(bufs[4], bufs[i])) return fail(MLSTM_ERR_INVALID_ARG, "y overlaps %s", bufs[i].name);
+  if (y != h && overlaps(bufs[4], bufs[0]))
+    return fail(MLSTM_ERR_INVALID_ARG, "y overlaps h without being h");
+  mlstm::GnArgs a{};
+  a.rows = B * H * T; a.H = H; a.T = T; a.dv = (int)d_v;
+  a.h_bf16 = h_dtype == MLSTM_BF16; a.o_bf16 = o_dtype == MLSTM_BF16; a.eps = eps;
+  a.h = h; a.o_pre = o_pre; a.gamma = gamma; a.beta = beta; a.y = y;
+  return device_status(mlstm::launch_groupnorm_ogate(a, static_cast<hipStream_t>(stream)),
+                       "groupnorm_ogate");
+}
+
+mlstm_status_t mlstm_causal_conv1d(int64_t B, int64_t T, int64_t C, int64_t K,
+                                   mlstm_dtype_t dtype, const void* x, const float* w,
+                                   const float* bias, const float* state_in, void* y,
+                                   float* state_out, void* stream) {
+  if (B <= 0 || T <= 0 || C <= 0 || K <= 0)
+    return fail(MLSTM_ERR_INVALID_ARG, "sizes must be positive (B=%lld T=%lld C=%lld K=%lld)",
+                (long long)B, (long long)T, (long long)C, (long long)K);
+  if (dtype != MLSTM_F32 && dtype != MLSTM_BF16)
+    return fail(MLSTM_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (!x || !w || !y) return fail(MLSTM_ERR_INVALID_ARG, "x, w and y are required");
+  if (K > 8) return fail(MLSTM_ERR_UNSUPPORTED, "K=%lld: at most 8", (long long)K);
+  const int64_t ve = dtype == MLSTM_BF16 ? 8 : 4;
+  if (C % ve != 0)
+    return fail(MLSTM_ERR_UNSUPPORTED, "C=%lld: need a multiple of %lld", (long long)C, (long long)ve);
+  if (B * T * C > ((int64_t)1 << 40))
+    return fail(MLSTM_ERR_UNSUPPORTED, "B*T*C=%lld too large", (long long)(B * T * C));
+  const size_t n = (size_t)(B * T * C), sx = dsize(dtype), ns = (size_t)(B * (K - 1) * C) * 4;
+  const Buf bufs[] = {
+      {"x", x, n * sx, 16},            {"w", w, (size_t)(C * K) * 4, 4},
+      {"bias", bias, (size_t)C * 4, 4}, {"state_in", state_in, ns, 4},
+      // outputs from here (index 4 on)
+      {"y", y, n * sx, 16},            {"state_out", state_out, ns, 4},
+  };
+  const int nb = sizeof(bufs) / sizeof(bufs[0]);
+  for (int i = 0; i < nb; ++i)
+    if (bufs[i].p && !aligned(bufs[i]))
+      return fail(MLSTM_ERR_INVALID_ARG, "%s is not %zu-byte aligned", bufs[i].name, bufs[i].align);
+  for (int o = 4; o < nb; ++o)
+    for (int i = 0; i < nb; ++i)
+      if (i != o && overlaps(bufs[o], bufs[i]))
+        return fail(MLSTM_ERR_INVALID_ARG, "%s overlaps %s", bufs[o].name, bufs[i].name);
+  mlstm::ConvArgs a{};
+  a.B = B; a.T = T; a.C = C; a.K = (int)K; a.x_bf16 = dtype == MLSTM_BF16;
+  a.x = x; a.w = w; a.bias = bias; a.state_in = state_in; a.y = y; a.state_out = state_out;
+  return device_status(mlstm::launch_causal_conv(a, static_cast<hipStream_t>(stream)),
+                       "causal_conv1d");
+}
+
 mlstm_status_t mlstm_fwd_parallel_workspace_bytes(const mlstm_problem_t* p, size_t* bytes) {
   if (!bytes) return fail(MLSTM_ERR_INVALID_ARG, "bytes is NULL");
   mlstm_status_t s = check_problem(p, true);

@@ -119,6 +119,35 @@ bool bwd_mfma_supported(const BwdArgs& a);
 hipError_t launch_bwd_states_mfma(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_rev_mfma(const BwdArgs& a, hipStream_t stream);
 
+// Block operations around the cell (block_ops.hip).
+struct GnArgs {
+  int64_t rows;     // B * H * T
+  int64_t H, T;
+  int dv;
+  int h_bf16;       // h and y are bfloat16 (else float32)
+  int o_bf16;       // o_pre is bfloat16 (else float32)
+  float eps;
+  const void* h;
+  const void* o_pre;    // null: no output gate
+  const float* gamma;   // [H, d_v] or null (1)
+  const float* beta;    // [H, d_v] or null (0)
+  void* y;
+};
+hipError_t launch_groupnorm_ogate(const GnArgs& a, hipStream_t stream);
+
+struct ConvArgs {
+  int64_t B, T, C;
+  int K;
+  int x_bf16;             // x and y are bfloat16 (else float32)
+  const void* x;          // [B, T, C]
+  const float* w;         // [C, K]
+  const float* bias;      // [C] or null
+  const float* state_in;  // [B, K-1, C] or null (zeros)
+  void* y;                // [B, T, C]
+  float* state_out;       // [B, K-1, C] or null
+};
+hipError_t launch_causal_conv(const ConvArgs& a, hipStream_t stream);
+
 // Parallel (quadratic) form.
 size_t parallel_workspace(const SeqArgs& a);
 hipError_t launch_parallel(const SeqArgs& a, void* ws, hipStream_t stream);

@@ -256,3 +256,56 @@ def test_bwd_workspace(lib):
     assert r == M.MLSTM_ERR_INVALID_ARG and "workspace" in det
     r, det = bwd_call(lib, p, ws=ctypes.c_void_p(FAKE + 64))   # inside q
     assert r == M.MLSTM_ERR_INVALID_ARG and "overlaps" in det
+
+
+# ---- block operations (no kernel runs: every call below fails its checks)
+
+def gn_call(lib, B=1, H=2, T=4, dv=64, hdt=1, odt=0, eps=1e-5, **over):
+    v = dict(h=ctypes.c_void_p(FAKE), o=None, g=None, b=None, y=ctypes.c_void_p(FAKE + (1 << 30)))
+    v.update(over)
+    r = lib.mlstm_groupnorm_ogate(B, H, T, dv, hdt, odt, v["h"], v["o"], v["g"], v["b"],
+                                  ctypes.c_float(eps), v["y"], None)
+    return r, lib.mlstm_last_error_detail().decode()
+
+
+def test_groupnorm_rejections(lib):
+    assert gn_call(lib, h=None)[0] == M.MLSTM_ERR_INVALID_ARG
+    assert gn_call(lib, y=None)[0] == M.MLSTM_ERR_INVALID_ARG
+    assert gn_call(lib, T=0)[0] == M.MLSTM_ERR_INVALID_ARG
+    assert gn_call(lib, hdt=7)[0] == M.MLSTM_ERR_INVALID_ARG
+    assert gn_call(lib, eps=-1.0)[0] == M.MLSTM_ERR_INVALID_ARG
+    assert gn_call(lib, eps=float("nan"))[0] == M.MLSTM_ERR_INVALID_ARG
+    assert gn_call(lib, dv=6)[0] == M.MLSTM_ERR_UNSUPPORTED
+    assert gn_call(lib, dv=2048)[0] == M.MLSTM_ERR_UNSUPPORTED
+    r, det = gn_call(lib, o=ctypes.c_void_p(FAKE + (2 << 30) + 4))   # float32 o needs 8 bytes
+    assert r == M.MLSTM_ERR_INVALID_ARG and "o_pre" in det
+    r, det = gn_call(lib, y=ctypes.c_void_p(FAKE + 64))              # inside h, not h
+    assert r == M.MLSTM_ERR_INVALID_ARG and "overlaps" in det
+    r, det = gn_call(lib, g=ctypes.c_void_p(FAKE + (1 << 30) + 128))  # gamma inside y
+    assert r == M.MLSTM_ERR_INVALID_ARG and "overlaps" in det
+
+
+def conv_call(lib, B=1, T=16, C=64, K=4, dt=1, **over):
+    names = ["x", "w", "bias", "sin", "y", "sout"]
+    v = dict(zip(names, ptrs(len(names))))
+    v["bias"] = v["sin"] = v["sout"] = None
+    v.update(over)
+    r = lib.mlstm_causal_conv1d(B, T, C, K, dt, *(v[n] for n in names), None)
+    return r, lib.mlstm_last_error_detail().decode()
+
+
+def test_conv_rejections(lib):
+    for n in ("x", "w", "y"):
+        assert conv_call(lib, **{n: None})[0] == M.MLSTM_ERR_INVALID_ARG, n
+    assert conv_call(lib, K=0)[0] == M.MLSTM_ERR_INVALID_ARG
+    assert conv_call(lib, dt=3)[0] == M.MLSTM_ERR_INVALID_ARG
+    assert conv_call(lib, K=9)[0] == M.MLSTM_ERR_UNSUPPORTED
+    assert conv_call(lib, C=12)[0] == M.MLSTM_ERR_UNSUPPORTED            # bf16: C % 8
+    assert conv_call(lib, C=12, dt=0, x=None)[0] == M.MLSTM_ERR_INVALID_ARG
+    r, det = conv_call(lib, x=ctypes.c_void_p(FAKE + 8))
+    assert r == M.MLSTM_ERR_INVALID_ARG and "aligned" in det
+    r, det = conv_call(lib, sout=ctypes.c_void_p(FAKE + 16))             # inside x
+    assert r == M.MLSTM_ERR_INVALID_ARG and "overlaps" in det
+    r, det = conv_call(lib, sin=ctypes.c_void_p(FAKE + (4 << 30)),
+                       sout=ctypes.c_void_p(FAKE + (4 << 30)))          # in place is refused
+    assert r == M.MLSTM_ERR_INVALID_ARG and "overlaps" in det
