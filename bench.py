@@ -73,6 +73,42 @@ def bwd_algorithmic(B, H, T, dqk, dv, L, o_bytes):
     return flops, byts
 
 
+def groupnorm_algorithmic(B, H, T, dv, h_bytes=2, o_bytes=4):
+    """Bytes of the group normalization with o-gate: h and o~ in, y out,
+    gamma and beta once."""
+    return B * H * T * dv * (2 * h_bytes + o_bytes) + 2 * H * dv * 4
+
+
+def conv_algorithmic(B, T, C, K, x_bytes=2):
+    """Bytes of the causal depthwise convolution: x in, y out, weights, bias
+    and the carried window in and out once."""
+    return 2 * B * T * C * x_bytes + C * (K + 1) * 4 + 2 * B * (K - 1) * C * 4
+
+
+# shapes of the block-operation lines: the cell output of the measured
+# workload, and its q/k path before the projections ([B, T, H*d_qk])
+GN_SHAPE = dict(B=8, H=8, T=8192, dv=256)
+CONV_SHAPE = dict(B=8, T=8192, C=2048, K=4)
+
+
+def block_inputs(dev, seed=7):
+    import torch
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    B, H, T, dv = GN_SHAPE["B"], GN_SHAPE["H"], GN_SHAPE["T"], GN_SHAPE["dv"]
+    gn = dict(h=torch.randn((B, H, T, dv), generator=g).to(torch.bfloat16).to(dev),
+              o=torch.randn((B, H, T, dv), generator=g).to(dev),
+              gamma=(torch.randn((H, dv), generator=g) * 0.5 + 1).to(dev),
+              beta=(torch.randn((H, dv), generator=g) * 0.5).to(dev))
+    gn["y"] = torch.empty_like(gn["h"])
+    B, T, C, K = CONV_SHAPE["B"], CONV_SHAPE["T"], CONV_SHAPE["C"], CONV_SHAPE["K"]
+    cv = dict(x=torch.randn((B, T, C), generator=g).to(torch.bfloat16).to(dev),
+              w=(torch.randn((C, K), generator=g) / 2).to(dev),
+              b=torch.randn((C,), generator=g).to(dev),
+              s=torch.randn((B, K - 1, C), generator=g).to(dev))
+    cv["y"] = torch.empty_like(cv["x"])
+    return gn, cv
+
+
 def step_algorithmic(B, H, dqk, dv, qkv_bytes=2, o_bytes=4):
     """Bytes one decode step must move: C~ read + write, n~ read + write, m,
     q, k, v, gates, o-gate, h."""
@@ -85,6 +121,8 @@ def step_algorithmic(B, H, dqk, dv, qkv_bytes=2, o_bytes=4):
 SETTLE_S = 0.15
 
 KERNEL_SOURCES = {
+    "groupnorm": ["block_ops.hip", "common.hpp", "kernels.hpp"],
+    "conv": ["block_ops.hip", "common.hpp", "kernels.hpp"],
     "chunkwise": ["chunk_ws.hip", "mfma_util.hpp", "common.hpp", "kernels.hpp"],
     "step": ["step.hip", "common.hpp", "kernels.hpp"],
 }
@@ -140,6 +178,11 @@ def profile_workload():
                  s["C0"], s["n0"], s["m0"], inplace=True)
     torch.cuda.synchronize()
     del s
+    gn, cv = block_inputs(dev)
+    M.mlstm_groupnorm_ogate(gn["h"], gn["o"], gn["gamma"], gn["beta"], 1e-5, out=gn["y"])
+    M.mlstm_causal_conv1d(cv["x"], cv["w"], cv["b"], cv["s"], out=cv["y"])
+    torch.cuda.synchronize()
+    del gn, cv
     x = torch.ones(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
     y = torch.empty_like(x)
     y.copy_(x)
@@ -168,6 +211,7 @@ def main():
     ap.add_argument("--skip-step", action="store_true")
     ap.add_argument("--skip-extra", action="store_true")
     ap.add_argument("--skip-bwd", action="store_true")
+    ap.add_argument("--skip-block", action="store_true")
     ap.add_argument("--profile-workload", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -319,6 +363,40 @@ def main():
             "workspace_bytes": wsb.numel(),
         }
         del dh, dC1, dn1, wsb
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ block operations
+    if not args.skip_block:
+        gn, cv = block_inputs(dev)
+
+        def run_gn():
+            M.mlstm_groupnorm_ogate(gn["h"], gn["o"], gn["gamma"], gn["beta"], 1e-5, out=gn["y"])
+
+        def run_conv():
+            M.mlstm_causal_conv1d(cv["x"], cv["w"], cv["b"], cv["s"], out=cv["y"])
+
+        for fn, key in ((run_gn, "groupnorm_ogate"), (run_conv, "causal_conv1d")):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            ms_x = time_events(fn, max(5, args.steps), stream)
+            if key == "groupnorm_ogate":
+                byts = groupnorm_algorithmic(**GN_SHAPE)
+                wl = (f"per-head group normalization + o-gate of the cell output, h [{GN_SHAPE['B']},"
+                      f"{GN_SHAPE['H']},{GN_SHAPE['T']},{GN_SHAPE['dv']}] bf16, f32 o-gate, affine")
+                tr = measured_traffic("groupnorm")
+            else:
+                byts = conv_algorithmic(**CONV_SHAPE)
+                wl = (f"causal depthwise conv1d K={CONV_SHAPE['K']}, x [{CONV_SHAPE['B']},"
+                      f"{CONV_SHAPE['T']},{CONV_SHAPE['C']}] bf16, bias, carried window in and out")
+                tr = measured_traffic("conv")
+            gbs = byts / (ms_x / 1e3) / 1e9
+            result[key] = {"workload": wl, "ms": ms_x,
+                           "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
+                                        "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                                        "traffic": tr},
+                           "algorithmic_bytes": byts}
+        del gn, cv
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ CPU oracle
