@@ -85,6 +85,18 @@ def conv_algorithmic(B, T, C, K, x_bytes=2):
     return 2 * B * T * C * x_bytes + C * (K + 1) * 4 + 2 * B * (K - 1) * C * 4
 
 
+# sLSTM line: 64 sequences x 4 heads of 128 units fill the 256 CUs with one
+# (batch, head) sequence each
+SLSTM_SHAPE = dict(B=64, NH=4, T=4096, DH=128)
+FP32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector, TFLOP/s
+
+
+def slstm_flops(B, NH, T, DH):
+    """The recurrent mat-vec products: 4 gates x DH x DH multiply-adds per
+    (sequence, head, step); the gate arithmetic is not counted."""
+    return 2 * 4 * DH * DH * B * NH * T
+
+
 # shapes of the block-operation lines: the cell output of the measured
 # workload, and its q/k path before the projections ([B, T, H*d_qk])
 GN_SHAPE = dict(B=8, H=8, T=8192, dv=256)
@@ -212,6 +224,7 @@ def main():
     ap.add_argument("--skip-extra", action="store_true")
     ap.add_argument("--skip-bwd", action="store_true")
     ap.add_argument("--skip-block", action="store_true")
+    ap.add_argument("--skip-slstm", action="store_true")
     ap.add_argument("--profile-workload", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -397,6 +410,36 @@ def main():
                                         "traffic": tr},
                            "algorithmic_bytes": byts}
         del gn, cv
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ sLSTM cell
+    if not args.skip_slstm:
+        import math
+        B_, NH_, T_, DH_ = (SLSTM_SHAPE[k] for k in ("B", "NH", "T", "DH"))
+        g = torch.Generator(device="cpu").manual_seed(11)
+        wx = torch.randn((B_, NH_, T_, 4, DH_), generator=g)
+        wx[:, :, :, 0] -= 1.0
+        wx[:, :, :, 1] += 3.0
+        wx = wx.to(torch.bfloat16).to(dev)
+        Rm = (torch.randn((NH_, 4, DH_, DH_), generator=g) * (0.5 / math.sqrt(DH_))).to(dev)
+        hs = torch.empty((B_, NH_, T_, DH_), dtype=torch.bfloat16, device=dev)
+
+        def run_slstm():
+            M.mlstm_slstm_fwd(wx, Rm, return_state=False, out=hs)
+
+        run_slstm()
+        torch.cuda.synchronize()
+        ms_s = time_events(run_slstm, 3, stream)
+        fl = slstm_flops(**SLSTM_SHAPE)
+        tf = fl / (ms_s / 1e3) / 1e12
+        result["slstm"] = {
+            "workload": f"sLSTM forward, B={B_} NH={NH_} DH={DH_} T={T_}, bf16 wx and h, sigmoid "
+                        f"forget gate, zero state; one workgroup per (batch, head)",
+            "ms": ms_s, "tokens_per_s": B_ * T_ / (ms_s / 1e3), "us_per_step": ms_s * 1e3 / T_,
+            "roofline": {"bound": "alu", "achieved": tf, "peak": FP32_VALU_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": tf / FP32_VALU_PEAK_TFLOPS, "traffic": None},
+        }
+        del wx, Rm, hs
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ CPU oracle

@@ -237,6 +237,42 @@ mlstm_status_t mlstm_causal_conv1d(int64_t B, int64_t T, int64_t C, int64_t K,
                                    const float* bias, const float* state_in, void* y,
                                    float* state_out, void* stream);
 
+/* ---- sLSTM forward cell ------------------------------------------------------
+ * The scalar-memory cell of the xLSTM post (llms.blog), section 2 "sLSTM:
+ * Scalar Memory with Exponential Gating and Normalization".  Per step t,
+ * head hd, unit u:
+ *   pre_g = wx[b,hd,t,g,u] + sum_v R[hd,g,u,v] h_{t-1}[b,hd,v]   (g = i, f, z, o)
+ *   m_t = max(log f + m_{t-1}, i~),  c_t = e^{log f + m_{t-1} - m_t} c_{t-1}
+ *         + e^{i~ - m_t} z,  n_t = e^{log f + m_{t-1} - m_t} n_{t-1} + e^{i~ - m_t},
+ *   h_t = sigmoid(o~) c_t / n_t
+ * with log f = f~ (MLSTM_FGATE_EXP) or log sigmoid(f~) (MLSTM_FGATE_SIGMOID);
+ * z is used as is (no squashing).  The state (c, n, m, h) is the stabilized
+ * one; h is the gated output that feeds the next step.
+ */
+typedef struct {
+  int64_t B, NH, T, DH;   /* batch, heads, steps, units per head */
+  mlstm_dtype_t x_dtype;  /* dtype of wx and h */
+  mlstm_fgate_t fgate;
+} mlstm_slstm_problem_t;
+
+/* sLSTM forward over T steps.
+ *   wx: [B,NH,T,4,DH] in x_dtype, the input projections W x_t + b of the
+ *       gates in the order (i, f, z, o).
+ *   R:  [NH,4,DH,DH] float32, the recurrent matrices of each head
+ *       (pre = R h, row index u, column index v).
+ *   c0, n0, m0, h0: [B,NH,DH] float32 each, all set or all NULL (zero state).
+ *   h:  [B,NH,T,DH] in x_dtype.
+ *   c1, n1, m1, h1: [B,NH,DH] float32 each, all set or all NULL (not
+ *       written); they may not overlap the inputs (run two buffers to chain).
+ * Supported: DH = 16, 32, 64 or 128.  R must be 16-byte aligned, every
+ * other pointer aligned to its element size.  One workgroup per (b, head)
+ * runs the steps in order; arithmetic is float32 and the recurrent h stays
+ * float32 (a bf16 h output is a rounded copy). */
+mlstm_status_t mlstm_slstm_fwd(const mlstm_slstm_problem_t* p, const void* wx, const float* R,
+                               const float* c0, const float* n0, const float* m0,
+                               const float* h0, void* h, float* c1, float* n1, float* m1,
+                               float* h1, void* stream);
+
 /* Static description of a status code. */
 const char* mlstm_status_string(mlstm_status_t s);
 

@@ -12,6 +12,7 @@ fallback: if the library is missing or a call fails, an exception is raised.
     h, (C, n, m)    = mlstm_step(q, k, v, i_pre, f_pre, o_pre, C, n, m)
     y               = mlstm_groupnorm_ogate(h, o_pre, gamma, beta, eps=1e-5)
     y, state        = mlstm_causal_conv1d(x, w, bias, state)
+    h, (c, n, m, h1) = mlstm_slstm_fwd(wx, R, c0, n0, m0, h0)     # sLSTM cell
 
 Shapes: q, k [B,H,T,d_qk]; v, o_pre, h [B,H,T,d_v]; i_pre, f_pre [B,H,T];
 C [B,H,d_qk,d_v]; n [B,H,d_qk]; m [B,H] (the step drops T).  q, k, v are
@@ -29,6 +30,7 @@ import torch
 __all__ = [
     "mlstm_fwd_chunkwise", "mlstm_fwd_parallel", "mlstm_step", "mlstm_bwd_chunkwise",
     "mlstm_bwd_chunkwise_workspace_bytes", "mlstm_groupnorm_ogate", "mlstm_causal_conv1d",
+    "mlstm_slstm_fwd", "SlstmProblem",
     "mlstm_fwd_chunkwise_workspace_bytes", "mlstm_fwd_parallel_workspace_bytes",
     "mlstm_version", "library_path", "load_library", "MLSTMError",
     "MLSTM_OK", "MLSTM_ERR_INVALID_ARG", "MLSTM_ERR_UNSUPPORTED", "MLSTM_ERR_DEVICE",
@@ -100,6 +102,8 @@ def load_library():
     lib.mlstm_causal_conv1d.argtypes = [i64, i64, i64, i64, ctypes.c_int, vp, vp, vp, vp, vp,
                                         vp, vp]
     lib.mlstm_causal_conv1d.restype = ctypes.c_int
+    lib.mlstm_slstm_fwd.argtypes = [ctypes.POINTER(SlstmProblem)] + [vp] * 12
+    lib.mlstm_slstm_fwd.restype = ctypes.c_int
     lib.mlstm_status_string.argtypes = [ctypes.c_int]
     lib.mlstm_status_string.restype = ctypes.c_char_p
     lib.mlstm_last_error_detail.argtypes = []
@@ -385,3 +389,35 @@ def mlstm_causal_conv1d(x, w, bias=None, state=None, *, return_state: bool = Tru
     _check(lib.mlstm_causal_conv1d(B, T, C, K, _DT[x.dtype], _ptr(x), _ptr(w), _ptr(bias),
                                    _ptr(state), _ptr(y), _ptr(st_out), _stream_handle(stream)))
     return y, st_out
+
+
+class SlstmProblem(ctypes.Structure):
+    """mlstm_slstm_problem_t."""
+    _fields_ = [("B", ctypes.c_int64), ("NH", ctypes.c_int64), ("T", ctypes.c_int64),
+                ("DH", ctypes.c_int64), ("x_dtype", ctypes.c_int32), ("fgate", ctypes.c_int32)]
+
+
+def mlstm_slstm_fwd(wx, R, c0=None, n0=None, m0=None, h0=None, *, fgate="sigmoid",
+                    return_state: bool = True, out: Optional[torch.Tensor] = None, stream=None):
+    """sLSTM forward cell (see mlstm_slstm_fwd in include/mlstm.h).
+
+    wx [B,NH,T,4,DH] float32 or bfloat16 (gate order i, f, z, o); R
+    [NH,4,DH,DH] float32; c0, n0, m0, h0 [B,NH,DH] float32 (all or none).
+    Returns (h [B,NH,T,DH] in wx's dtype, (c1, n1, m1, h1)) or (h, None)."""
+    lib = load_library()
+    wx = _dev_tensor("wx", wx, (torch.float32, torch.bfloat16))
+    if wx.dim() != 5 or wx.shape[3] != 4:
+        raise ValueError("wx must be [B,NH,T,4,DH]")
+    B, NH, T, _, DH = wx.shape
+    dev = wx.device
+    R = _dev_tensor("R", R, torch.float32, (NH, 4, DH, DH), dev)
+    st = [_dev_tensor(nm, x, torch.float32, (B, NH, DH), dev)
+          for nm, x in (("c0", c0), ("n0", n0), ("m0", m0), ("h0", h0))]
+    h = (torch.empty((B, NH, T, DH), dtype=wx.dtype, device=dev) if out is None
+         else _dev_tensor("out", out, wx.dtype, (B, NH, T, DH), dev))
+    fin = ([torch.empty((B, NH, DH), dtype=torch.float32, device=dev) for _ in range(4)]
+           if return_state else [None] * 4)
+    p = SlstmProblem(B, NH, T, DH, _DT[wx.dtype], _fgate(fgate))
+    _check(lib.mlstm_slstm_fwd(ctypes.byref(p), _ptr(wx), _ptr(R), *(_ptr(x) for x in st),
+                               _ptr(h), *(_ptr(x) for x in fin), _stream_handle(stream)))
+    return h, (tuple(fin) if return_state else None)

@@ -380,6 +380,54 @@ mlstm_status_t mlstm_causal_conv1d(int64_t B, int64_t T, int64_t C, int64_t K,
                        "causal_conv1d");
 }
 
+mlstm_status_t mlstm_slstm_fwd(const mlstm_slstm_problem_t* p, const void* wx, const float* R,
+                               const float* c0, const float* n0, const float* m0,
+                               const float* h0, void* h, float* c1, float* n1, float* m1,
+                               float* h1, void* stream) {
+  if (!p) return fail(MLSTM_ERR_INVALID_ARG, "problem descriptor is NULL");
+  if (p->B <= 0 || p->NH <= 0 || p->T <= 0 || p->DH <= 0)
+    return fail(MLSTM_ERR_INVALID_ARG, "sizes must be positive (B=%lld NH=%lld T=%lld DH=%lld)",
+                (long long)p->B, (long long)p->NH, (long long)p->T, (long long)p->DH);
+  if (p->x_dtype != MLSTM_F32 && p->x_dtype != MLSTM_BF16)
+    return fail(MLSTM_ERR_INVALID_ARG, "unknown x_dtype %d", p->x_dtype);
+  if (p->fgate != MLSTM_FGATE_SIGMOID && p->fgate != MLSTM_FGATE_EXP)
+    return fail(MLSTM_ERR_INVALID_ARG, "unknown fgate %d", p->fgate);
+  if (!wx || !R || !h) return fail(MLSTM_ERR_INVALID_ARG, "wx, R and h are required");
+  const int in_state = (c0 != nullptr) + (n0 != nullptr) + (m0 != nullptr) + (h0 != nullptr);
+  if (in_state != 0 && in_state != 4)
+    return fail(MLSTM_ERR_INVALID_ARG, "initial state must be all of c0, n0, m0, h0 or none");
+  const int out_state = (c1 != nullptr) + (n1 != nullptr) + (m1 != nullptr) + (h1 != nullptr);
+  if (out_state != 0 && out_state != 4)
+    return fail(MLSTM_ERR_INVALID_ARG, "final state must be all of c1, n1, m1, h1 or none");
+  if (p->DH != 16 && p->DH != 32 && p->DH != 64 && p->DH != 128)
+    return fail(MLSTM_ERR_UNSUPPORTED, "DH=%lld: supported 16, 32, 64, 128", (long long)p->DH);
+  if (p->B * p->NH > ((int64_t)1 << 31) - 1 || p->T > ((int64_t)1 << 40))
+    return fail(MLSTM_ERR_UNSUPPORTED, "B*NH or T too large");
+  const size_t BH = (size_t)(p->B * p->NH), T = (size_t)p->T, DH = (size_t)p->DH;
+  const size_t sx = dsize(p->x_dtype), st = BH * DH * 4;
+  const Buf bufs[] = {
+      {"wx", wx, BH * T * 4 * DH * sx, sx}, {"R", R, (size_t)p->NH * 4 * DH * DH * 4, 16},
+      {"c0", c0, st, 4}, {"n0", n0, st, 4}, {"m0", m0, st, 4}, {"h0", h0, st, 4},
+      // outputs from here (index 6 on)
+      {"h", h, BH * T * DH * sx, sx},
+      {"c1", c1, st, 4}, {"n1", n1, st, 4}, {"m1", m1, st, 4}, {"h1", h1, st, 4},
+  };
+  const int nb = sizeof(bufs) / sizeof(bufs[0]);
+  for (int i = 0; i < nb; ++i)
+    if (bufs[i].p && !aligned(bufs[i]))
+      return fail(MLSTM_ERR_INVALID_ARG, "%s is not %zu-byte aligned", bufs[i].name, bufs[i].align);
+  for (int o = 6; o < nb; ++o)
+    for (int i = 0; i < nb; ++i)
+      if (i != o && overlaps(bufs[o], bufs[i]))
+        return fail(MLSTM_ERR_INVALID_ARG, "%s overlaps %s", bufs[o].name, bufs[i].name);
+  mlstm::SlstmArgs a{};
+  a.B = p->B; a.NH = p->NH; a.T = p->T; a.DH = (int)p->DH;
+  a.x_bf16 = p->x_dtype == MLSTM_BF16; a.fgate_exp = p->fgate == MLSTM_FGATE_EXP;
+  a.wx = wx; a.R = R; a.c0 = c0; a.n0 = n0; a.m0 = m0; a.h0 = h0;
+  a.h = h; a.c1 = c1; a.n1 = n1; a.m1 = m1; a.h1 = h1;
+  return device_status(mlstm::launch_slstm(a, static_cast<hipStream_t>(stream)), "slstm_fwd");
+}
+
 mlstm_status_t mlstm_fwd_parallel_workspace_bytes(const mlstm_problem_t* p, size_t* bytes) {
   if (!bytes) return fail(MLSTM_ERR_INVALID_ARG, "bytes is NULL");
   mlstm_status_t s = check_problem(p, true);

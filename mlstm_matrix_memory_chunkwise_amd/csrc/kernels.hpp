@@ -148,6 +148,26 @@ struct ConvArgs {
 };
 hipError_t launch_causal_conv(const ConvArgs& a, hipStream_t stream);
 
+// sLSTM forward cell (slstm.hip).
+struct SlstmArgs {
+  int64_t B, NH, T;
+  int DH;                 // 16, 32, 64 or 128
+  int x_bf16;             // wx and h are bfloat16 (else float32)
+  int fgate_exp;          // forget gate: 1 = exponential, 0 = sigmoid
+  const void* wx;         // [B, NH, T, 4, DH] input projections of (i, f, z, o)
+  const float* R;         // [NH, 4, DH, DH] recurrent matrices
+  const float* c0;        // [B, NH, DH] each; all null = zero state
+  const float* n0;
+  const float* m0;
+  const float* h0;
+  void* h;                // [B, NH, T, DH]
+  float* c1;              // all null = not written
+  float* n1;
+  float* m1;
+  float* h1;
+};
+hipError_t launch_slstm(const SlstmArgs& a, hipStream_t stream);
+
 // Parallel (quadratic) form.
 size_t parallel_workspace(const SeqArgs& a);
 hipError_t launch_parallel(const SeqArgs& a, void* ws, hipStream_t stream);

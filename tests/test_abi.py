@@ -309,3 +309,45 @@ def test_conv_rejections(lib):
     r, det = conv_call(lib, sin=ctypes.c_void_p(FAKE + (4 << 30)),
                        sout=ctypes.c_void_p(FAKE + (4 << 30)))          # in place is refused
     assert r == M.MLSTM_ERR_INVALID_ARG and "overlaps" in det
+
+
+# ---- sLSTM cell
+
+def test_slstm_problem_layout(tmp_path):
+    src = tmp_path / "s.c"
+    src.write_text('#include "mlstm.h"\nint main(void){ return sizeof(mlstm_slstm_problem_t) == 40 ? 0 : 1; }\n')
+    import subprocess
+    exe = tmp_path / "s"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    str(src), "-o", str(exe)], check=True)
+    assert subprocess.run([str(exe)]).returncode == 0
+    assert ctypes.sizeof(M.SlstmProblem) == 40
+
+
+def slstm_call(lib, B=2, NH=2, T=8, DH=32, dt=0, fg=0, **over):
+    names = ["wx", "R", "c0", "n0", "m0", "h0", "h", "c1", "n1", "m1", "h1"]
+    v = dict(zip(names, ptrs(len(names))))
+    for n in ("c0", "n0", "m0", "h0", "c1", "n1", "m1", "h1"):
+        v[n] = None
+    v.update(over)
+    p = M.SlstmProblem(B, NH, T, DH, dt, fg)
+    r = lib.mlstm_slstm_fwd(ctypes.byref(p), *(v[n] for n in names), None)
+    return r, lib.mlstm_last_error_detail().decode()
+
+
+def test_slstm_rejections(lib):
+    for n in ("wx", "R", "h"):
+        assert slstm_call(lib, **{n: None})[0] == M.MLSTM_ERR_INVALID_ARG, n
+    assert slstm_call(lib, T=0)[0] == M.MLSTM_ERR_INVALID_ARG
+    assert slstm_call(lib, dt=5)[0] == M.MLSTM_ERR_INVALID_ARG
+    assert slstm_call(lib, fg=9)[0] == M.MLSTM_ERR_INVALID_ARG
+    assert slstm_call(lib, DH=48)[0] == M.MLSTM_ERR_UNSUPPORTED
+    assert slstm_call(lib, DH=256)[0] == M.MLSTM_ERR_UNSUPPORTED
+    r, det = slstm_call(lib, c0=ctypes.c_void_p(FAKE + (2 << 30)))
+    assert r == M.MLSTM_ERR_INVALID_ARG and "initial state" in det
+    r, det = slstm_call(lib, c1=ctypes.c_void_p(FAKE + (7 << 30)))
+    assert r == M.MLSTM_ERR_INVALID_ARG and "final state" in det
+    r, det = slstm_call(lib, R=ctypes.c_void_p(FAKE + (1 << 30) + 4))
+    assert r == M.MLSTM_ERR_INVALID_ARG and "R" in det and "aligned" in det
+    r, det = slstm_call(lib, h=ctypes.c_void_p(FAKE + 64))                # inside wx
+    assert r == M.MLSTM_ERR_INVALID_ARG and "overlaps" in det
