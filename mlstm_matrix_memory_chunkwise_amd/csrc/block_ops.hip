@@ -6,15 +6,17 @@
 //  * Per-head group normalization with the output gate, on the cell output
 //    h [B, H, T, d_v]: y = sigmoid(o~) (gamma (h - mean) / sqrt(var + eps) +
 //    beta), mean and (biased) variance over the d_v features of one (b, head,
-//    t).  One wave per (b, head, t) row: the row is loaded once into
-//    registers, reduced twice across the wave (mean, then the centred second
-//    moment, so no cancellation), and written once.
+//    t).  One wave per 4, 2 or 1 (b, head, t) rows (d_v up to 256, 512,
+//    1024): the rows are loaded once into registers with every load issued
+//    before the first reduction, reduced twice across the wave (mean, then
+//    the centred second moment, so no cancellation), and written once.
 //  * Causal depthwise convolution over the token axis, x [B, T, C]:
 //    y[t, c] = bias[c] + sum_{s<K} w[c, s] x[t - K + 1 + s, c], with an
 //    optional carried window of the K - 1 inputs before t = 0.  One thread per
-//    (b, 8 or 4 channels, run of tokens) slides the window along its run in
-//    registers; a wave covers 64 neighbouring channel groups, so every token
-//    row is read as contiguous 16-byte pieces.
+//    (b, 8 or 4 channels, run of 32 tokens) slides the window along its run
+//    in registers, with 8 tokens of loads in flight; a wave covers 64
+//    neighbouring channel groups, so every token row is read as contiguous
+//    16-byte pieces.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -24,15 +26,37 @@ namespace {
 // ---------------------------------------------------------------- GroupNorm
 
 constexpr int GN_WAVES = 4;
-constexpr int GN_MAXC = 4;   // 4-element pieces per lane: d_v <= 1024
+
+// Data read or written exactly once go through non-temporal accesses, so
+// that streaming them does not evict what the caches hold for others.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint2 ld8_nt(const void* p) {
+  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return make_uint2(v[0], v[1]);
+}
+__device__ __forceinline__ uint4 ld16_nt(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void st8_nt(void* p, uint2 x) {
+  const u32x2 v = {x.x, x.y};
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
+}
+__device__ __forceinline__ void st16_nt(void* p, uint4 x) {
+  const u32x4 v = {x.x, x.y, x.z, x.w};
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
 
 __device__ __forceinline__ void load4(const void* p, int bf16, int64_t i, float* x) {
   if (bf16) {
-    const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(p) + i);
+    const uint2 u = ld8_nt(static_cast<const bf16_t*>(p) + i);
     x[0] = bf_lo(u.x); x[1] = bf_hi(u.x); x[2] = bf_lo(u.y); x[3] = bf_hi(u.y);
   } else {
-    const float4 f = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
-    x[0] = f.x; x[1] = f.y; x[2] = f.z; x[3] = f.w;
+    const uint4 f = ld16_nt(static_cast<const float*>(p) + i);
+    x[0] = __uint_as_float(f.x); x[1] = __uint_as_float(f.y);
+    x[2] = __uint_as_float(f.z); x[3] = __uint_as_float(f.w);
   }
 }
 
@@ -42,71 +66,92 @@ __device__ __forceinline__ float wave_allsum(float x) {
   return x;
 }
 
+// NCH 4-feature pieces per lane (d_v <= 256 NCH), RW rows per wave: every
+// load of the wave's RW rows (h and o~) is issued before the first
+// reduction, so that RW * NCH * 64 * (h + o~ bytes) are in flight per wave.
+template <int NCH, int RW>
 __global__ __launch_bounds__(GN_WAVES * 64) void groupnorm_ogate_kernel(GnArgs a) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * GN_WAVES + (threadIdx.x >> 6);
-  if (row >= a.rows) return;
+  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * GN_WAVES + (threadIdx.x >> 6)) * RW;
   const int dv = a.dv;
-  const int64_t base = row * dv;
-  const int head = static_cast<int>((row / a.T) % a.H);
-  float x[GN_MAXC][4];
-  float s = 0.0f;
+  float x[RW][NCH][4], o[RW][NCH][4];
 #pragma unroll
-  for (int c = 0; c < GN_MAXC; ++c) {
-    const int e = 4 * lane + 256 * c;
-    if (e < dv) {
-      load4(a.h, a.h_bf16, base + e, x[c]);
-      s += (x[c][0] + x[c][1]) + (x[c][2] + x[c][3]);
-    }
-  }
-  const float mean = wave_allsum(s) / static_cast<float>(dv);
-  float s2 = 0.0f;
+  for (int w = 0; w < RW; ++w) {
+    const int64_t row = row0 + w;
 #pragma unroll
-  for (int c = 0; c < GN_MAXC; ++c) {
-    const int e = 4 * lane + 256 * c;
-    if (e < dv) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        x[c][j] -= mean;
-        s2 += x[c][j] * x[c][j];
+    for (int c = 0; c < NCH; ++c) {
+      const int e = 4 * lane + 256 * c;
+      if (row < a.rows && e < dv) {
+        load4(a.h, a.h_bf16, row * dv + e, x[w][c]);
+        if (a.o_pre) load4(a.o_pre, a.o_bf16, row * dv + e, o[w][c]);
       }
     }
   }
-  const float rstd = rsqrtf(wave_allsum(s2) / static_cast<float>(dv) + a.eps);
 #pragma unroll
-  for (int c = 0; c < GN_MAXC; ++c) {
-    const int e = 4 * lane + 256 * c;
-    if (e >= dv) continue;
-    float y[4];
+  for (int w = 0; w < RW; ++w) {
+    const int64_t row = row0 + w;
+    if (row >= a.rows) break;   // uniform across the wave
+    const int64_t base = row * dv;
+    const int head = static_cast<int>((row / a.T) % a.H);
+    float s = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) y[j] = x[c][j] * rstd;
-    if (a.gamma) {
-      const float4 g = *reinterpret_cast<const float4*>(a.gamma + static_cast<int64_t>(head) * dv + e);
-      y[0] *= g.x; y[1] *= g.y; y[2] *= g.z; y[3] *= g.w;
-    }
-    if (a.beta) {
-      const float4 b = *reinterpret_cast<const float4*>(a.beta + static_cast<int64_t>(head) * dv + e);
-      y[0] += b.x; y[1] += b.y; y[2] += b.z; y[3] += b.w;
-    }
-    if (a.o_pre) {
-      float o[4];
-      load4(a.o_pre, a.o_bf16, base + e, o);
+    for (int c = 0; c < NCH; ++c)
+      if (4 * lane + 256 * c < dv) s += (x[w][c][0] + x[w][c][1]) + (x[w][c][2] + x[w][c][3]);
+    const float mean = wave_allsum(s) / static_cast<float>(dv);
+    float s2 = 0.0f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) y[j] *= 1.0f / (1.0f + __expf(-o[j]));
+    for (int c = 0; c < NCH; ++c) {
+      if (4 * lane + 256 * c < dv) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          x[w][c][j] -= mean;
+          s2 += x[w][c][j] * x[w][c][j];
+        }
+      }
     }
-    if (a.h_bf16) {
-      *reinterpret_cast<uint2*>(static_cast<bf16_t*>(a.y) + base + e) =
-          make_uint2(pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3]));
-    } else {
-      *reinterpret_cast<float4*>(static_cast<float*>(a.y) + base + e) = make_float4(y[0], y[1], y[2], y[3]);
+    const float rstd = rsqrtf(wave_allsum(s2) / static_cast<float>(dv) + a.eps);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int e = 4 * lane + 256 * c;
+      if (e >= dv) continue;
+      float y[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) y[j] = x[w][c][j] * rstd;
+      if (a.gamma) {
+        const float4 g = *reinterpret_cast<const float4*>(a.gamma + static_cast<int64_t>(head) * dv + e);
+        y[0] *= g.x; y[1] *= g.y; y[2] *= g.z; y[3] *= g.w;
+      }
+      if (a.beta) {
+        const float4 b = *reinterpret_cast<const float4*>(a.beta + static_cast<int64_t>(head) * dv + e);
+        y[0] += b.x; y[1] += b.y; y[2] += b.z; y[3] += b.w;
+      }
+      if (a.o_pre) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) y[j] *= 1.0f / (1.0f + __expf(-o[w][c][j]));
+      }
+      if (a.h_bf16) {
+        st8_nt(static_cast<bf16_t*>(a.y) + base + e, make_uint2(pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3])));
+      } else {
+        st16_nt(static_cast<float*>(a.y) + base + e,
+                make_uint4(__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]),
+                           __float_as_uint(y[3])));
+      }
     }
   }
+}
+
+template <int NCH, int RW>
+hipError_t launch_gn(const GnArgs& a, hipStream_t st) {
+  const int64_t per_block = static_cast<int64_t>(GN_WAVES) * RW;
+  const unsigned blocks = static_cast<unsigned>((a.rows + per_block - 1) / per_block);
+  groupnorm_ogate_kernel<NCH, RW><<<blocks, GN_WAVES * 64, 0, st>>>(a);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- causal conv
 
 constexpr int CONV_THREADS = 256;
-constexpr int CONV_RUN = 64;      // tokens per thread
+constexpr int CONV_RUN = 32;      // tokens per thread
 
 // VE channels per thread (8 for bf16, 4 for float32), kernel size K.
 template <int VE, int K>
@@ -158,7 +203,7 @@ __global__ __launch_bounds__(CONV_THREADS) void causal_conv_kernel(ConvArgs a) {
       for (int v = 0; v < VE; ++v) win[s][v] = 0.0f;
     }
   }
-  constexpr int U = 4;   // tokens loaded ahead together
+  constexpr int U = 8;   // tokens loaded ahead together
   for (int64_t t = t0; t < t1; t += U) {
     float cur[U][VE];
 #pragma unroll
@@ -227,9 +272,9 @@ hipError_t launch_conv_ve(const ConvArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_groupnorm_ogate(const GnArgs& a, hipStream_t st) {
-  const unsigned blocks = static_cast<unsigned>((a.rows + GN_WAVES - 1) / GN_WAVES);
-  groupnorm_ogate_kernel<<<blocks, GN_WAVES * 64, 0, st>>>(a);
-  return hipGetLastError();
+  if (a.dv <= 256) return launch_gn<1, 4>(a, st);
+  if (a.dv <= 512) return launch_gn<2, 2>(a, st);
+  return launch_gn<4, 1>(a, st);
 }
 
 hipError_t launch_causal_conv(const ConvArgs& a, hipStream_t st) {
