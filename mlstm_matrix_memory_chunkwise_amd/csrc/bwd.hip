@@ -431,7 +431,7 @@ __global__ __launch_bounds__(NTB) void bwd_head_kernel(BwdArgs a, int ncb, int n
   // constant term from the final-state gradient
   float kend = 0.0f;
   if (a.dC1) {
-    const float* CT = a.ws_C + (bh * nb + nc) * dqk * dv;
+    const float* CT = a.ws_CT ? a.ws_CT + bh * dqk * dv : a.ws_C + (bh * nb + nc) * dqk * dv;
     for (int64_t e = tid; e < dqk * dv; e += NTB) kend += a.dC1[bh * dqk * dv + e] * CT[e];
     for (int64_t e = tid; e < dqk; e += NTB) kend += a.dn1[bh * dqk + e] * a.ws_n[(bh * nb + nc) * dqk + e];
   }
@@ -520,7 +520,11 @@ size_t bwd_workspace(const BwdArgs& a, size_t offsets[8]) {
   const size_t nb = static_cast<size_t>(a.T / a.L) + 1, dqk = static_cast<size_t>(a.dqk);
   const size_t dv = static_cast<size_t>(a.dv);
   const size_t ncb = dv / static_cast<size_t>(bwd_tile_columns(a));
-  const size_t sizes[8] = {BH * nb * dqk * dv * 4, BH * nb * dqk * 4, BH * nb * 4, BH * T * 4,
+  // chunk 64 keeps the boundary states the reverse pass reads as bf16 tiles,
+  // and the final state (for the forget-gate term) in float32 after them
+  const size_t states = a.L == 64 ? round_up(BH * (nb - 1) * dqk * dv * 2) + BH * dqk * dv * 4
+                                  : BH * nb * dqk * dv * 4;
+  const size_t sizes[8] = {states, BH * nb * dqk * 4, BH * nb * 4, BH * T * 4,
                            ncb * BH * T * dqk * 4, ncb * BH * T * dqk * 4, BH * T * 4, ncb * BH * 4};
   size_t off = 0;
   for (int i = 0; i < 8; ++i) {
@@ -534,7 +538,17 @@ hipError_t launch_bwd(BwdArgs a, void* ws, hipStream_t st) {
   size_t off[8];
   bwd_workspace(a, off);
   char* base = static_cast<char*>(ws);
-  a.ws_C = reinterpret_cast<float*>(base + off[0]);
+  if (a.L == 64) {
+    const size_t tiles = static_cast<size_t>(a.B * a.H) * static_cast<size_t>(a.T / 64) *
+                         static_cast<size_t>(a.dqk * a.dv) * 2;
+    a.ws_C = nullptr;
+    a.ws_Cb = reinterpret_cast<uint16_t*>(base + off[0]);
+    a.ws_CT = reinterpret_cast<float*>(base + off[0] + round_up(tiles));
+  } else {
+    a.ws_C = reinterpret_cast<float*>(base + off[0]);
+    a.ws_Cb = nullptr;
+    a.ws_CT = nullptr;
+  }
   a.ws_n = reinterpret_cast<float*>(base + off[1]);
   a.ws_m = reinterpret_cast<float*>(base + off[2]);
   a.ws_beta = reinterpret_cast<float*>(base + off[3]);

@@ -82,6 +82,7 @@ __global__ __launch_bounds__(NT4, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
   __shared__ __align__(1024) char sW[TB];
   __shared__ __align__(1024) char sDS[TB];
   __shared__ __align__(1024) char sCX[DK * 128];   // [DK][64]: C~_s, then dC
+  __shared__ __align__(1024) char sGD[16 * 128];   // rows 0, 1: g (.) dnq as bf16 hi / lo; rest 0
   __shared__ float sN[DK], sDn[DK];
   __shared__ float sRs[4][LC];
   __shared__ float sQn[LC], sDen[LC], sDnq[LC], sBeta[LC];
@@ -114,6 +115,7 @@ __global__ __launch_bounds__(NT4, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
     }
   }
   for (int x = tid; x < DK; x += NT4) sDn[x] = a.dn1 ? a.dn1[bh * DK + x] : 0.0f;
+  reinterpret_cast<uint2*>(sGD)[tid] = make_uint2(0u, 0u);
 
   for (int c = nc - 1; c >= 0; --c) {
     const int64_t tok0 = bh * T + static_cast<int64_t>(c) * LC;
@@ -140,16 +142,11 @@ __global__ __launch_bounds__(NT4, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
         const int r = e >> 3, cc = (e & 7) * 8;
         *reinterpret_cast<uint4*>(sV + swz(r, cc)) = *reinterpret_cast<const uint4*>(v + static_cast<int64_t>(r) * dv + cc);
       }
-      const float* Cs = a.ws_C + ((bh * nb + c) * DK) * dv + c0;
+      // C~_s: the state pass stored it as this workgroup's swizzled bf16 tile
+      const uint4* Cs = reinterpret_cast<const uint4*>(a.ws_Cb + ((bh * ncb + cb) * nc + c) * (DK * TVC));
 #pragma unroll
-      for (int p = 0; p < DK * TVC / 8 / NT4; ++p) {
-        const int e = tid + p * NT4;
-        const int r = e >> 3, cc = (e & 7) * 8;
-        const float4 x0 = *reinterpret_cast<const float4*>(Cs + static_cast<int64_t>(r) * dv + cc);
-        const float4 x1 = *reinterpret_cast<const float4*>(Cs + static_cast<int64_t>(r) * dv + cc + 4);
-        *reinterpret_cast<uint4*>(sCX + swz(r, cc)) =
-            make_uint4(pk2(x0.x, x0.y), pk2(x0.z, x0.w), pk2(x1.x, x1.y), pk2(x1.z, x1.w));
-      }
+      for (int p = 0; p < DK * TVC / 8 / NT4; ++p)
+        *reinterpret_cast<uint4*>(sCX + 16 * (tid + p * NT4)) = Cs[tid + p * NT4];
     }
     for (int x = tid; x < DK; x += NT4) sN[x] = a.ws_n[(bh * nb + c) * DK + x];
     if (tid < LC) sBeta[tid] = a.ws_beta[tok0 + tid];
@@ -206,7 +203,14 @@ __global__ __launch_bounds__(NT4, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
       const float floor_ = __expf(-G.m[i]);
       const float den = fmaxf(fabsf(nq), floor_);
       sDen[i] = den;
-      sDnq[i] = fabsf(nq) >= floor_ ? (nq >= 0.0f ? -sBeta[i] / den : sBeta[i] / den) : 0.0f;
+      const float dnq = fabsf(nq) >= floor_ ? (nq >= 0.0f ? -sBeta[i] / den : sBeta[i] / den) : 0.0f;
+      sDnq[i] = dnq;
+      if (lead) {   // the A operand of dn += sum_i g_i dnq_i q_i (hi and lo rows)
+        const float gd = G.g[i] * dnq;
+        const bf16_t hi = f2bf(gd);
+        *reinterpret_cast<bf16_t*>(sGD + swz(0, i)) = hi;
+        *reinterpret_cast<bf16_t*>(sGD + swz(1, i)) = f2bf(gd - bf2f(hi));
+      }
     }
     __syncthreads();
     // ---- r, g r, w V (bf16 to LDS) and do~ (16 columns per thread)
@@ -416,29 +420,40 @@ __global__ __launch_bounds__(NT4, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
                         accA[jt][2] + wj * accB[jt][2], accA[jt][3] + wj * accB[jt][3]);
       }
     }
-    // ---- dC^T <- g_L dC^T + (g R)^T Q
+    // ---- dC^T <- g_L dC^T + (g R)^T Q; in column block 0 also the
+    // normalizer's sum_i g_i dnq_i q_i for this wave's x tiles (rows 0 + 1)
+    f32x4 dnacc[XPW];
     {
       const float gL = G.g[LC - 1];
 #pragma unroll
       for (int xt = 0; xt < NXT; ++xt) dCt[xt] *= gL;
+#pragma unroll
+      for (int p = 0; p < XPW; ++p) dnacc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const bf16x8 Ag = colfrag(sGR, 32 * ks, wave * 16, g, kr, kq);
 #pragma unroll
         for (int xt = 0; xt < NXT; ++xt)
           dCt[xt] = mfma16x16x32(Ag, colfrag(wide(sQ, xt * 16), 32 * ks, (xt * 16) & 63, g, kr, kq), dCt[xt]);
+        if (lead) {
+          const bf16x8 Ad = rowfrag(sGD, l16, 32 * ks + 8 * g);
+#pragma unroll
+          for (int p = 0; p < XPW; ++p) {
+            const int xt = wave * XPW + p;
+            dnacc[p] = mfma16x16x32(Ad, colfrag(wide(sQ, xt * 16), 32 * ks, (xt * 16) & 63, g, kr, kq), dnacc[p]);
+          }
+        }
       }
     }
     __syncthreads();   // every read of sDn (dk) is done
-    // ---- dn <- g_L dn + sum_i g_i dnq_i q_i
-    for (int x = tid; x < DK; x += NT4) {
-      float s = G.g[LC - 1] * sDn[x];
-      const char* qt = wide(sQ, x);
-      for (int i = 0; i < LC; ++i) {
-        const bf16_t qv = *reinterpret_cast<const bf16_t*>(qt + swz(i, x & 63));
-        s += G.g[i] * sDnq[i] * bf2f(qv);
+    // ---- dn <- g_L dn + sum_i g_i dnq_i q_i (column block 0 only uses dn)
+    if (lead && g == 0) {
+      const float gL = G.g[LC - 1];
+#pragma unroll
+      for (int p = 0; p < XPW; ++p) {
+        const int x = (wave * XPW + p) * 16 + l16;
+        sDn[x] = gL * sDn[x] + (dnacc[p][0] + dnacc[p][1]);
       }
-      sDn[x] = s;
     }
   }
   // ---- the initial state's gradients and dm0's share
@@ -540,12 +555,22 @@ __global__ __launch_bounds__(NT4, 1) void bwd_states_mfma_kernel(BwdArgs a) {
     // chunk's reads of sK[(c + 1) & 1], sWH, sWL and G are done
     wait_vm<0>();
     __syncthreads();
-    // the stored state at boundary c
-    float* wsC = a.ws_C + (bh * nb + c) * DK * dv + c0 + wave * 16 + 4 * g;
+    // the stored state at boundary c: before a chunk as this workgroup's
+    // swizzled bf16 tile (the reverse pass's LDS image), after the last
+    // chunk in float32
+    if (c < nc) {
+      char* tile = reinterpret_cast<char*>(a.ws_Cb + ((bh * ncb + cb) * nc + c) * (DK * TVC));
 #pragma unroll
-    for (int xt = 0; xt < NXT; ++xt)
-      *reinterpret_cast<float4*>(wsC + static_cast<int64_t>(xt * 16 + l16) * dv) =
-          make_float4(Ct[xt][0], Ct[xt][1], Ct[xt][2], Ct[xt][3]);
+      for (int xt = 0; xt < NXT; ++xt)
+        *reinterpret_cast<uint2*>(tile + swz(xt * 16 + l16, wave * 16 + 4 * g)) =
+            make_uint2(pk2(Ct[xt][0], Ct[xt][1]), pk2(Ct[xt][2], Ct[xt][3]));
+    } else {
+      float* wsC = a.ws_CT + bh * DK * dv + c0 + wave * 16 + 4 * g;
+#pragma unroll
+      for (int xt = 0; xt < NXT; ++xt)
+        *reinterpret_cast<float4*>(wsC + static_cast<int64_t>(xt * 16 + l16) * dv) =
+            make_float4(Ct[xt][0], Ct[xt][1], Ct[xt][2], Ct[xt][3]);
+    }
     if (lead) {
       if (tid < DK) a.ws_n[(bh * nb + c) * DK + tid] = n;
       if (tid == 0) a.ws_m[bh * nb + c] = m;

@@ -101,7 +101,9 @@ struct BwdArgs {
   float* dn0;
   float* dm0;
   // workspace pieces (set by launch_bwd)
-  float* ws_C;
+  float* ws_C;      // float32 boundary states [bh][c][x][b] (chunk 16/32)
+  uint16_t* ws_Cb;  // chunk 64: bf16 boundary states as swizzled [d_qk][64] tiles, [bh][cb][c]
+  float* ws_CT;     // chunk 64: float32 final state [bh][x][b]
   float* ws_n;
   float* ws_m;
   float* ws_beta;
