@@ -47,6 +47,21 @@ __device__ __forceinline__ bf16x8 colfrag(const char* t, int k0, int m0, int g, 
 // the 64-column tile of a wide [64][DK] matrix holding column c
 __device__ __forceinline__ const char* wide(const char* base, int c) { return base + (c >> 6) * TB; }
 
+// Workgroup -> (head, column block).  Workgroups are dealt to the 8 XCDs in
+// turn (block id mod 8); with B*H a multiple of 8 the column blocks of one
+// head get ids equal mod 8, so their shared q/k reads meet in one L2.
+__device__ __forceinline__ void head_block(int64_t nhead, int ncb, int64_t& bh, int& cb) {
+  const int64_t w = blockIdx.x;
+  if (nhead % 8 == 0) {
+    const int64_t grp = w / (8 * ncb), r = w % (8 * ncb);
+    cb = static_cast<int>(r / 8);
+    bh = grp * 8 + r % 8;
+  } else {
+    bh = w / ncb;
+    cb = static_cast<int>(w % ncb);
+  }
+}
+
 struct Gate64 {
   float u[LC], M[LC], m[LC], g[LC], w[LC];
 };
@@ -93,8 +108,9 @@ __global__ __launch_bounds__(NT4, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
   const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const int kr = l16 >> 2, kq = l16 & 3;
   const int ncb = static_cast<int>(a.dv / TVC);
-  const int64_t bh = blockIdx.x / ncb;
-  const int cb = blockIdx.x % ncb;
+  int64_t bh;
+  int cb;
+  head_block(a.B * a.H, ncb, bh, cb);
   const bool lead = cb == 0;
   const int dv = static_cast<int>(a.dv);
   const int64_t T = a.T;
@@ -150,6 +166,25 @@ __global__ __launch_bounds__(NT4, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
     }
     for (int x = tid; x < DK; x += NT4) sN[x] = a.ws_n[(bh * nb + c) * DK + x];
     if (tid < LC) sBeta[tid] = a.ws_beta[tok0 + tid];
+    // this thread's dh, h and o~ (row tid / 4, 16 columns) for the r step,
+    // loaded now so that their latency overlaps the score products
+    uint4 pdh[2], ph[2], po[4];
+    {
+      const int64_t gi = (tok0 + (tid >> 2)) * dv + c0 + (tid & 3) * 16;
+#pragma unroll
+      for (int h8 = 0; h8 < 2; ++h8) {
+        pdh[h8] = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(a.dh) + gi + 8 * h8);
+        if (a.o_pre) {
+          ph[h8] = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(a.h) + gi + 8 * h8);
+          if (sizeof(TO) == 4) {
+            po[2 * h8] = *reinterpret_cast<const uint4*>(static_cast<const float*>(a.o_pre) + gi + 8 * h8);
+            po[2 * h8 + 1] = *reinterpret_cast<const uint4*>(static_cast<const float*>(a.o_pre) + gi + 8 * h8 + 4);
+          } else {
+            po[h8] = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(a.o_pre) + gi + 8 * h8);
+          }
+        }
+      }
+    }
     __syncthreads();
 
     // ---- S^T = K Q^T for key tile jt = wave; DS = D (.) S to LDS; row sums
@@ -219,11 +254,10 @@ __global__ __launch_bounds__(NT4, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
       const int64_t gi = (tok0 + i) * dv + c0 + b0;
       const float inv = 1.0f / sDen[i];
       const float gi_ = G.g[i], wi = G.w[i];
-      const bf16_t* dh = static_cast<const bf16_t*>(a.dh) + gi;
       uint32_t rp[8], gp[8], wp[8];
 #pragma unroll
       for (int h8 = 0; h8 < 2; ++h8) {
-        const uint4 d8 = *reinterpret_cast<const uint4*>(dh + 8 * h8);
+        const uint4 d8 = pdh[h8];
         const uint4 v8 = lds_ld16(sV, swz(i, b0 + 8 * h8));
         float dhv[8] = {bf_lo(d8.x), bf_hi(d8.x), bf_lo(d8.y), bf_hi(d8.y),
                         bf_lo(d8.z), bf_hi(d8.z), bf_lo(d8.w), bf_hi(d8.w)};
@@ -231,17 +265,18 @@ __global__ __launch_bounds__(NT4, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
                        bf_lo(v8.z), bf_hi(v8.z), bf_lo(v8.w), bf_hi(v8.w)};
         float gate[8];
         if (a.o_pre) {
-          const uint4 h8v = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(a.h) + gi + 8 * h8);
+          const uint4 h8v = ph[h8];
           const float hv[8] = {bf_lo(h8v.x), bf_hi(h8v.x), bf_lo(h8v.y), bf_hi(h8v.y),
                                bf_lo(h8v.z), bf_hi(h8v.z), bf_lo(h8v.w), bf_hi(h8v.w)};
           float ov[8];
           if (sizeof(TO) == 4) {
-            const float4 o0 = *reinterpret_cast<const float4*>(static_cast<const float*>(a.o_pre) + gi + 8 * h8);
-            const float4 o1 = *reinterpret_cast<const float4*>(static_cast<const float*>(a.o_pre) + gi + 8 * h8 + 4);
-            ov[0] = o0.x; ov[1] = o0.y; ov[2] = o0.z; ov[3] = o0.w;
-            ov[4] = o1.x; ov[5] = o1.y; ov[6] = o1.z; ov[7] = o1.w;
+            const uint4 o0 = po[2 * h8], o1 = po[2 * h8 + 1];
+            ov[0] = __uint_as_float(o0.x); ov[1] = __uint_as_float(o0.y);
+            ov[2] = __uint_as_float(o0.z); ov[3] = __uint_as_float(o0.w);
+            ov[4] = __uint_as_float(o1.x); ov[5] = __uint_as_float(o1.y);
+            ov[6] = __uint_as_float(o1.z); ov[7] = __uint_as_float(o1.w);
           } else {
-            const uint4 o8 = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(a.o_pre) + gi + 8 * h8);
+            const uint4 o8 = po[h8];
             ov[0] = bf_lo(o8.x); ov[1] = bf_hi(o8.x); ov[2] = bf_lo(o8.y); ov[3] = bf_hi(o8.y);
             ov[4] = bf_lo(o8.z); ov[5] = bf_hi(o8.z); ov[6] = bf_lo(o8.w); ov[7] = bf_hi(o8.w);
           }
@@ -522,8 +557,9 @@ __global__ __launch_bounds__(NT4, 1) void bwd_states_mfma_kernel(BwdArgs a) {
   const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const int kr = l16 >> 2, kq = l16 & 3;
   const int ncb = static_cast<int>(a.dv / TVC);
-  const int64_t bh = blockIdx.x / ncb;
-  const int cb = blockIdx.x % ncb;
+  int64_t bh;
+  int cb;
+  head_block(a.B * a.H, ncb, bh, cb);
   const int dv = static_cast<int>(a.dv);
   const int64_t T = a.T;
   const int nc = static_cast<int>(T / LC);   // >= 1
