@@ -14,7 +14,8 @@
 //    y[t, c] = bias[c] + sum_{s<K} w[c, s] x[t - K + 1 + s, c], with an
 //    optional carried window of the K - 1 inputs before t = 0.  One thread per
 //    (b, 8 or 4 channels, run of 32 tokens) slides the window along its run
-//    in registers, with 8 tokens of loads in flight; a wave covers 64
+//    in registers, loading the next 4 tokens while it computes the current
+//    4 (software pipeline); a wave covers 64
 //    neighbouring channel groups, so every token row is read as contiguous
 //    16-byte pieces.
 #include "common.hpp"
@@ -203,22 +204,45 @@ __global__ __launch_bounds__(CONV_THREADS) void causal_conv_kernel(ConvArgs a) {
       for (int v = 0; v < VE; ++v) win[s][v] = 0.0f;
     }
   }
-  constexpr int U = 8;   // tokens loaded ahead together
-  for (int64_t t = t0; t < t1; t += U) {
-    float cur[U][VE];
+  // Software pipeline over batches of U tokens: the raw 16-byte rows of the
+  // next batch are requested before the current batch is computed.  Loads
+  // past the run's end re-read its last token (always in bounds, no branch).
+  constexpr int U = 4;
+  const char* xrow = static_cast<const char*>(a.x) + (b * a.T * a.C + c0) * (a.x_bf16 ? 2 : 4);
+  const int64_t rstride = a.C * (a.x_bf16 ? 2 : 4);
+  uint4 nxt[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (t + u < t1) load(t + u, cur[u]);
+  for (int u = 0; u < U; ++u) {
+    const int64_t tt = t0 + u < t1 ? t0 + u : t1 - 1;
+    nxt[u] = *reinterpret_cast<const uint4*>(xrow + tt * rstride);
+  }
+  for (int64_t t = t0; t < t1; t += U) {
+    uint4 cur[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t tt = t + U + u < t1 ? t + U + u : t1 - 1;
+      nxt[u] = *reinterpret_cast<const uint4*>(xrow + tt * rstride);
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (t + u >= t1) break;
+      float xv[VE];
+      {
+        const uint32_t wd[4] = {cur[u].x, cur[u].y, cur[u].z, cur[u].w};
+#pragma unroll
+        for (int v = 0; v < VE; ++v)
+          xv[v] = a.x_bf16 ? ((v & 1) ? bf_hi(wd[(v >> 1) & 3]) : bf_lo(wd[(v >> 1) & 3]))
+                           : __uint_as_float(wd[v & 3]);
+      }
       float y[VE];
 #pragma unroll
       for (int v = 0; v < VE; ++v) {
         float acc = bias[v];
 #pragma unroll
         for (int s = 0; s < K - 1; ++s) acc += w[v][s] * win[s][v];
-        y[v] = acc + w[v][K - 1] * cur[u][v];
+        y[v] = acc + w[v][K - 1] * xv[v];
       }
 #pragma unroll
       for (int s = 0; s + 1 < K - 1; ++s)
@@ -226,7 +250,7 @@ __global__ __launch_bounds__(CONV_THREADS) void causal_conv_kernel(ConvArgs a) {
         for (int v = 0; v < VE; ++v) win[s][v] = win[s + 1][v];
       if (K > 1) {
 #pragma unroll
-        for (int v = 0; v < VE; ++v) win[K > 1 ? K - 2 : 0][v] = cur[u][v];
+        for (int v = 0; v < VE; ++v) win[K > 1 ? K - 2 : 0][v] = xv[v];
       }
       const int64_t o = (b * a.T + t + u) * a.C + c0;
       if (a.x_bf16) {
