@@ -6,10 +6,12 @@
 //  * Per-head group normalization with the output gate, on the cell output
 //    h [B, H, T, d_v]: y = sigmoid(o~) (gamma (h - mean) / sqrt(var + eps) +
 //    beta), mean and (biased) variance over the d_v features of one (b, head,
-//    t).  One wave per 4, 2 or 1 (b, head, t) rows (d_v up to 256, 512,
-//    1024): the rows are loaded once into registers with every load issued
-//    before the first reduction, reduced twice across the wave (mean, then
-//    the centred second moment, so no cancellation), and written once.
+//    t).  With d_v a multiple of 8, a row is held by half a wave in 16-byte
+//    pieces (8 features per lane), so each load instruction covers two rows;
+//    otherwise one wave per row, 4 features per lane.  The rows are loaded
+//    once into registers with every load issued before the first reduction,
+//    reduced twice (mean, then the centred second moment, so no
+//    cancellation), and written once.
 //  * Causal depthwise convolution over the token axis, x [B, T, C]:
 //    y[t, c] = bias[c] + sum_{s<K} w[c, s] x[t - K + 1 + s, c], with an
 //    optional carried window of the K - 1 inputs before t = 0.  One thread per
@@ -139,6 +141,122 @@ __global__ __launch_bounds__(GN_WAVES * 64) void groupnorm_ogate_kernel(GnArgs a
       }
     }
   }
+}
+
+// 8 features per lane (16-byte bf16 h loads): a row of d_v <= 256 NCH8
+// features is held by one half-wave (32 lanes) in NCH8 pieces, so one load
+// instruction covers two rows; RW row pairs per wave, every load issued
+// before the first reduction.  d_v must be a multiple of 8.
+__device__ __forceinline__ float half_allsum(float x) {
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+__device__ __forceinline__ void load8(const void* p, int bf16, int64_t i, float* x) {
+  if (bf16) {
+    const uint4 u = ld16_nt(static_cast<const bf16_t*>(p) + i);
+    x[0] = bf_lo(u.x); x[1] = bf_hi(u.x); x[2] = bf_lo(u.y); x[3] = bf_hi(u.y);
+    x[4] = bf_lo(u.z); x[5] = bf_hi(u.z); x[6] = bf_lo(u.w); x[7] = bf_hi(u.w);
+  } else {
+    const uint4 f0 = ld16_nt(static_cast<const float*>(p) + i);
+    const uint4 f1 = ld16_nt(static_cast<const float*>(p) + i + 4);
+    x[0] = __uint_as_float(f0.x); x[1] = __uint_as_float(f0.y);
+    x[2] = __uint_as_float(f0.z); x[3] = __uint_as_float(f0.w);
+    x[4] = __uint_as_float(f1.x); x[5] = __uint_as_float(f1.y);
+    x[6] = __uint_as_float(f1.z); x[7] = __uint_as_float(f1.w);
+  }
+}
+
+template <int NCH8, int RW>
+__global__ __launch_bounds__(GN_WAVES * 64) void groupnorm_ogate8_kernel(GnArgs a) {
+  const int lane = threadIdx.x & 63, hl = lane & 31, half = lane >> 5;
+  const int64_t pair0 = (static_cast<int64_t>(blockIdx.x) * GN_WAVES + (threadIdx.x >> 6)) * RW;
+  const int dv = a.dv;
+  float x[RW][NCH8][8], o[RW][NCH8][8];
+#pragma unroll
+  for (int w = 0; w < RW; ++w) {
+    const int64_t row = 2 * (pair0 + w) + half;
+#pragma unroll
+    for (int c = 0; c < NCH8; ++c) {
+      const int e = 8 * hl + 256 * c;
+      if (row < a.rows && e < dv) {
+        load8(a.h, a.h_bf16, row * dv + e, x[w][c]);
+        if (a.o_pre) load8(a.o_pre, a.o_bf16, row * dv + e, o[w][c]);
+      }
+    }
+  }
+#pragma unroll
+  for (int w = 0; w < RW; ++w) {
+    const int64_t row = 2 * (pair0 + w) + half;
+    const bool live = row < a.rows;   // the two halves may differ only at the very end
+    float s = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NCH8; ++c)
+      if (live && 8 * hl + 256 * c < dv)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s += x[w][c][j];
+    const float mean = half_allsum(s) / static_cast<float>(dv);
+    float s2 = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NCH8; ++c) {
+      if (live && 8 * hl + 256 * c < dv) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          x[w][c][j] -= mean;
+          s2 += x[w][c][j] * x[w][c][j];
+        }
+      }
+    }
+    const float rstd = rsqrtf(half_allsum(s2) / static_cast<float>(dv) + a.eps);
+    if (!live) continue;
+    const int64_t base = row * dv;
+    const int head = static_cast<int>((row / a.T) % a.H);
+#pragma unroll
+    for (int c = 0; c < NCH8; ++c) {
+      const int e = 8 * hl + 256 * c;
+      if (e >= dv) continue;
+      float y[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) y[j] = x[w][c][j] * rstd;
+      if (a.gamma) {
+        const float4 g0 = *reinterpret_cast<const float4*>(a.gamma + static_cast<int64_t>(head) * dv + e);
+        const float4 g1 = *reinterpret_cast<const float4*>(a.gamma + static_cast<int64_t>(head) * dv + e + 4);
+        y[0] *= g0.x; y[1] *= g0.y; y[2] *= g0.z; y[3] *= g0.w;
+        y[4] *= g1.x; y[5] *= g1.y; y[6] *= g1.z; y[7] *= g1.w;
+      }
+      if (a.beta) {
+        const float4 b0 = *reinterpret_cast<const float4*>(a.beta + static_cast<int64_t>(head) * dv + e);
+        const float4 b1 = *reinterpret_cast<const float4*>(a.beta + static_cast<int64_t>(head) * dv + e + 4);
+        y[0] += b0.x; y[1] += b0.y; y[2] += b0.z; y[3] += b0.w;
+        y[4] += b1.x; y[5] += b1.y; y[6] += b1.z; y[7] += b1.w;
+      }
+      if (a.o_pre) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) y[j] *= 1.0f / (1.0f + __expf(-o[w][c][j]));
+      }
+      if (a.h_bf16) {
+        st16_nt(static_cast<bf16_t*>(a.y) + base + e,
+                make_uint4(pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3]), pack_bf2(y[4], y[5]),
+                           pack_bf2(y[6], y[7])));
+      } else {
+        float* yp = static_cast<float*>(a.y) + base + e;
+        st16_nt(yp, make_uint4(__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]),
+                               __float_as_uint(y[3])));
+        st16_nt(yp + 4, make_uint4(__float_as_uint(y[4]), __float_as_uint(y[5]), __float_as_uint(y[6]),
+                                   __float_as_uint(y[7])));
+      }
+    }
+  }
+}
+
+template <int NCH8, int RW>
+hipError_t launch_gn8(const GnArgs& a, hipStream_t st) {
+  const int64_t pairs = (a.rows + 1) / 2;
+  const int64_t per_block = static_cast<int64_t>(GN_WAVES) * RW;
+  const unsigned blocks = static_cast<unsigned>((pairs + per_block - 1) / per_block);
+  groupnorm_ogate8_kernel<NCH8, RW><<<blocks, GN_WAVES * 64, 0, st>>>(a);
+  return hipGetLastError();
 }
 
 template <int NCH, int RW>
@@ -296,6 +414,11 @@ hipError_t launch_conv_ve(const ConvArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_groupnorm_ogate(const GnArgs& a, hipStream_t st) {
+  if (a.dv % 8 == 0) {
+    if (a.dv <= 256) return launch_gn8<1, 2>(a, st);
+    if (a.dv <= 512) return launch_gn8<2, 1>(a, st);
+    return launch_gn8<4, 1>(a, st);
+  }
   if (a.dv <= 256) return launch_gn<1, 4>(a, st);
   if (a.dv <= 512) return launch_gn<2, 2>(a, st);
   return launch_gn<4, 1>(a, st);
