@@ -95,12 +95,12 @@ __global__ __launch_bounds__(NT4, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
   __shared__ __align__(1024) char sR[TB];
   __shared__ __align__(1024) char sGR[TB];
   __shared__ __align__(1024) char sW[TB];
-  __shared__ __align__(1024) char sDS[TB];
+  __shared__ __align__(1024) char sDST[TB];   // (D (.) S)^T: [j][i]
   __shared__ __align__(1024) char sCX[DK * 128];   // [DK][64]: C~_s, then dC
   __shared__ __align__(1024) char sGD[16 * 128];   // rows 0, 1: g (.) dnq as bf16 hi / lo; rest 0
   __shared__ float sN[DK], sDn[DK];
-  __shared__ float sRs[4][LC];
-  __shared__ float sQn[LC], sDen[LC], sDnq[LC], sBeta[LC];
+  __shared__ float sRs[LC];
+  __shared__ float sDnq[LC], sBeta[LC];
   __shared__ Gate64 G;
   __shared__ float sRed[4];
 
@@ -187,35 +187,53 @@ __global__ __launch_bounds__(NT4, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
     }
     __syncthreads();
 
-    // ---- S^T = K Q^T for key tile jt = wave; DS = D (.) S to LDS; row sums
+    // ---- S = Q K^T for query tile it = wave (all key tiles): D (.) S goes to
+    // LDS transposed ([j][i]); its row sums stay inside the wave, so the
+    // denominators and the r step below need no workgroup barrier
     {
       f32x4 acc[4];
 #pragma unroll
-      for (int it = 0; it < 4; ++it) acc[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int jt = 0; jt < 4; ++jt) acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < DK / 32; ++ks) {
         const int x0 = 32 * ks;
-        const bf16x8 A = rowfrag(wide(sK, x0), wave * 16 + l16, (x0 & 63) + 8 * g);
+        const bf16x8 A = rowfrag(wide(sQ, x0), wave * 16 + l16, (x0 & 63) + 8 * g);
 #pragma unroll
-        for (int it = 0; it < 4; ++it)
-          acc[it] = mfma16x16x32(A, rowfrag(wide(sQ, x0), it * 16 + l16, (x0 & 63) + 8 * g), acc[it]);
+        for (int jt = 0; jt < 4; ++jt)
+          acc[jt] = mfma16x16x32(A, rowfrag(wide(sK, x0), jt * 16 + l16, (x0 & 63) + 8 * g), acc[jt]);
+      }
+      // lane: S[i = 16 wave + 4 g + e][j = 16 jt + l16]
+      float Mi[4], rs[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        Mi[e] = G.M[wave * 16 + 4 * g + e];
+        rs[e] = 0.0f;
       }
 #pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int i = it * 16 + l16;
-        const float Mi = G.M[i];
+      for (int jt = 0; jt < 4; ++jt) {
+        const int j = jt * 16 + l16;
+        const float uj = G.u[j];
         float ds[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int j = wave * 16 + 4 * g + e;
-          ds[e] = j <= i ? __expf(G.u[j] - Mi) * acc[it][e] : 0.0f;
+          ds[e] = j <= wave * 16 + 4 * g + e ? __expf(uj - Mi[e]) * acc[jt][e] : 0.0f;
+          rs[e] += ds[e];
         }
-        *reinterpret_cast<uint2*>(sDS + swz(i, wave * 16 + 4 * g)) = make_uint2(pk2(ds[0], ds[1]), pk2(ds[2], ds[3]));
-        const float rs = sum_groups((ds[0] + ds[1]) + (ds[2] + ds[3]));
-        if (g == 0) sRs[wave][i] = rs;
+        *reinterpret_cast<uint2*>(sDST + swz(j, wave * 16 + 4 * g)) = make_uint2(pk2(ds[0], ds[1]), pk2(ds[2], ds[3]));
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) rs[e] += __shfl_xor(rs[e], o, 64);   // over the 16 j lanes
+      }
+      if (l16 == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sRs[wave * 16 + 4 * g + e] = rs[e];
       }
     }
-    // q . n~_s (four threads per token)
+    // q . n~_s, the denominator and the normalizer gradient: the four threads
+    // of token i = tid / 4 (the query rows of this wave) each hold them
+    float den;
     {
       const int i = tid >> 2, qq = tid & 3;
       float s = 0.0f;
@@ -228,31 +246,29 @@ __global__ __launch_bounds__(NT4, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
       }
       s += __shfl_xor(s, 1, 64);
       s += __shfl_xor(s, 2, 64);
-      if (qq == 0) sQn[i] = s;
-    }
-    __syncthreads();
-    // ---- denominators and the normalizer gradient
-    if (tid < LC) {
-      const int i = tid;
-      const float nq = G.g[i] * sQn[i] + ((sRs[0][i] + sRs[1][i]) + (sRs[2][i] + sRs[3][i]));
+      // the row sums of this wave's rows were written by lanes of this wave
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const float nq = G.g[i] * s + sRs[i];
       const float floor_ = __expf(-G.m[i]);
-      const float den = fmaxf(fabsf(nq), floor_);
-      sDen[i] = den;
+      den = fmaxf(fabsf(nq), floor_);
       const float dnq = fabsf(nq) >= floor_ ? (nq >= 0.0f ? -sBeta[i] / den : sBeta[i] / den) : 0.0f;
-      sDnq[i] = dnq;
-      if (lead) {   // the A operand of dn += sum_i g_i dnq_i q_i (hi and lo rows)
-        const float gd = G.g[i] * dnq;
-        const bf16_t hi = f2bf(gd);
-        *reinterpret_cast<bf16_t*>(sGD + swz(0, i)) = hi;
-        *reinterpret_cast<bf16_t*>(sGD + swz(1, i)) = f2bf(gd - bf2f(hi));
+      if (qq == 0) {
+        sDnq[i] = dnq;
+        if (lead) {   // the A operand of dn += sum_i g_i dnq_i q_i (hi and lo rows)
+          const float gd = G.g[i] * dnq;
+          const bf16_t hi = f2bf(gd);
+          *reinterpret_cast<bf16_t*>(sGD + swz(0, i)) = hi;
+          *reinterpret_cast<bf16_t*>(sGD + swz(1, i)) = f2bf(gd - bf2f(hi));
+        }
       }
     }
-    __syncthreads();
     // ---- r, g r, w V (bf16 to LDS) and do~ (16 columns per thread)
     {
       const int i = tid >> 2, b0 = (tid & 3) * 16;
       const int64_t gi = (tok0 + i) * dv + c0 + b0;
-      const float inv = 1.0f / sDen[i];
+      const float inv = 1.0f / den;
       const float gi_ = G.g[i], wi = G.w[i];
       uint32_t rp[8], gp[8], wp[8];
 #pragma unroll
@@ -436,7 +452,8 @@ __global__ __launch_bounds__(NT4, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
       for (int ks = 0; ks < 2; ++ks) {
         const bf16x8 Ar = colfrag(sR, 32 * ks, wave * 16, g, kr, kq);
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) accA[jt] = mfma16x16x32(Ar, colfrag(sDS, 32 * ks, jt * 16, g, kr, kq), accA[jt]);
+        for (int jt = 0; jt < 4; ++jt)
+          accA[jt] = mfma16x16x32(Ar, rowfrag(sDST, jt * 16 + l16, 32 * ks + 8 * g), accA[jt]);
       }
 #pragma unroll
       for (int ks = 0; ks < DK / 32; ++ks) {
