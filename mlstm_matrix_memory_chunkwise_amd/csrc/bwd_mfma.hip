@@ -32,6 +32,8 @@ namespace {
 
 using namespace mk;
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int NT4 = 256;           // 4 waves
 constexpr int LC = 64;             // chunk
 constexpr int TVC = 64;            // value columns per workgroup
@@ -133,36 +135,77 @@ __global__ __launch_bounds__(NT4, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
   for (int x = tid; x < DK; x += NT4) sDn[x] = a.dn1 ? a.dn1[bh * DK + x] : 0.0f;
   reinterpret_cast<uint2*>(sGD)[tid] = make_uint2(0u, 0u);
 
+  // The chunk's q, k, v (own columns) and C~_s (the state pass's bf16 tile)
+  // are loaded into registers one chunk ahead: the loads of chunk c - 1 are
+  // in flight while chunk c is computed, and land in LDS at the next top.
+  constexpr int NQK = LC * DK / 8 / NT4;    // 16-byte pieces of q (and of k) per thread
+  constexpr int NVV = LC * TVC / 8 / NT4;
+  constexpr int NCC = DK * TVC / 8 / NT4;
+  // native vectors: HIP's uint4 struct would be copied through private memory
+  u32x4 pq[NQK], pk[NQK], pv[NVV], pc[NCC];
+  {
+    const int64_t t0 = bh * T + static_cast<int64_t>(nc - 1) * LC;
+    const bf16_t* q = static_cast<const bf16_t*>(a.q) + t0 * DK;
+    const bf16_t* k = static_cast<const bf16_t*>(a.k) + t0 * DK;
+#pragma unroll
+    for (int p = 0; p < NQK; ++p) {
+      const int e = tid + p * NT4;
+      const int r = e / (DK / 8), col = (e % (DK / 8)) * 8;
+      pq[p] = *reinterpret_cast<const u32x4*>(q + r * DK + col);
+      pk[p] = *reinterpret_cast<const u32x4*>(k + r * DK + col);
+    }
+    const bf16_t* v = static_cast<const bf16_t*>(a.v) + t0 * dv + c0;
+#pragma unroll
+    for (int p = 0; p < NVV; ++p) {
+      const int e = tid + p * NT4;
+      pv[p] = *reinterpret_cast<const u32x4*>(v + static_cast<int64_t>(e >> 3) * dv + (e & 7) * 8);
+    }
+    const u32x4* Cs = reinterpret_cast<const u32x4*>(a.ws_Cb + ((bh * ncb + cb) * nc + (nc - 1)) * (DK * TVC));
+#pragma unroll
+    for (int p = 0; p < NCC; ++p) pc[p] = Cs[tid + p * NT4];
+  }
+
   for (int c = nc - 1; c >= 0; --c) {
     const int64_t tok0 = bh * T + static_cast<int64_t>(c) * LC;
     const float ms = a.ws_m[bh * nb + c];
     __syncthreads();
-    // ---- loads: gates, Q, K, V (own columns), C~_s (own columns, to bf16), n~_s, beta
+    // ---- this chunk's operands into LDS; the next chunk's loads go out
     if (wave == 0) gate_scan64(a, tok0, ms, G);
+#pragma unroll
+    for (int p = 0; p < NQK; ++p) {
+      const int e = tid + p * NT4;
+      const int r = e / (DK / 8), col = (e % (DK / 8)) * 8;
+      *reinterpret_cast<u32x4*>(sQ + (col >> 6) * TB + swz(r, col & 63)) = pq[p];
+      *reinterpret_cast<u32x4*>(sK + (col >> 6) * TB + swz(r, col & 63)) = pk[p];
+    }
+#pragma unroll
+    for (int p = 0; p < NVV; ++p) {
+      const int e = tid + p * NT4;
+      *reinterpret_cast<u32x4*>(sV + swz(e >> 3, (e & 7) * 8)) = pv[p];
+    }
+#pragma unroll
+    for (int p = 0; p < NCC; ++p) *reinterpret_cast<u32x4*>(sCX + 16 * (tid + p * NT4)) = pc[p];
+    // the next chunk's loads (chunk 0 fetches itself again: in bounds, unused)
     {
-      const bf16_t* q = static_cast<const bf16_t*>(a.q) + tok0 * DK;
-      const bf16_t* k = static_cast<const bf16_t*>(a.k) + tok0 * DK;
+      const int64_t t0 = bh * T + static_cast<int64_t>(c > 0 ? c - 1 : 0) * LC;
+      const bf16_t* q = static_cast<const bf16_t*>(a.q) + t0 * DK;
+      const bf16_t* k = static_cast<const bf16_t*>(a.k) + t0 * DK;
 #pragma unroll
-      for (int p = 0; p < LC * DK / 8 / NT4; ++p) {
+      for (int p = 0; p < NQK; ++p) {
         const int e = tid + p * NT4;
-        const int r = e / (DK / 8), cc = (e % (DK / 8)) * 8;
-        const uint4 vq = *reinterpret_cast<const uint4*>(q + r * DK + cc);
-        const uint4 vk = *reinterpret_cast<const uint4*>(k + r * DK + cc);
-        *reinterpret_cast<uint4*>(sQ + (cc >> 6) * TB + swz(r, cc & 63)) = vq;
-        *reinterpret_cast<uint4*>(sK + (cc >> 6) * TB + swz(r, cc & 63)) = vk;
+        const int r = e / (DK / 8), col = (e % (DK / 8)) * 8;
+        pq[p] = *reinterpret_cast<const u32x4*>(q + r * DK + col);
+        pk[p] = *reinterpret_cast<const u32x4*>(k + r * DK + col);
       }
-      const bf16_t* v = static_cast<const bf16_t*>(a.v) + tok0 * dv + c0;
+      const bf16_t* v = static_cast<const bf16_t*>(a.v) + t0 * dv + c0;
 #pragma unroll
-      for (int p = 0; p < LC * TVC / 8 / NT4; ++p) {
+      for (int p = 0; p < NVV; ++p) {
         const int e = tid + p * NT4;
-        const int r = e >> 3, cc = (e & 7) * 8;
-        *reinterpret_cast<uint4*>(sV + swz(r, cc)) = *reinterpret_cast<const uint4*>(v + static_cast<int64_t>(r) * dv + cc);
+        pv[p] = *reinterpret_cast<const u32x4*>(v + static_cast<int64_t>(e >> 3) * dv + (e & 7) * 8);
       }
-      // C~_s: the state pass stored it as this workgroup's swizzled bf16 tile
-      const uint4* Cs = reinterpret_cast<const uint4*>(a.ws_Cb + ((bh * ncb + cb) * nc + c) * (DK * TVC));
+      const u32x4* Cs = reinterpret_cast<const u32x4*>(a.ws_Cb + ((bh * ncb + cb) * nc + (c > 0 ? c - 1 : 0)) * (DK * TVC));
 #pragma unroll
-      for (int p = 0; p < DK * TVC / 8 / NT4; ++p)
-        *reinterpret_cast<uint4*>(sCX + 16 * (tid + p * NT4)) = Cs[tid + p * NT4];
+      for (int p = 0; p < NCC; ++p) pc[p] = Cs[tid + p * NT4];
     }
     for (int x = tid; x < DK; x += NT4) sN[x] = a.ws_n[(bh * nb + c) * DK + x];
     if (tid < LC) sBeta[tid] = a.ws_beta[tok0 + tid];
