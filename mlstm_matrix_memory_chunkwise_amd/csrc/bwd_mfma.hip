@@ -611,6 +611,7 @@ __global__ __launch_bounds__(NT4, 1) void bwd_states_mfma_kernel(BwdArgs a) {
   __shared__ __align__(1024) char sK[2][NQT * TB];
   __shared__ __align__(1024) char sWH[TB];
   __shared__ __align__(1024) char sWL[TB];
+  __shared__ __align__(1024) char sWD[16 * 128];   // rows 0, 1: w as bf16 hi / lo; rest 0
   __shared__ Gate64 G;
 
   const int tid = threadIdx.x;
@@ -637,7 +638,14 @@ __global__ __launch_bounds__(NT4, 1) void bwd_states_mfma_kernel(BwdArgs a) {
       Ct[xt] = f32x4{v4.x, v4.y, v4.z, v4.w};
     }
   }
-  float n = (a.C0 && tid < DK) ? a.n0[bh * DK + tid] : 0.0f;
+  // n~ lives in column block 0 only, in the lanes of group 0 of each wave:
+  // lane l16 holds x = 16 (wave XPW + p) + l16
+  constexpr int XPW = NXT / 4;
+  float nx[XPW];
+#pragma unroll
+  for (int p = 0; p < XPW; ++p)
+    nx[p] = (a.C0 && g == 0) ? a.n0[bh * DK + (wave * XPW + p) * 16 + l16] : 0.0f;
+  reinterpret_cast<uint2*>(sWD)[tid] = make_uint2(0u, 0u);
   float m = a.C0 ? a.m0[bh] : 0.0f;
 
   // v rows tid / 4, columns c0 + 16 (tid % 4) .. + 15 of a chunk
@@ -668,7 +676,10 @@ __global__ __launch_bounds__(NT4, 1) void bwd_states_mfma_kernel(BwdArgs a) {
             make_float4(Ct[xt][0], Ct[xt][1], Ct[xt][2], Ct[xt][3]);
     }
     if (lead) {
-      if (tid < DK) a.ws_n[(bh * nb + c) * DK + tid] = n;
+      if (g == 0) {
+#pragma unroll
+        for (int p = 0; p < XPW; ++p) a.ws_n[(bh * nb + c) * DK + (wave * XPW + p) * 16 + l16] = nx[p];
+      }
       if (tid == 0) a.ws_m[bh * nb + c] = m;
     }
     if (c == nc) break;
@@ -703,15 +714,11 @@ __global__ __launch_bounds__(NT4, 1) void bwd_states_mfma_kernel(BwdArgs a) {
       }
     }
     const float gL = G.g[LC - 1];
-    if (lead && tid < DK) {
-      const char* kt = wide(kc, tid);
-      float s0 = 0.0f, s1 = 0.0f;
-#pragma unroll 8
-      for (int j = 0; j < LC; j += 2) {
-        s0 += G.w[j] * bf2f(*reinterpret_cast<const bf16_t*>(kt + swz(j, tid & 63)));
-        s1 += G.w[j + 1] * bf2f(*reinterpret_cast<const bf16_t*>(kt + swz(j + 1, tid & 63)));
-      }
-      n = gL * n + (s0 + s1);
+    if (lead && tid < LC) {   // the A operand of n~ += sum_j w_j k_j (hi and lo rows)
+      const float wj = G.w[tid];
+      const bf16_t hi = f2bf(wj);
+      *reinterpret_cast<bf16_t*>(sWD + swz(0, tid)) = hi;
+      *reinterpret_cast<bf16_t*>(sWD + swz(1, tid)) = f2bf(wj - bf2f(hi));
     }
     __syncthreads();
 #pragma unroll
@@ -726,6 +733,22 @@ __global__ __launch_bounds__(NT4, 1) void bwd_states_mfma_kernel(BwdArgs a) {
         Ct[xt] = mfma16x16x32(Ah, Bk, Ct[xt]);
         Ct[xt] = mfma16x16x32(Al, Bk, Ct[xt]);
       }
+    }
+    if (lead) {   // n~ <- g_L n~ + K^T w for this wave's x tiles (D rows 0 + 1)
+      f32x4 nacc[XPW];
+#pragma unroll
+      for (int p = 0; p < XPW; ++p) nacc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 Aw = rowfrag(sWD, l16, 32 * ks + 8 * g);
+#pragma unroll
+        for (int p = 0; p < XPW; ++p) {
+          const int xt = wave * XPW + p;
+          nacc[p] = mfma16x16x32(Aw, colfrag(wide(kc, xt * 16), 32 * ks, (xt * 16) & 63, g, kr, kq), nacc[p]);
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < XPW; ++p) nx[p] = gL * nx[p] + (nacc[p][0] + nacc[p][1]);
     }
     m = G.m[LC - 1];
   }
