@@ -168,8 +168,8 @@ mlstm_status_t mlstm_step(const mlstm_problem_t* p, const void* q,
  *   or 16; at chunk 64 the states before each chunk are bf16, about
  *   B*H*(T/64)*d_qk*d_v*2 + B*H*d_qk*d_v*4 + 2*(d_v/64)*B*H*T*d_qk*4
  *   bytes), 16-byte aligned, not overlapping any argument.
- *   q, k and v must be 16-byte aligned; at chunk 64 also o_pre, C0, h, dh,
- *   dC1, dv, d_o and dC0; every other pointer 4-byte aligned.
+ *   q, k, v, h, dh, dq and dk must be 16-byte aligned; at chunk 64 also
+ *   o_pre, C0, dC1, dv, d_o and dC0; every other pointer 4-byte aligned.
  * Supported: chunk 16 or 32 with d_qk <= 256 (float32 arithmetic
  * throughout), or chunk 64 with bf16 q/k/v, d_v a multiple of 64 and d_qk
  * 64, 128 or 256 (matrix products on bf16 matrix cores with float32

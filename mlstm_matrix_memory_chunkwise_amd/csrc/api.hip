@@ -268,11 +268,11 @@ mlstm_status_t mlstm_bwd_chunkwise(const mlstm_problem_t* p, int64_t chunk, cons
       {"v", v, BH * T * dvv * sq, 16},      {"i_pre", i_pre, BH * T * 4, 4},
       {"f_pre", f_pre, BH * T * 4, 4},      {"o_pre", o_pre, BH * T * dvv * dsize(p->o_dtype), va},
       {"C0", C0, BH * dqk * dvv * 4, va},   {"n0", n0, BH * dqk * 4, 4},
-      {"m0", m0, BH * 4, 4},                {"h", h, BH * T * dvv * sq, va},
-      {"dh", dh, BH * T * dvv * sq, va},    {"dC1", dC1, BH * dqk * dvv * 4, va},
+      {"m0", m0, BH * 4, 4},                {"h", h, BH * T * dvv * sq, 16},
+      {"dh", dh, BH * T * dvv * sq, 16},    {"dC1", dC1, BH * dqk * dvv * 4, va},
       {"dn1", dn1, BH * dqk * 4, 4},
       // outputs from here (index 13 on)
-      {"dq", dq, BH * T * dqk * 4, 4},      {"dk", dk, BH * T * dqk * 4, 4},
+      {"dq", dq, BH * T * dqk * 4, 16},     {"dk", dk, BH * T * dqk * 4, 16},
       {"dv", dv, BH * T * dvv * 4, va},     {"di", di, BH * T * 4, 4},
       {"df", df, BH * T * 4, 4},            {"d_o", d_o, BH * T * dvv * 4, va},
       {"dC0", dC0, BH * dqk * dvv * 4, va}, {"dn0", dn0, BH * dqk * 4, 4},

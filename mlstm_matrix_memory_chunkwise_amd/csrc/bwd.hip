@@ -122,16 +122,40 @@ __device__ __forceinline__ float block_sum(float x, float* red) {
   return s;
 }
 
-// ---- pass 1: beta_t = dh_t . h_t (one wave per token)
+// ---- pass 1: beta_t = dh_t . h_t: half a wave per token, 8 elements (16 or
+// 32 bytes) per lane per step; d_v is a multiple of 16
+template <typename T>
+__device__ __forceinline__ void load8f(const void* p, int64_t i, float* x) {
+  if (sizeof(T) == 2) {
+    const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(p) + i);
+    x[0] = bf_lo(u.x); x[1] = bf_hi(u.x); x[2] = bf_lo(u.y); x[3] = bf_hi(u.y);
+    x[4] = bf_lo(u.z); x[5] = bf_hi(u.z); x[6] = bf_lo(u.w); x[7] = bf_hi(u.w);
+  } else {
+    const float4 f0 = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+    const float4 f1 = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i + 4);
+    x[0] = f0.x; x[1] = f0.y; x[2] = f0.z; x[3] = f0.w;
+    x[4] = f1.x; x[5] = f1.y; x[6] = f1.z; x[7] = f1.w;
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(NTB) void bwd_beta_kernel(BwdArgs a) {
-  const int64_t tok = static_cast<int64_t>(blockIdx.x) * (NTB / 64) + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (tok >= a.B * a.H * a.T) return;
+  const int lane = threadIdx.x & 63, hl = lane & 31;
+  const int64_t tok = (static_cast<int64_t>(blockIdx.x) * (NTB / 64) + (threadIdx.x >> 6)) * 2 + (lane >> 5);
+  const bool live = tok < a.B * a.H * a.T;
   float s = 0.0f;
-  for (int64_t b = lane; b < a.dv; b += 64) s += ld<T>(a.dh, tok * a.dv + b) * ld<T>(a.h, tok * a.dv + b);
-  s = wave_sum(s);
-  if (lane == 0) a.ws_beta[tok] = s;
+  if (live) {
+    for (int64_t b = 8 * hl; b < a.dv; b += 256) {
+      float x[8], y[8];
+      load8f<T>(a.dh, tok * a.dv + b, x);
+      load8f<T>(a.h, tok * a.dv + b, y);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += x[e] * y[e];
+    }
+  }
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);   // within the half-wave
+  if (live && hl == 0) a.ws_beta[tok] = s;
 }
 
 // Gate scan of one chunk of L <= 64 tokens by wave 0 into LDS: per token j,
@@ -391,7 +415,19 @@ __global__ __launch_bounds__(NTB) void bwd_rev_kernel(BwdArgs a) {
 }
 
 // ---- pass 4: per token, the partial sums of dq and dk, di~ and q.dq - k.dk
-// (one wave per token)
+// (one wave per token, 4 consecutive d_qk entries per lane per step: 16-byte
+// partial loads; d_qk is a multiple of 16)
+template <typename T>
+__device__ __forceinline__ void load4f(const void* p, int64_t i, float* x) {
+  if (sizeof(T) == 2) {
+    const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(p) + i);
+    x[0] = bf_lo(u.x); x[1] = bf_hi(u.x); x[2] = bf_lo(u.y); x[3] = bf_hi(u.y);
+  } else {
+    const float4 f = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+    x[0] = f.x; x[1] = f.y; x[2] = f.z; x[3] = f.w;
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(NTB) void bwd_tok_kernel(BwdArgs a, int ncb) {
   const int64_t ntok = a.B * a.H * a.T;
@@ -400,16 +436,22 @@ __global__ __launch_bounds__(NTB) void bwd_tok_kernel(BwdArgs a, int ncb) {
   if (tok >= ntok) return;
   const int64_t dqk = a.dqk;
   float kdk = 0.0f, qdq = 0.0f;
-  for (int64_t x = lane; x < dqk; x += 64) {
-    float sq = 0.0f, sk = 0.0f;
+  for (int64_t x = 4 * lane; x < dqk; x += 256) {
+    float4 sq = make_float4(0.f, 0.f, 0.f, 0.f), sk = sq;
     for (int p = 0; p < ncb; ++p) {
-      sq += a.ws_dq[(static_cast<int64_t>(p) * ntok + tok) * dqk + x];
-      sk += a.ws_dk[(static_cast<int64_t>(p) * ntok + tok) * dqk + x];
+      const int64_t o = (static_cast<int64_t>(p) * ntok + tok) * dqk + x;
+      const float4 vq = *reinterpret_cast<const float4*>(a.ws_dq + o);
+      const float4 vk = *reinterpret_cast<const float4*>(a.ws_dk + o);
+      sq.x += vq.x; sq.y += vq.y; sq.z += vq.z; sq.w += vq.w;
+      sk.x += vk.x; sk.y += vk.y; sk.z += vk.z; sk.w += vk.w;
     }
-    a.d_q[tok * dqk + x] = sq;
-    a.d_k[tok * dqk + x] = sk;
-    qdq += ld<T>(a.q, tok * dqk + x) * sq;
-    kdk += ld<T>(a.k, tok * dqk + x) * sk;
+    *reinterpret_cast<float4*>(a.d_q + tok * dqk + x) = sq;
+    *reinterpret_cast<float4*>(a.d_k + tok * dqk + x) = sk;
+    float qv[4], kv[4];
+    load4f<T>(a.q, tok * dqk + x, qv);
+    load4f<T>(a.k, tok * dqk + x, kv);
+    qdq += (qv[0] * sq.x + qv[1] * sq.y) + (qv[2] * sq.z + qv[3] * sq.w);
+    kdk += (kv[0] * sk.x + kv[1] * sk.y) + (kv[2] * sk.z + kv[3] * sk.w);
   }
   qdq = wave_sum(qdq);
   kdk = wave_sum(kdk);
@@ -420,10 +462,9 @@ __global__ __launch_bounds__(NTB) void bwd_tok_kernel(BwdArgs a, int ncb) {
 }
 
 // ---- pass 5: per head, d(log f_t) = sum_{t'>=t} s_t' + <dC1, C~_T> + <dn1, n~_T>
-// (a reverse prefix sum over blocks of T / NTB tokens), df~ and dm0.
+// (a reverse prefix sum, one block scan per tile of NTB tokens), df~ and dm0.
 __global__ __launch_bounds__(NTB) void bwd_head_kernel(BwdArgs a, int ncb, int nc) {
   __shared__ float sRed[NTB / 64];
-  __shared__ float sBlk[NTB];
   const int tid = threadIdx.x;
   const int64_t bh = blockIdx.x;
   const int64_t T = a.T, dqk = a.dqk, dv = a.dv;
@@ -432,23 +473,54 @@ __global__ __launch_bounds__(NTB) void bwd_head_kernel(BwdArgs a, int ncb, int n
   float kend = 0.0f;
   if (a.dC1) {
     const float* CT = a.ws_CT ? a.ws_CT + bh * dqk * dv : a.ws_C + (bh * nb + nc) * dqk * dv;
-    for (int64_t e = tid; e < dqk * dv; e += NTB) kend += a.dC1[bh * dqk * dv + e] * CT[e];
+    const float* G1 = a.dC1 + bh * dqk * dv;
+    float k4[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // independent sums: loads overlap
+    int64_t e = tid;
+    for (; e + 3 * NTB < dqk * dv; e += 4 * NTB) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) k4[u] += G1[e + u * NTB] * CT[e + u * NTB];
+    }
+    for (; e < dqk * dv; e += NTB) k4[0] += G1[e] * CT[e];
+    kend += (k4[0] + k4[1]) + (k4[2] + k4[3]);
     for (int64_t e = tid; e < dqk; e += NTB) kend += a.dn1[bh * dqk + e] * a.ws_n[(bh * nb + nc) * dqk + e];
   }
   kend = block_sum(kend, sRed);
-  // reverse prefix sum: thread t owns tokens [t * per, (t + 1) * per)
-  const int64_t per = (T + NTB - 1) / NTB;
-  const int64_t t0 = tid * per, t1 = (t0 + per < T) ? t0 + per : T;
-  float own = 0.0f;
-  for (int64_t t = t0; t < t1; ++t) own += a.ws_s[bh * T + t];
-  sBlk[tid] = own;
-  __syncthreads();
-  float after = kend;   // sum over the blocks after this thread's
-  for (int u = tid + 1; u < NTB; ++u) after += sBlk[u];
-  for (int64_t t = t1 - 1; t >= t0; --t) {
-    after += a.ws_s[bh * T + t];
-    const float fpre = a.f_pre[bh * T + t];
-    a.d_f[bh * T + t] = a.fgate_exp ? after : after * (1.0f - mk::sigmoid_fast(fpre));
+  // reverse prefix sum over tiles of NTB tokens, last tile first: thread
+  // tid takes token tile * NTB + NTB - 1 - tid, so an inclusive prefix sum
+  // over the threads is the sum over the tokens after it in the tile
+  // (coalesced loads, one block scan per tile)
+  const int lane = tid & 63, wave = tid >> 6;
+  float carry = kend;   // sum over the tiles after this one, plus the constant term
+  __syncthreads();      // every read of sRed by block_sum is done
+  const int64_t ntile = (T + NTB - 1) / NTB;
+  float sv_n, fp_n;   // the next tile's inputs, loaded one tile ahead
+  {
+    const int64_t t = (ntile - 1) * NTB + (NTB - 1 - tid);
+    sv_n = t < T ? a.ws_s[bh * T + t] : 0.0f;
+    fp_n = t < T ? a.f_pre[bh * T + t] : 0.0f;
+  }
+  for (int64_t tile = ntile - 1; tile >= 0; --tile) {
+    const int64_t t = tile * NTB + (NTB - 1 - tid);
+    const float sv = sv_n, fpre = fp_n;
+    if (tile > 0) {
+      sv_n = a.ws_s[bh * T + t - NTB];
+      fp_n = a.f_pre[bh * T + t - NTB];
+    }
+    const float incl = mk::scan_add(sv);
+    if (lane == 63) sRed[wave] = incl;
+    __syncthreads();
+    float before = 0.0f, total = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NTB / 64; ++w) {
+      before += w < wave ? sRed[w] : 0.0f;
+      total += sRed[w];
+    }
+    __syncthreads();   // sRed is rewritten by the next tile
+    if (t < T) {
+      const float after = carry + before + incl;
+      a.d_f[bh * T + t] = a.fgate_exp ? after : after * (1.0f - mk::sigmoid_fast(fpre));
+    }
+    carry += total;
   }
   if (a.dm0 && tid == 0) {
     float s = 0.0f;
@@ -464,7 +536,7 @@ hipError_t launch_typed(const BwdArgs& a, hipStream_t st) {
   const int nc = static_cast<int>(a.T / L);
   const unsigned tok_blocks = static_cast<unsigned>((ntok + NTB / 64 - 1) / (NTB / 64));
   const unsigned wgs = static_cast<unsigned>(a.B * a.H * ncb);
-  bwd_beta_kernel<T><<<tok_blocks, NTB, 0, st>>>(a);
+  bwd_beta_kernel<T><<<(tok_blocks + 1) / 2, NTB, 0, st>>>(a);
   bwd_states_kernel<T, TV, L><<<wgs, NTB, 0, st>>>(a);
   bwd_rev_kernel<T, TO, TV, L><<<wgs, NTB, 0, st>>>(a);
   bwd_tok_kernel<T><<<tok_blocks, NTB, 0, st>>>(a, ncb);
@@ -480,7 +552,7 @@ hipError_t launch_mfma(const BwdArgs& a, hipStream_t st) {
   const int ncb = static_cast<int>(a.dv / 64);
   const int nc = static_cast<int>(a.T / 64);
   const unsigned tok_blocks = static_cast<unsigned>((ntok + NTB / 64 - 1) / (NTB / 64));
-  bwd_beta_kernel<T><<<tok_blocks, NTB, 0, st>>>(a);
+  bwd_beta_kernel<T><<<(tok_blocks + 1) / 2, NTB, 0, st>>>(a);
   hipError_t e = launch_bwd_states_mfma(a, st);
   if (e != hipSuccess) return e;
   e = launch_bwd_rev_mfma(a, st);

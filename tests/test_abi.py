@@ -235,14 +235,22 @@ def test_bwd_unsupported(lib):
     assert bwd_call(lib, P(dqk=272, dv=48))[0] == M.MLSTM_ERR_UNSUPPORTED
 
 
-def test_bwd_chunk64_alignment(lib):
-    """Chunk 64 moves the [.., d_v] arrays in 16-byte pieces: 4-byte
-    aligned dh is rejected there (and accepted by chunk 32)."""
+def test_bwd_alignment(lib):
+    """h and dh are read in 16-byte pieces at every chunk; chunk 64 moves the
+    other [.., d_v] arrays that way too (4-byte aligned dv is accepted by
+    chunk 32 only)."""
     p = P(dqk=64, dv=64, qkv=1)
-    odd = ctypes.c_void_p(FAKE + 10 * (1 << 30) + 4)
-    r, det = bwd_call(lib, p, chunk=64, dh=odd)
-    assert r == M.MLSTM_ERR_INVALID_ARG and "dh" in det and "aligned" in det
-    r, det = bwd_call(lib, p, chunk=32, dh=odd, ws_bytes=0)
+    odd_dh = ctypes.c_void_p(FAKE + 10 * (1 << 30) + 4)
+    for chunk in (32, 64):
+        r, det = bwd_call(lib, p, chunk=chunk, dh=odd_dh)
+        assert r == M.MLSTM_ERR_INVALID_ARG and "dh" in det and "aligned" in det
+    odd_dq = ctypes.c_void_p(FAKE + 13 * (1 << 30) + 4)
+    r, det = bwd_call(lib, p, chunk=32, dq=odd_dq)
+    assert r == M.MLSTM_ERR_INVALID_ARG and "dq" in det and "aligned" in det
+    odd_dv = ctypes.c_void_p(FAKE + 15 * (1 << 30) + 4)
+    r, det = bwd_call(lib, p, chunk=64, dv=odd_dv)
+    assert r == M.MLSTM_ERR_INVALID_ARG and "dv" in det and "aligned" in det
+    r, det = bwd_call(lib, p, chunk=32, dv=odd_dv, ws_bytes=0)
     assert r == M.MLSTM_ERR_INVALID_ARG and "workspace" in det
 
 
