@@ -100,6 +100,7 @@ __global__ __launch_bounds__(NT4, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
   __shared__ __align__(1024) char sDST[TB];   // (D (.) S)^T: [j][i]
   __shared__ __align__(1024) char sCX[DK * 128];   // [DK][64]: C~_s, then dC
   __shared__ __align__(1024) char sGD[16 * 128];   // rows 0, 1: g (.) dnq as bf16 hi / lo; rest 0
+  __shared__ __align__(16) char sTW[4 * 2048];     // per wave: [32 x][16 b] bf16 hi, then lo
   __shared__ float sN[DK], sDn[DK];
   __shared__ float sRs[LC];
   __shared__ float sDnq[LC], sBeta[LC];
@@ -442,44 +443,50 @@ __global__ __launch_bounds__(NT4, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
       *reinterpret_cast<uint2*>(sCX + swz(xt * 16 + l16, wave * 16 + 4 * g)) =
           make_uint2(pk2(dCt[xt][0], dCt[xt][1]), pk2(dCt[xt][2], dCt[xt][3]));
     __syncthreads();
-    // ---- dk^T = Q^T W + dC (w V)^T (+ w dn)
+    // ---- dk^T = Q^T W + dC (w V)^T (+ w dn), in two halves of the key tiles
+    // (half the accumulators live at a time: the register budget is full)
     {
-      f32x4 acc[XPW][4];
+      float* out = a.ws_dk + ((static_cast<int64_t>(cb) * BH + bh) * T + static_cast<int64_t>(c) * LC) * DK;
 #pragma unroll
-      for (int p = 0; p < XPW; ++p)
+      for (int jh = 0; jh < 2; ++jh) {
+        f32x4 acc[XPW][2];
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) acc[p][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int p = 0; p < XPW; ++p) {
+          acc[p][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+          acc[p][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        bf16x8 Bw[4], Bv[4];
+        for (int ks = 0; ks < 2; ++ks) {
+          bf16x8 Bw[2], Bv[2];
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
-          Bw[jt] = colfrag(sW, 32 * ks, jt * 16, g, kr, kq);
-          Bv[jt] = rowfrag(sWV, jt * 16 + l16, 32 * ks + 8 * g);
+          for (int u = 0; u < 2; ++u) {
+            const int jt = 2 * jh + u;
+            Bw[u] = colfrag(sW, 32 * ks, jt * 16, g, kr, kq);
+            Bv[u] = rowfrag(sWV, jt * 16 + l16, 32 * ks + 8 * g);
+          }
+#pragma unroll
+          for (int p = 0; p < XPW; ++p) {
+            const int xt = wave * XPW + p;
+            const bf16x8 Aq = colfrag(wide(sQ, xt * 16), 32 * ks, (xt * 16) & 63, g, kr, kq);
+            const bf16x8 Ac = rowfrag(sCX, xt * 16 + l16, 32 * ks + 8 * g);
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              acc[p][u] = mfma16x16x32(Aq, Bw[u], acc[p][u]);
+              acc[p][u] = mfma16x16x32(Ac, Bv[u], acc[p][u]);
+            }
+          }
         }
 #pragma unroll
         for (int p = 0; p < XPW; ++p) {
-          const int xt = wave * XPW + p;
-          const bf16x8 Aq = colfrag(wide(sQ, xt * 16), 32 * ks, (xt * 16) & 63, g, kr, kq);
-          const bf16x8 Ac = rowfrag(sCX, xt * 16 + l16, 32 * ks + 8 * g);
+          const int x0 = (wave * XPW + p) * 16 + 4 * g;
 #pragma unroll
-          for (int jt = 0; jt < 4; ++jt) {
-            acc[p][jt] = mfma16x16x32(Aq, Bw[jt], acc[p][jt]);
-            acc[p][jt] = mfma16x16x32(Ac, Bv[jt], acc[p][jt]);
+          for (int u = 0; u < 2; ++u) {
+            const int j = (2 * jh + u) * 16 + l16;
+            const float f = lead ? G.w[j] : 0.0f;
+            *reinterpret_cast<float4*>(out + j * DK + x0) =
+                make_float4(acc[p][u][0] + f * sDn[x0], acc[p][u][1] + f * sDn[x0 + 1],
+                            acc[p][u][2] + f * sDn[x0 + 2], acc[p][u][3] + f * sDn[x0 + 3]);
           }
-        }
-      }
-      float* out = a.ws_dk + ((static_cast<int64_t>(cb) * BH + bh) * T + static_cast<int64_t>(c) * LC) * DK;
-#pragma unroll
-      for (int p = 0; p < XPW; ++p) {
-        const int x0 = (wave * XPW + p) * 16 + 4 * g;
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
-          const int j = jt * 16 + l16;
-          const float f = lead ? G.w[j] : 0.0f;
-          *reinterpret_cast<float4*>(out + j * DK + x0) =
-              make_float4(acc[p][jt][0] + f * sDn[x0], acc[p][jt][1] + f * sDn[x0 + 1],
-                          acc[p][jt][2] + f * sDn[x0 + 2], acc[p][jt][3] + f * sDn[x0 + 3]);
         }
       }
     }
@@ -498,13 +505,40 @@ __global__ __launch_bounds__(NT4, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
         for (int jt = 0; jt < 4; ++jt)
           accA[jt] = mfma16x16x32(Ar, rowfrag(sDST, jt * 16 + l16, 32 * ks + 8 * g), accA[jt]);
       }
+      // dC^T K^T: this wave's 16 value columns of the carried dC (float32, in
+      // its own registers) enter as a bf16 (hi, lo) pair, transposed 32 rows
+      // at a time through a wave-private LDS tile.  A single bf16 copy of dC
+      // costs up to ~2% of dv where the two terms of dv cancel.
+      char* tw = sTW + wave * 2048;
 #pragma unroll
       for (int ks = 0; ks < DK / 32; ++ks) {
         const int x0 = 32 * ks;
-        const bf16x8 Ac = colfrag(sCX, x0, wave * 16, g, kr, kq);
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt)
-          accB[jt] = mfma16x16x32(Ac, rowfrag(wide(sK, x0), jt * 16 + l16, (x0 & 63) + 8 * g), accB[jt]);
+        for (int t = 0; t < 2; ++t) {   // lane: dC^T[b = 4 g + e][x = x0 + 16 t + l16]
+          const f32x4 v = dCt[2 * ks + t];
+          const uint32_t h0 = pk2(v[0], v[1]), h1 = pk2(v[2], v[3]);
+          const int off = (16 * t + l16) * 32 + g * 8;   // row x (32 bytes), columns b = 4 g ..
+          *reinterpret_cast<uint2*>(tw + off) = make_uint2(h0, h1);
+          *reinterpret_cast<uint2*>(tw + 1024 + off) =
+              make_uint2(pk2(v[0] - bf_lo(h0), v[1] - bf_hi(h0)), pk2(v[2] - bf_lo(h1), v[3] - bf_hi(h1)));
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // A[b = l16][x = 8 g + e]: transposed reads of rows 8 g + kr (+4), columns 4 kq
+        const int ro = (8 * g + kr) * 32 + 8 * kq;
+        const bf16x8 Ah = join(lds_tr(tw, ro), lds_tr(tw, ro + 4 * 32));
+        const bf16x8 Al = join(lds_tr(tw + 1024, ro), lds_tr(tw + 1024, ro + 4 * 32));
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+          const bf16x8 Bk = rowfrag(wide(sK, x0), jt * 16 + l16, (x0 & 63) + 8 * g);
+          accB[jt] = mfma16x16x32(Ah, Bk, accB[jt]);
+          accB[jt] = mfma16x16x32(Al, Bk, accB[jt]);
+        }
+        // the next rows overwrite the tile only after these reads
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       }
 #pragma unroll
       for (int jt = 0; jt < 4; ++jt) {

@@ -96,6 +96,10 @@ CASES = [
     ("bf16 d128/192 chunk 64 exp gate bf16 o", torch.bfloat16, 2, 1, 192, 128, 192, 64, "exp", True, torch.bfloat16, False, True),
     ("bf16 d256 chunk 64 no o", torch.bfloat16, 1, 2, 256, 256, 256, 64, "sigmoid", False, None, True, False),
     ("bf16 d256/128 chunk 64 single chunk", torch.bfloat16, 1, 3, 64, 256, 128, 64, "sigmoid", True, torch.float32, True, True),
+    ("bf16 d256/512 chunk 64 eight column blocks", torch.bfloat16, 1, 1, 128, 256, 512, 64, "sigmoid", True, torch.float32, True, True),
+    # one column block: dv's two terms partly cancel here, which exposed the
+    # bf16 rounding of the carried dC in the dv product (now a hi/lo pair)
+    ("bf16 d128/64 chunk 64 one column block", torch.bfloat16, 2, 1, 128, 128, 64, 64, "sigmoid", True, torch.float32, True, True),
 ]
 
 
