@@ -1,28 +1,33 @@
-// Reverse pass of the chunkwise backward on bf16 MFMA (gfx950): chunk 64,
-// 64 value columns per workgroup, d_qk in {64, 128, 256}, bf16 q/k/v/h/dh.
+// State and reverse passes of the chunkwise backward on bf16 MFMA (gfx950):
+// chunk 64, 64 value columns per workgroup, d_qk in {64, 128, 256}, bf16
+// q/k/v/h/dh.
 //
-// The same gradient as the float32 reverse pass in bwd.hip (the derivative of
-// the forward pass of the xLSTM post, llms.blog, section 3 "Associative
-// Matrix Cell State" and "The Parallel Dual Form", with the running maximum of
+// The same gradient as the float32 passes in bwd.hip (the derivative of the
+// forward pass of the xLSTM post, llms.blog, section 3 "Associative Matrix
+// Cell State" and "The Parallel Dual Form", with the running maximum of
 // section 2 "The Normalizer State and Numerical Stabilization"), with every
 // matrix product on 16x16x32 MFMAs.  Per chunk of 64 tokens, with the stored
-// state (C~_s, n~_s, m_s) and the carried memory gradient dC:
+// state (C~_s, n~_s, m_s) and the carried memory gradient dC, the reverse
+// pass forms
 //
-//   S^T = K Q^T,  DS = D (.) S            (masked, bf16 in LDS; row sums fp32)
+//   S = Q K^T,  DS = D (.) S              (masked; stored transposed, bf16;
+//                                          row sums in float32)
 //   r = sigmoid(o~) dh / den,  g r,  w V (bf16 in LDS)
 //   W = D (.) (R V^T + dnq)               (bf16 in LDS)
 //   dq^T = K^T W^T + C~_s (g R)^T  (+ g dnq n~_s)
 //   dk^T = Q^T W + dC (w V)^T      (+ w dn)
-//   dv^T = R^T DS + w (dC^T K^T)
-//   dC^T <- g_L dC^T + (g R)^T Q
+//   dv^T = R^T DS + w (dC^T K^T)          (dC as a bf16 hi / lo pair)
+//   dC^T <- g_L dC^T + (g R)^T Q,  dn <- g_L dn + sum_i g_i dnq_i q_i
 //
 // Operands are read from swizzled [rows][64] bf16 LDS tiles either as row
 // fragments (8 consecutive columns, ds_read_b128) or as transposed column
 // fragments (8 consecutive rows, two ds_read_b64_tr_b16), both in natural
-// index order.  The memory gradient is carried transposed (dC^T tiles, one
-// 16-column block per wave), which makes its bf16 copy for the products a run
-// of 4 consecutive columns per lane.  The products round their operands to
-// bf16 (accumulation stays float32); q, k, v are exact.
+// index order.  The memory gradient is carried transposed in float32
+// registers (dC^T tiles, one 16-column block per wave), which makes its bf16
+// copy for the products a run of 4 consecutive columns per lane.  The
+// products round their other operands to bf16 (accumulation stays float32);
+// q, k, v are exact.  Vectors that meet a matrix in float32 precision (dn's
+// g dnq, the state pass's w (.) V and w) enter as bf16 hi / lo pairs.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mfma_util.hpp"
