@@ -442,6 +442,34 @@ def main():
         del wx, Rm, hs
         torch.cuda.empty_cache()
 
+    # ------------------------------------------------------------ achievable rates
+    # What this GPU reaches on plain library work, beside the datasheet peaks
+    # the roofline fractions use: a 1 GiB device-to-device copy and a bf16
+    # GEMM (torch.matmul on contiguous 2-D operands).
+    if not args.skip_extra:
+        xa = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        ya = torch.empty_like(xa)
+        for _ in range(3):
+            ya.copy_(xa)
+        ms_c = time_events(lambda: ya.copy_(xa), 10, stream)
+        copy_gbs = 2 * xa.numel() * 4 / (ms_c / 1e3) / 1e9
+        del xa, ya
+        ga = torch.randn((8192, 8192), device=dev).to(torch.bfloat16)
+        gb = torch.randn((8192, 8192), device=dev).to(torch.bfloat16)
+        gc = torch.empty((8192, 8192), dtype=torch.bfloat16, device=dev)
+        for _ in range(5):   # library selection and first-call setup stay untimed
+            torch.matmul(ga, gb, out=gc)
+        torch.cuda.synchronize()
+        ms_g = time_events(lambda: torch.matmul(ga, gb, out=gc), 10, stream)
+        gemm_tf = 2 * 8192 ** 3 / (ms_g / 1e3) / 1e12
+        del ga, gb, gc
+        torch.cuda.empty_cache()
+        result["achievable"] = {
+            "copy_GBps": copy_gbs, "copy_frac_of_peak": copy_gbs / HBM_PEAK_GBS,
+            "bf16_gemm_TFLOPs": gemm_tf, "gemm_frac_of_peak": gemm_tf / MFMA_BF16_PEAK_TFLOPS,
+            "chunkwise_frac_of_copy": result["roofline"]["achieved"] / copy_gbs,
+        }
+
     # ------------------------------------------------------------ CPU oracle
     if not args.skip_cpu:
         import oracle
