@@ -322,10 +322,11 @@ mlstm_status_t mlstm_groupnorm_ogate(int64_t B, int64_t H, int64_t T, int64_t d_
   if (B * H * T > ((int64_t)1 << 40))
     return fail(MLSTM_ERR_UNSUPPORTED, "B*H*T=%lld too large", (long long)(B * H * T));
   const size_t n = (size_t)(B * H * T * d_v), sh = dsize(h_dtype), so = dsize(o_dtype);
+  // rows move in 16-byte pieces
   const Buf bufs[] = {
-      {"h", h, n * sh, 2 * sh},     {"o_pre", o_pre, n * so, 2 * so},
+      {"h", h, n * sh, 16},         {"o_pre", o_pre, n * so, 16},
       {"gamma", gamma, (size_t)(H * d_v) * 4, 16}, {"beta", beta, (size_t)(H * d_v) * 4, 16},
-      {"y", y, n * sh, 2 * sh},
+      {"y", y, n * sh, 16},
   };
   for (const Buf& b : bufs)
     if (b.p && !aligned(b))

@@ -285,7 +285,7 @@ def test_groupnorm_rejections(lib):
     assert gn_call(lib, eps=float("nan"))[0] == M.MLSTM_ERR_INVALID_ARG
     assert gn_call(lib, dv=6)[0] == M.MLSTM_ERR_UNSUPPORTED
     assert gn_call(lib, dv=2048)[0] == M.MLSTM_ERR_UNSUPPORTED
-    r, det = gn_call(lib, o=ctypes.c_void_p(FAKE + (2 << 30) + 4))   # float32 o needs 8 bytes
+    r, det = gn_call(lib, o=ctypes.c_void_p(FAKE + (2 << 30) + 8))   # rows move in 16-byte pieces
     assert r == M.MLSTM_ERR_INVALID_ARG and "o_pre" in det
     r, det = gn_call(lib, y=ctypes.c_void_p(FAKE + 64))              # inside h, not h
     assert r == M.MLSTM_ERR_INVALID_ARG and "overlaps" in det
