@@ -59,7 +59,7 @@ typedef enum {
                                 workspace too small */
   MLSTM_ERR_UNSUPPORTED = 2, /* valid but not implemented: d not a multiple of
                                 16 or above 512, chunk not in {16,32,64,128},
-                                T not a multiple of chunk */
+                                T not a multiple of chunk (backward only) */
   MLSTM_ERR_DEVICE = 3       /* a HIP call or kernel launch failed */
 } mlstm_status_t;
 
@@ -88,7 +88,13 @@ typedef struct {
  *   C1, n1, m1: all NULL (final state not written) or all set.
  *   State outputs must not overlap state inputs; h must not overlap any input.
  *   workspace: device scratch of at least the size given by
- *   mlstm_fwd_chunkwise_workspace_bytes (may be NULL when that size is 0).
+ *   mlstm_fwd_chunkwise_workspace_bytes (may be NULL when that size is 0);
+ *   it must not overlap any other argument.
+ * Any T >= 1 is accepted.  When T is not a multiple of `chunk`, the last
+ * T % chunk tokens form one shorter chunk: on the bf16 matrix-core path they
+ * run on the float32 vector kernel, continuing from the state the first
+ * T - T % chunk tokens leave in the workspace (B*H*(d_qk*d_v + d_qk + 1)
+ * floats).
  * Returns MLSTM_OK or an error code; on error, mlstm_last_error_detail()
  * describes it.
  */

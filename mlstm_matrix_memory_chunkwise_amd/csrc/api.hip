@@ -108,6 +108,7 @@ mlstm_status_t check_seq(const mlstm_problem_t* p, const void* q, const void* k,
         return fail(MLSTM_ERR_INVALID_ARG, "%s overlaps %s", bufs[o].name, bufs[i].name);
   mlstm::SeqArgs a;
   a.B = p->B; a.H = p->H; a.T = p->T; a.dqk = p->d_qk; a.dv = p->d_v;
+  a.Ts = p->T; a.t0 = 0;
   a.qkv_bf16 = p->qkv_dtype == MLSTM_BF16;
   a.o_mode = o_pre ? (p->o_dtype == MLSTM_BF16 ? mlstm::O_BF16 : mlstm::O_F32) : mlstm::O_NONE;
   a.fgate_exp = p->fgate == MLSTM_FGATE_EXP;
@@ -121,15 +122,13 @@ mlstm_status_t check_chunk(const mlstm_problem_t* p, int64_t chunk) {
   if (chunk != 16 && chunk != 32 && chunk != 64 && chunk != 128)
     return fail(MLSTM_ERR_UNSUPPORTED, "chunk=%lld: supported chunks are 16, 32, 64, 128",
                 (long long)chunk);
-  if (p->T % chunk != 0)
-    return fail(MLSTM_ERR_UNSUPPORTED, "T=%lld is not a multiple of chunk=%lld",
-                (long long)p->T, (long long)chunk);
   return MLSTM_OK;
 }
 
 mlstm::SeqArgs problem_args(const mlstm_problem_t* p) {
   mlstm::SeqArgs a{};
   a.B = p->B; a.H = p->H; a.T = p->T; a.dqk = p->d_qk; a.dv = p->d_v;
+  a.Ts = p->T; a.t0 = 0;
   a.qkv_bf16 = p->qkv_dtype == MLSTM_BF16;
   return a;
 }
@@ -191,6 +190,35 @@ const char* mlstm_status_string(mlstm_status_t s) {
 
 const char* mlstm_last_error_detail(void) { return g_detail; }
 
+// How a chunkwise call runs.  When T is not a multiple of the chunk and an
+// MFMA kernel covers the shape, that kernel runs the first Tm = T - (T % chunk)
+// tokens and leaves its final state (C~, n~, m) in the workspace; the VALU
+// kernel continues from that state over the last T % chunk tokens, as one
+// shorter chunk.  Otherwise a single kernel runs the whole sequence (the VALU
+// kernel takes a shorter last chunk by itself).
+struct FwdPlan {
+  bool mfma;        // an MFMA kernel runs tokens 0 .. Tm-1
+  bool tail;        // then the VALU kernel runs tokens Tm .. T-1
+  int64_t Tm;
+  size_t mid_off;   // byte offset of the carried state in the workspace
+  size_t need;      // workspace bytes
+};
+
+FwdPlan fwd_plan(const mlstm::SeqArgs& a, int64_t chunk) {
+  FwdPlan f{};
+  f.Tm = a.T - a.T % chunk;
+  mlstm::SeqArgs m = a;
+  m.T = f.Tm;
+  f.mfma = f.Tm > 0 && mlstm::chunk_mfma_supported(m, chunk);
+  f.tail = f.mfma && f.Tm < a.T;
+  const size_t mfma_ws = f.mfma ? mlstm::chunk_mfma_workspace(m, chunk) : 0;
+  f.mid_off = (mfma_ws + 255) / 256 * 256;
+  const size_t BH = static_cast<size_t>(a.B * a.H);
+  const size_t mid = f.tail ? 4 * BH * (static_cast<size_t>(a.dqk) * a.dv + a.dqk + 1) : 0;
+  f.need = f.tail ? f.mid_off + mid : mfma_ws;
+  return f;
+}
+
 mlstm_status_t mlstm_fwd_chunkwise_workspace_bytes(const mlstm_problem_t* p, int64_t chunk,
                                                    size_t* bytes) {
   if (!bytes) return fail(MLSTM_ERR_INVALID_ARG, "bytes is NULL");
@@ -198,8 +226,7 @@ mlstm_status_t mlstm_fwd_chunkwise_workspace_bytes(const mlstm_problem_t* p, int
   if (s != MLSTM_OK) return s;
   s = check_chunk(p, chunk);
   if (s != MLSTM_OK) return s;
-  const mlstm::SeqArgs a = problem_args(p);
-  *bytes = mlstm::chunk_mfma_supported(a, chunk) ? mlstm::chunk_mfma_workspace(a, chunk) : 0;
+  *bytes = fwd_plan(problem_args(p), chunk).need;
   return ok();
 }
 
@@ -214,16 +241,29 @@ mlstm_status_t mlstm_fwd_chunkwise(const mlstm_problem_t* p, int64_t chunk, cons
   if (s != MLSTM_OK) return s;
   s = check_chunk(p, chunk);
   if (s != MLSTM_OK) return s;
-  const bool mfma = mlstm::chunk_mfma_supported(a, chunk);
-  const size_t need = mfma ? mlstm::chunk_mfma_workspace(a, chunk) : 0;
-  if (workspace_bytes < need || (need > 0 && !workspace))
+  const FwdPlan f = fwd_plan(a, chunk);
+  if (workspace_bytes < f.need || (f.need > 0 && !workspace))
     return fail(MLSTM_ERR_INVALID_ARG, "workspace of %zu bytes given, %zu needed",
-                workspace_bytes, need);
-  if (need > 0 && !aligned16(workspace))
+                workspace_bytes, f.need);
+  if (f.need > 0 && !aligned16(workspace))
     return fail(MLSTM_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (mfma) return device_status(mlstm::launch_chunk_mfma(a, chunk, workspace, st), "chunkwise (mfma)");
-  return device_status(mlstm::launch_chunk_valu(a, chunk, st), "chunkwise (valu)");
+  if (!f.mfma) return device_status(mlstm::launch_chunk_valu(a, chunk, st), "chunkwise (valu)");
+  if (!f.tail)
+    return device_status(mlstm::launch_chunk_mfma(a, chunk, workspace, st), "chunkwise (mfma)");
+  const size_t BH = static_cast<size_t>(a.B * a.H);
+  float* midC = reinterpret_cast<float*>(static_cast<char*>(workspace) + f.mid_off);
+  float* midn = midC + BH * a.dqk * a.dv;
+  float* midm = midn + BH * a.dqk;
+  mlstm::SeqArgs head = a;   // tokens 0 .. Tm-1 on MFMA, state into the workspace
+  head.T = f.Tm;
+  head.C1 = midC; head.n1 = midn; head.m1 = midm;
+  s = device_status(mlstm::launch_chunk_mfma(head, chunk, workspace, st), "chunkwise (mfma)");
+  if (s != MLSTM_OK) return s;
+  mlstm::SeqArgs tail = a;   // tokens Tm .. T-1 from that state
+  tail.t0 = f.Tm;
+  tail.C0 = midC; tail.n0 = midn; tail.m0 = midm;
+  return device_status(mlstm::launch_chunk_valu(tail, chunk, st), "chunkwise tail (valu)");
 }
 
 mlstm_status_t mlstm_bwd_chunkwise_workspace_bytes(const mlstm_problem_t* p, int64_t chunk,

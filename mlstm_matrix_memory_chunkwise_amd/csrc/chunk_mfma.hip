@@ -122,16 +122,16 @@ __global__ __launch_bounds__(NTH, 1) void chunk_mfma_kernel(SeqArgs a) {
     }
   }
   const int dv = static_cast<int>(a.dv);
-  const int64_t T = a.T;
+  const int64_t T = a.T, Ts = a.Ts;   // tokens per head; token stride between heads
   const int nchunks = static_cast<int>(T / L);
   const int b0w = vt * TV + wave * 16;
 
-  const bf16_t* gq = static_cast<const bf16_t*>(a.q) + head * T * DQK;
-  const bf16_t* gk = static_cast<const bf16_t*>(a.k) + head * T * DQK;
-  const bf16_t* gv = static_cast<const bf16_t*>(a.v) + head * T * dv + vt * TV;
-  const float* gi = a.i_pre + head * T;
-  const float* gf = a.f_pre + head * T;
-  bf16_t* gh = static_cast<bf16_t*>(a.h) + head * T * dv;
+  const bf16_t* gq = static_cast<const bf16_t*>(a.q) + head * Ts * DQK;
+  const bf16_t* gk = static_cast<const bf16_t*>(a.k) + head * Ts * DQK;
+  const bf16_t* gv = static_cast<const bf16_t*>(a.v) + head * Ts * dv + vt * TV;
+  const float* gi = a.i_pre + head * Ts;
+  const float* gf = a.f_pre + head * Ts;
+  bf16_t* gh = static_cast<bf16_t*>(a.h) + head * Ts * dv;
 
   // ---- state
   f32x4 cacc[C::NCT];
@@ -195,7 +195,7 @@ __global__ __launch_bounds__(NTH, 1) void chunk_mfma_kernel(SeqArgs a) {
         const int row = RPI * G + lane / NCH;
         const int pc = lane % NCH;
         const int lc = (OM == O_F32) ? (pc ^ (row & 15)) : (pc ^ ((row >> 1) & 7));
-        const int64_t r = head * T + static_cast<int64_t>(c) * L + row;
+        const int64_t r = head * Ts + static_cast<int64_t>(c) * L + row;
         const char* src = (OM == O_F32)
             ? reinterpret_cast<const char*>(static_cast<const float*>(a.o_pre) + r * dv + vt * TV + 4 * lc)
             : reinterpret_cast<const char*>(static_cast<const bf16_t*>(a.o_pre) + r * dv + vt * TV + 8 * lc);

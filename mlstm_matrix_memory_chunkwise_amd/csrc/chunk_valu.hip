@@ -20,7 +20,10 @@
 // arithmetic), and every exponent is <= 0.
 //
 // Grid: (B*H, ceil(d_v / 16)); one workgroup walks all chunks of one head for
-// 16 value columns; its C~ tile [d_qk][16] and n~ stay in LDS.
+// 16 value columns; its C~ tile [d_qk][16] and n~ stay in LDS.  It processes
+// tokens t0 .. T-1 of each head (heads Ts tokens apart); the last chunk may
+// hold fewer than L tokens, which serves sequences whose length is not a
+// multiple of the chunk.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -35,7 +38,8 @@ __global__ __launch_bounds__(kThreads) void chunk_valu_kernel(SeqArgs a, int L) 
   extern __shared__ float smem[];
   const int dqk = static_cast<int>(a.dqk);
   const int dv = static_cast<int>(a.dv);
-  const int T = static_cast<int>(a.T);
+  const int T = static_cast<int>(a.T), t0 = static_cast<int>(a.t0);
+  const int64_t Ts = a.Ts;
   float* sC = smem;                      // [dqk][kTV]
   float* sN = sC + dqk * kTV;            // [dqk]
   float* sP = sN + dqk;                  // [L][L]
@@ -52,12 +56,12 @@ __global__ __launch_bounds__(kThreads) void chunk_valu_kernel(SeqArgs a, int L) 
   const int tid = threadIdx.x;
   const int64_t bh = blockIdx.x;
   const int b0 = blockIdx.y * kTV;
-  const TQ* q = static_cast<const TQ*>(a.q) + bh * static_cast<int64_t>(T) * dqk;
-  const TQ* k = static_cast<const TQ*>(a.k) + bh * static_cast<int64_t>(T) * dqk;
-  const TQ* v = static_cast<const TQ*>(a.v) + bh * static_cast<int64_t>(T) * dv;
-  const float* ip = a.i_pre + bh * T;
-  const float* fp = a.f_pre + bh * T;
-  TQ* h = static_cast<TQ*>(a.h) + bh * static_cast<int64_t>(T) * dv;
+  const TQ* q = static_cast<const TQ*>(a.q) + bh * Ts * dqk;
+  const TQ* k = static_cast<const TQ*>(a.k) + bh * Ts * dqk;
+  const TQ* v = static_cast<const TQ*>(a.v) + bh * Ts * dv;
+  const float* ip = a.i_pre + bh * Ts;
+  const float* fp = a.f_pre + bh * Ts;
+  TQ* h = static_cast<TQ*>(a.h) + bh * Ts * dv;
 
   for (int idx = tid; idx < dqk * kTV; idx += kThreads) {
     const int r = idx / kTV, c = b0 + idx % kTV;
@@ -67,13 +71,14 @@ __global__ __launch_bounds__(kThreads) void chunk_valu_kernel(SeqArgs a, int L) 
   if (tid == 0) sMs[0] = a.C0 ? a.m0[bh] : 0.0f;
   __syncthreads();
 
-  for (int c0 = 0; c0 < T; c0 += L) {
+  for (int c0 = t0; c0 < T; c0 += L) {
+    const int Lc = min(L, T - c0);   // tokens in this chunk
     const float ms = sMs[0];
-    for (int j = tid; j < L; j += kThreads) sLf[j] = log_forget(fp[c0 + j], a.fgate_exp);
+    for (int j = tid; j < Lc; j += kThreads) sLf[j] = log_forget(fp[c0 + j], a.fgate_exp);
     __syncthreads();
     if (tid == 0) {
       float b = 0.0f, Mx = ms;
-      for (int j = 0; j < L; ++j) {
+      for (int j = 0; j < Lc; ++j) {
         b += sLf[j];
         const float u = ip[c0 + j] - b;
         Mx = fmaxf(Mx, u);
@@ -84,14 +89,14 @@ __global__ __launch_bounds__(kThreads) void chunk_valu_kernel(SeqArgs a, int L) 
       sMs[0] = b + Mx;  // m at the chunk's last token
     }
     __syncthreads();
-    for (int j = tid; j < L; j += kThreads) {
+    for (int j = tid; j < Lc; j += kThreads) {
       sG[j] = expf(ms - sM[j]);
-      sW[j] = expf(sU[j] - sM[L - 1]);
+      sW[j] = expf(sU[j] - sM[Lc - 1]);
       sEm[j] = expf(-(sLf[j] + sM[j]));
     }
     // P_ij = (q_i . k_j) D_ij
-    for (int idx = tid; idx < L * L; idx += kThreads) {
-      const int i = idx / L, j = idx % L;
+    for (int idx = tid; idx < Lc * Lc; idx += kThreads) {
+      const int i = idx / Lc, j = idx % Lc;
       float s = 0.0f;
       if (j <= i) {
         const TQ* qi = q + static_cast<int64_t>(c0 + i) * dqk;
@@ -99,10 +104,10 @@ __global__ __launch_bounds__(kThreads) void chunk_valu_kernel(SeqArgs a, int L) 
         for (int r = 0; r < dqk; ++r) s += to_f32(qi[r]) * to_f32(kj[r]);
         s *= expf(sU[j] - sM[i]);
       }
-      sP[idx] = s;
+      sP[i * L + j] = s;
     }
     __syncthreads();
-    for (int i = tid; i < L; i += kThreads) {
+    for (int i = tid; i < Lc; i += kThreads) {
       float rs = 0.0f;
       for (int j = 0; j <= i; ++j) rs += sP[i * L + j];
       sRs[i] = rs;
@@ -112,7 +117,7 @@ __global__ __launch_bounds__(kThreads) void chunk_valu_kernel(SeqArgs a, int L) 
       sQn[i] = qn;
     }
     __syncthreads();
-    for (int idx = tid; idx < L * kTV; idx += kThreads) {
+    for (int idx = tid; idx < Lc * kTV; idx += kThreads) {
       const int i = idx / kTV, cc = idx % kTV, c = b0 + cc;
       if (c >= dv) continue;
       const TQ* qi = q + static_cast<int64_t>(c0 + i) * dqk;
@@ -123,25 +128,25 @@ __global__ __launch_bounds__(kThreads) void chunk_valu_kernel(SeqArgs a, int L) 
       const float num = sG[i] * inter + intra;
       const float den = fmaxf(fabsf(sG[i] * sQn[i] + sRs[i]), sEm[i]);
       float gate = 1.0f;
-      const int64_t oi = (bh * T + c0 + i) * static_cast<int64_t>(dv) + c;
+      const int64_t oi = (bh * Ts + c0 + i) * static_cast<int64_t>(dv) + c;
       if (OM == O_F32) gate = sigmoidf_(static_cast<const float*>(a.o_pre)[oi]);
       if (OM == O_BF16) gate = sigmoidf_(bf2f(static_cast<const bf16_t*>(a.o_pre)[oi]));
       h[static_cast<int64_t>(c0 + i) * dv + c] = from_f32<TQ>(gate * num / den);
     }
     __syncthreads();
-    const float gL = sG[L - 1];
+    const float gL = sG[Lc - 1];
     for (int idx = tid; idx < dqk * kTV; idx += kThreads) {
       const int r = idx / kTV, cc = idx % kTV, c = b0 + cc;
       if (c >= dv) continue;
       float acc = gL * sC[idx];
-      for (int j = 0; j < L; ++j)
+      for (int j = 0; j < Lc; ++j)
         acc += sW[j] * to_f32(k[static_cast<int64_t>(c0 + j) * dqk + r]) *
                to_f32(v[static_cast<int64_t>(c0 + j) * dv + c]);
       sC[idx] = acc;
     }
     for (int r = tid; r < dqk; r += kThreads) {
       float acc = gL * sN[r];
-      for (int j = 0; j < L; ++j) acc += sW[j] * to_f32(k[static_cast<int64_t>(c0 + j) * dqk + r]);
+      for (int j = 0; j < Lc; ++j) acc += sW[j] * to_f32(k[static_cast<int64_t>(c0 + j) * dqk + r]);
       sN[r] = acc;
     }
     __syncthreads();

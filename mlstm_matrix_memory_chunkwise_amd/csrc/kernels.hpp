@@ -15,6 +15,10 @@ enum OGate : int { O_NONE = 0, O_F32 = 1, O_BF16 = 2 };
 // pointers; optional ones are nullptr.  Dtype codes: 0 = f32, 1 = bf16.
 struct SeqArgs {
   int64_t B, H, T, dqk, dv;
+  // Tokens t0 .. T-1 of each head are processed; heads lie Ts tokens apart in
+  // q, k, v, i_pre, f_pre, o_pre and h (Ts >= T).  A whole sequence has t0 = 0
+  // and Ts = T; the MFMA chunk kernels handle t0 = 0 only.
+  int64_t Ts, t0;
   int qkv_bf16;     // q, k, v, h are bfloat16 (else float32)
   int o_mode;       // OGate: none / f32 / bf16
   int fgate_exp;    // forget gate: 1 = exponential, 0 = sigmoid
@@ -70,6 +74,7 @@ hipError_t launch_chunk_mfma8(const SeqArgs& a, hipStream_t stream);
 bool chunk_ws_supported(const SeqArgs& a, int64_t chunk);
 hipError_t launch_chunk_ws(const SeqArgs& a, hipStream_t stream);
 // Generic VALU chunkwise kernel (float32 path; bf16 shapes outside MFMA cover).
+// Tokens t0 .. T-1 in chunks of `chunk`; the last chunk may be shorter.
 hipError_t launch_chunk_valu(const SeqArgs& a, int64_t chunk, hipStream_t stream);
 
 // Chunkwise backward pass.  Gradients are float32; d_o is written only when

@@ -117,7 +117,24 @@ def test_chunkwise_unsupported(lib):
     assert chunk_call(lib, P(dqk=24))[0] == M.MLSTM_ERR_UNSUPPORTED
     assert chunk_call(lib, P(dv=528))[0] == M.MLSTM_ERR_UNSUPPORTED
     assert chunk_call(lib, P(T=64), chunk=48)[0] == M.MLSTM_ERR_UNSUPPORTED
-    assert chunk_call(lib, P(T=72), chunk=16)[0] == M.MLSTM_ERR_UNSUPPORTED
+
+
+def test_chunkwise_ragged_T_workspace(lib):
+    """T = 72 at chunk 64 on the bf16 matrix-core path: the last 8 tokens
+    continue from the state of the first 64, which the workspace holds, so a
+    call without one is refused before anything is launched."""
+    n = ctypes.c_size_t(0)
+    p = P(B=2, H=3, T=72, dqk=64, dv=64, qkv=1)
+    assert lib.mlstm_fwd_chunkwise_workspace_bytes(ctypes.byref(p), 64, ctypes.byref(n)) == 0
+    assert n.value == 4 * 6 * (64 * 64 + 64 + 1)
+    r, det = chunk_call(lib, p, chunk=64)
+    assert r == M.MLSTM_ERR_INVALID_ARG and "workspace" in det
+    # no carried state is needed for a multiple of the chunk, for T below one
+    # chunk, or on the float32 path (one kernel takes the short last chunk)
+    for q, chunk in ((P(T=128, dqk=64, dv=64, qkv=1), 64), (P(T=40, dqk=64, dv=64, qkv=1), 64),
+                     (P(T=72), 16)):
+        assert lib.mlstm_fwd_chunkwise_workspace_bytes(ctypes.byref(q), chunk, ctypes.byref(n)) == 0
+        assert n.value == 0
 
 
 def test_chunkwise_rejects_misalignment(lib):

@@ -124,6 +124,15 @@ EDGE = [
     ("d_qk 256: exp forget gate", "bf16", 1, 2, 512, 256, 64, 64, True, True, "exp"),
     ("d_qk 256: input-gate spikes", "bf16", 1, 2, 1024, 256, 64, 64, True, True, "sigmoid"),
     ("d_qk 256: d_v 512", "bf16", 1, 1, 256, 256, 512, 64, True, True, "sigmoid"),
+    # T not a multiple of the chunk: the matrix-core kernel runs the whole
+    # chunks, the float32 VALU kernel the tail from the carried state
+    ("ragged: d_qk 256, 2 chunks + 17", "bf16", 1, 2, 145, 256, 128, 64, True, True, "sigmoid"),
+    ("ragged: d_qk 128, 3 chunks + 63, exp gate", "bf16", 2, 3, 255, 128, 64, 64, True, True, "exp"),
+    ("ragged: chunk 32, 4 chunks + 1", "bf16", 1, 2, 129, 64, 64, 32, False, True, "sigmoid"),
+    ("ragged: chunk 128, 2 chunks + 100", "bf16", 1, 1, 356, 256, 128, 128, True, False, "sigmoid"),
+    ("ragged: T below one chunk", "bf16", 1, 2, 40, 64, 64, 64, True, True, "sigmoid"),
+    ("ragged: T = 1", "bf16", 1, 1, 1, 64, 64, 64, True, True, "sigmoid"),
+    ("ragged: fp32 chunk 64, 1 chunk + 36", "f32", 1, 2, 100, 32, 48, 64, True, True, "sigmoid"),
 ]
 
 
@@ -213,14 +222,16 @@ def test_deterministic():
         assert torch.equal(x, y)
 
 
-@pytest.mark.parametrize("dtype,chunk,dqk,dv", [("bf16", 64, 64, 128), ("bf16", 64, 256, 128),
-                                                ("bf16", 32, 64, 48), ("f32", 16, 64, 32)])
-def test_every_output_written(dtype, chunk, dqk, dv):
-    """Outputs pre-filled with NaN come back finite: every element was written."""
-    cfg = workloads.Config("canary", 8, dtype, 2, 3, 4 * chunk, dqk, dv, (chunk,), (0.0, 1.0),
+@pytest.mark.parametrize("dtype,chunk,dqk,dv,tail", [("bf16", 64, 64, 128, 0), ("bf16", 64, 256, 128, 0),
+                                                     ("bf16", 32, 64, 48, 0), ("f32", 16, 64, 32, 0),
+                                                     ("bf16", 64, 256, 128, 9), ("f32", 16, 64, 32, 5)])
+def test_every_output_written(dtype, chunk, dqk, dv, tail):
+    """Outputs pre-filled with NaN come back finite: every element was written
+    (also the tokens of a last, shorter chunk)."""
+    cfg = workloads.Config("canary", 8, dtype, 2, 3, 4 * chunk + tail, dqk, dv, (chunk,), (0.0, 1.0),
                            (3.0, 1.0), (0.0, 1.0), True)
     inp = workloads.make_chunkwise_inputs(cfg)
-    log(f"chunkwise canary {dtype} chunk={chunk} dqk={dqk} dv={dv}")
+    log(f"chunkwise canary {dtype} chunk={chunk} dqk={dqk} dv={dv} tail={tail}")
     d = to_dev(inp)
     M = _M()
     out = nan_like(tuple(d["v"].shape), d["q"].dtype)
