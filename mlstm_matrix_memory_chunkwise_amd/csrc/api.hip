@@ -118,6 +118,30 @@ mlstm_status_t check_seq(const mlstm_problem_t* p, const void* q, const void* k,
   return MLSTM_OK;
 }
 
+// The workspace (`need` bytes) of a whole-sequence call must not overlap any
+// tensor argument.
+mlstm_status_t check_seq_workspace(const mlstm_problem_t* p, const void* q, const void* k,
+                                   const void* v, const float* i_pre, const float* f_pre,
+                                   const void* o_pre, const float* C0, const float* n0,
+                                   const float* m0, const void* h, const float* C1,
+                                   const float* n1, const float* m1, const void* workspace,
+                                   size_t need) {
+  const Buf ws{"workspace", workspace, need, 16};
+  const size_t BH = (size_t)(p->B * p->H), T = (size_t)p->T, sq = dsize(p->qkv_dtype);
+  const Buf all[] = {
+      {"q", q, BH * T * p->d_qk * sq, 16}, {"k", k, BH * T * p->d_qk * sq, 16},
+      {"v", v, BH * T * p->d_v * sq, 16},  {"i_pre", i_pre, BH * T * 4, 4},
+      {"f_pre", f_pre, BH * T * 4, 4},
+      {"o_pre", o_pre, BH * T * p->d_v * dsize(p->o_dtype), 16},
+      {"C0", C0, BH * p->d_qk * p->d_v * 4, 16}, {"n0", n0, BH * p->d_qk * 4, 4},
+      {"m0", m0, BH * 4, 4},               {"h", h, BH * T * p->d_v * sq, 16},
+      {"C1", C1, BH * p->d_qk * p->d_v * 4, 16}, {"n1", n1, BH * p->d_qk * 4, 4},
+      {"m1", m1, BH * 4, 4}};
+  for (const Buf& b : all)
+    if (overlaps(ws, b)) return fail(MLSTM_ERR_INVALID_ARG, "workspace overlaps %s", b.name);
+  return MLSTM_OK;
+}
+
 mlstm_status_t check_chunk(const mlstm_problem_t* p, int64_t chunk) {
   if (chunk != 16 && chunk != 32 && chunk != 64 && chunk != 128)
     return fail(MLSTM_ERR_UNSUPPORTED, "chunk=%lld: supported chunks are 16, 32, 64, 128",
@@ -247,6 +271,9 @@ mlstm_status_t mlstm_fwd_chunkwise(const mlstm_problem_t* p, int64_t chunk, cons
                 workspace_bytes, f.need);
   if (f.need > 0 && !aligned16(workspace))
     return fail(MLSTM_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  s = check_seq_workspace(p, q, k, v, i_pre, f_pre, o_pre, C0, n0, m0, h, C1, n1, m1, workspace,
+                          f.need);
+  if (s != MLSTM_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (!f.mfma) return device_status(mlstm::launch_chunk_valu(a, chunk, st), "chunkwise (valu)");
   if (!f.tail)
@@ -490,20 +517,9 @@ mlstm_status_t mlstm_fwd_parallel(const mlstm_problem_t* p, const void* q, const
     return fail(MLSTM_ERR_INVALID_ARG, "workspace of %zu bytes given, %zu needed",
                 workspace_bytes, need);
   if (!aligned16(workspace)) return fail(MLSTM_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
-  const Buf ws{"workspace", workspace, need, 16};
-  // the workspace must not overlap any tensor argument
-  const size_t BH = (size_t)(p->B * p->H), T = (size_t)p->T, sq = dsize(p->qkv_dtype);
-  const Buf all[] = {
-      {"q", q, BH * T * p->d_qk * sq, 16}, {"k", k, BH * T * p->d_qk * sq, 16},
-      {"v", v, BH * T * p->d_v * sq, 16},  {"i_pre", i_pre, BH * T * 4, 4},
-      {"f_pre", f_pre, BH * T * 4, 4},
-      {"o_pre", o_pre, BH * T * p->d_v * dsize(p->o_dtype), 16},
-      {"C0", C0, BH * p->d_qk * p->d_v * 4, 16}, {"n0", n0, BH * p->d_qk * 4, 4},
-      {"m0", m0, BH * 4, 4},               {"h", h, BH * T * p->d_v * sq, 16},
-      {"C1", C1, BH * p->d_qk * p->d_v * 4, 16}, {"n1", n1, BH * p->d_qk * 4, 4},
-      {"m1", m1, BH * 4, 4}};
-  for (const Buf& b : all)
-    if (overlaps(ws, b)) return fail(MLSTM_ERR_INVALID_ARG, "workspace overlaps %s", b.name);
+  s = check_seq_workspace(p, q, k, v, i_pre, f_pre, o_pre, C0, n0, m0, h, C1, n1, m1, workspace,
+                          need);
+  if (s != MLSTM_OK) return s;
   return device_status(mlstm::launch_parallel(a, workspace, static_cast<hipStream_t>(stream)),
                        "parallel");
 }

@@ -129,6 +129,14 @@ def test_chunkwise_ragged_T_workspace(lib):
     assert n.value == 4 * 6 * (64 * 64 + 64 + 1)
     r, det = chunk_call(lib, p, chunk=64)
     assert r == M.MLSTM_ERR_INVALID_ARG and "workspace" in det
+    # a workspace placed over h is refused too
+    names = ["q", "k", "v", "i", "f", "o", "C0", "n0", "m0", "h", "C1", "n1", "m1"]
+    vals = dict(zip(names, ptrs(len(names))))
+    vals.update(o=None, C0=None, n0=None, m0=None, C1=None, n1=None, m1=None)
+    r = lib.mlstm_fwd_chunkwise(ctypes.byref(p), 64, *(vals[k] for k in names),
+                                vals["h"], n.value, None)
+    assert r == M.MLSTM_ERR_INVALID_ARG
+    assert "workspace overlaps h" in lib.mlstm_last_error_detail().decode()
     # no carried state is needed for a multiple of the chunk, for T below one
     # chunk, or on the float32 path (one kernel takes the short last chunk)
     for q, chunk in ((P(T=128, dqk=64, dv=64, qkv=1), 64), (P(T=40, dqk=64, dv=64, qkv=1), 64),
