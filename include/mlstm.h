@@ -59,7 +59,7 @@ typedef enum {
                                 workspace too small */
   MLSTM_ERR_UNSUPPORTED = 2, /* valid but not implemented: d not a multiple of
                                 16 or above 512, chunk not in {16,32,64,128},
-                                T not a multiple of chunk (backward only) */
+                                backward shapes without a kernel */
   MLSTM_ERR_DEVICE = 3       /* a HIP call or kernel launch failed */
 } mlstm_status_t;
 
@@ -179,9 +179,12 @@ mlstm_status_t mlstm_step(const mlstm_problem_t* p, const void* q,
  * Supported: chunk 16 or 32 with d_qk <= 256 (float32 arithmetic
  * throughout), or chunk 64 with bf16 q/k/v, d_v a multiple of 64 and d_qk
  * 64, 128 or 256 (matrix products on bf16 matrix cores with float32
- * accumulation, operands such as the memory gradient rounded to bf16); T a
- * multiple of chunk; otherwise MLSTM_ERR_UNSUPPORTED.  The result does not
- * depend on chunk beyond rounding.
+ * accumulation, operands such as the memory gradient rounded to bf16);
+ * otherwise MLSTM_ERR_UNSUPPORTED.  The result does not depend on chunk
+ * beyond rounding.  Any T >= 1: when T is not a multiple of chunk, the pass
+ * runs on copies of the per-token arrays padded to the next multiple Tp, at
+ * the front of the workspace (14 arrays of B*H*Tp tokens each); a padding
+ * token keeps the memory unchanged and contributes nothing to any gradient.
  */
 mlstm_status_t mlstm_bwd_chunkwise(const mlstm_problem_t* p, int64_t chunk,
                                    const void* q, const void* k, const void* v,

@@ -162,9 +162,6 @@ mlstm_status_t check_bwd_shape(const mlstm_problem_t* p, int64_t chunk) {
   if (chunk != 16 && chunk != 32 && chunk != 64)
     return fail(MLSTM_ERR_UNSUPPORTED, "backward: chunk=%lld: supported chunks are 16, 32, 64",
                 (long long)chunk);
-  if (p->T % chunk != 0)
-    return fail(MLSTM_ERR_UNSUPPORTED, "T=%lld is not a multiple of chunk=%lld",
-                (long long)p->T, (long long)chunk);
   if (chunk == 64) {
     if (p->qkv_dtype != MLSTM_BF16 || p->d_v % 64 != 0 ||
         (p->d_qk != 64 && p->d_qk != 128 && p->d_qk != 256))
@@ -293,6 +290,45 @@ mlstm_status_t mlstm_fwd_chunkwise(const mlstm_problem_t* p, int64_t chunk, cons
   return device_status(mlstm::launch_chunk_valu(tail, chunk, st), "chunkwise tail (valu)");
 }
 
+// Backward of a sequence whose length T is not a multiple of the chunk: the
+// pass runs on copies padded to Tp = ceil(T / chunk) chunks, placed at the
+// front of the workspace.  A padding token leaves the memory as it is
+// (log f = 0: f~ = 1e4 for the sigmoid gate, 0 for the exponential one;
+// i = 0: i~ = -1e4) and has q = k = v = h = dh = o~ = 0, so it adds nothing
+// to any gradient, and dC1, dn1 given at Tp are the gradients at T.  The
+// gradients of the first T tokens are copied out afterwards.
+struct BwdPad {
+  int64_t Tp;
+  enum { Q, K, V, I, F, O, H, DH, DQ, DK, DV, DI, DF, DO, N };
+  size_t off[N];
+  size_t row[N];    // bytes per token
+  size_t bytes;     // 0: no padding
+};
+
+BwdPad bwd_pad_plan(const mlstm_problem_t* p, int64_t chunk) {
+  BwdPad b{};
+  b.Tp = (p->T + chunk - 1) / chunk * chunk;
+  if (b.Tp == p->T) return b;
+  const size_t sq = dsize(p->qkv_dtype), so = dsize(p->o_dtype);
+  const size_t dqk = (size_t)p->d_qk, dv = (size_t)p->d_v;
+  const size_t rows[BwdPad::N] = {dqk * sq, dqk * sq, dv * sq, 4, 4, dv * so, dv * sq, dv * sq,
+                                  dqk * 4, dqk * 4, dv * 4, 4, 4, dv * 4};
+  size_t at = 0;
+  for (int i = 0; i < BwdPad::N; ++i) {
+    b.row[i] = rows[i];
+    b.off[i] = at;
+    at += (static_cast<size_t>(p->B * p->H) * b.Tp * rows[i] + 255) / 256 * 256;
+  }
+  b.bytes = at;
+  return b;
+}
+
+mlstm::BwdArgs bwd_padded_args(const mlstm_problem_t* p, int64_t chunk, const BwdPad& pad) {
+  mlstm::BwdArgs a = bwd_problem_args(p, chunk);
+  a.T = pad.Tp;
+  return a;
+}
+
 mlstm_status_t mlstm_bwd_chunkwise_workspace_bytes(const mlstm_problem_t* p, int64_t chunk,
                                                    size_t* bytes) {
   if (!bytes) return fail(MLSTM_ERR_INVALID_ARG, "bytes is NULL");
@@ -300,7 +336,8 @@ mlstm_status_t mlstm_bwd_chunkwise_workspace_bytes(const mlstm_problem_t* p, int
   if (s != MLSTM_OK) return s;
   s = check_bwd_shape(p, chunk);
   if (s != MLSTM_OK) return s;
-  *bytes = mlstm::bwd_workspace(bwd_problem_args(p, chunk), nullptr);
+  const BwdPad pad = bwd_pad_plan(p, chunk);
+  *bytes = pad.bytes + mlstm::bwd_workspace(bwd_padded_args(p, chunk, pad), nullptr);
   return ok();
 }
 
@@ -353,8 +390,9 @@ mlstm_status_t mlstm_bwd_chunkwise(const mlstm_problem_t* p, int64_t chunk, cons
     for (int i = 0; i < nb; ++i)
       if (i != o && overlaps(bufs[o], bufs[i]))
         return fail(MLSTM_ERR_INVALID_ARG, "%s overlaps %s", bufs[o].name, bufs[i].name);
-  mlstm::BwdArgs a = bwd_problem_args(p, chunk);
-  const size_t need = mlstm::bwd_workspace(a, nullptr);
+  const BwdPad pad = bwd_pad_plan(p, chunk);
+  mlstm::BwdArgs a = bwd_padded_args(p, chunk, pad);
+  const size_t need = pad.bytes + mlstm::bwd_workspace(a, nullptr);
   if (!workspace || workspace_bytes < need)
     return fail(MLSTM_ERR_INVALID_ARG, "workspace of %zu bytes given, %zu needed", workspace_bytes,
                 need);
@@ -367,8 +405,51 @@ mlstm_status_t mlstm_bwd_chunkwise(const mlstm_problem_t* p, int64_t chunk, cons
   a.C0 = C0; a.n0 = n0; a.m0 = m0; a.h = h; a.dh = dh; a.dC1 = dC1; a.dn1 = dn1;
   a.d_q = dq; a.d_k = dk; a.d_v = dv; a.d_i = di; a.d_f = df; a.d_o = d_o;
   a.dC0 = dC0; a.dn0 = dn0; a.dm0 = dm0;
-  return device_status(mlstm::launch_bwd(a, workspace, static_cast<hipStream_t>(stream)),
-                       "chunkwise backward");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (pad.bytes == 0)
+    return device_status(mlstm::launch_bwd(a, workspace, st), "chunkwise backward");
+
+  // padded copies: rows of T tokens copied, tokens T .. Tp-1 filled
+  char* w = static_cast<char*>(workspace);
+  const int64_t BHr = p->B * p->H, Tr = p->T, Tp = pad.Tp;
+  auto at = [&](int i) { return static_cast<void*>(w + pad.off[i]); };
+  const float fpad = p->fgate == MLSTM_FGATE_EXP ? 0.0f : 1.0e4f, ipad = -1.0e4f;
+  const void* src[BwdPad::DQ] = {q, k, v, i_pre, f_pre, o_pre, h, dh};
+  hipError_t e = hipSuccess;
+  for (int i = 0; i < BwdPad::DQ && e == hipSuccess; ++i) {
+    if (!src[i]) continue;
+    const size_t r = pad.row[i];
+    e = hipMemcpy2DAsync(at(i), Tp * r, src[i], Tr * r, Tr * r, BHr, hipMemcpyDeviceToDevice, st);
+    float fill = 0.0f;
+    if (i == BwdPad::I) fill = ipad;
+    if (i == BwdPad::F) fill = fpad;
+    uint32_t word;
+    std::memcpy(&word, &fill, 4);
+    if (e == hipSuccess)
+      e = mlstm::launch_fill_words(static_cast<uint32_t*>(at(i)), BHr, Tp * r / 4, Tr * r / 4,
+                                   (Tp - Tr) * r / 4, word, st);
+  }
+  if (e != hipSuccess) return device_status(e, "chunkwise backward (padding)");
+  a.q = at(BwdPad::Q); a.k = at(BwdPad::K); a.v = at(BwdPad::V);
+  a.i_pre = static_cast<const float*>(at(BwdPad::I));
+  a.f_pre = static_cast<const float*>(at(BwdPad::F));
+  a.o_pre = o_pre ? at(BwdPad::O) : nullptr;
+  a.h = at(BwdPad::H); a.dh = at(BwdPad::DH);
+  a.d_q = static_cast<float*>(at(BwdPad::DQ)); a.d_k = static_cast<float*>(at(BwdPad::DK));
+  a.d_v = static_cast<float*>(at(BwdPad::DV)); a.d_i = static_cast<float*>(at(BwdPad::DI));
+  a.d_f = static_cast<float*>(at(BwdPad::DF));
+  a.d_o = d_o ? static_cast<float*>(at(BwdPad::DO)) : nullptr;
+  s = device_status(mlstm::launch_bwd(a, w + pad.bytes, st), "chunkwise backward");
+  if (s != MLSTM_OK) return s;
+  void* dst[BwdPad::N] = {};
+  dst[BwdPad::DQ] = dq; dst[BwdPad::DK] = dk; dst[BwdPad::DV] = dv;
+  dst[BwdPad::DI] = di; dst[BwdPad::DF] = df; dst[BwdPad::DO] = d_o;
+  for (int i = BwdPad::DQ; i < BwdPad::N && e == hipSuccess; ++i) {
+    if (!dst[i]) continue;
+    const size_t r = pad.row[i];
+    e = hipMemcpy2DAsync(dst[i], Tr * r, at(i), Tp * r, Tr * r, BHr, hipMemcpyDeviceToDevice, st);
+  }
+  return device_status(e, "chunkwise backward (copy out)");
 }
 
 mlstm_status_t mlstm_groupnorm_ogate(int64_t B, int64_t H, int64_t T, int64_t d_v,

@@ -636,4 +636,26 @@ hipError_t launch_bwd(BwdArgs a, void* ws, hipStream_t st) {
   return launch_dt<float, float>(a, st);
 }
 
+namespace {
+__global__ __launch_bounds__(NTB) void fill_words_kernel(uint32_t* base, int64_t rows, int64_t pitch,
+                                                         int64_t off, int64_t count, uint32_t value) {
+  const int64_t n = rows * count;
+  for (int64_t e = blockIdx.x * static_cast<int64_t>(NTB) + threadIdx.x; e < n;
+       e += static_cast<int64_t>(gridDim.x) * NTB) {
+    const int64_t r = e / count, c = e % count;
+    base[r * pitch + off + c] = value;
+  }
+}
+}  // namespace
+
+hipError_t launch_fill_words(uint32_t* base, int64_t rows, int64_t pitch, int64_t off, int64_t count,
+                             uint32_t value, hipStream_t st) {
+  const int64_t n = rows * count;
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + NTB - 1) / NTB;
+  const unsigned grid = static_cast<unsigned>(blocks < 4096 ? blocks : 4096);
+  fill_words_kernel<<<grid, NTB, 0, st>>>(base, rows, pitch, off, count, value);
+  return hipGetLastError();
+}
+
 }  // namespace mlstm

@@ -247,15 +247,33 @@ def test_bwd_pairing_rules(lib):
     assert r == M.MLSTM_ERR_INVALID_ARG and "initial state" in det
 
 
+def test_bwd_ragged_T_workspace(lib):
+    """T not a multiple of the chunk: the pass runs on 14 per-token arrays
+    padded to the next multiple Tp at the front of the workspace, followed by
+    the workspace of the padded problem.  Without room for them the call is
+    refused before anything is launched."""
+    n, n_pad = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    for p, pp, chunk in ((P(T=96, dqk=64, dv=64, qkv=1), P(T=128, dqk=64, dv=64, qkv=1), 64),
+                         (P(T=40), P(T=48), 16)):
+        assert lib.mlstm_bwd_chunkwise_workspace_bytes(ctypes.byref(p), chunk, ctypes.byref(n)) == 0
+        assert lib.mlstm_bwd_chunkwise_workspace_bytes(ctypes.byref(pp), chunk,
+                                                       ctypes.byref(n_pad)) == 0
+        sq, so = (2 if p.qkv_dtype else 4), 4
+        rows = [p.d_qk * sq] * 2 + [p.d_v * sq, 4, 4, p.d_v * so, p.d_v * sq, p.d_v * sq,
+                                    p.d_qk * 4, p.d_qk * 4, p.d_v * 4, 4, 4, p.d_v * 4]
+        pad = sum((pp.T * r + 255) // 256 * 256 for r in rows)
+        assert n.value == pad + n_pad.value
+        r, det = bwd_call(lib, p, chunk=chunk, ws_bytes=n.value - 1)
+        assert r == M.MLSTM_ERR_INVALID_ARG and "workspace" in det
+
+
 def test_bwd_unsupported(lib):
     # chunk 64 is the MFMA path: bf16 q/k/v, d_v % 64 == 0, d_qk in {64, 128, 256}
     assert bwd_call(lib, P(), chunk=64)[0] == M.MLSTM_ERR_UNSUPPORTED
     assert bwd_call(lib, P(dqk=64, dv=64), chunk=64)[0] == M.MLSTM_ERR_UNSUPPORTED
     assert bwd_call(lib, P(dqk=96, dv=64, qkv=1), chunk=64)[0] == M.MLSTM_ERR_UNSUPPORTED
     assert bwd_call(lib, P(dqk=64, dv=32, qkv=1), chunk=64)[0] == M.MLSTM_ERR_UNSUPPORTED
-    assert bwd_call(lib, P(T=96, dqk=64, dv=64, qkv=1), chunk=64)[0] == M.MLSTM_ERR_UNSUPPORTED
     assert bwd_call(lib, P(), chunk=128)[0] == M.MLSTM_ERR_UNSUPPORTED
-    assert bwd_call(lib, P(T=40))[0] == M.MLSTM_ERR_UNSUPPORTED
     assert bwd_call(lib, P(dqk=512, dv=32))[0] == M.MLSTM_ERR_UNSUPPORTED
     assert bwd_call(lib, P(dqk=272, dv=48))[0] == M.MLSTM_ERR_UNSUPPORTED
 

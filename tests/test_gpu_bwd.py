@@ -100,6 +100,14 @@ CASES = [
     # one column block: dv's two terms partly cancel here, which exposed the
     # bf16 rounding of the carried dC in the dv product (now a hi/lo pair)
     ("bf16 d128/64 chunk 64 one column block", torch.bfloat16, 2, 1, 128, 128, 64, 64, "sigmoid", True, torch.float32, True, True),
+    # T not a multiple of the chunk: the pass runs on copies padded with
+    # tokens that keep the memory unchanged
+    ("ragged fp32 d32/48 chunk 16 T=37", torch.float32, 1, 2, 37, 32, 48, 16, "sigmoid", True, torch.float32, True, True),
+    ("ragged fp32 chunk 32 exp gate no o T=50", torch.float32, 2, 1, 50, 64, 32, 32, "exp", False, None, True, True),
+    ("ragged bf16 d256/128 chunk 64 T=150", torch.bfloat16, 1, 2, 150, 256, 128, 64, "sigmoid", True, torch.float32, True, True),
+    ("ragged bf16 d128/192 chunk 64 exp gate bf16 o T=100", torch.bfloat16, 1, 1, 100, 128, 192, 64, "exp", True, torch.bfloat16, False, True),
+    ("ragged bf16 d64 chunk 64 T=9", torch.bfloat16, 1, 2, 9, 64, 64, 64, "sigmoid", True, torch.float32, True, True),
+    ("ragged bf16 d64 chunk 64 T=1", torch.bfloat16, 1, 1, 1, 64, 64, 64, "sigmoid", True, torch.float32, True, True),
 ]
 
 
