@@ -177,14 +177,14 @@ def profile_workload():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     M.load_library()
-    cfg = workloads.CONFIGS["c2"]
+    cfg = workloads.CONFIGS["d256_T8192"]
     d = {k: (None if v is None else v.to(dev)) for k, v in workloads.make_chunkwise_inputs(cfg).items()}
     h = torch.empty((cfg.B, cfg.H, cfg.T, cfg.dv), dtype=torch.bfloat16, device=dev)
     M.mlstm_fwd_chunkwise(d["q"], d["k"], d["v"], d["i_pre"], d["f_pre"], d["o_pre"],
                           d["C0"], d["n0"], d["m0"], chunk=64, out=h)
     torch.cuda.synchronize()
     del d, h
-    cfg3 = workloads.CONFIGS["c3"]
+    cfg3 = workloads.CONFIGS["step_d512"]
     s = {k: (None if v is None else v.to(dev)) for k, v in workloads.make_step_inputs(cfg3).items()}
     M.mlstm_step(s["q"][0], s["k"][0], s["v"][0], s["i_pre"][0], s["f_pre"][0], s["o_pre"][0],
                  s["C0"], s["n0"], s["m0"], inplace=True)
@@ -249,7 +249,7 @@ def main():
         print(msg, file=sys.stderr, flush=True)
 
     # ------------------------------------------------------------ chunkwise
-    cfg = workloads.CONFIGS["c2"]
+    cfg = workloads.CONFIGS["d256_T8192"]
     log(f"bench: generating {cfg.describe()}")
     inp = workloads.make_chunkwise_inputs(cfg)
     d = {k: (None if v is None else v.to(dev)) for k, v in inp.items()}
@@ -496,7 +496,7 @@ def main():
 
     # ------------------------------------------------------------ decode step
     if not args.skip_step:
-        cfg3 = workloads.CONFIGS["c3"]
+        cfg3 = workloads.CONFIGS["step_d512"]
         log(f"bench: generating {cfg3.describe()}")
         s = workloads.make_step_inputs(cfg3)
         ds = {k: (None if v is None else v.to(dev)) for k, v in s.items()}

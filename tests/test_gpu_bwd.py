@@ -132,23 +132,23 @@ def test_bwd_chunk_independent():
 
 
 @pytest.fixture(scope="module")
-def c2_case():
+def d256_case():
     """The measured workload's shape (B=8, H=8, T=8192, d=256, bf16, f32 o-gate,
     random state in, final-state gradient), with the oracle's gradients of two
     sampled heads."""
-    log("bwd c2 full: inputs")
+    log("bwd d256 T8192 full: inputs")
     inp, gin = make_inputs(2, torch.bfloat16, 8, 8, 8192, 256, 256)
     heads = sample_heads(8, 8, 2, seed=5)
-    log(f"bwd c2 full: oracle on heads {heads}")
+    log(f"bwd d256 T8192 full: oracle on heads {heads}")
     r = run_oracle(inp, gin, "sigmoid", torch.float32, heads=heads)
     return inp, gin, heads, r
 
 
 @pytest.mark.parametrize("chunk", [32, 64])
-def test_bwd_c2_sampled_heads(c2_case, chunk):
+def test_bwd_d256_T8192_sampled_heads(d256_case, chunk):
     """The GPU computes every head of the measured workload, the oracle two
     sampled heads (chunk 32: the float32 reverse pass; chunk 64: MFMA)."""
-    inp, gin, heads, r = c2_case
-    log(f"bwd c2 full: GPU chunk {chunk}")
+    inp, gin, heads, r = d256_case
+    log(f"bwd d256 T8192 full: GPU chunk {chunk}")
     g = run_gpu(inp, gin, chunk, "sigmoid", torch.float32)
-    compare(g, r, TOL_BF16, f"c2 sampled chunk {chunk}", True, heads=heads)
+    compare(g, r, TOL_BF16, f"d256 T8192 sampled chunk {chunk}", True, heads=heads)

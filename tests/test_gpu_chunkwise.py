@@ -54,50 +54,50 @@ def compare(gpu, ref, tol, heads=None, label=""):
 
 
 # ----------------------------------------------------------------- workloads
-def test_c0_fp32():
-    cfg = workloads.CONFIGS["c0"]
-    log("chunkwise c0 fp32")
+def test_tiny_fp32():
+    cfg = workloads.CONFIGS["tiny_fp32"]
+    log("chunkwise tiny fp32")
     inp = workloads.make_chunkwise_inputs(cfg)
-    compare(run_gpu(inp, 16), run_oracle(inp), TOL_F32, label="c0")
+    compare(run_gpu(inp, 16), run_oracle(inp), TOL_F32, label="tiny fp32")
 
 
-def test_c1_bf16_full():
-    cfg = workloads.CONFIGS["c1"]
-    log("chunkwise c1 bf16 full")
+def test_d128_T2048_full():
+    cfg = workloads.CONFIGS["d128_T2048"]
+    log("chunkwise d128 T2048 full")
     inp = workloads.make_chunkwise_inputs(cfg)
-    compare(run_gpu(inp, 64), run_oracle(inp), TOL_BF16, label="c1")
+    compare(run_gpu(inp, 64), run_oracle(inp), TOL_BF16, label="d128 T2048")
 
 
 @pytest.mark.parametrize("chunk", [64, 128])
-def test_c2_reduced(chunk):
-    """c2's distributions and random initial state, B=1, H=2, T=1024."""
-    cfg = workloads.CONFIGS["c2"]
-    log(f"chunkwise c2 reduced chunk={chunk}")
+def test_d256_T8192_reduced(chunk):
+    """The d256 T8192 workload's distributions and random initial state, at B=1, H=2, T=1024."""
+    cfg = workloads.CONFIGS["d256_T8192"]
+    log(f"chunkwise d256 reduced chunk={chunk}")
     inp = workloads.make_chunkwise_inputs(cfg, B=1, H=2, T=1024)
-    compare(run_gpu(inp, chunk), run_oracle(inp), TOL_BF16, label=f"c2r L={chunk}")
+    compare(run_gpu(inp, chunk), run_oracle(inp), TOL_BF16, label=f"d256 reduced L={chunk}")
 
 
 @pytest.mark.parametrize("chunk", [64, 128])
-def test_c2_full_sampled_heads(chunk):
-    cfg = workloads.CONFIGS["c2"]
-    log(f"chunkwise c2 full chunk={chunk}: inputs")
+def test_d256_T8192_full_sampled_heads(chunk):
+    cfg = workloads.CONFIGS["d256_T8192"]
+    log(f"chunkwise d256 T8192 full chunk={chunk}: inputs")
     inp = workloads.make_chunkwise_inputs(cfg)
     heads = sample_heads(cfg.B, cfg.H, 6, seed=chunk)
-    log(f"chunkwise c2 full chunk={chunk}: GPU")
+    log(f"chunkwise d256 T8192 full chunk={chunk}: GPU")
     gpu = run_gpu(inp, chunk)
-    log(f"chunkwise c2 full chunk={chunk}: oracle on {len(heads)} heads")
-    compare(gpu, run_oracle(inp, heads), TOL_BF16, heads, label=f"c2 L={chunk}")
+    log(f"chunkwise d256 T8192 full chunk={chunk}: oracle on {len(heads)} heads")
+    compare(gpu, run_oracle(inp, heads), TOL_BF16, heads, label=f"d256 T8192 L={chunk}")
 
 
-def test_c4_full_sampled_heads():
-    cfg = workloads.CONFIGS["c4"]
-    log("chunkwise c4 full: inputs")
+def test_d256x512_T65536_sampled_heads():
+    cfg = workloads.CONFIGS["d256x512_T65536"]
+    log("chunkwise d256/512 T65536 full: inputs")
     inp = workloads.make_chunkwise_inputs(cfg)
     heads = sample_heads(cfg.B, cfg.H, 2, seed=4)
-    log("chunkwise c4 full: GPU")
+    log("chunkwise d256/512 T65536 full: GPU")
     gpu = run_gpu(inp, 128)
-    log(f"chunkwise c4 full: oracle on {len(heads)} heads")
-    compare(gpu, run_oracle(inp, heads), TOL_BF16, heads, label="c4")
+    log(f"chunkwise d256/512 T65536 full: oracle on {len(heads)} heads")
+    compare(gpu, run_oracle(inp, heads), TOL_BF16, heads, label="d256/512 T65536")
 
 
 # ----------------------------------------------------------------- edge cases
@@ -150,7 +150,7 @@ def test_edge_cases(case):
 
 
 def test_bf16_output_gate():
-    cfg = workloads.CONFIGS["c2"]
+    cfg = workloads.CONFIGS["d256_T8192"]
     inp = workloads.make_chunkwise_inputs(cfg, B=1, H=1, T=256)
     log("chunkwise bf16 o")
     compare(run_gpu(inp, 64, o_dtype=torch.bfloat16), run_oracle(inp, o_dtype=torch.bfloat16),
@@ -190,7 +190,7 @@ def test_split_at_chunk_boundary_bf16():
     """bf16 MFMA path: two calls with the carried state agree with one call.
     Not bit for bit: inside one call the state is carried as (scale, scaled
     accumulator) and crossing the call boundary rounds it to C~ once."""
-    cfg = workloads.CONFIGS["c2"]
+    cfg = workloads.CONFIGS["d256_T8192"]
     inp = workloads.make_chunkwise_inputs(cfg, B=1, H=8, T=512)
     log("chunkwise split (bf16)")
     (h, C1, n1, m1), (h2, C2, n2, m2) = _split_run(inp, 64, 192)
@@ -201,7 +201,7 @@ def test_split_at_chunk_boundary_bf16():
 
 
 def test_chunk_64_and_128_agree():
-    cfg = workloads.CONFIGS["c2"]
+    cfg = workloads.CONFIGS["d256_T8192"]
     inp = workloads.make_chunkwise_inputs(cfg, B=1, H=8, T=1024)
     log("chunkwise 64 vs 128")
     a = run_gpu(inp, 64)
@@ -213,7 +213,7 @@ def test_chunk_64_and_128_agree():
 
 
 def test_deterministic():
-    cfg = workloads.CONFIGS["c2"]
+    cfg = workloads.CONFIGS["d256_T8192"]
     inp = workloads.make_chunkwise_inputs(cfg, B=1, H=8, T=512)
     log("chunkwise determinism")
     a = run_gpu(inp, 64)
@@ -243,7 +243,7 @@ def test_every_output_written(dtype, chunk, dqk, dv, tail):
 
 
 def test_no_state_out():
-    cfg = workloads.CONFIGS["c1"]
+    cfg = workloads.CONFIGS["d128_T2048"]
     inp = workloads.make_chunkwise_inputs(cfg, B=1, H=2, T=256)
     d = to_dev(inp)
     M = _M()

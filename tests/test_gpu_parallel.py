@@ -31,18 +31,18 @@ def _cmp(inp, tol, label, fgate="sigmoid"):
     assert max(e_h, eC, en, em) < tol
 
 
-def test_parallel_c0_fp32():
-    log("parallel c0")
-    _cmp(workloads.make_chunkwise_inputs(workloads.CONFIGS["c0"]), TOL_F32, "c0")
+def test_parallel_tiny_fp32():
+    log("parallel tiny fp32")
+    _cmp(workloads.make_chunkwise_inputs(workloads.CONFIGS["tiny_fp32"]), TOL_F32, "tiny fp32")
 
 
-def test_parallel_c1_bf16():
-    log("parallel c1")
-    _cmp(workloads.make_chunkwise_inputs(workloads.CONFIGS["c1"]), TOL_BF16, "c1")
+def test_parallel_d128_T2048():
+    log("parallel d128 T2048")
+    _cmp(workloads.make_chunkwise_inputs(workloads.CONFIGS["d128_T2048"]), TOL_BF16, "d128 T2048")
 
 
 def test_parallel_state_ragged_T():
-    """Random initial state, c2 distributions, T not a multiple of the 64-token
+    """Random initial state, the d256 T8192 distributions, T not a multiple of the 64-token
     blocks, asymmetric dims."""
     cfg = workloads.Config("par", 5, "bf16", 2, 2, 300, 64, 96, (), (-2.0, 3.0), (4.0, 2.0),
                            (0.0, 1.0), True)
@@ -59,7 +59,7 @@ def test_parallel_fp32_exp_gate():
 
 def test_parallel_matches_chunkwise():
     import mlstm_matrix_memory_chunkwise_amd as M
-    cfg = workloads.CONFIGS["c1"]
+    cfg = workloads.CONFIGS["d128_T2048"]
     inp = workloads.make_chunkwise_inputs(cfg, B=1, H=4, T=512)
     d = to_dev(inp)
     hp, _ = M.mlstm_fwd_parallel(d["q"], d["k"], d["v"], d["i_pre"], d["f_pre"], d["o_pre"])

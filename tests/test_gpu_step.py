@@ -107,18 +107,18 @@ def test_step_bf16_output_gate():
     assert e_h < TOL_BF16_ROUNDED
 
 
-def test_step_full_c3_sampled_heads():
+def test_step_d512_full_sampled_heads():
     """The full decode workload (B=128, H=8, d=512, 256 consecutive in-place
     steps, fp32 o-gate) on the GPU; the oracle follows 6 sampled heads."""
-    cfg = workloads.CONFIGS["c3"]
-    log("step c3 full: generating inputs")
+    cfg = workloads.CONFIGS["step_d512"]
+    log("step d512 full: generating inputs")
     inp = workloads.make_step_inputs(cfg)
     heads = sample_heads(cfg.B, cfg.H, 6, seed=3)
     M = _lib()
     d = to_dev(inp)
     C, n, m = d["C0"], d["n0"], d["m0"]
     hs = []
-    log("step c3 full: 256 GPU steps")
+    log("step d512 full: 256 GPU steps")
     for s in range(cfg.T):
         h, _ = M.mlstm_step(d["q"][s], d["k"][s], d["v"][s], d["i_pre"][s], d["f_pre"][s],
                             d["o_pre"][s], C, n, m, inplace=True)
@@ -129,7 +129,7 @@ def test_step_full_c3_sampled_heads():
     n_gpu = gather_heads(n, heads).cpu()
     m_gpu = gather_heads(m, heads).cpu()
     del d, C, n, m
-    log("step c3 full: oracle on sampled heads")
+    log("step d512 full: oracle on sampled heads")
     sub = {k: (None if v is None else torch.stack([v[:, b, hh] for (b, hh) in heads], dim=1).unsqueeze(1))
            for k, v in inp.items() if k in ("q", "k", "v", "i_pre", "f_pre", "o_pre")}
     sub["C0"] = gather_heads(inp["C0"], heads)
@@ -139,6 +139,6 @@ def test_step_full_c3_sampled_heads():
     e_h = slice_rel_err(h_gpu.permute(1, 0, 2).unsqueeze(0),
                         torch.from_numpy(hr[:, 0]).permute(1, 0, 2).unsqueeze(0))
     eC, en, em = state_errors(C_gpu, n_gpu, m_gpu, Cr, nr, mr)
-    log(f"  c3: h {e_h:.2e} C {eC:.2e} n {en:.2e} m {em:.2e}")
+    log(f"  step d512: h {e_h:.2e} C {eC:.2e} n {en:.2e} m {em:.2e}")
     assert e_h < TOL_BF16_ROUNDED
     assert max(eC, en, em) < TOL_F32

@@ -225,20 +225,20 @@ def _head_from_config(cfg, b, hh, T=None, with_o=True):
     return c
 
 
-def test_quadratic_form_c0():
-    c = _head_from_config(workloads.CONFIGS["c0"], 0, 0)
+def test_quadratic_form_tiny_fp32():
+    c = _head_from_config(workloads.CONFIGS["tiny_fp32"], 0, 0)
     _check_quadratic(c, "sigmoid")
 
 
-def test_quadratic_form_c1_head():
-    """One head of the c1 shape (T=2048, d=128), reduced to B=H=1."""
-    c = _head_from_config(workloads.CONFIGS["c1"], 0, 0)
+def test_quadratic_form_d128_T2048_head():
+    """One head of the d128 T2048 workload, reduced to B=H=1."""
+    c = _head_from_config(workloads.CONFIGS["d128_T2048"], 0, 0)
     _check_quadratic(c, "sigmoid")
 
 
-def test_quadratic_form_c2_distributions_with_state():
-    """c2's gate distributions (i~ ~ N(-2,3)) and random state, T=512."""
-    cfg = workloads.CONFIGS["c2"]
+def test_quadratic_form_d256_distributions_with_state():
+    """The d256 T8192 workload's gate distributions (i~ ~ N(-2,3)) and random state, T=512."""
+    cfg = workloads.CONFIGS["d256_T8192"]
     inp = workloads.make_chunkwise_inputs(cfg, B=1, H=1, T=512)
     # narrow d to keep the test fast while keeping d_qk != d_v
     c = dict(q=inp["q"][0, 0, :, :32].double().numpy(),
@@ -302,7 +302,7 @@ def test_stabilizer_shift_invariance():
 def test_split_resume_is_bitwise(split):
     """Processing T tokens in one call equals two calls with the carried
     (C~, n~, m) state, bit for bit (same operation order)."""
-    cfg = workloads.CONFIGS["c2"]
+    cfg = workloads.CONFIGS["d256_T8192"]
     inp = workloads.make_chunkwise_inputs(cfg, B=2, H=2, T=64)
     f64 = lambda x: None if x is None else x.double().numpy()  # noqa: E731
     a = {kk: f64(vv) for kk, vv in inp.items()}

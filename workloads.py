@@ -8,14 +8,18 @@ two sides always see the same bits.
 The pages train on language-model data and print no layer shapes, so the
 workloads are synthetic tensors shaped like language-model mLSTM layers:
 
-  c0  fp32, B=1, H=1, T=64, d_qk=d_v=16, chunk 16; zero initial state
-  c1  bf16 q/k/v, fp32 gates and state, B=4, H=4, T=2048, d=128, chunk 64
-  c2  bf16, B=8, H=8, T=8192, d=256, chunk 64 and 128; i~ ~ N(-2,3),
-      f~ ~ N(4,2); random initial state N(0,1)
-  c3  decode step, bf16 q/k/v, fp32 state, B=128, H=8, d=512, 256 steps;
-      initial state N(0,1); per-step gates as c0
-  c4  bf16, B=1, H=16, T=65536, d_qk=256, d_v=512, chunk 128; f~ ~ N(6,1),
-      i~ ~ N(0,2); zero initial state
+  tiny_fp32        fp32, B=1, H=1, T=64, d_qk=d_v=16, chunk 16; zero state
+  d128_T2048       bf16 q/k/v, fp32 gates and state, B=4, H=4, T=2048,
+                   d=128, chunk 64
+  d256_T8192       bf16, B=8, H=8, T=8192, d=256, chunk 64 and 128;
+                   i~ ~ N(-2,3), f~ ~ N(4,2); random initial state N(0,1)
+  step_d512        decode step, bf16 q/k/v, fp32 state, B=128, H=8, d=512,
+                   256 steps; initial state N(0,1); per-step gates as
+                   tiny_fp32
+  d256x512_T65536  bf16, B=1, H=16, T=65536, d_qk=256, d_v=512, chunk 128;
+                   f~ ~ N(6,1), i~ ~ N(0,2); zero initial state
+
+The seed index of each (0 to 4, in the order above) fixes its generator.
 
 Recipe (every config): a CPU ``torch.Generator`` seeded with 1000 + index.
 Draw order: q, k, v, i~, f~, o~, then (if the state is random) C0, n0, m0.
@@ -23,7 +27,7 @@ Every draw is float32 ``normal(mean, std)`` (std is the second number).
 k is multiplied by 1/sqrt(d_qk) in float32 before any cast.  For bf16 configs
 q, k, v are then rounded to bfloat16 (round to nearest even); gates, o~ and the
 state stay float32.  The forget gate goes through logsigmoid (sigmoid gate).
-For c3 the state is drawn first, then per step s = 0..S-1 the tuple
+For step_d512 the state is drawn first, then per step s = 0..S-1 the tuple
 (q, k, v, i~, f~, o~), each as one [S,B,H,...] tensor in that order.
 """
 from __future__ import annotations
@@ -67,15 +71,15 @@ class Config:
 
 
 CONFIGS: Dict[str, Config] = {
-    "c0": Config("c0", 0, "f32", 1, 1, 64, 16, 16, (16,), (0.0, 1.0), (3.0, 1.0),
+    "tiny_fp32": Config("tiny_fp32", 0, "f32", 1, 1, 64, 16, 16, (16,), (0.0, 1.0), (3.0, 1.0),
                  (0.0, 1.0), False),
-    "c1": Config("c1", 1, "bf16", 4, 4, 2048, 128, 128, (64,), (0.0, 1.0), (3.0, 1.0),
+    "d128_T2048": Config("d128_T2048", 1, "bf16", 4, 4, 2048, 128, 128, (64,), (0.0, 1.0), (3.0, 1.0),
                  (0.0, 1.0), False),
-    "c2": Config("c2", 2, "bf16", 8, 8, 8192, 256, 256, (64, 128), (-2.0, 3.0),
+    "d256_T8192": Config("d256_T8192", 2, "bf16", 8, 8, 8192, 256, 256, (64, 128), (-2.0, 3.0),
                  (4.0, 2.0), (0.0, 1.0), True),
-    "c3": Config("c3", 3, "bf16", 128, 8, 256, 512, 512, (), (0.0, 1.0), (3.0, 1.0),
+    "step_d512": Config("step_d512", 3, "bf16", 128, 8, 256, 512, 512, (), (0.0, 1.0), (3.0, 1.0),
                  (0.0, 1.0), True, kind="step"),
-    "c4": Config("c4", 4, "bf16", 1, 16, 65536, 256, 512, (128,), (0.0, 2.0),
+    "d256x512_T65536": Config("d256x512_T65536", 4, "bf16", 1, 16, 65536, 256, 512, (128,), (0.0, 2.0),
                  (6.0, 1.0), (0.0, 1.0), False),
 }
 
