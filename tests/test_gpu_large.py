@@ -1,0 +1,63 @@
+"""Problems whose tensors hold more than 2^31 elements: every index past 2^31
+must be formed in 64 bits.  The GPU runs the whole problem; the oracle checks
+the last heads, whose elements all lie beyond 2^31, and the first head."""
+from __future__ import annotations
+
+import pytest
+import torch
+
+import oracle
+import workloads
+from helpers import TOL_BF16, has_gpu, log, slice_rel_err, state_errors
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not has_gpu(), reason="needs a GPU")]
+
+
+def _M():
+    import mlstm_matrix_memory_chunkwise_amd as M
+    return M
+
+
+def test_chunkwise_beyond_2_31_elements():
+    B, H, T, d = 1, 1100, 8192, 256       # q, k, v, h: 2.31e9 elements each
+    assert B * H * T * d > 2 ** 31
+    log(f"large chunkwise B={B} H={H} T={T} d={d}: inputs on the GPU")
+    inp = workloads.make_large_device_inputs(B, H, T, d, d, seed=2311, device="cuda")
+    log("large chunkwise: GPU")
+    h, (C1, n1, m1) = _M().mlstm_fwd_chunkwise(inp["q"], inp["k"], inp["v"], inp["i_pre"],
+                                              inp["f_pre"], None, chunk=64)
+    torch.cuda.synchronize()
+    for heads in (slice(H - 2, H), slice(0, 1)):
+        sl = {k: (None if x is None else x[:, heads].cpu()) for k, x in inp.items()}
+        log(f"large chunkwise: oracle on heads {heads.start}..{heads.stop - 1}")
+        hr, Cr, nr, mr = oracle.recurrent(sl["q"], sl["k"], sl["v"], sl["i_pre"], sl["f_pre"])
+        e_h = slice_rel_err(h[:, heads].cpu(), hr)
+        eC, en, em = state_errors(C1[:, heads].cpu(), n1[:, heads].cpu(), m1[:, heads].cpu(),
+                                  Cr, nr, mr)
+        log(f"  heads {heads.start}..{heads.stop - 1}: h {e_h:.2e} C {eC:.2e} n {en:.2e} "
+            f"m {em:.2e} (tol {TOL_BF16:g})")
+        assert max(e_h, eC, en, em) < TOL_BF16
+
+
+def test_step_beyond_2_31_state_elements():
+    B, H, d = 1025, 8, 512                # C: 2.15e9 elements
+    assert B * H * d * d > 2 ** 31
+    log(f"large step B={B} H={H} d={d}: inputs on the GPU")
+    s = workloads.make_large_device_step(B, H, d, d, seed=2312, device="cuda")
+    # the oracle's copies of the last two heads and the first one, before the in-place update
+    picks = ((B - 1, slice(H - 2, H)), (0, slice(0, 1)))
+    host = [{k: x[b:b + 1, hs].cpu() for k, x in s.items()} for b, hs in picks]
+    log("large step: GPU (in place)")
+    h, (C, n, m) = _M().mlstm_step(s["q"], s["k"], s["v"], s["i_pre"], s["f_pre"], s["o_pre"],
+                                   s["C"], s["n"], s["m"], inplace=True)
+    torch.cuda.synchronize()
+    for (b, hs), x in zip(picks, host):
+        hr, Cr, nr, mr = oracle.step(x["q"], x["k"], x["v"], x["i_pre"], x["f_pre"], x["o_pre"],
+                                     x["C"], x["n"], x["m"])
+        e_h = slice_rel_err(h[b:b + 1, hs].cpu(), hr)
+        eC, en, em = state_errors(C[b:b + 1, hs].cpu(), n[b:b + 1, hs].cpu(), m[b:b + 1, hs].cpu(),
+                                  Cr, nr, mr)
+        log(f"  batch {b} heads {hs.start}..{hs.stop - 1}: h {e_h:.2e} C {eC:.2e} n {en:.2e} "
+            f"m {em:.2e} (tol {TOL_BF16:g})")
+        assert max(e_h, eC, en, em) < TOL_BF16

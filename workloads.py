@@ -149,3 +149,55 @@ def make_step_inputs(cfg: Config, *, B: Optional[int] = None,
     dt = cfg.torch_dtype
     return dict(q=q.to(dt), k=k.to(dt), v=v.to(dt), i_pre=i_pre, f_pre=f_pre,
                 o_pre=o_pre, C0=C0, n0=n0, m0=m0)
+
+
+def make_large_device_inputs(B: int, H: int, T: int, dqk: int, dv: int, seed: int,
+                             device) -> Dict[str, Optional[torch.Tensor]]:
+    """Inputs of a whole-sequence problem too large to draw on the host, drawn
+    on `device` with a device generator seeded with `seed`.  Same recipe as the
+    workloads above otherwise (draw order q, k, v, i~, f~; float32 normal draws;
+    k scaled by 1/sqrt(d_qk) before the cast; q, k, v rounded to bfloat16):
+    q, k, v ~ N(0,1), i~ ~ N(-1, 2), f~ ~ N(3, 1); no output gate and a zero
+    initial state.  A check on the host copies slices of these same tensors."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+
+    def draw(shape, mean, std, scale=1.0, bf16=False):
+        x = torch.empty(shape, dtype=torch.float32, device=device)
+        x.normal_(mean, std, generator=g)
+        if scale != 1.0:
+            x.mul_(scale)
+        return x.to(torch.bfloat16) if bf16 else x
+
+    q = draw((B, H, T, dqk), 0.0, 1.0, bf16=True)
+    k = draw((B, H, T, dqk), 0.0, 1.0, scale=1.0 / math.sqrt(dqk), bf16=True)
+    v = draw((B, H, T, dv), 0.0, 1.0, bf16=True)
+    i_pre = draw((B, H, T), -1.0, 2.0)
+    f_pre = draw((B, H, T), 3.0, 1.0)
+    return dict(q=q, k=k, v=v, i_pre=i_pre, f_pre=f_pre, o_pre=None, C0=None, n0=None, m0=None)
+
+
+def make_large_device_step(B: int, H: int, dqk: int, dv: int, seed: int,
+                           device) -> Dict[str, torch.Tensor]:
+    """One decode step over a state too large to draw on the host: state C~,
+    n~, m ~ N(0,1) drawn first, then q, k, v (bf16, k scaled by 1/sqrt(d_qk)),
+    i~ ~ N(0,1), f~ ~ N(3,1), o~ ~ N(0,1), on `device` with a generator seeded
+    with `seed`."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+
+    def draw(shape, mean, std):
+        x = torch.empty(shape, dtype=torch.float32, device=device)
+        x.normal_(mean, std, generator=g)
+        return x
+
+    C = draw((B, H, dqk, dv), 0.0, 1.0)
+    n = draw((B, H, dqk), 0.0, 1.0)
+    m = draw((B, H), 0.0, 1.0)
+    q = draw((B, H, dqk), 0.0, 1.0).to(torch.bfloat16)
+    k = (draw((B, H, dqk), 0.0, 1.0) / math.sqrt(dqk)).to(torch.bfloat16)
+    v = draw((B, H, dv), 0.0, 1.0).to(torch.bfloat16)
+    i_pre = draw((B, H), 0.0, 1.0)
+    f_pre = draw((B, H), 3.0, 1.0)
+    o_pre = draw((B, H, dv), 0.0, 1.0)
+    return dict(q=q, k=k, v=v, i_pre=i_pre, f_pre=f_pre, o_pre=o_pre, C=C, n=n, m=m)
