@@ -223,8 +223,8 @@ mlstm_status_t mlstm_bwd_chunkwise_workspace_bytes(const mlstm_problem_t* p,
  *   eps:   added to the variance, >= 0 and finite.
  *   y:     [B,H,T,d_v] in h_dtype.  y may be h itself (in place); otherwise
  *          it must not overlap any input.
- * Supported: d_v a multiple of 4, at most 1024; h, o_pre, y, gamma and beta
- * 16-byte aligned.  Arithmetic is float32. */
+ * Supported: d_v a multiple of 4, at most 1024; B*H*T at most 2^32; h,
+ * o_pre, y, gamma and beta 16-byte aligned.  Arithmetic is float32. */
 mlstm_status_t mlstm_groupnorm_ogate(int64_t B, int64_t H, int64_t T, int64_t d_v,
                                      mlstm_dtype_t h_dtype, mlstm_dtype_t o_dtype,
                                      const void* h, const void* o_pre,

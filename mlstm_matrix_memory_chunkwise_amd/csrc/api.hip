@@ -467,8 +467,9 @@ mlstm_status_t mlstm_groupnorm_ogate(int64_t B, int64_t H, int64_t T, int64_t d_
     return fail(MLSTM_ERR_INVALID_ARG, "eps must be finite and >= 0");
   if (d_v % 4 != 0 || d_v > 1024)
     return fail(MLSTM_ERR_UNSUPPORTED, "d_v=%lld: need a multiple of 4, at most 1024", (long long)d_v);
-  if (B * H * T > ((int64_t)1 << 40))
-    return fail(MLSTM_ERR_UNSUPPORTED, "B*H*T=%lld too large", (long long)(B * H * T));
+  // at most 2^32 rows keeps the grid (4 rows or more per workgroup) below 2^31 workgroups
+  if (B * H * T > ((int64_t)1 << 32))
+    return fail(MLSTM_ERR_UNSUPPORTED, "B*H*T=%lld exceeds 2^32", (long long)(B * H * T));
   const size_t n = (size_t)(B * H * T * d_v), sh = dsize(h_dtype), so = dsize(o_dtype);
   // rows move in 16-byte pieces
   const Buf bufs[] = {

@@ -323,6 +323,8 @@ def test_groupnorm_rejections(lib):
     assert gn_call(lib, h=None)[0] == M.MLSTM_ERR_INVALID_ARG
     assert gn_call(lib, y=None)[0] == M.MLSTM_ERR_INVALID_ARG
     assert gn_call(lib, T=0)[0] == M.MLSTM_ERR_INVALID_ARG
+    r, det = gn_call(lib, B=2, H=1 << 16, T=(1 << 15) + 1)
+    assert r == M.MLSTM_ERR_UNSUPPORTED and "2^32" in det
     assert gn_call(lib, hdt=7)[0] == M.MLSTM_ERR_INVALID_ARG
     assert gn_call(lib, eps=-1.0)[0] == M.MLSTM_ERR_INVALID_ARG
     assert gn_call(lib, eps=float("nan"))[0] == M.MLSTM_ERR_INVALID_ARG
