@@ -61,3 +61,46 @@ def test_step_beyond_2_31_state_elements():
         log(f"  batch {b} heads {hs.start}..{hs.stop - 1}: h {e_h:.2e} C {eC:.2e} n {en:.2e} "
             f"m {em:.2e} (tol {TOL_BF16:g})")
         assert max(e_h, eC, en, em) < TOL_BF16
+
+
+def test_block_ops_beyond_2_31_elements():
+    from oracle import block_ops
+    from helpers import TOL_BF16_ROUNDED
+    M = _M()
+    log("large block ops: inputs on the GPU")
+    d = workloads.make_large_device_block_inputs(seed=2313, device="cuda")
+    # group normalization + output gate over h [1, 1100, 8192, 256]
+    assert d["h"].numel() > 2 ** 31
+    log("large group normalization: GPU")
+    y = M.mlstm_groupnorm_ogate(d["h"], d["o_pre"], d["gamma"], d["beta"])
+    torch.cuda.synchronize()
+    for hs, ts in ((slice(1098, 1100), slice(8192 - 64, 8192)), (slice(0, 1), slice(0, 64))):
+        ref = block_ops.groupnorm_ogate(d["h"][:, hs, ts].cpu(), d["o_pre"][:, hs, ts].cpu(),
+                                        d["gamma"][hs].cpu(), d["beta"][hs].cpu())
+        e = slice_rel_err(y[:, hs, ts].cpu(), ref, lead=3)
+        log(f"  heads {hs.start}..{hs.stop - 1} tokens {ts.start}..{ts.stop - 1}: y {e:.2e} "
+            f"(tol {TOL_BF16_ROUNDED:.2e})")
+        assert e < TOL_BF16_ROUNDED
+    del y
+    # causal conv over x [8, 131200, 2048]
+    assert d["x"].numel() > 2 ** 31
+    log("large causal conv: GPU")
+    yc, st = M.mlstm_causal_conv1d(d["x"], d["w"], d["bias"])
+    torch.cuda.synchronize()
+    K = d["w"].shape[1]
+    TX = d["x"].shape[1]
+    for b, ts, cs in ((7, slice(TX - 96, TX), slice(2048 - 64, 2048)),
+                      (0, slice(0, 96), slice(0, 64))):
+        xs = d["x"][b:b + 1, ts, cs].cpu()
+        t0 = ts.start
+        if t0 >= K - 1:
+            state = d["x"][b:b + 1, t0 - K + 1:t0, cs].float().cpu()
+        else:
+            state = None
+        ref, _ = block_ops.causal_conv1d(xs, d["w"][cs].cpu(), d["bias"][cs].cpu(), state)
+        e = slice_rel_err(yc[b:b + 1, ts, cs].cpu(), ref, lead=1)
+        log(f"  batch {b} tokens {ts.start}..{ts.stop - 1} channels {cs.start}..{cs.stop - 1}: "
+            f"y {e:.2e} (tol {TOL_BF16_ROUNDED:.2e})")
+        assert e < TOL_BF16_ROUNDED
+    ref_state = d["x"][7:8, TX - (K - 1):, 2048 - 64:].float().cpu()
+    assert torch.equal(st[7:8, :, 2048 - 64:].cpu(), ref_state)

@@ -201,3 +201,27 @@ def make_large_device_step(B: int, H: int, dqk: int, dv: int, seed: int,
     f_pre = draw((B, H), 3.0, 1.0)
     o_pre = draw((B, H, dv), 0.0, 1.0)
     return dict(q=q, k=k, v=v, i_pre=i_pre, f_pre=f_pre, o_pre=o_pre, C=C, n=n, m=m)
+
+
+def make_large_device_block_inputs(seed: int, device) -> Dict[str, torch.Tensor]:
+    """Block-operation inputs past 2^31 elements, drawn on `device` with a
+    generator seeded with `seed`, in this order: group normalization h
+    [1, 1100, 8192, 256] bf16 ~ N(0,1), o~ float32 ~ N(0,1), gamma ~ N(1, 0.5)
+    and beta ~ N(0, 0.5) [1100, 256]; causal conv x [8, 131200, 2048] bf16
+    ~ N(0,1), w [2048, 4] ~ N(0, 1/2), bias [2048] ~ N(0,1)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+
+    def draw(shape, mean, std, bf16=False):
+        x = torch.empty(shape, dtype=torch.float32, device=device)
+        x.normal_(mean, std, generator=g)
+        return x.to(torch.bfloat16) if bf16 else x
+
+    out = dict(h=draw((1, 1100, 8192, 256), 0.0, 1.0, bf16=True))
+    out["o_pre"] = draw((1, 1100, 8192, 256), 0.0, 1.0)
+    out["gamma"] = draw((1100, 256), 1.0, 0.5)
+    out["beta"] = draw((1100, 256), 0.0, 0.5)
+    out["x"] = draw((8, 131200, 2048), 0.0, 1.0, bf16=True)
+    out["w"] = draw((2048, 4), 0.0, 0.5)
+    out["bias"] = draw((2048,), 0.0, 1.0)
+    return out
