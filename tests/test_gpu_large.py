@@ -104,3 +104,32 @@ def test_block_ops_beyond_2_31_elements():
         assert e < TOL_BF16_ROUNDED
     ref_state = d["x"][7:8, TX - (K - 1):, 2048 - 64:].float().cpu()
     assert torch.equal(st[7:8, :, 2048 - 64:].cpu(), ref_state)
+
+
+def test_backward_beyond_2_31_elements():
+    """Chunk-64 backward (matrix-core passes) with q, k, v, h, dh of 2.31e9
+    elements each and float32 gradients of the same size."""
+    B, H, T, d = 1, 1100, 8192, 256
+    torch.cuda.empty_cache()
+    log(f"large backward B={B} H={H} T={T} d={d}: inputs on the GPU")
+    inp = workloads.make_large_device_inputs(B, H, T, d, d, seed=2314, device="cuda")
+    gin = workloads.make_large_device_grads(B, H, T, d, d, seed=2315, device="cuda")
+    M = _M()
+    log("large backward: GPU forward")
+    h, _ = M.mlstm_fwd_chunkwise(inp["q"], inp["k"], inp["v"], inp["i_pre"], inp["f_pre"], None,
+                                 chunk=64, return_state=False)
+    log("large backward: GPU backward")
+    g = M.mlstm_bwd_chunkwise(inp["q"], inp["k"], inp["v"], inp["i_pre"], inp["f_pre"], None,
+                              None, None, None, h, gin["dh"], gin["dC1"], gin["dn1"], chunk=64)
+    torch.cuda.synchronize()
+    for heads in (slice(H - 2, H), slice(0, 1)):
+        x = {k: (None if t is None else t[:, heads].cpu()) for k, t in {**inp, **gin}.items()}
+        log(f"large backward: oracle on heads {heads.start}..{heads.stop - 1}")
+        r = oracle.backward(x["q"], x["k"], x["v"], x["i_pre"], x["f_pre"], None, None, None, None,
+                            x["dh"], x["dC1"], x["dn1"])
+        errs = {n: slice_rel_err(g[n][:, heads].cpu(), r[n]) for n in ("dq", "dk", "dv", "di", "df",
+                                                                       "dC0", "dn0")}
+        log(f"  heads {heads.start}..{heads.stop - 1}: "
+            + " ".join(f"{k} {v:.1e}" for k, v in errs.items()) + f" (tol {TOL_BF16:g})")
+        bad = {k: v for k, v in errs.items() if not v < TOL_BF16}
+        assert not bad, bad

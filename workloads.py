@@ -225,3 +225,21 @@ def make_large_device_block_inputs(seed: int, device) -> Dict[str, torch.Tensor]
     out["w"] = draw((2048, 4), 0.0, 0.5)
     out["bias"] = draw((2048,), 0.0, 1.0)
     return out
+
+
+def make_large_device_grads(B: int, H: int, T: int, dqk: int, dv: int, seed: int,
+                            device) -> Dict[str, torch.Tensor]:
+    """Output gradients for the backward of a problem from
+    make_large_device_inputs, drawn on `device` with a generator seeded with
+    `seed`: dh [B,H,T,d_v] bf16 ~ N(0,1), then dC1 [B,H,d_qk,d_v] and dn1
+    [B,H,d_qk] float32 ~ N(0,1)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+
+    def draw(shape):
+        x = torch.empty(shape, dtype=torch.float32, device=device)
+        x.normal_(0.0, 1.0, generator=g)
+        return x
+
+    return dict(dh=draw((B, H, T, dv)).to(torch.bfloat16), dC1=draw((B, H, dqk, dv)),
+                dn1=draw((B, H, dqk)))
