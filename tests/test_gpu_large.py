@@ -133,3 +133,24 @@ def test_backward_beyond_2_31_elements():
             + " ".join(f"{k} {v:.1e}" for k, v in errs.items()) + f" (tol {TOL_BF16:g})")
         bad = {k: v for k, v in errs.items() if not v < TOL_BF16}
         assert not bad, bad
+
+
+def test_slstm_beyond_2_31_elements():
+    """sLSTM cell with wx of 2.15e9 elements: 256 sequences of 16400 steps."""
+    from oracle import slstm
+    from helpers import TOL_BF16_ROUNDED
+    B, NH, T, DH = 64, 4, 16400, 128
+    assert B * NH * T * 4 * DH > 2 ** 31
+    torch.cuda.empty_cache()
+    log(f"large sLSTM B={B} NH={NH} T={T} DH={DH}: inputs on the GPU")
+    d = workloads.make_large_device_slstm(B, NH, T, DH, seed=2316, device="cuda")
+    log("large sLSTM: GPU")
+    h, _ = _M().mlstm_slstm_fwd(d["wx"], d["R"], return_state=False)
+    torch.cuda.synchronize()
+    for b, hd in ((B - 1, NH - 1), (0, 0)):
+        log(f"large sLSTM: oracle on batch {b} head {hd}")
+        wx = d["wx"][b:b + 1, hd:hd + 1].cpu()
+        ref, _ = slstm.slstm_forward(wx, d["R"][hd:hd + 1].cpu())
+        e = slice_rel_err(h[b:b + 1, hd:hd + 1].cpu(), ref)
+        log(f"  batch {b} head {hd}: h {e:.2e} (tol {TOL_BF16_ROUNDED:.2e})")
+        assert e < TOL_BF16_ROUNDED

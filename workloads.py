@@ -243,3 +243,21 @@ def make_large_device_grads(B: int, H: int, T: int, dqk: int, dv: int, seed: int
 
     return dict(dh=draw((B, H, T, dv)).to(torch.bfloat16), dC1=draw((B, H, dqk, dv)),
                 dn1=draw((B, H, dqk)))
+
+
+def make_large_device_slstm(B: int, NH: int, T: int, DH: int, seed: int,
+                            device) -> Dict[str, torch.Tensor]:
+    """sLSTM inputs past 2^31 elements, drawn on `device` with a generator
+    seeded with `seed`: wx [B,NH,T,4,DH] float32 ~ N(0,1) with the input gate
+    row ~ N(-1, 1) and the forget gate row ~ N(3, 1), rounded to bfloat16;
+    then R [NH,4,DH,DH] float32 ~ N(0, 0.5/sqrt(DH)); zero initial state."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    wx = torch.empty((B, NH, T, 4, DH), dtype=torch.float32, device=device)
+    wx.normal_(0.0, 1.0, generator=g)
+    wx[:, :, :, 0].add_(-1.0)
+    wx[:, :, :, 1].add_(3.0)
+    wx = wx.to(torch.bfloat16)
+    R = torch.empty((NH, 4, DH, DH), dtype=torch.float32, device=device)
+    R.normal_(0.0, 0.5 / math.sqrt(DH), generator=g)
+    return dict(wx=wx, R=R)
