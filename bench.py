@@ -228,8 +228,9 @@ def main():
     ap.add_argument("--profile-workload", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: every (batch, head) is independent and this "
-              "build runs on a single MI355X; run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: every (batch, head) is independent, so the "
+              "workload shards over GPUs without communication and the per-GPU rate is the "
+              "one-GPU rate; run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     if args.profile_workload:
         profile_workload()
