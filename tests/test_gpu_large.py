@@ -154,3 +154,26 @@ def test_slstm_beyond_2_31_elements():
         e = slice_rel_err(h[b:b + 1, hd:hd + 1].cpu(), ref)
         log(f"  batch {b} head {hd}: h {e:.2e} (tol {TOL_BF16_ROUNDED:.2e})")
         assert e < TOL_BF16_ROUNDED
+
+
+def test_parallel_beyond_2_31_elements():
+    """Quadratic (parallel) form with q, k, v, h of 2.15e9 elements each: many
+    short heads keep its O(T^2) work small."""
+    B, H, T, d = 1, 16400, 512, 256
+    assert B * H * T * d > 2 ** 31
+    torch.cuda.empty_cache()
+    log(f"large parallel B={B} H={H} T={T} d={d}: inputs on the GPU")
+    inp = workloads.make_large_device_inputs(B, H, T, d, d, seed=2317, device="cuda")
+    log("large parallel: GPU")
+    h, (C1, n1, m1) = _M().mlstm_fwd_parallel(inp["q"], inp["k"], inp["v"], inp["i_pre"],
+                                             inp["f_pre"])
+    torch.cuda.synchronize()
+    for heads in (slice(H - 2, H), slice(0, 1)):
+        sl = {k: (None if x is None else x[:, heads].cpu()) for k, x in inp.items()}
+        hr, Cr, nr, mr = oracle.recurrent(sl["q"], sl["k"], sl["v"], sl["i_pre"], sl["f_pre"])
+        e_h = slice_rel_err(h[:, heads].cpu(), hr)
+        eC, en, em = state_errors(C1[:, heads].cpu(), n1[:, heads].cpu(), m1[:, heads].cpu(),
+                                  Cr, nr, mr)
+        log(f"  heads {heads.start}..{heads.stop - 1}: h {e_h:.2e} C {eC:.2e} n {en:.2e} "
+            f"m {em:.2e} (tol {TOL_BF16:g})")
+        assert max(e_h, eC, en, em) < TOL_BF16
