@@ -41,6 +41,16 @@
  * caller's next synchronization.  NaN or Inf in the inputs propagate to the
  * outputs without an error code.  Supported range: |m| <= 80 (exp(-m) stays
  * finite in float32).
+ *
+ * Empty inputs.  Sizes may be 0 (negative sizes, and zero head or feature
+ * dimensions, are MLSTM_ERR_INVALID_ARG).  With no heads (B*H = 0), or no
+ * rows for the group normalization, a call returns MLSTM_OK and enqueues
+ * nothing.  With T = 0 the per-token pointers may be NULL and nothing is
+ * computed for them: a final state that is asked for equals the initial state
+ * (zeros without one; for the convolution, the carried window), and the
+ * backward gives dC0 = dC1, dn0 = dn1 (zeros without them) and
+ * dm0 = <dC1, C~0> + <dn1, n~0> (zero without an initial state).  Those
+ * copies are enqueued on `stream` like any other work.
  */
 #ifndef MLSTM_H
 #define MLSTM_H

@@ -49,8 +49,9 @@ size_t dsize(int32_t dt) { return dt == MLSTM_BF16 ? 2 : 4; }
 
 mlstm_status_t check_problem(const mlstm_problem_t* p, bool need_T) {
   if (!p) return fail(MLSTM_ERR_INVALID_ARG, "problem descriptor is NULL");
-  if (p->B <= 0 || p->H <= 0 || p->d_qk <= 0 || p->d_v <= 0 || (need_T && p->T <= 0))
-    return fail(MLSTM_ERR_INVALID_ARG, "sizes must be positive (B=%lld H=%lld T=%lld d_qk=%lld d_v=%lld)",
+  if (p->B < 0 || p->H < 0 || p->d_qk <= 0 || p->d_v <= 0 || (need_T && p->T < 0))
+    return fail(MLSTM_ERR_INVALID_ARG,
+                "sizes must be non-negative and d_qk, d_v positive (B=%lld H=%lld T=%lld d_qk=%lld d_v=%lld)",
                 (long long)p->B, (long long)p->H, (long long)p->T, (long long)p->d_qk,
                 (long long)p->d_v);
   if (p->qkv_dtype != MLSTM_F32 && p->qkv_dtype != MLSTM_BF16)
@@ -193,23 +194,65 @@ mlstm_status_t device_status(hipError_t e, const char* what) {
   return ok();
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* mlstm_version(void) { return "mlstm-gfx950 0.1.0"; }
-
-const char* mlstm_status_string(mlstm_status_t s) {
-  switch (s) {
-    case MLSTM_OK: return "ok";
-    case MLSTM_ERR_INVALID_ARG: return "invalid argument";
-    case MLSTM_ERR_UNSUPPORTED: return "unsupported problem";
-    case MLSTM_ERR_DEVICE: return "device error";
-  }
-  return "unknown status";
+// dst <- src (`bytes`, a multiple of 4), or zeros when src is NULL; nothing
+// when dst is NULL.  Zeros come from a fill kernel, not a memset node.
+hipError_t copy_or_zero(void* dst, const void* src, size_t bytes, hipStream_t st) {
+  if (!dst || bytes == 0) return hipSuccess;
+  if (src) return hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, st);
+  const int64_t words = static_cast<int64_t>(bytes / 4);
+  return mlstm::launch_fill_words(static_cast<uint32_t*>(dst), 1, words, 0, words, 0u, st);
 }
 
-const char* mlstm_last_error_detail(void) { return g_detail; }
+// A state triple/quadruple given all-or-none; the copies of an empty
+// sequence's pass-through state must not overlap their sources.
+struct StateBufs {
+  const char* names[4];
+  const void* in[4];
+  void* out[4];
+  size_t bytes[4];
+  int n;
+};
+
+mlstm_status_t pass_state(const StateBufs& sb, const char* what, hipStream_t st) {
+  int nin = 0, nout = 0;
+  for (int i = 0; i < sb.n; ++i) {
+    nin += sb.in[i] != nullptr;
+    nout += sb.out[i] != nullptr;
+  }
+  if (nin != 0 && nin != sb.n)
+    return fail(MLSTM_ERR_INVALID_ARG, "%s: initial state must be given whole or not at all", what);
+  if (nout != 0 && nout != sb.n)
+    return fail(MLSTM_ERR_INVALID_ARG, "%s: final state must be given whole or not at all", what);
+  for (int i = 0; i < sb.n; ++i) {
+    const size_t al = 4;   // copied or filled as 32-bit words only
+    if ((sb.in[i] && (reinterpret_cast<uintptr_t>(sb.in[i]) & (al - 1))) ||
+        (sb.out[i] && (reinterpret_cast<uintptr_t>(sb.out[i]) & (al - 1))))
+      return fail(MLSTM_ERR_INVALID_ARG, "%s: %s is not %zu-byte aligned", what, sb.names[i], al);
+    for (int j = 0; j < sb.n; ++j) {
+      const Buf o{sb.names[i], sb.out[i], sb.bytes[i], 4};
+      if (overlaps(o, Buf{"in", sb.in[j], sb.bytes[j], 4}) ||
+          (j != i && overlaps(o, Buf{"out", sb.out[j], sb.bytes[j], 4})))
+        return fail(MLSTM_ERR_INVALID_ARG, "%s: final state %s overlaps another state buffer", what,
+                    sb.names[i]);
+    }
+  }
+  hipError_t e = hipSuccess;
+  for (int i = 0; i < sb.n && e == hipSuccess; ++i) e = copy_or_zero(sb.out[i], sb.in[i], sb.bytes[i], st);
+  return device_status(e, what);
+}
+
+// A whole-sequence call with B*H = 0 does nothing; with T = 0 its final
+// state is its initial state (zeros without one).
+mlstm_status_t seq_empty(const mlstm_problem_t* p, const float* C0, const float* n0,
+                         const float* m0, float* C1, float* n1, float* m1, void* stream) {
+  const size_t BH = (size_t)(p->B * p->H), dqk = (size_t)p->d_qk, dv = (size_t)p->d_v;
+  if (BH == 0) return ok();
+  const StateBufs sb{{"C1", "n1", "m1", ""}, {C0, n0, m0, nullptr}, {C1, n1, m1, nullptr},
+                     {BH * dqk * dv * 4, BH * dqk * 4, BH * 4, 0}, 3};
+  return pass_state(sb, "empty sequence", static_cast<hipStream_t>(stream));
+}
+
+bool seq_is_empty(const mlstm_problem_t* p) { return p->B * p->H == 0 || p->T == 0; }
 
 // How a chunkwise call runs.  When T is not a multiple of the chunk and an
 // MFMA kernel covers the shape, that kernel runs the first Tm = T - (T % chunk)
@@ -238,56 +281,6 @@ FwdPlan fwd_plan(const mlstm::SeqArgs& a, int64_t chunk) {
   const size_t mid = f.tail ? 4 * BH * (static_cast<size_t>(a.dqk) * a.dv + a.dqk + 1) : 0;
   f.need = f.tail ? f.mid_off + mid : mfma_ws;
   return f;
-}
-
-mlstm_status_t mlstm_fwd_chunkwise_workspace_bytes(const mlstm_problem_t* p, int64_t chunk,
-                                                   size_t* bytes) {
-  if (!bytes) return fail(MLSTM_ERR_INVALID_ARG, "bytes is NULL");
-  mlstm_status_t s = check_problem(p, true);
-  if (s != MLSTM_OK) return s;
-  s = check_chunk(p, chunk);
-  if (s != MLSTM_OK) return s;
-  *bytes = fwd_plan(problem_args(p), chunk).need;
-  return ok();
-}
-
-mlstm_status_t mlstm_fwd_chunkwise(const mlstm_problem_t* p, int64_t chunk, const void* q,
-                                   const void* k, const void* v, const float* i_pre,
-                                   const float* f_pre, const void* o_pre, const float* C0,
-                                   const float* n0, const float* m0, void* h, float* C1,
-                                   float* n1, float* m1, void* workspace,
-                                   size_t workspace_bytes, void* stream) {
-  mlstm::SeqArgs a;
-  mlstm_status_t s = check_seq(p, q, k, v, i_pre, f_pre, o_pre, C0, n0, m0, h, C1, n1, m1, &a);
-  if (s != MLSTM_OK) return s;
-  s = check_chunk(p, chunk);
-  if (s != MLSTM_OK) return s;
-  const FwdPlan f = fwd_plan(a, chunk);
-  if (workspace_bytes < f.need || (f.need > 0 && !workspace))
-    return fail(MLSTM_ERR_INVALID_ARG, "workspace of %zu bytes given, %zu needed",
-                workspace_bytes, f.need);
-  if (f.need > 0 && !aligned16(workspace))
-    return fail(MLSTM_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
-  s = check_seq_workspace(p, q, k, v, i_pre, f_pre, o_pre, C0, n0, m0, h, C1, n1, m1, workspace,
-                          f.need);
-  if (s != MLSTM_OK) return s;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if (!f.mfma) return device_status(mlstm::launch_chunk_valu(a, chunk, st), "chunkwise (valu)");
-  if (!f.tail)
-    return device_status(mlstm::launch_chunk_mfma(a, chunk, workspace, st), "chunkwise (mfma)");
-  const size_t BH = static_cast<size_t>(a.B * a.H);
-  float* midC = reinterpret_cast<float*>(static_cast<char*>(workspace) + f.mid_off);
-  float* midn = midC + BH * a.dqk * a.dv;
-  float* midm = midn + BH * a.dqk;
-  mlstm::SeqArgs head = a;   // tokens 0 .. Tm-1 on MFMA, state into the workspace
-  head.T = f.Tm;
-  head.C1 = midC; head.n1 = midn; head.m1 = midm;
-  s = device_status(mlstm::launch_chunk_mfma(head, chunk, workspace, st), "chunkwise (mfma)");
-  if (s != MLSTM_OK) return s;
-  mlstm::SeqArgs tail = a;   // tokens Tm .. T-1 from that state
-  tail.t0 = f.Tm;
-  tail.C0 = midC; tail.n0 = midn; tail.m0 = midm;
-  return device_status(mlstm::launch_chunk_valu(tail, chunk, st), "chunkwise tail (valu)");
 }
 
 // Backward of a sequence whose length T is not a multiple of the chunk: the
@@ -329,6 +322,109 @@ mlstm::BwdArgs bwd_padded_args(const mlstm_problem_t* p, int64_t chunk, const Bw
   return a;
 }
 
+// Backward of an empty sequence: dC0 = dC1, dn0 = dn1 and
+// dm0 = <dC1, C~0> + <dn1, n~0>, with zeros for what is not given.
+mlstm_status_t bwd_empty(const mlstm_problem_t* p, int64_t chunk, const float* C0,
+                         const float* n0, const float* m0, const float* dC1, const float* dn1,
+                         float* dC0, float* dn0, float* dm0, void* stream) {
+  const int in_state = (C0 != nullptr) + (n0 != nullptr) + (m0 != nullptr);
+  if (in_state != 0 && in_state != 3)
+    return fail(MLSTM_ERR_INVALID_ARG, "initial state must be all of C0, n0, m0 or none");
+  if ((dC1 != nullptr) != (dn1 != nullptr))
+    return fail(MLSTM_ERR_INVALID_ARG, "final-state gradient must be both of dC1, dn1 or none");
+  const size_t BH = (size_t)(p->B * p->H), dqk = (size_t)p->d_qk, dvv = (size_t)p->d_v;
+  const Buf bufs[] = {
+      {"C0", C0, BH * dqk * dvv * 4, 4}, {"n0", n0, BH * dqk * 4, 4}, {"m0", m0, BH * 4, 4},
+      {"dC1", dC1, BH * dqk * dvv * 4, 4}, {"dn1", dn1, BH * dqk * 4, 4},
+      {"dC0", dC0, BH * dqk * dvv * 4, 4}, {"dn0", dn0, BH * dqk * 4, 4}, {"dm0", dm0, BH * 4, 4}};
+  const int nb = sizeof(bufs) / sizeof(bufs[0]);
+  for (int i = 0; i < nb; ++i)
+    if (bufs[i].p && !aligned(bufs[i]))
+      return fail(MLSTM_ERR_INVALID_ARG, "%s is not 4-byte aligned", bufs[i].name);
+  for (int o = 5; o < nb; ++o)
+    for (int i = 0; i < nb; ++i)
+      if (i != o && overlaps(bufs[o], bufs[i]))
+        return fail(MLSTM_ERR_INVALID_ARG, "%s overlaps %s", bufs[o].name, bufs[i].name);
+  mlstm::BwdArgs a = bwd_problem_args(p, chunk);
+  a.C0 = C0; a.n0 = n0; a.m0 = m0; a.dC1 = dC1; a.dn1 = dn1;
+  a.dC0 = dC0; a.dn0 = dn0; a.dm0 = dm0;
+  return device_status(mlstm::launch_bwd_empty(a, static_cast<hipStream_t>(stream)),
+                       "backward of an empty sequence");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mlstm_version(void) { return "mlstm-gfx950 0.1.0"; }
+
+const char* mlstm_status_string(mlstm_status_t s) {
+  switch (s) {
+    case MLSTM_OK: return "ok";
+    case MLSTM_ERR_INVALID_ARG: return "invalid argument";
+    case MLSTM_ERR_UNSUPPORTED: return "unsupported problem";
+    case MLSTM_ERR_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+const char* mlstm_last_error_detail(void) { return g_detail; }
+
+mlstm_status_t mlstm_fwd_chunkwise_workspace_bytes(const mlstm_problem_t* p, int64_t chunk,
+                                                   size_t* bytes) {
+  if (!bytes) return fail(MLSTM_ERR_INVALID_ARG, "bytes is NULL");
+  mlstm_status_t s = check_problem(p, true);
+  if (s != MLSTM_OK) return s;
+  s = check_chunk(p, chunk);
+  if (s != MLSTM_OK) return s;
+  *bytes = fwd_plan(problem_args(p), chunk).need;
+  return ok();
+}
+
+mlstm_status_t mlstm_fwd_chunkwise(const mlstm_problem_t* p, int64_t chunk, const void* q,
+                                   const void* k, const void* v, const float* i_pre,
+                                   const float* f_pre, const void* o_pre, const float* C0,
+                                   const float* n0, const float* m0, void* h, float* C1,
+                                   float* n1, float* m1, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  if (p && check_problem(p, true) == MLSTM_OK && seq_is_empty(p)) {
+    const mlstm_status_t sc = check_chunk(p, chunk);
+    if (sc != MLSTM_OK) return sc;
+    return seq_empty(p, C0, n0, m0, C1, n1, m1, stream);
+  }
+  mlstm::SeqArgs a;
+  mlstm_status_t s = check_seq(p, q, k, v, i_pre, f_pre, o_pre, C0, n0, m0, h, C1, n1, m1, &a);
+  if (s != MLSTM_OK) return s;
+  s = check_chunk(p, chunk);
+  if (s != MLSTM_OK) return s;
+  const FwdPlan f = fwd_plan(a, chunk);
+  if (workspace_bytes < f.need || (f.need > 0 && !workspace))
+    return fail(MLSTM_ERR_INVALID_ARG, "workspace of %zu bytes given, %zu needed",
+                workspace_bytes, f.need);
+  if (f.need > 0 && !aligned16(workspace))
+    return fail(MLSTM_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  s = check_seq_workspace(p, q, k, v, i_pre, f_pre, o_pre, C0, n0, m0, h, C1, n1, m1, workspace,
+                          f.need);
+  if (s != MLSTM_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (!f.mfma) return device_status(mlstm::launch_chunk_valu(a, chunk, st), "chunkwise (valu)");
+  if (!f.tail)
+    return device_status(mlstm::launch_chunk_mfma(a, chunk, workspace, st), "chunkwise (mfma)");
+  const size_t BH = static_cast<size_t>(a.B * a.H);
+  float* midC = reinterpret_cast<float*>(static_cast<char*>(workspace) + f.mid_off);
+  float* midn = midC + BH * a.dqk * a.dv;
+  float* midm = midn + BH * a.dqk;
+  mlstm::SeqArgs head = a;   // tokens 0 .. Tm-1 on MFMA, state into the workspace
+  head.T = f.Tm;
+  head.C1 = midC; head.n1 = midn; head.m1 = midm;
+  s = device_status(mlstm::launch_chunk_mfma(head, chunk, workspace, st), "chunkwise (mfma)");
+  if (s != MLSTM_OK) return s;
+  mlstm::SeqArgs tail = a;   // tokens Tm .. T-1 from that state
+  tail.t0 = f.Tm;
+  tail.C0 = midC; tail.n0 = midn; tail.m0 = midm;
+  return device_status(mlstm::launch_chunk_valu(tail, chunk, st), "chunkwise tail (valu)");
+}
+
 mlstm_status_t mlstm_bwd_chunkwise_workspace_bytes(const mlstm_problem_t* p, int64_t chunk,
                                                    size_t* bytes) {
   if (!bytes) return fail(MLSTM_ERR_INVALID_ARG, "bytes is NULL");
@@ -336,6 +432,10 @@ mlstm_status_t mlstm_bwd_chunkwise_workspace_bytes(const mlstm_problem_t* p, int
   if (s != MLSTM_OK) return s;
   s = check_bwd_shape(p, chunk);
   if (s != MLSTM_OK) return s;
+  if (seq_is_empty(p)) {
+    *bytes = 0;
+    return ok();
+  }
   const BwdPad pad = bwd_pad_plan(p, chunk);
   *bytes = pad.bytes + mlstm::bwd_workspace(bwd_padded_args(p, chunk, pad), nullptr);
   return ok();
@@ -353,6 +453,8 @@ mlstm_status_t mlstm_bwd_chunkwise(const mlstm_problem_t* p, int64_t chunk, cons
   if (s != MLSTM_OK) return s;
   s = check_bwd_shape(p, chunk);
   if (s != MLSTM_OK) return s;
+  if (p->B * p->H == 0) return ok();
+  if (p->T == 0) return bwd_empty(p, chunk, C0, n0, m0, dC1, dn1, dC0, dn0, dm0, stream);
   if (!q || !k || !v || !i_pre || !f_pre || !h || !dh || !dq || !dk || !dv || !di || !df)
     return fail(MLSTM_ERR_INVALID_ARG,
                 "q, k, v, i_pre, f_pre, h, dh, dq, dk, dv, di and df are required");
@@ -457,11 +559,13 @@ mlstm_status_t mlstm_groupnorm_ogate(int64_t B, int64_t H, int64_t T, int64_t d_
                                      const void* h, const void* o_pre,
                                      const float* gamma, const float* beta, float eps,
                                      void* y, void* stream) {
-  if (B <= 0 || H <= 0 || T <= 0 || d_v <= 0)
-    return fail(MLSTM_ERR_INVALID_ARG, "sizes must be positive (B=%lld H=%lld T=%lld d_v=%lld)",
+  if (B < 0 || H < 0 || T < 0 || d_v <= 0)
+    return fail(MLSTM_ERR_INVALID_ARG,
+                "sizes must be non-negative and d_v positive (B=%lld H=%lld T=%lld d_v=%lld)",
                 (long long)B, (long long)H, (long long)T, (long long)d_v);
   if ((h_dtype != MLSTM_F32 && h_dtype != MLSTM_BF16) || (o_dtype != MLSTM_F32 && o_dtype != MLSTM_BF16))
     return fail(MLSTM_ERR_INVALID_ARG, "unknown dtype (h %d, o %d)", h_dtype, o_dtype);
+  if (B * H * T == 0) return ok();   // no rows
   if (!h || !y) return fail(MLSTM_ERR_INVALID_ARG, "h and y are required");
   if (!(eps >= 0.0f) || eps == __builtin_inff())
     return fail(MLSTM_ERR_INVALID_ARG, "eps must be finite and >= 0");
@@ -496,11 +600,20 @@ mlstm_status_t mlstm_causal_conv1d(int64_t B, int64_t T, int64_t C, int64_t K,
                                    mlstm_dtype_t dtype, const void* x, const float* w,
                                    const float* bias, const float* state_in, void* y,
                                    float* state_out, void* stream) {
-  if (B <= 0 || T <= 0 || C <= 0 || K <= 0)
-    return fail(MLSTM_ERR_INVALID_ARG, "sizes must be positive (B=%lld T=%lld C=%lld K=%lld)",
+  if (B < 0 || T < 0 || C <= 0 || K <= 0)
+    return fail(MLSTM_ERR_INVALID_ARG,
+                "sizes must be non-negative and C, K positive (B=%lld T=%lld C=%lld K=%lld)",
                 (long long)B, (long long)T, (long long)C, (long long)K);
   if (dtype != MLSTM_F32 && dtype != MLSTM_BF16)
     return fail(MLSTM_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (B == 0) return ok();
+  if (T == 0) {   // no tokens: the carried window passes through
+    if (K > 8) return fail(MLSTM_ERR_UNSUPPORTED, "K=%lld: at most 8", (long long)K);
+    const size_t ns = (size_t)(B * (K - 1) * C) * 4;
+    const StateBufs sb{{"state_out", "", "", ""}, {state_in, nullptr, nullptr, nullptr},
+                       {state_out, nullptr, nullptr, nullptr}, {ns, 0, 0, 0}, 1};
+    return pass_state(sb, "causal conv with T = 0", static_cast<hipStream_t>(stream));
+  }
   if (!x || !w || !y) return fail(MLSTM_ERR_INVALID_ARG, "x, w and y are required");
   if (K > 8) return fail(MLSTM_ERR_UNSUPPORTED, "K=%lld: at most 8", (long long)K);
   const int64_t ve = dtype == MLSTM_BF16 ? 8 : 4;
@@ -535,13 +648,21 @@ mlstm_status_t mlstm_slstm_fwd(const mlstm_slstm_problem_t* p, const void* wx, c
                                const float* h0, void* h, float* c1, float* n1, float* m1,
                                float* h1, void* stream) {
   if (!p) return fail(MLSTM_ERR_INVALID_ARG, "problem descriptor is NULL");
-  if (p->B <= 0 || p->NH <= 0 || p->T <= 0 || p->DH <= 0)
-    return fail(MLSTM_ERR_INVALID_ARG, "sizes must be positive (B=%lld NH=%lld T=%lld DH=%lld)",
+  if (p->B < 0 || p->NH < 0 || p->T < 0 || p->DH <= 0)
+    return fail(MLSTM_ERR_INVALID_ARG,
+                "sizes must be non-negative and DH positive (B=%lld NH=%lld T=%lld DH=%lld)",
                 (long long)p->B, (long long)p->NH, (long long)p->T, (long long)p->DH);
   if (p->x_dtype != MLSTM_F32 && p->x_dtype != MLSTM_BF16)
     return fail(MLSTM_ERR_INVALID_ARG, "unknown x_dtype %d", p->x_dtype);
   if (p->fgate != MLSTM_FGATE_SIGMOID && p->fgate != MLSTM_FGATE_EXP)
     return fail(MLSTM_ERR_INVALID_ARG, "unknown fgate %d", p->fgate);
+  if (p->B * p->NH == 0) return ok();
+  if (p->T == 0) {   // no steps: the final state is the initial one (zeros without it)
+    const size_t stb = (size_t)(p->B * p->NH * p->DH) * 4;
+    const StateBufs sb{{"c1", "n1", "m1", "h1"}, {c0, n0, m0, h0}, {c1, n1, m1, h1},
+                       {stb, stb, stb, stb}, 4};
+    return pass_state(sb, "sLSTM with T = 0", static_cast<hipStream_t>(stream));
+  }
   if (!wx || !R || !h) return fail(MLSTM_ERR_INVALID_ARG, "wx, R and h are required");
   const int in_state = (c0 != nullptr) + (n0 != nullptr) + (m0 != nullptr) + (h0 != nullptr);
   if (in_state != 0 && in_state != 4)
@@ -591,6 +712,8 @@ mlstm_status_t mlstm_fwd_parallel(const mlstm_problem_t* p, const void* q, const
                                   const void* o_pre, const float* C0, const float* n0,
                                   const float* m0, void* h, float* C1, float* n1, float* m1,
                                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (p && check_problem(p, true) == MLSTM_OK && seq_is_empty(p))
+    return seq_empty(p, C0, n0, m0, C1, n1, m1, stream);
   mlstm::SeqArgs a;
   mlstm_status_t s = check_seq(p, q, k, v, i_pre, f_pre, o_pre, C0, n0, m0, h, C1, n1, m1, &a);
   if (s != MLSTM_OK) return s;
@@ -612,6 +735,7 @@ mlstm_status_t mlstm_step(const mlstm_problem_t* p, const void* q, const void* k
                           float* C_out, float* n_out, float* m_out, void* h, void* stream) {
   mlstm_status_t s = check_problem(p, false);
   if (s != MLSTM_OK) return s;
+  if (p->B * p->H == 0) return ok();   // no heads: nothing to do
   if (!q || !k || !v || !i_pre || !f_pre || !C_in || !n_in || !m_in || !C_out || !n_out ||
       !m_out || !h)
     return fail(MLSTM_ERR_INVALID_ARG,

@@ -648,6 +648,37 @@ __global__ __launch_bounds__(NTB) void fill_words_kernel(uint32_t* base, int64_t
 }
 }  // namespace
 
+namespace {
+// Backward of an empty sequence (T = 0), one workgroup per head: the memory
+// gradients pass through (dC0 = dC1, dn0 = dn1; zeros without them) and
+// dm0 = <dC1, C~0> + <dn1, n~0> (zero without an initial state).
+__global__ __launch_bounds__(NTB) void bwd_empty_kernel(BwdArgs a) {
+  __shared__ float sRed[NTB / 64];
+  const int tid = threadIdx.x;
+  const int64_t bh = blockIdx.x, S = a.dqk * a.dv;
+  float acc = 0.0f;
+  for (int64_t e = tid; e < S; e += NTB) {
+    const float gC = a.dC1 ? a.dC1[bh * S + e] : 0.0f;
+    if (a.dC0) a.dC0[bh * S + e] = gC;
+    if (a.C0) acc += gC * a.C0[bh * S + e];
+  }
+  for (int64_t e = tid; e < a.dqk; e += NTB) {
+    const float gn = a.dn1 ? a.dn1[bh * a.dqk + e] : 0.0f;
+    if (a.dn0) a.dn0[bh * a.dqk + e] = gn;
+    if (a.C0) acc += gn * a.n0[bh * a.dqk + e];
+  }
+  acc = block_sum(acc, sRed);
+  if (tid == 0 && a.dm0) a.dm0[bh] = acc;
+}
+}  // namespace
+
+hipError_t launch_bwd_empty(const BwdArgs& a, hipStream_t st) {
+  const int64_t BH = a.B * a.H;
+  if (BH <= 0) return hipSuccess;
+  bwd_empty_kernel<<<static_cast<unsigned>(BH), NTB, 0, st>>>(a);
+  return hipGetLastError();
+}
+
 hipError_t launch_fill_words(uint32_t* base, int64_t rows, int64_t pitch, int64_t off, int64_t count,
                              uint32_t value, hipStream_t st) {
   const int64_t n = rows * count;

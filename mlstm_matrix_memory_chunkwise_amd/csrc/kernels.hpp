@@ -121,6 +121,8 @@ bool bwd_supported(const BwdArgs& a);
 int bwd_tile_columns(const BwdArgs& a);
 size_t bwd_workspace(const BwdArgs& a, size_t offsets[8]);
 hipError_t launch_bwd(BwdArgs a, void* ws, hipStream_t stream);
+// Backward of a sequence of T = 0 tokens: state gradients only.
+hipError_t launch_bwd_empty(const BwdArgs& a, hipStream_t stream);
 // words [off, off + count) of each of `rows` rows (row pitch `pitch` 32-bit
 // words) set to `value`; pads sequences for the backward pass
 hipError_t launch_fill_words(uint32_t* base, int64_t rows, int64_t pitch, int64_t off, int64_t count,

@@ -26,7 +26,7 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(mlstm_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(mlstm_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_entry_points():
@@ -40,6 +40,18 @@ def test_header_declares_the_entry_points():
 def test_library_exports_every_declared_symbol(lib):
     for n in declared_functions():
         assert hasattr(lib, n), f"{n} not exported"
+
+
+def test_library_exports_nothing_else():
+    """The only C-linkage functions of the library are the declared entry
+    points (C++ helpers carry mangled names; the HIP runtime adds its
+    per-module ids)."""
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", M.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    names = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    plain = {n for n in names if not n.startswith("_Z") and not n.startswith("__hip_cuid")}
+    assert plain == set(declared_functions()), plain ^ set(declared_functions())
 
 
 def test_header_compiles_as_c(tmp_path):
@@ -99,12 +111,37 @@ def test_chunkwise_rejects_partial_state(lib):
     assert r == M.MLSTM_ERR_INVALID_ARG and "final state" in det
 
 
-@pytest.mark.parametrize("field,value", [("B", 0), ("H", -1), ("T", 0), ("d_qk", 0), ("d_v", 0)])
+@pytest.mark.parametrize("field,value", [("B", -1), ("H", -1), ("T", -1), ("d_qk", 0), ("d_v", 0)])
 def test_chunkwise_rejects_bad_sizes(lib, field, value):
     p = P()
     setattr(p, field, value)
     r, _ = chunk_call(lib, p)
     assert r == M.MLSTM_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("field", ["B", "H", "T"])
+def test_empty_sequences_are_no_ops(lib, field):
+    """B*H = 0 or T = 0: nothing to compute, every per-token pointer may be
+    NULL, and without state pointers nothing is enqueued (so this runs without
+    a GPU)."""
+    p = P()
+    setattr(p, field, 0)
+    none = [None] * 13
+    assert lib.mlstm_fwd_chunkwise(ctypes.byref(p), 16, *none, None, 0, None) == 0
+    assert lib.mlstm_fwd_parallel(ctypes.byref(p), *none, None, 0, None) == 0
+    n = ctypes.c_size_t(7)
+    assert lib.mlstm_fwd_chunkwise_workspace_bytes(ctypes.byref(p), 64, ctypes.byref(n)) == 0
+    assert n.value == 0
+    assert lib.mlstm_bwd_chunkwise_workspace_bytes(ctypes.byref(p), 16, ctypes.byref(n)) == 0
+    assert n.value == 0
+    if field != "T":   # no heads: the backward and the step do nothing either
+        assert lib.mlstm_bwd_chunkwise(ctypes.byref(p), 16, *([None] * 22), None, 0, None) == 0
+        assert lib.mlstm_step(ctypes.byref(p), *([None] * 14), None) == 0
+    # partial state is still an error
+    r = lib.mlstm_fwd_chunkwise(ctypes.byref(p), 16, *([None] * 6), ctypes.c_void_p(FAKE),
+                                *([None] * 6), None, 0, None)
+    assert r == M.MLSTM_ERR_INVALID_ARG or field != "T"
+
 
 
 def test_chunkwise_rejects_bad_enums(lib):
@@ -322,7 +359,8 @@ def gn_call(lib, B=1, H=2, T=4, dv=64, hdt=1, odt=0, eps=1e-5, **over):
 def test_groupnorm_rejections(lib):
     assert gn_call(lib, h=None)[0] == M.MLSTM_ERR_INVALID_ARG
     assert gn_call(lib, y=None)[0] == M.MLSTM_ERR_INVALID_ARG
-    assert gn_call(lib, T=0)[0] == M.MLSTM_ERR_INVALID_ARG
+    assert gn_call(lib, T=-1)[0] == M.MLSTM_ERR_INVALID_ARG
+    assert gn_call(lib, T=0, h=None, y=None)[0] == 0   # no rows: nothing to do
     r, det = gn_call(lib, B=2, H=1 << 16, T=(1 << 15) + 1)
     assert r == M.MLSTM_ERR_UNSUPPORTED and "2^32" in det
     assert gn_call(lib, hdt=7)[0] == M.MLSTM_ERR_INVALID_ARG
@@ -351,6 +389,9 @@ def test_conv_rejections(lib):
     for n in ("x", "w", "y"):
         assert conv_call(lib, **{n: None})[0] == M.MLSTM_ERR_INVALID_ARG, n
     assert conv_call(lib, K=0)[0] == M.MLSTM_ERR_INVALID_ARG
+    assert conv_call(lib, T=-1)[0] == M.MLSTM_ERR_INVALID_ARG
+    assert conv_call(lib, B=0, x=None, w=None, y=None)[0] == 0   # nothing to do
+    assert conv_call(lib, T=0, x=None, y=None)[0] == 0           # no window to carry
     assert conv_call(lib, dt=3)[0] == M.MLSTM_ERR_INVALID_ARG
     assert conv_call(lib, K=9)[0] == M.MLSTM_ERR_UNSUPPORTED
     assert conv_call(lib, C=12)[0] == M.MLSTM_ERR_UNSUPPORTED            # bf16: C % 8
@@ -391,7 +432,10 @@ def slstm_call(lib, B=2, NH=2, T=8, DH=32, dt=0, fg=0, **over):
 def test_slstm_rejections(lib):
     for n in ("wx", "R", "h"):
         assert slstm_call(lib, **{n: None})[0] == M.MLSTM_ERR_INVALID_ARG, n
-    assert slstm_call(lib, T=0)[0] == M.MLSTM_ERR_INVALID_ARG
+    assert slstm_call(lib, T=-1)[0] == M.MLSTM_ERR_INVALID_ARG
+    # no steps and no state: nothing to do (state pointers are None by default)
+    assert slstm_call(lib, T=0, wx=None, R=None, h=None)[0] == 0
+    assert slstm_call(lib, B=0, wx=None, R=None, h=None)[0] == 0
     assert slstm_call(lib, dt=5)[0] == M.MLSTM_ERR_INVALID_ARG
     assert slstm_call(lib, fg=9)[0] == M.MLSTM_ERR_INVALID_ARG
     assert slstm_call(lib, DH=48)[0] == M.MLSTM_ERR_UNSUPPORTED
