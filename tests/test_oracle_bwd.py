@@ -181,3 +181,30 @@ def test_mutants_rejected(tmp_path, name, orig, mut):
         c = make_case(seed, T=20, fgate=fgate, o=o, state=state, dstate=dstate)
         worst = max(worst, fd_check(c, fgate, grads(c, fgate, lib=lib), seed=seed))
     assert worst > 1e-4, name
+
+
+def test_empty_sequence_closed_form():
+    """T = 0: the final memory is the initial one, so its gradient passes
+    through (dC0 = dC1, dn0 = dn1 in the stored scale) and the derivative
+    through e^{m0} is <dC1, C~0> + <dn1, n~0>; the forward returns the state."""
+    import numpy as np
+    import torch
+    import oracle
+    g = torch.Generator().manual_seed(11)
+    B, H, dqk, dv = 2, 3, 8, 5
+    z = torch.zeros
+    q, k, v = z(B, H, 0, dqk), z(B, H, 0, dqk), z(B, H, 0, dv)
+    i_pre = f_pre = z(B, H, 0)
+    C0, n0, m0 = torch.randn(B, H, dqk, dv, generator=g), torch.randn(B, H, dqk, generator=g), \
+        torch.randn(B, H, generator=g)
+    h, C1, n1, m1 = oracle.recurrent(q, k, v, i_pre, f_pre, None, C0, n0, m0)
+    assert h.shape == (B, H, 0, dv)
+    np.testing.assert_array_equal(C1, C0.double().numpy())
+    np.testing.assert_array_equal(n1, n0.double().numpy())
+    np.testing.assert_array_equal(m1, m0.double().numpy())
+    dC1, dn1 = torch.randn(B, H, dqk, dv, generator=g), torch.randn(B, H, dqk, generator=g)
+    r = oracle.backward(q, k, v, i_pre, f_pre, None, C0, n0, m0, z(B, H, 0, dv), dC1, dn1)
+    np.testing.assert_allclose(r["dC0"], dC1.double().numpy(), rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(r["dn0"], dn1.double().numpy(), rtol=1e-13, atol=1e-13)
+    ref = (dC1.double() * C0.double()).sum((2, 3)) + (dn1.double() * n0.double()).sum(2)
+    np.testing.assert_allclose(r["dm0"], ref.numpy(), rtol=1e-12, atol=1e-12)
