@@ -100,11 +100,11 @@ typedef struct {
  *   workspace: device scratch of at least the size given by
  *   mlstm_fwd_chunkwise_workspace_bytes (may be NULL when that size is 0);
  *   it must not overlap any other argument.
- * Any T >= 1 is accepted.  When T is not a multiple of `chunk`, the last
- * T % chunk tokens form one shorter chunk: on the bf16 matrix-core path they
- * run on the float32 vector kernel, continuing from the state the first
- * T - T % chunk tokens leave in the workspace (B*H*(d_qk*d_v + d_qk + 1)
- * floats).
+ * Any T >= 0 is accepted (T = 0: see "Empty inputs" above).  When T is not
+ * a multiple of `chunk`, the last T % chunk tokens form one shorter chunk:
+ * on the bf16 matrix-core path they run on the float32 vector kernel,
+ * continuing from the state the first T - T % chunk tokens leave in the
+ * workspace (B*H*(d_qk*d_v + d_qk + 1) floats).
  * Returns MLSTM_OK or an error code; on error, mlstm_last_error_detail()
  * describes it.
  */
@@ -191,10 +191,11 @@ mlstm_status_t mlstm_step(const mlstm_problem_t* p, const void* q,
  * 64, 128 or 256 (matrix products on bf16 matrix cores with float32
  * accumulation, operands such as the memory gradient rounded to bf16);
  * otherwise MLSTM_ERR_UNSUPPORTED.  The result does not depend on chunk
- * beyond rounding.  Any T >= 1: when T is not a multiple of chunk, the pass
- * runs on copies of the per-token arrays padded to the next multiple Tp, at
- * the front of the workspace (14 arrays of B*H*Tp tokens each); a padding
- * token keeps the memory unchanged and contributes nothing to any gradient.
+ * beyond rounding.  Any T >= 0 (T = 0: see "Empty inputs"); when T is not a
+ * multiple of chunk, the pass runs on copies of the per-token arrays padded
+ * to the next multiple Tp, at the front of the workspace (14 arrays of
+ * B*H*Tp tokens each); a padding token keeps the memory unchanged and
+ * contributes nothing to any gradient.
  */
 mlstm_status_t mlstm_bwd_chunkwise(const mlstm_problem_t* p, int64_t chunk,
                                    const void* q, const void* k, const void* v,
