@@ -199,6 +199,11 @@ __global__ __launch_bounds__(kThreads) void step_stream_kernel(StepArgs a) {
   }
 }
 
+// In place (m_out == m_in, n_out == n_in): every thread reads m_in at entry,
+// and each n~ element is read and written by the same thread.  m_out is
+// written only after the barrier, when every wave of the workgroup has read
+// m_in; without it a late wave could read the new m and scale its n~ rows
+// with the wrong factors.
 template <typename TQ>
 __global__ __launch_bounds__(kThreads) void step_state_kernel(StepArgs a) {
   const int64_t bh = blockIdx.x;
@@ -207,6 +212,7 @@ __global__ __launch_bounds__(kThreads) void step_state_kernel(StepArgs a) {
   const TQ* k = static_cast<const TQ*>(a.k) + bh * dqk;
   for (int r = threadIdx.x; r < dqk; r += kThreads)
     a.n_out[bh * dqk + r] = sc.g * a.n_in[bh * dqk + r] + sc.w * to_f32(k[r]);
+  __syncthreads();
   if (threadIdx.x == 0) a.m_out[bh] = sc.m_new;
 }
 
