@@ -88,7 +88,10 @@ def conv_algorithmic(B, T, C, K, x_bytes=2):
 # sLSTM line: 64 sequences x 4 heads of 128 units fill the 256 CUs with one
 # (batch, head) sequence each
 SLSTM_SHAPE = dict(B=64, NH=4, T=4096, DH=128)
-FP32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector, TFLOP/s
+# MI355X fp32 vector peak without packed FP32: 256 CUs x 64 FMA/clk x 2 flop x
+# 2.4 GHz = 78.6 TFLOP/s.  The library is built with packed FP32 off, so the
+# 157.3 TFLOP/s datasheet figure (two lanes per FMA) is out of reach.
+FP32_VALU_PEAK_TFLOPS = 78.6
 
 
 def slstm_flops(B, NH, T, DH):

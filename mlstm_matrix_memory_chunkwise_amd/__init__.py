@@ -21,7 +21,9 @@ None; gates and state are float32.  k is expected pre-scaled by 1/sqrt(d_qk).
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
+import functools
 import os
 from typing import Optional, Tuple
 
@@ -162,6 +164,24 @@ def _stream_handle(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on_stream(stream):
+    """Context in which a call allocates its outputs and scratch: the stream
+    the kernels are enqueued on.  torch's caching allocator then hands a freed
+    block (the workspace, released on return) only to work ordered after
+    these kernels on that stream, never to another stream while they still
+    use it."""
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
+def _allocates_on_stream(fn):
+    """Runs an entry point (keyword argument ``stream``) under _on_stream."""
+    @functools.wraps(fn)
+    def wrapper(*args, **kwargs):
+        with _on_stream(kwargs.get("stream")):
+            return fn(*args, **kwargs)
+    return wrapper
+
+
 def _seq_problem(q, k, v, i_pre, f_pre, o_pre, C0, n0, m0, fgate):
     q = _dev_tensor("q", q, (torch.float32, torch.bfloat16))
     if q.dim() != 4:
@@ -184,14 +204,20 @@ def _seq_problem(q, k, v, i_pre, f_pre, o_pre, C0, n0, m0, fgate):
     return p, (q, k, v, i_pre, f_pre, o_pre, C0, n0, m0)
 
 
-def _outputs(p, q, out, return_state):
+def _outputs(p, q, out, return_state, state_out=None):
     B, H, T, dqk, dv = p.B, p.H, p.T, p.d_qk, p.d_v
     dev = q.device
     if out is not None:
         h = _dev_tensor("out", out, q.dtype, (B, H, T, dv), dev)
     else:
         h = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev)
-    if return_state:
+    if state_out is not None:
+        if not return_state:
+            raise ValueError("state_out is given but return_state is False")
+        C1 = _dev_tensor("C1", state_out[0], torch.float32, (B, H, dqk, dv), dev)
+        n1 = _dev_tensor("n1", state_out[1], torch.float32, (B, H, dqk), dev)
+        m1 = _dev_tensor("m1", state_out[2], torch.float32, (B, H), dev)
+    elif return_state:
         C1 = torch.empty((B, H, dqk, dv), dtype=torch.float32, device=dev)
         n1 = torch.empty((B, H, dqk), dtype=torch.float32, device=dev)
         m1 = torch.empty((B, H), dtype=torch.float32, device=dev)
@@ -213,15 +239,17 @@ def mlstm_fwd_parallel_workspace_bytes(p: Problem) -> int:
     return int(n.value)
 
 
+@_allocates_on_stream
 def mlstm_fwd_chunkwise(q, k, v, i_pre, f_pre, o_pre=None, C0=None, n0=None, m0=None, *,
                         chunk: int = 64, fgate="sigmoid", return_state: bool = True,
                         out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                        stream=None):
-    """Chunkwise forward pass.  Returns (h, (C1, n1, m1)) or (h, None)."""
+                        state_out=None, stream=None):
+    """Chunkwise forward pass.  Returns (h, (C1, n1, m1)) or (h, None).
+    ``state_out`` = (C1, n1, m1) tensors to write the final state into."""
     lib = load_library()
     p, (q, k, v, i_pre, f_pre, o_pre, C0, n0, m0) = _seq_problem(
         q, k, v, i_pre, f_pre, o_pre, C0, n0, m0, fgate)
-    h, C1, n1, m1 = _outputs(p, q, out, return_state)
+    h, C1, n1, m1 = _outputs(p, q, out, return_state, state_out)
     need = mlstm_fwd_chunkwise_workspace_bytes(p, chunk)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -233,15 +261,17 @@ def mlstm_fwd_chunkwise(q, k, v, i_pre, f_pre, o_pre=None, C0=None, n0=None, m0=
     return h, ((C1, n1, m1) if return_state else None)
 
 
+@_allocates_on_stream
 def mlstm_fwd_parallel(q, k, v, i_pre, f_pre, o_pre=None, C0=None, n0=None, m0=None, *,
                        fgate="sigmoid", return_state: bool = True,
                        out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                       stream=None):
-    """Parallel (quadratic) forward pass.  Returns (h, (C1, n1, m1)) or (h, None)."""
+                       state_out=None, stream=None):
+    """Parallel (quadratic) forward pass.  Returns (h, (C1, n1, m1)) or (h, None).
+    ``state_out`` = (C1, n1, m1) tensors to write the final state into."""
     lib = load_library()
     p, (q, k, v, i_pre, f_pre, o_pre, C0, n0, m0) = _seq_problem(
         q, k, v, i_pre, f_pre, o_pre, C0, n0, m0, fgate)
-    h, C1, n1, m1 = _outputs(p, q, out, return_state)
+    h, C1, n1, m1 = _outputs(p, q, out, return_state, state_out)
     need = mlstm_fwd_parallel_workspace_bytes(p)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
@@ -260,6 +290,7 @@ def mlstm_bwd_chunkwise_workspace_bytes(p: Problem, chunk: int) -> int:
     return int(n.value)
 
 
+@_allocates_on_stream
 def mlstm_bwd_chunkwise(q, k, v, i_pre, f_pre, o_pre, C0, n0, m0, h, dh, dC1=None, dn1=None, *,
                         chunk: int = 32, fgate="sigmoid", workspace: Optional[torch.Tensor] = None,
                         stream=None):
@@ -300,6 +331,7 @@ def mlstm_bwd_chunkwise(q, k, v, i_pre, f_pre, o_pre, C0, n0, m0, h, dh, dC1=Non
     return g
 
 
+@_allocates_on_stream
 def mlstm_step(q, k, v, i_pre, f_pre, o_pre, C, n, m, *, fgate="sigmoid",
                inplace: bool = False, out: Optional[torch.Tensor] = None,
                state_out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
@@ -341,6 +373,7 @@ def mlstm_step(q, k, v, i_pre, f_pre, o_pre, C, n, m, *, fgate="sigmoid",
     return h, (C1, n1, m1)
 
 
+@_allocates_on_stream
 def mlstm_groupnorm_ogate(h, o_pre=None, gamma=None, beta=None, eps: float = 1e-5, *,
                           out: Optional[torch.Tensor] = None, stream=None):
     """Per-head group normalization of the cell output with the output gate
@@ -365,6 +398,7 @@ def mlstm_groupnorm_ogate(h, o_pre=None, gamma=None, beta=None, eps: float = 1e-
     return y
 
 
+@_allocates_on_stream
 def mlstm_causal_conv1d(x, w, bias=None, state=None, *, return_state: bool = True,
                         out: Optional[torch.Tensor] = None, stream=None):
     """Causal depthwise convolution over the token axis (see
@@ -397,6 +431,7 @@ class SlstmProblem(ctypes.Structure):
                 ("DH", ctypes.c_int64), ("x_dtype", ctypes.c_int32), ("fgate", ctypes.c_int32)]
 
 
+@_allocates_on_stream
 def mlstm_slstm_fwd(wx, R, c0=None, n0=None, m0=None, h0=None, *, fgate="sigmoid",
                     return_state: bool = True, out: Optional[torch.Tensor] = None, stream=None):
     """sLSTM forward cell (see mlstm_slstm_fwd in include/mlstm.h).
