@@ -105,7 +105,7 @@ def load_library(path: str):
     lib.oracle_step.restype = None
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ctypes.c_int
-    lib.oracle_backward.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int] + [P] * 21 + [ctypes.c_int]
+    lib.oracle_backward.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int] + [P] * 27 + [ctypes.c_int]
     lib.oracle_backward.restype = None
     return lib
 
@@ -194,20 +194,27 @@ def step(q, k, v, i_pre, f_pre, o_pre, C, n, m, fgate="sigmoid",
 
 
 def backward(q, k, v, i_pre, f_pre, o_pre, C0, n0, m0, dh, dC1=None, dn1=None,
-             fgate="sigmoid", nthreads: int = 0, lib=None):
+             fgate="sigmoid", nthreads: int = 0, lib=None, h=None):
     """Gradient of L = sum dh . h + e^{-m_T} (<dC1, C_T> + <dn1, n_T>) (see
     ``mlstm_oracle_bwd.c``) with respect to every input of the forward pass.
 
     Shapes as in ``recurrent``; dh like v; dC1 [B,H,dqk,dv], dn1 [B,H,dqk] or
-    both None.  Returns a dict of float64 arrays: dq, dk, dv, di, df, do (None
-    without o~), dC0, dn0, dm0 (the initial-state gradients in its stored
-    scale; computed for the zero state too).
+    both None.  ``h`` (like v, optional) is the forward output as a caller
+    hands it to a backward pass; the gradient's two terms that depend on h
+    itself (dh . h in the denominator term, and do~) then use it instead of
+    the oracle's own fp64 h.  Returns a dict of float64 arrays: dq, dk, dv,
+    di, df, do (None without o~), dC0, dn0, dm0 (the initial-state gradients
+    in its stored scale; computed for the zero state too), and cond_dq,
+    cond_dk, cond_di, cond_df, cond_dm0: the conditioning scale of dq, dk,
+    di, df, dm0 (the sum of the absolute values of their memory and
+    normalizer paths, which partly cancel on the active branch of the
+    denominator).
     """
     lib = lib or _load()
     q, k, v = _f64(q), _f64(k), _f64(v)
     i_pre, f_pre, o_pre = _f64(i_pre), _f64(f_pre), _f64(o_pre)
     C0, n0, m0 = _f64(C0), _f64(n0), _f64(m0)
-    dh, dC1, dn1 = _f64(dh), _f64(dC1), _f64(dn1)
+    dh, dC1, dn1, h = _f64(dh), _f64(dC1), _f64(dn1), _f64(h)
     if (C0 is None) != (n0 is None) or (C0 is None) != (m0 is None):
         raise ValueError("initial state must be given whole or not at all")
     if (dC1 is None) != (dn1 is None):
@@ -215,13 +222,21 @@ def backward(q, k, v, i_pre, f_pre, o_pre, C0, n0, m0, dh, dC1=None, dn1=None,
     B, H, T, dqk = q.shape
     dv = v.shape[-1]
     assert dh.shape == (B, H, T, dv)
+    if h is not None:
+        assert h.shape == (B, H, T, dv)
     out = dict(dq=np.empty((B, H, T, dqk)), dk=np.empty((B, H, T, dqk)),
                dv=np.empty((B, H, T, dv)), di=np.empty((B, H, T)), df=np.empty((B, H, T)),
                do=None if o_pre is None else np.empty((B, H, T, dv)),
-               dC0=np.empty((B, H, dqk, dv)), dn0=np.empty((B, H, dqk)), dm0=np.empty((B, H)))
+               dC0=np.empty((B, H, dqk, dv)), dn0=np.empty((B, H, dqk)), dm0=np.empty((B, H)),
+               cond_dq=np.empty((B, H, T, dqk)), cond_dk=np.empty((B, H, T, dqk)),
+               cond_di=np.empty((B, H, T)), cond_df=np.empty((B, H, T)),
+               cond_dm0=np.empty((B, H)))
     lib.oracle_backward(B, H, T, dqk, dv, fgate_code(fgate), _ptr(q), _ptr(k), _ptr(v),
                         _ptr(i_pre), _ptr(f_pre), _ptr(o_pre), _ptr(C0), _ptr(n0), _ptr(m0),
-                        _ptr(dh), _ptr(dC1), _ptr(dn1), _ptr(out["dq"]), _ptr(out["dk"]),
-                        _ptr(out["dv"]), _ptr(out["di"]), _ptr(out["df"]), _ptr(out["do"]),
-                        _ptr(out["dC0"]), _ptr(out["dn0"]), _ptr(out["dm0"]), int(nthreads))
+                        _ptr(dh), _ptr(h), _ptr(dC1), _ptr(dn1), _ptr(out["dq"]),
+                        _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["di"]), _ptr(out["df"]),
+                        _ptr(out["do"]), _ptr(out["dC0"]), _ptr(out["dn0"]), _ptr(out["dm0"]),
+                        _ptr(out["cond_dq"]), _ptr(out["cond_dk"]), _ptr(out["cond_di"]),
+                        _ptr(out["cond_df"]), _ptr(out["cond_dm0"]),
+                        int(nthreads))
     return out

@@ -40,11 +40,12 @@
  * e^{m0} of the true initial memory).
  *
  * Reverse step at token t (GC, Gn: dL/dC_t, dL/dn_t accumulated so far):
- *   dnum = gate (.) dh_t / den_t,  dden = -(sum_b dh_t[b] gate[b] num[b]) / den_t^2
+ *   h_t = gate (.) num / den_t (or the given h_in, below)
+ *   dnum = gate (.) dh_t / den_t,  dden = -(dh_t . h_t) / den_t
  *   dnq  = dden * sign(nq_t) where |nq_t| >= 1, else 0
  *   GC += q_t dnum^T,  Gn += dnq q_t
  *   dq_t = C_t dnum + dnq n_t
- *   do~_t = dh_t (.) (num / den_t) (.) gate (1 - gate)
+ *   do~_t = dh_t (.) h_t (.) (1 - gate)
  *   dk_t = i_t (GC v_t + Gn),  dv_t = i_t GC^T k_t
  *   di~_t = i_t (k_t^T GC v_t + k_t . Gn)
  *   df~_t = (<GC, C_{t-1}> + <Gn, n_{t-1}>) * df_t/df~_t
@@ -54,6 +55,33 @@
  * The states C_{t-1} of the reverse sweep are recomputed segment by segment
  * (SEG tokens) from checkpoints taken in the forward sweep.  Sums run in
  * ascending index order.
+ *
+ * Given forward output (h_in).  A backward pass that is handed the forward
+ * output h uses it where the gradient depends on h itself: the denominator
+ * term, dden = -(dh_t . h_t) / den_t, and do~_t = dh_t (.) h_t (.) (1 - gate).
+ * With h_in = NULL these use the oracle's own fp64 h (num/den above, the
+ * same value).  With h_in set (e.g. the fp64 h rounded to bfloat16, as a
+ * bf16 forward pass hands it over) the result is that same formula
+ * evaluated at the given h, so two implementations handed the same h can be
+ * compared without the rounding of h in between.
+ *
+ * Conditioning (cond_dq, cond_dk, cond_di, cond_df, cond_dm0).  These five
+ * gradients are each the sum of a memory path and a normalizer path:
+ *   dq_t   = C_t dnum + dnq n_t,
+ *   dk_t   = i_t (GC v_t + Gn),
+ *   di~_t  = i_t (k_t^T GC v_t + k_t . Gn),
+ *   df~_t  = (<GC, C_{t-1}> + <Gn, n_{t-1}>) df_t/df~_t,
+ *   dm0    = <GC, C_0> + <Gn, n_0>.
+ * On the active branch of the denominator (|n.q| >= 1) the readout does not
+ * change when q is scaled, nor when C and n are scaled together, so the two
+ * paths partly cancel.  The returned cond = the same sums with each path's
+ * absolute value (elementwise for dq, dk):
+ *   |C_t dnum| + |dnq n_t|,  i_t (|GC v_t| + |Gn|),
+ *   i_t (|k_t^T GC v_t| + |k_t . Gn|),
+ *   (|<GC, C_{t-1}>| + |<Gn, n_{t-1}>|) |df_t/df~_t|,  |<GC, C_0>| + |<Gn, n_0>|,
+ * is the scale against which an error made in the paths is measured: a
+ * relative error e in the paths gives an error of about e cond in the sum,
+ * however small the sum itself is.
  */
 #include <math.h>
 #include <stddef.h>
@@ -89,20 +117,24 @@ static void bwd_update(int64_t dqk, int64_t dv, double f, double i,
 }
 
 /*
- * Layouts (row-major, contiguous): q, k, dq, dk [B,H,T,dqk]; v, o, dh, dv_out,
- * do_out [B,H,T,dv]; i_pre, f_pre, di, df [B,H,T]; C0, dC1, dC0 [B,H,dqk,dv];
- * n0, dn1, dn0 [B,H,dqk]; m0, dm0 [B,H].  o, C0/n0/m0 (together), dC1/dn1
- * (together) may be NULL; do_out must be non-NULL when o is; dC0, dn0, dm0 may
+ * Layouts (row-major, contiguous): q, k, dq, dk, cond_dq, cond_dk [B,H,T,dqk];
+ * v, o, dh, h_in,
+ * dv_out, do_out [B,H,T,dv]; i_pre, f_pre, di, df, cond_di, cond_df [B,H,T];
+ * C0, dC1, dC0 [B,H,dqk,dv]; n0, dn1, dn0 [B,H,dqk]; m0, dm0, cond_dm0
+ * [B,H].  o, h_in, C0/n0/m0 (together), dC1/dn1 (together) may be NULL;
+ * do_out must be non-NULL when o is; dC0, dn0, dm0 and the cond_ arrays may
  * be NULL.
  */
 void oracle_backward(int64_t B, int64_t H, int64_t T, int64_t dqk, int64_t dv,
                      int fgate, const double* q, const double* k,
                      const double* v, const double* i_pre, const double* f_pre,
                      const double* o, const double* C0, const double* n0,
-                     const double* m0, const double* dh, const double* dC1,
-                     const double* dn1, double* dq, double* dk, double* dv_out,
-                     double* di, double* df, double* do_out, double* dC0,
-                     double* dn0, double* dm0, int nthreads) {
+                     const double* m0, const double* dh, const double* h_in,
+                     const double* dC1, const double* dn1, double* dq, double* dk,
+                     double* dv_out, double* di, double* df, double* do_out,
+                     double* dC0, double* dn0, double* dm0, double* cond_dq,
+                     double* cond_dk, double* cond_di, double* cond_df,
+                     double* cond_dm0, int nthreads) {
 #ifdef _OPENMP
   if (nthreads > 0) omp_set_num_threads(nthreads);
 #else
@@ -176,17 +208,18 @@ void oracle_backward(int64_t B, int64_t H, int64_t T, int64_t dqk, int64_t dv,
         double nq = 0.0;
         for (int64_t a = 0; a < dqk; ++a) nq += nt[a] * qt[a];
         const double den = fabs(nq) > 1.0 ? fabs(nq) : 1.0;
-        double sden = 0.0;
+        double sden = 0.0;   /* sum_b dh_t[b] h_t[b] */
         for (int64_t b = 0; b < dv; ++b) {
           double acc = 0.0;
           for (int64_t a = 0; a < dqk; ++a) acc += qt[a] * Ct[a * dv + b];
           num[b] = acc;
           const double gate = o ? bwd_sigmoid(o[tok * dv + b]) : 1.0;
+          const double hb = h_in ? h_in[tok * dv + b] : gate * acc / den;
           dnum[b] = gate * dht[b] / den;
-          sden += dht[b] * gate * acc;
-          if (o) do_out[tok * dv + b] = dht[b] * (acc / den) * gate * (1.0 - gate);
+          sden += dht[b] * hb;
+          if (o) do_out[tok * dv + b] = dht[b] * hb * (1.0 - gate);
         }
-        const double dden = -sden / (den * den);
+        const double dden = -sden / den;
         const double dnq = fabs(nq) >= 1.0 ? (nq >= 0.0 ? dden : -dden) : 0.0;
         for (int64_t a = 0; a < dqk; ++a) {
           double acc = 0.0;
@@ -196,35 +229,47 @@ void oracle_backward(int64_t B, int64_t H, int64_t T, int64_t dqk, int64_t dv,
           }
           Gn[a] += dnq * qt[a];
           dq[tok * dqk + a] = acc + dnq * nt[a];
+          if (cond_dq) cond_dq[tok * dqk + a] = fabs(acc) + fabs(dnq * nt[a]);
         }
         double dI = 0.0, dF = 0.0;
+        double dI_mem = 0.0, dI_nrm = 0.0, dF_mem = 0.0, dF_nrm = 0.0;   /* the two paths */
         for (int64_t a = 0; a < dqk; ++a) {
-          double gv = 0.0;
+          double gv = 0.0, fc = 0.0;
           for (int64_t b = 0; b < dv; ++b) {
             gv += GC[a * dv + b] * vt[b];
-            dF += GC[a * dv + b] * Cp[a * dv + b];
+            fc += GC[a * dv + b] * Cp[a * dv + b];
           }
           dk[tok * dqk + a] = i * (gv + Gn[a]);
+          if (cond_dk) cond_dk[tok * dqk + a] = i * (fabs(gv) + fabs(Gn[a]));
           dI += kt[a] * (gv + Gn[a]);
-          dF += Gn[a] * np[a];
+          dF += fc + Gn[a] * np[a];
+          dI_mem += kt[a] * gv;
+          dI_nrm += kt[a] * Gn[a];
+          dF_mem += fc;
+          dF_nrm += Gn[a] * np[a];
         }
         for (int64_t b = 0; b < dv; ++b) {
           double acc = 0.0;
           for (int64_t a = 0; a < dqk; ++a) acc += GC[a * dv + b] * kt[a];
           dv_out[tok * dv + b] = i * acc;
         }
+        const double dfdf = (fgate == BWD_FGATE_SIGMOID) ? f * (1.0 - f) : f;
         di[tok] = i * dI;
-        df[tok] = dF * ((fgate == BWD_FGATE_SIGMOID) ? f * (1.0 - f) : f);
+        df[tok] = dF * dfdf;
+        if (cond_di) cond_di[tok] = i * (fabs(dI_mem) + fabs(dI_nrm));
+        if (cond_df) cond_df[tok] = (fabs(dF_mem) + fabs(dF_nrm)) * dfdf;
         for (int64_t x = 0; x < S; ++x) G[x] *= f;
       }
     }
     /* ---- initial state, in its stored scale */
     if (dC0) for (int64_t x = 0; x < dqk * dv; ++x) dC0[bh * dqk * dv + x] = GC[x] * scale0;
     if (dn0) for (int64_t a = 0; a < dqk; ++a) dn0[bh * dqk + a] = Gn[a] * scale0;
-    if (dm0) {
-      double acc = 0.0;
-      for (int64_t x = 0; x < S; ++x) acc += G[x] * ck[x];
-      dm0[bh] = acc;
+    if (dm0 || cond_dm0) {
+      double acc_mem = 0.0, acc_nrm = 0.0;
+      for (int64_t x = 0; x < dqk * dv; ++x) acc_mem += G[x] * ck[x];
+      for (int64_t x = dqk * dv; x < S; ++x) acc_nrm += G[x] * ck[x];
+      if (dm0) dm0[bh] = acc_mem + acc_nrm;
+      if (cond_dm0) cond_dm0[bh] = fabs(acc_mem) + fabs(acc_nrm);
     }
     free(ck);
     free(seg);

@@ -166,7 +166,7 @@ BWD_MUTANTS = [
     ("key gradient without the normalizer path",
      "dk[tok * dqk + a] = i * (gv + Gn[a]);", "dk[tok * dqk + a] = i * gv;"),
     ("forget gradient against the updated state",
-     "dF += GC[a * dv + b] * Cp[a * dv + b];", "dF += GC[a * dv + b] * Ct[a * dv + b];"),
+     "fc += GC[a * dv + b] * Cp[a * dv + b];", "fc += GC[a * dv + b] * Ct[a * dv + b];"),
 ]
 
 
@@ -208,3 +208,92 @@ def test_empty_sequence_closed_form():
     np.testing.assert_allclose(r["dn0"], dn1.double().numpy(), rtol=1e-13, atol=1e-13)
     ref = (dC1.double() * C0.double()).sum((2, 3)) + (dn1.double() * n0.double()).sum(2)
     np.testing.assert_allclose(r["dm0"], ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_given_h_equal_to_own_h_changes_nothing():
+    """Handing the oracle its own fp64 forward output as h gives the same
+    gradients as leaving h out (the two h-dependent terms are the same
+    numbers, computed from the given h instead of num/den)."""
+    c = make_case(21, T=70, o=True, state=True, dstate=True)
+    h, *_ = oracle.recurrent(c["q"], c["k"], c["v"], c["i_pre"], c["f_pre"], c["o_pre"],
+                             c["C0"], c["n0"], c["m0"])
+    g0 = grads(c, "sigmoid")
+    g1 = oracle.backward(c["q"], c["k"], c["v"], c["i_pre"], c["f_pre"], c["o_pre"], c["C0"],
+                         c["n0"], c["m0"], c["dh"], c["dC1"], c["dn1"], h=h)
+    for name in ("dq", "dk", "dv", "di", "df", "do", "dC0", "dn0", "dm0"):
+        np.testing.assert_allclose(g1[name], g0[name], rtol=1e-12, atol=1e-13, err_msg=name)
+
+
+def test_given_h_single_token_closed_form():
+    """One token from the zero state on the active branch (|i q.k| = 4), with a
+    given output h' = sign(q.k) v + delta instead of the exact sign(q.k) v.
+    The denominator term is dnq = -s (dh . h') / den with s = sign(q.k) and
+    den = i |q.k|, so dq = i k (v . dh - s dh . h') / den = -k s (dh . delta) /
+    |q.k| and dk likewise with q; the exact h gives zero.  With an o-gate,
+    do~ = dh (.) h' (.) (1 - sigmoid(o~))."""
+    rng = np.random.default_rng(13)
+    dqk, dv = 5, 3
+    q = rng.normal(0, 1, dqk)
+    k = rng.normal(0, 1, dqk) / np.sqrt(dqk)
+    v = rng.normal(0, 1, dv)
+    dh = rng.normal(0, 1, dv)
+    delta = rng.normal(0, 0.01, dv)
+    qk = q @ k
+    s = np.sign(qk)
+    ip = np.log(4.0 / abs(qk))
+    e = lambda a: np.asarray(a, dtype=np.float64).reshape((1, 1, 1) + np.shape(a))  # noqa: E731
+    g = oracle.backward(e(q), e(k), e(v), e(ip), e(1.0), None, None, None, None, e(dh),
+                        h=e(s * v + delta))
+    np.testing.assert_allclose(g["dq"].reshape(-1), -k * s * (dh @ delta) / abs(qk),
+                               rtol=1e-11, atol=1e-15)
+    np.testing.assert_allclose(g["dk"].reshape(-1), -q * s * (dh @ delta) / abs(qk),
+                               rtol=1e-11, atol=1e-15)
+    o = rng.normal(0, 1, dv)
+    sig = 1.0 / (1.0 + np.exp(-o))
+    hp = s * sig * v + delta
+    g = oracle.backward(e(q), e(k), e(v), e(ip), e(1.0), e(o), None, None, None, e(dh), h=e(hp))
+    np.testing.assert_allclose(g["do"].reshape(-1), dh * hp * (1 - sig), rtol=1e-13, atol=0)
+
+
+def test_conditioning_single_token_closed_form():
+    """One token on the active branch with the exact h: the memory and
+    normalizer paths of dq, dk and di cancel exactly (the results are 0,
+    test_single_token_closed_form), and the conditioning scale is the sum of
+    their sizes: cond_dq = 2 |k| |v . dh| / |q.k|, cond_dk = 2 |q| |v . dh| /
+    |q.k|, cond_di = 2 |v . dh|."""
+    rng = np.random.default_rng(17)
+    dqk, dv = 4, 6
+    q = rng.normal(0, 1, dqk)
+    k = rng.normal(0, 1, dqk) / np.sqrt(dqk)
+    v = rng.normal(0, 1, dv)
+    dh = rng.normal(0, 1, dv)
+    qk = q @ k
+    ip = np.log(3.0 / abs(qk))
+    e = lambda a: np.asarray(a, dtype=np.float64).reshape((1, 1, 1) + np.shape(a))  # noqa: E731
+    g = oracle.backward(e(q), e(k), e(v), e(ip), e(1.0), None, None, None, None, e(dh))
+    vd = abs(v @ dh)
+    np.testing.assert_allclose(g["cond_dq"].reshape(-1), 2 * np.abs(k) * vd / abs(qk), rtol=1e-12)
+    np.testing.assert_allclose(g["cond_dk"].reshape(-1), 2 * np.abs(q) * vd / abs(qk), rtol=1e-12)
+    np.testing.assert_allclose(g["cond_di"].item(), 2 * vd, rtol=1e-12)
+
+
+def test_conditioning_bounds_and_linear_attention():
+    """cond >= |gradient| always (triangle inequality), and with no active
+    denominator anywhere (causal linear attention, |n.q| < 1) the normalizer
+    paths vanish, so cond equals |gradient| exactly."""
+    c = make_case(23, T=70, o=True, state=True, dstate=True)
+    g = grads(c, "sigmoid")
+    for name in ("dq", "dk", "di", "df", "dm0"):
+        assert np.all(g["cond_" + name] >= np.abs(g[name]) * (1 - 1e-12) - 1e-300), name
+    rng = np.random.default_rng(5)
+    T, dqk, dv = 40, 6, 4
+    q = rng.normal(0, 1, (T, dqk)) * 0.1
+    k = rng.normal(0, 1, (T, dqk)) * 0.1 / np.sqrt(dqk)
+    v = rng.normal(0, 1, (T, dv))
+    dh = rng.normal(0, 1, (T, dv))
+    e = lambda a: np.asarray(a, dtype=np.float64)[None, None]  # noqa: E731
+    g = oracle.backward(e(q), e(k), e(v), e(np.zeros(T)), e(np.zeros(T)), None, None, None, None,
+                        e(dh), fgate="exp")
+    for name in ("dq", "dk", "di", "df"):
+        np.testing.assert_allclose(g["cond_" + name], np.abs(g[name]), rtol=1e-12, atol=1e-300,
+                                   err_msg=name)
