@@ -51,6 +51,23 @@ def slice_rel_err(x, r, lead: int = 2) -> float:
     return float(np.max(num / den))
 
 
+def elem_rel_err(x, r, lead: int = 2) -> float:
+    """Elementwise diagnostic beside the normwise error: max over the leading
+    `lead` axes of max |x - r| / (|r| + 1e-3 max|r|).  It shows where single
+    small elements are off, which the normwise figure hides; it is logged, not
+    held to a tolerance."""
+    x = f64(x)
+    r = f64(r)
+    assert x.shape == r.shape, (x.shape, r.shape)
+    if np.isnan(x).any():
+        return float("inf")
+    xs = x.reshape(int(np.prod(x.shape[:lead])), -1)
+    rs = r.reshape(xs.shape)
+    floor = 1e-3 * np.max(np.abs(rs), axis=1, keepdims=True)
+    den = np.maximum(np.abs(rs) + floor, 1e-300)
+    return float(np.max(np.abs(xs - rs) / den))
+
+
 def state_errors(C, n, m, Cr, nr, mr, lead: int = 2):
     """Errors of a final state against the oracle's.  The representation is
     unique only up to (C e^{-c}, n e^{-c}, m + c), so C and n are brought to the

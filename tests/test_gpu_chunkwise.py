@@ -3,13 +3,14 @@ fp64 oracle, on the five workloads (full size: the GPU runs every head, the
 oracle a fixed sample of heads) and on edge cases."""
 from __future__ import annotations
 
+import numpy as np
 import pytest
 import torch
 
 import oracle
 import workloads
-from helpers import (TOL_BF16, TOL_F32, finite, gather_heads, has_gpu, log, nan_like,
-                     sample_heads, slice_rel_err, state_errors, to_dev)
+from helpers import (TOL_BF16, TOL_F32, elem_rel_err, f64, finite, gather_heads, has_gpu, log,
+                     nan_like, sample_heads, slice_rel_err, state_errors, to_dev)
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not has_gpu(), reason="needs a GPU")]
@@ -48,7 +49,11 @@ def compare(gpu, ref, tol, heads=None, label=""):
     hr, Cr, nr, mr = ref
     e_h = slice_rel_err(h, hr)
     eC, en, em = state_errors(C1, n1, m1, Cr, nr, mr)
-    log(f"  {label}: h {e_h:.2e} C {eC:.2e} n {en:.2e} m {em:.2e} (tol {tol:g})")
+    # elementwise diagnostic (logged only): h, and C~ brought to the oracle's m
+    scale = np.exp(f64(m1) - mr)[..., None, None]
+    d_h, d_C = elem_rel_err(h, hr), elem_rel_err(f64(C1) * scale, Cr)
+    log(f"  {label}: h {e_h:.2e} C {eC:.2e} n {en:.2e} m {em:.2e} (tol {tol:g}); "
+        f"elementwise h {d_h:.1e} C {d_C:.1e}")
     assert max(e_h, eC, en, em) < tol, (e_h, eC, en, em)
     return e_h, eC, en, em
 
@@ -226,8 +231,9 @@ def test_deterministic():
                                                      ("bf16", 32, 64, 48, 0), ("f32", 16, 64, 32, 0),
                                                      ("bf16", 64, 256, 128, 9), ("f32", 16, 64, 32, 5)])
 def test_every_output_written(dtype, chunk, dqk, dv, tail):
-    """Outputs pre-filled with NaN come back finite: every element was written
-    (also the tokens of a last, shorter chunk)."""
+    """Outputs pre-filled with NaN (h and the final state C1, n1, m1) come back
+    finite: every element was written (also the tokens of a last, shorter
+    chunk)."""
     cfg = workloads.Config("canary", 8, dtype, 2, 3, 4 * chunk + tail, dqk, dv, (chunk,), (0.0, 1.0),
                            (3.0, 1.0), (0.0, 1.0), True)
     inp = workloads.make_chunkwise_inputs(cfg)
@@ -235,9 +241,13 @@ def test_every_output_written(dtype, chunk, dqk, dv, tail):
     d = to_dev(inp)
     M = _M()
     out = nan_like(tuple(d["v"].shape), d["q"].dtype)
+    B, H, dqk_, dv_ = cfg.B, cfg.H, cfg.dqk, cfg.dv
+    st = (nan_like((B, H, dqk_, dv_), torch.float32), nan_like((B, H, dqk_), torch.float32),
+          nan_like((B, H), torch.float32))
     h, (C1, n1, m1) = M.mlstm_fwd_chunkwise(d["q"], d["k"], d["v"], d["i_pre"], d["f_pre"],
                                             d["o_pre"], d["C0"], d["n0"], d["m0"], chunk=chunk,
-                                            out=out)
+                                            out=out, state_out=st)
+    assert C1 is st[0] and n1 is st[1] and m1 is st[2]
     torch.cuda.synchronize()
     assert finite(h) and finite(C1) and finite(n1) and finite(m1)
 
