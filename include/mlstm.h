@@ -33,7 +33,8 @@
  * q, k, v, o~, h and C~ must be 16-byte aligned (the kernels use 16-byte
  * vector accesses on them; mlstm_step needs this only for v and C~); every
  * other pointer needs 4-byte alignment.  The library allocates nothing and keeps no
- * state between calls except a per-thread error string; it is reentrant.
+ * state between calls except a per-thread error string (and the fixed device
+ * scratch of mlstm_fwd_chunkwise_noalloc); it is reentrant.
  * Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
  * stream); the library never synchronizes.  Argument checks run on the host
  * before anything is enqueued; a failed check enqueues nothing.  A launch
@@ -120,6 +121,32 @@ mlstm_status_t mlstm_fwd_chunkwise(const mlstm_problem_t* p, int64_t chunk,
 /* Workspace needed by mlstm_fwd_chunkwise for this problem (bytes). */
 mlstm_status_t mlstm_fwd_chunkwise_workspace_bytes(const mlstm_problem_t* p,
                                                    int64_t chunk, size_t* bytes);
+
+/*
+ * mlstm_fwd_chunkwise without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  It computes exactly what
+ * mlstm_fwd_chunkwise computes, with the same kernels, and allocates nothing:
+ * where that call needs a workspace (T not a multiple of `chunk` on the bf16
+ * matrix-core path: B*H*(d_qk*d_v + d_qk + 1) floats), it uses a fixed
+ * device array of 64 MiB that the library holds on every GPU it runs on
+ * until the process ends.
+ *   Arguments, layouts and rules: as mlstm_fwd_chunkwise.  `stream` must
+ *   belong to the current device (NULL: its null stream).
+ *   A problem that needs more than 64 MiB of workspace returns
+ *   MLSTM_ERR_UNSUPPORTED (mlstm_fwd_chunkwise_workspace_bytes gives the
+ *   size) and enqueues nothing.
+ *   Calls on one GPU share that GPU's array: calls whose execution overlaps
+ *   on one GPU (on two streams, or from two threads) race on it and must be
+ *   ordered by the caller.  Nothing in the array needs clearing between
+ *   calls.
+ */
+mlstm_status_t mlstm_fwd_chunkwise_noalloc(const mlstm_problem_t* p, int64_t chunk,
+                                           const void* q, const void* k, const void* v,
+                                           const float* i_pre, const float* f_pre,
+                                           const void* o_pre, const float* C0,
+                                           const float* n0, const float* m0, void* h,
+                                           float* C1, float* n1, float* m1, void* stream);
 
 /*
  * Parallel (quadratic) forward pass (section 3, "The Parallel Dual Form":

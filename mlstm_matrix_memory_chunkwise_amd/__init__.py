@@ -30,7 +30,8 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = [
-    "mlstm_fwd_chunkwise", "mlstm_fwd_parallel", "mlstm_step", "mlstm_bwd_chunkwise",
+    "mlstm_fwd_chunkwise", "mlstm_fwd_chunkwise_noalloc", "mlstm_fwd_parallel", "mlstm_step",
+    "mlstm_bwd_chunkwise",
     "mlstm_bwd_chunkwise_workspace_bytes", "mlstm_groupnorm_ogate", "mlstm_causal_conv1d",
     "mlstm_slstm_fwd", "SlstmProblem",
     "mlstm_fwd_chunkwise_workspace_bytes", "mlstm_fwd_parallel_workspace_bytes",
@@ -86,6 +87,8 @@ def load_library():
     seq = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.mlstm_fwd_chunkwise.argtypes = [PP, i64] + seq
     lib.mlstm_fwd_chunkwise.restype = ctypes.c_int
+    lib.mlstm_fwd_chunkwise_noalloc.argtypes = [PP, i64] + [vp] * 13 + [vp]
+    lib.mlstm_fwd_chunkwise_noalloc.restype = ctypes.c_int
     lib.mlstm_fwd_parallel.argtypes = [PP] + seq
     lib.mlstm_fwd_parallel.restype = ctypes.c_int
     lib.mlstm_step.argtypes = [PP] + [vp] * 14
@@ -259,6 +262,26 @@ def mlstm_fwd_chunkwise(q, k, v, i_pre, f_pre, o_pre=None, C0=None, n0=None, m0=
                                    _ptr(m0), _ptr(h), _ptr(C1), _ptr(n1), _ptr(m1),
                                    _ptr(workspace), wbytes, _stream_handle(stream)))
     return h, ((C1, n1, m1) if return_state else None)
+
+
+def mlstm_fwd_chunkwise_noalloc(q, k, v, i_pre, f_pre, o_pre=None, C0=None, n0=None, m0=None, *,
+                                out, state_out=None, chunk: int = 64, fgate="sigmoid",
+                                stream=None):
+    """mlstm_fwd_chunkwise through the entry point that allocates nothing (its
+    scratch is a fixed device array of the library).  The caller passes every
+    output: ``out`` (h) and optionally ``state_out`` = (C1, n1, m1).  Returns
+    (h, (C1, n1, m1)) or (h, None)."""
+    lib = load_library()
+    p, (q, k, v, i_pre, f_pre, o_pre, C0, n0, m0) = _seq_problem(
+        q, k, v, i_pre, f_pre, o_pre, C0, n0, m0, fgate)
+    if out is None:
+        raise ValueError("out is required (this entry point allocates nothing)")
+    h, C1, n1, m1 = _outputs(p, q, out, state_out is not None, state_out)
+    _check(lib.mlstm_fwd_chunkwise_noalloc(ctypes.byref(p), int(chunk), _ptr(q), _ptr(k), _ptr(v),
+                                           _ptr(i_pre), _ptr(f_pre), _ptr(o_pre), _ptr(C0),
+                                           _ptr(n0), _ptr(m0), _ptr(h), _ptr(C1), _ptr(n1),
+                                           _ptr(m1), _stream_handle(stream)))
+    return h, ((C1, n1, m1) if state_out is not None else None)
 
 
 @_allocates_on_stream

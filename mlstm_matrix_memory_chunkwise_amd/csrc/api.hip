@@ -11,6 +11,54 @@
 #include "../../include/mlstm.h"
 #include "kernels.hpp"
 
+#include <mutex>
+
+// Fixed device scratch of mlstm_fwd_chunkwise_noalloc, for callers that cannot
+// allocate.  Every GPU the library runs on holds one copy of this array (in
+// its own memory, at its own address) until the process ends.  In host code
+// `scratch` names a host-side stand-in, never a device address: the address
+// of a device's copy comes from hipGetSymbolAddress, looked up once per
+// device with that device current (scratch_address below), and only that
+// address is handed to kernels.  Calls on one GPU share its copy, so calls
+// that overlap in time on one GPU race; what the kernels read from it they
+// first write in the same call (the state carried from the matrix-core
+// kernel to the tail kernel), so nothing needs clearing between calls.
+static constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Address of the current device's copy of `scratch`; the stream (NULL: the
+// null stream of the current device) must belong to the current device.
+hipError_t scratch_address(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (stream) {
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) return e;
+    if (sdev != dev) return hipErrorInvalidDevice;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
 namespace {
 
 thread_local char g_detail[512] = "";
@@ -352,6 +400,70 @@ mlstm_status_t bwd_empty(const mlstm_problem_t* p, int64_t chunk, const float* C
                        "backward of an empty sequence");
 }
 
+
+// The chunkwise forward pass behind both entry points.  With fixed_scratch
+// the workspace is the library's own device array (below) instead of the
+// caller's (workspace, workspace_bytes are then ignored); every check still
+// runs before the first HIP call.
+mlstm_status_t fwd_chunkwise(const mlstm_problem_t* p, int64_t chunk, const void* q,
+                             const void* k, const void* v, const float* i_pre,
+                             const float* f_pre, const void* o_pre, const float* C0,
+                             const float* n0, const float* m0, void* h, float* C1, float* n1,
+                             float* m1, void* workspace, size_t workspace_bytes,
+                             bool fixed_scratch, void* stream) {
+  if (p && check_problem(p, true) == MLSTM_OK && seq_is_empty(p)) {
+    const mlstm_status_t sc = check_chunk(p, chunk);
+    if (sc != MLSTM_OK) return sc;
+    return seq_empty(p, C0, n0, m0, C1, n1, m1, stream);
+  }
+  mlstm::SeqArgs a;
+  mlstm_status_t s = check_seq(p, q, k, v, i_pre, f_pre, o_pre, C0, n0, m0, h, C1, n1, m1, &a);
+  if (s != MLSTM_OK) return s;
+  s = check_chunk(p, chunk);
+  if (s != MLSTM_OK) return s;
+  const FwdPlan f = fwd_plan(a, chunk);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (fixed_scratch) {
+    if (f.need > kScratchBytes)
+      return fail(MLSTM_ERR_UNSUPPORTED,
+                  "this problem needs %zu bytes of scratch; the fixed scratch of "
+                  "mlstm_fwd_chunkwise_noalloc holds %zu (use mlstm_fwd_chunkwise with a workspace)",
+                  f.need, kScratchBytes);
+    workspace = nullptr;
+    workspace_bytes = 0;
+    if (f.need > 0) {   // the first HIP call of this path
+      const hipError_t e = scratch_address(st, &workspace);
+      if (e != hipSuccess) return device_status(e, "fixed scratch");
+      workspace_bytes = kScratchBytes;
+    }
+  } else {
+    if (workspace_bytes < f.need || (f.need > 0 && !workspace))
+      return fail(MLSTM_ERR_INVALID_ARG, "workspace of %zu bytes given, %zu needed",
+                  workspace_bytes, f.need);
+    if (f.need > 0 && !aligned16(workspace))
+      return fail(MLSTM_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+    s = check_seq_workspace(p, q, k, v, i_pre, f_pre, o_pre, C0, n0, m0, h, C1, n1, m1, workspace,
+                            f.need);
+    if (s != MLSTM_OK) return s;
+  }
+  if (!f.mfma) return device_status(mlstm::launch_chunk_valu(a, chunk, st), "chunkwise (valu)");
+  if (!f.tail)
+    return device_status(mlstm::launch_chunk_mfma(a, chunk, workspace, st), "chunkwise (mfma)");
+  const size_t BH = static_cast<size_t>(a.B * a.H);
+  float* midC = reinterpret_cast<float*>(static_cast<char*>(workspace) + f.mid_off);
+  float* midn = midC + BH * a.dqk * a.dv;
+  float* midm = midn + BH * a.dqk;
+  mlstm::SeqArgs head = a;   // tokens 0 .. Tm-1 on MFMA, state into the workspace
+  head.T = f.Tm;
+  head.C1 = midC; head.n1 = midn; head.m1 = midm;
+  s = device_status(mlstm::launch_chunk_mfma(head, chunk, workspace, st), "chunkwise (mfma)");
+  if (s != MLSTM_OK) return s;
+  mlstm::SeqArgs tail = a;   // tokens Tm .. T-1 from that state
+  tail.t0 = f.Tm;
+  tail.C0 = midC; tail.n0 = midn; tail.m0 = midm;
+  return device_status(mlstm::launch_chunk_valu(tail, chunk, st), "chunkwise tail (valu)");
+}
+
 }  // namespace
 
 extern "C" {
@@ -387,42 +499,18 @@ mlstm_status_t mlstm_fwd_chunkwise(const mlstm_problem_t* p, int64_t chunk, cons
                                    const float* n0, const float* m0, void* h, float* C1,
                                    float* n1, float* m1, void* workspace,
                                    size_t workspace_bytes, void* stream) {
-  if (p && check_problem(p, true) == MLSTM_OK && seq_is_empty(p)) {
-    const mlstm_status_t sc = check_chunk(p, chunk);
-    if (sc != MLSTM_OK) return sc;
-    return seq_empty(p, C0, n0, m0, C1, n1, m1, stream);
-  }
-  mlstm::SeqArgs a;
-  mlstm_status_t s = check_seq(p, q, k, v, i_pre, f_pre, o_pre, C0, n0, m0, h, C1, n1, m1, &a);
-  if (s != MLSTM_OK) return s;
-  s = check_chunk(p, chunk);
-  if (s != MLSTM_OK) return s;
-  const FwdPlan f = fwd_plan(a, chunk);
-  if (workspace_bytes < f.need || (f.need > 0 && !workspace))
-    return fail(MLSTM_ERR_INVALID_ARG, "workspace of %zu bytes given, %zu needed",
-                workspace_bytes, f.need);
-  if (f.need > 0 && !aligned16(workspace))
-    return fail(MLSTM_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
-  s = check_seq_workspace(p, q, k, v, i_pre, f_pre, o_pre, C0, n0, m0, h, C1, n1, m1, workspace,
-                          f.need);
-  if (s != MLSTM_OK) return s;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if (!f.mfma) return device_status(mlstm::launch_chunk_valu(a, chunk, st), "chunkwise (valu)");
-  if (!f.tail)
-    return device_status(mlstm::launch_chunk_mfma(a, chunk, workspace, st), "chunkwise (mfma)");
-  const size_t BH = static_cast<size_t>(a.B * a.H);
-  float* midC = reinterpret_cast<float*>(static_cast<char*>(workspace) + f.mid_off);
-  float* midn = midC + BH * a.dqk * a.dv;
-  float* midm = midn + BH * a.dqk;
-  mlstm::SeqArgs head = a;   // tokens 0 .. Tm-1 on MFMA, state into the workspace
-  head.T = f.Tm;
-  head.C1 = midC; head.n1 = midn; head.m1 = midm;
-  s = device_status(mlstm::launch_chunk_mfma(head, chunk, workspace, st), "chunkwise (mfma)");
-  if (s != MLSTM_OK) return s;
-  mlstm::SeqArgs tail = a;   // tokens Tm .. T-1 from that state
-  tail.t0 = f.Tm;
-  tail.C0 = midC; tail.n0 = midn; tail.m0 = midm;
-  return device_status(mlstm::launch_chunk_valu(tail, chunk, st), "chunkwise tail (valu)");
+  return fwd_chunkwise(p, chunk, q, k, v, i_pre, f_pre, o_pre, C0, n0, m0, h, C1, n1, m1,
+                       workspace, workspace_bytes, false, stream);
+}
+
+mlstm_status_t mlstm_fwd_chunkwise_noalloc(const mlstm_problem_t* p, int64_t chunk,
+                                           const void* q, const void* k, const void* v,
+                                           const float* i_pre, const float* f_pre,
+                                           const void* o_pre, const float* C0, const float* n0,
+                                           const float* m0, void* h, float* C1, float* n1,
+                                           float* m1, void* stream) {
+  return fwd_chunkwise(p, chunk, q, k, v, i_pre, f_pre, o_pre, C0, n0, m0, h, C1, n1, m1,
+                       nullptr, 0, true, stream);
 }
 
 mlstm_status_t mlstm_bwd_chunkwise_workspace_bytes(const mlstm_problem_t* p, int64_t chunk,

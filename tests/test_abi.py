@@ -448,3 +448,37 @@ def test_slstm_rejections(lib):
     assert r == M.MLSTM_ERR_INVALID_ARG and "R" in det and "aligned" in det
     r, det = slstm_call(lib, h=ctypes.c_void_p(FAKE + 64))                # inside wx
     assert r == M.MLSTM_ERR_INVALID_ARG and "overlaps" in det
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch(lib):
+    """mlstm_fwd_chunkwise_noalloc: a ragged bf16 problem whose carried state
+    (B*H*(d_qk*d_v + d_qk + 1) floats) exceeds the fixed 64 MiB scratch is
+    refused on the host with MLSTM_ERR_UNSUPPORTED, naming the size; one that
+    fits gets past that check (and here, without a GPU, fails on the device
+    lookup instead)."""
+    names = ["q", "k", "v", "i", "f", "o", "C0", "n0", "m0", "h", "C1", "n1", "m1"]
+
+    def call(p):
+        vals = dict(zip(names, ptrs(len(names))))
+        for n in ("o", "C0", "n0", "m0", "C1", "n1", "m1"):
+            vals[n] = None
+        r = lib.mlstm_fwd_chunkwise_noalloc(ctypes.byref(p), 64, *(vals[n] for n in names), None)
+        return r, lib.mlstm_last_error_detail().decode()
+
+    big = P(B=1, H=128, T=129, dqk=256, dv=512, qkv=1)
+    need = M.mlstm_fwd_chunkwise_workspace_bytes(big, 64)
+    assert need > 64 << 20
+    r, det = call(big)
+    assert r == M.MLSTM_ERR_UNSUPPORTED and str(need) in det and "noalloc" in det, det
+    # a problem without a tail needs no scratch at all; nor does an empty one
+    assert M.mlstm_fwd_chunkwise_workspace_bytes(P(B=1, H=128, T=128, dqk=256, dv=512, qkv=1),
+                                                 64) == 0
+    small = P(B=1, H=2, T=129, dqk=256, dv=512, qkv=1)
+    r, det = call(small)
+    if not torch_has_gpu():
+        assert r == M.MLSTM_ERR_DEVICE, det
+
+
+def torch_has_gpu():
+    import torch
+    return torch.cuda.is_available()
