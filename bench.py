@@ -6,13 +6,17 @@ o-gate preactivation, random initial state carried in and the final state
 written out.  value = tokens/s (B*T tokens per pass).  Also reported on the
 same line: the decode step (mlstm_step) on its workload (B=128, H=8, d=512,
 256 consecutive in-place steps) as GB/s against 8 TB/s, the chunk-128
-variant, the parallel form, the roofline of the dominant kernel, and the fp64
-CPU oracle timed on a bounded sample of the chunkwise workload.
+variant, the variant without o-gate and the cell followed by the group
+normalization pass, the long-context workload (B=1, H=16, T=65536, d_qk=256,
+d_v=512, chunk 128), the backward pass, the block operations, the sLSTM
+cell, the roofline of the dominant kernel, and the fp64 CPU oracle timed on a
+bounded sample of the chunkwise workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--chunk 64]
-                       [--skip-cpu] [--skip-step] [--skip-extra]
-       python bench.py --profile-workload   (one chunkwise pass, one decode
-           step and a 1 GiB copy, for rocprofv3 counter runs; prints nothing)
+                       [--skip-cpu] [--skip-step] [--skip-extra] [--skip-long]
+       python bench.py --profile-workload   (one chunkwise pass and its
+           backward, one decode step, the block operations and a 1 GiB
+           copy, for rocprofv3 counter runs; prints nothing)
 
 roofline.traffic is the HBM traffic per launch of the dominant kernel from
 the committed counter summary (profiles/hbm_traffic.txt: FETCH_SIZE and
@@ -186,7 +190,16 @@ def profile_workload():
     M.mlstm_fwd_chunkwise(d["q"], d["k"], d["v"], d["i_pre"], d["f_pre"], d["o_pre"],
                           d["C0"], d["n0"], d["m0"], chunk=64, out=h)
     torch.cuda.synchronize()
-    del d, h
+    # the backward of the same pass (chunk 64), as timed by the bench
+    gen = torch.Generator(device="cpu").manual_seed(cfg.seed + 1)
+    dh = torch.randn((cfg.B, cfg.H, cfg.T, cfg.dv), generator=gen).to(torch.bfloat16).to(dev)
+    dC1 = torch.randn((cfg.B, cfg.H, cfg.dqk, cfg.dv), generator=gen).to(dev)
+    dn1 = torch.randn((cfg.B, cfg.H, cfg.dqk), generator=gen).to(dev)
+    M.mlstm_bwd_chunkwise(d["q"], d["k"], d["v"], d["i_pre"], d["f_pre"], d["o_pre"],
+                          d["C0"], d["n0"], d["m0"], h, dh, dC1, dn1, chunk=64)
+    torch.cuda.synchronize()
+    del d, h, dh, dC1, dn1
+    torch.cuda.empty_cache()
     cfg3 = workloads.CONFIGS["step_d512"]
     s = {k: (None if v is None else v.to(dev)) for k, v in workloads.make_step_inputs(cfg3).items()}
     M.mlstm_step(s["q"][0], s["k"][0], s["v"][0], s["i_pre"][0], s["f_pre"][0], s["o_pre"][0],
@@ -228,6 +241,7 @@ def main():
     ap.add_argument("--skip-bwd", action="store_true")
     ap.add_argument("--skip-block", action="store_true")
     ap.add_argument("--skip-slstm", action="store_true")
+    ap.add_argument("--skip-long", action="store_true")
     ap.add_argument("--profile-workload", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -346,6 +360,32 @@ def main():
         result["no_ogate"] = {"ms": ms3, "tokens_per_s": B * T / (ms3 / 1e3),
                               "mfma_frac": f3 / (ms3 / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                               "hbm_frac": b3 / (ms3 / 1e3) / 1e9 / HBM_PEAK_GBS}
+        # the block's gating done after the per-head normalization: the cell
+        # without its gate, then group normalization + o-gate on its output,
+        # against the cell with its own gate (what the normalization pass costs
+        # on top of the cell)
+        g7 = torch.Generator(device="cpu").manual_seed(cfg.seed + 7)
+        gamma = (torch.randn((H, dv), generator=g7) * 0.5 + 1).to(dev)
+        beta = (torch.randn((H, dv), generator=g7) * 0.5).to(dev)
+        y = torch.empty_like(h)
+
+        def run_pipe():
+            M.mlstm_fwd_chunkwise(d["q"], d["k"], d["v"], d["i_pre"], d["f_pre"], None,
+                                  d["C0"], d["n0"], d["m0"], chunk=args.chunk, out=h)
+            M.mlstm_groupnorm_ogate(h, d["o_pre"], gamma, beta, 1e-5, out=y)
+
+        run_pipe()
+        torch.cuda.synchronize()
+        ms_p = time_events(run_pipe, max(3, args.steps // 2), stream)
+        result["cell_then_groupnorm"] = {
+            "workload": "cell without o-gate, then per-head group normalization + o-gate (f32 "
+                        "o~, affine) of its bf16 output, same inputs as the headline pass",
+            "ms": ms_p, "tokens_per_s": B * T / (ms_p / 1e3),
+            "cell_with_ogate_ms": ms_events,
+            "extra_ms_over_cell_with_ogate": ms_p - ms_events,
+            "extra_bytes": 2 * B * H * T * dv * 2,
+        }
+        del y, gamma, beta
 
     # ------------------------------------------------------------ backward
     if not args.skip_bwd:
@@ -531,6 +571,38 @@ def main():
             "algorithmic_bytes_per_step": sb,
         }
         del ds, C, n, m
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ long context
+    if not args.skip_long:
+        cfg4 = workloads.CONFIGS["d256x512_T65536"]
+        log(f"bench: generating {cfg4.describe()}")
+        d4 = {k: (None if v is None else v.to(dev))
+              for k, v in workloads.make_chunkwise_inputs(cfg4).items()}
+        B4, H4, T4, dqk4, dv4, L4 = cfg4.B, cfg4.H, cfg4.T, cfg4.dqk, cfg4.dv, cfg4.chunks[0]
+        h4 = torch.empty((B4, H4, T4, dv4), dtype=torch.bfloat16, device=dev)
+
+        def run_long():
+            M.mlstm_fwd_chunkwise(d4["q"], d4["k"], d4["v"], d4["i_pre"], d4["f_pre"],
+                                  d4["o_pre"], chunk=L4, out=h4)
+
+        for _ in range(2):
+            run_long()
+        torch.cuda.synchronize()
+        ms4 = time_events(run_long, 5, stream)
+        f4, b4 = chunk_algorithmic(B4, H4, T4, dqk4, dv4, L4, 4, state_in=False)
+        gbs4 = b4 / (ms4 / 1e3) / 1e9
+        result["long_context"] = {
+            "workload": f"chunkwise forward, long context: bf16 q/k/v, fp32 gates/o-gate, B={B4} "
+                        f"H={H4} T={T4} d_qk={dqk4} d_v={dv4} chunk={L4}, zero initial state, "
+                        f"final state out",
+            "ms": ms4, "tokens_per_s": B4 * T4 / (ms4 / 1e3),
+            "roofline": {"bound": "hbm", "achieved": gbs4, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs4 / HBM_PEAK_GBS, "traffic": None},
+            "mfma_frac": f4 / (ms4 / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "algorithmic_bytes": b4, "algorithmic_gflop": f4 / 1e9,
+        }
+        del d4, h4
         torch.cuda.empty_cache()
 
     print(json.dumps(result), flush=True)
