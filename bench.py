@@ -144,6 +144,7 @@ KERNEL_SOURCES = {
     "conv": ["block_ops.hip", "common.hpp", "kernels.hpp"],
     "chunkwise": ["chunk_ws.hip", "mfma_util.hpp", "common.hpp", "kernels.hpp"],
     "step": ["step.hip", "common.hpp", "kernels.hpp"],
+    "backward": ["bwd.hip", "bwd_mfma.hip", "mfma_util.hpp", "common.hpp", "kernels.hpp"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 
@@ -157,9 +158,9 @@ def kernel_sources_sha(which):
     return h.hexdigest()
 
 
-def measured_traffic(which):
-    """Calibrated HBM bytes per launch from profiles/hbm_traffic.txt, or None
-    when absent or taken on other kernel sources."""
+def measured_traffic(which, key=None):
+    """Calibrated HBM bytes per launch (or `key`) from profiles/hbm_traffic.txt,
+    or None when absent or taken on other kernel sources."""
     try:
         with open(TRAFFIC_FILE) as fh:
             kv = dict(line.split(":", 1) for line in fh if ":" in line and not line.startswith("#"))
@@ -169,7 +170,7 @@ def measured_traffic(which):
     if kv.get(f"{which}_sources_sha256") != kernel_sources_sha(which):
         return None
     try:
-        return float(kv[f"{which}_calibrated_bytes_per_launch"])
+        return float(kv[key or f"{which}_calibrated_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
 
@@ -417,6 +418,9 @@ def main():
             "algorithmic_bytes": bb,
             "hbm_frac": bb / (ms_b / 1e3) / 1e9 / HBM_PEAK_GBS,
             "mfma_frac": fb / (ms_b / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            # all five launches, from the counters (workspace states and
+            # partial sums included)
+            "traffic_bytes": measured_traffic("backward", "backward_calibrated_bytes_per_pass"),
             "workspace_bytes": wsb.numel(),
         }
         del dh, dC1, dn1, wsb
