@@ -29,6 +29,11 @@
 //   0 of chunk c+1.
 // The VALU-heavy finishing of one chunk thus overlaps the MFMA-heavy state
 // work of the next on every SIMD, and no wave waits for a chunk epilogue.
+// h leaves through a small LDS staging tile: each intra wave computes 16 of
+// the 64 columns, and written directly every 128-byte row of h would reach
+// memory as four 32-byte pieces from four waves (measured: a third more
+// write traffic than h itself).  Staged, a row is written by one wave as
+// eight 16-byte lane stores, one stage after it was computed.
 //
 // Loads are global->LDS DMAs issued from asm, with compile-time vmcnt
 // waits; q/k come in 64-wide d_qk slices through a ring of D+1 slots, v once
@@ -93,6 +98,9 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
   __shared__ __align__(16) bf16_t sNs[4][DQK];
   __shared__ __align__(16) bf16_t sWs[3][4][L];
   __shared__ __align__(256) float sGin[2][2][64];
+  // h of two query tiles (32 rows x the 64 columns), staged so that each
+  // row leaves in one 128-byte piece
+  __shared__ __align__(16) char sH[32 * 128];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -367,6 +375,31 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
     HOp x;
     h_prep(it0, cp, gb, ob, x);
     h_store(o, x, it0, cp);
+  };
+  // in the loop: h of query tiles it0, it0 + 1 into sH (16-byte chunks
+  // swizzled by row), written out after the next barrier as whole rows
+  auto h_stage = [&](const f32x4* o, const HOp& x) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      float hv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) hv[e] = o[r][e] * x.inv[r];
+      if (OM != O_NONE) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hv[e] *= sigmoid_fast(x.ov[r][e]);
+      }
+      const int srow = 16 * r + l16, col = cg * 16 + 4 * g;
+      *reinterpret_cast<uint2*>(sH + srow * 128 + (((col >> 3) ^ (srow & 7)) << 4) + (col & 7) * 2) =
+          make_uint2(cvt2(hv[0], hv[1]), cvt2(hv[2], hv[3]));
+    }
+  };
+  bf16_t* const hrow = static_cast<bf16_t*>(a.h) + head * Ts * dv + vt * TV;
+  auto h_flush = [&](int it0, int cp) {
+    typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+    const int srow = 8 * cg + (lane >> 3), ch = lane & 7;
+    const u32x4v v = *reinterpret_cast<const u32x4v*>(sH + srow * 128 + ((ch ^ (srow & 7)) << 4));
+    bf16_t* dst = hrow + (static_cast<int64_t>(cp) * L + it0 * 16 + srow) * dv + 8 * ch;
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4v*>(dst));
   };
   // value fragments (V^T, this wave's 16 columns) of the chunk in sV
   auto load_vf = [&](bf16x8* dst, uint2* raw) {
@@ -682,11 +715,15 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
         // finishing of chunk c - 1: P V of query tiles 0, 1 at stage 1, their
         // h at stage 2, P V of tiles 2, 3 and the operands of their h at
         // stage 3, and that h at stage 0 of the next chunk
-        if (s == 0 && c > 1) h_store(oacc, hx, 2, c - 2);
+        if (s == 0 && c > 1) h_stage(oacc, hx);
+        if (s == 1 && c > 1) h_flush(2, c - 2);
+        if (s == 3 && c > 0) h_flush(0, c - 1);
         if (c > 0) {
           if (s == 1) pv_tiles(Vp, 0, oacc);
           if (s == 2) {
-            h_tiles(oacc, 0, c - 1, gbp, (c - 1) & 1);
+            HOp hy;
+            h_prep(0, c - 1, gbp, (c - 1) & 1, hy);
+            h_stage(oacc, hy);
             pv_init(2, oacc);   // (the state waves rewrite the readout at stage 3)
           }
           if (s == 3) {
