@@ -308,11 +308,46 @@ bool seq_is_empty(const mlstm_problem_t* p) { return p->B * p->H == 0 || p->T ==
 // kernel continues from that state over the last T % chunk tokens, as one
 // shorter chunk.  Otherwise a single kernel runs the whole sequence (the VALU
 // kernel takes a shorter last chunk by itself).
+//
+// Sequence split.  The MFMA kernels run one workgroup per (head, 64 value
+// columns) through the whole sequence, so a problem with few heads leaves
+// most of the 256 compute units idle.  When that grid has at most kSplitGroups
+// workgroups and the sequence is long, the call instead:
+//   1. runs the state-only pass (chunk_state.hip) over the first half, giving
+//      the exact state at T/2;
+//   2. runs the MFMA kernel once over both halves at the same time: half s of
+//      head h is laid out in memory exactly like head 2h + s of a problem with
+//      2H heads of T/2 tokens, whose initial states are the caller's (or
+//      zero) for s = 0 and the state from step 1 for s = 1;
+//   3. copies the final states of the second halves out.
+// The states of the 2H half-heads live in the workspace.
+constexpr int64_t kSplitGroups = 128;      // half the compute units of an MI355X
+constexpr int64_t kSplitMinTokens = 2048;  // per half
+
+// One block of float32 states for n heads: C~ [n][d_qk][d_v], then n~ [n][d_qk],
+// then m [n], each 256-byte aligned, from byte offset `at`.
+struct StateBlock {
+  size_t C, n, m, end;
+};
+StateBlock state_block(size_t at, size_t nheads, size_t dqk, size_t dv) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  StateBlock b;
+  b.C = up(at);
+  b.n = up(b.C + 4 * nheads * dqk * dv);
+  b.m = up(b.n + 4 * nheads * dqk);
+  b.end = up(b.m + 4 * nheads);
+  return b;
+}
+
 struct FwdPlan {
   bool mfma;        // an MFMA kernel runs tokens 0 .. Tm-1
   bool tail;        // then the VALU kernel runs tokens Tm .. T-1
   int64_t Tm;
   size_t mid_off;   // byte offset of the carried state in the workspace
+  bool split;       // the sequence split above (no tail)
+  StateBlock s_in;  // initial states of the 2 B H half-heads
+  StateBlock s_out; // their final states
+  StateBlock s_mid; // the state at T/2 of the B H heads
   size_t need;      // workspace bytes
 };
 
@@ -326,9 +361,81 @@ FwdPlan fwd_plan(const mlstm::SeqArgs& a, int64_t chunk) {
   const size_t mfma_ws = f.mfma ? mlstm::chunk_mfma_workspace(m, chunk) : 0;
   f.mid_off = (mfma_ws + 255) / 256 * 256;
   const size_t BH = static_cast<size_t>(a.B * a.H);
-  const size_t mid = f.tail ? 4 * BH * (static_cast<size_t>(a.dqk) * a.dv + a.dqk + 1) : 0;
+  const size_t dqk = static_cast<size_t>(a.dqk), dv = static_cast<size_t>(a.dv);
+  const size_t mid = f.tail ? 4 * BH * (dqk * dv + dqk + 1) : 0;
   f.need = f.tail ? f.mid_off + mid : mfma_ws;
+  if (f.mfma && !f.tail) {
+    const int64_t unit = 2 * (chunk > 64 ? chunk : 64);   // halves of whole chunks and of 64
+    mlstm::SeqArgs half = a;
+    half.T = a.T / 2;
+    half.H = 2 * a.H;
+    f.split = a.T % unit == 0 && a.T / 2 >= kSplitMinTokens &&
+              a.B * a.H * (a.dv / 64) <= kSplitGroups && mlstm::chunk_state_supported(half) &&
+              mlstm::chunk_mfma_supported(half, chunk);
+  }
+  if (f.split) {
+    f.s_in = state_block(f.mid_off, 2 * BH, dqk, dv);
+    f.s_out = state_block(f.s_in.end, 2 * BH, dqk, dv);
+    f.s_mid = state_block(f.s_out.end, BH, dqk, dv);
+    f.need = f.s_mid.end;
+  }
   return f;
+}
+
+// Copies `width` bytes per head from n heads of src (pitch spitch) to dst
+// (pitch dpitch), or fills them with zeros when src is NULL.
+hipError_t copy_heads(void* dst, size_t dpitch, const void* src, size_t spitch, size_t width,
+                      size_t nheads, hipStream_t st) {
+  if (src)
+    return hipMemcpy2DAsync(dst, dpitch, src, spitch, width, nheads, hipMemcpyDeviceToDevice, st);
+  return mlstm::launch_fill_words(static_cast<uint32_t*>(dst), static_cast<int64_t>(nheads),
+                                  static_cast<int64_t>(dpitch / 4), 0,
+                                  static_cast<int64_t>(width / 4), 0u, st);
+}
+
+// The sequence split (see fwd_plan) on a checked call.
+hipError_t run_split(const mlstm::SeqArgs& a, int64_t chunk, const FwdPlan& f, void* workspace,
+                     hipStream_t st) {
+  char* w = static_cast<char*>(workspace);
+  const size_t BH = static_cast<size_t>(a.B * a.H);
+  const size_t dqk = static_cast<size_t>(a.dqk), dv = static_cast<size_t>(a.dv);
+  const size_t cB = 4 * dqk * dv, nB = 4 * dqk;   // bytes of one head's C~, n~
+  float* inC = reinterpret_cast<float*>(w + f.s_in.C);
+  float* inN = reinterpret_cast<float*>(w + f.s_in.n);
+  float* inM = reinterpret_cast<float*>(w + f.s_in.m);
+  float* midC = reinterpret_cast<float*>(w + f.s_mid.C);
+  float* midN = reinterpret_cast<float*>(w + f.s_mid.n);
+  float* midM = reinterpret_cast<float*>(w + f.s_mid.m);
+  // 1. the state at T/2
+  mlstm::SeqArgs p1 = a;
+  p1.T = a.T / 2;           // tokens 0 .. T/2 - 1 of each head (heads T apart)
+  p1.C1 = midC; p1.n1 = midN; p1.m1 = midM;
+  hipError_t e = mlstm::launch_chunk_state(p1, st);
+  // initial states of the half-heads: 2h <- the caller's (or zero), 2h+1 <- step 1
+  if (e == hipSuccess) e = copy_heads(inC, 2 * cB, a.C0, cB, cB, BH, st);
+  if (e == hipSuccess) e = copy_heads(inN, 2 * nB, a.n0, nB, nB, BH, st);
+  if (e == hipSuccess) e = copy_heads(inM, 8, a.m0, 4, 4, BH, st);
+  if (e == hipSuccess) e = copy_heads(reinterpret_cast<char*>(inC) + cB, 2 * cB, midC, cB, cB, BH, st);
+  if (e == hipSuccess) e = copy_heads(reinterpret_cast<char*>(inN) + nB, 2 * nB, midN, nB, nB, BH, st);
+  if (e == hipSuccess) e = copy_heads(reinterpret_cast<char*>(inM) + 4, 8, midM, 4, 4, BH, st);
+  if (e != hipSuccess) return e;
+  // 2. both halves at once, as 2 H heads of T/2 tokens
+  mlstm::SeqArgs p2 = a;
+  p2.H = 2 * a.H;
+  p2.T = a.T / 2;
+  p2.Ts = a.T / 2;
+  p2.C0 = inC; p2.n0 = inN; p2.m0 = inM;
+  const bool out = a.C1 != nullptr;
+  p2.C1 = out ? reinterpret_cast<float*>(w + f.s_out.C) : nullptr;
+  p2.n1 = out ? reinterpret_cast<float*>(w + f.s_out.n) : nullptr;
+  p2.m1 = out ? reinterpret_cast<float*>(w + f.s_out.m) : nullptr;
+  e = mlstm::launch_chunk_mfma(p2, chunk, nullptr, st);
+  if (e != hipSuccess || !out) return e;
+  // 3. the final state is that of the second halves
+  e = copy_heads(a.C1, cB, w + f.s_out.C + cB, 2 * cB, cB, BH, st);
+  if (e == hipSuccess) e = copy_heads(a.n1, nB, w + f.s_out.n + nB, 2 * nB, nB, BH, st);
+  if (e == hipSuccess) e = copy_heads(a.m1, 4, w + f.s_out.m + 4, 8, 4, BH, st);
+  return e;
 }
 
 // Backward of a sequence whose length T is not a multiple of the chunk: the
@@ -447,6 +554,7 @@ mlstm_status_t fwd_chunkwise(const mlstm_problem_t* p, int64_t chunk, const void
     if (s != MLSTM_OK) return s;
   }
   if (!f.mfma) return device_status(mlstm::launch_chunk_valu(a, chunk, st), "chunkwise (valu)");
+  if (f.split) return device_status(run_split(a, chunk, f, workspace, st), "chunkwise (split)");
   if (!f.tail)
     return device_status(mlstm::launch_chunk_mfma(a, chunk, workspace, st), "chunkwise (mfma)");
   const size_t BH = static_cast<size_t>(a.B * a.H);

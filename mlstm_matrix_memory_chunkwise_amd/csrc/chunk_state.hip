@@ -1,0 +1,274 @@
+// State-only chunkwise pass: the state (C~, n~, m) after T tokens of every
+// head, from a given initial state, with no outputs.  It carries the state
+// across the first half of a long sequence so that the forward kernels can
+// run both halves at once (see the sequence split in api.hip).
+//
+// Method: xLSTM post (llms.blog), section 3 "Associative Matrix Cell State"
+// (C_t = f_t C_{t-1} + i_t v_t k_t^T, n_t = f_t n_{t-1} + i_t k_t) with the
+// running maximum of section 2 "The Normalizer State and Numerical
+// Stabilization", applied a chunk of 64 tokens at a time as in section 3 "The
+// Parallel Dual Form" split at chunk boundaries: with chunk-local cumulative
+// log forget gates b_j and u_j = i~_j - b_j,
+//   M = max(m_s, max_j u_j),  g_L = exp(m_s - M),  w_j = exp(u_j - M),
+//   C~ <- g_L C~ + K^T diag(w) V,  n~ <- g_L n~ + K^T w,  m <- b_L + M.
+// The result does not depend on the chunk length beyond rounding.
+//
+// Design (CDNA4): one workgroup of 4 waves per (head, 64 value columns); each
+// wave keeps its 16 columns of C~ (all d_qk rows) in float32 registers with a
+// lazy scale (C~ = sig * acc, as in the forward kernels), and a quarter of the
+// n~ rows.  Every wave loads a quarter of each chunk's K and V tiles (and its
+// own copy of the gates) global -> LDS through a ring of 3 chunk slots, two
+// chunks ahead; one barrier per chunk publishes a slot.  Every wave runs the
+// gate scan of the chunk itself (DPP scans), so no gate values cross waves.
+// The update K^T (w V) runs on bf16 MFMA with the K^T fragments read with the
+// LDS transpose read; the n~ increment K^T w on MFMA with w split into three
+// bf16 terms (about 24 bits), as in the forward kernel.
+#include "common.hpp"
+#include "kernels.hpp"
+#include "mfma_util.hpp"
+
+namespace mlstm {
+namespace {
+
+using namespace mk;
+
+constexpr int NW = 4;
+constexpr int NTH = 256;
+constexpr int TV = 64;            // value columns per workgroup
+constexpr int L = 64;             // tokens per chunk
+constexpr int NKS = L / 32;       // 32-token MFMA k-steps
+constexpr int SUBT = L * 128;     // one [64 tokens x 64] bf16 tile (128-byte rows)
+constexpr int D = 2;              // chunks in flight
+constexpr int NSLOT = D + 1;
+
+template <int DQK>
+__global__ __launch_bounds__(NTH, 1) void chunk_state_kernel(SeqArgs a) {
+  constexpr int NSUB = DQK / 64;          // 64-wide d_qk sub-tiles of K
+  constexpr int NCT = DQK / 16;           // 16-row C~ tiles per wave
+  constexpr int NB_K = 2 * NSUB;          // 1 KB K loads per wave per chunk
+  constexpr int NB_V = 2;                 // 1 KB V loads per wave per chunk
+  constexpr int NB = NB_K + NB_V + 2;     // + the wave's two gate loads
+  __shared__ __align__(1024) char sK[NSLOT][NSUB][SUBT];
+  __shared__ __align__(1024) char sV[NSLOT][SUBT];
+  __shared__ __align__(256) float sG[NSLOT][NW][2][L];   // raw gates, one copy per wave
+  __shared__ __align__(16) bf16_t sW[NW][4][L];          // w as three bf16 terms + a zero row
+  __shared__ __align__(16) float sWv[NW][L];             // w / sig' (the update's scale)
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l16 = lane & 15;
+  const int g = lane >> 4;
+
+  const int nvt = static_cast<int>(a.dv / TV);
+  const int64_t nhead = a.B * a.H;
+  int64_t head;
+  int vt;
+  {
+    // the value tiles of one head on one XCD (block ids equal mod 8), so
+    // their shared K reads meet in one L2
+    const int64_t w = blockIdx.x;
+    if (nhead % 8 == 0) {
+      const int64_t grp = w / (8 * nvt), r = w % (8 * nvt);
+      vt = static_cast<int>(r / 8);
+      head = grp * 8 + r % 8;
+    } else {
+      head = w / nvt;
+      vt = static_cast<int>(w % nvt);
+    }
+  }
+  const int dv = static_cast<int>(a.dv);
+  const int64_t Ts = a.Ts;
+  const int nchunks = static_cast<int>(a.T / L);
+  const int b0w = vt * TV + wave * 16;
+  const bf16_t* gk = static_cast<const bf16_t*>(a.k) + head * Ts * DQK;
+  const bf16_t* gv = static_cast<const bf16_t*>(a.v) + head * Ts * dv + vt * TV;
+  const float* gi = a.i_pre + head * Ts;
+  const float* gf = a.f_pre + head * Ts;
+
+  // ---- loads: this wave's quarter of the K and V tiles of chunk c, and its
+  // own copy of the chunk's gates.  A 1 KB load covers 8 rows of a tile:
+  // lane l writes row 8G + l/8, physical 16-byte chunk l%8, which holds the
+  // logical chunk (l%8) ^ ((row/2)%8) (the swz layout).
+  const int ld_r = lane >> 3, ld_pc = lane & 7;
+  auto issue_chunk = [&](int c) {
+    const int cc = c < nchunks ? c : nchunks - 1;   // past the end: a harmless re-read
+    const int slot = c % NSLOT;
+#pragma unroll
+    for (int m = 0; m < NB_K; ++m) {
+      const int item = wave * NB_K + m;             // 0 .. 8 NSUB - 1
+      const int sb = item / 8, G = item % 8;
+      const int row = 8 * G + ld_r;
+      const bf16_t* src = gk + (static_cast<int64_t>(cc) * L + row) * DQK + sb * 64 +
+                          8 * (ld_pc ^ ((row >> 1) & 7));
+      dma16(src, lds_addr(sK[slot][sb] + G * 1024));
+    }
+#pragma unroll
+    for (int m = 0; m < NB_V; ++m) {
+      const int G = wave * NB_V + m;
+      const int row = 8 * G + ld_r;
+      const bf16_t* src = gv + (static_cast<int64_t>(cc) * L + row) * dv + 8 * (ld_pc ^ ((row >> 1) & 7));
+      dma16_nt(src, lds_addr(sV[slot] + G * 1024));
+    }
+    dma4(gi + static_cast<int64_t>(cc) * L + lane, lds_addr(&sG[slot][wave][0][0]));
+    dma4(gf + static_cast<int64_t>(cc) * L + lane, lds_addr(&sG[slot][wave][1][0]));
+  };
+
+  // ---- state.  C~ of this wave's 16 columns: tile t holds the d_qk rows
+  // 32 (t/2) + 8 g + 4 (t%2) + e (the row order in which the update's output
+  // lands, see the K^T fragments below).
+  f32x4 cacc[NCT];
+#pragma unroll
+  for (int t = 0; t < NCT; ++t) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int arow = 32 * (t >> 1) + 8 * g + 4 * (t & 1) + e;
+      cacc[t][e] = a.C0 ? a.C0[(head * DQK + arow) * dv + b0w + l16] : 0.0f;
+    }
+  }
+  // n~ rows of tile `wave` of every sub-tile: lane l holds row nrow(sb)
+  const int nrow0 = 32 * (wave >> 1) + 8 * (l16 >> 2) + 4 * (wave & 1) + (l16 & 3);
+  float nst[NSUB];
+#pragma unroll
+  for (int sb = 0; sb < NSUB; ++sb) nst[sb] = a.C0 ? a.n0[head * DQK + 64 * sb + nrow0] : 0.0f;
+  float m_s = a.C0 ? a.m0[head] : 0.0f;
+  float sig = 1.0f;
+  sW[wave][3][lane] = 0;
+
+  // ---- prologue: chunks 0 .. D-1 in flight
+#pragma unroll
+  for (int c = 0; c < D; ++c) issue_chunk(c);
+
+  const int kr = l16 >> 2, kq = l16 & 3;
+  for (int c = 0; c < nchunks; ++c) {
+    const int slot = c % NSLOT;
+    // this chunk's loads were issued D chunks ago; (D - 1) NB loads of this
+    // wave came after them
+    wait_vm<(D - 1) * NB>();
+    __syncthreads();
+    issue_chunk(c + D);   // into the slot of chunk c - 1, which every wave has left
+
+    // ---- gate scan (each wave its own copy): lane j = token j of the chunk
+    const float xi = sG[slot][wave][0][lane];
+    const float lf = log_forget_fast(sG[slot][wave][1][lane], a.fgate_exp);
+    const float bcum = scan_add(lf);
+    const float u = xi - bcum;
+    const float Mx = fmaxf(m_s, scan_max(u));
+    const float ML = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, Mx), L - 1));
+    const float bL = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bcum), L - 1));
+    const float gL = __expf(m_s - ML);
+    const float wj = __expf(u - ML);
+    // lazy scale: C~_new = g_L C~ + K^T (w V) = sig' (acc + K^T ((w / sig') V)),
+    // sig' = g_L sig; when sig' gets tiny the accumulators take g_L sig now
+    const bool renorm = gL * sig < 0x1p-64f;
+    const float sig_new = renorm ? 1.0f : gL * sig;
+    split3_bf16(wj, sW[wave][0][lane], sW[wave][1][lane], sW[wave][2][lane]);
+    sWv[wave][lane] = wj * __builtin_amdgcn_rcpf(sig_new);
+    m_s = bL + ML;
+
+    // w (three terms) as the A operand of the n~ increment, and w / sig' for
+    // this lane's tokens 32 ks + 8 g + 0..7 (wave-private LDS: written and
+    // read by this wave, in order)
+    uint4 Wx[NKS];
+    bf16x8 wVf[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      Wx[ks] = *reinterpret_cast<const uint4*>(&sW[wave][l16 & 3][32 * ks + 8 * g]);
+      const float4 w0 = *reinterpret_cast<const float4*>(&sWv[wave][32 * ks + 8 * g]);
+      const float4 w1 = *reinterpret_cast<const float4*>(&sWv[wave][32 * ks + 8 * g + 4]);
+      // V^T fragment of this wave's 16 columns: lane (g, c) gets column c
+      // for tokens 32 ks + 8 g + 0..7
+      const int col = wave * 16 + 4 * kq;
+      const uint2 lo = lds_tr(sV[slot], swz(32 * ks + 8 * g + kr, col));
+      const uint2 hi = lds_tr(sV[slot], swz(32 * ks + 8 * g + 4 + kr, col));
+      float xw[8];
+      xw[0] = bf_lo(lo.x) * w0.x; xw[1] = bf_hi(lo.x) * w0.y;
+      xw[2] = bf_lo(lo.y) * w0.z; xw[3] = bf_hi(lo.y) * w0.w;
+      xw[4] = bf_lo(hi.x) * w1.x; xw[5] = bf_hi(hi.x) * w1.y;
+      xw[6] = bf_lo(hi.y) * w1.z; xw[7] = bf_hi(hi.y) * w1.w;
+      wVf[ks] = cvt8(xw);
+    }
+    if (renorm) {
+      const float f = gL * sig;
+#pragma unroll
+      for (int t = 0; t < NCT; ++t) cacc[t] *= f;
+    }
+    sig = sig_new;
+
+    // ---- update, one 64-row sub-tile of K at a time.  The A operand of C~
+    // tile (sb, tl) is the K^T fragment: lane (g, c) holds the d_qk row
+    // 64 sb + 32 (tl/2) + 8 (c/4) + 4 (tl%2) + c%4 for tokens 32 ks + 8 g +
+    // 0..7 (two transposed reads of 4 tokens each).  Tile tl = wave of each
+    // sub-tile also feeds this wave's n~ rows.
+#pragma unroll
+    for (int sb = 0; sb < NSUB; ++sb) {
+      const char* Kb = sK[slot][sb];
+      uint2 Klo[NKS][4], Khi[NKS][4];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+        for (int tl = 0; tl < 4; ++tl) {
+          const int col = 32 * (tl >> 1) + 8 * kq + 4 * (tl & 1);
+          Klo[ks][tl] = lds_tr(Kb, swz(32 * ks + 8 * g + kr, col));
+          Khi[ks][tl] = lds_tr(Kb, swz(32 * ks + 8 * g + 4 + kr, col));
+        }
+      }
+      f32x4 ni = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+        for (int tl = 0; tl < 4; ++tl) {
+          const bf16x8 kf = join(Klo[ks][tl], Khi[ks][tl]);
+          cacc[4 * sb + tl] = mfma16x16x32(kf, wVf[ks], cacc[4 * sb + tl]);
+        }
+        // n~ increment of tile (sb, wave): rows 4r..4r+2 of the A operand are
+        // the three terms of w, so D[4r + e][c] is term e of (K^T w)[row c]
+        bf16x8 kw = join(Klo[ks][0], Khi[ks][0]);
+        if (wave == 1) kw = join(Klo[ks][1], Khi[ks][1]);
+        if (wave == 2) kw = join(Klo[ks][2], Khi[ks][2]);
+        if (wave == 3) kw = join(Klo[ks][3], Khi[ks][3]);
+        ni = mfma16x16x32(as_bf16x8(Wx[ks]), kw, ni);
+      }
+      nst[sb] = gL * nst[sb] + ((ni[0] + ni[1]) + ni[2]);
+    }
+  }
+  // no LDS load may still be in flight when the workgroup ends
+  wait_vm<0>();
+  __syncthreads();
+
+  // ---- final state
+#pragma unroll
+  for (int t = 0; t < NCT; ++t) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int arow = 32 * (t >> 1) + 8 * g + 4 * (t & 1) + e;
+      a.C1[(head * DQK + arow) * dv + b0w + l16] = cacc[t][e] * sig;
+    }
+  }
+  if (vt == 0) {
+    if (g == 0) {
+#pragma unroll
+      for (int sb = 0; sb < NSUB; ++sb) a.n1[head * DQK + 64 * sb + nrow0] = nst[sb];
+    }
+    if (tid == 0) a.m1[head] = m_s;
+  }
+}
+
+}  // namespace
+
+bool chunk_state_supported(const SeqArgs& a) {
+  return a.qkv_bf16 && (a.dqk == 64 || a.dqk == 128 || a.dqk == 256) && a.dv % TV == 0 &&
+         a.T % L == 0 && a.T > 0;
+}
+
+hipError_t launch_chunk_state(const SeqArgs& a, hipStream_t stream) {
+  const unsigned nwg = static_cast<unsigned>(a.B * a.H * (a.dv / TV));
+  switch (a.dqk) {
+    case 64: chunk_state_kernel<64><<<dim3(nwg), dim3(NTH), 0, stream>>>(a); break;
+    case 128: chunk_state_kernel<128><<<dim3(nwg), dim3(NTH), 0, stream>>>(a); break;
+    default: chunk_state_kernel<256><<<dim3(nwg), dim3(NTH), 0, stream>>>(a); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mlstm

@@ -73,6 +73,11 @@ hipError_t launch_chunk_mfma8(const SeqArgs& a, hipStream_t stream);
 // by one chunk; launch_chunk_mfma routes to it first.
 bool chunk_ws_supported(const SeqArgs& a, int64_t chunk);
 hipError_t launch_chunk_ws(const SeqArgs& a, hipStream_t stream);
+// State-only pass: the final (C~, n~, m) after T tokens (T a multiple of 64)
+// from (C0, n0, m0), no outputs; bf16 k/v, d_qk 64/128/256, d_v % 64 == 0.
+// C1, n1, m1 are required.
+bool chunk_state_supported(const SeqArgs& a);
+hipError_t launch_chunk_state(const SeqArgs& a, hipStream_t stream);
 // Generic VALU chunkwise kernel (float32 path; bf16 shapes outside MFMA cover).
 // Tokens t0 .. T-1 in chunks of `chunk`; the last chunk may be shorter.
 hipError_t launch_chunk_valu(const SeqArgs& a, int64_t chunk, hipStream_t stream);

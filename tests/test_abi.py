@@ -482,3 +482,20 @@ def test_noalloc_rejects_problems_beyond_its_scratch(lib):
 def torch_has_gpu():
     import torch
     return torch.cuda.is_available()
+
+
+def test_sequence_split_plan():
+    """A chunkwise call whose grid (B*H*d_v/64 workgroups) covers at most 128
+    compute units and whose halves are at least 2048 tokens (whole chunks and
+    multiples of 64) runs as two halves: the workspace holds the half-heads'
+    states.  Larger grids, short or ragged sequences, and the float32 path do
+    not split (no workspace when T is a multiple of the chunk)."""
+    ws = lambda p, c: M.mlstm_fwd_chunkwise_workspace_bytes(p, c)  # noqa: E731
+    BH, dqk, dv = 16, 256, 512
+    state = BH * (dqk * dv + dqk + 1) * 4
+    assert ws(P(B=1, H=16, T=65536, dqk=256, dv=512, qkv=1), 128) >= 5 * state
+    assert ws(P(B=1, H=2, T=4096, dqk=256, dv=128, qkv=1), 64) > 0
+    assert ws(P(B=8, H=8, T=8192, dqk=256, dv=256, qkv=1), 64) == 0     # 256 workgroups
+    assert ws(P(B=1, H=2, T=2048, dqk=256, dv=128, qkv=1), 64) == 0     # halves too short
+    assert ws(P(B=1, H=2, T=4096 + 64, dqk=256, dv=128, qkv=1), 64) == 0   # halves not multiples of 64
+    assert ws(P(B=1, H=2, T=4096, dqk=256, dv=128, qkv=0), 64) == 0     # float32 path

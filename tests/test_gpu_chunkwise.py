@@ -138,6 +138,15 @@ EDGE = [
     ("ragged: T below one chunk", "bf16", 1, 2, 40, 64, 64, 64, True, True, "sigmoid"),
     ("ragged: T = 1", "bf16", 1, 1, 1, 64, 64, 64, True, True, "sigmoid"),
     ("ragged: fp32 chunk 64, 1 chunk + 36", "f32", 1, 2, 100, 32, 48, 64, True, True, "sigmoid"),
+    # sequence split: few heads and a long sequence; a state-only pass over
+    # the first half, then both halves at once (the oracle runs straight
+    # through, so every token after the split point checks the carried state)
+    ("split: d_qk 256 d_v 128, random state", "bf16", 1, 2, 4096, 256, 128, 64, True, True, "sigmoid"),
+    ("split: chunk 128, d_qk 128, zero state, exp gate, no o-gate", "bf16", 2, 1, 8192, 128, 64, 128,
+     False, False, "exp"),
+    ("split: chunk 32, d_qk 64 d_v 192", "bf16", 1, 3, 4096, 64, 192, 32, True, True, "sigmoid"),
+    ("split: d_qk 256 d_v 128 chunk 128, input-gate spikes", "bf16", 1, 1, 4096, 256, 128, 128, True,
+     True, "sigmoid"),
 ]
 
 
@@ -250,6 +259,58 @@ def test_every_output_written(dtype, chunk, dqk, dv, tail):
     assert C1 is st[0] and n1 is st[1] and m1 is st[2]
     torch.cuda.synchronize()
     assert finite(h) and finite(C1) and finite(n1) and finite(m1)
+
+
+def test_split_matches_unsplit_on_spikes():
+    """The sequence split against the same inputs run without it (the head
+    repeated 17 times: 136 workgroups, so no split), on an input-gate-spike
+    recipe at d_v 512, chunk 128.  At token 306 of this input the normalizer
+    product cancels (n.q = 3.1e-5 against sum |n_a q_a| = 13.2, so h reaches
+    7.7e4): there both paths are 3.9e-2 from the oracle, the float32
+    conditioning of that denominator.  The split must agree with the unsplit
+    run far more closely than that."""
+    names = ("q", "k", "v", "i_pre", "f_pre", "o_pre", "C0", "n0", "m0")
+    cfg = workloads.Config("edge", 7, "bf16", 1, 1, 4096, 256, 512, (128,), (0.0, 15.0), (3.0, 1.0),
+                           (0.0, 1.0), True)
+    inp = workloads.make_chunkwise_inputs(cfg)
+    log("chunkwise split vs unsplit (input-gate spikes, d_v 512, chunk 128)")
+    d = to_dev(inp)
+    M = _M()
+    h1, (C1, n1, m1) = M.mlstm_fwd_chunkwise(*(d[k] for k in names), chunk=128)
+    rep = {k: (None if v is None else v.repeat_interleave(17, dim=1).contiguous()) for k, v in d.items()}
+    h2, (C2, n2, m2) = M.mlstm_fwd_chunkwise(*(rep[k] for k in names), chunk=128)
+    torch.cuda.synchronize()
+    e_h = slice_rel_err(h1.cpu(), h2[:, :1].cpu())
+    eC, en, em = state_errors(C1.cpu(), n1.cpu(), m1.cpu(), C2[:, :1].cpu(), n2[:, :1].cpu(),
+                              m2[:, :1].cpu())
+    hr, *_ = run_oracle(inp)
+    log(f"  split vs unsplit: h {e_h:.2e} C {eC:.2e} n {en:.2e} m {em:.2e}; vs oracle: split "
+        f"{slice_rel_err(h1.cpu(), hr):.2e}, unsplit {slice_rel_err(h2[:, :1].cpu(), hr):.2e}")
+    assert max(e_h, eC, en, em) < 1e-3
+
+
+def test_split_every_output_written():
+    """The sequence split writes every element of h and of the final state
+    (outputs pre-filled with NaN), also without a final state asked for."""
+    cfg = workloads.Config("canary_split", 9, "bf16", 1, 2, 4096, 256, 128, (64,), (0.0, 1.0),
+                           (3.0, 1.0), (0.0, 1.0), True)
+    inp = workloads.make_chunkwise_inputs(cfg)
+    log("chunkwise canary: sequence split")
+    d = to_dev(inp)
+    M = _M()
+    B, H, T, dqk, dv = cfg.B, cfg.H, cfg.T, cfg.dqk, cfg.dv
+    assert M.mlstm_fwd_chunkwise_workspace_bytes(M.Problem(B, H, T, dqk, dv, 1, 0, 0, 0), 64) > 0
+    out = nan_like((B, H, T, dv), torch.bfloat16)
+    st = (nan_like((B, H, dqk, dv), torch.float32), nan_like((B, H, dqk), torch.float32),
+          nan_like((B, H), torch.float32))
+    args = [d[k] for k in ("q", "k", "v", "i_pre", "f_pre", "o_pre", "C0", "n0", "m0")]
+    h, (C1, n1, m1) = M.mlstm_fwd_chunkwise(*args, chunk=64, out=out, state_out=st)
+    out2 = nan_like((B, H, T, dv), torch.bfloat16)
+    h2, none = M.mlstm_fwd_chunkwise(*args, chunk=64, out=out2, return_state=False)
+    torch.cuda.synchronize()
+    assert none is None
+    assert finite(h) and finite(C1) and finite(n1) and finite(m1) and finite(h2)
+    assert torch.equal(h, h2)
 
 
 def test_no_state_out():
