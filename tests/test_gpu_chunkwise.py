@@ -283,10 +283,16 @@ def test_split_matches_unsplit_on_spikes():
     e_h = slice_rel_err(h1.cpu(), h2[:, :1].cpu())
     eC, en, em = state_errors(C1.cpu(), n1.cpu(), m1.cpu(), C2[:, :1].cpu(), n2[:, :1].cpu(),
                               m2[:, :1].cpu())
-    hr, *_ = run_oracle(inp)
+    hr, Cr, nr, mr = run_oracle(inp)
+    s_err = state_errors(C1.cpu(), n1.cpu(), m1.cpu(), Cr, nr, mr)
     log(f"  split vs unsplit: h {e_h:.2e} C {eC:.2e} n {en:.2e} m {em:.2e}; vs oracle: split "
-        f"{slice_rel_err(h1.cpu(), hr):.2e}, unsplit {slice_rel_err(h2[:, :1].cpu(), hr):.2e}")
-    assert max(e_h, eC, en, em) < 1e-3
+        f"h {slice_rel_err(h1.cpu(), hr):.2e} C {s_err[0]:.2e}, unsplit "
+        f"h {slice_rel_err(h2[:, :1].cpu(), hr):.2e}")
+    # h of the two runs agree to far below the bf16 tolerance; the final
+    # states take different rounding paths (the state-only pass carries the
+    # first half) and are each held to the oracle
+    assert e_h < 1e-3
+    assert max(eC, en, em) < TOL_BF16 and max(s_err) < TOL_BF16
 
 
 def test_split_every_output_written():
