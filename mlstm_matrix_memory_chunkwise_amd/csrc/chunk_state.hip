@@ -13,12 +13,15 @@
 //   C~ <- g_L C~ + K^T diag(w) V,  n~ <- g_L n~ + K^T w,  m <- b_L + M.
 // The result does not depend on the chunk length beyond rounding.
 //
-// Design (CDNA4): one workgroup of 4 waves per (head, 64 value columns); each
-// wave keeps its 16 columns of C~ (all d_qk rows) in float32 registers with a
-// lazy scale (C~ = sig * acc, as in the forward kernels), and a quarter of the
-// n~ rows.  Every wave loads a quarter of each chunk's K and V tiles (and its
-// own copy of the gates) global -> LDS through a ring of 3 chunk slots, two
-// chunks ahead; one barrier per chunk publishes a slot.  Every wave runs the
+// Design (CDNA4): one workgroup of 4 waves per (head, 32 value columns): the
+// pass runs where the forward's grid leaves compute units idle, so it uses
+// twice as many workgroups.  Wave w keeps 16 columns (w % 2) of C~ for half
+// of the d_qk rows (w / 2) in float32 registers with a lazy scale (C~ = sig *
+// acc, as in the forward kernels), and a quarter of the n~ rows.  Every wave
+// loads a quarter of each chunk's K tile, and of the 64-column V block that
+// holds the workgroup's columns (and its own copy of the gates), global ->
+// LDS through a ring of 3 chunk slots, two chunks ahead; one barrier per
+// chunk publishes a slot.  Every wave runs the
 // gate scan of the chunk itself (DPP scans), so no gate values cross waves.
 // The update K^T (w V) runs on bf16 MFMA with the K^T fragments read with the
 // LDS transpose read; the n~ increment K^T w on MFMA with w split into three
@@ -34,7 +37,7 @@ using namespace mk;
 
 constexpr int NW = 4;
 constexpr int NTH = 256;
-constexpr int TV = 64;            // value columns per workgroup
+constexpr int TV = 32;            // value columns per workgroup
 constexpr int L = 64;             // tokens per chunk
 constexpr int NKS = L / 32;       // 32-token MFMA k-steps
 constexpr int SUBT = L * 128;     // one [64 tokens x 64] bf16 tile (128-byte rows)
@@ -44,7 +47,7 @@ constexpr int NSLOT = D + 1;
 template <int DQK>
 __global__ __launch_bounds__(NTH, 1) void chunk_state_kernel(SeqArgs a) {
   constexpr int NSUB = DQK / 64;          // 64-wide d_qk sub-tiles of K
-  constexpr int NCT = DQK / 16;           // 16-row C~ tiles per wave
+  constexpr int NCTW = DQK / 32;          // 16-row C~ tiles per wave (half the rows)
   constexpr int NB_K = 2 * NSUB;          // 1 KB K loads per wave per chunk
   constexpr int NB_V = 2;                 // 1 KB V loads per wave per chunk
   constexpr int NB = NB_K + NB_V + 2;     // + the wave's two gate loads
@@ -59,13 +62,15 @@ __global__ __launch_bounds__(NTH, 1) void chunk_state_kernel(SeqArgs a) {
   const int lane = tid & 63;
   const int l16 = lane & 15;
   const int g = lane >> 4;
+  const int cgw = wave & 1;               // 16-column group
+  const int rh = wave >> 1;               // half of the d_qk rows
 
   const int nvt = static_cast<int>(a.dv / TV);
   const int64_t nhead = a.B * a.H;
   int64_t head;
   int vt;
   {
-    // the value tiles of one head on one XCD (block ids equal mod 8), so
+    // the column tiles of one head on one XCD (block ids equal mod 8), so
     // their shared K reads meet in one L2
     const int64_t w = blockIdx.x;
     if (nhead % 8 == 0) {
@@ -80,16 +85,17 @@ __global__ __launch_bounds__(NTH, 1) void chunk_state_kernel(SeqArgs a) {
   const int dv = static_cast<int>(a.dv);
   const int64_t Ts = a.Ts;
   const int nchunks = static_cast<int>(a.T / L);
-  const int b0w = vt * TV + wave * 16;
+  const int vcol = 32 * (vt & 1) + 16 * cgw;      // this wave's columns in the 64-column V block
+  const int b0w = 64 * (vt >> 1) + vcol;          // ... and in the head
   const bf16_t* gk = static_cast<const bf16_t*>(a.k) + head * Ts * DQK;
-  const bf16_t* gv = static_cast<const bf16_t*>(a.v) + head * Ts * dv + vt * TV;
+  const bf16_t* gv = static_cast<const bf16_t*>(a.v) + head * Ts * dv + 64 * (vt >> 1);
   const float* gi = a.i_pre + head * Ts;
   const float* gf = a.f_pre + head * Ts;
 
-  // ---- loads: this wave's quarter of the K and V tiles of chunk c, and its
-  // own copy of the chunk's gates.  A 1 KB load covers 8 rows of a tile:
-  // lane l writes row 8G + l/8, physical 16-byte chunk l%8, which holds the
-  // logical chunk (l%8) ^ ((row/2)%8) (the swz layout).
+  // ---- loads: a quarter of the K tile and of the V block of chunk c, and
+  // this wave's own copy of the chunk's gates.  A 1 KB load covers 8 rows of
+  // a [64 x 64] tile: lane l writes row 8G + l/8, physical 16-byte chunk l%8,
+  // which holds the logical chunk (l%8) ^ ((row/2)%8) (the swz layout).
   const int ld_r = lane >> 3, ld_pc = lane & 7;
   auto issue_chunk = [&](int c) {
     const int cc = c < nchunks ? c : nchunks - 1;   // past the end: a harmless re-read
@@ -108,29 +114,39 @@ __global__ __launch_bounds__(NTH, 1) void chunk_state_kernel(SeqArgs a) {
       const int G = wave * NB_V + m;
       const int row = 8 * G + ld_r;
       const bf16_t* src = gv + (static_cast<int64_t>(cc) * L + row) * dv + 8 * (ld_pc ^ ((row >> 1) & 7));
-      dma16_nt(src, lds_addr(sV[slot] + G * 1024));
+      dma16(src, lds_addr(sV[slot] + G * 1024));
     }
     dma4(gi + static_cast<int64_t>(cc) * L + lane, lds_addr(&sG[slot][wave][0][0]));
     dma4(gf + static_cast<int64_t>(cc) * L + lane, lds_addr(&sG[slot][wave][1][0]));
   };
 
-  // ---- state.  C~ of this wave's 16 columns: tile t holds the d_qk rows
-  // 32 (t/2) + 8 g + 4 (t%2) + e (the row order in which the update's output
-  // lands, see the K^T fragments below).
-  f32x4 cacc[NCT];
+  // ---- state.  The wave's C~ tiles are the 16-row tiles T = rh NCTW + t
+  // (t = 0 .. NCTW-1) of the d_qk rows; tile T holds the rows 32 (T/2) + 8 g +
+  // 4 (T%2) + e (the row order in which the update's output lands, see the
+  // K^T fragments below), i.e. rows 64 sb + 32 (tl/2) + 8 g + 4 (tl%2) + e
+  // with sb = T / 4, tl = T % 4.
+  auto arow_of = [&](int t, int e) {
+    const int T = rh * NCTW + t;
+    return 32 * (T >> 1) + 8 * g + 4 * (T & 1) + e;
+  };
+  f32x4 cacc[NCTW];
 #pragma unroll
-  for (int t = 0; t < NCT; ++t) {
+  for (int t = 0; t < NCTW; ++t) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int arow = 32 * (t >> 1) + 8 * g + 4 * (t & 1) + e;
-      cacc[t][e] = a.C0 ? a.C0[(head * DQK + arow) * dv + b0w + l16] : 0.0f;
-    }
+    for (int e = 0; e < 4; ++e)
+      cacc[t][e] = a.C0 ? a.C0[(head * DQK + arow_of(t, e)) * dv + b0w + l16] : 0.0f;
   }
-  // n~ rows of tile `wave` of every sub-tile: lane l holds row nrow(sb)
-  const int nrow0 = 32 * (wave >> 1) + 8 * (l16 >> 2) + 4 * (wave & 1) + (l16 & 3);
-  float nst[NSUB];
+  // n~: of the wave's tiles, those with t % 2 == cgw; lane l holds the row
+  // 32 (T/2) + 8 (l16/4) + 4 (T%2) + l16%4 of tile T (the column order of the
+  // K^T fragment used as the B operand below)
+  constexpr int NNT = NCTW / 2;
+  auto nrow_of = [&](int j) {
+    const int T = rh * NCTW + 2 * j + cgw;
+    return 32 * (T >> 1) + 8 * (l16 >> 2) + 4 * (T & 1) + (l16 & 3);
+  };
+  float nst[NNT];
 #pragma unroll
-  for (int sb = 0; sb < NSUB; ++sb) nst[sb] = a.C0 ? a.n0[head * DQK + 64 * sb + nrow0] : 0.0f;
+  for (int j = 0; j < NNT; ++j) nst[j] = a.C0 ? a.n0[head * DQK + nrow_of(j)] : 0.0f;
   float m_s = a.C0 ? a.m0[head] : 0.0f;
   float sig = 1.0f;
   sW[wave][3][lane] = 0;
@@ -178,7 +194,7 @@ __global__ __launch_bounds__(NTH, 1) void chunk_state_kernel(SeqArgs a) {
       const float4 w1 = *reinterpret_cast<const float4*>(&sWv[wave][32 * ks + 8 * g + 4]);
       // V^T fragment of this wave's 16 columns: lane (g, c) gets column c
       // for tokens 32 ks + 8 g + 0..7
-      const int col = wave * 16 + 4 * kq;
+      const int col = vcol + 4 * kq;
       const uint2 lo = lds_tr(sV[slot], swz(32 * ks + 8 * g + kr, col));
       const uint2 hi = lds_tr(sV[slot], swz(32 * ks + 8 * g + 4 + kr, col));
       float xw[8];
@@ -191,45 +207,39 @@ __global__ __launch_bounds__(NTH, 1) void chunk_state_kernel(SeqArgs a) {
     if (renorm) {
       const float f = gL * sig;
 #pragma unroll
-      for (int t = 0; t < NCT; ++t) cacc[t] *= f;
+      for (int t = 0; t < NCTW; ++t) cacc[t] *= f;
     }
     sig = sig_new;
 
-    // ---- update, one 64-row sub-tile of K at a time.  The A operand of C~
-    // tile (sb, tl) is the K^T fragment: lane (g, c) holds the d_qk row
+    // ---- update of the wave's tiles.  The A operand of C~ tile T (sub-tile
+    // sb = T/4, tl = T%4) is the K^T fragment: lane (g, c) holds the d_qk row
     // 64 sb + 32 (tl/2) + 8 (c/4) + 4 (tl%2) + c%4 for tokens 32 ks + 8 g +
-    // 0..7 (two transposed reads of 4 tokens each).  Tile tl = wave of each
-    // sub-tile also feeds this wave's n~ rows.
+    // 0..7 (two transposed reads of 4 tokens each).  As a B operand the same
+    // fragment gives the n~ increment of those rows, with the three terms of
+    // w in rows 4r..4r+2 of the A operand: D[4r + e][c] is term e of
+    // (K^T w)[row c].
 #pragma unroll
-    for (int sb = 0; sb < NSUB; ++sb) {
-      const char* Kb = sK[slot][sb];
-      uint2 Klo[NKS][4], Khi[NKS][4];
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-#pragma unroll
-        for (int tl = 0; tl < 4; ++tl) {
-          const int col = 32 * (tl >> 1) + 8 * kq + 4 * (tl & 1);
-          Klo[ks][tl] = lds_tr(Kb, swz(32 * ks + 8 * g + kr, col));
-          Khi[ks][tl] = lds_tr(Kb, swz(32 * ks + 8 * g + 4 + kr, col));
-        }
-      }
-      f32x4 ni = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < NCTW; ++t) {
+      const int T = rh * NCTW + t;
+      const char* Kb = sK[slot][T >> 2];
+      const int tl = T & 3;
+      const int col = 32 * (tl >> 1) + 8 * kq + 4 * (tl & 1);
+      uint2 Klo[NKS], Khi[NKS];
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-#pragma unroll
-        for (int tl = 0; tl < 4; ++tl) {
-          const bf16x8 kf = join(Klo[ks][tl], Khi[ks][tl]);
-          cacc[4 * sb + tl] = mfma16x16x32(kf, wVf[ks], cacc[4 * sb + tl]);
-        }
-        // n~ increment of tile (sb, wave): rows 4r..4r+2 of the A operand are
-        // the three terms of w, so D[4r + e][c] is term e of (K^T w)[row c]
-        bf16x8 kw = join(Klo[ks][0], Khi[ks][0]);
-        if (wave == 1) kw = join(Klo[ks][1], Khi[ks][1]);
-        if (wave == 2) kw = join(Klo[ks][2], Khi[ks][2]);
-        if (wave == 3) kw = join(Klo[ks][3], Khi[ks][3]);
-        ni = mfma16x16x32(as_bf16x8(Wx[ks]), kw, ni);
+        Klo[ks] = lds_tr(Kb, swz(32 * ks + 8 * g + kr, col));
+        Khi[ks] = lds_tr(Kb, swz(32 * ks + 8 * g + 4 + kr, col));
       }
-      nst[sb] = gL * nst[sb] + ((ni[0] + ni[1]) + ni[2]);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        cacc[t] = mfma16x16x32(join(Klo[ks], Khi[ks]), wVf[ks], cacc[t]);
+      if ((t & 1) == cgw) {
+        f32x4 ni = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+          ni = mfma16x16x32(as_bf16x8(Wx[ks]), join(Klo[ks], Khi[ks]), ni);
+        nst[t >> 1] = gL * nst[t >> 1] + ((ni[0] + ni[1]) + ni[2]);
+      }
     }
   }
   // no LDS load may still be in flight when the workgroup ends
@@ -238,17 +248,15 @@ __global__ __launch_bounds__(NTH, 1) void chunk_state_kernel(SeqArgs a) {
 
   // ---- final state
 #pragma unroll
-  for (int t = 0; t < NCT; ++t) {
+  for (int t = 0; t < NCTW; ++t) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int arow = 32 * (t >> 1) + 8 * g + 4 * (t & 1) + e;
-      a.C1[(head * DQK + arow) * dv + b0w + l16] = cacc[t][e] * sig;
-    }
+    for (int e = 0; e < 4; ++e)
+      a.C1[(head * DQK + arow_of(t, e)) * dv + b0w + l16] = cacc[t][e] * sig;
   }
   if (vt == 0) {
     if (g == 0) {
 #pragma unroll
-      for (int sb = 0; sb < NSUB; ++sb) a.n1[head * DQK + 64 * sb + nrow0] = nst[sb];
+      for (int j = 0; j < NNT; ++j) a.n1[head * DQK + nrow_of(j)] = nst[j];
     }
     if (tid == 0) a.m1[head] = m_s;
   }
@@ -257,7 +265,7 @@ __global__ __launch_bounds__(NTH, 1) void chunk_state_kernel(SeqArgs a) {
 }  // namespace
 
 bool chunk_state_supported(const SeqArgs& a) {
-  return a.qkv_bf16 && (a.dqk == 64 || a.dqk == 128 || a.dqk == 256) && a.dv % TV == 0 &&
+  return a.qkv_bf16 && (a.dqk == 64 || a.dqk == 128 || a.dqk == 256) && a.dv % 64 == 0 &&
          a.T % L == 0 && a.T > 0;
 }
 
