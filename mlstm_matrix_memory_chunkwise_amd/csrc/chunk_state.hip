@@ -13,19 +13,22 @@
 //   C~ <- g_L C~ + K^T diag(w) V,  n~ <- g_L n~ + K^T w,  m <- b_L + M.
 // The result does not depend on the chunk length beyond rounding.
 //
-// Design (CDNA4): one workgroup of 4 waves per (head, 32 value columns): the
+// Design (CDNA4): one workgroup of 8 waves per (head, 32 value columns): the
 // pass runs where the forward's grid leaves compute units idle, so it uses
-// twice as many workgroups.  Wave w keeps 16 columns (w % 2) of C~ for half
-// of the d_qk rows (w / 2) in float32 registers with a lazy scale (C~ = sig *
-// acc, as in the forward kernels), and a quarter of the n~ rows.  Every wave
-// loads a quarter of each chunk's K tile, and of the 64-column V block that
-// holds the workgroup's columns (and its own copy of the gates), global ->
-// LDS through a ring of 3 chunk slots, two chunks ahead; one barrier per
-// chunk publishes a slot.  Every wave runs the
-// gate scan of the chunk itself (DPP scans), so no gate values cross waves.
-// The update K^T (w V) runs on bf16 MFMA with the K^T fragments read with the
-// LDS transpose read; the n~ increment K^T w on MFMA with w split into three
-// bf16 terms (about 24 bits), as in the forward kernel.
+// twice as many workgroups.  Wave w keeps 16 columns (w % 2) of C~ for a
+// quarter of the d_qk rows (w / 2) in float32 registers with a lazy scale
+// (C~ = sig * acc, as in the forward kernels), and the n~ rows of half of its
+// row tiles; two waves share each SIMD, so one wave's LDS and MFMA latencies
+// overlap the other's work.  Every wave loads an eighth of each chunk's K
+// tile and of the 64-column V block that holds the workgroup's columns (and
+// its own copy of the next chunk's gates), global -> LDS through a ring of 3
+// chunk slots, two chunks ahead; one barrier per chunk publishes a slot.
+// Every wave runs the gate scan itself (DPP scans, so no gate values cross
+// waves), one chunk ahead: the scan of chunk c + 1 depends only on its gates
+// and on m after chunk c, so it runs beside chunk c's products instead of
+// before them.  The update K^T (w V) runs on bf16 MFMA with the K^T fragments
+// read with the LDS transpose read; the n~ increment K^T w on MFMA with w
+// split into three bf16 terms (about 24 bits), as in the forward kernel.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mfma_util.hpp"
@@ -35,8 +38,8 @@ namespace {
 
 using namespace mk;
 
-constexpr int NW = 4;
-constexpr int NTH = 256;
+constexpr int NW = 8;
+constexpr int NTH = 512;
 constexpr int TV = 32;            // value columns per workgroup
 constexpr int L = 64;             // tokens per chunk
 constexpr int NKS = L / 32;       // 32-token MFMA k-steps
@@ -47,15 +50,16 @@ constexpr int NSLOT = D + 1;
 template <int DQK>
 __global__ __launch_bounds__(NTH, 1) void chunk_state_kernel(SeqArgs a) {
   constexpr int NSUB = DQK / 64;          // 64-wide d_qk sub-tiles of K
-  constexpr int NCTW = DQK / 32;          // 16-row C~ tiles per wave (half the rows)
-  constexpr int NB_K = 2 * NSUB;          // 1 KB K loads per wave per chunk
-  constexpr int NB_V = 2;                 // 1 KB V loads per wave per chunk
-  constexpr int NB = NB_K + NB_V + 2;     // + the wave's two gate loads
+  constexpr int NCTW = DQK / 64;          // 16-row C~ tiles per wave (a quarter of the rows)
+  constexpr int NB_K = NSUB;              // 1 KB K loads per wave per chunk
+  constexpr int NB = NB_K + 1 + 2;        // + one V load and the wave's two gate loads
   __shared__ __align__(1024) char sK[NSLOT][NSUB][SUBT];
   __shared__ __align__(1024) char sV[NSLOT][SUBT];
   __shared__ __align__(256) float sG[NSLOT][NW][2][L];   // raw gates, one copy per wave
-  __shared__ __align__(16) bf16_t sW[NW][4][L];          // w as three bf16 terms + a zero row
-  __shared__ __align__(16) float sWv[NW][L];             // w / sig' (the update's scale)
+  // per chunk parity: w as three bf16 terms + a zero row, and w / sig' (the
+  // update's scale); wave-private
+  __shared__ __align__(16) bf16_t sW[2][NW][4][L];
+  __shared__ __align__(16) float sWv[2][NW][L];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -63,7 +67,7 @@ __global__ __launch_bounds__(NTH, 1) void chunk_state_kernel(SeqArgs a) {
   const int l16 = lane & 15;
   const int g = lane >> 4;
   const int cgw = wave & 1;               // 16-column group
-  const int rh = wave >> 1;               // half of the d_qk rows
+  const int rq = wave >> 1;               // quarter of the d_qk rows
 
   const int nvt = static_cast<int>(a.dv / TV);
   const int64_t nhead = a.B * a.H;
@@ -92,13 +96,19 @@ __global__ __launch_bounds__(NTH, 1) void chunk_state_kernel(SeqArgs a) {
   const float* gi = a.i_pre + head * Ts;
   const float* gf = a.f_pre + head * Ts;
 
-  // ---- loads: a quarter of the K tile and of the V block of chunk c, and
-  // this wave's own copy of the chunk's gates.  A 1 KB load covers 8 rows of
-  // a [64 x 64] tile: lane l writes row 8G + l/8, physical 16-byte chunk l%8,
-  // which holds the logical chunk (l%8) ^ ((row/2)%8) (the swz layout).
+  // ---- loads: an eighth of the K tile and of the V block of chunk c, and
+  // this wave's own copy of the gates of chunk c + 1.  A 1 KB load covers 8
+  // rows of a [64 x 64] tile: lane l writes row 8G + l/8, physical 16-byte
+  // chunk l%8, which holds the logical chunk (l%8) ^ ((row/2)%8) (the swz
+  // layout).
   const int ld_r = lane >> 3, ld_pc = lane & 7;
-  auto issue_chunk = [&](int c) {
+  auto issue_gates = [&](int c) {
     const int cc = c < nchunks ? c : nchunks - 1;   // past the end: a harmless re-read
+    dma4(gi + static_cast<int64_t>(cc) * L + lane, lds_addr(&sG[c % NSLOT][wave][0][0]));
+    dma4(gf + static_cast<int64_t>(cc) * L + lane, lds_addr(&sG[c % NSLOT][wave][1][0]));
+  };
+  auto issue_chunk = [&](int c) {
+    const int cc = c < nchunks ? c : nchunks - 1;
     const int slot = c % NSLOT;
 #pragma unroll
     for (int m = 0; m < NB_K; ++m) {
@@ -109,24 +119,20 @@ __global__ __launch_bounds__(NTH, 1) void chunk_state_kernel(SeqArgs a) {
                           8 * (ld_pc ^ ((row >> 1) & 7));
       dma16(src, lds_addr(sK[slot][sb] + G * 1024));
     }
-#pragma unroll
-    for (int m = 0; m < NB_V; ++m) {
-      const int G = wave * NB_V + m;
-      const int row = 8 * G + ld_r;
+    {
+      const int row = 8 * wave + ld_r;
       const bf16_t* src = gv + (static_cast<int64_t>(cc) * L + row) * dv + 8 * (ld_pc ^ ((row >> 1) & 7));
-      dma16(src, lds_addr(sV[slot] + G * 1024));
+      dma16(src, lds_addr(sV[slot] + wave * 1024));
     }
-    dma4(gi + static_cast<int64_t>(cc) * L + lane, lds_addr(&sG[slot][wave][0][0]));
-    dma4(gf + static_cast<int64_t>(cc) * L + lane, lds_addr(&sG[slot][wave][1][0]));
+    issue_gates(c + 1);
   };
 
-  // ---- state.  The wave's C~ tiles are the 16-row tiles T = rh NCTW + t
-  // (t = 0 .. NCTW-1) of the d_qk rows; tile T holds the rows 32 (T/2) + 8 g +
-  // 4 (T%2) + e (the row order in which the update's output lands, see the
-  // K^T fragments below), i.e. rows 64 sb + 32 (tl/2) + 8 g + 4 (tl%2) + e
-  // with sb = T / 4, tl = T % 4.
+  // ---- state.  The wave's C~ tiles are the 16-row tiles T = rq NCTW + t
+  // (t = 0 .. NCTW-1) of the d_qk rows, all in the K sub-tile T / 4; tile T
+  // holds the rows 32 (T/2) + 8 g + 4 (T%2) + e (the row order in which the
+  // update's output lands, see the K^T fragments below).
   auto arow_of = [&](int t, int e) {
-    const int T = rh * NCTW + t;
+    const int T = rq * NCTW + t;
     return 32 * (T >> 1) + 8 * g + 4 * (T & 1) + e;
   };
   f32x4 cacc[NCTW];
@@ -136,35 +142,29 @@ __global__ __launch_bounds__(NTH, 1) void chunk_state_kernel(SeqArgs a) {
     for (int e = 0; e < 4; ++e)
       cacc[t][e] = a.C0 ? a.C0[(head * DQK + arow_of(t, e)) * dv + b0w + l16] : 0.0f;
   }
-  // n~: of the wave's tiles, those with t % 2 == cgw; lane l holds the row
-  // 32 (T/2) + 8 (l16/4) + 4 (T%2) + l16%4 of tile T (the column order of the
-  // K^T fragment used as the B operand below)
-  constexpr int NNT = NCTW / 2;
-  auto nrow_of = [&](int j) {
-    const int T = rh * NCTW + 2 * j + cgw;
+  // n~: the wave keeps the rows of its tiles T with T % 2 == cgw (so each
+  // tile's rows are kept by one wave); lane l holds the row 32 (T/2) +
+  // 8 (l16/4) + 4 (T%2) + l16%4 of tile T (the column order of the K^T
+  // fragment used as the B operand below)
+  auto n_tile = [&](int t) { return ((rq * NCTW + t) & 1) == cgw; };
+  auto nrow_of = [&](int t) {
+    const int T = rq * NCTW + t;
     return 32 * (T >> 1) + 8 * (l16 >> 2) + 4 * (T & 1) + (l16 & 3);
   };
-  float nst[NNT];
+  float nst[NCTW];
 #pragma unroll
-  for (int j = 0; j < NNT; ++j) nst[j] = a.C0 ? a.n0[head * DQK + nrow_of(j)] : 0.0f;
+  for (int t = 0; t < NCTW; ++t) nst[t] = (a.C0 && n_tile(t)) ? a.n0[head * DQK + nrow_of(t)] : 0.0f;
   float m_s = a.C0 ? a.m0[head] : 0.0f;
   float sig = 1.0f;
-  sW[wave][3][lane] = 0;
+  sW[0][wave][3][lane] = 0;
+  sW[1][wave][3][lane] = 0;
 
-  // ---- prologue: chunks 0 .. D-1 in flight
-#pragma unroll
-  for (int c = 0; c < D; ++c) issue_chunk(c);
-
-  const int kr = l16 >> 2, kq = l16 & 3;
-  for (int c = 0; c < nchunks; ++c) {
-    const int slot = c % NSLOT;
-    // this chunk's loads were issued D chunks ago; (D - 1) NB loads of this
-    // wave came after them
-    wait_vm<(D - 1) * NB>();
-    __syncthreads();
-    issue_chunk(c + D);   // into the slot of chunk c - 1, which every wave has left
-
-    // ---- gate scan (each wave its own copy): lane j = token j of the chunk
+  // Gate scan of chunk c (this wave's copy; lane j = token j): writes w (three
+  // terms) and w / sig' into the wave's buffers of the chunk's parity, and
+  // returns g_L and whether the accumulators take the scale, advancing m and
+  // sig to their values after the chunk.
+  auto scan = [&](int c, float& gL, bool& renorm) {
+    const int slot = c % NSLOT, par = c & 1;
     const float xi = sG[slot][wave][0][lane];
     const float lf = log_forget_fast(sG[slot][wave][1][lane], a.fgate_exp);
     const float bcum = scan_add(lf);
@@ -172,26 +172,49 @@ __global__ __launch_bounds__(NTH, 1) void chunk_state_kernel(SeqArgs a) {
     const float Mx = fmaxf(m_s, scan_max(u));
     const float ML = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, Mx), L - 1));
     const float bL = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bcum), L - 1));
-    const float gL = __expf(m_s - ML);
+    gL = __expf(m_s - ML);
     const float wj = __expf(u - ML);
     // lazy scale: C~_new = g_L C~ + K^T (w V) = sig' (acc + K^T ((w / sig') V)),
-    // sig' = g_L sig; when sig' gets tiny the accumulators take g_L sig now
-    const bool renorm = gL * sig < 0x1p-64f;
+    // sig' = g_L sig; when sig' gets tiny the accumulators take g_L sig
+    renorm = gL * sig < 0x1p-64f;
     const float sig_new = renorm ? 1.0f : gL * sig;
-    split3_bf16(wj, sW[wave][0][lane], sW[wave][1][lane], sW[wave][2][lane]);
-    sWv[wave][lane] = wj * __builtin_amdgcn_rcpf(sig_new);
+    split3_bf16(wj, sW[par][wave][0][lane], sW[par][wave][1][lane], sW[par][wave][2][lane]);
+    sWv[par][wave][lane] = wj * __builtin_amdgcn_rcpf(sig_new);
     m_s = bL + ML;
+    sig = sig_new;
+  };
+
+  // ---- prologue: the gates of chunk 0, then chunks 0 .. D-1 (with the
+  // gates of chunks 1 .. D) in flight; chunk 0's scan once its gates land
+  issue_gates(0);
+#pragma unroll
+  for (int c = 0; c < D; ++c) issue_chunk(c);
+  wait_vm<D * NB>();
+  // gL, renorm: chunk c's, from its scan; sig_prev, m_prev: the scale and
+  // m before chunk c while it is processed (after it, once the loop ends)
+  float gL = 1.0f, sig_prev = 1.0f, m_prev = m_s;
+  bool renorm = false;
+  scan(0, gL, renorm);
+
+  const int kr = l16 >> 2, kq = l16 & 3;
+  for (int c = 0; c < nchunks; ++c) {
+    const int slot = c % NSLOT, par = c & 1;
+    // chunk c's loads (and the gates of chunk c + 1) were issued D chunks
+    // ago; (D - 1) NB loads of this wave came after them
+    wait_vm<(D - 1) * NB>();
+    __syncthreads();
+    issue_chunk(c + D);   // into the slots of chunk c - 1, which every wave has left
 
     // w (three terms) as the A operand of the n~ increment, and w / sig' for
-    // this lane's tokens 32 ks + 8 g + 0..7 (wave-private LDS: written and
-    // read by this wave, in order)
+    // this lane's tokens 32 ks + 8 g + 0..7 (wave-private LDS, written by the
+    // scan of this chunk one iteration earlier)
     uint4 Wx[NKS];
     bf16x8 wVf[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      Wx[ks] = *reinterpret_cast<const uint4*>(&sW[wave][l16 & 3][32 * ks + 8 * g]);
-      const float4 w0 = *reinterpret_cast<const float4*>(&sWv[wave][32 * ks + 8 * g]);
-      const float4 w1 = *reinterpret_cast<const float4*>(&sWv[wave][32 * ks + 8 * g + 4]);
+      Wx[ks] = *reinterpret_cast<const uint4*>(&sW[par][wave][l16 & 3][32 * ks + 8 * g]);
+      const float4 w0 = *reinterpret_cast<const float4*>(&sWv[par][wave][32 * ks + 8 * g]);
+      const float4 w1 = *reinterpret_cast<const float4*>(&sWv[par][wave][32 * ks + 8 * g + 4]);
       // V^T fragment of this wave's 16 columns: lane (g, c) gets column c
       // for tokens 32 ks + 8 g + 0..7
       const int col = vcol + 4 * kq;
@@ -205,11 +228,11 @@ __global__ __launch_bounds__(NTH, 1) void chunk_state_kernel(SeqArgs a) {
       wVf[ks] = cvt8(xw);
     }
     if (renorm) {
-      const float f = gL * sig;
+      const float f = gL * sig_prev;
 #pragma unroll
       for (int t = 0; t < NCTW; ++t) cacc[t] *= f;
     }
-    sig = sig_new;
+    const float gLc = gL;
 
     // ---- update of the wave's tiles.  The A operand of C~ tile T (sub-tile
     // sb = T/4, tl = T%4) is the K^T fragment: lane (g, c) holds the d_qk row
@@ -220,7 +243,7 @@ __global__ __launch_bounds__(NTH, 1) void chunk_state_kernel(SeqArgs a) {
     // (K^T w)[row c].
 #pragma unroll
     for (int t = 0; t < NCTW; ++t) {
-      const int T = rh * NCTW + t;
+      const int T = rq * NCTW + t;
       const char* Kb = sK[slot][T >> 2];
       const int tl = T & 3;
       const int col = 32 * (tl >> 1) + 8 * kq + 4 * (tl & 1);
@@ -233,32 +256,39 @@ __global__ __launch_bounds__(NTH, 1) void chunk_state_kernel(SeqArgs a) {
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
         cacc[t] = mfma16x16x32(join(Klo[ks], Khi[ks]), wVf[ks], cacc[t]);
-      if ((t & 1) == cgw) {
+      if (n_tile(t)) {
         f32x4 ni = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
           ni = mfma16x16x32(as_bf16x8(Wx[ks]), join(Klo[ks], Khi[ks]), ni);
-        nst[t >> 1] = gL * nst[t >> 1] + ((ni[0] + ni[1]) + ni[2]);
+        nst[t] = gLc * nst[t] + ((ni[0] + ni[1]) + ni[2]);
       }
     }
+    // ---- the next chunk's gate scan (its gates landed with this chunk's
+    // loads); it reads nothing this chunk's products write
+    sig_prev = sig;
+    m_prev = m_s;
+    scan(c + 1, gL, renorm);
   }
   // no LDS load may still be in flight when the workgroup ends
   wait_vm<0>();
   __syncthreads();
 
-  // ---- final state
+  // ---- final state (sig_prev, m_prev: after the last chunk; the scan past
+  // the end changed only values that are not used)
 #pragma unroll
   for (int t = 0; t < NCTW; ++t) {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      a.C1[(head * DQK + arow_of(t, e)) * dv + b0w + l16] = cacc[t][e] * sig;
+      a.C1[(head * DQK + arow_of(t, e)) * dv + b0w + l16] = cacc[t][e] * sig_prev;
   }
   if (vt == 0) {
     if (g == 0) {
 #pragma unroll
-      for (int j = 0; j < NNT; ++j) a.n1[head * DQK + nrow_of(j)] = nst[j];
+      for (int t = 0; t < NCTW; ++t)
+        if (n_tile(t)) a.n1[head * DQK + nrow_of(t)] = nst[t];
     }
-    if (tid == 0) a.m1[head] = m_s;
+    if (tid == 0) a.m1[head] = m_prev;
   }
 }
 
