@@ -17,10 +17,13 @@
 // SIMD:
 // * state waves 0..3 (16 value columns each) keep C~ in registers and, per
 //   64-row d_qk slice ("stage"), run the readout C~^T Q^T, the update
-//   K^T (w V) and the transposed score tiles S^T = K Q^T of key tile W
-//   against every query tile on MFMA; at the end of a chunk they leave the
-//   scaled readout g_i sig C~^T q_i and P = S (.) D (query tiles 0, 1; tiles
-//   2, 3 at stage 0 of the next chunk) in LDS;
+//   K^T (w V) and their share of the causal transposed score tiles
+//   S^T = K Q^T on MFMA (wave W: key tile W against query tiles W..3, with
+//   (key 0, query 3) moved from wave 0 to wave 3, so 3, 3, 2, 2 tiles; the
+//   wave index is a compile-time constant in each wave's copy of the loop);
+//   at the end of a chunk they leave the scaled readout g_i sig C~^T q_i and
+//   P = S (.) D in LDS (query tiles 2, 3 in one of two buffers by chunk
+//   parity, since the intra waves still read the previous chunk's);
 // * intra waves 4..7 compute q.n~ and the n~ increment K^T w (MFMAs with
 //   the vector split into three bf16 terms), issue and await every
 //   global->LDS load, and, during the stages of chunk c, finish chunk c-1:
@@ -35,10 +38,20 @@
 // write traffic than h itself).  Staged, a row is written by one wave as
 // eight 16-byte lane stores, one stage after it was computed.
 //
+// Inside a stage the state waves work in two halves of 32 d_qk rows: the
+// Q/K fragments of a half are read one half ahead (those of a stage's first
+// half during the previous stage, whose barrier already published the
+// slot), and the high/remainder bf16 pair of the next half's C~ rows is
+// formed between the current half's MFMAs.  On a SIMD, vector-ALU and MFMA
+// work do not overlap (measured), so the chunk costs the sum of both roles'
+// instructions: the score tiles above the diagonal are not computed, and
+// the gate scan runs on the wave with the fewest tiles.
+//
 // Loads are global->LDS DMAs issued from asm, with compile-time vmcnt
 // waits; q/k come in 64-wide d_qk slices through a ring of D+1 slots, v once
 // per chunk, the o~ tile once per chunk into one of two slots, the gates two
-// chunks ahead.
+// chunks ahead.  At the top of stage x the loading waves wait for the loads
+// of stage x + 1 (the state waves' read-ahead), issued D - 1 stages earlier.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mfma_util.hpp"
@@ -71,6 +84,18 @@ constexpr int NWL = 4;
 constexpr int NB_QK = 2 * TILE / 1024 / NWL;   // 1 KB loads per loading wave per stage
 constexpr int NB_V = TILE / 1024 / NWL;
 constexpr int NB_G = 2;
+
+// Loads issued after those of stage x + 1 when the loading wave waits at the
+// top of stage x (slice s), before it issues stage x + D: the stage groups
+// x + 2 .. x + D - 1 and the per-chunk loads issued at the tops of stages
+// x + 1 - D .. x - 1.
+template <int NBX>
+__host__ __device__ constexpr int loads_after_next(int s) {
+  int n = 0;
+  for (int k = 2; k < D; ++k) n += NB_QK + (((s + k) % NS) == 0 ? NB_V : 0);
+  for (int k = 1; k <= D - 1; ++k) n += (((s - k) % NS + NS) % NS == 0) ? NBX : 0;
+  return n;
+}
 static_assert(NS == 4 && D <= NS - 1, "one value slot needs the look-ahead inside a chunk");
 
 template <int OM>
@@ -88,7 +113,9 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
   __shared__ __align__(1024) char sV[TILE];
   __shared__ __align__(1024) char sO[2][C::OTILE];         // o~ by chunk parity
   __shared__ __align__(16) float sR[4][NT][64][4];         // scaled readout
-  __shared__ __align__(16) bf16_t sP[L * PROW];
+  // P: query tiles 0, 1 in rows 0..31, tiles 2, 3 by chunk parity in rows
+  // 32..63 and 64..95
+  __shared__ __align__(16) bf16_t sP[(L + 32) * PROW];
   // per chunk mod 3: u, M, g, exp(-m), w / sig'
   __shared__ __align__(16) float sGate[3][5][L];
   __shared__ float sQn[L];
@@ -144,6 +171,14 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
     sNs[3][tid] = 0;
   }
   if (tid < 3 * L) sWs[tid / L][3][tid % L] = 0;
+  // P tiles above the diagonal that P V reads (key tile 1 of query tile 0,
+  // key tile 3 of query tile 2 in both buffers): zero once, never written
+  for (int x = tid; x < 3 * 256; x += NTH) {
+    const int t = x >> 8, r = (x >> 4) & 15, cc = x & 15;
+    const int row = t == 0 ? r : 32 + 32 * (t - 1) + r;
+    const int col = t == 0 ? 16 + cc : 48 + cc;
+    sP[row * PROW + col] = 0;
+  }
   float m_s = a.C0 ? a.m0[head] : 0.0f;
 
   // ---- loads (the loading role; lw = 0..3 is the loading wave's index)
@@ -255,8 +290,9 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
     wait_vm<0>();
   }
   __syncthreads();
-  // the gate scans run on state wave 0 (SCAN_WAVE)
-  constexpr int SCAN_WAVE = 0;
+  // the gate scans run on state wave 3 (SCAN_WAVE), which has the fewest
+  // score tiles
+  constexpr int SCAN_WAVE = 3;
   float m_n1 = 0.0f;   // m after the current chunk (scan wave)
   if (wave == SCAN_WAVE) m_n1 = scan_gates(0, 0, m_s, 1.0f);
   __syncthreads();
@@ -278,36 +314,24 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
     return r;
   };
 
-  // P = S (.) D of key tile jt and query tiles it0, it0 + 1 of the chunk
-  // whose transposed scores are in sp[0..1], and their row sums; tiles above
-  // the diagonal come out as zeros.  The gate operands (from buffer gb) are
-  // read first, so that their LDS latency can be hidden.
-  struct POp {
-    float Mi[2];
-    float uj[4];
-  };
-  auto p_load = [&](int it0, int jt, int gb, POp& x) {
-    const float4 uj = *reinterpret_cast<const float4*>(&sGate[gb][0][jt * 16 + 4 * g]);
-    x.uj[0] = uj.x; x.uj[1] = uj.y; x.uj[2] = uj.z; x.uj[3] = uj.w;
+  // P = S (.) D of one tile (key tile jt, query tile it) of the chunk whose
+  // transposed scores are in sp, and its row sums (gates from buffer gbx);
+  // the part above the diagonal comes out as zeros
+  auto finish_one = [&](const f32x4& sp, int it, int jt, int par, int gbx) {
+    const float4 uj = *reinterpret_cast<const float4*>(&sGate[gbx][0][jt * 16 + 4 * g]);
+    const float uj4[4] = {uj.x, uj.y, uj.z, uj.w};
+    const int i = it * 16 + l16;
+    const float Mi = sGate[gbx][1][i];
+    float pe[4];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) x.Mi[r] = sGate[gb][1][(it0 + r) * 16 + l16];
-  };
-  auto finish_p = [&](const f32x4* sp, int it0, int jt, int par, const POp& x) {
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int it = it0 + r;
-      const int i = it * 16 + l16;
-      float pe[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = jt * 16 + 4 * g + e;
-        const float pv = sp[r][e] * __expf(x.uj[e] - x.Mi[r]);
-        pe[e] = (j <= i) ? pv : 0.0f;
-      }
-      *reinterpret_cast<uint2*>(sP + i * PROW + jt * 16 + 4 * g) =
-          make_uint2(cvt2(pe[0], pe[1]), cvt2(pe[2], pe[3]));
-      sRs[par][jt][it][l16] = sum_groups((pe[0] + pe[1]) + (pe[2] + pe[3]));
+    for (int e = 0; e < 4; ++e) {
+      const int j = jt * 16 + 4 * g + e;
+      const float pv = sp[e] * __expf(uj4[e] - Mi);
+      pe[e] = (j <= i) ? pv : 0.0f;
     }
+    *reinterpret_cast<uint2*>(sP + (i < 32 ? i : i + 32 * par) * PROW + jt * 16 + 4 * g) =
+        make_uint2(cvt2(pe[0], pe[1]), cvt2(pe[2], pe[3]));
+    sRs[par][jt][it][l16] = sum_groups((pe[0] + pe[1]) + (pe[2] + pe[3]));
   };
   // P V of query tiles it0, it0 + 1 onto their scaled readout, in two steps
   // (the readout can be read a stage before the products)
@@ -315,23 +339,26 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
 #pragma unroll
     for (int r = 0; r < 2; ++r) o[r] = *reinterpret_cast<const f32x4*>(&sR[cg][it0 + r][lane][0]);
   };
-  auto pv_mma = [&](const bf16x8* vfr, int it0, f32x4* o) {
+  auto pv_mma = [&](const bf16x8* vfr, int it0, int par, f32x4* o) {
+    uint4 Pf[2][NKS];
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-      const int it = it0 + r;
-      const int i = it * 16 + l16;
+      const int i = (it0 + r) * 16 + l16;
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        if (32 * ks <= it * 16 + 15) {
-          const uint4 Pf = *reinterpret_cast<const uint4*>(sP + i * PROW + 32 * ks + 8 * g);
-          o[r] = mfma16x16x32(vfr[ks], as_bf16x8(Pf), o[r]);
-        }
+      for (int ks = 0; ks < NKS; ++ks)
+        Pf[r][ks] = *reinterpret_cast<const uint4*>(sP + (i < 32 ? i : i + 32 * par) * PROW + 32 * ks + 8 * g);
+    }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        if (32 * ks <= (it0 + r) * 16 + 15) o[r] = mfma16x16x32(vfr[ks], as_bf16x8(Pf[r][ks]), o[r]);
       }
     }
   };
-  auto pv_tiles = [&](const bf16x8* vfr, int it0, f32x4* o) {
+  auto pv_tiles = [&](const bf16x8* vfr, int it0, int par, f32x4* o) {
     pv_init(it0, o);
-    pv_mma(vfr, it0, o);
+    pv_mma(vfr, it0, par, o);
   };
   // h of query tiles it0, it0 + 1 of chunk cp in two steps: the reciprocal
   // denominators and the o~ values (gates gb, o~ slot ob), then h from the
@@ -416,10 +443,18 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
   // its own loop so that its registers are its own.  The loading role waits
   // for the stage's loads before the barrier and issues the loads D stages
   // ahead after it.
+  auto wait_next_stage = [&](int s) {
+    switch (s) {
+      case 0: wait_vm<loads_after_next<C::NB_X>(0)>(); break;
+      case 1: wait_vm<loads_after_next<C::NB_X>(1)>(); break;
+      case 2: wait_vm<loads_after_next<C::NB_X>(2)>(); break;
+      default: wait_vm<loads_after_next<C::NB_X>(3)>(); break;
+    }
+  };
   auto stage_top_load = [&](int c, int s) {
     const int x = c * NS + s;
     if (x < D) wait_vm<0>();
-    else wait_stage<NS, D, NB_QK, NB_V, C::NB_X>(s);
+    else wait_next_stage(s);
     __syncthreads();
     issue_stage(x + D);
     if (s == 0) issue_chunk_extras(c);
@@ -437,7 +472,9 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
   };
 
   if (state_wave) {
-    const int W = cg;
+    // compiled once per state wave: its score tiles are fixed at compile time
+    for_wave<4>(cg, [&](auto Wc) {
+    constexpr int W = decltype(Wc)::value;
     // C~ of this wave's 16 columns: tile t holds rows 32 (t/2) + 8 g + 4 (t%2) + e
     f32x4 cacc[NCT];
 #pragma unroll
@@ -455,8 +492,89 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
     float sig = 1.0f;    // C~ = sig * cacc
     f32x4 outT[NT];
     bf16x8 wVf[NKS];
-    // transposed score tiles S^T = K Q^T of key tile W and every query tile
-    f32x4 sacc[NT], sp23[2];
+    // score tiles of this wave: key tile W against query tiles W..3, except
+    // that wave 3 takes (key 0, query 3) from wave 0 (in sacc_x): 3, 3, 2, 2
+    // tiles for waves 0..3
+    f32x4 sacc[NT], sacc_x;
+    auto own_tile = [&](int it) { return it >= W && !(W == 0 && it == NT - 1); };
+    // fragments of one half slice (32 d_qk rows): Q of every query tile and
+    // K of key tile W (and of key tile 0 on wave 3) for the scores and the
+    // readout; K^T of the half's two C~ row tiles for the update (Kt)
+    struct Frag {
+      uint4 Qf[NT], Kf, Kf0;
+    };
+    auto load_half = [&](Frag& f, const char* Qb, const char* Kb, int p) __attribute__((always_inline)) {
+#pragma unroll
+      for (int it = 0; it < NT; ++it) f.Qf[it] = lds_ld16(Qb, swz(it * 16 + l16, 32 * p + 8 * g));
+      f.Kf = lds_ld16(Kb, W * 2048 + swz(l16, 32 * p + 8 * g));
+      if (W == 3) f.Kf0 = lds_ld16(Kb, swz(l16, 32 * p + 8 * g));
+    };
+    bf16x8 Kt[NKS][2];
+    auto load_kt = [&](const char* Kb, int p) __attribute__((always_inline)) {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int col = 32 * p + 8 * kq + 4 * j;
+          Kt[ks][j] = join(lds_tr(Kb, swz(32 * ks + 8 * g + kr, col)),
+                           lds_tr(Kb, swz(32 * ks + 8 * g + 4 + kr, col)));
+        }
+      }
+    };
+    // C~ enters the readout as a (high, remainder) pair of bf16 operands:
+    // rounding it to bf16 alone costs up to ~2% of h where the carried and
+    // the in-chunk terms cancel.  The pair of the next half's rows is formed
+    // during this half's products (those rows are final for the chunk).
+    bf16x8 Ahi[2], Alo[2];
+    auto split_rows = [&](int t0, bf16x8& hi, bf16x8& lo) __attribute__((always_inline)) {
+      float ca[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ca[e] = cacc[t0][e];
+        ca[4 + e] = cacc[t0 + 1][e];
+      }
+      cvt8_split(ca, hi, lo);
+    };
+    // scores, readout and update of half p of slice s (C~ row tiles
+    // 4 s + 2 p + j): the readout of the rows comes before their update
+    auto compute_half = [&](const Frag& f, int s, int p, bool renorm, float rf) __attribute__((always_inline)) {
+      const int t0 = 4 * s + 2 * p;
+#pragma unroll
+      for (int it = 0; it < NT; ++it)
+        if (own_tile(it)) sacc[it] = mfma16x16x32(as_bf16x8(f.Kf), as_bf16x8(f.Qf[it]), sacc[it]);
+      if (W == 3) sacc_x = mfma16x16x32(as_bf16x8(f.Kf0), as_bf16x8(f.Qf[NT - 1]), sacc_x);
+#pragma unroll
+      for (int it = 0; it < NT; ++it) outT[it] = mfma16x16x32(Ahi[p], as_bf16x8(f.Qf[it]), outT[it]);
+#pragma unroll
+      for (int it = 0; it < NT; ++it) outT[it] = mfma16x16x32(Alo[p], as_bf16x8(f.Qf[it]), outT[it]);
+      split_rows((t0 + 2) & (NCT - 1), Ahi[p ^ 1], Alo[p ^ 1]);
+      // scheduling hint: one MFMA, then two VALU, twelve times
+#pragma unroll
+      for (int k = 0; k < 12; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+      }
+      {
+        // the pair is formed here, beside the products, not sunk past the
+        // renormalisation branch to its first use
+        const uint4 h_ = __builtin_bit_cast(uint4, Ahi[p ^ 1]), l_ = __builtin_bit_cast(uint4, Alo[p ^ 1]);
+        asm volatile("" :: "v"(h_.x), "v"(h_.y), "v"(h_.z), "v"(h_.w), "v"(l_.x), "v"(l_.y), "v"(l_.z), "v"(l_.w));
+      }
+      // the renormalisation (rare) scales the rows before their update
+      if (renorm) {
+        cacc[t0] *= rf;
+        cacc[t0 + 1] *= rf;
+      }
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          cacc[t0 + j] = mfma16x16x32(Kt[ks][j], wVf[ks], cacc[t0 + j]);
+      }
+    };
+    Frag F0, F1;
+    load_half(F0, sRing[0][0], sRing[0][1], 0);
+    split_rows(0, Ahi[0], Alo[0]);
     int gb = 0, gbn = 1, gbp = 2;   // gate buffers of chunks c, c + 1, c - 1
     for (int c = 0; c < nchunks; ++c) {
       // the chunk's gates are read after the first stage's barrier (the
@@ -496,97 +614,43 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
             outT[it] = f32x4{0.f, 0.f, 0.f, 0.f};
             sacc[it] = f32x4{0.f, 0.f, 0.f, 0.f};
           }
-        }
-        // ---- the stage's LDS reads are issued ahead of the arithmetic that
-        // consumes them (reads return in order, so each MFMA waits only for
-        // its own operands): Q and K fragments, then the score and readout
-        // MFMAs, then the update MFMAs
-        uint4 Qf[2][NT], Kf[2];
-        uint2 Klo[NKS][AS / 16], Khi[NKS][AS / 16];
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-#pragma unroll
-          for (int it = 0; it < NT; ++it) Qf[p][it] = lds_ld16(Qb, swz(it * 16 + l16, 32 * p + 8 * g));
-          Kf[p] = lds_ld16(Kb, W * 2048 + swz(l16, 32 * p + 8 * g));
+          sacc_x = f32x4{0.f, 0.f, 0.f, 0.f};
         }
         // gate operands of this stage's P pass and scaled readout
-        POp pop;
         float gi4[NT];
-        if (s == 0) p_load(2, W, gbp, pop);
         if (s == NS - 1) {
-          p_load(0, W, gb, pop);
 #pragma unroll
           for (int it = 0; it < NT; ++it) gi4[it] = sGate[gb][2][it * 16 + l16];
         }
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-#pragma unroll
-          for (int tl = 0; tl < AS / 16; ++tl) {
-            const int col = 32 * (tl >> 1) + 8 * kq + 4 * (tl & 1);
-            Klo[ks][tl] = lds_tr(Kb, swz(32 * ks + 8 * g + kr, col));
-            Khi[ks][tl] = lds_tr(Kb, swz(32 * ks + 8 * g + 4 + kr, col));
-          }
+        // the slice in two halves of 32 d_qk rows; the fragments of each half
+        // are read one half ahead (those of half 0 during the previous
+        // stage, from the slot its barrier published)
+        load_kt(Kb, 0);
+        load_half(F1, Qb, Kb, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_half(F0, s, 0, renorm, gL * sig);
+        __builtin_amdgcn_sched_barrier(0);
+        load_kt(Kb, 1);
+        {
+          const int nslot = (c * NS + s + 1) % NSLOT;
+          load_half(F0, sRing[nslot][0], sRing[nslot][1], 0);
         }
         __builtin_amdgcn_sched_barrier(0);
-        // score tiles over the slice first (P at the last stage waits only
-        // for them; above-diagonal tiles are included and masked with P)
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-#pragma unroll
-          for (int it = 0; it < NT; ++it)
-            sacc[it] = mfma16x16x32(as_bf16x8(Kf[p]), as_bf16x8(Qf[p][it]), sacc[it]);
-        }
-        // readout: query tiles x the slice's two 32-row k-steps
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          const int P = 2 * s + p;
-          float ca[8];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            ca[e] = cacc[2 * P][e];
-            ca[4 + e] = cacc[2 * P + 1][e];
-          }
-          // C~ enters as a (high, remainder) pair of bf16 operands: rounding
-          // it to bf16 alone costs up to ~2% of h where the carried and the
-          // in-chunk terms cancel
-          bf16x8 A_hi, A_lo;
-          cvt8_split(ca, A_hi, A_lo);
-#pragma unroll
-          for (int it = 0; it < NT; ++it) {
-            outT[it] = mfma16x16x32(A_hi, as_bf16x8(Qf[p][it]), outT[it]);
-            outT[it] = mfma16x16x32(A_lo, as_bf16x8(Qf[p][it]), outT[it]);
-          }
-        }
+        compute_half(F1, s, 1, renorm, gL * sig);
         __builtin_amdgcn_sched_barrier(0);
-        // state update of the slice's rows (after their readout); the
-        // renormalisation (rare) scales them first
-        if (renorm) {
-          const float f = gL * sig;
-#pragma unroll
-          for (int tl = 0; tl < AS / 16; ++tl) cacc[s * (AS / 16) + tl] *= f;
-        }
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-#pragma unroll
-          for (int tl = 0; tl < AS / 16; ++tl) {
-            const int t = s * (AS / 16) + tl;
-            cacc[t] = mfma16x16x32(join(Klo[ks][tl], Khi[ks][tl]), wVf[ks], cacc[t]);
-          }
-        }
         if (s == NS - 1) {
           // scaled readout for the intra waves
 #pragma unroll
           for (int it = 0; it < NT; ++it)
             *reinterpret_cast<f32x4*>(&sR[W][it][lane][0]) = outT[it] * (gi4[it] * sig);
         }
-        // P of the chunk: query tiles 0, 1 at the last stage (read from
-        // stage 1 of the next chunk on), tiles 2, 3 at stage 0 of the next
-        // chunk (read from its stage 2 on)
-        if (s == 0 && c > 0) finish_p(sp23, 2, W, (c - 1) & 1, pop);
+        // P of the chunk at the last stage (tiles 0, 1 are read from stage 1
+        // of the next chunk on, tiles 2, 3 from its stage 3)
         if (s == NS - 1) {
-          finish_p(sacc, 0, W, c & 1, pop);
-          sp23[0] = sacc[2];
-          sp23[1] = sacc[3];
+#pragma unroll
+          for (int it = 0; it < NT; ++it)
+            if (own_tile(it)) finish_one(sacc[it], it, W, c & 1, gb);
+          if (W == 3) finish_one(sacc_x, NT - 1, 0, c & 1, gb);
         }
         // gate scan of the next chunk: part 0 at stage 0, parts 1 and 2 at
         // stage 1, part 3 at stage 2 (the last stage carries the P pass)
@@ -606,14 +670,9 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
       gb = gbn;
       gbn = (gbn == 2) ? 0 : gbn + 1;
     }
-    // ---- drain: P of the last chunk's query tiles 2, 3
+    // ---- drain (the two barriers of the intra role's drain)
     if (STATE_LOADS) wait_vm<0>();
     __syncthreads();
-    {
-      POp pop;
-      p_load(2, W, gbp, pop);
-      finish_p(sp23, 2, W, (nchunks - 1) & 1, pop);
-    }
     __syncthreads();
     if (a.C1) {
 #pragma unroll
@@ -626,9 +685,10 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
       }
       if (vt == 0) {
         if (tid < DQK) a.n1[head * DQK + tid] = sN[tid];
-        if (tid == 0) a.m1[head] = m_s;
+        if (wave == SCAN_WAVE && lane == 0) a.m1[head] = m_s;
       }
     }
+    });
   } else {
     const int W = cg;
     // q.n~ of query tile qt = W
@@ -719,7 +779,7 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
         if (s == 1 && c > 1) h_flush(2, c - 2);
         if (s == 3 && c > 0) h_flush(0, c - 1);
         if (c > 0) {
-          if (s == 1) pv_tiles(Vp, 0, oacc);
+          if (s == 1) pv_tiles(Vp, 0, (c - 1) & 1, oacc);
           if (s == 2) {
             HOp hy;
             h_prep(0, c - 1, gbp, (c - 1) & 1, hy);
@@ -727,7 +787,7 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
             pv_init(2, oacc);   // (the state waves rewrite the readout at stage 3)
           }
           if (s == 3) {
-            pv_mma(Vp, 2, oacc);
+            pv_mma(Vp, 2, (c - 1) & 1, oacc);
             h_prep(2, c - 1, gbp, (c - 1) & 1, hx);
           }
         }
@@ -749,7 +809,7 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws_kernel(SeqArgs a) {
     __syncthreads();
 #pragma unroll
     for (int it0 = 0; it0 < NT; it0 += 2) {
-      pv_tiles(Vf, it0, oacc);
+      pv_tiles(Vf, it0, (nchunks - 1) & 1, oacc);
       h_tiles(oacc, it0, nchunks - 1, gbp, (nchunks - 1) & 1);
     }
   }
