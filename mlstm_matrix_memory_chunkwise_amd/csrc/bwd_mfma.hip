@@ -634,28 +634,54 @@ __device__ __forceinline__ void dma_k_chunk(const BwdArgs& a, int64_t tok0, int 
   }
 }
 
+// Direct global -> LDS load of one chunk's k for the 8-wave state pass: the
+// same tiles and lane layout as dma_k_chunk, DK / 64 instructions per wave.
+template <int DK>
+__device__ __forceinline__ void dma_k_chunk8(const BwdArgs& a, int64_t tok0, int wave, int lane, char* dst) {
+  constexpr int PER_WAVE = DK / 64;   // (DK / 64 tiles) x (8 row groups) / 8 waves
+  const bf16_t* k = static_cast<const bf16_t*>(a.k) + tok0 * DK;
+#pragma unroll
+  for (int q = 0; q < PER_WAVE; ++q) {
+    const int R = wave * PER_WAVE + q;
+    const int qt = R >> 3, rg = R & 7;
+    const int row = rg * 8 + (lane >> 3), slot = lane & 7;
+    const bf16_t* src = k + static_cast<int64_t>(row) * DK + qt * 64 + 8 * (slot ^ ((row >> 1) & 7));
+    dma16(src, static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(
+                   static_cast<int>(lds_addr(dst + qt * TB + rg * 1024)))));
+  }
+}
+
+constexpr int NT8 = 512;           // 8 waves
+
 // Chunk-boundary states for the reverse pass: (C~, n~, m) before every chunk
 // and after the last, C~_{c+1} = g_L C~_c + K^T (w (.) V) and
-// n~_{c+1} = g_L n~_c + K^T w.  Workgroup = (head, 64 value columns); the
-// state is carried transposed in float32 registers (wave w: value columns
-// 16 w..16 w + 15, all d_qk rows), w (.) V enters the MFMAs as a bf16 hi/lo
-// pair (about 16 significant bits; k is exact), n~ is a float32 sum on the
-// vector ALUs (column block 0 only, which also writes n~ and m).  k of the
-// next chunk streams into the other half of a double-buffered LDS tile while
-// the current one is used; v of the next chunk is held in registers.
+// n~_{c+1} = g_L n~_c + K^T w.  Workgroup = (head, 64 value columns), 8
+// waves, two per SIMD; the state is carried transposed in float32 registers
+// (wave w: value columns 16 (w % 4)..+15, half of the d_qk rows by w / 4),
+// w (.) V enters the MFMAs as a bf16 hi/lo pair (about 16 significant bits;
+// k is exact), n~ on MFMA with w as a hi/lo pair (column block 0 only, which
+// also writes n~ and m).  Every wave runs the gate scan itself (DPP scans),
+// one chunk ahead: at chunk c it scans the gates of chunk c + 1 (loaded at
+// the top of chunk c) and writes chunk c + 1's w (.) V and w into the LDS
+// buffers of that chunk's parity, so the loop has one barrier per chunk.  k
+// of the next chunk streams into the other half of a double-buffered LDS
+// tile while the current one is used.
 template <int DK>
-__global__ __launch_bounds__(NT4, 1) void bwd_states_mfma_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NT8, 1) void bwd_states_mfma_kernel(BwdArgs a) {
   constexpr int NXT = DK / 16;
+  constexpr int NXH = NXT / 2;            // x tiles per wave
+  constexpr int NXN = (NXT + 7) / 8;      // n~ x tiles per wave (column block 0)
   constexpr int NQT = DK / 64;
   __shared__ __align__(1024) char sK[2][NQT * TB];
-  __shared__ __align__(1024) char sWH[TB];
-  __shared__ __align__(1024) char sWL[TB];
-  __shared__ __align__(1024) char sWD[16 * 128];   // rows 0, 1: w as bf16 hi / lo; rest 0
-  __shared__ Gate64 G;
+  __shared__ __align__(1024) char sWH[2][TB];          // w (.) V, bf16 hi, by chunk parity
+  __shared__ __align__(1024) char sWL[2][TB];          // ... and lo
+  __shared__ __align__(1024) char sWD[2][16 * 128];    // rows 0, 1: w as bf16 hi / lo; rest 0
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const int kr = l16 >> 2, kq = l16 & 3;
+  const int cg = wave & 3, rh = wave >> 2;
   const int ncb = static_cast<int>(a.dv / TVC);
   int64_t bh;
   int cb;
@@ -667,35 +693,85 @@ __global__ __launch_bounds__(NT4, 1) void bwd_states_mfma_kernel(BwdArgs a) {
   const int c0 = cb * TVC;
   const bool lead = cb == 0;
 
-  f32x4 Ct[NXT];
+  // Ct[t]: C~^T[b = 16 cg + 4 g + e][x = 16 (rh NXH + t) + l16]
+  f32x4 Ct[NXH];
 #pragma unroll
-  for (int xt = 0; xt < NXT; ++xt) {
-    Ct[xt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < NXH; ++t) {
+    Ct[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (a.C0) {
       const float4 v4 = *reinterpret_cast<const float4*>(
-          a.C0 + (bh * DK + xt * 16 + l16) * dv + c0 + wave * 16 + 4 * g);
-      Ct[xt] = f32x4{v4.x, v4.y, v4.z, v4.w};
+          a.C0 + (bh * DK + (rh * NXH + t) * 16 + l16) * dv + c0 + cg * 16 + 4 * g);
+      Ct[t] = f32x4{v4.x, v4.y, v4.z, v4.w};
     }
   }
-  // n~ lives in column block 0 only, in the lanes of group 0 of each wave:
-  // lane l16 holds x = 16 (wave XPW + p) + l16
-  constexpr int XPW = NXT / 4;
-  float nx[XPW];
+  // n~ (column block 0): lane l16 of group 0 holds x = 16 (wave NXN + p) + l16
+  float nx[NXN];
 #pragma unroll
-  for (int p = 0; p < XPW; ++p)
-    nx[p] = (a.C0 && g == 0) ? a.n0[bh * DK + (wave * XPW + p) * 16 + l16] : 0.0f;
-  reinterpret_cast<uint2*>(sWD)[tid] = make_uint2(0u, 0u);
-  float m = a.C0 ? a.m0[bh] : 0.0f;
+  for (int p = 0; p < NXN; ++p) {
+    const int xt = wave * NXN + p;
+    nx[p] = (a.C0 && g == 0 && xt < NXT) ? a.n0[bh * DK + xt * 16 + l16] : 0.0f;
+  }
+  for (int x = tid; x < 2 * 16 * 128 / 8; x += NT8) reinterpret_cast<uint2*>(&sWD[0][0])[x] = make_uint2(0u, 0u);
+  float m = a.C0 ? a.m0[bh] : 0.0f;   // m before the chunk (every wave keeps it)
 
-  // v rows tid / 4, columns c0 + 16 (tid % 4) .. + 15 of a chunk
-  const bf16_t* vrow = static_cast<const bf16_t*>(a.v) + (bh * T + (tid >> 2)) * dv + c0 + (tid & 3) * 16;
-  uint4 nv0 = *reinterpret_cast<const uint4*>(vrow);
-  uint4 nv1 = *reinterpret_cast<const uint4*>(vrow + 8);
-  dma_k_chunk<DK>(a, bh * T, wave, lane, sK[0]);
+  // this thread's v: row tid / 8, columns c0 + 8 (tid % 8) .. + 7 of a chunk
+  const int vj = tid >> 3, vb = (tid & 7) * 8;
+  const bf16_t* vrow = static_cast<const bf16_t*>(a.v) + (bh * T + vj) * dv + c0 + vb;
+
+  // Gate scan of the chunk at tok0 from its raw gates (this wave's copy):
+  // w_j = exp(u_j - M_L) in lane j, g_L, and m after the chunk.
+  struct Scan {
+    float w, gL, m_after;
+  };
+  auto scan = [&](float fpre, float ipre, float ms) {
+    const float lf = a.fgate_exp ? fpre : log_sigmoid(fpre);
+    const float bc = scan_add(lf);
+    const float u = ipre - bc;
+    const float Mx = fmaxf(ms, scan_max(u));
+    const float ML = __shfl(Mx, LC - 1, 64);
+    Scan r;
+    r.w = __expf(u - ML);
+    r.gL = __shfl(__expf(ms - Mx), LC - 1, 64);
+    r.m_after = __shfl(bc + Mx, LC - 1, 64);
+    return r;
+  };
+  // w (.) V of this thread's row as a bf16 hi / lo pair into the buffers of
+  // parity par; wave 0 also writes w itself (rows 0, 1 of sWD)
+  auto split_wv = [&](const uint4 v8, float wlane, int par) {
+    const float wj = __shfl(wlane, vj, 64);
+    const float x[8] = {bf_lo(v8.x), bf_hi(v8.x), bf_lo(v8.y), bf_hi(v8.y),
+                        bf_lo(v8.z), bf_hi(v8.z), bf_lo(v8.w), bf_hi(v8.w)};
+    uint32_t hp[4], lp[4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const float y0 = wj * x[e], y1 = wj * x[e + 1];
+      const uint32_t h2 = pk2(y0, y1);
+      hp[e / 2] = h2;
+      lp[e / 2] = pk2(y0 - bf_lo(h2), y1 - bf_hi(h2));
+    }
+    *reinterpret_cast<uint4*>(sWH[par] + swz(vj, vb)) = make_uint4(hp[0], hp[1], hp[2], hp[3]);
+    *reinterpret_cast<uint4*>(sWL[par] + swz(vj, vb)) = make_uint4(lp[0], lp[1], lp[2], lp[3]);
+    if (lead && wave == 0) {   // the A operand of n~ += sum_j w_j k_j (hi and lo rows)
+      const bf16_t hi = f2bf(wlane);
+      *reinterpret_cast<bf16_t*>(sWD[par] + swz(0, lane)) = hi;
+      *reinterpret_cast<bf16_t*>(sWD[par] + swz(1, lane)) = f2bf(wlane - bf2f(hi));
+    }
+  };
+
+  // ---- prologue: k of chunk 0 in flight; chunk 0's scan and w (.) V
+  dma_k_chunk8<DK>(a, bh * T, wave, lane, sK[0]);
+  float gL, m_next;   // g_L of the current chunk, m after it
+  {
+    const Scan r = scan(a.f_pre[bh * T + lane], a.i_pre[bh * T + lane], m);
+    gL = r.gL;
+    m_next = r.m_after;
+    split_wv(*reinterpret_cast<const uint4*>(vrow), r.w, 0);
+  }
 
   for (int c = 0; c <= nc; ++c) {
-    // every load issued so far (k of chunk c, v) has landed; the previous
-    // chunk's reads of sK[(c + 1) & 1], sWH, sWL and G are done
+    const int par = c & 1;
+    // every load issued so far (k of chunk c) has landed, and every wave has
+    // written chunk c's w (.) V and w and left the previous chunk's buffers
     wait_vm<0>();
     __syncthreads();
     // the stored state at boundary c: before a chunk as this workgroup's
@@ -704,98 +780,83 @@ __global__ __launch_bounds__(NT4, 1) void bwd_states_mfma_kernel(BwdArgs a) {
     if (c < nc) {
       char* tile = reinterpret_cast<char*>(a.ws_Cb + ((bh * ncb + cb) * nc + c) * (DK * TVC));
 #pragma unroll
-      for (int xt = 0; xt < NXT; ++xt)
-        *reinterpret_cast<uint2*>(tile + swz(xt * 16 + l16, wave * 16 + 4 * g)) =
-            make_uint2(pk2(Ct[xt][0], Ct[xt][1]), pk2(Ct[xt][2], Ct[xt][3]));
+      for (int t = 0; t < NXH; ++t)
+        *reinterpret_cast<uint2*>(tile + swz((rh * NXH + t) * 16 + l16, cg * 16 + 4 * g)) =
+            make_uint2(pk2(Ct[t][0], Ct[t][1]), pk2(Ct[t][2], Ct[t][3]));
     } else {
-      float* wsC = a.ws_CT + bh * DK * dv + c0 + wave * 16 + 4 * g;
+      float* wsC = a.ws_CT + bh * DK * dv + c0 + cg * 16 + 4 * g;
 #pragma unroll
-      for (int xt = 0; xt < NXT; ++xt)
-        *reinterpret_cast<float4*>(wsC + static_cast<int64_t>(xt * 16 + l16) * dv) =
-            make_float4(Ct[xt][0], Ct[xt][1], Ct[xt][2], Ct[xt][3]);
+      for (int t = 0; t < NXH; ++t)
+        *reinterpret_cast<float4*>(wsC + static_cast<int64_t>((rh * NXH + t) * 16 + l16) * dv) =
+            make_float4(Ct[t][0], Ct[t][1], Ct[t][2], Ct[t][3]);
     }
     if (lead) {
       if (g == 0) {
 #pragma unroll
-        for (int p = 0; p < XPW; ++p) a.ws_n[(bh * nb + c) * DK + (wave * XPW + p) * 16 + l16] = nx[p];
+        for (int p = 0; p < NXN; ++p) {
+          const int xt = wave * NXN + p;
+          if (xt < NXT) a.ws_n[(bh * nb + c) * DK + xt * 16 + l16] = nx[p];
+        }
       }
       if (tid == 0) a.ws_m[bh * nb + c] = m;
     }
     if (c == nc) break;
     const int64_t tok0 = bh * T + static_cast<int64_t>(c) * LC;
-    const char* kc = sK[c & 1];
-    if (c + 1 < nc) dma_k_chunk<DK>(a, tok0 + LC, wave, lane, sK[(c + 1) & 1]);
-    if (wave == 0) gate_scan64(a, tok0, m, G);
-    const uint4 v0 = nv0, v1 = nv1;
-    if (c + 1 < nc) {
-      nv0 = *reinterpret_cast<const uint4*>(vrow + static_cast<int64_t>(c + 1) * LC * dv);
-      nv1 = *reinterpret_cast<const uint4*>(vrow + static_cast<int64_t>(c + 1) * LC * dv + 8);
-    }
-    __syncthreads();
-    {
-      const int j = tid >> 2, b0 = (tid & 3) * 16;
-      const float wj = G.w[j];
-      const float x[16] = {bf_lo(v0.x), bf_hi(v0.x), bf_lo(v0.y), bf_hi(v0.y), bf_lo(v0.z), bf_hi(v0.z),
-                           bf_lo(v0.w), bf_hi(v0.w), bf_lo(v1.x), bf_hi(v1.x), bf_lo(v1.y), bf_hi(v1.y),
-                           bf_lo(v1.z), bf_hi(v1.z), bf_lo(v1.w), bf_hi(v1.w)};
-      uint32_t hp[8], lp[8];
+    const char* kc = sK[par];
+    // the next chunk: k into the other LDS half (its last reads were the
+    // previous chunk's), its gates and this thread's v into registers
+    const bool more = c + 1 < nc;
+    if (more) dma_k_chunk8<DK>(a, tok0 + LC, wave, lane, sK[par ^ 1]);
+    const int64_t tn = more ? tok0 + LC : tok0;   // (past the end: a harmless re-read)
+    const float fpre_n = a.f_pre[tn + lane], ipre_n = a.i_pre[tn + lane];
+    const uint4 vn = *reinterpret_cast<const uint4*>(vrow + (more ? static_cast<int64_t>(c + 1) * LC * dv : 0));
+
+    // ---- C~ <- g_L C~ + K^T (w (.) V) for this wave's tiles
 #pragma unroll
-      for (int e = 0; e < 16; e += 2) {
-        const float y0 = wj * x[e], y1 = wj * x[e + 1];
-        const uint32_t h2 = pk2(y0, y1);
-        hp[e / 2] = h2;
-        lp[e / 2] = pk2(y0 - bf_lo(h2), y1 - bf_hi(h2));
-      }
-#pragma unroll
-      for (int h8 = 0; h8 < 2; ++h8) {
-        *reinterpret_cast<uint4*>(sWH + swz(j, b0 + 8 * h8)) = make_uint4(hp[4 * h8], hp[4 * h8 + 1], hp[4 * h8 + 2], hp[4 * h8 + 3]);
-        *reinterpret_cast<uint4*>(sWL + swz(j, b0 + 8 * h8)) = make_uint4(lp[4 * h8], lp[4 * h8 + 1], lp[4 * h8 + 2], lp[4 * h8 + 3]);
-      }
-    }
-    const float gL = G.g[LC - 1];
-    if (lead && tid < LC) {   // the A operand of n~ += sum_j w_j k_j (hi and lo rows)
-      const float wj = G.w[tid];
-      const bf16_t hi = f2bf(wj);
-      *reinterpret_cast<bf16_t*>(sWD + swz(0, tid)) = hi;
-      *reinterpret_cast<bf16_t*>(sWD + swz(1, tid)) = f2bf(wj - bf2f(hi));
-    }
-    __syncthreads();
-#pragma unroll
-    for (int xt = 0; xt < NXT; ++xt) Ct[xt] *= gL;
+    for (int t = 0; t < NXH; ++t) Ct[t] *= gL;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 Ah = colfrag(sWH, 32 * ks, wave * 16, g, kr, kq);
-      const bf16x8 Al = colfrag(sWL, 32 * ks, wave * 16, g, kr, kq);
+      const bf16x8 Ah = colfrag(sWH[par], 32 * ks, cg * 16, g, kr, kq);
+      const bf16x8 Al = colfrag(sWL[par], 32 * ks, cg * 16, g, kr, kq);
 #pragma unroll
-      for (int xt = 0; xt < NXT; ++xt) {
+      for (int t = 0; t < NXH; ++t) {
+        const int xt = rh * NXH + t;
         const bf16x8 Bk = colfrag(wide(kc, xt * 16), 32 * ks, (xt * 16) & 63, g, kr, kq);
-        Ct[xt] = mfma16x16x32(Ah, Bk, Ct[xt]);
-        Ct[xt] = mfma16x16x32(Al, Bk, Ct[xt]);
+        Ct[t] = mfma16x16x32(Ah, Bk, Ct[t]);
+        Ct[t] = mfma16x16x32(Al, Bk, Ct[t]);
       }
     }
     if (lead) {   // n~ <- g_L n~ + K^T w for this wave's x tiles (D rows 0 + 1)
-      f32x4 nacc[XPW];
+      f32x4 nacc[NXN];
 #pragma unroll
-      for (int p = 0; p < XPW; ++p) nacc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int p = 0; p < NXN; ++p) nacc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 Aw = rowfrag(sWD, l16, 32 * ks + 8 * g);
+        const bf16x8 Aw = rowfrag(sWD[par], l16, 32 * ks + 8 * g);
 #pragma unroll
-        for (int p = 0; p < XPW; ++p) {
-          const int xt = wave * XPW + p;
-          nacc[p] = mfma16x16x32(Aw, colfrag(wide(kc, xt * 16), 32 * ks, (xt * 16) & 63, g, kr, kq), nacc[p]);
+        for (int p = 0; p < NXN; ++p) {
+          const int xt = wave * NXN + p;
+          if (xt < NXT)
+            nacc[p] = mfma16x16x32(Aw, colfrag(wide(kc, xt * 16), 32 * ks, (xt * 16) & 63, g, kr, kq), nacc[p]);
         }
       }
 #pragma unroll
-      for (int p = 0; p < XPW; ++p) nx[p] = gL * nx[p] + (nacc[p][0] + nacc[p][1]);
+      for (int p = 0; p < NXN; ++p) nx[p] = gL * nx[p] + (nacc[p][0] + nacc[p][1]);
     }
-    m = G.m[LC - 1];
+    // ---- the next chunk's scan and w (.) V (into the other parity)
+    m = m_next;
+    if (more) {
+      const Scan r = scan(fpre_n, ipre_n, m);
+      split_wv(vn, r.w, par ^ 1);
+      gL = r.gL;
+      m_next = r.m_after;
+    }
   }
 }
 
 template <int DK>
 hipError_t launch_states_dk(const BwdArgs& a, hipStream_t st) {
-  bwd_states_mfma_kernel<DK><<<static_cast<unsigned>(a.B * a.H * (a.dv / TVC)), NT4, 0, st>>>(a);
+  bwd_states_mfma_kernel<DK><<<static_cast<unsigned>(a.B * a.H * (a.dv / TVC)), NT8, 0, st>>>(a);
   return hipGetLastError();
 }
 
