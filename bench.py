@@ -218,6 +218,14 @@ def profile_workload():
     torch.cuda.synchronize()
 
 
+def parallel_flops(B, H, T, dqk, dv):
+    """Algorithmic flops of the parallel form's outputs: per head and query i,
+    (i + 1) keys times (2 d_qk for q.k, 2 d_v for the weighted sum of v, plus
+    the D weighting and the row sum), i.e. the causal half of QK^T and of P V."""
+    pairs = T * (T + 1) // 2
+    return B * H * pairs * (2 * dqk + 2 * dv + 2)
+
+
 def time_events(fn, reps, stream):
     import torch
     start = torch.cuda.Event(enable_timing=True)
@@ -243,6 +251,7 @@ def main():
     ap.add_argument("--skip-block", action="store_true")
     ap.add_argument("--skip-slstm", action="store_true")
     ap.add_argument("--skip-long", action="store_true")
+    ap.add_argument("--skip-parallel", action="store_true")
     ap.add_argument("--profile-workload", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -607,6 +616,38 @@ def main():
             "algorithmic_bytes": b4, "algorithmic_gflop": f4 / 1e9,
         }
         del d4, h4
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ parallel form
+    if not args.skip_parallel:
+        cfg1 = workloads.CONFIGS["d128_T2048"]
+        log(f"bench: generating {cfg1.describe()}")
+        d1 = {k: (None if v is None else v.to(dev))
+              for k, v in workloads.make_chunkwise_inputs(cfg1).items()}
+        B1, H1, T1, dqk1, dv1 = cfg1.B, cfg1.H, cfg1.T, cfg1.dqk, cfg1.dv
+        h1 = torch.empty((B1, H1, T1, dv1), dtype=torch.bfloat16, device=dev)
+        ws1 = torch.empty(M.mlstm_fwd_parallel_workspace_bytes(
+            M.Problem(B1, H1, T1, dqk1, dv1, 1, 0, 0, 0)), dtype=torch.uint8, device=dev)
+
+        def run_par():
+            M.mlstm_fwd_parallel(d1["q"], d1["k"], d1["v"], d1["i_pre"], d1["f_pre"], d1["o_pre"],
+                                 return_state=False, out=h1, workspace=ws1)
+
+        for _ in range(3):
+            run_par()
+        torch.cuda.synchronize()
+        ms1 = time_events(run_par, 20, stream)
+        f1 = parallel_flops(B1, H1, T1, dqk1, dv1)
+        tf1 = f1 / (ms1 / 1e3) / 1e12
+        result["parallel_form"] = {
+            "workload": f"parallel (quadratic) form, outputs only: bf16 q/k/v, fp32 gates/o-gate, "
+                        f"B={B1} H={H1} T={T1} d_qk={dqk1} d_v={dv1}, zero initial state",
+            "ms": ms1, "tokens_per_s": B1 * T1 / (ms1 / 1e3),
+            "roofline": {"bound": "mfma", "achieved": tf1, "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": tf1 / MFMA_BF16_PEAK_TFLOPS, "traffic": None},
+            "algorithmic_gflop": f1 / 1e9,
+        }
+        del d1, h1, ws1
         torch.cuda.empty_cache()
 
     print(json.dumps(result), flush=True)

@@ -67,3 +67,34 @@ def test_parallel_matches_chunkwise():
                                   chunk=64)
     torch.cuda.synchronize()
     assert slice_rel_err(hp.cpu(), hc.cpu()) < TOL_BF16
+
+
+# The bf16 MFMA output kernel (d_qk 64/128/256, d_v a multiple of 64): ragged
+# T (the last query and key blocks partial), the initial-state readout, every
+# o-gate form, both forget gates, input-gate spikes, several column blocks,
+# T below one block and T = 1.  A T that is a multiple of 64 takes the final
+# state from the state-only chunk pass, any other T from the per-element
+# kernel.
+MFMA_CASES = [
+    # label, B, H, T, d_qk, d_v, random state, o-gate dtype, fgate, i dist
+    ("d64 dv64 T300 state", 2, 2, 300, 64, 64, True, "f32", "sigmoid", (0.0, 1.0)),
+    ("d128 dv128 T1000 state bf16-o", 1, 3, 1000, 128, 128, True, "bf16", "sigmoid", (-2.0, 3.0)),
+    ("d256 dv192 T512 state", 1, 2, 512, 256, 192, True, "f32", "sigmoid", (-2.0, 3.0)),
+    ("d256 dv64 T640 no o-gate exp gate", 1, 2, 640, 256, 64, False, None, "exp", (0.0, 1.0)),
+    ("d128 dv64 T37 (one partial block)", 2, 1, 37, 128, 64, True, "f32", "sigmoid", (0.0, 1.0)),
+    ("d64 dv64 T1", 1, 2, 1, 64, 64, True, "f32", "sigmoid", (0.0, 1.0)),
+    ("d256 dv128 T1024 input-gate spikes", 1, 2, 1024, 256, 128, True, "f32", "sigmoid", (0.0, 15.0)),
+]
+
+
+@pytest.mark.parametrize("case", MFMA_CASES, ids=[c[0] for c in MFMA_CASES])
+def test_parallel_mfma_cases(case):
+    label, B, H, T, dqk, dv, state, odt, fgate, idist = case
+    fdist = (-0.05, 0.1) if fgate == "exp" else (3.0, 1.0)
+    cfg = workloads.Config("parm", 7, "bf16", B, H, T, dqk, dv, (), idist, fdist,
+                           None if odt is None else (0.0, 1.0), state, fgate)
+    inp = workloads.make_chunkwise_inputs(cfg)
+    if odt == "bf16":
+        inp["o_pre"] = inp["o_pre"].to(torch.bfloat16)
+    log(f"parallel MFMA {label}")
+    _cmp(inp, TOL_BF16, label, fgate=fgate)
