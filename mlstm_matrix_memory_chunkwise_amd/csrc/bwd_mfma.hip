@@ -73,6 +73,21 @@ struct Gate64 {
   float u[LC], M[LC], m[LC], g[LC], w[LC];
 };
 
+// the same from gate values already in registers (lane = token)
+__device__ __forceinline__ void gate_scan64_v(float fpre, float ipre, int fgate_exp, float ms, Gate64& G) {
+  const int lane = threadIdx.x & 63;
+  const float lf = fgate_exp ? fpre : log_sigmoid(fpre);
+  const float bc = scan_add(lf);
+  const float u = ipre - bc;
+  const float Mx = fmaxf(ms, scan_max(u));
+  const float ML = __shfl(Mx, LC - 1, 64);
+  G.u[lane] = u;
+  G.M[lane] = Mx;
+  G.m[lane] = bc + Mx;
+  G.g[lane] = __expf(ms - Mx);
+  G.w[lane] = __expf(u - ML);
+}
+
 __device__ __forceinline__ void gate_scan64(const BwdArgs& a, int64_t tok0, float ms, Gate64& G) {
   const int lane = threadIdx.x & 63;
   const float fpre = a.f_pre[tok0 + lane];
@@ -171,12 +186,36 @@ __global__ __launch_bounds__(NT4, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
     for (int p = 0; p < NCC; ++p) pc[p] = Cs[tid + p * NT4];
   }
 
+  // the small per-chunk inputs (gates, m, n~ at the chunk start, beta) are
+  // also read one chunk ahead, into registers, so that no global latency sits
+  // between a chunk's first barrier and its gate scan
+  constexpr int NNR = (DK + NT4 - 1) / NT4;
+  float pf_f, pf_i, pf_ms, pf_b, pf_n[NNR];
+  auto prefetch_small = [&](int cc) {
+    const int64_t t0 = bh * T + static_cast<int64_t>(cc) * LC;
+    pf_f = a.f_pre[t0 + lane];
+    pf_i = a.i_pre[t0 + lane];
+    pf_ms = a.ws_m[bh * nb + cc];
+    pf_b = a.ws_beta[t0 + (tid & (LC - 1))];
+#pragma unroll
+    for (int r = 0; r < NNR; ++r) {
+      const int x = tid + r * NT4;
+      pf_n[r] = x < DK ? a.ws_n[(bh * nb + cc) * DK + x] : 0.0f;
+    }
+  };
+  prefetch_small(nc - 1);
+
   for (int c = nc - 1; c >= 0; --c) {
     const int64_t tok0 = bh * T + static_cast<int64_t>(c) * LC;
-    const float ms = a.ws_m[bh * nb + c];
     __syncthreads();
     // ---- this chunk's operands into LDS; the next chunk's loads go out
-    if (wave == 0) gate_scan64(a, tok0, ms, G);
+    if (wave == 0) gate_scan64_v(pf_f, pf_i, a.fgate_exp, pf_ms, G);
+#pragma unroll
+    for (int r = 0; r < NNR; ++r) {
+      const int x = tid + r * NT4;
+      if (x < DK) sN[x] = pf_n[r];
+    }
+    if (tid < LC) sBeta[tid] = pf_b;
 #pragma unroll
     for (int p = 0; p < NQK; ++p) {
       const int e = tid + p * NT4;
@@ -213,8 +252,7 @@ __global__ __launch_bounds__(NT4, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
 #pragma unroll
       for (int p = 0; p < NCC; ++p) pc[p] = Cs[tid + p * NT4];
     }
-    for (int x = tid; x < DK; x += NT4) sN[x] = a.ws_n[(bh * nb + c) * DK + x];
-    if (tid < LC) sBeta[tid] = a.ws_beta[tok0 + tid];
+    prefetch_small(c > 0 ? c - 1 : 0);   // (chunk 0 reads itself again: unused)
     // this thread's dh, h and o~ (row tid / 4, 16 columns) for the r step,
     // loaded now so that their latency overlaps the score products
     uint4 pdh[2], ph[2], po[4];
