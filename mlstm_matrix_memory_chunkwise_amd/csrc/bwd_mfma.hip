@@ -1,5 +1,5 @@
-// State and reverse passes of the chunkwise backward on bf16 MFMA (gfx950):
-// chunk 64, 64 value columns per workgroup, d_qk in {64, 128, 256}, bf16
+// State, reverse and dq/dk passes of the chunkwise backward on bf16 MFMA
+// (gfx950): chunk 64, d_qk in {64, 128, 256}, d_v a multiple of 64, bf16
 // q/k/v/h/dh.
 //
 // The same gradient as the float32 passes in bwd.hip (the derivative of the
@@ -8,26 +8,35 @@
 // section 2 "The Normalizer State and Numerical Stabilization"), with every
 // matrix product on 16x16x32 MFMAs.  Per chunk of 64 tokens, with the stored
 // state (C~_s, n~_s, m_s) and the carried memory gradient dC, the reverse
-// pass forms
+// pass (one workgroup per head and 64 value columns, sequential over the
+// chunks) forms
 //
 //   S = Q K^T,  DS = D (.) S              (masked; stored transposed, bf16;
 //                                          row sums in float32)
-//   r = sigmoid(o~) dh / den,  g r,  w V (bf16 in LDS)
-//   W = D (.) (R V^T + dnq)               (bf16 in LDS)
-//   dq^T = K^T W^T + C~_s (g R)^T  (+ g dnq n~_s)
-//   dk^T = Q^T W + dC (w V)^T      (+ w dn)
+//   r = sigmoid(o~) dh / den,  g r        (bf16 in LDS; r also to HBM)
 //   dv^T = R^T DS + w (dC^T K^T)          (dC as a bf16 hi / lo pair)
 //   dC^T <- g_L dC^T + (g R)^T Q,  dn <- g_L dn + sum_i g_i dnq_i q_i
+//
+// and stores, per chunk, the dC and dn it enters with (the gradient at the
+// chunk's end) and dnq.  The dq/dk pass then runs on every (head, chunk,
+// d_qk slice) at once, over all of d_v:
+//
+//   dS = R V^T,  W = D (.) (dS + dnq)     (float32 sum over d_v, bf16 W)
+//   dq^T = g (C~_s R^T) + K^T W^T + g dnq n~_s
+//   dk^T = w (dC V^T)   + Q^T W   + w dn
+//
+// so that no workgroup writes a partial sum over its own value columns.
 //
 // Operands are read from swizzled [rows][64] bf16 LDS tiles either as row
 // fragments (8 consecutive columns, ds_read_b128) or as transposed column
 // fragments (8 consecutive rows, two ds_read_b64_tr_b16), both in natural
-// index order.  The memory gradient is carried transposed in float32
-// registers (dC^T tiles, one 16-column block per wave), which makes its bf16
-// copy for the products a run of 4 consecutive columns per lane.  The
-// products round their other operands to bf16 (accumulation stays float32);
-// q, k, v are exact.  Vectors that meet a matrix in float32 precision (dn's
-// g dnq, the state pass's w (.) V and w) enter as bf16 hi / lo pairs.
+// index order; the dq/dk pass reads its d_v-contracted operands straight
+// from HBM as 16-byte fragments.  The memory gradient is carried transposed
+// in float32 registers (dC^T tiles, one 16-column block per wave), which
+// makes its bf16 copy a run of 4 consecutive columns per lane.  The products
+// round their other operands to bf16 (accumulation stays float32); q, k, v
+// are exact.  Vectors that meet a matrix in float32 precision (dn's g dnq,
+// the state pass's w (.) V and w) enter as bf16 hi / lo pairs.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mfma_util.hpp"
@@ -108,22 +117,20 @@ __device__ __forceinline__ uint32_t pk2(float a, float b) { return cvt2(a, b); }
 template <int DK, typename TO>
 __global__ __launch_bounds__(NT4, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
   constexpr int NXT = DK / 16;      // 16-row tiles of x (d_qk)
-  constexpr int XPW = NXT / 4;      // x tiles per wave in the dq / dk products
+  constexpr int XPW = NXT / 4;      // x tiles per wave in the dn product
   constexpr int NQT = DK / 64;
   __shared__ __align__(1024) char sQ[NQT * TB];
   __shared__ __align__(1024) char sK[NQT * TB];
   __shared__ __align__(1024) char sV[TB];
-  __shared__ __align__(1024) char sWV[TB];
   __shared__ __align__(1024) char sR[TB];
   __shared__ __align__(1024) char sGR[TB];
-  __shared__ __align__(1024) char sW[TB];
   __shared__ __align__(1024) char sDST[TB];   // (D (.) S)^T: [j][i]
-  __shared__ __align__(1024) char sCX[DK * 128];   // [DK][64]: C~_s, then dC
+  __shared__ __align__(1024) char sCX[DK * 128];   // [DK][64]: dC at the chunk's end, bf16
   __shared__ __align__(1024) char sGD[16 * 128];   // rows 0, 1: g (.) dnq as bf16 hi / lo; rest 0
   __shared__ __align__(16) char sTW[4 * 2048];     // per wave: [32 x][16 b] bf16 hi, then lo
   __shared__ float sN[DK], sDn[DK];
   __shared__ float sRs[LC];
-  __shared__ float sDnq[LC], sBeta[LC];
+  __shared__ float sBeta[LC];
   __shared__ Gate64 G;
   __shared__ float sRed[4];
 
@@ -156,14 +163,14 @@ __global__ __launch_bounds__(NT4, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
   for (int x = tid; x < DK; x += NT4) sDn[x] = a.dn1 ? a.dn1[bh * DK + x] : 0.0f;
   reinterpret_cast<uint2*>(sGD)[tid] = make_uint2(0u, 0u);
 
-  // The chunk's q, k, v (own columns) and C~_s (the state pass's bf16 tile)
-  // are loaded into registers one chunk ahead: the loads of chunk c - 1 are
-  // in flight while chunk c is computed, and land in LDS at the next top.
+  // The chunk's q, k and v (own columns) are loaded into registers one
+  // chunk ahead: the loads of chunk c - 1 are in flight while chunk c is
+  // computed, and land in LDS at the next top.
   constexpr int NQK = LC * DK / 8 / NT4;    // 16-byte pieces of q (and of k) per thread
   constexpr int NVV = LC * TVC / 8 / NT4;
-  constexpr int NCC = DK * TVC / 8 / NT4;
+  constexpr int NCC = DK * TVC / 8 / NT4;   // 16-byte pieces of a [DK][64] bf16 tile
   // native vectors: HIP's uint4 struct would be copied through private memory
-  u32x4 pq[NQK], pk[NQK], pv[NVV], pc[NCC];
+  u32x4 pq[NQK], pk[NQK], pv[NVV];
   {
     const int64_t t0 = bh * T + static_cast<int64_t>(nc - 1) * LC;
     const bf16_t* q = static_cast<const bf16_t*>(a.q) + t0 * DK;
@@ -181,9 +188,6 @@ __global__ __launch_bounds__(NT4, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
       const int e = tid + p * NT4;
       pv[p] = *reinterpret_cast<const u32x4*>(v + static_cast<int64_t>(e >> 3) * dv + (e & 7) * 8);
     }
-    const u32x4* Cs = reinterpret_cast<const u32x4*>(a.ws_Cb + ((bh * ncb + cb) * nc + (nc - 1)) * (DK * TVC));
-#pragma unroll
-    for (int p = 0; p < NCC; ++p) pc[p] = Cs[tid + p * NT4];
   }
 
   // the small per-chunk inputs (gates, m, n~ at the chunk start, beta) are
@@ -228,8 +232,15 @@ __global__ __launch_bounds__(NT4, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
       const int e = tid + p * NT4;
       *reinterpret_cast<u32x4*>(sV + swz(e >> 3, (e & 7) * 8)) = pv[p];
     }
+    // dC at this chunk's end (bf16, [x][b]) for the HBM copy below, and (in
+    // column block 0) dn at this chunk's end, for the dq/dk pass
 #pragma unroll
-    for (int p = 0; p < NCC; ++p) *reinterpret_cast<u32x4*>(sCX + 16 * (tid + p * NT4)) = pc[p];
+    for (int xt = 0; xt < NXT; ++xt)
+      *reinterpret_cast<uint2*>(sCX + swz(xt * 16 + l16, wave * 16 + 4 * g)) =
+          make_uint2(pk2(dCt[xt][0], dCt[xt][1]), pk2(dCt[xt][2], dCt[xt][3]));
+    if (lead) {
+      for (int x = tid; x < DK; x += NT4) a.ws_dn[(bh * nc + c) * DK + x] = sDn[x];
+    }
     // the next chunk's loads (chunk 0 fetches itself again: in bounds, unused)
     {
       const int64_t t0 = bh * T + static_cast<int64_t>(c > 0 ? c - 1 : 0) * LC;
@@ -248,9 +259,6 @@ __global__ __launch_bounds__(NT4, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
         const int e = tid + p * NT4;
         pv[p] = *reinterpret_cast<const u32x4*>(v + static_cast<int64_t>(e >> 3) * dv + (e & 7) * 8);
       }
-      const u32x4* Cs = reinterpret_cast<const u32x4*>(a.ws_Cb + ((bh * ncb + cb) * nc + (c > 0 ? c - 1 : 0)) * (DK * TVC));
-#pragma unroll
-      for (int p = 0; p < NCC; ++p) pc[p] = Cs[tid + p * NT4];
     }
     prefetch_small(c > 0 ? c - 1 : 0);   // (chunk 0 reads itself again: unused)
     // this thread's dh, h and o~ (row tid / 4, 16 columns) for the r step,
@@ -273,6 +281,14 @@ __global__ __launch_bounds__(NT4, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
       }
     }
     __syncthreads();
+    // ---- the dC tile to HBM, in the same swizzled tile order as the stored
+    // states (this workgroup's 64 columns of chunk c)
+    {
+      u32x4* dst = reinterpret_cast<u32x4*>(a.ws_dCb + ((bh * ncb + cb) * nc + c) * (DK * TVC));
+#pragma unroll
+      for (int p = 0; p < NCC; ++p)
+        dst[tid + p * NT4] = *reinterpret_cast<const u32x4*>(sCX + 16 * (tid + p * NT4));
+    }
 
     // ---- S = Q K^T for query tile it = wave (all key tiles): D (.) S goes to
     // LDS transposed ([j][i]); its row sums stay inside the wave, so the
@@ -341,9 +357,9 @@ __global__ __launch_bounds__(NT4, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
       const float floor_ = __expf(-G.m[i]);
       den = fmaxf(fabsf(nq), floor_);
       const float dnq = fabsf(nq) >= floor_ ? (nq >= 0.0f ? -sBeta[i] / den : sBeta[i] / den) : 0.0f;
-      if (qq == 0) {
-        sDnq[i] = dnq;
-        if (lead) {   // the A operand of dn += sum_i g_i dnq_i q_i (hi and lo rows)
+      if (qq == 0 && lead) {
+        a.ws_dnq[tok0 + i] = dnq;
+        {   // the A operand of dn += sum_i g_i dnq_i q_i (hi and lo rows)
           const float gd = G.g[i] * dnq;
           const bf16_t hi = f2bf(gd);
           *reinterpret_cast<bf16_t*>(sGD + swz(0, i)) = hi;
@@ -351,21 +367,19 @@ __global__ __launch_bounds__(NT4, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
         }
       }
     }
-    // ---- r, g r, w V (bf16 to LDS) and do~ (16 columns per thread)
+    // ---- r and g r (bf16 to LDS; r also to HBM for the dq/dk pass) and do~
+    // (16 columns per thread)
     {
       const int i = tid >> 2, b0 = (tid & 3) * 16;
       const int64_t gi = (tok0 + i) * dv + c0 + b0;
       const float inv = 1.0f / den;
-      const float gi_ = G.g[i], wi = G.w[i];
-      uint32_t rp[8], gp[8], wp[8];
+      const float gi_ = G.g[i];
+      uint32_t rp[8], gp[8];
 #pragma unroll
       for (int h8 = 0; h8 < 2; ++h8) {
         const uint4 d8 = pdh[h8];
-        const uint4 v8 = lds_ld16(sV, swz(i, b0 + 8 * h8));
         float dhv[8] = {bf_lo(d8.x), bf_hi(d8.x), bf_lo(d8.y), bf_hi(d8.y),
                         bf_lo(d8.z), bf_hi(d8.z), bf_lo(d8.w), bf_hi(d8.w)};
-        float vv[8] = {bf_lo(v8.x), bf_hi(v8.x), bf_lo(v8.y), bf_hi(v8.y),
-                       bf_lo(v8.z), bf_hi(v8.z), bf_lo(v8.w), bf_hi(v8.w)};
         float gate[8];
         if (a.o_pre) {
           const uint4 h8v = ph[h8];
@@ -401,138 +415,17 @@ __global__ __launch_bounds__(NT4, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
           const float r0 = gate[e] * dhv[e] * inv, r1 = gate[e + 1] * dhv[e + 1] * inv;
           rp[4 * h8 + e / 2] = pk2(r0, r1);
           gp[4 * h8 + e / 2] = pk2(gi_ * r0, gi_ * r1);
-          wp[4 * h8 + e / 2] = pk2(wi * vv[e], wi * vv[e + 1]);
         }
       }
 #pragma unroll
       for (int h8 = 0; h8 < 2; ++h8) {
-        *reinterpret_cast<uint4*>(sR + swz(i, b0 + 8 * h8)) = make_uint4(rp[4 * h8], rp[4 * h8 + 1], rp[4 * h8 + 2], rp[4 * h8 + 3]);
+        const u32x4 r4 = {rp[4 * h8], rp[4 * h8 + 1], rp[4 * h8 + 2], rp[4 * h8 + 3]};
+        *reinterpret_cast<u32x4*>(sR + swz(i, b0 + 8 * h8)) = r4;
+        *reinterpret_cast<u32x4*>(a.ws_R + gi + 8 * h8) = r4;
         *reinterpret_cast<uint4*>(sGR + swz(i, b0 + 8 * h8)) = make_uint4(gp[4 * h8], gp[4 * h8 + 1], gp[4 * h8 + 2], gp[4 * h8 + 3]);
-        *reinterpret_cast<uint4*>(sWV + swz(i, b0 + 8 * h8)) = make_uint4(wp[4 * h8], wp[4 * h8 + 1], wp[4 * h8 + 2], wp[4 * h8 + 3]);
       }
     }
     __syncthreads();
-    // ---- W = D (.) (R V^T + dnq): (R V^T)^T = V R^T for key tile jt = wave
-    {
-      f32x4 acc[4];
-#pragma unroll
-      for (int it = 0; it < 4; ++it) acc[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < TVC / 32; ++ks) {
-        const bf16x8 A = rowfrag(sV, wave * 16 + l16, 32 * ks + 8 * g);
-#pragma unroll
-        for (int it = 0; it < 4; ++it)
-          acc[it] = mfma16x16x32(A, rowfrag(sR, it * 16 + l16, 32 * ks + 8 * g), acc[it]);
-      }
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int i = it * 16 + l16;
-        const float Mi = G.M[i], dq_ = lead ? sDnq[i] : 0.0f;
-        float wv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = wave * 16 + 4 * g + e;
-          wv[e] = j <= i ? __expf(G.u[j] - Mi) * (acc[it][e] + dq_) : 0.0f;
-        }
-        *reinterpret_cast<uint2*>(sW + swz(i, wave * 16 + 4 * g)) = make_uint2(pk2(wv[0], wv[1]), pk2(wv[2], wv[3]));
-      }
-    }
-    __syncthreads();
-    // ---- dq^T = K^T W^T + C~_s (g R)^T (+ g dnq n~_s): x tiles of this wave x query tiles
-    {
-      f32x4 acc[XPW][4];
-#pragma unroll
-      for (int p = 0; p < XPW; ++p)
-#pragma unroll
-        for (int it = 0; it < 4; ++it) acc[p][it] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        bf16x8 Bw[4], Bg[4];
-#pragma unroll
-        for (int it = 0; it < 4; ++it) {
-          Bw[it] = rowfrag(sW, it * 16 + l16, 32 * ks + 8 * g);
-          Bg[it] = rowfrag(sGR, it * 16 + l16, 32 * ks + 8 * g);
-        }
-#pragma unroll
-        for (int p = 0; p < XPW; ++p) {
-          const int xt = wave * XPW + p;
-          const bf16x8 Ak = colfrag(wide(sK, xt * 16), 32 * ks, (xt * 16) & 63, g, kr, kq);
-          const bf16x8 Ac = rowfrag(sCX, xt * 16 + l16, 32 * ks + 8 * g);
-#pragma unroll
-          for (int it = 0; it < 4; ++it) {
-            acc[p][it] = mfma16x16x32(Ak, Bw[it], acc[p][it]);
-            acc[p][it] = mfma16x16x32(Ac, Bg[it], acc[p][it]);
-          }
-        }
-      }
-      float* out = a.ws_dq + ((static_cast<int64_t>(cb) * BH + bh) * T + static_cast<int64_t>(c) * LC) * DK;
-#pragma unroll
-      for (int p = 0; p < XPW; ++p) {
-        const int x0 = (wave * XPW + p) * 16 + 4 * g;
-#pragma unroll
-        for (int it = 0; it < 4; ++it) {
-          const int i = it * 16 + l16;
-          const float f = lead ? G.g[i] * sDnq[i] : 0.0f;
-          *reinterpret_cast<float4*>(out + i * DK + x0) =
-              make_float4(acc[p][it][0] + f * sN[x0], acc[p][it][1] + f * sN[x0 + 1],
-                          acc[p][it][2] + f * sN[x0 + 2], acc[p][it][3] + f * sN[x0 + 3]);
-        }
-      }
-    }
-    __syncthreads();   // C~_s is no longer read
-    // ---- dC (carried, float32) to LDS as bf16 [x][b]
-#pragma unroll
-    for (int xt = 0; xt < NXT; ++xt)
-      *reinterpret_cast<uint2*>(sCX + swz(xt * 16 + l16, wave * 16 + 4 * g)) =
-          make_uint2(pk2(dCt[xt][0], dCt[xt][1]), pk2(dCt[xt][2], dCt[xt][3]));
-    __syncthreads();
-    // ---- dk^T = Q^T W + dC (w V)^T (+ w dn), in two halves of the key tiles
-    // (half the accumulators live at a time: the register budget is full)
-    {
-      float* out = a.ws_dk + ((static_cast<int64_t>(cb) * BH + bh) * T + static_cast<int64_t>(c) * LC) * DK;
-#pragma unroll
-      for (int jh = 0; jh < 2; ++jh) {
-        f32x4 acc[XPW][2];
-#pragma unroll
-        for (int p = 0; p < XPW; ++p) {
-          acc[p][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-          acc[p][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          bf16x8 Bw[2], Bv[2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int jt = 2 * jh + u;
-            Bw[u] = colfrag(sW, 32 * ks, jt * 16, g, kr, kq);
-            Bv[u] = rowfrag(sWV, jt * 16 + l16, 32 * ks + 8 * g);
-          }
-#pragma unroll
-          for (int p = 0; p < XPW; ++p) {
-            const int xt = wave * XPW + p;
-            const bf16x8 Aq = colfrag(wide(sQ, xt * 16), 32 * ks, (xt * 16) & 63, g, kr, kq);
-            const bf16x8 Ac = rowfrag(sCX, xt * 16 + l16, 32 * ks + 8 * g);
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              acc[p][u] = mfma16x16x32(Aq, Bw[u], acc[p][u]);
-              acc[p][u] = mfma16x16x32(Ac, Bv[u], acc[p][u]);
-            }
-          }
-        }
-#pragma unroll
-        for (int p = 0; p < XPW; ++p) {
-          const int x0 = (wave * XPW + p) * 16 + 4 * g;
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int j = (2 * jh + u) * 16 + l16;
-            const float f = lead ? G.w[j] : 0.0f;
-            *reinterpret_cast<float4*>(out + j * DK + x0) =
-                make_float4(acc[p][u][0] + f * sDn[x0], acc[p][u][1] + f * sDn[x0 + 1],
-                            acc[p][u][2] + f * sDn[x0 + 2], acc[p][u][3] + f * sDn[x0 + 3]);
-          }
-        }
-      }
-    }
     // ---- dv^T = R^T DS + w (dC^T K^T) for value tile bt = wave
     {
       f32x4 accA[4], accB[4];
@@ -617,8 +510,8 @@ __global__ __launch_bounds__(NT4, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
         }
       }
     }
-    __syncthreads();   // every read of sDn (dk) is done
-    // ---- dn <- g_L dn + sum_i g_i dnq_i q_i (column block 0 only uses dn)
+    // ---- dn <- g_L dn + sum_i g_i dnq_i q_i (column block 0 only; sDn was
+    // last read at this chunk's top, before the second barrier)
     if (lead && g == 0) {
       const float gL = G.g[LC - 1];
 #pragma unroll
@@ -892,6 +785,251 @@ __global__ __launch_bounds__(NT8, 1) void bwd_states_mfma_kernel(BwdArgs a) {
   }
 }
 
+// dq and dk of one chunk over all of d_v, for every (head, chunk, d_qk slice)
+// at once.  The reverse pass has stored, per chunk, r (bf16 [T][d_v]), the
+// memory gradient at the chunk's end (dC, bf16 tiles in the state tiles'
+// order), dn at the chunk's end and dnq; the state pass the boundary state
+// C~_s and n~_s.  With g_i = exp(m_s - M_i), w_j = exp(u_j - M_L) and
+// D_ij = exp(u_j - M_i) (j <= i) from the chunk's gate scan:
+//
+//   dq_i = g_i (C~_s r_i + dnq_i n~_s) + sum_j W_ij k_j
+//   dk_j = w_j (dC v_j + dn)           + sum_i W_ij q_i
+//   W_ij = D_ij (r_i . v_j + dnq_i)
+//
+// Workgroup = (head, chunk, XW rows x of d_qk), 4 waves; wave w owns the x
+// tiles w XPW .. w XPW + XPW - 1 of the slice and, for W, the key tile j =
+// 16 w .. 16 w + 15.  The d_v contractions (C~_s R^T, dC V^T, V R^T) read
+// their operands straight from HBM / L2 as 16-byte MFMA fragments, one
+// 32-column step ahead; the row scales g_i and w_j are applied to the float32
+// accumulators, after which the intra-chunk products add K^T W^T and Q^T W
+// from the LDS copies of this slice of q and k.  The per-token dots q . dq
+// and k . dk of the slice go to HBM for the per-head pass.
+template <int DK>
+__global__ __launch_bounds__(NT4, 2) void bwd_qk_mfma_kernel(BwdArgs a) {
+  constexpr int XW = DK < 128 ? DK : 128;   // d_qk rows per workgroup
+  constexpr int NSPL = DK / XW;
+  constexpr int XPW = XW / 64;              // 16-row x tiles per wave
+  constexpr int NXQ = XW / 64;              // [64][64] tiles of the q (k) slice
+  __shared__ __align__(1024) char sQ[NXQ * TB];
+  __shared__ __align__(1024) char sK[NXQ * TB];
+  __shared__ __align__(1024) char sW[TB];
+  __shared__ Gate64 G;
+  __shared__ float sN[XW], sDn[XW];
+  __shared__ float sDnq[LC];
+  __shared__ float sDot[2][4][LC];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+  const int kr = l16 >> 2, kq = l16 & 3;
+  const int dv = static_cast<int>(a.dv);
+  const int ncb = dv / TVC;
+  const int64_t T = a.T;
+  const int nc = static_cast<int>(T / LC);
+  const int64_t nb = nc + 1;
+  const int64_t BH = a.B * a.H;
+  // workgroup -> (unit = head * nc + chunk, slice): with the unit count a
+  // multiple of 8, the slices of one unit get ids equal mod 8 (one XCD), so
+  // their shared r and v reads meet in one L2
+  int64_t unit;
+  int sp;
+  {
+    const int64_t w = blockIdx.x, nu = BH * nc;
+    if (NSPL == 1) {
+      unit = w;
+      sp = 0;
+    } else if (nu % 8 == 0) {
+      const int64_t grp = w / (8 * NSPL), r = w % (8 * NSPL);
+      sp = static_cast<int>(r / 8);
+      unit = grp * 8 + r % 8;
+    } else {
+      unit = w / NSPL;
+      sp = static_cast<int>(w % NSPL);
+    }
+  }
+  const int64_t bh = unit / nc;
+  const int c = static_cast<int>(unit % nc);
+  const int64_t tok0 = bh * T + static_cast<int64_t>(c) * LC;
+  const int xs = sp * XW;   // first d_qk row of the slice
+
+  // ---- this slice of q and k into LDS (direct loads; waited for before
+  // the barrier that precedes the intra-chunk products).  Load G of 8 * NXQ
+  // per matrix fills rows 8 (G % 8) .. + 7 of tile G / 8; lane l writes
+  // physical chunk l % 8 of row 8 (G % 8) + l / 8, which holds the logical
+  // chunk (l % 8) ^ ((row / 2) % 8).
+  {
+    const bf16_t* q = static_cast<const bf16_t*>(a.q) + tok0 * DK + xs;
+    const bf16_t* k = static_cast<const bf16_t*>(a.k) + tok0 * DK + xs;
+    const int row8 = lane >> 3, pc = lane & 7;
+#pragma unroll
+    for (int p = 0; p < 2 * NXQ; ++p) {
+      const int Gi = wave * 2 * NXQ + p;          // 0 .. 8 NXQ - 1
+      const int t = Gi >> 3, rg = Gi & 7;
+      const int row = 8 * rg + row8;
+      const int64_t off = static_cast<int64_t>(row) * DK + 64 * t + 8 * (pc ^ ((row >> 1) & 7));
+      const uint32_t lq = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(lds_addr(sQ + t * TB + rg * 1024))));
+      const uint32_t lk = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(lds_addr(sK + t * TB + rg * 1024))));
+      dma16(q + off, lq);
+      dma16(k + off, lk);
+    }
+  }
+  if (wave == 0) gate_scan64(a, tok0, a.ws_m[bh * nb + c], G);
+  for (int x = tid; x < XW; x += NT4) {
+    sN[x] = a.ws_n[(bh * nb + c) * DK + xs + x];
+    sDn[x] = a.ws_dn[(bh * nc + c) * DK + xs + x];
+  }
+  if (tid < LC) sDnq[tid] = a.ws_dnq[tok0 + tid];
+
+  // ---- the d_v contractions, 32 columns (one MFMA k step) at a time
+  // fragment sources: lane (l16, g) reads columns b0 + 8 g .. + 7 of
+  //   C~_s and dC rows x = xs + 16 (wave XPW + p) + l16  (A operands)
+  //   r rows i = 16 it + l16, v rows j = 16 jt + l16      (B operands)
+  //   v row 16 wave + l16                                 (A of V R^T)
+  const char* Cst = reinterpret_cast<const char*>(a.ws_Cb);
+  const char* dCt = reinterpret_cast<const char*>(a.ws_dCb);
+  const bf16_t* rrow = a.ws_R + tok0 * dv + 8 * g;
+  const bf16_t* vrow = static_cast<const bf16_t*>(a.v) + tok0 * dv + 8 * g;
+  struct Frag {
+    u32x4 C[XPW], D[XPW], R[4], V[4], Va;
+  };
+  auto load = [&](int ks, Frag& F) {
+    const int b0 = 32 * ks;
+    const int64_t tile = ((bh * ncb + (b0 >> 6)) * nc + c) * static_cast<int64_t>(DK * TVC * 2);
+#pragma unroll
+    for (int p = 0; p < XPW; ++p) {
+      const int x = xs + 16 * (wave * XPW + p) + l16;
+      const int off = swz(x, (b0 & 63) + 8 * g);
+      F.C[p] = *reinterpret_cast<const u32x4*>(Cst + tile + off);
+      F.D[p] = *reinterpret_cast<const u32x4*>(dCt + tile + off);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      F.R[t] = *reinterpret_cast<const u32x4*>(rrow + static_cast<int64_t>(16 * t + l16) * dv + b0);
+      F.V[t] = *reinterpret_cast<const u32x4*>(vrow + static_cast<int64_t>(16 * t + l16) * dv + b0);
+    }
+    F.Va = *reinterpret_cast<const u32x4*>(vrow + static_cast<int64_t>(16 * wave + l16) * dv + b0);
+  };
+  // accQ[p][it]: dq^T[x = 16 (wave XPW + p) + 4 g + e][i = 16 it + l16]
+  // accK[p][jt]: dk^T[x][j = 16 jt + l16]
+  // accS[it]:    (R V^T)^T[j = 16 wave + 4 g + e][i = 16 it + l16]
+  f32x4 accQ[XPW][4], accK[XPW][4], accS[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    accS[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < XPW; ++p) {
+      accQ[p][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      accK[p][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  auto compute = [&](const Frag& F) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const bf16x8 Br = __builtin_bit_cast(bf16x8, F.R[t]);
+      const bf16x8 Bv = __builtin_bit_cast(bf16x8, F.V[t]);
+      accS[t] = mfma16x16x32(__builtin_bit_cast(bf16x8, F.Va), Br, accS[t]);
+#pragma unroll
+      for (int p = 0; p < XPW; ++p) {
+        accQ[p][t] = mfma16x16x32(__builtin_bit_cast(bf16x8, F.C[p]), Br, accQ[p][t]);
+        accK[p][t] = mfma16x16x32(__builtin_bit_cast(bf16x8, F.D[p]), Bv, accK[p][t]);
+      }
+    }
+  };
+  const int nks = dv / 32;   // even: d_v is a multiple of 64
+  Frag F0, F1;
+  load(0, F0);
+  __syncthreads();   // G, sN, sDn, sDnq
+  for (int ks = 0; ks < nks; ks += 2) {
+    load(ks + 1, F1);
+    compute(F0);
+    if (ks + 2 < nks) load(ks + 2, F0);
+    compute(F1);
+  }
+
+  // ---- W = D (.) (R V^T + dnq) for key tile j = 16 wave + 4 g + e (bf16,
+  // [i][j] in LDS); the inter-chunk terms take their row scales
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int i = it * 16 + l16;
+    const float Mi = G.M[i], dq_ = sDnq[i], gi_ = G.g[i], wi = G.w[i];
+    float wv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = wave * 16 + 4 * g + e;
+      wv[e] = j <= i ? __expf(G.u[j] - Mi) * (accS[it][e] + dq_) : 0.0f;
+    }
+    *reinterpret_cast<uint2*>(sW + swz(i, wave * 16 + 4 * g)) = make_uint2(pk2(wv[0], wv[1]), pk2(wv[2], wv[3]));
+#pragma unroll
+    for (int p = 0; p < XPW; ++p) {
+      accQ[p][it] *= gi_;
+      accK[p][it] *= wi;   // here it is the key tile: w of key 16 it + l16
+    }
+  }
+  wait_vm<0>();      // this thread's part of the q / k slice has landed
+  __syncthreads();   // W and the slice are visible
+  // ---- dq^T += K^T W^T,  dk^T += Q^T W  (contraction over the chunk's tokens)
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    bf16x8 Bw[4], Bwt[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      Bw[t] = rowfrag(sW, t * 16 + l16, 32 * ks + 8 * g);    // [k = j][n = i] = W[i][j]
+      Bwt[t] = colfrag(sW, 32 * ks, t * 16, g, kr, kq);      // [k = i][n = j] = W[i][j]
+    }
+#pragma unroll
+    for (int p = 0; p < XPW; ++p) {
+      const int xl = 16 * (wave * XPW + p);
+      const bf16x8 Ak = colfrag(wide(sK, xl), 32 * ks, xl & 63, g, kr, kq);
+      const bf16x8 Aq = colfrag(wide(sQ, xl), 32 * ks, xl & 63, g, kr, kq);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        accQ[p][t] = mfma16x16x32(Ak, Bw[t], accQ[p][t]);
+        accK[p][t] = mfma16x16x32(Aq, Bwt[t], accK[p][t]);
+      }
+    }
+  }
+  // ---- the normalizer terms, dq and dk to HBM, and the slice's dots
+  float qd[4], kd[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int i = t * 16 + l16;
+    const float fq = G.g[i] * sDnq[i], fk = G.w[i];
+    qd[t] = 0.0f;
+    kd[t] = 0.0f;
+#pragma unroll
+    for (int p = 0; p < XPW; ++p) {
+      const int xl = 16 * (wave * XPW + p) + 4 * g;
+      float vq[4], vk[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vq[e] = accQ[p][t][e] + fq * sN[xl + e];
+        vk[e] = accK[p][t][e] + fk * sDn[xl + e];
+      }
+      const int64_t o = (tok0 + i) * DK + xs + xl;
+      *reinterpret_cast<float4*>(a.d_q + o) = make_float4(vq[0], vq[1], vq[2], vq[3]);
+      *reinterpret_cast<float4*>(a.d_k + o) = make_float4(vk[0], vk[1], vk[2], vk[3]);
+      const uint2 q4 = *reinterpret_cast<const uint2*>(wide(sQ, xl) + swz(i, xl & 63));
+      const uint2 k4 = *reinterpret_cast<const uint2*>(wide(sK, xl) + swz(i, xl & 63));
+      qd[t] += (bf_lo(q4.x) * vq[0] + bf_hi(q4.x) * vq[1]) + (bf_lo(q4.y) * vq[2] + bf_hi(q4.y) * vq[3]);
+      kd[t] += (bf_lo(k4.x) * vk[0] + bf_hi(k4.x) * vk[1]) + (bf_lo(k4.y) * vk[2] + bf_hi(k4.y) * vk[3]);
+    }
+    // over the four lane groups g (the x rows of each tile)
+    qd[t] += __shfl_xor(qd[t], 16, 64);
+    qd[t] += __shfl_xor(qd[t], 32, 64);
+    kd[t] += __shfl_xor(kd[t], 16, 64);
+    kd[t] += __shfl_xor(kd[t], 32, 64);
+    if (g == 0) {
+      sDot[0][wave][i] = qd[t];
+      sDot[1][wave][i] = kd[t];
+    }
+  }
+  __syncthreads();
+  if (tid < 2 * LC) {
+    const int which = tid >> 6, i = tid & 63;
+    const float s = (sDot[which][0][i] + sDot[which][1][i]) + (sDot[which][2][i] + sDot[which][3][i]);
+    (which ? a.ws_kd : a.ws_qd)[sp * BH * T + tok0 + i] = s;
+  }
+}
+
 template <int DK>
 hipError_t launch_states_dk(const BwdArgs& a, hipStream_t st) {
   bwd_states_mfma_kernel<DK><<<static_cast<unsigned>(a.B * a.H * (a.dv / TVC)), NT8, 0, st>>>(a);
@@ -906,7 +1044,17 @@ hipError_t launch_dk(const BwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int DK>
+hipError_t launch_qk_dk(const BwdArgs& a, hipStream_t st) {
+  constexpr int NSPL = DK < 128 ? 1 : DK / 128;
+  const unsigned wgs = static_cast<unsigned>(a.B * a.H * (a.T / LC) * NSPL);
+  bwd_qk_mfma_kernel<DK><<<wgs, NT4, 0, st>>>(a);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+int bwd_qk_slices(const BwdArgs& a) { return a.dqk < 128 ? 1 : static_cast<int>(a.dqk / 128); }
 
 bool bwd_mfma_supported(const BwdArgs& a) {
   return a.qkv_bf16 && a.L == LC && a.T % LC == 0 && a.dv % TVC == 0 &&
@@ -926,6 +1074,14 @@ hipError_t launch_bwd_rev_mfma(const BwdArgs& a, hipStream_t st) {
     case 64: return launch_dk<64>(a, st);
     case 128: return launch_dk<128>(a, st);
     default: return launch_dk<256>(a, st);
+  }
+}
+
+hipError_t launch_bwd_qk_mfma(const BwdArgs& a, hipStream_t st) {
+  switch (a.dqk) {
+    case 64: return launch_qk_dk<64>(a, st);
+    case 128: return launch_qk_dk<128>(a, st);
+    default: return launch_qk_dk<256>(a, st);
   }
 }
 

@@ -117,14 +117,21 @@ struct BwdArgs {
   float* ws_n;
   float* ws_m;
   float* ws_beta;
-  float* ws_dq;
+  float* ws_dq;     // chunk 16/32: per-column-block partials of dq, dk
   float* ws_dk;
   float* ws_s;
   float* ws_dm0;
+  // chunk 64 only
+  uint16_t* ws_dCb; // bf16 dC at each chunk's end, tiles as ws_Cb
+  uint16_t* ws_R;   // bf16 r = sigmoid(o~) dh / den, [bh T][d_v]
+  float* ws_dnq;    // normalizer gradient per token
+  float* ws_dn;     // dn at each chunk's end, [bh][c][d_qk]
+  float* ws_qd;     // q . dq and k . dk per d_qk slice, [slice][bh T]
+  float* ws_kd;
 };
 bool bwd_supported(const BwdArgs& a);
 int bwd_tile_columns(const BwdArgs& a);
-size_t bwd_workspace(const BwdArgs& a, size_t offsets[8]);
+size_t bwd_workspace(const BwdArgs& a, size_t offsets[12]);
 hipError_t launch_bwd(BwdArgs a, void* ws, hipStream_t stream);
 // Backward of a sequence of T = 0 tokens: state gradients only.
 hipError_t launch_bwd_empty(const BwdArgs& a, hipStream_t stream);
@@ -136,6 +143,8 @@ hipError_t launch_fill_words(uint32_t* base, int64_t rows, int64_t pitch, int64_
 bool bwd_mfma_supported(const BwdArgs& a);
 hipError_t launch_bwd_states_mfma(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_rev_mfma(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_qk_mfma(const BwdArgs& a, hipStream_t stream);
+int bwd_qk_slices(const BwdArgs& a);
 
 // Block operations around the cell (block_ops.hip).
 struct GnArgs {
