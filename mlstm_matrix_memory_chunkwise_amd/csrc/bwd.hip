@@ -462,10 +462,9 @@ __global__ __launch_bounds__(NTB) void bwd_tok_kernel(BwdArgs a, int ncb) {
 }
 
 // ---- pass 5: per head, d(log f_t) = sum_{t'>=t} s_t' + <dC1, C~_T> + <dn1, n~_T>
-// (a reverse prefix sum, one block scan per tile of NTB tokens), df~ and dm0.
-// With nspl > 0 (chunk 64) s_t = q.dq - k.dk is summed here from the dq/dk
-// pass's nspl d_qk slices, and d~i_t = k.dk is written as well.
-__global__ __launch_bounds__(NTB) void bwd_head_kernel(BwdArgs a, int ncb, int nc, int nspl) {
+// (a reverse prefix sum, one block scan per tile of NTB tokens), df~ and dm0
+// (chunk 16/32; chunk 64 has its own pass in bwd_mfma.hip).
+__global__ __launch_bounds__(NTB) void bwd_head_kernel(BwdArgs a, int ncb, int nc) {
   __shared__ float sRed[NTB / 64];
   const int tid = threadIdx.x;
   const int64_t bh = blockIdx.x;
@@ -495,17 +494,7 @@ __global__ __launch_bounds__(NTB) void bwd_head_kernel(BwdArgs a, int ncb, int n
   float carry = kend;   // sum over the tiles after this one, plus the constant term
   __syncthreads();      // every read of sRed by block_sum is done
   const int64_t ntile = (T + NTB - 1) / NTB;
-  const int64_t BHT = a.B * a.H * T;
-  auto s_at = [&](int64_t t) {
-    if (nspl == 0) return a.ws_s[bh * T + t];
-    float qd = 0.0f, kd = 0.0f;
-    for (int p = 0; p < nspl; ++p) {
-      qd += a.ws_qd[p * BHT + bh * T + t];
-      kd += a.ws_kd[p * BHT + bh * T + t];
-    }
-    a.d_i[bh * T + t] = kd;
-    return qd - kd;
-  };
+  auto s_at = [&](int64_t t) { return a.ws_s[bh * T + t]; };
   float sv_n, fp_n;   // the next tile's inputs, loaded one tile ahead
   {
     const int64_t t = (ntile - 1) * NTB + (NTB - 1 - tid);
@@ -553,17 +542,15 @@ hipError_t launch_typed(const BwdArgs& a, hipStream_t st) {
   bwd_states_kernel<T, TV, L><<<wgs, NTB, 0, st>>>(a);
   bwd_rev_kernel<T, TO, TV, L><<<wgs, NTB, 0, st>>>(a);
   bwd_tok_kernel<T><<<tok_blocks, NTB, 0, st>>>(a, ncb);
-  bwd_head_kernel<<<static_cast<unsigned>(a.B * a.H), NTB, 0, st>>>(a, ncb, nc, 0);
+  bwd_head_kernel<<<static_cast<unsigned>(a.B * a.H), NTB, 0, st>>>(a, ncb, nc);
   return hipGetLastError();
 }
 
-// Chunk 64 (bf16 q, k, v): the state, reverse and dq/dk passes on MFMA
-// (bwd_mfma.hip); the per-token sums come with the per-head pass.
+// Chunk 64 (bf16 q, k, v): the state, reverse and dq/dk passes on MFMA and
+// the per-chunk gate pass (bwd_mfma.hip).
 template <typename T>
 hipError_t launch_mfma(const BwdArgs& a, hipStream_t st) {
   const int64_t ntok = a.B * a.H * a.T;
-  const int ncb = static_cast<int>(a.dv / 64);
-  const int nc = static_cast<int>(a.T / 64);
   const unsigned tok_blocks = static_cast<unsigned>((ntok + NTB / 64 - 1) / (NTB / 64));
   bwd_beta_kernel<T><<<(tok_blocks + 1) / 2, NTB, 0, st>>>(a);
   hipError_t e = launch_bwd_states_mfma(a, st);
@@ -572,8 +559,7 @@ hipError_t launch_mfma(const BwdArgs& a, hipStream_t st) {
   if (e != hipSuccess) return e;
   e = launch_bwd_qk_mfma(a, st);
   if (e != hipSuccess) return e;
-  bwd_head_kernel<<<static_cast<unsigned>(a.B * a.H), NTB, 0, st>>>(a, ncb, nc, bwd_qk_slices(a));
-  return hipGetLastError();
+  return launch_bwd_gates_mfma(a, st);
 }
 
 template <typename T, typename TO>
@@ -602,24 +588,24 @@ bool bwd_supported(const BwdArgs& a) {
 
 // Workspace layout, in order: the boundary states, ws_n, ws_m, ws_beta, then
 // chunk 16/32: ws_dq, ws_dk (per-column-block partials), ws_s, ws_dm0;
-// chunk 64: ws_dCb, ws_R, ws_qd, ws_kd, ws_dm0, ws_dnq, ws_dn.
-size_t bwd_workspace(const BwdArgs& a, size_t offsets[12]) {
+// chunk 64: ws_dCb, ws_R, ws_qd, ws_kd, ws_dm0, ws_dnq, ws_dn, ws_csum, ws_kend.
+size_t bwd_workspace(const BwdArgs& a, size_t offsets[16]) {
   const size_t BH = static_cast<size_t>(a.B * a.H), T = static_cast<size_t>(a.T);
   const size_t nb = static_cast<size_t>(a.T / a.L) + 1, dqk = static_cast<size_t>(a.dqk);
   const size_t dv = static_cast<size_t>(a.dv);
   const size_t ncb = dv / static_cast<size_t>(bwd_tile_columns(a));
   const size_t nc = nb - 1;
-  size_t sizes[12] = {0};
+  size_t sizes[16] = {0};
   size_t n = 0;
   if (a.L == 64) {
     // the boundary states the reverse pass reads as bf16 tiles, and the
     // final state (for the forget-gate term) in float32 after them
     const size_t nspl = static_cast<size_t>(bwd_qk_slices(a));
     const size_t tiles = BH * nc * dqk * dv * 2;
-    const size_t s64[11] = {round_up(tiles) + BH * dqk * dv * 4, BH * nb * dqk * 4, BH * nb * 4, BH * T * 4,
+    const size_t s64[13] = {round_up(tiles) + BH * dqk * dv * 4, BH * nb * dqk * 4, BH * nb * 4, BH * T * 4,
                             tiles, BH * T * dv * 2, nspl * BH * T * 4, nspl * BH * T * 4, ncb * BH * 4,
-                            BH * T * 4, BH * nc * dqk * 4};
-    n = 11;
+                            BH * T * 4, BH * nc * dqk * 4, nspl * BH * nc * 2 * 4, ncb * BH * 4};
+    n = 13;
     for (size_t i = 0; i < n; ++i) sizes[i] = s64[i];
   } else {
     const size_t s16[8] = {BH * nb * dqk * dv * 4, BH * nb * dqk * 4, BH * nb * 4, BH * T * 4,
@@ -628,7 +614,7 @@ size_t bwd_workspace(const BwdArgs& a, size_t offsets[12]) {
     for (size_t i = 0; i < n; ++i) sizes[i] = s16[i];
   }
   size_t off = 0;
-  for (size_t i = 0; i < 12; ++i) {
+  for (size_t i = 0; i < 16; ++i) {
     if (offsets) offsets[i] = off;
     off += round_up(sizes[i]);
   }
@@ -636,14 +622,14 @@ size_t bwd_workspace(const BwdArgs& a, size_t offsets[12]) {
 }
 
 hipError_t launch_bwd(BwdArgs a, void* ws, hipStream_t st) {
-  size_t off[12];
+  size_t off[16];
   bwd_workspace(a, off);
   char* base = static_cast<char*>(ws);
   a.ws_n = reinterpret_cast<float*>(base + off[1]);
   a.ws_m = reinterpret_cast<float*>(base + off[2]);
   a.ws_beta = reinterpret_cast<float*>(base + off[3]);
   a.ws_dCb = a.ws_R = nullptr;
-  a.ws_dnq = a.ws_dn = a.ws_qd = a.ws_kd = nullptr;
+  a.ws_dnq = a.ws_dn = a.ws_qd = a.ws_kd = a.ws_csum = a.ws_kend = nullptr;
   if (a.L == 64) {
     const size_t tiles = static_cast<size_t>(a.B * a.H) * static_cast<size_t>(a.T / 64) *
                          static_cast<size_t>(a.dqk * a.dv) * 2;
@@ -657,6 +643,8 @@ hipError_t launch_bwd(BwdArgs a, void* ws, hipStream_t st) {
     a.ws_dm0 = reinterpret_cast<float*>(base + off[8]);
     a.ws_dnq = reinterpret_cast<float*>(base + off[9]);
     a.ws_dn = reinterpret_cast<float*>(base + off[10]);
+    a.ws_csum = reinterpret_cast<float*>(base + off[11]);
+    a.ws_kend = reinterpret_cast<float*>(base + off[12]);
     a.ws_dq = a.ws_dk = a.ws_s = nullptr;
   } else {
     a.ws_C = reinterpret_cast<float*>(base + off[0]);

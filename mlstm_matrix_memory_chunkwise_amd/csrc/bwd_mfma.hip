@@ -162,6 +162,24 @@ __global__ __launch_bounds__(NT4, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
   }
   for (int x = tid; x < DK; x += NT4) sDn[x] = a.dn1 ? a.dn1[bh * DK + x] : 0.0f;
   reinterpret_cast<uint2*>(sGD)[tid] = make_uint2(0u, 0u);
+  // this column block's share of the final-state term of every d log f_t:
+  // <dC1, C~_T> over its columns (+ <dn1, n~_T> in column block 0)
+  if (a.dC1) {
+    float part = 0.0f;
+#pragma unroll
+    for (int xt = 0; xt < NXT; ++xt) {
+      const float4 c4 = *reinterpret_cast<const float4*>(
+          a.ws_CT + (bh * DK + xt * 16 + l16) * dv + c0 + wave * 16 + 4 * g);
+      part += (dCt[xt][0] * c4.x + dCt[xt][1] * c4.y) + (dCt[xt][2] * c4.z + dCt[xt][3] * c4.w);
+    }
+    if (lead) {
+      for (int x = tid; x < DK; x += NT4) part += a.dn1[bh * DK + x] * a.ws_n[(bh * nb + nc) * DK + x];
+    }
+    part = wave_sum(part);
+    if (lane == 0) sRed[wave] = part;
+    __syncthreads();
+    if (tid == 0) a.ws_kend[static_cast<int64_t>(cb) * BH + bh] = (sRed[0] + sRed[1]) + (sRed[2] + sRed[3]);
+  }
 
   // The chunk's q, k and v (own columns) are loaded into registers one
   // chunk ahead: the loads of chunk c - 1 are in flight while chunk c is
@@ -798,21 +816,28 @@ __global__ __launch_bounds__(NT8, 1) void bwd_states_mfma_kernel(BwdArgs a) {
 //
 // Workgroup = (head, chunk, XW rows x of d_qk), 4 waves; wave w owns the x
 // tiles w XPW .. w XPW + XPW - 1 of the slice and, for W, the key tile j =
-// 16 w .. 16 w + 15.  The d_v contractions (C~_s R^T, dC V^T, V R^T) read
-// their operands straight from HBM / L2 as 16-byte MFMA fragments, one
-// 32-column step ahead; the row scales g_i and w_j are applied to the float32
-// accumulators, after which the intra-chunk products add K^T W^T and Q^T W
-// from the LDS copies of this slice of q and k.  The per-token dots q . dq
-// and k . dk of the slice go to HBM for the per-head pass.
+// 16 w .. 16 w + 15.  In the d_v contractions (C~_s R^T, dC V^T, V R^T)
+// each wave reads its own C~_s and dC rows straight from HBM as 16-byte MFMA
+// fragments, while r and v, which every wave needs whole, pass once per
+// workgroup through LDS (each wave reading them itself doubled the L2
+// requests and cost 0.33 ms per backward at d = 256, T = 8192).  The row
+// scales g_i and w_j are applied to the float32 accumulators, after which the
+// intra-chunk products add K^T W^T and Q^T W from the LDS copies of this
+// slice of q and k.  The per-token dots q . dq and k . dk of the slice go to
+// HBM for the per-head pass.
+constexpr int QK_XW = 128;      // d_qk rows per workgroup of the dq/dk pass (at most)
+constexpr int QK_OCC = 2;       // its workgroups per CU (waves per SIMD)
+
 template <int DK>
-__global__ __launch_bounds__(NT4, 2) void bwd_qk_mfma_kernel(BwdArgs a) {
-  constexpr int XW = DK < 128 ? DK : 128;   // d_qk rows per workgroup
+__global__ __launch_bounds__(NT4, QK_OCC) void bwd_qk_mfma_kernel(BwdArgs a) {
+  constexpr int XW = DK < QK_XW ? DK : QK_XW;   // d_qk rows per workgroup
   constexpr int NSPL = DK / XW;
   constexpr int XPW = XW / 64;              // 16-row x tiles per wave
   constexpr int NXQ = XW / 64;              // [64][64] tiles of the q (k) slice
   __shared__ __align__(1024) char sQ[NXQ * TB];
   __shared__ __align__(1024) char sK[NXQ * TB];
   __shared__ __align__(1024) char sW[TB];
+  __shared__ __align__(1024) char sRV[2][2][TB];   // [step parity][r, v]: 64 columns of d_v
   __shared__ Gate64 G;
   __shared__ float sN[XW], sDn[XW];
   __shared__ float sDnq[LC];
@@ -879,19 +904,20 @@ __global__ __launch_bounds__(NT4, 2) void bwd_qk_mfma_kernel(BwdArgs a) {
   }
   if (tid < LC) sDnq[tid] = a.ws_dnq[tok0 + tid];
 
-  // ---- the d_v contractions, 32 columns (one MFMA k step) at a time
-  // fragment sources: lane (l16, g) reads columns b0 + 8 g .. + 7 of
-  //   C~_s and dC rows x = xs + 16 (wave XPW + p) + l16  (A operands)
-  //   r rows i = 16 it + l16, v rows j = 16 jt + l16      (B operands)
-  //   v row 16 wave + l16                                 (A of V R^T)
+  // ---- the d_v contractions, one MFMA k step (32 columns) at a time.
+  // Fragments: lane (l16, g) holds columns b0 + 8 g .. + 7 of
+  //   C~_s and dC rows x = xs + 16 (wave XPW + p) + l16  (A operands, HBM)
+  //   r rows i = 16 it + l16, v rows j = 16 jt + l16      (B operands, LDS)
+  //   v row 16 wave + l16                                 (A of V R^T, LDS)
   const char* Cst = reinterpret_cast<const char*>(a.ws_Cb);
   const char* dCt = reinterpret_cast<const char*>(a.ws_dCb);
-  const bf16_t* rrow = a.ws_R + tok0 * dv + 8 * g;
-  const bf16_t* vrow = static_cast<const bf16_t*>(a.v) + tok0 * dv + 8 * g;
-  struct Frag {
-    u32x4 C[XPW], D[XPW], R[4], V[4], Va;
+  struct FragCD {
+    u32x4 C[XPW], D[XPW];
   };
-  auto load = [&](int ks, Frag& F) {
+  struct FragRV {
+    u32x4 R[4], V[4], Va;
+  };
+  auto load_cd = [&](int ks, FragCD& F) {
     const int b0 = 32 * ks;
     const int64_t tile = ((bh * ncb + (b0 >> 6)) * nc + c) * static_cast<int64_t>(DK * TVC * 2);
 #pragma unroll
@@ -901,12 +927,6 @@ __global__ __launch_bounds__(NT4, 2) void bwd_qk_mfma_kernel(BwdArgs a) {
       F.C[p] = *reinterpret_cast<const u32x4*>(Cst + tile + off);
       F.D[p] = *reinterpret_cast<const u32x4*>(dCt + tile + off);
     }
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      F.R[t] = *reinterpret_cast<const u32x4*>(rrow + static_cast<int64_t>(16 * t + l16) * dv + b0);
-      F.V[t] = *reinterpret_cast<const u32x4*>(vrow + static_cast<int64_t>(16 * t + l16) * dv + b0);
-    }
-    F.Va = *reinterpret_cast<const u32x4*>(vrow + static_cast<int64_t>(16 * wave + l16) * dv + b0);
   };
   // accQ[p][it]: dq^T[x = 16 (wave XPW + p) + 4 g + e][i = 16 it + l16]
   // accK[p][jt]: dk^T[x][j = 16 jt + l16]
@@ -921,12 +941,12 @@ __global__ __launch_bounds__(NT4, 2) void bwd_qk_mfma_kernel(BwdArgs a) {
       accK[p][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
-  auto compute = [&](const Frag& F) {
+  auto compute = [&](const FragCD& F, const FragRV& G) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const bf16x8 Br = __builtin_bit_cast(bf16x8, F.R[t]);
-      const bf16x8 Bv = __builtin_bit_cast(bf16x8, F.V[t]);
-      accS[t] = mfma16x16x32(__builtin_bit_cast(bf16x8, F.Va), Br, accS[t]);
+      const bf16x8 Br = __builtin_bit_cast(bf16x8, G.R[t]);
+      const bf16x8 Bv = __builtin_bit_cast(bf16x8, G.V[t]);
+      accS[t] = mfma16x16x32(__builtin_bit_cast(bf16x8, G.Va), Br, accS[t]);
 #pragma unroll
       for (int p = 0; p < XPW; ++p) {
         accQ[p][t] = mfma16x16x32(__builtin_bit_cast(bf16x8, F.C[p]), Br, accQ[p][t]);
@@ -934,15 +954,59 @@ __global__ __launch_bounds__(NT4, 2) void bwd_qk_mfma_kernel(BwdArgs a) {
       }
     }
   };
-  const int nks = dv / 32;   // even: d_v is a multiple of 64
-  Frag F0, F1;
-  load(0, F0);
-  __syncthreads();   // G, sN, sDn, sDnq
-  for (int ks = 0; ks < nks; ks += 2) {
-    load(ks + 1, F1);
-    compute(F0);
-    if (ks + 2 < nks) load(ks + 2, F0);
-    compute(F1);
+  {
+    // 64 columns of d_v per step: this thread's share of the step's r and v
+    // (rows e / 8, 16-byte chunk e % 8 of each [64][64] tile) is read into
+    // registers one step ahead and written to the LDS buffer of the step's
+    // parity at its top; C~_s and dC fragments (per wave) one step ahead in
+    // registers.  One barrier per step: a buffer is rewritten two steps after
+    // it was read, and every wave has passed the previous step's barrier.
+    constexpr int NRV = 2 * LC * 64 / 8 / NT4;
+    u32x4 rv[NRV];
+    const bf16_t* rb = a.ws_R + tok0 * dv;
+    const bf16_t* vb = static_cast<const bf16_t*>(a.v) + tok0 * dv;
+    auto load_rv_regs = [&](int st) {
+#pragma unroll
+      for (int p = 0; p < NRV; ++p) {
+        const int e = tid + p * NT4, mat = e >> 9, row = (e >> 3) & 63, ch = e & 7;
+        rv[p] = *reinterpret_cast<const u32x4*>((mat ? vb : rb) + static_cast<int64_t>(row) * dv + 64 * st + 8 * ch);
+      }
+    };
+    auto store_rv = [&](int par) {
+#pragma unroll
+      for (int p = 0; p < NRV; ++p) {
+        const int e = tid + p * NT4, mat = e >> 9, row = (e >> 3) & 63, ch = e & 7;
+        *reinterpret_cast<u32x4*>(sRV[par][mat] + swz(row, 8 * ch)) = rv[p];
+      }
+    };
+    const int nst = dv / 64;
+    FragCD Fa[2], Fb[2];
+    load_rv_regs(0);
+    load_cd(0, Fa[0]);
+    load_cd(1, Fa[1]);
+    for (int st = 0; st < nst; ++st) {
+      const int par = st & 1;
+      store_rv(par);
+      if (st + 1 < nst) {
+        load_rv_regs(st + 1);
+        load_cd(2 * st + 2, Fb[0]);
+        load_cd(2 * st + 3, Fb[1]);
+      }
+      __syncthreads();   // this step's r, v (and, at the first step, G, sN, sDn, sDnq)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        FragRV Gf;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          Gf.R[t] = __builtin_bit_cast(u32x4, lds_ld16(sRV[par][0], swz(16 * t + l16, 32 * kk + 8 * g)));
+          Gf.V[t] = __builtin_bit_cast(u32x4, lds_ld16(sRV[par][1], swz(16 * t + l16, 32 * kk + 8 * g)));
+        }
+        Gf.Va = __builtin_bit_cast(u32x4, lds_ld16(sRV[par][1], swz(16 * wave + l16, 32 * kk + 8 * g)));
+        compute(Fa[kk], Gf);
+      }
+      Fa[0] = Fb[0];
+      Fa[1] = Fb[1];
+    }
   }
 
   // ---- W = D (.) (R V^T + dnq) for key tile j = 16 wave + 4 g + e (bf16,
@@ -1023,10 +1087,56 @@ __global__ __launch_bounds__(NT4, 2) void bwd_qk_mfma_kernel(BwdArgs a) {
     }
   }
   __syncthreads();
-  if (tid < 2 * LC) {
+  if (tid < 2 * LC) {   // wave 0: q . dq, wave 1: k . dk; and their sums over the chunk
     const int which = tid >> 6, i = tid & 63;
     const float s = (sDot[which][0][i] + sDot[which][1][i]) + (sDot[which][2][i] + sDot[which][3][i]);
     (which ? a.ws_kd : a.ws_qd)[sp * BH * T + tok0 + i] = s;
+    const float tot = wave_sum(s);
+    if (i == 0) a.ws_csum[(sp * BH * nc + unit) * 2 + which] = tot;
+  }
+}
+
+// d~i and d log f per token, and dm0, one wave per (head, chunk).  From
+// the dq/dk pass's per-token q . dq and k . dk (per d_qk slice) and their
+// chunk sums, and the final-state term from the reverse pass:
+//   d~i_t = k_t . dk_t
+//   d log f_t = sum_{t' >= t} (q_t' . dq_t' - k_t' . dk_t') + <dC1, C~_T> + <dn1, n~_T>
+// (the derivative of the cumulative log forget gates of the chunkwise form).
+// The sum over the chunks after this one comes from their chunk sums; within
+// the chunk, lane l takes token 63 - l, so a prefix sum over the lanes is the
+// sum over the tokens at and after it.
+__global__ __launch_bounds__(NT4) void bwd_gates64_kernel(BwdArgs a, int nspl, int ncb) {
+  const int lane = threadIdx.x & 63;
+  const int64_t T = a.T, BH = a.B * a.H;
+  const int nc = static_cast<int>(T / LC);
+  const int64_t unit = static_cast<int64_t>(blockIdx.x) * (NT4 / 64) + (threadIdx.x >> 6);
+  if (unit >= BH * nc) return;   // (no barriers below)
+  const int64_t bh = unit / nc;
+  const int c = static_cast<int>(unit % nc);
+  float carry = 0.0f;
+  for (int c2 = c + 1 + lane; c2 < nc; c2 += 64) {
+    for (int p = 0; p < nspl; ++p) {
+      const float* cs = a.ws_csum + (p * BH * nc + bh * nc + c2) * 2;
+      carry += cs[0] - cs[1];
+    }
+  }
+  if (a.dC1) {
+    for (int cb = lane; cb < ncb; cb += 64) carry += a.ws_kend[static_cast<int64_t>(cb) * BH + bh];
+  }
+  carry = wave_sum(carry);
+  const int64_t t = bh * T + static_cast<int64_t>(c) * LC + (LC - 1 - lane);
+  float qd = 0.0f, kd = 0.0f;
+  for (int p = 0; p < nspl; ++p) {
+    qd += a.ws_qd[p * BH * T + t];
+    kd += a.ws_kd[p * BH * T + t];
+  }
+  a.d_i[t] = kd;
+  const float after = carry + scan_add(qd - kd);
+  a.d_f[t] = a.fgate_exp ? after : after * (1.0f - sigmoid_fast(a.f_pre[t]));
+  if (a.dm0 && c == 0 && lane == 0) {
+    float s = 0.0f;
+    for (int cb = 0; cb < ncb; ++cb) s += a.ws_dm0[static_cast<int64_t>(cb) * BH + bh];
+    a.dm0[bh] = s;
   }
 }
 
@@ -1046,7 +1156,7 @@ hipError_t launch_dk(const BwdArgs& a, hipStream_t st) {
 
 template <int DK>
 hipError_t launch_qk_dk(const BwdArgs& a, hipStream_t st) {
-  constexpr int NSPL = DK < 128 ? 1 : DK / 128;
+  constexpr int NSPL = DK < QK_XW ? 1 : DK / QK_XW;
   const unsigned wgs = static_cast<unsigned>(a.B * a.H * (a.T / LC) * NSPL);
   bwd_qk_mfma_kernel<DK><<<wgs, NT4, 0, st>>>(a);
   return hipGetLastError();
@@ -1054,7 +1164,7 @@ hipError_t launch_qk_dk(const BwdArgs& a, hipStream_t st) {
 
 }  // namespace
 
-int bwd_qk_slices(const BwdArgs& a) { return a.dqk < 128 ? 1 : static_cast<int>(a.dqk / 128); }
+int bwd_qk_slices(const BwdArgs& a) { return a.dqk < QK_XW ? 1 : static_cast<int>(a.dqk / QK_XW); }
 
 bool bwd_mfma_supported(const BwdArgs& a) {
   return a.qkv_bf16 && a.L == LC && a.T % LC == 0 && a.dv % TVC == 0 &&
@@ -1083,6 +1193,13 @@ hipError_t launch_bwd_qk_mfma(const BwdArgs& a, hipStream_t st) {
     case 128: return launch_qk_dk<128>(a, st);
     default: return launch_qk_dk<256>(a, st);
   }
+}
+
+hipError_t launch_bwd_gates_mfma(const BwdArgs& a, hipStream_t st) {
+  const int64_t units = a.B * a.H * (a.T / LC);
+  const unsigned wgs = static_cast<unsigned>((units + NT4 / 64 - 1) / (NT4 / 64));
+  bwd_gates64_kernel<<<wgs, NT4, 0, st>>>(a, bwd_qk_slices(a), static_cast<int>(a.dv / TVC));
+  return hipGetLastError();
 }
 
 }  // namespace mlstm

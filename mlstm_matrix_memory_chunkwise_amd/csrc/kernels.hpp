@@ -128,10 +128,12 @@ struct BwdArgs {
   float* ws_dn;     // dn at each chunk's end, [bh][c][d_qk]
   float* ws_qd;     // q . dq and k . dk per d_qk slice, [slice][bh T]
   float* ws_kd;
+  float* ws_csum;   // their sums over each chunk, [slice][bh][c][q, k]
+  float* ws_kend;   // <dC1, C~_T> (+ <dn1, n~_T> in block 0) per column block, [cb][bh]
 };
 bool bwd_supported(const BwdArgs& a);
 int bwd_tile_columns(const BwdArgs& a);
-size_t bwd_workspace(const BwdArgs& a, size_t offsets[12]);
+size_t bwd_workspace(const BwdArgs& a, size_t offsets[16]);
 hipError_t launch_bwd(BwdArgs a, void* ws, hipStream_t stream);
 // Backward of a sequence of T = 0 tokens: state gradients only.
 hipError_t launch_bwd_empty(const BwdArgs& a, hipStream_t stream);
@@ -144,6 +146,7 @@ bool bwd_mfma_supported(const BwdArgs& a);
 hipError_t launch_bwd_states_mfma(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_rev_mfma(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_qk_mfma(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_gates_mfma(const BwdArgs& a, hipStream_t stream);
 int bwd_qk_slices(const BwdArgs& a);
 
 // Block operations around the cell (block_ops.hip).
