@@ -114,29 +114,50 @@ __device__ __forceinline__ void gate_scan64(const BwdArgs& a, int64_t tok0, floa
 
 __device__ __forceinline__ uint32_t pk2(float a, float b) { return cvt2(a, b); }
 
+constexpr int NT8 = 512;           // 8 waves
+
+// The reverse pass: one workgroup of 8 waves per (head, 64 value columns),
+// two roles.  Waves 0-3 ("score" waves, one query tile / 16 columns each)
+// form everything of a chunk that does not depend on the carried dC: S, the
+// denominators and dnq, r, g r and do~.  Waves 4-7 ("memory" waves, 16 value
+// columns each) own dC^T in float32 registers; while the score waves work
+// they store dC at the chunk's end to HBM and form dC^T K^T, and after the
+// chunk's third barrier they finish dv (adding R^T DS) and update dC and dn.
+// Each SIMD runs one wave of each role, and the dC-only work of a chunk
+// overlaps its score work.  The roles run separate loops with the same
+// barrier sequence (one before the loop when dC1 is given, three per chunk,
+// two after it), so that the registers of one role's values are free in the
+// other's code.
 template <int DK, typename TO>
-__global__ __launch_bounds__(NT4, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NT8, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
   constexpr int NXT = DK / 16;      // 16-row tiles of x (d_qk)
-  constexpr int XPW = NXT / 4;      // x tiles per wave in the dn product
+  constexpr int XPW = NXT / 4;      // x tiles per memory wave in the dn product
   constexpr int NQT = DK / 64;
+  constexpr int KH = DK / 64;       // 32-row blocks of x per half of d_qk
   __shared__ __align__(1024) char sQ[NQT * TB];
   __shared__ __align__(1024) char sK[NQT * TB];
-  __shared__ __align__(1024) char sV[TB];
   __shared__ __align__(1024) char sR[TB];
   __shared__ __align__(1024) char sGR[TB];
   __shared__ __align__(1024) char sDST[TB];   // (D (.) S)^T: [j][i]
-  __shared__ __align__(1024) char sCX[DK * 128];   // [DK][64]: dC at the chunk's end, bf16
+  // [DK][64]: dC at the chunk's end (bf16), written by the memory waves at
+  // the chunk's top.  Memory wave v then copies rows 16 KH v .. + 16 KH - 1
+  // (bytes KH 2048 v ..) to HBM and reuses them for its transposes of dC (two
+  // halves of [32 x][16 b] hi / lo tiles): every access after the second
+  // barrier is private to one wave.
+  __shared__ __align__(1024) char sCX[DK * 128];
   __shared__ __align__(1024) char sGD[16 * 128];   // rows 0, 1: g (.) dnq as bf16 hi / lo; rest 0
-  __shared__ __align__(16) char sTW[4 * 2048];     // per wave: [32 x][16 b] bf16 hi, then lo
   __shared__ float sN[DK], sDn[DK];
   __shared__ float sRs[LC];
   __shared__ float sBeta[LC];
   __shared__ Gate64 G;
-  __shared__ float sRed[4];
+  __shared__ float sRed[8];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const int kr = l16 >> 2, kq = l16 & 3;
+  const int rw = wave & 3;          // the wave's index within its role
+  const int rtid = tid & (NT4 - 1); // the thread's index within its role
   const int ncb = static_cast<int>(a.dv / TVC);
   int64_t bh;
   int cb;
@@ -149,364 +170,376 @@ __global__ __launch_bounds__(NT4, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
   const int64_t BH = a.B * a.H;
   const int c0 = cb * TVC;
 
-  // carried dC^T: tile xt holds dC^T[b = 16 wave + 4 g + e][x = 16 xt + l16]
-  f32x4 dCt[NXT];
-#pragma unroll
-  for (int xt = 0; xt < NXT; ++xt) {
-    dCt[xt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (a.dC1) {
-      const float4 v4 = *reinterpret_cast<const float4*>(
-          a.dC1 + (bh * DK + xt * 16 + l16) * dv + c0 + wave * 16 + 4 * g);
-      dCt[xt] = f32x4{v4.x, v4.y, v4.z, v4.w};
-    }
-  }
-  for (int x = tid; x < DK; x += NT4) sDn[x] = a.dn1 ? a.dn1[bh * DK + x] : 0.0f;
-  reinterpret_cast<uint2*>(sGD)[tid] = make_uint2(0u, 0u);
-  // this column block's share of the final-state term of every d log f_t:
-  // <dC1, C~_T> over its columns (+ <dn1, n~_T> in column block 0)
-  if (a.dC1) {
-    float part = 0.0f;
-#pragma unroll
-    for (int xt = 0; xt < NXT; ++xt) {
-      const float4 c4 = *reinterpret_cast<const float4*>(
-          a.ws_CT + (bh * DK + xt * 16 + l16) * dv + c0 + wave * 16 + 4 * g);
-      part += (dCt[xt][0] * c4.x + dCt[xt][1] * c4.y) + (dCt[xt][2] * c4.z + dCt[xt][3] * c4.w);
-    }
-    if (lead) {
-      for (int x = tid; x < DK; x += NT4) part += a.dn1[bh * DK + x] * a.ws_n[(bh * nb + nc) * DK + x];
-    }
-    part = wave_sum(part);
-    if (lane == 0) sRed[wave] = part;
-    __syncthreads();
-    if (tid == 0) a.ws_kend[static_cast<int64_t>(cb) * BH + bh] = (sRed[0] + sRed[1]) + (sRed[2] + sRed[3]);
-  }
+  for (int x = tid; x < DK; x += NT8) sDn[x] = a.dn1 ? a.dn1[bh * DK + x] : 0.0f;
+  if (tid < 16 * 128 / 8) reinterpret_cast<uint2*>(sGD)[tid] = make_uint2(0u, 0u);
 
-  // The chunk's q, k and v (own columns) are loaded into registers one
-  // chunk ahead: the loads of chunk c - 1 are in flight while chunk c is
-  // computed, and land in LDS at the next top.
-  constexpr int NQK = LC * DK / 8 / NT4;    // 16-byte pieces of q (and of k) per thread
-  constexpr int NVV = LC * TVC / 8 / NT4;
-  constexpr int NCC = DK * TVC / 8 / NT4;   // 16-byte pieces of a [DK][64] bf16 tile
+  // The chunk's q and k are loaded into the score waves' registers after
+  // the previous chunk's third barrier: they are in flight while the memory
+  // waves finish that chunk (the score waves are idle then), and land in LDS
+  // at the next top.
+  constexpr int NQK = LC * DK / 8 / NT4;
   // native vectors: HIP's uint4 struct would be copied through private memory
-  u32x4 pq[NQK], pk[NQK], pv[NVV];
-  {
-    const int64_t t0 = bh * T + static_cast<int64_t>(nc - 1) * LC;
+  u32x4 pq[NQK], pk[NQK];
+  auto load_qk = [&](int cc) {
+    const int64_t t0 = bh * T + static_cast<int64_t>(cc) * LC;
     const bf16_t* q = static_cast<const bf16_t*>(a.q) + t0 * DK;
     const bf16_t* k = static_cast<const bf16_t*>(a.k) + t0 * DK;
 #pragma unroll
     for (int p = 0; p < NQK; ++p) {
-      const int e = tid + p * NT4;
+      const int e = rtid + p * NT4;
       const int r = e / (DK / 8), col = (e % (DK / 8)) * 8;
       pq[p] = *reinterpret_cast<const u32x4*>(q + r * DK + col);
       pk[p] = *reinterpret_cast<const u32x4*>(k + r * DK + col);
     }
-    const bf16_t* v = static_cast<const bf16_t*>(a.v) + t0 * dv + c0;
-#pragma unroll
-    for (int p = 0; p < NVV; ++p) {
-      const int e = tid + p * NT4;
-      pv[p] = *reinterpret_cast<const u32x4*>(v + static_cast<int64_t>(e >> 3) * dv + (e & 7) * 8);
-    }
-  }
-
-  // the small per-chunk inputs (gates, m, n~ at the chunk start, beta) are
-  // also read one chunk ahead, into registers, so that no global latency sits
-  // between a chunk's first barrier and its gate scan
-  constexpr int NNR = (DK + NT4 - 1) / NT4;
-  float pf_f, pf_i, pf_ms, pf_b, pf_n[NNR];
-  auto prefetch_small = [&](int cc) {
-    const int64_t t0 = bh * T + static_cast<int64_t>(cc) * LC;
-    pf_f = a.f_pre[t0 + lane];
-    pf_i = a.i_pre[t0 + lane];
-    pf_ms = a.ws_m[bh * nb + cc];
-    pf_b = a.ws_beta[t0 + (tid & (LC - 1))];
-#pragma unroll
-    for (int r = 0; r < NNR; ++r) {
-      const int x = tid + r * NT4;
-      pf_n[r] = x < DK ? a.ws_n[(bh * nb + cc) * DK + x] : 0.0f;
-    }
   };
-  prefetch_small(nc - 1);
-
-  for (int c = nc - 1; c >= 0; --c) {
-    const int64_t tok0 = bh * T + static_cast<int64_t>(c) * LC;
-    __syncthreads();
-    // ---- this chunk's operands into LDS; the next chunk's loads go out
-    if (wave == 0) gate_scan64_v(pf_f, pf_i, a.fgate_exp, pf_ms, G);
-#pragma unroll
-    for (int r = 0; r < NNR; ++r) {
-      const int x = tid + r * NT4;
-      if (x < DK) sN[x] = pf_n[r];
-    }
-    if (tid < LC) sBeta[tid] = pf_b;
+  auto store_qk = [&]() {
 #pragma unroll
     for (int p = 0; p < NQK; ++p) {
-      const int e = tid + p * NT4;
+      const int e = rtid + p * NT4;
       const int r = e / (DK / 8), col = (e % (DK / 8)) * 8;
       *reinterpret_cast<u32x4*>(sQ + (col >> 6) * TB + swz(r, col & 63)) = pq[p];
       *reinterpret_cast<u32x4*>(sK + (col >> 6) * TB + swz(r, col & 63)) = pk[p];
     }
-#pragma unroll
-    for (int p = 0; p < NVV; ++p) {
-      const int e = tid + p * NT4;
-      *reinterpret_cast<u32x4*>(sV + swz(e >> 3, (e & 7) * 8)) = pv[p];
-    }
-    // dC at this chunk's end (bf16, [x][b]) for the HBM copy below, and (in
-    // column block 0) dn at this chunk's end, for the dq/dk pass
-#pragma unroll
-    for (int xt = 0; xt < NXT; ++xt)
-      *reinterpret_cast<uint2*>(sCX + swz(xt * 16 + l16, wave * 16 + 4 * g)) =
-          make_uint2(pk2(dCt[xt][0], dCt[xt][1]), pk2(dCt[xt][2], dCt[xt][3]));
+  };
+  // dn at the chunk's end (column block 0), for the dq/dk pass
+  auto store_dn = [&](int c) {
     if (lead) {
-      for (int x = tid; x < DK; x += NT4) a.ws_dn[(bh * nc + c) * DK + x] = sDn[x];
+      for (int x = tid; x < DK; x += NT8) a.ws_dn[(bh * nc + c) * DK + x] = sDn[x];
     }
-    // the next chunk's loads (chunk 0 fetches itself again: in bounds, unused)
-    {
-      const int64_t t0 = bh * T + static_cast<int64_t>(c > 0 ? c - 1 : 0) * LC;
-      const bf16_t* q = static_cast<const bf16_t*>(a.q) + t0 * DK;
-      const bf16_t* k = static_cast<const bf16_t*>(a.k) + t0 * DK;
+  };
+  // the workgroup's sum of one value per wave, into *out (thread 0)
+  auto wg_sum = [&](float part, float* out) {
+    part = wave_sum(part);
+    if (lane == 0) sRed[wave] = part;
+    __syncthreads();
+    if (tid == 0) {
+      float s8 = 0.0f;
 #pragma unroll
-      for (int p = 0; p < NQK; ++p) {
-        const int e = tid + p * NT4;
-        const int r = e / (DK / 8), col = (e % (DK / 8)) * 8;
-        pq[p] = *reinterpret_cast<const u32x4*>(q + r * DK + col);
-        pk[p] = *reinterpret_cast<const u32x4*>(k + r * DK + col);
-      }
-      const bf16_t* v = static_cast<const bf16_t*>(a.v) + t0 * dv + c0;
-#pragma unroll
-      for (int p = 0; p < NVV; ++p) {
-        const int e = tid + p * NT4;
-        pv[p] = *reinterpret_cast<const u32x4*>(v + static_cast<int64_t>(e >> 3) * dv + (e & 7) * 8);
-      }
+      for (int w = 0; w < 8; ++w) s8 += sRed[w];
+      *out = s8;
     }
-    prefetch_small(c > 0 ? c - 1 : 0);   // (chunk 0 reads itself again: unused)
-    // this thread's dh, h and o~ (row tid / 4, 16 columns) for the r step,
-    // loaded now so that their latency overlaps the score products
-    uint4 pdh[2], ph[2], po[4];
-    {
-      const int64_t gi = (tok0 + (tid >> 2)) * dv + c0 + (tid & 3) * 16;
+  };
+  if (wave < 4) {
+    // ================= score waves
+    // the small per-chunk inputs (gates, m, n~ at the chunk start, beta) are
+    // read one chunk ahead into registers, so that no global latency sits
+    // between a chunk's first barrier and its gate scan
+    constexpr int NNR = (DK + NT4 - 1) / NT4;
+    float pf_f, pf_i, pf_ms, pf_b, pf_n[NNR];
+    auto prefetch_small = [&](int cc) {
+      const int64_t t0 = bh * T + static_cast<int64_t>(cc) * LC;
+      pf_f = a.f_pre[t0 + lane];
+      pf_i = a.i_pre[t0 + lane];
+      pf_ms = a.ws_m[bh * nb + cc];
+      pf_b = a.ws_beta[t0 + (rtid & (LC - 1))];
 #pragma unroll
-      for (int h8 = 0; h8 < 2; ++h8) {
-        pdh[h8] = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(a.dh) + gi + 8 * h8);
-        if (a.o_pre) {
-          ph[h8] = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(a.h) + gi + 8 * h8);
-          if (sizeof(TO) == 4) {
-            po[2 * h8] = *reinterpret_cast<const uint4*>(static_cast<const float*>(a.o_pre) + gi + 8 * h8);
-            po[2 * h8 + 1] = *reinterpret_cast<const uint4*>(static_cast<const float*>(a.o_pre) + gi + 8 * h8 + 4);
-          } else {
-            po[h8] = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(a.o_pre) + gi + 8 * h8);
+      for (int r = 0; r < NNR; ++r) {
+        const int x = rtid + r * NT4;
+        pf_n[r] = x < DK ? a.ws_n[(bh * nb + cc) * DK + x] : 0.0f;
+      }
+    };
+    prefetch_small(nc - 1);
+    load_qk(nc - 1);
+    // final-state term: <dn1, n~_T> (column block 0)
+    if (a.dC1) {
+      float part = 0.0f;
+      if (lead) {
+        for (int x = rtid; x < DK; x += NT4) part += a.dn1[bh * DK + x] * a.ws_n[(bh * nb + nc) * DK + x];
+      }
+      wg_sum(part, a.ws_kend + static_cast<int64_t>(cb) * BH + bh);   // barrier
+    }
+    for (int c = nc - 1; c >= 0; --c) {
+      const int64_t tok0 = bh * T + static_cast<int64_t>(c) * LC;
+      __syncthreads();   // (1)
+      if (wave == 0) gate_scan64_v(pf_f, pf_i, a.fgate_exp, pf_ms, G);
+#pragma unroll
+      for (int r = 0; r < NNR; ++r) {
+        const int x = rtid + r * NT4;
+        if (x < DK) sN[x] = pf_n[r];
+      }
+      if (rtid < LC) sBeta[rtid] = pf_b;
+      store_qk();
+      store_dn(c);
+      prefetch_small(c > 0 ? c - 1 : 0);   // (chunk 0 reads itself again: unused)
+      // this thread's dh, h and o~ (row rtid / 4, 16 columns) for the r step,
+      // loaded now so that their latency overlaps the score products
+      uint4 pdh[2], ph[2], po[4];
+      {
+        const int64_t gi = (tok0 + (rtid >> 2)) * dv + c0 + (rtid & 3) * 16;
+#pragma unroll
+        for (int h8 = 0; h8 < 2; ++h8) {
+          pdh[h8] = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(a.dh) + gi + 8 * h8);
+          if (a.o_pre) {
+            ph[h8] = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(a.h) + gi + 8 * h8);
+            if (sizeof(TO) == 4) {
+              po[2 * h8] = *reinterpret_cast<const uint4*>(static_cast<const float*>(a.o_pre) + gi + 8 * h8);
+              po[2 * h8 + 1] = *reinterpret_cast<const uint4*>(static_cast<const float*>(a.o_pre) + gi + 8 * h8 + 4);
+            } else {
+              po[h8] = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(a.o_pre) + gi + 8 * h8);
+            }
           }
         }
       }
-    }
-    __syncthreads();
-    // ---- the dC tile to HBM, in the same swizzled tile order as the stored
-    // states (this workgroup's 64 columns of chunk c)
-    {
-      u32x4* dst = reinterpret_cast<u32x4*>(a.ws_dCb + ((bh * ncb + cb) * nc + c) * (DK * TVC));
+      __syncthreads();   // (2)
+      // ---- S = Q K^T for query tile it = rw (all key tiles): D (.) S goes
+      // to LDS transposed ([j][i]); its row sums stay inside the wave, so the
+      // denominators and the r step below need no workgroup barrier
+      {
+        f32x4 acc[4];
 #pragma unroll
-      for (int p = 0; p < NCC; ++p)
-        dst[tid + p * NT4] = *reinterpret_cast<const u32x4*>(sCX + 16 * (tid + p * NT4));
-    }
-
-    // ---- S = Q K^T for query tile it = wave (all key tiles): D (.) S goes to
-    // LDS transposed ([j][i]); its row sums stay inside the wave, so the
-    // denominators and the r step below need no workgroup barrier
-    {
-      f32x4 acc[4];
+        for (int jt = 0; jt < 4; ++jt) acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int jt = 0; jt < 4; ++jt) acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int ks = 0; ks < DK / 32; ++ks) {
+          const int x0 = 32 * ks;
+          const bf16x8 A = rowfrag(wide(sQ, x0), rw * 16 + l16, (x0 & 63) + 8 * g);
 #pragma unroll
-      for (int ks = 0; ks < DK / 32; ++ks) {
-        const int x0 = 32 * ks;
-        const bf16x8 A = rowfrag(wide(sQ, x0), wave * 16 + l16, (x0 & 63) + 8 * g);
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt)
-          acc[jt] = mfma16x16x32(A, rowfrag(wide(sK, x0), jt * 16 + l16, (x0 & 63) + 8 * g), acc[jt]);
-      }
-      // lane: S[i = 16 wave + 4 g + e][j = 16 jt + l16]
-      float Mi[4], rs[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        Mi[e] = G.M[wave * 16 + 4 * g + e];
-        rs[e] = 0.0f;
-      }
-#pragma unroll
-      for (int jt = 0; jt < 4; ++jt) {
-        const int j = jt * 16 + l16;
-        const float uj = G.u[j];
-        float ds[4];
+          for (int jt = 0; jt < 4; ++jt)
+            acc[jt] = mfma16x16x32(A, rowfrag(wide(sK, x0), jt * 16 + l16, (x0 & 63) + 8 * g), acc[jt]);
+        }
+        // lane: S[i = 16 rw + 4 g + e][j = 16 jt + l16]
+        float Mi[4], rs[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          ds[e] = j <= wave * 16 + 4 * g + e ? __expf(uj - Mi[e]) * acc[jt][e] : 0.0f;
-          rs[e] += ds[e];
+          Mi[e] = G.M[rw * 16 + 4 * g + e];
+          rs[e] = 0.0f;
         }
-        *reinterpret_cast<uint2*>(sDST + swz(j, wave * 16 + 4 * g)) = make_uint2(pk2(ds[0], ds[1]), pk2(ds[2], ds[3]));
-      }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
+        for (int jt = 0; jt < 4; ++jt) {
+          const int j = jt * 16 + l16;
+          const float uj = G.u[j];
+          float ds[4];
 #pragma unroll
-        for (int o = 8; o > 0; o >>= 1) rs[e] += __shfl_xor(rs[e], o, 64);   // over the 16 j lanes
-      }
-      if (l16 == 0) {
+          for (int e = 0; e < 4; ++e) {
+            ds[e] = j <= rw * 16 + 4 * g + e ? __expf(uj - Mi[e]) * acc[jt][e] : 0.0f;
+            rs[e] += ds[e];
+          }
+          *reinterpret_cast<uint2*>(sDST + swz(j, rw * 16 + 4 * g)) = make_uint2(pk2(ds[0], ds[1]), pk2(ds[2], ds[3]));
+        }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sRs[wave * 16 + 4 * g + e] = rs[e];
-      }
-    }
-    // q . n~_s, the denominator and the normalizer gradient: the four threads
-    // of token i = tid / 4 (the query rows of this wave) each hold them
-    float den;
-    {
-      const int i = tid >> 2, qq = tid & 3;
-      float s = 0.0f;
+        for (int e = 0; e < 4; ++e) {
 #pragma unroll
-      for (int x8 = qq * (DK / 4); x8 < (qq + 1) * (DK / 4); x8 += 8) {
-        const uint4 v8 = lds_ld16(wide(sQ, x8), swz(i, x8 & 63));
-        s += bf_lo(v8.x) * sN[x8] + bf_hi(v8.x) * sN[x8 + 1] + bf_lo(v8.y) * sN[x8 + 2] +
-             bf_hi(v8.y) * sN[x8 + 3] + bf_lo(v8.z) * sN[x8 + 4] + bf_hi(v8.z) * sN[x8 + 5] +
-             bf_lo(v8.w) * sN[x8 + 6] + bf_hi(v8.w) * sN[x8 + 7];
+          for (int o = 8; o > 0; o >>= 1) rs[e] += __shfl_xor(rs[e], o, 64);   // over the 16 j lanes
+        }
+        if (l16 == 0) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sRs[rw * 16 + 4 * g + e] = rs[e];
+        }
       }
-      s += __shfl_xor(s, 1, 64);
-      s += __shfl_xor(s, 2, 64);
-      // the row sums of this wave's rows were written by lanes of this wave
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      const float nq = G.g[i] * s + sRs[i];
-      const float floor_ = __expf(-G.m[i]);
-      den = fmaxf(fabsf(nq), floor_);
-      const float dnq = fabsf(nq) >= floor_ ? (nq >= 0.0f ? -sBeta[i] / den : sBeta[i] / den) : 0.0f;
-      if (qq == 0 && lead) {
-        a.ws_dnq[tok0 + i] = dnq;
-        {   // the A operand of dn += sum_i g_i dnq_i q_i (hi and lo rows)
+      // q . n~_s, the denominator and the normalizer gradient: the four
+      // threads of token i = rtid / 4 (the query rows of this wave) each hold them
+      float den;
+      {
+        const int i = rtid >> 2, qq = rtid & 3;
+        float s = 0.0f;
+#pragma unroll
+        for (int x8 = qq * (DK / 4); x8 < (qq + 1) * (DK / 4); x8 += 8) {
+          const uint4 v8 = lds_ld16(wide(sQ, x8), swz(i, x8 & 63));
+          s += bf_lo(v8.x) * sN[x8] + bf_hi(v8.x) * sN[x8 + 1] + bf_lo(v8.y) * sN[x8 + 2] +
+               bf_hi(v8.y) * sN[x8 + 3] + bf_lo(v8.z) * sN[x8 + 4] + bf_hi(v8.z) * sN[x8 + 5] +
+               bf_lo(v8.w) * sN[x8 + 6] + bf_hi(v8.w) * sN[x8 + 7];
+        }
+        s += __shfl_xor(s, 1, 64);
+        s += __shfl_xor(s, 2, 64);
+        // the row sums of this wave's rows were written by lanes of this wave
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const float nq = G.g[i] * s + sRs[i];
+        const float floor_ = __expf(-G.m[i]);
+        den = fmaxf(fabsf(nq), floor_);
+        const float dnq = fabsf(nq) >= floor_ ? (nq >= 0.0f ? -sBeta[i] / den : sBeta[i] / den) : 0.0f;
+        if (qq == 0 && lead) {
+          a.ws_dnq[tok0 + i] = dnq;
+          // the A operand of dn += sum_i g_i dnq_i q_i (hi and lo rows)
           const float gd = G.g[i] * dnq;
           const bf16_t hi = f2bf(gd);
           *reinterpret_cast<bf16_t*>(sGD + swz(0, i)) = hi;
           *reinterpret_cast<bf16_t*>(sGD + swz(1, i)) = f2bf(gd - bf2f(hi));
         }
       }
-    }
-    // ---- r and g r (bf16 to LDS; r also to HBM for the dq/dk pass) and do~
-    // (16 columns per thread)
-    {
-      const int i = tid >> 2, b0 = (tid & 3) * 16;
-      const int64_t gi = (tok0 + i) * dv + c0 + b0;
-      const float inv = 1.0f / den;
-      const float gi_ = G.g[i];
-      uint32_t rp[8], gp[8];
+      // ---- r and g r (bf16 to LDS; r also to HBM for the dq/dk pass) and
+      // do~ (16 columns per thread)
+      {
+        const int i = rtid >> 2, b0 = (rtid & 3) * 16;
+        const int64_t gi = (tok0 + i) * dv + c0 + b0;
+        const float inv = 1.0f / den;
+        const float gi_ = G.g[i];
+        uint32_t rp[8], gp[8];
 #pragma unroll
-      for (int h8 = 0; h8 < 2; ++h8) {
-        const uint4 d8 = pdh[h8];
-        float dhv[8] = {bf_lo(d8.x), bf_hi(d8.x), bf_lo(d8.y), bf_hi(d8.y),
-                        bf_lo(d8.z), bf_hi(d8.z), bf_lo(d8.w), bf_hi(d8.w)};
-        float gate[8];
-        if (a.o_pre) {
-          const uint4 h8v = ph[h8];
-          const float hv[8] = {bf_lo(h8v.x), bf_hi(h8v.x), bf_lo(h8v.y), bf_hi(h8v.y),
-                               bf_lo(h8v.z), bf_hi(h8v.z), bf_lo(h8v.w), bf_hi(h8v.w)};
-          float ov[8];
-          if (sizeof(TO) == 4) {
-            const uint4 o0 = po[2 * h8], o1 = po[2 * h8 + 1];
-            ov[0] = __uint_as_float(o0.x); ov[1] = __uint_as_float(o0.y);
-            ov[2] = __uint_as_float(o0.z); ov[3] = __uint_as_float(o0.w);
-            ov[4] = __uint_as_float(o1.x); ov[5] = __uint_as_float(o1.y);
-            ov[6] = __uint_as_float(o1.z); ov[7] = __uint_as_float(o1.w);
+        for (int h8 = 0; h8 < 2; ++h8) {
+          const uint4 d8 = pdh[h8];
+          float dhv[8] = {bf_lo(d8.x), bf_hi(d8.x), bf_lo(d8.y), bf_hi(d8.y),
+                          bf_lo(d8.z), bf_hi(d8.z), bf_lo(d8.w), bf_hi(d8.w)};
+          float gate[8];
+          if (a.o_pre) {
+            const uint4 h8v = ph[h8];
+            const float hv[8] = {bf_lo(h8v.x), bf_hi(h8v.x), bf_lo(h8v.y), bf_hi(h8v.y),
+                                 bf_lo(h8v.z), bf_hi(h8v.z), bf_lo(h8v.w), bf_hi(h8v.w)};
+            float ov[8];
+            if (sizeof(TO) == 4) {
+              const uint4 o0 = po[2 * h8], o1 = po[2 * h8 + 1];
+              ov[0] = __uint_as_float(o0.x); ov[1] = __uint_as_float(o0.y);
+              ov[2] = __uint_as_float(o0.z); ov[3] = __uint_as_float(o0.w);
+              ov[4] = __uint_as_float(o1.x); ov[5] = __uint_as_float(o1.y);
+              ov[6] = __uint_as_float(o1.z); ov[7] = __uint_as_float(o1.w);
+            } else {
+              const uint4 o8 = po[h8];
+              ov[0] = bf_lo(o8.x); ov[1] = bf_hi(o8.x); ov[2] = bf_lo(o8.y); ov[3] = bf_hi(o8.y);
+              ov[4] = bf_lo(o8.z); ov[5] = bf_hi(o8.z); ov[6] = bf_lo(o8.w); ov[7] = bf_hi(o8.w);
+            }
+            float dov[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              gate[e] = sigmoid_fast(ov[e]);
+              dov[e] = dhv[e] * hv[e] * (1.0f - gate[e]);
+            }
+            float* dO = a.d_o + gi + 8 * h8;
+            *reinterpret_cast<float4*>(dO) = make_float4(dov[0], dov[1], dov[2], dov[3]);
+            *reinterpret_cast<float4*>(dO + 4) = make_float4(dov[4], dov[5], dov[6], dov[7]);
           } else {
-            const uint4 o8 = po[h8];
-            ov[0] = bf_lo(o8.x); ov[1] = bf_hi(o8.x); ov[2] = bf_lo(o8.y); ov[3] = bf_hi(o8.y);
-            ov[4] = bf_lo(o8.z); ov[5] = bf_hi(o8.z); ov[6] = bf_lo(o8.w); ov[7] = bf_hi(o8.w);
-          }
-          float dov[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            gate[e] = sigmoid_fast(ov[e]);
-            dov[e] = dhv[e] * hv[e] * (1.0f - gate[e]);
+            for (int e = 0; e < 8; ++e) gate[e] = 1.0f;
           }
-          float* dO = a.d_o + gi + 8 * h8;
-          *reinterpret_cast<float4*>(dO) = make_float4(dov[0], dov[1], dov[2], dov[3]);
-          *reinterpret_cast<float4*>(dO + 4) = make_float4(dov[4], dov[5], dov[6], dov[7]);
-        } else {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) gate[e] = 1.0f;
+          for (int e = 0; e < 8; e += 2) {
+            const float r0 = gate[e] * dhv[e] * inv, r1 = gate[e + 1] * dhv[e + 1] * inv;
+            rp[4 * h8 + e / 2] = pk2(r0, r1);
+            gp[4 * h8 + e / 2] = pk2(gi_ * r0, gi_ * r1);
+          }
         }
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const float r0 = gate[e] * dhv[e] * inv, r1 = gate[e + 1] * dhv[e + 1] * inv;
-          rp[4 * h8 + e / 2] = pk2(r0, r1);
-          gp[4 * h8 + e / 2] = pk2(gi_ * r0, gi_ * r1);
+        for (int h8 = 0; h8 < 2; ++h8) {
+          const u32x4 r4 = {rp[4 * h8], rp[4 * h8 + 1], rp[4 * h8 + 2], rp[4 * h8 + 3]};
+          *reinterpret_cast<u32x4*>(sR + swz(i, b0 + 8 * h8)) = r4;
+          *reinterpret_cast<u32x4*>(a.ws_R + gi + 8 * h8) = r4;
+          *reinterpret_cast<uint4*>(sGR + swz(i, b0 + 8 * h8)) = make_uint4(gp[4 * h8], gp[4 * h8 + 1], gp[4 * h8 + 2], gp[4 * h8 + 3]);
         }
       }
-#pragma unroll
-      for (int h8 = 0; h8 < 2; ++h8) {
-        const u32x4 r4 = {rp[4 * h8], rp[4 * h8 + 1], rp[4 * h8 + 2], rp[4 * h8 + 3]};
-        *reinterpret_cast<u32x4*>(sR + swz(i, b0 + 8 * h8)) = r4;
-        *reinterpret_cast<u32x4*>(a.ws_R + gi + 8 * h8) = r4;
-        *reinterpret_cast<uint4*>(sGR + swz(i, b0 + 8 * h8)) = make_uint4(gp[4 * h8], gp[4 * h8 + 1], gp[4 * h8 + 2], gp[4 * h8 + 3]);
-      }
+      __syncthreads();   // (3)
+      load_qk(c > 0 ? c - 1 : 0);   // (chunk 0 fetches itself again: in bounds, unused)
     }
     __syncthreads();
-    // ---- dv^T = R^T DS + w (dC^T K^T) for value tile bt = wave
-    {
-      f32x4 accA[4], accB[4];
-#pragma unroll
-      for (int jt = 0; jt < 4; ++jt) {
-        accA[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        accB[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 Ar = colfrag(sR, 32 * ks, wave * 16, g, kr, kq);
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt)
-          accA[jt] = mfma16x16x32(Ar, rowfrag(sDST, jt * 16 + l16, 32 * ks + 8 * g), accA[jt]);
-      }
-      // dC^T K^T: this wave's 16 value columns of the carried dC (float32, in
-      // its own registers) enter as a bf16 (hi, lo) pair, transposed 32 rows
-      // at a time through a wave-private LDS tile.  A single bf16 copy of dC
-      // costs up to ~2% of dv where the two terms of dv cancel.
-      char* tw = sTW + wave * 2048;
-#pragma unroll
-      for (int ks = 0; ks < DK / 32; ++ks) {
-        const int x0 = 32 * ks;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {   // lane: dC^T[b = 4 g + e][x = x0 + 16 t + l16]
-          const f32x4 v = dCt[2 * ks + t];
-          const uint32_t h0 = pk2(v[0], v[1]), h1 = pk2(v[2], v[3]);
-          const int off = (16 * t + l16) * 32 + g * 8;   // row x (32 bytes), columns b = 4 g ..
-          *reinterpret_cast<uint2*>(tw + off) = make_uint2(h0, h1);
-          *reinterpret_cast<uint2*>(tw + 1024 + off) =
-              make_uint2(pk2(v[0] - bf_lo(h0), v[1] - bf_hi(h0)), pk2(v[2] - bf_lo(h1), v[3] - bf_hi(h1)));
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // A[b = l16][x = 8 g + e]: transposed reads of rows 8 g + kr (+4), columns 4 kq
-        const int ro = (8 * g + kr) * 32 + 8 * kq;
-        const bf16x8 Ah = join(lds_tr(tw, ro), lds_tr(tw, ro + 4 * 32));
-        const bf16x8 Al = join(lds_tr(tw + 1024, ro), lds_tr(tw + 1024, ro + 4 * 32));
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
-          const bf16x8 Bk = rowfrag(wide(sK, x0), jt * 16 + l16, (x0 & 63) + 8 * g);
-          accB[jt] = mfma16x16x32(Ah, Bk, accB[jt]);
-          accB[jt] = mfma16x16x32(Al, Bk, accB[jt]);
-        }
-        // the next rows overwrite the tile only after these reads
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      }
-#pragma unroll
-      for (int jt = 0; jt < 4; ++jt) {
-        const int j = jt * 16 + l16;
-        const float wj = G.w[j];
-        *reinterpret_cast<float4*>(a.d_v + (tok0 + j) * dv + c0 + wave * 16 + 4 * g) =
-            make_float4(accA[jt][0] + wj * accB[jt][0], accA[jt][1] + wj * accB[jt][1],
-                        accA[jt][2] + wj * accB[jt][2], accA[jt][3] + wj * accB[jt][3]);
+    float part = 0.0f;
+    if (lead) {
+      for (int x = rtid; x < DK; x += NT4) {
+        if (a.dn0) a.dn0[bh * DK + x] = sDn[x];
+        if (a.C0) part += sDn[x] * a.n0[bh * DK + x];
       }
     }
-    // ---- dC^T <- g_L dC^T + (g R)^T Q; in column block 0 also the
-    // normalizer's sum_i g_i dnq_i q_i for this wave's x tiles (rows 0 + 1)
-    f32x4 dnacc[XPW];
-    {
+    wg_sum(part, a.ws_dm0 + static_cast<int64_t>(cb) * BH + bh);   // barrier
+  } else {
+    // ================= memory waves
+    // carried dC^T: tile xt holds dC^T[b = 16 rw + 4 g + e][x = 16 xt + l16]
+    f32x4 dCt[NXT];
+#pragma unroll
+    for (int xt = 0; xt < NXT; ++xt) {
+      dCt[xt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (a.dC1) {
+        const float4 v4 = *reinterpret_cast<const float4*>(
+            a.dC1 + (bh * DK + xt * 16 + l16) * dv + c0 + rw * 16 + 4 * g);
+        dCt[xt] = f32x4{v4.x, v4.y, v4.z, v4.w};
+      }
+    }
+    // final-state term: <dC1, C~_T> over this workgroup's columns
+    if (a.dC1) {
+      float part = 0.0f;
+#pragma unroll
+      for (int xt = 0; xt < NXT; ++xt) {
+        const float4 c4 = *reinterpret_cast<const float4*>(
+            a.ws_CT + (bh * DK + xt * 16 + l16) * dv + c0 + rw * 16 + 4 * g);
+        part += (dCt[xt][0] * c4.x + dCt[xt][1] * c4.y) + (dCt[xt][2] * c4.z + dCt[xt][3] * c4.w);
+      }
+      wg_sum(part, nullptr);   // barrier (the score waves' thread 0 writes the sum)
+    }
+    char* tw = sCX + rw * (KH * 2048);
+    for (int c = nc - 1; c >= 0; --c) {
+      const int64_t tok0 = bh * T + static_cast<int64_t>(c) * LC;
+      __syncthreads();   // (1)
+      // dC at this chunk's end (bf16, [x][b]) for its copy to HBM
+#pragma unroll
+      for (int xt = 0; xt < NXT; ++xt)
+        *reinterpret_cast<uint2*>(sCX + swz(xt * 16 + l16, rw * 16 + 4 * g)) =
+            make_uint2(pk2(dCt[xt][0], dCt[xt][1]), pk2(dCt[xt][2], dCt[xt][3]));
+      store_dn(c);
+      __syncthreads();   // (2)
+      // ---- this wave's rows of the dC tile to HBM, in the stored states'
+      // tile order
+      {
+        u32x4* dst = reinterpret_cast<u32x4*>(a.ws_dCb + ((bh * ncb + cb) * nc + c) * (DK * TVC) + rw * (KH * 1024));
+#pragma unroll
+        for (int p = 0; p < KH * 2; ++p)
+          dst[lane + 64 * p] = *reinterpret_cast<const u32x4*>(tw + 16 * (lane + 64 * p));
+      }
+      // ---- dC^T K^T for value tile rw: this wave's 16 value columns of the
+      // carried dC (float32) enter as a bf16 (hi, lo) pair, transposed
+      // through its rows of sCX half of d_qk at a time (a wave-level sync
+      // before each half's writes, after the copy above or the first half's
+      // reads, and between writes and reads).  A single bf16 copy of dC costs
+      // up to ~2% of dv where the two terms of dv cancel.
+      f32x4 accB[4];
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) accB[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int kh = 0; kh < KH; ++kh) {
+          const int ks = hf * KH + kh;
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {   // lane: dC^T[b = 4 g + e][x = 32 ks + 16 t + l16]
+            const f32x4 v = dCt[2 * ks + t];
+            const uint32_t h0 = pk2(v[0], v[1]), h1 = pk2(v[2], v[3]);
+            const int off = kh * 2048 + (16 * t + l16) * 32 + g * 8;   // row x (32 bytes), columns b = 4 g ..
+            *reinterpret_cast<uint2*>(tw + off) = make_uint2(h0, h1);
+            *reinterpret_cast<uint2*>(tw + 1024 + off) =
+                make_uint2(pk2(v[0] - bf_lo(h0), v[1] - bf_hi(h0)), pk2(v[2] - bf_lo(h1), v[3] - bf_hi(h1)));
+          }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int kh = 0; kh < KH; ++kh) {
+          const int x0 = 32 * (hf * KH + kh);
+          // A[b = l16][x = 8 g + e]: transposed reads of rows 8 g + kr (+4), columns 4 kq
+          const int ro = kh * 2048 + (8 * g + kr) * 32 + 8 * kq;
+          const bf16x8 Ah = join(lds_tr(tw, ro), lds_tr(tw, ro + 4 * 32));
+          const bf16x8 Al = join(lds_tr(tw + 1024, ro), lds_tr(tw + 1024, ro + 4 * 32));
+#pragma unroll
+          for (int jt = 0; jt < 4; ++jt) {
+            const bf16x8 Bk = rowfrag(wide(sK, x0), jt * 16 + l16, (x0 & 63) + 8 * g);
+            accB[jt] = mfma16x16x32(Ah, Bk, accB[jt]);
+            accB[jt] = mfma16x16x32(Al, Bk, accB[jt]);
+          }
+        }
+      }
+      __syncthreads();   // (3)
+      // ---- dv^T = R^T DS + w (dC^T K^T) for value tile rw
+      {
+        f32x4 accA[4];
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) accA[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const bf16x8 Ar = colfrag(sR, 32 * ks, rw * 16, g, kr, kq);
+#pragma unroll
+          for (int jt = 0; jt < 4; ++jt)
+            accA[jt] = mfma16x16x32(Ar, rowfrag(sDST, jt * 16 + l16, 32 * ks + 8 * g), accA[jt]);
+        }
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+          const int j = jt * 16 + l16;
+          const float wj = G.w[j];
+          *reinterpret_cast<float4*>(a.d_v + (tok0 + j) * dv + c0 + rw * 16 + 4 * g) =
+              make_float4(accA[jt][0] + wj * accB[jt][0], accA[jt][1] + wj * accB[jt][1],
+                          accA[jt][2] + wj * accB[jt][2], accA[jt][3] + wj * accB[jt][3]);
+        }
+      }
+      // ---- dC^T <- g_L dC^T + (g R)^T Q; in column block 0 also the
+      // normalizer's sum_i g_i dnq_i q_i for this wave's x tiles (rows 0 + 1)
+      f32x4 dnacc[XPW];
       const float gL = G.g[LC - 1];
 #pragma unroll
       for (int xt = 0; xt < NXT; ++xt) dCt[xt] *= gL;
@@ -514,7 +547,7 @@ __global__ __launch_bounds__(NT4, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
       for (int p = 0; p < XPW; ++p) dnacc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 Ag = colfrag(sGR, 32 * ks, wave * 16, g, kr, kq);
+        const bf16x8 Ag = colfrag(sGR, 32 * ks, rw * 16, g, kr, kq);
 #pragma unroll
         for (int xt = 0; xt < NXT; ++xt)
           dCt[xt] = mfma16x16x32(Ag, colfrag(wide(sQ, xt * 16), 32 * ks, (xt * 16) & 63, g, kr, kq), dCt[xt]);
@@ -522,46 +555,35 @@ __global__ __launch_bounds__(NT4, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
           const bf16x8 Ad = rowfrag(sGD, l16, 32 * ks + 8 * g);
 #pragma unroll
           for (int p = 0; p < XPW; ++p) {
-            const int xt = wave * XPW + p;
+            const int xt = rw * XPW + p;
             dnacc[p] = mfma16x16x32(Ad, colfrag(wide(sQ, xt * 16), 32 * ks, (xt * 16) & 63, g, kr, kq), dnacc[p]);
           }
         }
       }
-    }
-    // ---- dn <- g_L dn + sum_i g_i dnq_i q_i (column block 0 only; sDn was
-    // last read at this chunk's top, before the second barrier)
-    if (lead && g == 0) {
-      const float gL = G.g[LC - 1];
+      // ---- dn <- g_L dn + sum_i g_i dnq_i q_i (column block 0 only; sDn was
+      // last read at this chunk's top, before the second barrier)
+      if (lead && g == 0) {
 #pragma unroll
-      for (int p = 0; p < XPW; ++p) {
-        const int x = (wave * XPW + p) * 16 + l16;
-        sDn[x] = gL * sDn[x] + (dnacc[p][0] + dnacc[p][1]);
+        for (int p = 0; p < XPW; ++p) {
+          const int x = (rw * XPW + p) * 16 + l16;
+          sDn[x] = gL * sDn[x] + (dnacc[p][0] + dnacc[p][1]);
+        }
       }
     }
-  }
-  // ---- the initial state's gradients and dm0's share
-  __syncthreads();
-  float part = 0.0f;
+    // ---- the initial state's gradients and dm0's share
+    __syncthreads();
+    float part = 0.0f;
 #pragma unroll
-  for (int xt = 0; xt < NXT; ++xt) {
-    const int64_t gi = (bh * DK + xt * 16 + l16) * dv + c0 + wave * 16 + 4 * g;
-    if (a.dC0) *reinterpret_cast<float4*>(a.dC0 + gi) = make_float4(dCt[xt][0], dCt[xt][1], dCt[xt][2], dCt[xt][3]);
-    if (a.C0) {
-      const float4 c4 = *reinterpret_cast<const float4*>(a.C0 + gi);
-      part += (dCt[xt][0] * c4.x + dCt[xt][1] * c4.y) + (dCt[xt][2] * c4.z + dCt[xt][3] * c4.w);
+    for (int xt = 0; xt < NXT; ++xt) {
+      const int64_t gi = (bh * DK + xt * 16 + l16) * dv + c0 + rw * 16 + 4 * g;
+      if (a.dC0) *reinterpret_cast<float4*>(a.dC0 + gi) = make_float4(dCt[xt][0], dCt[xt][1], dCt[xt][2], dCt[xt][3]);
+      if (a.C0) {
+        const float4 c4 = *reinterpret_cast<const float4*>(a.C0 + gi);
+        part += (dCt[xt][0] * c4.x + dCt[xt][1] * c4.y) + (dCt[xt][2] * c4.z + dCt[xt][3] * c4.w);
+      }
     }
+    wg_sum(part, nullptr);   // barrier (the score waves' thread 0 writes the sum)
   }
-  if (lead) {
-    for (int x = tid; x < DK; x += NT4) {
-      if (a.dn0) a.dn0[bh * DK + x] = sDn[x];
-      if (a.C0) part += sDn[x] * a.n0[bh * DK + x];
-    }
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
-  if (lane == 0) sRed[wave] = part;
-  __syncthreads();
-  if (tid == 0) a.ws_dm0[static_cast<int64_t>(cb) * BH + bh] = (sRed[0] + sRed[1]) + (sRed[2] + sRed[3]);
 }
 
 // Direct global -> LDS load of one chunk's k ([64][DK] bf16) into swizzled
@@ -599,8 +621,6 @@ __device__ __forceinline__ void dma_k_chunk8(const BwdArgs& a, int64_t tok0, int
                    static_cast<int>(lds_addr(dst + qt * TB + rg * 1024)))));
   }
 }
-
-constexpr int NT8 = 512;           // 8 waves
 
 // Chunk-boundary states for the reverse pass: (C~, n~, m) before every chunk
 // and after the last, C~_{c+1} = g_L C~_c + K^T (w (.) V) and
@@ -1149,8 +1169,8 @@ hipError_t launch_states_dk(const BwdArgs& a, hipStream_t st) {
 template <int DK>
 hipError_t launch_dk(const BwdArgs& a, hipStream_t st) {
   const unsigned wgs = static_cast<unsigned>(a.B * a.H * (a.dv / TVC));
-  if (a.o_mode == O_BF16) bwd_rev_mfma_kernel<DK, bf16_t><<<wgs, NT4, 0, st>>>(a);
-  else bwd_rev_mfma_kernel<DK, float><<<wgs, NT4, 0, st>>>(a);
+  if (a.o_mode == O_BF16) bwd_rev_mfma_kernel<DK, bf16_t><<<wgs, NT8, 0, st>>>(a);
+  else bwd_rev_mfma_kernel<DK, float><<<wgs, NT8, 0, st>>>(a);
   return hipGetLastError();
 }
 
