@@ -121,10 +121,10 @@ constexpr int NT8 = 512;           // 8 waves
 // form everything of a chunk that does not depend on the carried dC: S, the
 // denominators and dnq, r, g r and do~.  Waves 4-7 ("memory" waves, 16 value
 // columns each) own dC^T in float32 registers; while the score waves work
-// they store dC at the chunk's end to HBM and form dC^T K^T, and after the
-// chunk's third barrier they finish dv (adding R^T DS) and update dC and dn.
-// Each SIMD runs one wave of each role, and the dC-only work of a chunk
-// overlaps its score work.  The roles run separate loops with the same
+// they store dC at the chunk's end to HBM and form w (.) (dC^T K^T) (into
+// LDS); after the chunk's third barrier they update dC and dn while the score
+// waves finish dv = R^T DS + w (.) (dC^T K^T).  Each SIMD runs one wave of
+// each role, and the dC-only work of a chunk overlaps its score work.  The roles run separate loops with the same
 // barrier sequence (one before the loop when dC1 is given, three per chunk,
 // two after it), so that the registers of one role's values are free in the
 // other's code.
@@ -146,6 +146,7 @@ __global__ __launch_bounds__(NT8, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
   // barrier is private to one wave.
   __shared__ __align__(1024) char sCX[DK * 128];
   __shared__ __align__(1024) char sGD[16 * 128];   // rows 0, 1: g (.) dnq as bf16 hi / lo; rest 0
+  __shared__ __align__(16) float sDVM[LC][TVC + 4];  // w (.) (dC^T K^T) as [token j][value column b]
   __shared__ float sN[DK], sDn[DK];
   __shared__ float sRs[LC];
   __shared__ float sBeta[LC];
@@ -417,6 +418,27 @@ __global__ __launch_bounds__(NT8, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
       }
       __syncthreads();   // (3)
       load_qk(c > 0 ? c - 1 : 0);   // (chunk 0 fetches itself again: in bounds, unused)
+      // ---- dv^T = R^T DS + w (dC^T K^T) for value tile rw (the memory
+      // waves' term from LDS)
+      {
+        f32x4 accA[4];
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) accA[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const bf16x8 Ar = colfrag(sR, 32 * ks, rw * 16, g, kr, kq);
+#pragma unroll
+          for (int jt = 0; jt < 4; ++jt)
+            accA[jt] = mfma16x16x32(Ar, rowfrag(sDST, jt * 16 + l16, 32 * ks + 8 * g), accA[jt]);
+        }
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+          const int j = jt * 16 + l16;
+          const float4 m4 = *reinterpret_cast<const float4*>(&sDVM[j][rw * 16 + 4 * g]);
+          *reinterpret_cast<float4*>(a.d_v + (tok0 + j) * dv + c0 + rw * 16 + 4 * g) =
+              make_float4(accA[jt][0] + m4.x, accA[jt][1] + m4.y, accA[jt][2] + m4.z, accA[jt][3] + m4.w);
+        }
+      }
     }
     __syncthreads();
     float part = 0.0f;
@@ -515,28 +537,15 @@ __global__ __launch_bounds__(NT8, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
           }
         }
       }
-      __syncthreads();   // (3)
-      // ---- dv^T = R^T DS + w (dC^T K^T) for value tile rw
-      {
-        f32x4 accA[4];
+      // lane: (dC^T K^T)^T[j = 16 jt + l16][b = 16 rw + 4 g + e], scaled by w_j
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) accA[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const bf16x8 Ar = colfrag(sR, 32 * ks, rw * 16, g, kr, kq);
-#pragma unroll
-          for (int jt = 0; jt < 4; ++jt)
-            accA[jt] = mfma16x16x32(Ar, rowfrag(sDST, jt * 16 + l16, 32 * ks + 8 * g), accA[jt]);
-        }
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
-          const int j = jt * 16 + l16;
-          const float wj = G.w[j];
-          *reinterpret_cast<float4*>(a.d_v + (tok0 + j) * dv + c0 + rw * 16 + 4 * g) =
-              make_float4(accA[jt][0] + wj * accB[jt][0], accA[jt][1] + wj * accB[jt][1],
-                          accA[jt][2] + wj * accB[jt][2], accA[jt][3] + wj * accB[jt][3]);
-        }
+      for (int jt = 0; jt < 4; ++jt) {
+        const int j = jt * 16 + l16;
+        const float wj = G.w[j];
+        *reinterpret_cast<float4*>(&sDVM[j][rw * 16 + 4 * g]) =
+            make_float4(wj * accB[jt][0], wj * accB[jt][1], wj * accB[jt][2], wj * accB[jt][3]);
       }
+      __syncthreads();   // (3)
       // ---- dC^T <- g_L dC^T + (g R)^T Q; in column block 0 also the
       // normalizer's sum_i g_i dnq_i q_i for this wave's x tiles (rows 0 + 1)
       f32x4 dnacc[XPW];
