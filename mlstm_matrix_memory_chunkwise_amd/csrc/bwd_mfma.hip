@@ -332,9 +332,12 @@ __global__ __launch_bounds__(NT8, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
       {
         const int i = rtid >> 2, qq = rtid & 3;
         float s = 0.0f;
+        // thread qq takes the 16-byte chunks 4 it + qq of row i: the four
+        // threads of a token read four chunks of one tile row at a time
 #pragma unroll
-        for (int x8 = qq * (DK / 4); x8 < (qq + 1) * (DK / 4); x8 += 8) {
-          const uint4 v8 = lds_ld16(wide(sQ, x8), swz(i, x8 & 63));
+        for (int it = 0; it < DK / 32; ++it) {
+          const int x8 = 32 * it + 8 * qq;
+          const uint4 v8 = lds_ld16(wide(sQ, 32 * it), swz(i, x8 & 63));
           s += bf_lo(v8.x) * sN[x8] + bf_hi(v8.x) * sN[x8 + 1] + bf_lo(v8.y) * sN[x8 + 2] +
                bf_hi(v8.y) * sN[x8 + 3] + bf_lo(v8.z) * sN[x8 + 4] + bf_hi(v8.z) * sN[x8 + 5] +
                bf_lo(v8.w) * sN[x8 + 6] + bf_hi(v8.w) * sN[x8 + 7];
@@ -474,6 +477,10 @@ __global__ __launch_bounds__(NT8, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
       wg_sum(part, nullptr);   // barrier (the score waves' thread 0 writes the sum)
     }
     char* tw = sCX + rw * (KH * 2048);
+    // row x of a transposition tile sits at row x ^ 4 when x / 8 is odd: a
+    // transposed read takes rows 8 g + 0..3 (or 4..7) in lane group g, and
+    // this puts groups g and g + 1 on different halves of the banks
+    auto trow = [](int x) { return x ^ (((x >> 3) & 1) << 2); };
     for (int c = nc - 1; c >= 0; --c) {
       const int64_t tok0 = bh * T + static_cast<int64_t>(c) * LC;
       __syncthreads();   // (1)
@@ -513,7 +520,7 @@ __global__ __launch_bounds__(NT8, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
           for (int t = 0; t < 2; ++t) {   // lane: dC^T[b = 4 g + e][x = 32 ks + 16 t + l16]
             const f32x4 v = dCt[2 * ks + t];
             const uint32_t h0 = pk2(v[0], v[1]), h1 = pk2(v[2], v[3]);
-            const int off = kh * 2048 + (16 * t + l16) * 32 + g * 8;   // row x (32 bytes), columns b = 4 g ..
+            const int off = kh * 2048 + trow(16 * t + l16) * 32 + g * 8;   // row x (32 bytes), columns b = 4 g ..
             *reinterpret_cast<uint2*>(tw + off) = make_uint2(h0, h1);
             *reinterpret_cast<uint2*>(tw + 1024 + off) =
                 make_uint2(pk2(v[0] - bf_lo(h0), v[1] - bf_hi(h0)), pk2(v[2] - bf_lo(h1), v[3] - bf_hi(h1)));
@@ -526,9 +533,10 @@ __global__ __launch_bounds__(NT8, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
         for (int kh = 0; kh < KH; ++kh) {
           const int x0 = 32 * (hf * KH + kh);
           // A[b = l16][x = 8 g + e]: transposed reads of rows 8 g + kr (+4), columns 4 kq
-          const int ro = kh * 2048 + (8 * g + kr) * 32 + 8 * kq;
-          const bf16x8 Ah = join(lds_tr(tw, ro), lds_tr(tw, ro + 4 * 32));
-          const bf16x8 Al = join(lds_tr(tw + 1024, ro), lds_tr(tw + 1024, ro + 4 * 32));
+          const int r0 = kh * 2048 + trow(8 * g + kr) * 32 + 8 * kq;
+          const int r1 = kh * 2048 + trow(8 * g + 4 + kr) * 32 + 8 * kq;
+          const bf16x8 Ah = join(lds_tr(tw, r0), lds_tr(tw, r1));
+          const bf16x8 Al = join(lds_tr(tw + 1024, r0), lds_tr(tw + 1024, r1));
 #pragma unroll
           for (int jt = 0; jt < 4; ++jt) {
             const bf16x8 Bk = rowfrag(wide(sK, x0), jt * 16 + l16, (x0 & 63) + 8 * g);
