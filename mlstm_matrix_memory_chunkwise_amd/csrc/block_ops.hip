@@ -15,7 +15,7 @@
 //  * Causal depthwise convolution over the token axis, x [B, T, C]:
 //    y[t, c] = bias[c] + sum_{s<K} w[c, s] x[t - K + 1 + s, c], with an
 //    optional carried window of the K - 1 inputs before t = 0.  One thread per
-//    (b, 8 or 4 channels, run of 32 tokens) slides the window along its run
+//    (b, 8 or 4 channels, run of 128 tokens) slides the window along its run
 //    in registers, loading the next 4 tokens while it computes the current
 //    4 (software pipeline); a wave covers 64
 //    neighbouring channel groups, so every token row is read as contiguous
@@ -270,7 +270,7 @@ hipError_t launch_gn(const GnArgs& a, hipStream_t st) {
 // ---------------------------------------------------------------- causal conv
 
 constexpr int CONV_THREADS = 256;
-constexpr int CONV_RUN = 32;      // tokens per thread
+constexpr int CONV_RUN = 128;     // tokens per thread (longer runs: fewer window and weight loads)
 
 // VE channels per thread (8 for bf16, 4 for float32), kernel size K.
 template <int VE, int K>
