@@ -205,12 +205,15 @@ mlstm_status_t mlstm_step(const mlstm_problem_t* p, const void* q,
  *   derivative through the factor e^{m0} (zero without an initial state).
  *   Outputs must not overlap inputs or each other.
  *   workspace: device scratch of at least
- *   mlstm_bwd_chunkwise_workspace_bytes (it holds the state at every chunk
- *   boundary and per-column-block partial sums: about
+ *   mlstm_bwd_chunkwise_workspace_bytes, 16-byte aligned, not overlapping
+ *   any argument.  At chunk 16/32 it holds the state at every chunk boundary
+ *   and per-column-block partial sums of dq and dk: about
  *   B*H*(T/chunk+1)*d_qk*d_v*4 + 2*(d_v/w)*B*H*T*d_qk*4 bytes with w = 32
- *   or 16; at chunk 64 the states before each chunk are bf16, about
- *   B*H*(T/64)*d_qk*d_v*2 + B*H*d_qk*d_v*4 + 2*(d_v/64)*B*H*T*d_qk*4
- *   bytes), 16-byte aligned, not overlapping any argument.
+ *   or 16.  At chunk 64 it holds the state before each chunk and the memory
+ *   gradient at each chunk's end as bf16, the final state in float32, and
+ *   r = sigmoid(o~) dh / den as bf16: about 2*B*H*(T/64)*d_qk*d_v*2 +
+ *   B*H*d_qk*d_v*4 + B*H*T*d_v*2 bytes, plus per-token and per-chunk arrays
+ *   of O(B*H*T) floats.
  *   q, k, v, h, dh, dq and dk must be 16-byte aligned; at chunk 64 also
  *   o_pre, C0, dC1, dv, d_o and dC0; every other pointer 4-byte aligned.
  * Supported: chunk 16 or 32 with d_qk <= 256 (float32 arithmetic
