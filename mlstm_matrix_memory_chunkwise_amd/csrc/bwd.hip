@@ -36,6 +36,8 @@
 //   5. per head: the reverse prefix sum that gives df~, and dm0.
 // All arithmetic is float32 on the vector ALUs; this is the first, simple
 // form of the backward pass.
+#include <mutex>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mfma_util.hpp"
@@ -547,14 +549,68 @@ hipError_t launch_typed(const BwdArgs& a, hipStream_t st) {
 }
 
 // Chunk 64 (bf16 q, k, v): the state, reverse and dq/dk passes on MFMA and
-// the per-chunk gate pass (bwd_mfma.hip).
+// the per-chunk gate pass (bwd_mfma.hip).  beta (a bandwidth-bound pass over
+// dh and h) is needed first by the reverse pass, not by the state pass, which
+// is latency-bound and leaves room on every CU: beta runs on a side stream of
+// the library's own, forked from the caller's stream after everything already
+// queued there and joined back before the reverse pass (two events; the same
+// fork and join when the caller's stream is being captured into a graph).
+constexpr int kSideDevices = 64;
+struct SideStream {
+  hipStream_t st = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;   // one fork / join sequence at a time per process
+SideStream g_side[kSideDevices];
+
+hipError_t side_stream(hipStream_t st, SideStream** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (st) {
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice(st, &sdev);
+    if (e != hipSuccess) return e;
+    dev = sdev;
+  }
+  if (dev < 0 || dev >= kSideDevices) return hipErrorInvalidDevice;
+  SideStream& s = g_side[dev];
+  if (!s.st) {
+    int cur = -1;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    hipStream_t ns = nullptr;
+    hipEvent_t ef = nullptr, ej = nullptr;
+    e = hipStreamCreateWithFlags(&ns, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ef, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ej, hipEventDisableTiming);
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess) return e;
+    s.st = ns;
+    s.fork = ef;
+    s.join = ej;
+  }
+  *out = &s;
+  return hipSuccess;
+}
+
 template <typename T>
 hipError_t launch_mfma(const BwdArgs& a, hipStream_t st) {
   const int64_t ntok = a.B * a.H * a.T;
   const unsigned tok_blocks = static_cast<unsigned>((ntok + NTB / 64 - 1) / (NTB / 64));
-  bwd_beta_kernel<T><<<(tok_blocks + 1) / 2, NTB, 0, st>>>(a);
-  hipError_t e = launch_bwd_states_mfma(a, st);
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  SideStream* side = nullptr;
+  hipError_t e = side_stream(st, &side);
   if (e != hipSuccess) return e;
+  if ((e = hipEventRecord(side->fork, st)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(side->st, side->fork, 0)) != hipSuccess) return e;
+  bwd_beta_kernel<T><<<(tok_blocks + 1) / 2, NTB, 0, side->st>>>(a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = hipEventRecord(side->join, side->st)) != hipSuccess) return e;
+  e = launch_bwd_states_mfma(a, st);
+  if (e != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(st, side->join, 0)) != hipSuccess) return e;
   e = launch_bwd_rev_mfma(a, st);
   if (e != hipSuccess) return e;
   e = launch_bwd_qk_mfma(a, st);

@@ -454,6 +454,9 @@ __global__ __launch_bounds__(NT8, 1) void bwd_rev_mfma_kernel(BwdArgs a) {
     wg_sum(part, a.ws_dm0 + static_cast<int64_t>(cb) * BH + bh);   // barrier
   } else {
     // ================= memory waves
+    // (their dC chain is the sequential critical path: issue ahead of the
+    // score wave on the same SIMD; measured 0.5% faster per pass)
+    __builtin_amdgcn_s_setprio(2);
     // carried dC^T: tile xt holds dC^T[b = 16 rw + 4 g + e][x = 16 xt + l16]
     f32x4 dCt[NXT];
 #pragma unroll
