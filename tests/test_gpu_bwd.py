@@ -231,3 +231,38 @@ def test_bwd_d256_T8192_sampled_heads(d256_case, chunk):
     g = run_gpu(inp, gin, chunk, "sigmoid", torch.float32, h)
     compare(g, r, TOL_BF16, f"d256 T8192 sampled chunk {chunk}", True, heads=heads, C0=inp["C0"],
             n0=inp["n0"])
+
+
+def test_bwd_graph_capture_replays():
+    """The chunk-64 backward captured into a HIP graph (its beta pass forks
+    onto the library's side stream and joins back inside the capture): three
+    replays, with eager work and a synchronization between them, each equal
+    bit for bit to the eager call (the passes are deterministic)."""
+    M = _M()
+    inp, gin = make_inputs(11, torch.bfloat16, 2, 2, 256, 128, 128)
+    h = oracle_h(inp, "sigmoid", torch.float32).to("cuda")
+    d = to_dev(inp)
+    gd = to_dev(gin)
+    args = (d["q"], d["k"], d["v"], d["i_pre"], d["f_pre"], d["o_pre"], d["C0"], d["n0"], d["m0"],
+            h, gd["dh"], gd["dC1"], gd["dn1"])
+    eager = M.mlstm_bwd_chunkwise(*args, chunk=64)
+    torch.cuda.synchronize()
+    eager = {k: v.clone() for k, v in eager.items() if v is not None}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm-up on another stream before capturing
+        M.mlstm_bwd_chunkwise(*args, chunk=64)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        out = M.mlstm_bwd_chunkwise(*args, chunk=64)
+    for rep in range(3):
+        for v in out.values():
+            if v is not None:
+                v.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k, v in eager.items():
+            assert torch.equal(out[k], v), (rep, k)
