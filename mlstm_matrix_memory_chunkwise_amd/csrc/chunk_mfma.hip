@@ -573,6 +573,7 @@ size_t chunk_mfma_workspace(const SeqArgs&, int64_t) { return 0; }
 
 hipError_t launch_chunk_mfma(const SeqArgs& a, int64_t chunk, void*, hipStream_t stream) {
   if (chunk_ws_supported(a, chunk)) return launch_chunk_ws(a, stream);
+  if (chunk_ws128_supported(a, chunk)) return launch_chunk_ws128(a, stream);
   if (chunk_mfma8_supported(a, chunk)) return launch_chunk_mfma8(a, stream);
   switch (a.o_mode) {
     case O_F32: return launch_D<O_F32>(a, chunk, stream);

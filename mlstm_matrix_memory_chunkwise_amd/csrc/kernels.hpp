@@ -73,6 +73,10 @@ hipError_t launch_chunk_mfma8(const SeqArgs& a, hipStream_t stream);
 // by one chunk; launch_chunk_mfma routes to it first.
 bool chunk_ws_supported(const SeqArgs& a, int64_t chunk);
 hipError_t launch_chunk_ws(const SeqArgs& a, hipStream_t stream);
+// Chunk-128, d_qk-256 variant with state and score wave groups pipelined by
+// one chunk (P kept in registers); launch_chunk_mfma routes to it first.
+bool chunk_ws128_supported(const SeqArgs& a, int64_t chunk);
+hipError_t launch_chunk_ws128(const SeqArgs& a, hipStream_t stream);
 // State-only pass: the final (C~, n~, m) after T tokens (T a multiple of 64)
 // from (C0, n0, m0), no outputs; bf16 k/v, d_qk 64/128/256, d_v % 64 == 0.
 // C1, n1, m1 are required.

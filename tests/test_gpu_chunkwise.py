@@ -118,6 +118,12 @@ EDGE = [
     ("fp32 chunk 128 d 32/96", "f32", 1, 2, 256, 32, 96, 128, True, True, "sigmoid"),
     ("fp32 exp gate chunk 64", "f32", 2, 1, 128, 48, 16, 64, True, False, "exp"),
     ("d_qk 256 d_v 512 chunk 128", "bf16", 1, 2, 512, 256, 512, 128, False, True, "sigmoid"),
+    # d_qk 256 at chunk 128: the kernel with state and score wave roles
+    ("chunk 128 d_qk 256: one chunk", "bf16", 1, 1, 128, 256, 64, 128, True, True, "sigmoid"),
+    ("chunk 128 d_qk 256: exp forget gate", "bf16", 1, 2, 512, 256, 128, 128, True, True, "exp"),
+    ("chunk 128 d_qk 256: input-gate spikes", "bf16", 1, 2, 1024, 256, 64, 128, True, True, "sigmoid"),
+    ("chunk 128 d_qk 256: no o-gate, zero state, 6 heads, 2 value tiles", "bf16", 2, 3, 384, 256, 128,
+     128, False, False, "sigmoid"),
     # input-gate spikes: the running maximum jumps by tens, so whole chunks of
     # decay underflow to zero and the state's scale is reset
     ("input-gate spikes", "bf16", 1, 2, 1024, 128, 64, 64, True, True, "sigmoid"),
@@ -163,12 +169,13 @@ def test_edge_cases(case):
     compare(run_gpu(inp, chunk, fgate=fgate), run_oracle(inp, fgate=fgate), tol, label=name)
 
 
-def test_bf16_output_gate():
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_bf16_output_gate(chunk):
     cfg = workloads.CONFIGS["d256_T8192"]
     inp = workloads.make_chunkwise_inputs(cfg, B=1, H=1, T=256)
-    log("chunkwise bf16 o")
-    compare(run_gpu(inp, 64, o_dtype=torch.bfloat16), run_oracle(inp, o_dtype=torch.bfloat16),
-            TOL_BF16, label="bf16 o")
+    log(f"chunkwise bf16 o, chunk {chunk}")
+    compare(run_gpu(inp, chunk, o_dtype=torch.bfloat16), run_oracle(inp, o_dtype=torch.bfloat16),
+            TOL_BF16, label=f"bf16 o chunk {chunk}")
 
 
 # ----------------------------------------------------------------- properties
