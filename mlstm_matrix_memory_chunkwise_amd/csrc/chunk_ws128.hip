@@ -23,13 +23,14 @@
 // * score waves 4..7: wave 4 + V owns query tiles V and 7 - V (nine causal
 //   16x16 score tiles per wave) and accumulates S^T = K Q^T and q.n~ over
 //   the stages of chunk c.  At the chunk's last stage it forms P = S (.) D
-//   and the row sums in registers: the MFMA output of S^T, with the keys of
+//   and the row sums in registers (its second query tile at the first stage
+//   of the next chunk): the MFMA output of S^T, with the keys of
 //   a 32-key step taken in the order (4g..4g+3, 16+4g..16+4g+3), is the B
 //   operand of P V as it stands (the value fragments are read in the same
 //   key order), so P never goes through LDS.  During the first stages of
 //   chunk c + 1 the wave finishes chunk c: P V onto the scaled readout, the
-//   denominators, the output gate (o~ read straight into registers two
-//   chunks' stages ahead) and h.  Wave 4 also folds the normaliser
+//   denominators, the output gate (o~ read straight into registers at the
+//   chunk's last stage) and h.  Wave 4 also folds the normaliser
 //   increments into n~ one slice behind the state waves, wave 7 runs the gate
 //   scan of the next chunk.
 // The finishing work of one chunk (vector ALU) thus overlaps the MFMA work
@@ -64,7 +65,7 @@ constexpr int NSLOT = D + 1;
 constexpr int NB_QK = 2 * QKT / 1024 / 4;   // 1 KB loads per loading wave per stage
 constexpr int NB_V = VTB / 1024 / 4;        // ... per value tile
 constexpr int NB_G = 1;                     // 256 B gate loads per loading wave per chunk
-constexpr int O_STAGE = 5;          // stage of chunk c at which chunk c's o~ is read
+constexpr int O_STAGE = 7;          // stage of chunk c at which chunk c's o~ is read
 constexpr int SCAN_WAVE = 7;
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -302,7 +303,7 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws128_kernel(SeqArgs a) {
         const char* Qb = sRing[x % NSLOT][0];
         const char* Kb = sRing[x % NSLOT][1];
         if (s == 0) {
-          gL = sGate[gb][2][L - 1];
+          gL = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sGate[gb][2][L - 1])));
           renorm = gL * sig < 0x1p-64f;
           sig_new = renorm ? 1.0f : gL * sig;
           // w V (w / sig' from the scan) as the update's B operand: lane
@@ -344,12 +345,12 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws128_kernel(SeqArgs a) {
 #pragma unroll
           for (int it = 0; it < NT / 2; ++it) Qf[it] = lds_ld16(Qb, swz4((4 * h2 + it) * 16 + l16, 8 * g));
 #pragma unroll
-          for (int it = 0; it < NT / 2; ++it) {
+          for (int it = 0; it < NT / 2; ++it)
             outT[4 * h2 + it] = mfma16x16x32(Ahi, as_bf16x8(Qf[it]), outT[4 * h2 + it]);
+#pragma unroll
+          for (int it = 0; it < NT / 2; ++it)
             outT[4 * h2 + it] = mfma16x16x32(Alo, as_bf16x8(Qf[it]), outT[4 * h2 + it]);
-          }
         }
-        __builtin_amdgcn_sched_barrier(0);
         // then their update on the K^T fragments of the slice's two row tiles
         // (lane c of tile j holds d_qk row 8 (c/4) + 4 j + c%4 of the slice)
         bf16x8 Kt[NKS][2];
@@ -376,8 +377,13 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws128_kernel(SeqArgs a) {
         // zero), B = the K^T fragment, so D[4r + e][c] is term e of
         // sum_j w_j K[j][row c]
         {
-          const bf16x8 B0 = nk ? (nj ? Kt[1][1] : Kt[1][0]) : (nj ? Kt[0][1] : Kt[0][0]);
-          const bf16x8 B1 = nk ? (nj ? Kt[3][1] : Kt[3][0]) : (nj ? Kt[2][1] : Kt[2][0]);
+          // (the K^T fragments of k-steps nk, nk + 2 and row tile nj, read
+          // again from LDS rather than selected among registers)
+          const int ncol = 8 * kq + 4 * nj;
+          const bf16x8 B0 = join(lds_tr(Kb, swz4(32 * nk + 8 * g + kr, ncol)),
+                                 lds_tr(Kb, swz4(32 * nk + 8 * g + 4 + kr, ncol)));
+          const bf16x8 B1 = join(lds_tr(Kb, swz4(32 * (nk + 2) + 8 * g + kr, ncol)),
+                                 lds_tr(Kb, swz4(32 * (nk + 2) + 8 * g + 4 + kr, ncol)));
           const uint4 W0 = *reinterpret_cast<const uint4*>(&sWs[gb][l16 & 3][32 * nk + 8 * g]);
           const uint4 W1 = *reinterpret_cast<const uint4*>(&sWs[gb][l16 & 3][32 * (nk + 2) + 8 * g]);
           f32x4 ni = mfma16x16x32(as_bf16x8(W0), B0, f32x4{0.f, 0.f, 0.f, 0.f});
@@ -469,19 +475,28 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws128_kernel(SeqArgs a) {
         const int i = qt * 16 + l16;
         const float gi_ = sGate[gbx][2][i];
         const float den = fmaxf(fabsf(gi_ * qv + rs), sGate[gbx][3][i]);
-        const float inv = __builtin_amdgcn_rcpf(den);
         bf16_t* dst = hbase + (static_cast<int64_t>(cp) * L + i) * dv;
+        // h = o~-gate * num / den = num / (den (1 + exp(-o~))): one
+        // reciprocal per element
+        const float inv = __builtin_amdgcn_rcpf(den);
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
           float hv[4];
+          if constexpr (OM == O_NONE) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) hv[e] = o[ct][e] * inv;
-          if constexpr (OM == O_F32) {
+            for (int e = 0; e < 4; ++e) hv[e] = o[ct][e] * inv;
+          } else {
+            float ov[4];
+            if constexpr (OM == O_F32) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) hv[e] *= sigmoid_fast(of[ct][e]);
-          } else if constexpr (OM == O_BF16) {
-            hv[0] *= sigmoid_fast(bf_lo(obf[ct][0])); hv[1] *= sigmoid_fast(bf_hi(obf[ct][0]));
-            hv[2] *= sigmoid_fast(bf_lo(obf[ct][1])); hv[3] *= sigmoid_fast(bf_hi(obf[ct][1]));
+              for (int e = 0; e < 4; ++e) ov[e] = of[ct][e];
+            } else {
+              ov[0] = bf_lo(obf[ct][0]); ov[1] = bf_hi(obf[ct][0]);
+              ov[2] = bf_lo(obf[ct][1]); ov[3] = bf_hi(obf[ct][1]);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              hv[e] = o[ct][e] * __builtin_amdgcn_rcpf(__builtin_fmaf(den, __expf(-ov[e]), den));
           }
           st8_nt(dst + 16 * ct, cvt2(hv[0], hv[1]), cvt2(hv[2], hv[3]));
         }
@@ -538,6 +553,9 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws128_kernel(SeqArgs a) {
           const char* Qb = sRing[x % NSLOT][0];
           const char* Kb = sRing[x % NSLOT][1];
           if (s == 0) {
+            // P of the previous chunk's second query tile (its scores stay
+            // in sb until here)
+            if (c > 0) form_p(sb, wave_c<QB>{}, Pb, rsb, qvb, qnb, gbp);
 #pragma unroll
             for (int jt = 0; jt <= QA; ++jt) sa[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -558,8 +576,10 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws128_kernel(SeqArgs a) {
           for (int jt = 0; jt <= QB; ++jt) sb[jt] = mfma16x16x32(as_bf16x8(Kf[jt]), as_bf16x8(QfB), sb[jt]);
           qna = mfma16x16x32(as_bf16x8(Nx), as_bf16x8(QfA), qna);
           qnb = mfma16x16x32(as_bf16x8(Nx), as_bf16x8(QfB), qnb);
-          // finishing of chunk c - 1: P V at stages 0, 1 (onto the scaled
-          // readout the state waves left at its last stage), h at 2, 3
+          // finishing of chunk c - 1, spread over the stages: P V one key
+          // step per stage from stage 1 on (onto the scaled readout the state
+          // waves left at its last stage; its value tile is overwritten from
+          // stage 5 on), h at stages 5, 6
           if (c > 0) {
             const char* Vb = sV[(c - 1) & 1];
             if (s == 0) {
@@ -568,11 +588,10 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws128_kernel(SeqArgs a) {
                 oa[ct] = *reinterpret_cast<const f32x4*>(&sR[ct][QA][lane][0]);
                 ob[ct] = *reinterpret_cast<const f32x4*>(&sR[ct][QB][lane][0]);
               }
-              pv_steps(0, 2, Vb);
             }
-            if (s == 1) pv_steps(2, KB, Vb);
-            if (s == 2) h_tile(QA, oa, ofa, oba, rsa, qva, c - 1, gbp);
-            if (s == 3) h_tile(QB, ob, ofb, obb, rsb, qvb, c - 1, gbp);
+            if (s >= 1 && s <= KB) pv_steps(s - 1, s, Vb);
+            if (s == 5) h_tile(QA, oa, ofa, oba, rsa, qva, c - 1, gbp);
+            if (s == 6) h_tile(QB, ob, ofb, obb, rsb, qvb, c - 1, gbp);
           }
           if (s == O_STAGE) load_o(c);
           // n~: fold the increments of the previous slice
@@ -582,19 +601,16 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws128_kernel(SeqArgs a) {
           }
           // gate scan of chunk c + 1
           if (V == SCAN_WAVE - 4) {
-            if (s == 4) {
+            if (s == 2) {
               scan_part(0, (c + 1) & 1, gb == 2 ? 0 : gb + 1, m_n1, sg1, gsc, m_n2, sg2);
               scan_part(1, (c + 1) & 1, gb == 2 ? 0 : gb + 1, m_n1, sg1, gsc, m_n2, sg2);
             }
-            if (s == 5) {
+            if (s == 3) {
               scan_part(2, (c + 1) & 1, gb == 2 ? 0 : gb + 1, m_n1, sg1, gsc, m_n2, sg2);
               scan_part(3, (c + 1) & 1, gb == 2 ? 0 : gb + 1, m_n1, sg1, gsc, m_n2, sg2);
             }
           }
-          if (s == NS - 1) {
-            form_p(sa, wave_c<QA>{}, Pa, rsa, qva, qna, gb);
-            form_p(sb, wave_c<QB>{}, Pb, rsb, qvb, qnb, gb);
-          }
+          if (s == NS - 1) form_p(sa, wave_c<QA>{}, Pa, rsa, qva, qna, gb);
         }
         m_s = m_n1;
         m_n1 = m_n2;
@@ -604,6 +620,7 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws128_kernel(SeqArgs a) {
       }
       // ---- drain: the last chunk
       __syncthreads();
+      form_p(sb, wave_c<QB>{}, Pb, rsb, qvb, qnb, gbp);
       {
         const char* Vb = sV[(nchunks - 1) & 1];
 #pragma unroll
