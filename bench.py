@@ -143,10 +143,11 @@ KERNEL_SOURCES = {
     "groupnorm": ["block_ops.hip", "common.hpp", "kernels.hpp"],
     "conv": ["block_ops.hip", "common.hpp", "kernels.hpp"],
     "chunkwise": ["chunk_ws.hip", "mfma_util.hpp", "common.hpp", "kernels.hpp"],
+    "chunk128": ["chunk_ws128.hip", "mfma_util.hpp", "common.hpp", "kernels.hpp"],
     "step": ["step.hip", "common.hpp", "kernels.hpp"],
     "backward": ["bwd.hip", "bwd_mfma.hip", "mfma_util.hpp", "common.hpp", "kernels.hpp"],
-    "long_context": ["chunk_mfma.hip", "chunk_state.hip", "api.hip", "mfma_util.hpp", "common.hpp",
-                     "kernels.hpp"],
+    "long_context": ["chunk_ws128.hip", "chunk_mfma.hip", "chunk_state.hip", "api.hip", "mfma_util.hpp",
+                     "common.hpp", "kernels.hpp"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 
@@ -192,6 +193,10 @@ def profile_workload():
     h = torch.empty((cfg.B, cfg.H, cfg.T, cfg.dv), dtype=torch.bfloat16, device=dev)
     M.mlstm_fwd_chunkwise(d["q"], d["k"], d["v"], d["i_pre"], d["f_pre"], d["o_pre"],
                           d["C0"], d["n0"], d["m0"], chunk=64, out=h)
+    torch.cuda.synchronize()
+    # the same pass at chunk 128
+    M.mlstm_fwd_chunkwise(d["q"], d["k"], d["v"], d["i_pre"], d["f_pre"], d["o_pre"],
+                          d["C0"], d["n0"], d["m0"], chunk=128, out=h)
     torch.cuda.synchronize()
     # the backward of the same pass (chunk 64), as timed by the bench
     gen = torch.Generator(device="cpu").manual_seed(cfg.seed + 1)
@@ -371,7 +376,9 @@ def main():
         f2, b2 = chunk_algorithmic(B, H, T, dqk, dv, other, 4)
         result[f"chunk{other}"] = {"ms": ms2, "tokens_per_s": B * T / (ms2 / 1e3),
                                    "mfma_frac": f2 / (ms2 / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-                                   "hbm_frac": b2 / (ms2 / 1e3) / 1e9 / HBM_PEAK_GBS}
+                                   "hbm_frac": b2 / (ms2 / 1e3) / 1e9 / HBM_PEAK_GBS,
+                                   "algorithmic_bytes": b2,
+                                   "traffic": measured_traffic("chunk128" if other == 128 else "chunkwise")}
         # no output gate (gating done at block level after GroupNorm)
         def run_noo():
             M.mlstm_fwd_chunkwise(d["q"], d["k"], d["v"], d["i_pre"], d["f_pre"], None,
