@@ -30,9 +30,9 @@
 //   key order), so P never goes through LDS.  During the first stages of
 //   chunk c + 1 the wave finishes chunk c: P V onto the scaled readout, the
 //   denominators, the output gate (o~ read straight into registers at the
-//   chunk's last stage) and h.  Wave 4 also folds the normaliser
-//   increments into n~ one slice behind the state waves, wave 7 runs the gate
-//   scan of the next chunk.
+//   chunk's last stage) and h.  Waves 5 and 6 also fold the normaliser
+//   increments into n~, half of the rows each, at stages where they are
+//   idle; wave 7 runs the gate scan of the next chunk.
 // The finishing work of one chunk (vector ALU) thus overlaps the MFMA work
 // of the next on every SIMD.
 //
@@ -533,13 +533,18 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws128_kernel(SeqArgs a) {
         rs = sum_groups(r);
         qv = (qn[0] + qn[1]) + qn[2];
       };
-      // n~ rows of slice sl after chunk cf: g_L n~ + the two partial sums
-      auto fold_n = [&](int cf, int sl, int gbf) {
-        const int row = 32 * sl + lane;
+      // n~ rows 128 hf .. 128 hf + 127 (slices 4 hf .. 4 hf + 3) after chunk
+      // cf: g_L n~ + the two partial sums
+      auto fold_n = [&](int cf, int hf, int gbf) {
         const int p = cf & 1;
-        const float nv = sGate[gbf][2][L - 1] * sN[p][row] + (sNp[0][row] + sNp[1][row]);
-        sN[p ^ 1][row] = nv;
-        split3_bf16(nv, sNs[p ^ 1][0][row], sNs[p ^ 1][1][row], sNs[p ^ 1][2][row]);
+        const float gLf = sGate[gbf][2][L - 1];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const int row = 128 * hf + 64 * r + lane;
+          const float nv = gLf * sN[p][row] + (sNp[0][row] + sNp[1][row]);
+          sN[p ^ 1][row] = nv;
+          split3_bf16(nv, sNs[p ^ 1][0][row], sNs[p ^ 1][1][row], sNs[p ^ 1][2][row]);
+        }
       };
 
       int gb = 0, gbp = 2;   // gate buffers of chunks c, c - 1
@@ -594,11 +599,14 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws128_kernel(SeqArgs a) {
             if (s == 6) h_tile(QB, ob, ofb, obb, rsb, qvb, c - 1, gbp);
           }
           if (s == O_STAGE) load_o(c);
-          // n~: fold the increments of the previous slice
-          if (V == 0 && lane < 32) {
-            if (s > 0) fold_n(c, s - 1, gb);
-            else if (c > 0) fold_n(c - 1, NS - 1, gbp);
-          }
+          // n~: the increments of slices 0..3 of chunk c are folded at stage 4
+          // (wave 6), those of slices 4..7 of chunk c - 1 at stage 2 of
+          // chunk c (wave 5), each before the next chunk's q.n~ reads the
+          // rows and before the state waves rewrite their partial sums; a
+          // fold is a chain of LDS round trips, so it sits at a stage where
+          // its wave has no other work
+          if (V == 2 && s == 4) fold_n(c, 0, gb);
+          if (V == 1 && s == 2 && c > 0) fold_n(c - 1, 1, gbp);
           // gate scan of chunk c + 1
           if (V == SCAN_WAVE - 4) {
             if (s == 2) {
@@ -632,8 +640,8 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws128_kernel(SeqArgs a) {
         h_tile(QA, oa, ofa, oba, rsa, qva, nchunks - 1, gbp);
         h_tile(QB, ob, ofb, obb, rsb, qvb, nchunks - 1, gbp);
       }
-      if (V == 0) {
-        if (lane < 32) fold_n(nchunks - 1, NS - 1, gbp);
+      if (V == 1) {
+        fold_n(nchunks - 1, 1, gbp);
         if (a.C1 && vt == 0) {
           const int p = nchunks & 1;
 #pragma unroll
