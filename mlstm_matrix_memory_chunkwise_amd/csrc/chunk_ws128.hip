@@ -101,7 +101,7 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws128_kernel(SeqArgs a) {
   __shared__ __align__(1024) char sRing[NSLOT][2][QKT];   // [slot][q|k]
   __shared__ __align__(1024) char sV[2][VTB];             // value tile by chunk parity
   __shared__ __align__(16) float sR[4][NT][64][4];        // scaled readout [col tile][query tile]
-  __shared__ __align__(16) float sGate[3][5][L];          // u, M, g, exp(-m), w / sig' by chunk mod 3
+  __shared__ __align__(16) float sGate[3][6][L];          // u, M, g, exp(-m), w / sig', w by chunk mod 3
   __shared__ __align__(16) bf16_t sWs[3][4][L];           // w as three bf16 terms and a zero row
   __shared__ __align__(16) float sN[2][DQK];              // n~ at the chunk start, by parity
   __shared__ __align__(16) bf16_t sNs[2][4][DQK];         // ... as three bf16 terms and a zero row
@@ -241,6 +241,7 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws128_kernel(SeqArgs a) {
         sGate[gb][2][j] = gv_[h];
         sGate[gb][3][j] = __expf(-(x.bc[h] + x.Mx[h]));
         sGate[gb][4][j] = wv[h] * rsg;
+        sGate[gb][5][j] = wv[h];
         split3_bf16(wv[h], sWs[gb][0][j], sWs[gb][1][j], sWs[gb][2][j]);
       }
       m_after = x.bL + x.ML;
@@ -507,18 +508,40 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws128_kernel(SeqArgs a) {
         constexpr int qt = decltype(qtc)::value;
         const int i = qt * 16 + l16;
         const float Mi = sGate[gbx][1][i];
+        const float dM = sGate[gbx][1][L - 1] - Mi;
         float pe[qt + 2][4];
         float r = 0.0f;
+        // D_ij = exp(u_j - M_i) = w_j exp(M_L - M_i), with w_j = exp(u_j - M_L)
+        // from the gate scan: two multiplies per element instead of an
+        // exponential.  While M_L - M_i <= 64 no factor overflows, and a w_j
+        // that underflows belongs to a weight below e^-23 of the row's
+        // largest (which is 1); a tile with a larger jump of the running
+        // maximum inside the chunk takes the direct form (a wave-wide vote).
+        if (__ballot(dM > 64.0f) == 0) {
+          const float bi = __expf(dM);
 #pragma unroll
-        for (int jt = 0; jt <= qt; ++jt) {
-          const float4 uj = *reinterpret_cast<const float4*>(&sGate[gbx][0][jt * 16 + 4 * g]);
-          const float ujv[4] = {uj.x, uj.y, uj.z, uj.w};
+          for (int jt = 0; jt <= qt; ++jt) {
+            const float4 wj = *reinterpret_cast<const float4*>(&sGate[gbx][5][jt * 16 + 4 * g]);
+            const float wjv[4] = {wj.x, wj.y, wj.z, wj.w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float pv = acc[jt][e] * __expf(ujv[e] - Mi);
-            pe[jt][e] = (jt < qt || 4 * g + e <= l16) ? pv : 0.0f;
+            for (int e = 0; e < 4; ++e) {
+              const float pv = (acc[jt][e] * bi) * wjv[e];
+              pe[jt][e] = (jt < qt || 4 * g + e <= l16) ? pv : 0.0f;
+            }
+            r += (pe[jt][0] + pe[jt][1]) + (pe[jt][2] + pe[jt][3]);
           }
-          r += (pe[jt][0] + pe[jt][1]) + (pe[jt][2] + pe[jt][3]);
+        } else {
+#pragma unroll
+          for (int jt = 0; jt <= qt; ++jt) {
+            const float4 uj = *reinterpret_cast<const float4*>(&sGate[gbx][0][jt * 16 + 4 * g]);
+            const float ujv[4] = {uj.x, uj.y, uj.z, uj.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float pv = acc[jt][e] * __expf(ujv[e] - Mi);
+              pe[jt][e] = (jt < qt || 4 * g + e <= l16) ? pv : 0.0f;
+            }
+            r += (pe[jt][0] + pe[jt][1]) + (pe[jt][2] + pe[jt][3]);
+          }
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) pe[qt + 1][e] = 0.0f;   // above the diagonal

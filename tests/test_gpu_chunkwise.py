@@ -178,6 +178,20 @@ def test_bf16_output_gate(chunk):
             TOL_BF16, label=f"bf16 o chunk {chunk}")
 
 
+def test_chunk128_running_max_jump():
+    """Chunk 128, d_qk 256: the running maximum jumps by more than 64 inside a
+    chunk (input-gate preactivations of 90 and 170 at tokens 200 and 330, in
+    the middle of chunks 1 and 2), so those chunks' score tiles take the
+    direct exponential form of the decay matrix instead of the factored one."""
+    cfg = workloads.Config("jump", 11, "bf16", 1, 2, 512, 256, 128, (128,), (-1.0, 2.0), (3.0, 1.0),
+                           (0.0, 1.0), True)
+    inp = workloads.make_chunkwise_inputs(cfg)
+    inp["i_pre"][:, :, 200] = 90.0
+    inp["i_pre"][:, :, 330] = 170.0
+    log("chunkwise chunk 128: running-maximum jump")
+    compare(run_gpu(inp, 128), run_oracle(inp), TOL_BF16, label="chunk 128 max jump")
+
+
 # ----------------------------------------------------------------- properties
 def _split_run(inp, chunk, s):
     M = _M()
