@@ -284,6 +284,12 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws128_kernel(SeqArgs a) {
         }
       }
     }
+    // Wait for these loads here: the compiler does not see the asm loads of
+    // the ring, and with the C~ loads still counted as pending in the loop it
+    // places waits at the first use of each row tile whose counts, once the
+    // ring's loads are in flight, would wait for those too (down to vmcnt(0)
+    // at the last stage of every chunk).
+    wait_vm<0>();
     float sig = 1.0f;   // C~ = sig * cacc
     f32x4 outT[NT];
     bf16x8 wVf[NKS];
