@@ -56,10 +56,10 @@ __global__ __launch_bounds__(NTH, 1) void chunk_state_kernel(SeqArgs a) {
   __shared__ __align__(1024) char sK[NSLOT][NSUB][SUBT];
   __shared__ __align__(1024) char sV[NSLOT][SUBT];
   __shared__ __align__(256) float sG[NSLOT][NW][2][L];   // raw gates, one copy per wave
-  // per chunk parity: w as three bf16 terms + a zero row, and w / sig' (the
-  // update's scale); wave-private
-  __shared__ __align__(16) bf16_t sW[2][NW][4][L];
-  __shared__ __align__(16) float sWv[2][NW][L];
+  // per slot: w as three bf16 terms + a zero row, and w / sig' (the update's
+  // scale); wave-private
+  __shared__ __align__(16) bf16_t sW[NSLOT][NW][4][L];
+  __shared__ __align__(16) float sWv[NSLOT][NW][L];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -100,31 +100,39 @@ __global__ __launch_bounds__(NTH, 1) void chunk_state_kernel(SeqArgs a) {
   // this wave's own copy of the gates of chunk c + 1.  A 1 KB load covers 8
   // rows of a [64 x 64] tile: lane l writes row 8G + l/8, physical 16-byte
   // chunk l%8, which holds the logical chunk (l%8) ^ ((row/2)%8) (the swz
-  // layout).
+  // layout).  Each load takes a wave-uniform chunk base (SGPRs) and a fixed
+  // per-lane byte offset, so no lane computes a 64-bit address per chunk.
   const int ld_r = lane >> 3, ld_pc = lane & 7;
-  auto issue_gates = [&](int c) {
+  uint32_t koff[NB_K];
+#pragma unroll
+  for (int m = 0; m < NB_K; ++m) {
+    const int item = wave * NB_K + m;             // 0 .. 8 NSUB - 1
+    const int sb = item / 8, G = item % 8;
+    const int row = 8 * G + ld_r;
+    koff[m] = static_cast<uint32_t>(2 * (row * DQK + sb * 64 + 8 * (ld_pc ^ ((row >> 1) & 7))));
+  }
+  const uint32_t voff = static_cast<uint32_t>(
+      2 * ((8 * wave + ld_r) * dv + 8 * (ld_pc ^ (((8 * wave + ld_r) >> 1) & 7))));
+  const uint32_t goff = static_cast<uint32_t>(4 * lane);
+  auto issue_gates = [&](auto Sg, int c) {
+    constexpr int S = decltype(Sg)::value;
     const int cc = c < nchunks ? c : nchunks - 1;   // past the end: a harmless re-read
-    dma4(gi + static_cast<int64_t>(cc) * L + lane, lds_addr(&sG[c % NSLOT][wave][0][0]));
-    dma4(gf + static_cast<int64_t>(cc) * L + lane, lds_addr(&sG[c % NSLOT][wave][1][0]));
+    dma4_s(gi + static_cast<int64_t>(cc) * L, goff, lds_addr(&sG[S][wave][0][0]));
+    dma4_s(gf + static_cast<int64_t>(cc) * L, goff, lds_addr(&sG[S][wave][1][0]));
   };
-  auto issue_chunk = [&](int c) {
+  // chunk c into slot S (= c % NSLOT), and the gates of chunk c + 1
+  auto issue_chunk = [&](auto Sc, int c) {
+    constexpr int S = decltype(Sc)::value;
     const int cc = c < nchunks ? c : nchunks - 1;
-    const int slot = c % NSLOT;
+    const bf16_t* kb = gk + static_cast<int64_t>(cc) * L * DQK;
 #pragma unroll
     for (int m = 0; m < NB_K; ++m) {
-      const int item = wave * NB_K + m;             // 0 .. 8 NSUB - 1
+      const int item = wave * NB_K + m;
       const int sb = item / 8, G = item % 8;
-      const int row = 8 * G + ld_r;
-      const bf16_t* src = gk + (static_cast<int64_t>(cc) * L + row) * DQK + sb * 64 +
-                          8 * (ld_pc ^ ((row >> 1) & 7));
-      dma16(src, lds_addr(sK[slot][sb] + G * 1024));
+      dma16_s(kb, koff[m], lds_addr(sK[S][sb] + G * 1024));
     }
-    {
-      const int row = 8 * wave + ld_r;
-      const bf16_t* src = gv + (static_cast<int64_t>(cc) * L + row) * dv + 8 * (ld_pc ^ ((row >> 1) & 7));
-      dma16(src, lds_addr(sV[slot] + wave * 1024));
-    }
-    issue_gates(c + 1);
+    dma16_s(gv + static_cast<int64_t>(cc) * L * dv, voff, lds_addr(sV[S] + wave * 1024));
+    issue_gates(wave_c<(S + 1) % NSLOT>{}, c + 1);
   };
 
   // ---- state.  The wave's C~ tiles are the 16-row tiles T = rq NCTW + t
@@ -156,17 +164,22 @@ __global__ __launch_bounds__(NTH, 1) void chunk_state_kernel(SeqArgs a) {
   for (int t = 0; t < NCTW; ++t) nst[t] = (a.C0 && n_tile(t)) ? a.n0[head * DQK + nrow_of(t)] : 0.0f;
   float m_s = a.C0 ? a.m0[head] : 0.0f;
   float sig = 1.0f;
-  sW[0][wave][3][lane] = 0;
-  sW[1][wave][3][lane] = 0;
+#pragma unroll
+  for (int s = 0; s < NSLOT; ++s) sW[s][wave][3][lane] = 0;
+  // the initial-state loads complete here, before any load of the ring:
+  // otherwise the compiler, which does not see the asm loads, waits for every
+  // outstanding load (vmcnt(0), a drain of the ring) at the first use of the
+  // state inside the chunk loop
+  wait_vm<0>();
 
-  // Gate scan of chunk c (this wave's copy; lane j = token j): writes w (three
-  // terms) and w / sig' into the wave's buffers of the chunk's parity, and
-  // returns g_L and whether the accumulators take the scale, advancing m and
-  // sig to their values after the chunk.
-  auto scan = [&](int c, float& gL, bool& renorm) {
-    const int slot = c % NSLOT, par = c & 1;
-    const float xi = sG[slot][wave][0][lane];
-    const float lf = log_forget_fast(sG[slot][wave][1][lane], a.fgate_exp);
+  // Gate scan of chunk c (this wave's copy, slot S = c % NSLOT; lane j =
+  // token j): writes w (three terms) and w / sig' into the wave's buffers of
+  // slot S, and returns g_L and whether the accumulators take the scale,
+  // advancing m and sig to their values after the chunk.
+  auto scan = [&](auto Sc, float& gL, bool& renorm) {
+    constexpr int S = decltype(Sc)::value;
+    const float xi = sG[S][wave][0][lane];
+    const float lf = log_forget_fast(sG[S][wave][1][lane], a.fgate_exp);
     const float bcum = scan_add(lf);
     const float u = xi - bcum;
     const float Mx = fmaxf(m_s, scan_max(u));
@@ -178,32 +191,35 @@ __global__ __launch_bounds__(NTH, 1) void chunk_state_kernel(SeqArgs a) {
     // sig' = g_L sig; when sig' gets tiny the accumulators take g_L sig
     renorm = gL * sig < 0x1p-64f;
     const float sig_new = renorm ? 1.0f : gL * sig;
-    split3_bf16(wj, sW[par][wave][0][lane], sW[par][wave][1][lane], sW[par][wave][2][lane]);
-    sWv[par][wave][lane] = wj * __builtin_amdgcn_rcpf(sig_new);
+    split3_bf16(wj, sW[S][wave][0][lane], sW[S][wave][1][lane], sW[S][wave][2][lane]);
+    sWv[S][wave][lane] = wj * __builtin_amdgcn_rcpf(sig_new);
     m_s = bL + ML;
     sig = sig_new;
   };
 
   // ---- prologue: the gates of chunk 0, then chunks 0 .. D-1 (with the
   // gates of chunks 1 .. D) in flight; chunk 0's scan once its gates land
-  issue_gates(0);
-#pragma unroll
-  for (int c = 0; c < D; ++c) issue_chunk(c);
+  static_assert(D == 2 && NSLOT == 3, "the prologue and the unrolled loop assume two chunks in flight");
+  issue_gates(wave_c<0>{}, 0);
+  issue_chunk(wave_c<0>{}, 0);
+  issue_chunk(wave_c<1>{}, 1);
   wait_vm<D * NB>();
   // gL, renorm: chunk c's, from its scan; sig_prev, m_prev: the scale and
   // m before chunk c while it is processed (after it, once the loop ends)
   float gL = 1.0f, sig_prev = 1.0f, m_prev = m_s;
   bool renorm = false;
-  scan(0, gL, renorm);
+  scan(wave_c<0>{}, gL, renorm);
 
   const int kr = l16 >> 2, kq = l16 & 3;
-  for (int c = 0; c < nchunks; ++c) {
-    const int slot = c % NSLOT, par = c & 1;
+  // one chunk; the slot S = c % NSLOT is a compile-time constant (the loop
+  // is unrolled by NSLOT), so every LDS address is a fixed per-lane offset
+  auto chunk_step = [&](auto Sc, int c) {
+    constexpr int S = decltype(Sc)::value;
     // chunk c's loads (and the gates of chunk c + 1) were issued D chunks
     // ago; (D - 1) NB loads of this wave came after them
     wait_vm<(D - 1) * NB>();
     __syncthreads();
-    issue_chunk(c + D);   // into the slots of chunk c - 1, which every wave has left
+    issue_chunk(wave_c<(S + D) % NSLOT>{}, c + D);   // into the slot of chunk c - 1, which every wave has left
 
     // w (three terms) as the A operand of the n~ increment, and w / sig' for
     // this lane's tokens 32 ks + 8 g + 0..7 (wave-private LDS, written by the
@@ -212,14 +228,14 @@ __global__ __launch_bounds__(NTH, 1) void chunk_state_kernel(SeqArgs a) {
     bf16x8 wVf[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      Wx[ks] = *reinterpret_cast<const uint4*>(&sW[par][wave][l16 & 3][32 * ks + 8 * g]);
-      const float4 w0 = *reinterpret_cast<const float4*>(&sWv[par][wave][32 * ks + 8 * g]);
-      const float4 w1 = *reinterpret_cast<const float4*>(&sWv[par][wave][32 * ks + 8 * g + 4]);
+      Wx[ks] = *reinterpret_cast<const uint4*>(&sW[S][wave][l16 & 3][32 * ks + 8 * g]);
+      const float4 w0 = *reinterpret_cast<const float4*>(&sWv[S][wave][32 * ks + 8 * g]);
+      const float4 w1 = *reinterpret_cast<const float4*>(&sWv[S][wave][32 * ks + 8 * g + 4]);
       // V^T fragment of this wave's 16 columns: lane (g, c) gets column c
       // for tokens 32 ks + 8 g + 0..7
       const int col = vcol + 4 * kq;
-      const uint2 lo = lds_tr(sV[slot], swz(32 * ks + 8 * g + kr, col));
-      const uint2 hi = lds_tr(sV[slot], swz(32 * ks + 8 * g + 4 + kr, col));
+      const uint2 lo = lds_tr(sV[S], swz(32 * ks + 8 * g + kr, col));
+      const uint2 hi = lds_tr(sV[S], swz(32 * ks + 8 * g + 4 + kr, col));
       float xw[8];
       xw[0] = bf_lo(lo.x) * w0.x; xw[1] = bf_hi(lo.x) * w0.y;
       xw[2] = bf_lo(lo.y) * w0.z; xw[3] = bf_hi(lo.y) * w0.w;
@@ -244,7 +260,7 @@ __global__ __launch_bounds__(NTH, 1) void chunk_state_kernel(SeqArgs a) {
 #pragma unroll
     for (int t = 0; t < NCTW; ++t) {
       const int T = rq * NCTW + t;
-      const char* Kb = sK[slot][T >> 2];
+      const char* Kb = sK[S][T >> 2];
       const int tl = T & 3;
       const int col = 32 * (tl >> 1) + 8 * kq + 4 * (tl & 1);
       uint2 Klo[NKS], Khi[NKS];
@@ -268,7 +284,12 @@ __global__ __launch_bounds__(NTH, 1) void chunk_state_kernel(SeqArgs a) {
     // loads); it reads nothing this chunk's products write
     sig_prev = sig;
     m_prev = m_s;
-    scan(c + 1, gL, renorm);
+    scan(wave_c<(S + 1) % NSLOT>{}, gL, renorm);
+  };
+  for (int c = 0; c < nchunks; c += NSLOT) {
+    chunk_step(wave_c<0>{}, c);
+    if (c + 1 < nchunks) chunk_step(wave_c<1>{}, c + 1);
+    if (c + 2 < nchunks) chunk_step(wave_c<2>{}, c + 2);
   }
   // no LDS load may still be in flight when the workgroup ends
   wait_vm<0>();

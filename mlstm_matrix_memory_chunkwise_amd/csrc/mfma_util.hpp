@@ -94,6 +94,16 @@ __device__ __forceinline__ void dma4(const void* gsrc, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
                :: "s"(lds), "v"(gsrc) : "memory");
 }
+// the same two loads from a wave-uniform base (SGPR pair) plus a 32-bit
+// per-lane byte offset: no per-lane 64-bit address arithmetic
+__device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds), "v"(voff), "s"(sbase) : "memory");
+}
+__device__ __forceinline__ void dma4_s(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
+               :: "s"(lds), "v"(voff), "s"(sbase) : "memory");
+}
 
 // 8-byte store of data written once
 __device__ __forceinline__ void st8_nt(void* p, uint32_t lo, uint32_t hi) {
