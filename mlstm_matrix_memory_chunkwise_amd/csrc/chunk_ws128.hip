@@ -478,7 +478,7 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws128_kernel(SeqArgs a) {
       };
       // h of query tile qt of chunk cp from its numerators, row sum and q.n~
       auto h_tile = [&](int qt, const f32x4* o, const f32x4* of, const u32x2* obf, float rs, float qv,
-                        int cp, int gbx) {
+                        int cp, int gbx, uint32_t* hk) {
         const int i = qt * 16 + l16;
         const float gi_ = sGate[gbx][2][i];
         const float den = fmaxf(fabsf(gi_ * qv + rs), sGate[gbx][3][i]);
@@ -505,8 +505,19 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws128_kernel(SeqArgs a) {
             for (int e = 0; e < 4; ++e)
               hv[e] = o[ct][e] * __builtin_amdgcn_rcpf(__builtin_fmaf(den, __expf(-ov[e]), den));
           }
-          st8_nt(dst + 16 * ct, cvt2(hv[0], hv[1]), cvt2(hv[2], hv[3]));
+          hk[2 * ct] = cvt2(hv[0], hv[1]);
+          hk[2 * ct + 1] = cvt2(hv[2], hv[3]);
+          st8_nt(dst + 16 * ct, hk[2 * ct], hk[2 * ct + 1]);
         }
+      };
+      // A store reads its data registers after it issues, so the compiler
+      // waits for the store to complete before those registers are written
+      // again.  Keeping the stored words live through the following stage
+      // moves that wait one stage later, when the store has long completed.
+      uint32_t hkA[8], hkB[8];
+      auto keep = [](const uint32_t* hk) {
+        asm volatile("" :: "v"(hk[0]), "v"(hk[1]), "v"(hk[2]), "v"(hk[3]), "v"(hk[4]), "v"(hk[5]),
+                     "v"(hk[6]), "v"(hk[7]));
       };
       // P = S (.) D of query tile qt (accumulators acc[0..qt]) as B operands
       // of P V, its float32 row sum (before rounding) and q.n~
@@ -597,6 +608,10 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws128_kernel(SeqArgs a) {
             qna = f32x4{0.f, 0.f, 0.f, 0.f};
             qnb = f32x4{0.f, 0.f, 0.f, 0.f};
           }
+          // the o~ loads (issued a chunk ago) complete here, on every path,
+          // before the h stores: once stores are in flight, the compiler's
+          // in-order wait for a late o~ load would also wait for those stores
+          if (s == 5) wait_vm<0>();
           // scores and q.n~ of chunk c over the slice
           uint4 Kf[QB + 1];
 #pragma unroll
@@ -624,8 +639,8 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws128_kernel(SeqArgs a) {
               }
             }
             if (s >= 1 && s <= KB) pv_steps(s - 1, s, Vb);
-            if (s == 5) h_tile(QA, oa, ofa, oba, rsa, qva, c - 1, gbp);
-            if (s == 6) h_tile(QB, ob, ofb, obb, rsb, qvb, c - 1, gbp);
+            if (s == 5) h_tile(QA, oa, ofa, oba, rsa, qva, c - 1, gbp, hkA);
+            if (s == 6) h_tile(QB, ob, ofb, obb, rsb, qvb, c - 1, gbp, hkB);
           }
           if (s == O_STAGE) load_o(c);
           // n~: the increments of slices 0..3 of chunk c are folded at stage 4
@@ -648,6 +663,8 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws128_kernel(SeqArgs a) {
             }
           }
           if (s == NS - 1) form_p(sa, wave_c<QA>{}, Pa, rsa, qva, qna, gb);
+          if (c > 0 && s == 6) keep(hkA);
+          if (c > 0 && s == 7) keep(hkB);
         }
         m_s = m_n1;
         m_n1 = m_n2;
@@ -666,8 +683,8 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws128_kernel(SeqArgs a) {
           ob[ct] = *reinterpret_cast<const f32x4*>(&sR[ct][QB][lane][0]);
         }
         pv_steps(0, KB, Vb);
-        h_tile(QA, oa, ofa, oba, rsa, qva, nchunks - 1, gbp);
-        h_tile(QB, ob, ofb, obb, rsb, qvb, nchunks - 1, gbp);
+        h_tile(QA, oa, ofa, oba, rsa, qva, nchunks - 1, gbp, hkA);
+        h_tile(QB, ob, ofb, obb, rsb, qvb, nchunks - 1, gbp, hkB);
       }
       if (V == 1) {
         fold_n(nchunks - 1, 1, gbp);
