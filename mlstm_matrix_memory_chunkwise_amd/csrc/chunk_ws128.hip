@@ -433,6 +433,26 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws128_kernel(SeqArgs a) {
       u32x2 oba[4], obb[4];           // o~ (bfloat16)
       bf16_t* const hbase = static_cast<bf16_t*>(a.h) + head * Ts * dv + vt * TV + 4 * g;
 
+      // o~ (float32) of chunk c - 1 reaches the wave through LDS: a global ->
+      // LDS copy at stage 1 of chunk c into this wave's 8 KB of the scaled
+      // readout buffer, which is dead between its read at stage 0 and its
+      // rewrite at stage 7.  Whole 256-byte rows per copy (direct 16-byte
+      // loads in the h layout touched 16 half lines per instruction); row r
+      // holds its 16-byte chunk j at slot j ^ (r % 16), so that the reads of
+      // the h layout (16 rows, one chunk each) meet every bank once.
+      char* const sOw = reinterpret_cast<char*>(&sR[0][0][0][0]) + V * 8192;
+      auto issue_o = [&](int cp) {
+        const float* ob_ = static_cast<const float*>(a.o_pre) + head * Ts * dv + vt * TV;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const int r = 4 * m + (lane >> 4);            // rows 0..15: tile QA, 16..31: tile QB
+          const int rr = r & 15;
+          const int qt = (r < 16) ? QA : QB;
+          const int lc = (lane & 15) ^ rr;              // the row's 16-byte chunk in this slot
+          dma16_nt(ob_ + (static_cast<int64_t>(cp) * L + qt * 16 + rr) * dv + 4 * lc,
+                   lds_addr(sOw + m * 1024));
+        }
+      };
       auto load_o = [&](int cp) {
         if constexpr (OM == O_F32) {
           const float* ob_ = static_cast<const float*>(a.o_pre) + head * Ts * dv + vt * TV + 4 * g;
@@ -478,7 +498,7 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws128_kernel(SeqArgs a) {
       };
       // h of query tile qt of chunk cp from its numerators, row sum and q.n~
       auto h_tile = [&](int qt, const f32x4* o, const f32x4* of, const u32x2* obf, float rs, float qv,
-                        int cp, int gbx, uint32_t* hk) {
+                        int cp, int gbx, uint32_t* hk, int tb, bool o_lds) {
         const int i = qt * 16 + l16;
         const float gi_ = sGate[gbx][2][i];
         const float den = fmaxf(fabsf(gi_ * qv + rs), sGate[gbx][3][i]);
@@ -495,8 +515,15 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws128_kernel(SeqArgs a) {
           } else {
             float ov[4];
             if constexpr (OM == O_F32) {
+              if (o_lds) {
+                const f32x4 o4 = *reinterpret_cast<const f32x4*>(
+                    sOw + (tb + l16) * 256 + 16 * ((4 * ct + g) ^ l16));
 #pragma unroll
-              for (int e = 0; e < 4; ++e) ov[e] = of[ct][e];
+                for (int e = 0; e < 4; ++e) ov[e] = o4[e];
+              } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ov[e] = of[ct][e];
+              }
             } else {
               ov[0] = bf_lo(obf[ct][0]); ov[1] = bf_hi(obf[ct][0]);
               ov[2] = bf_lo(obf[ct][1]); ov[3] = bf_hi(obf[ct][1]);
@@ -639,10 +666,15 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws128_kernel(SeqArgs a) {
               }
             }
             if (s >= 1 && s <= KB) pv_steps(s - 1, s, Vb);
-            if (s == 5) h_tile(QA, oa, ofa, oba, rsa, qva, c - 1, gbp, hkA);
-            if (s == 6) h_tile(QB, ob, ofb, obb, rsb, qvb, c - 1, gbp, hkB);
+            if constexpr (OM == O_F32) {
+              if (s == 1) issue_o(c - 1);
+            }
+            if (s == 5) h_tile(QA, oa, ofa, oba, rsa, qva, c - 1, gbp, hkA, 0, true);
+            if (s == 6) h_tile(QB, ob, ofb, obb, rsb, qvb, c - 1, gbp, hkB, 16, true);
           }
-          if (s == O_STAGE) load_o(c);
+          if constexpr (OM == O_BF16) {
+            if (s == O_STAGE) load_o(c);
+          }
           // n~: the increments of slices 0..3 of chunk c are folded at stage 4
           // (wave 6), those of slices 4..7 of chunk c - 1 at stage 2 of
           // chunk c (wave 5), each before the next chunk's q.n~ reads the
@@ -682,9 +714,12 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws128_kernel(SeqArgs a) {
           oa[ct] = *reinterpret_cast<const f32x4*>(&sR[ct][QA][lane][0]);
           ob[ct] = *reinterpret_cast<const f32x4*>(&sR[ct][QB][lane][0]);
         }
+        // (the last chunk's o~ straight into registers: the buffer above
+        // holds its scaled readout until this point)
+        if constexpr (OM == O_F32) load_o(nchunks - 1);
         pv_steps(0, KB, Vb);
-        h_tile(QA, oa, ofa, oba, rsa, qva, nchunks - 1, gbp, hkA);
-        h_tile(QB, ob, ofb, obb, rsb, qvb, nchunks - 1, gbp, hkB);
+        h_tile(QA, oa, ofa, oba, rsa, qva, nchunks - 1, gbp, hkA, 0, false);
+        h_tile(QB, ob, ofb, obb, rsb, qvb, nchunks - 1, gbp, hkB, 16, false);
       }
       if (V == 1) {
         fold_n(nchunks - 1, 1, gbp);
