@@ -180,15 +180,16 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws128_kernel(SeqArgs a) {
     for (int m = 0; m < NB_QK; ++m) {
       const int G = lw * NB_QK + m;
       const int mat = G >> 3;
-      dma16((mat ? gk : gq) + base + qk_off[m], lds_addr(slot + mat * QKT + (G & 7) * 1024));
+      dma16_s((mat ? gk : gq) + base, static_cast<uint32_t>(2 * qk_off[m]),
+              lds_addr(slot + mat * QKT + (G & 7) * 1024));
     }
     if (sx == 0) {
       // (a past-the-end value tile lands in the slot of chunk nchunks - 2,
       // whose last reader finished before this stage's barrier)
 #pragma unroll
       for (int m = 0; m < NB_V; ++m)
-        dma16_nt(gv + static_cast<int64_t>(cc) * L * dv + v_off[m],
-                 lds_addr(sV[cx & 1] + (lw * NB_V + m) * 1024));
+        dma16_nt_s(gv + static_cast<int64_t>(cc) * L * dv, static_cast<uint32_t>(2 * v_off[m]),
+                   lds_addr(sV[cx & 1] + (lw * NB_V + m) * 1024));
     }
   };
   // each loading wave brings one quarter of the gates of chunk c + 2
@@ -689,10 +690,8 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws128_kernel(SeqArgs a) {
               scan_part(0, (c + 1) & 1, gb == 2 ? 0 : gb + 1, m_n1, sg1, gsc, m_n2, sg2);
               scan_part(1, (c + 1) & 1, gb == 2 ? 0 : gb + 1, m_n1, sg1, gsc, m_n2, sg2);
             }
-            if (s == 3) {
-              scan_part(2, (c + 1) & 1, gb == 2 ? 0 : gb + 1, m_n1, sg1, gsc, m_n2, sg2);
-              scan_part(3, (c + 1) & 1, gb == 2 ? 0 : gb + 1, m_n1, sg1, gsc, m_n2, sg2);
-            }
+            if (s == 3) scan_part(2, (c + 1) & 1, gb == 2 ? 0 : gb + 1, m_n1, sg1, gsc, m_n2, sg2);
+            if (s == 4) scan_part(3, (c + 1) & 1, gb == 2 ? 0 : gb + 1, m_n1, sg1, gsc, m_n2, sg2);
           }
           if (s == NS - 1) form_p(sa, wave_c<QA>{}, Pa, rsa, qva, qna, gb);
           if (c > 0 && s == 6) keep(hkA);

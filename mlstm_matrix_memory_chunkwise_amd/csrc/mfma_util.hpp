@@ -100,6 +100,10 @@ __device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, uint32
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                :: "s"(lds), "v"(voff), "s"(sbase) : "memory");
 }
+__device__ __forceinline__ void dma16_nt_s(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+               :: "s"(lds), "v"(voff), "s"(sbase) : "memory");
+}
 __device__ __forceinline__ void dma4_s(const void* sbase, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
                :: "s"(lds), "v"(voff), "s"(sbase) : "memory");
