@@ -96,6 +96,30 @@ __device__ __forceinline__ void wait_stage8(int s) {
   }
 }
 
+// Loads issued by one loading wave after those of stage x + 1, counted at the
+// top of stage x (slice s) before that stage's own issue: the stage loads of
+// x + 2 .. x + D - 1 and the gate loads at the tops of stages x + 1 - D ..
+// x - 1 that open a chunk.
+template <int NS_, int D_, int NBQK, int NBV, int NBX>
+__host__ __device__ constexpr int loads_after_next_stage(int s) {
+  int n = 0;
+  for (int k = 2; k < D_; ++k) n += NBQK + (((s + k) % NS_) == 0 ? NBV : 0);
+  for (int j = 1; j < D_; ++j) n += (((s - j) % NS_ + NS_) % NS_ == 0) ? NBX : 0;
+  return n;
+}
+__device__ __forceinline__ void wait_next_stage8(int s) {
+  switch (s) {
+    case 0: wait_vm<loads_after_next_stage<NS, D, NB_QK, NB_V, NB_G>(0)>(); break;
+    case 1: wait_vm<loads_after_next_stage<NS, D, NB_QK, NB_V, NB_G>(1)>(); break;
+    case 2: wait_vm<loads_after_next_stage<NS, D, NB_QK, NB_V, NB_G>(2)>(); break;
+    case 3: wait_vm<loads_after_next_stage<NS, D, NB_QK, NB_V, NB_G>(3)>(); break;
+    case 4: wait_vm<loads_after_next_stage<NS, D, NB_QK, NB_V, NB_G>(4)>(); break;
+    case 5: wait_vm<loads_after_next_stage<NS, D, NB_QK, NB_V, NB_G>(5)>(); break;
+    case 6: wait_vm<loads_after_next_stage<NS, D, NB_QK, NB_V, NB_G>(6)>(); break;
+    default: wait_vm<loads_after_next_stage<NS, D, NB_QK, NB_V, NB_G>(7)>(); break;
+  }
+}
+
 template <int OM>
 __global__ __launch_bounds__(NTH, 1) void chunk_ws128_kernel(SeqArgs a) {
   __shared__ __align__(1024) char sRing[NSLOT][2][QKT];   // [slot][q|k]
@@ -298,13 +322,20 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws128_kernel(SeqArgs a) {
     // k-steps nk and nk + 2
     const int nj = W & 1, nk = W >> 1;
     int gb = 0;
+    // Q fragments of the first half of the query tiles of the next stage,
+    // read at the end of the stage before (the loading waves wait for the
+    // loads of stage x + 1 at the top of stage x, so that stage's barrier
+    // publishes them)
+    uint4 QfN[NT / 2];
+#pragma unroll
+    for (int it = 0; it < NT / 2; ++it) QfN[it] = lds_ld16(sRing[0][0], swz4(it * 16 + l16, 8 * g));
     for (int c = 0; c < nchunks; ++c) {
       float gL = 0.0f, sig_new = 0.0f;
       bool renorm = false;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const int x = c * NS + s;
-        if (x >= D) wait_stage8(s);
+        if (x + 1 >= D) wait_next_stage8(s);
         __syncthreads();
         issue_stage(x + D);
         if (s == 0) issue_gates(c);
@@ -351,7 +382,8 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws128_kernel(SeqArgs a) {
         for (int h2 = 0; h2 < 2; ++h2) {
           uint4 Qf[NT / 2];
 #pragma unroll
-          for (int it = 0; it < NT / 2; ++it) Qf[it] = lds_ld16(Qb, swz4((4 * h2 + it) * 16 + l16, 8 * g));
+          for (int it = 0; it < NT / 2; ++it)
+            Qf[it] = h2 == 0 ? QfN[it] : lds_ld16(Qb, swz4((4 * h2 + it) * 16 + l16, 8 * g));
 #pragma unroll
           for (int it = 0; it < NT / 2; ++it)
             outT[4 * h2 + it] = mfma16x16x32(Ahi, as_bf16x8(Qf[it]), outT[4 * h2 + it]);
@@ -402,6 +434,11 @@ __global__ __launch_bounds__(NTH, 1) void chunk_ws128_kernel(SeqArgs a) {
 #pragma unroll
           for (int it = 0; it < NT; ++it)
             *reinterpret_cast<f32x4*>(&sR[W][it][lane][0]) = outT[it] * (sGate[gb][2][it * 16 + l16] * sig);
+        }
+        {
+          const char* QbN = sRing[(x + 1) % NSLOT][0];
+#pragma unroll
+          for (int it = 0; it < NT / 2; ++it) QfN[it] = lds_ld16(QbN, swz4(it * 16 + l16, 8 * g));
         }
       }
       sig = sig_new;
