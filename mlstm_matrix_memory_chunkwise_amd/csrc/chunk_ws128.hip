@@ -29,8 +29,10 @@
 //   operand of P V as it stands (the value fragments are read in the same
 //   key order), so P never goes through LDS.  During the first stages of
 //   chunk c + 1 the wave finishes chunk c: P V onto the scaled readout, the
-//   denominators, the output gate (o~ read straight into registers at the
-//   chunk's last stage) and h.  Waves 5 and 6 also fold the normaliser
+//   denominators, the output gate (float32 o~ copied global -> LDS at
+//   stage 1 into the wave's part of the scaled-readout buffer, which is free
+//   until stage 7; bfloat16 o~ read straight into registers at the chunk's
+//   last stage) and h.  Waves 5 and 6 also fold the normaliser
 //   increments into n~, half of the rows each, at stages where they are
 //   idle; wave 7 runs the gate scan of the next chunk.
 // The finishing work of one chunk (vector ALU) thus overlaps the MFMA work
