@@ -313,8 +313,9 @@ bool seq_is_empty(const mlstm_problem_t* p) { return p->B * p->H == 0 || p->T ==
 // columns) through the whole sequence, so a problem with few heads leaves
 // most of the 256 compute units idle.  When that grid has at most kSplitGroups
 // workgroups and the sequence is long, the call instead:
-//   1. runs the state-only pass (chunk_state.hip) over the first half, giving
-//      the exact state at T/2;
+//   1. computes the exact state at T/2: as one weighted product over the
+//      first half's tokens (state_gemm.hip) where that covers the shape,
+//      else with the state-only chunk recurrence (chunk_state.hip);
 //   2. runs the MFMA kernel once over both halves at the same time: half s of
 //      head h is laid out in memory exactly like head 2h + s of a problem with
 //      2H heads of T/2 tokens, whose initial states are the caller's (or
@@ -348,6 +349,8 @@ struct FwdPlan {
   StateBlock s_in;  // initial states of the 2 B H half-heads
   StateBlock s_out; // their final states
   StateBlock s_mid; // the state at T/2 of the B H heads
+  bool state_gemm;  // step 1 of the split as one weighted product
+  size_t sg_off;    // its scratch
   size_t need;      // workspace bytes
 };
 
@@ -378,6 +381,13 @@ FwdPlan fwd_plan(const mlstm::SeqArgs& a, int64_t chunk) {
     f.s_out = state_block(f.s_in.end, 2 * BH, dqk, dv);
     f.s_mid = state_block(f.s_out.end, BH, dqk, dv);
     f.need = f.s_mid.end;
+    mlstm::SeqArgs first = a;
+    first.T = a.T / 2;
+    f.state_gemm = mlstm::state_gemm_supported(first);
+    if (f.state_gemm) {
+      f.sg_off = f.need;
+      f.need = f.sg_off + mlstm::state_gemm_workspace(first);
+    }
   }
   return f;
 }
@@ -410,7 +420,8 @@ hipError_t run_split(const mlstm::SeqArgs& a, int64_t chunk, const FwdPlan& f, v
   mlstm::SeqArgs p1 = a;
   p1.T = a.T / 2;           // tokens 0 .. T/2 - 1 of each head (heads T apart)
   p1.C1 = midC; p1.n1 = midN; p1.m1 = midM;
-  hipError_t e = mlstm::launch_chunk_state(p1, st);
+  hipError_t e = f.state_gemm ? mlstm::launch_state_gemm(p1, w + f.sg_off, st)
+                              : mlstm::launch_chunk_state(p1, st);
   // initial states of the half-heads: 2h <- the caller's (or zero), 2h+1 <- step 1
   if (e == hipSuccess) e = copy_heads(inC, 2 * cB, a.C0, cB, cB, BH, st);
   if (e == hipSuccess) e = copy_heads(inN, 2 * nB, a.n0, nB, nB, BH, st);

@@ -82,6 +82,11 @@ hipError_t launch_chunk_ws128(const SeqArgs& a, hipStream_t stream);
 // C1, n1, m1 are required.
 bool chunk_state_supported(const SeqArgs& a);
 hipError_t launch_chunk_state(const SeqArgs& a, hipStream_t stream);
+// The same state as one weighted product over the tokens (state_gemm.hip):
+// d_qk 256, d_v a multiple of 128, bf16; needs state_gemm_workspace(a) bytes.
+bool state_gemm_supported(const SeqArgs& a);
+size_t state_gemm_workspace(const SeqArgs& a);
+hipError_t launch_state_gemm(const SeqArgs& a, void* workspace, hipStream_t stream);
 // Generic VALU chunkwise kernel (float32 path; bf16 shapes outside MFMA cover).
 // Tokens t0 .. T-1 in chunks of `chunk`; the last chunk may be shorter.
 hipError_t launch_chunk_valu(const SeqArgs& a, int64_t chunk, hipStream_t stream);
