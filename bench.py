@@ -146,7 +146,8 @@ KERNEL_SOURCES = {
     "chunk128": ["chunk_ws128.hip", "mfma_util.hpp", "common.hpp", "kernels.hpp"],
     "step": ["step.hip", "common.hpp", "kernels.hpp"],
     "backward": ["bwd.hip", "bwd_mfma.hip", "mfma_util.hpp", "common.hpp", "kernels.hpp"],
-    "long_context": ["chunk_ws128.hip", "chunk_mfma.hip", "chunk_state.hip", "api.hip", "mfma_util.hpp",
+    "long_context": ["chunk_ws128.hip", "chunk_mfma.hip", "chunk_state.hip", "state_gemm.hip", "api.hip",
+                     "mfma_util.hpp",
                      "common.hpp", "kernels.hpp"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
