@@ -144,10 +144,16 @@ EDGE = [
     ("ragged: T below one chunk", "bf16", 1, 2, 40, 64, 64, 64, True, True, "sigmoid"),
     ("ragged: T = 1", "bf16", 1, 1, 1, 64, 64, 64, True, True, "sigmoid"),
     ("ragged: fp32 chunk 64, 1 chunk + 36", "f32", 1, 2, 100, 32, 48, 64, True, True, "sigmoid"),
-    # sequence split: few heads and a long sequence; a state-only pass over
-    # the first half, then both halves at once (the oracle runs straight
-    # through, so every token after the split point checks the carried state)
+    # sequence split: few heads and a long sequence; the state at the split
+    # point (at d_qk 256 and d_v a multiple of 128 as one weighted product over
+    # the first half, split over token segments; else the state-only chunk
+    # recurrence), then both halves at once (the oracle runs straight through,
+    # so every token after the split point checks the carried state)
     ("split: d_qk 256 d_v 128, random state", "bf16", 1, 2, 4096, 256, 128, 64, True, True, "sigmoid"),
+    ("split: d_qk 256 d_v 256, random state, exp gate", "bf16", 1, 3, 4096, 256, 256, 64, True, True,
+     "exp"),
+    ("split: d_qk 256 d_v 192 (state by chunk recurrence)", "bf16", 1, 2, 4096, 256, 192, 64, True, True,
+     "sigmoid"),
     ("split: chunk 128, d_qk 128, zero state, exp gate, no o-gate", "bf16", 2, 1, 8192, 128, 64, 128,
      False, False, "exp"),
     ("split: chunk 32, d_qk 64 d_v 192", "bf16", 1, 3, 4096, 64, 192, 32, True, True, "sigmoid"),
