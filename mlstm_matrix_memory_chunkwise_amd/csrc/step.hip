@@ -73,7 +73,7 @@ __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, float4 v) {
 }
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 8;
+constexpr int kUnroll = 16;
 
 // C~ is touched exactly once per step: stream it past the caches.
 __device__ __forceinline__ float4 ld_stream(const float* p) {
