@@ -105,7 +105,14 @@ typedef struct {
  * a multiple of `chunk`, the last T % chunk tokens form one shorter chunk:
  * on the bf16 matrix-core path they run on the float32 vector kernel,
  * continuing from the state the first T - T % chunk tokens leave in the
- * workspace (B*H*(d_qk*d_v + d_qk + 1) floats).
+ * workspace (B*H*(d_qk*d_v + d_qk + 1) floats).  A long sequence with few
+ * heads (at most 128 matrix-core workgroups of 64 value columns, T a multiple
+ * of 2 chunks, at least 2048 tokens per half) is split in two: the state at
+ * T/2 is computed first, then both halves run at once.  Its workspace holds
+ * five B*H states and, at d_qk 256 with d_v a multiple of 128, the token
+ * segments' partial sums of the state at T/2 (at most 16 states per head)
+ * and per-token gate weights.  mlstm_fwd_chunkwise_workspace_bytes gives
+ * the size in every case.
  * Returns MLSTM_OK or an error code; on error, mlstm_last_error_detail()
  * describes it.
  */
@@ -128,7 +135,7 @@ mlstm_status_t mlstm_fwd_chunkwise_workspace_bytes(const mlstm_problem_t* p,
  * harnesses that forbid hipMalloc).  It computes exactly what
  * mlstm_fwd_chunkwise computes, with the same kernels, and allocates nothing:
  * where that call needs a workspace (T not a multiple of `chunk` on the bf16
- * matrix-core path: B*H*(d_qk*d_v + d_qk + 1) floats), it uses a fixed
+ * matrix-core path, or the split of a long sequence with few heads), it uses a fixed
  * device array of 64 MiB that the library holds on every GPU it runs on
  * until the process ends.
  *   Arguments, layouts and rules: as mlstm_fwd_chunkwise.  `stream` must
