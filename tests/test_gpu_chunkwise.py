@@ -154,6 +154,8 @@ EDGE = [
      "exp"),
     ("split: d_qk 256 d_v 192 (state by chunk recurrence)", "bf16", 1, 2, 4096, 256, 192, 64, True, True,
      "sigmoid"),
+    # half of 2112 tokens: one token segment, a partial last block of gate sums
+    ("split: B 2, d_qk 256 d_v 128, T 4224", "bf16", 2, 1, 4224, 256, 128, 64, True, True, "sigmoid"),
     ("split: chunk 128, d_qk 128, zero state, exp gate, no o-gate", "bf16", 2, 1, 8192, 128, 64, 128,
      False, False, "exp"),
     ("split: chunk 32, d_qk 64 d_v 192", "bf16", 1, 3, 4096, 64, 192, 32, True, True, "sigmoid"),
