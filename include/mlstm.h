@@ -106,13 +106,15 @@ typedef struct {
  * on the bf16 matrix-core path they run on the float32 vector kernel,
  * continuing from the state the first T - T % chunk tokens leave in the
  * workspace (B*H*(d_qk*d_v + d_qk + 1) floats).  A long sequence with few
- * heads (at most 128 matrix-core workgroups of 64 value columns, T a multiple
- * of 2 chunks, at least 2048 tokens per half) is split in two: the state at
- * T/2 is computed first, then both halves run at once.  Its workspace holds
- * five B*H states and, at d_qk 256 with d_v a multiple of 128, the token
- * segments' partial sums of the state at T/2 (at most 16 states per head)
- * and per-token gate weights.  mlstm_fwd_chunkwise_workspace_bytes gives
- * the size in every case.
+ * heads (at most 128 matrix-core workgroups of 64 value columns) is split
+ * into P = 8, 4 or 2 equal segments: the largest P whose P-fold grid fits 256
+ * compute units, with T a multiple of P chunks (and of 64 P) and at least
+ * 2048 tokens per segment; P above 2 needs d_qk 256 and d_v a multiple of
+ * 128.  The states at the P - 1 split points are computed first, then all
+ * segments run at once.  Its workspace holds (3P - 1)*B*H states and, at
+ * d_qk 256 with d_v a multiple of 128, the token segments' partial sums of
+ * those states (at most 16 states per head) and per-token gate weights.
+ * mlstm_fwd_chunkwise_workspace_bytes gives the size in every case.
  * Returns MLSTM_OK or an error code; on error, mlstm_last_error_detail()
  * describes it.
  */
@@ -140,9 +142,12 @@ mlstm_status_t mlstm_fwd_chunkwise_workspace_bytes(const mlstm_problem_t* p,
  * until the process ends.
  *   Arguments, layouts and rules: as mlstm_fwd_chunkwise.  `stream` must
  *   belong to the current device (NULL: its null stream).
- *   A problem that needs more than 64 MiB of workspace returns
- *   MLSTM_ERR_UNSUPPORTED (mlstm_fwd_chunkwise_workspace_bytes gives the
- *   size) and enqueues nothing.
+ *   Where the sequence split would need more than 64 MiB, it takes a form
+ *   that fits: fewer segments, the state at the split point by the chunk
+ *   recurrence instead of the weighted products, or no split; the result
+ *   then equals mlstm_fwd_chunkwise's up to rounding instead of bit for bit.  A problem that still needs more than 64 MiB of workspace
+ *   (a long tail state) returns MLSTM_ERR_UNSUPPORTED
+ *   (mlstm_fwd_chunkwise_workspace_bytes gives the size) and enqueues nothing.
  *   Calls on one GPU share that GPU's array: calls whose execution overlaps
  *   on one GPU (on two streams, or from two threads) race on it and must be
  *   ordered by the caller.  Nothing in the array needs clearing between

@@ -311,19 +311,23 @@ bool seq_is_empty(const mlstm_problem_t* p) { return p->B * p->H == 0 || p->T ==
 //
 // Sequence split.  The MFMA kernels run one workgroup per (head, 64 value
 // columns) through the whole sequence, so a problem with few heads leaves
-// most of the 256 compute units idle.  When that grid has at most kSplitGroups
-// workgroups and the sequence is long, the call instead:
-//   1. computes the exact state at T/2: as one weighted product over the
-//      first half's tokens (state_gemm.hip) where that covers the shape,
-//      else with the state-only chunk recurrence (chunk_state.hip);
-//   2. runs the MFMA kernel once over both halves at the same time: half s of
-//      head h is laid out in memory exactly like head 2h + s of a problem with
-//      2H heads of T/2 tokens, whose initial states are the caller's (or
-//      zero) for s = 0 and the state from step 1 for s = 1;
-//   3. copies the final states of the second halves out.
-// The states of the 2H half-heads live in the workspace.
+// most of the 256 compute units idle.  When that grid has at most
+// kSplitGroups workgroups and the sequence is long, the call instead splits
+// the sequence into P = 2, 4 or 8 equal segments (the most that still fit the
+// compute units and leave at least kSplitMinTokens per segment):
+//   1. computes the exact states at the P - 1 split points: from weighted
+//      products over the tokens before them (state_gemm.hip) where that
+//      covers the shape, else (P = 2 only) with the state-only chunk
+//      recurrence over the first half (chunk_state.hip);
+//   2. runs the MFMA kernel once over all segments at the same time: segment
+//      s of head h is laid out in memory exactly like head P h + s of a
+//      problem with P H heads of T / P tokens, whose initial states are the
+//      caller's (or zero) for s = 0 and the state from step 1 otherwise;
+//   3. copies the final states of the last segments out.
+// The states of the P H segment-heads live in the workspace.
 constexpr int64_t kSplitGroups = 128;      // half the compute units of an MI355X
-constexpr int64_t kSplitMinTokens = 2048;  // per half
+constexpr int64_t kSplitCUs = 256;         // the grid of all segments fits these
+constexpr int64_t kSplitMinTokens = 2048;  // per segment
 
 // One block of float32 states for n heads: C~ [n][d_qk][d_v], then n~ [n][d_qk],
 // then m [n], each 256-byte aligned, from byte offset `at`.
@@ -346,15 +350,18 @@ struct FwdPlan {
   int64_t Tm;
   size_t mid_off;   // byte offset of the carried state in the workspace
   bool split;       // the sequence split above (no tail)
-  StateBlock s_in;  // initial states of the 2 B H half-heads
+  int P;            // its segment count
+  StateBlock s_in;  // initial states of the P B H segment-heads
   StateBlock s_out; // their final states
-  StateBlock s_mid; // the state at T/2 of the B H heads
-  bool state_gemm;  // step 1 of the split as one weighted product
-  size_t sg_off;    // its scratch
+  StateBlock s_mid; // the states at the P - 1 split points of the B H heads
+  bool state_gemm;  // step 1 of the split as weighted products
+  size_t sg_off;    // their scratch
   size_t need;      // workspace bytes
 };
 
-FwdPlan fwd_plan(const mlstm::SeqArgs& a, int64_t chunk) {
+// cap: the most workspace a split may take (the fixed scratch of the
+// no-allocation entry point); with less, fewer segments or none.
+FwdPlan fwd_plan(const mlstm::SeqArgs& a, int64_t chunk, size_t cap = SIZE_MAX) {
   FwdPlan f{};
   f.Tm = a.T - a.T % chunk;
   mlstm::SeqArgs m = a;
@@ -368,25 +375,38 @@ FwdPlan fwd_plan(const mlstm::SeqArgs& a, int64_t chunk) {
   const size_t mid = f.tail ? 4 * BH * (dqk * dv + dqk + 1) : 0;
   f.need = f.tail ? f.mid_off + mid : mfma_ws;
   if (f.mfma && !f.tail) {
-    const int64_t unit = 2 * (chunk > 64 ? chunk : 64);   // halves of whole chunks and of 64
-    mlstm::SeqArgs half = a;
-    half.T = a.T / 2;
-    half.H = 2 * a.H;
-    f.split = a.T % unit == 0 && a.T / 2 >= kSplitMinTokens &&
-              a.B * a.H * (a.dv / 64) <= kSplitGroups && mlstm::chunk_state_supported(half) &&
-              mlstm::chunk_mfma_supported(half, chunk);
-  }
-  if (f.split) {
-    f.s_in = state_block(f.mid_off, 2 * BH, dqk, dv);
-    f.s_out = state_block(f.s_in.end, 2 * BH, dqk, dv);
-    f.s_mid = state_block(f.s_out.end, BH, dqk, dv);
-    f.need = f.s_mid.end;
-    mlstm::SeqArgs first = a;
-    first.T = a.T / 2;
-    f.state_gemm = mlstm::state_gemm_supported(first);
-    if (f.state_gemm) {
-      f.sg_off = f.need;
-      f.need = f.sg_off + mlstm::state_gemm_workspace(first);
+    const int64_t unit = chunk > 64 ? chunk : 64;   // segments of whole chunks and of 64 tokens
+    const int64_t grid = a.B * a.H * (a.dv / 64);
+    for (int P = 8; P >= 2 && !f.split; P /= 2) {
+      if (grid > kSplitGroups || grid * P > kSplitCUs || a.T % (P * unit) != 0 ||
+          a.T / P < kSplitMinTokens)
+        continue;
+      mlstm::SeqArgs seg = a;
+      seg.T = a.T / P;
+      seg.H = P * a.H;
+      if (!mlstm::chunk_mfma_supported(seg, chunk)) continue;
+      mlstm::SeqArgs before = a;       // tokens before the last split point
+      before.T = a.T / P * (P - 1);
+      bool gemm = mlstm::state_gemm_supported(before, P - 1);
+      const bool recur = P == 2 && mlstm::chunk_state_supported(seg);
+      if (!gemm && !recur) continue;
+      const StateBlock s_in = state_block(f.mid_off, P * BH, dqk, dv);
+      const StateBlock s_out = state_block(s_in.end, P * BH, dqk, dv);
+      const StateBlock s_mid = state_block(s_out.end, (P - 1) * BH, dqk, dv);
+      size_t need = s_mid.end + (gemm ? mlstm::state_gemm_workspace(before, P - 1) : 0);
+      if (need > cap && gemm && recur) {   // the chunk recurrence needs no scratch of its own
+        gemm = false;
+        need = s_mid.end;
+      }
+      if (need > cap) continue;   // fewer segments need less scratch
+      f.split = true;
+      f.P = P;
+      f.state_gemm = gemm;
+      f.s_in = s_in;
+      f.s_out = s_out;
+      f.s_mid = s_mid;
+      f.sg_off = s_mid.end;
+      f.need = need;
     }
   }
   return f;
@@ -407,45 +427,60 @@ hipError_t copy_heads(void* dst, size_t dpitch, const void* src, size_t spitch, 
 hipError_t run_split(const mlstm::SeqArgs& a, int64_t chunk, const FwdPlan& f, void* workspace,
                      hipStream_t st) {
   char* w = static_cast<char*>(workspace);
+  const int P = f.P;
   const size_t BH = static_cast<size_t>(a.B * a.H);
   const size_t dqk = static_cast<size_t>(a.dqk), dv = static_cast<size_t>(a.dv);
   const size_t cB = 4 * dqk * dv, nB = 4 * dqk;   // bytes of one head's C~, n~
-  float* inC = reinterpret_cast<float*>(w + f.s_in.C);
-  float* inN = reinterpret_cast<float*>(w + f.s_in.n);
-  float* inM = reinterpret_cast<float*>(w + f.s_in.m);
+  char* inC = w + f.s_in.C;
+  char* inN = w + f.s_in.n;
+  char* inM = w + f.s_in.m;
   float* midC = reinterpret_cast<float*>(w + f.s_mid.C);
   float* midN = reinterpret_cast<float*>(w + f.s_mid.n);
   float* midM = reinterpret_cast<float*>(w + f.s_mid.m);
-  // 1. the state at T/2
+  // 1. the states at the split points T/P, 2T/P, .. (block k of the mid
+  // states: the state at (k + 1) T/P of every head)
   mlstm::SeqArgs p1 = a;
-  p1.T = a.T / 2;           // tokens 0 .. T/2 - 1 of each head (heads T apart)
-  p1.C1 = midC; p1.n1 = midN; p1.m1 = midM;
-  hipError_t e = f.state_gemm ? mlstm::launch_state_gemm(p1, w + f.sg_off, st)
-                              : mlstm::launch_chunk_state(p1, st);
-  // initial states of the half-heads: 2h <- the caller's (or zero), 2h+1 <- step 1
-  if (e == hipSuccess) e = copy_heads(inC, 2 * cB, a.C0, cB, cB, BH, st);
-  if (e == hipSuccess) e = copy_heads(inN, 2 * nB, a.n0, nB, nB, BH, st);
-  if (e == hipSuccess) e = copy_heads(inM, 8, a.m0, 4, 4, BH, st);
-  if (e == hipSuccess) e = copy_heads(reinterpret_cast<char*>(inC) + cB, 2 * cB, midC, cB, cB, BH, st);
-  if (e == hipSuccess) e = copy_heads(reinterpret_cast<char*>(inN) + nB, 2 * nB, midN, nB, nB, BH, st);
-  if (e == hipSuccess) e = copy_heads(reinterpret_cast<char*>(inM) + 4, 8, midM, 4, 4, BH, st);
+  p1.T = a.T / P * (P - 1);   // tokens before the last split point (heads T apart)
+  hipError_t e;
+  if (f.state_gemm) {
+    e = mlstm::launch_state_gemm(p1, P - 1, midC, midN, midM, w + f.sg_off, st);
+  } else {
+    p1.C1 = midC; p1.n1 = midN; p1.m1 = midM;   // (P = 2: the first half)
+    e = mlstm::launch_chunk_state(p1, st);
+  }
+  // initial states of the segment-heads: P h <- the caller's (or zero),
+  // P h + s <- the state at s T/P
+  if (e == hipSuccess) e = copy_heads(inC, P * cB, a.C0, cB, cB, BH, st);
+  if (e == hipSuccess) e = copy_heads(inN, P * nB, a.n0, nB, nB, BH, st);
+  if (e == hipSuccess) e = copy_heads(inM, P * 4, a.m0, 4, 4, BH, st);
+  for (int s = 1; s < P && e == hipSuccess; ++s) {
+    const size_t k = static_cast<size_t>(s - 1);
+    e = copy_heads(inC + s * cB, P * cB, reinterpret_cast<char*>(midC) + k * BH * cB, cB, cB, BH, st);
+    if (e == hipSuccess)
+      e = copy_heads(inN + s * nB, P * nB, reinterpret_cast<char*>(midN) + k * BH * nB, nB, nB, BH, st);
+    if (e == hipSuccess)
+      e = copy_heads(inM + s * 4, P * 4, reinterpret_cast<char*>(midM) + k * BH * 4, 4, 4, BH, st);
+  }
   if (e != hipSuccess) return e;
-  // 2. both halves at once, as 2 H heads of T/2 tokens
+  // 2. all segments at once, as P H heads of T/P tokens
   mlstm::SeqArgs p2 = a;
-  p2.H = 2 * a.H;
-  p2.T = a.T / 2;
-  p2.Ts = a.T / 2;
-  p2.C0 = inC; p2.n0 = inN; p2.m0 = inM;
+  p2.H = P * a.H;
+  p2.T = a.T / P;
+  p2.Ts = a.T / P;
+  p2.C0 = reinterpret_cast<float*>(inC);
+  p2.n0 = reinterpret_cast<float*>(inN);
+  p2.m0 = reinterpret_cast<float*>(inM);
   const bool out = a.C1 != nullptr;
   p2.C1 = out ? reinterpret_cast<float*>(w + f.s_out.C) : nullptr;
   p2.n1 = out ? reinterpret_cast<float*>(w + f.s_out.n) : nullptr;
   p2.m1 = out ? reinterpret_cast<float*>(w + f.s_out.m) : nullptr;
   e = mlstm::launch_chunk_mfma(p2, chunk, nullptr, st);
   if (e != hipSuccess || !out) return e;
-  // 3. the final state is that of the second halves
-  e = copy_heads(a.C1, cB, w + f.s_out.C + cB, 2 * cB, cB, BH, st);
-  if (e == hipSuccess) e = copy_heads(a.n1, nB, w + f.s_out.n + nB, 2 * nB, nB, BH, st);
-  if (e == hipSuccess) e = copy_heads(a.m1, 4, w + f.s_out.m + 4, 8, 4, BH, st);
+  // 3. the final state is that of the last segments
+  const size_t last = static_cast<size_t>(P - 1);
+  e = copy_heads(a.C1, cB, w + f.s_out.C + last * cB, P * cB, cB, BH, st);
+  if (e == hipSuccess) e = copy_heads(a.n1, nB, w + f.s_out.n + last * nB, P * nB, nB, BH, st);
+  if (e == hipSuccess) e = copy_heads(a.m1, 4, w + f.s_out.m + last * 4, P * 4, 4, BH, st);
   return e;
 }
 
@@ -539,7 +574,7 @@ mlstm_status_t fwd_chunkwise(const mlstm_problem_t* p, int64_t chunk, const void
   if (s != MLSTM_OK) return s;
   s = check_chunk(p, chunk);
   if (s != MLSTM_OK) return s;
-  const FwdPlan f = fwd_plan(a, chunk);
+  const FwdPlan f = fwd_plan(a, chunk, fixed_scratch ? kScratchBytes : SIZE_MAX);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (fixed_scratch) {
     if (f.need > kScratchBytes)

@@ -82,11 +82,14 @@ hipError_t launch_chunk_ws128(const SeqArgs& a, hipStream_t stream);
 // C1, n1, m1 are required.
 bool chunk_state_supported(const SeqArgs& a);
 hipError_t launch_chunk_state(const SeqArgs& a, hipStream_t stream);
-// The same state as one weighted product over the tokens (state_gemm.hip):
-// d_qk 256, d_v a multiple of 128, bf16; needs state_gemm_workspace(a) bytes.
-bool state_gemm_supported(const SeqArgs& a);
-size_t state_gemm_workspace(const SeqArgs& a);
-hipError_t launch_state_gemm(const SeqArgs& a, void* workspace, hipStream_t stream);
+// The states at the ends of Q equal segments of tokens 0 .. T-1 from weighted
+// products over the tokens (state_gemm.hip): d_qk 256, d_v a multiple of 128,
+// bf16.  State k goes to C_out + k B H d_qk d_v, n_out + k B H d_qk,
+// m_out + k B H; needs state_gemm_workspace(a, Q) bytes of scratch.
+bool state_gemm_supported(const SeqArgs& a, int Q);
+size_t state_gemm_workspace(const SeqArgs& a, int Q);
+hipError_t launch_state_gemm(const SeqArgs& a, int Q, float* C_out, float* n_out, float* m_out,
+                             void* workspace, hipStream_t stream);
 // Generic VALU chunkwise kernel (float32 path; bf16 shapes outside MFMA cover).
 // Tokens t0 .. T-1 in chunks of `chunk`; the last chunk may be shorter.
 hipError_t launch_chunk_valu(const SeqArgs& a, int64_t chunk, hipStream_t stream);

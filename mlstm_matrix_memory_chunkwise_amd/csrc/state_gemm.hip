@@ -1,5 +1,5 @@
-// The state after T tokens as one weighted product over all of them, for the
-// sequence split of long sequences with few heads (d_qk 256).
+// The states at the split points of a long sequence with few heads (d_qk
+// 256), each from weighted products over the tokens before it.
 //
 // Method: xLSTM post (llms.blog), section 3 "The Parallel Dual Form": the
 // unrolled memory is a sum over tokens, C_T = sum_j (prod_{t>j} f_t) i_j v_j k_j^T
@@ -13,6 +13,14 @@
 // which is the chunk update of the chunkwise kernels with the whole sequence
 // as one chunk.  The recurrence m_t = max(log f_t + m_{t-1}, i~_t) unrolls to
 // exactly this m_T, so the result equals the chunkwise state up to rounding.
+// For several split points the tokens before the last one form Q equal
+// summary segments.  Each segment gets its own summary from a zero state,
+// normalized by its own largest e_j (e_j and that maximum taken within the
+// segment).  The states at the segment ends follow in order from the
+// associative combine of the chunk update,
+//   m' = max(m + sum_seg log f, m_seg),
+//   C~' = exp(m + sum_seg log f - m') C~ + exp(m_seg - m') C~_seg,
+// every exponent <= 0.
 //
 // Design (CDNA4): the sum over tokens has no sequential dependency, so it is
 // split over token segments as well as heads and value columns until the
@@ -21,16 +29,18 @@
 // fragment read from LDS feeds four times the MFMAs):
 //   1. state_gsum_kernel: per block of 1024 tokens of a head, the sum of
 //      log f (float64);
-//   2. state_gexp_kernel: per block, e_j (float64 prefix sums over the
-//      blocks before it and a block scan, stored as float32) and the
-//      block's largest e_j;
-//   3. state_gemm_kernel: per (head, 128 value columns, token segment), m_T
-//      from the block maxima, w_j = exp(e_j - m_T), then K^T diag(w) V on
-//      bf16 MFMA (w V rounded to bf16, as in the chunk kernels' update) and
-//      K^T w with w split into three bf16 terms (about 24 bits), written as
-//      partial sums;
-//   4. state_reduce_*: g_0 C~_0 + the segments' partial sums, in a fixed
-//      order (deterministic), and m_T.
+//   2. state_gexp_kernel: per block, e_j within its summary segment (float64
+//      prefix sums over the segment's blocks before it and a block scan,
+//      stored as float32) and the block's largest e_j;
+//   3. state_gemm_kernel: per (head, 128 value columns, token segment; the
+//      token segments nest in the summary segments), the summary segment's
+//      largest e_j from the block maxima, w_j = exp(e_j - that maximum),
+//      then K^T diag(w) V on bf16 MFMA (w V rounded to bf16, as in the chunk
+//      kernels' update) and K^T w with w split into three bf16 terms (about
+//      24 bits), written as partial sums;
+//   4. state_scalars_kernel, state_scan_*: the combine factors of every
+//      segment end, then the states there from the initial state and the
+//      partial sums, in a fixed order (deterministic).
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mfma_util.hpp"
@@ -55,26 +65,30 @@ constexpr int kMaxSegments = 16;
 
 struct GemmArgs {
   int64_t BH, Tp, Ts, dv;
-  int S;                          // token segments
+  int S;                          // token segments (a multiple of Q)
+  int Q;                          // summary segments
   int nbk;                        // gate blocks per head
+  int bps;                        // gate blocks per summary segment
   const bf16_t* k;
   const bf16_t* v;
   const float* e;                 // e_j [BH][Tp]
   const double* psum;             // sum of log f per gate block [BH][nbk]
   const double* pmax;             // largest e_j per gate block [BH][nbk]
-  const float* m0;                // initial m per head, or NULL (0)
   float* part;                    // [S][BH][DQK][dv]
   float* npart;                   // [S][BH][DQK]
 };
 
-// sum_t log f_t and m_T = max(m_0 + sum_t log f_t, max_j e_j) of one head
-// from the per-block figures (the same order everywhere: bitwise equal)
-__device__ __forceinline__ void head_scalars(const double* psum, const double* pmax, int nbk,
-                                             int64_t bh, double m0, double& total, double& mT) {
+// sum log f and the largest e_j of summary segment k of one head, from the
+// per-block figures (the same order everywhere: bitwise equal)
+__device__ __forceinline__ void seg_scalars(const double* psum, const double* pmax, int nbk, int bps,
+                                            int64_t bh, int k, double& total, double& emax) {
   total = 0.0;
-  for (int b = 0; b < nbk; ++b) total += psum[bh * nbk + b];
-  mT = m0 + total;
-  for (int b = 0; b < nbk; ++b) mT = pmax[bh * nbk + b] > mT ? pmax[bh * nbk + b] : mT;
+  emax = -1.0e300;
+  const int b1 = (k + 1) * bps < nbk ? (k + 1) * bps : nbk;
+  for (int b = k * bps; b < b1; ++b) {
+    total += psum[bh * nbk + b];
+    emax = pmax[bh * nbk + b] > emax ? pmax[bh * nbk + b] : emax;
+  }
 }
 
 // ---- 1., 2. gate weights.  Block b of a head covers tokens GR b .. GR b +
@@ -110,13 +124,15 @@ __global__ __launch_bounds__(GT) void state_gsum_kernel(SeqArgs a, double* psum,
 }
 
 __global__ __launch_bounds__(GT) void state_gexp_kernel(SeqArgs a, const double* psum, float* e_out,
-                                                        double* pmax, int nbk) {
+                                                        double* pmax, int nbk, int bps) {
   __shared__ double s_x[2][GT];
   const int64_t bh = blockIdx.x / nbk;
   const int b = blockIdx.x % nbk;
   const int tid = threadIdx.x;
+  // sums over this block's summary segment: before it, and in all
+  const int k0 = (b / bps) * bps, k1 = k0 + bps < nbk ? k0 + bps : nbk;
   double before = 0.0, total = 0.0;
-  for (int k = 0; k < nbk; ++k) {
+  for (int k = k0; k < k1; ++k) {
     const double x = psum[bh * nbk + k];
     if (k < b) before += x;
     total += x;
@@ -138,7 +154,8 @@ __global__ __launch_bounds__(GT) void state_gexp_kernel(SeqArgs a, const double*
   }
   const double incl = s_x[p][tid];
   __syncthreads();
-  // e_j = i~_j + sum_{t > j} log f_t = i~_j + total - (sum_{t <= j} log f_t)
+  // e_j = i~_j + sum_{j < t <= segment end} log f_t
+  //     = i~_j + total - (sum_{segment start <= t <= j} log f_t)
   double run = before + incl - x;
   double emax = -1.0e300;
   if (live) {
@@ -200,15 +217,16 @@ __global__ __launch_bounds__(NTH, 1) void state_gemm_kernel(GemmArgs a) {
   const int nsteps = static_cast<int>(a.Tp / L);
   const int spb = nsteps / a.S;
   const int c0 = seg * spb, c1 = c0 + spb;
+  const int qseg = seg / (a.S / a.Q);      // the summary segment of these tokens
   const bool nwave = vt == 0 && hc == 0;   // this wave also forms K^T w for its rows
 
   const bf16_t* gk = a.k + head * a.Ts * DQK;
   const bf16_t* gv = a.v + head * a.Ts * dv + vt * TVG;
   const float* gw = a.e + head * a.Tp;
   if (tid == 0) {
-    double total, mT;
-    head_scalars(a.psum, a.pmax, a.nbk, head, a.m0 ? static_cast<double>(a.m0[head]) : 0.0, total, mT);
-    s_mT = static_cast<float>(mT);
+    double total, emax;
+    seg_scalars(a.psum, a.pmax, a.nbk, a.bps, head, qseg, total, emax);
+    s_mT = static_cast<float>(emax);
   }
 
   // loads (per-lane byte offsets fixed, chunk bases wave-uniform): a 1 KB
@@ -359,66 +377,89 @@ __global__ __launch_bounds__(NTH, 1) void state_gemm_kernel(GemmArgs a) {
   }
 }
 
-// ---- 4. g_0 C~_0 + the partial sums, segment by segment
-__global__ __launch_bounds__(256) void state_reduce_c_kernel(const float* part, const float* C0,
-                                                             const float* m0, const double* psum,
-                                                             const double* pmax, int nbk, float* C1,
-                                                             int64_t BH, int64_t per_head, int S) {
+// ---- 4. the states at the segment ends.  Per head and segment k: with m
+// before it (the initial m, or 0 for a zero state), m' = max(m + sum_k log f,
+// m_k), fa = exp(m + sum_k log f - m'), fb = exp(m_k - m'); the state after
+// segment k is fa * (state before) + fb * (segment k's summary).
+__global__ __launch_bounds__(64) void state_scalars_kernel(const double* psum, const double* pmax,
+                                                           int nbk, int bps, int Q, const float* m0,
+                                                           float* fab, float* m_out,
+                                                           int64_t m_kstride, int64_t BH) {
+  const int64_t bh = static_cast<int64_t>(blockIdx.x) * 64 + threadIdx.x;
+  if (bh >= BH) return;
+  double m = m0 ? static_cast<double>(m0[bh]) : 0.0;
+  for (int k = 0; k < Q; ++k) {
+    double total, emax;
+    seg_scalars(psum, pmax, nbk, bps, bh, k, total, emax);
+    const double md = m + total;
+    const double mn = md > emax ? md : emax;
+    fab[(bh * Q + k) * 2] = __expf(static_cast<float>(md - mn));
+    fab[(bh * Q + k) * 2 + 1] = __expf(static_cast<float>(emax - mn));
+    m_out[k * m_kstride + bh] = static_cast<float>(mn);
+    m = mn;
+  }
+}
+
+// C~: one float4 of one head per thread, the Q segment ends in order
+__global__ __launch_bounds__(256) void state_scan_c_kernel(const float* part, const float* C0,
+                                                           const float* fab, float* C_out,
+                                                           int64_t c_kstride, int64_t BH,
+                                                           int64_t per_head, int S, int Q) {
   const int64_t i4 = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;   // float4 index
   const int64_t n4 = BH * per_head / 4;
   if (i4 >= n4) return;
   const int64_t bh = (4 * i4) / per_head;
-  float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (C0) {
-    const float4 c = reinterpret_cast<const float4*>(C0)[i4];
-    double total, mT;
-    const double mm = static_cast<double>(m0[bh]);
-    head_scalars(psum, pmax, nbk, bh, mm, total, mT);
-    const float gg = __expf(static_cast<float>(mm + total - mT));
-    r = make_float4(gg * c.x, gg * c.y, gg * c.z, gg * c.w);
+  const int spq = S / Q;
+  float4 r = C0 ? reinterpret_cast<const float4*>(C0)[i4] : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int k = 0; k < Q; ++k) {
+    float4 p = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s = k * spq; s < (k + 1) * spq; ++s) {
+      const float4 x = reinterpret_cast<const float4*>(part)[s * n4 + i4];
+      p.x += x.x; p.y += x.y; p.z += x.z; p.w += x.w;
+    }
+    const float fa = fab[(bh * Q + k) * 2], fb = fab[(bh * Q + k) * 2 + 1];
+    r = make_float4(fa * r.x + fb * p.x, fa * r.y + fb * p.y, fa * r.z + fb * p.z, fa * r.w + fb * p.w);
+    reinterpret_cast<float4*>(C_out + k * c_kstride)[i4] = r;
   }
-  for (int s = 0; s < S; ++s) {
-    const float4 p = reinterpret_cast<const float4*>(part)[s * n4 + i4];
-    r.x += p.x; r.y += p.y; r.z += p.z; r.w += p.w;
-  }
-  reinterpret_cast<float4*>(C1)[i4] = r;
 }
 
-__global__ __launch_bounds__(DQK) void state_reduce_n_kernel(const float* npart, const float* n0,
-                                                             const float* m0, const double* psum,
-                                                             const double* pmax, int nbk, float* n1,
-                                                             float* m1, int64_t BH, int S) {
+__global__ __launch_bounds__(DQK) void state_scan_n_kernel(const float* npart, const float* n0,
+                                                           const float* fab, float* n_out,
+                                                           int64_t n_kstride, int64_t BH, int S, int Q) {
   const int64_t bh = blockIdx.x;
   const int r = threadIdx.x;
-  double total, mT;
-  const double mm = n0 ? static_cast<double>(m0[bh]) : 0.0;
-  head_scalars(psum, pmax, nbk, bh, mm, total, mT);
-  float x = n0 ? __expf(static_cast<float>(mm + total - mT)) * n0[bh * DQK + r] : 0.0f;
-  for (int s = 0; s < S; ++s) x += npart[(s * BH + bh) * DQK + r];
-  n1[bh * DQK + r] = x;
-  if (r == 0) m1[bh] = static_cast<float>(mT);
+  const int spq = S / Q;
+  float x = n0 ? n0[bh * DQK + r] : 0.0f;
+  for (int k = 0; k < Q; ++k) {
+    float p = 0.0f;
+    for (int s = k * spq; s < (k + 1) * spq; ++s) p += npart[(s * BH + bh) * DQK + r];
+    x = fab[(bh * Q + k) * 2] * x + fab[(bh * Q + k) * 2 + 1] * p;
+    n_out[k * n_kstride + bh * DQK + r] = x;
+  }
 }
 
 struct GemmLayout {
-  size_t e, psum, pmax, part, npart, end;
-  int S, nbk;
+  size_t e, psum, pmax, fab, part, npart, end;
+  int S, nbk, bps;
 };
 
-GemmLayout gemm_layout(const SeqArgs& a) {
+GemmLayout gemm_layout(const SeqArgs& a, int Q) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   GemmLayout l{};
   const int64_t BH = a.B * a.H;
   const int64_t groups = BH * (a.dv / TVG);
   const int64_t nsteps = a.T / L;
-  int S = 1;
+  int S = Q;
   while (S < kMaxSegments && groups * (2 * S) <= 256 && nsteps % (2 * S) == 0 && nsteps / (2 * S) >= 8)
     S *= 2;
   l.S = S;
   l.nbk = static_cast<int>((a.T + GR - 1) / GR);
+  l.bps = Q == 1 ? l.nbk : static_cast<int>(a.T / Q / GR);
   l.e = 0;
   l.psum = up(l.e + 4 * static_cast<size_t>(BH * a.T));
   l.pmax = up(l.psum + 8 * static_cast<size_t>(BH) * l.nbk);
-  l.part = up(l.pmax + 8 * static_cast<size_t>(BH) * l.nbk);
+  l.fab = up(l.pmax + 8 * static_cast<size_t>(BH) * l.nbk);
+  l.part = up(l.fab + 8 * static_cast<size_t>(BH) * Q);
   l.npart = up(l.part + 4 * static_cast<size_t>(S) * BH * DQK * a.dv);
   l.end = up(l.npart + 4 * static_cast<size_t>(S) * BH * DQK);
   return l;
@@ -426,48 +467,57 @@ GemmLayout gemm_layout(const SeqArgs& a) {
 
 }  // namespace
 
-bool state_gemm_supported(const SeqArgs& a) {
-  return a.qkv_bf16 && a.dqk == DQK && a.dv % TVG == 0 && a.T % L == 0 && a.T >= 8 * L && a.t0 == 0 &&
-         a.Ts % 4 == 0;
+bool state_gemm_supported(const SeqArgs& a, int Q) {
+  if (!(a.qkv_bf16 && a.dqk == DQK && a.dv % TVG == 0 && a.T % L == 0 && a.t0 == 0 && a.Ts % 4 == 0 &&
+        Q >= 1 && Q <= kMaxSegments))
+    return false;
+  if (a.T < 8 * L * Q) return false;
+  // several summary segments: whole gate blocks and whole 64-token steps each
+  return Q == 1 || (a.T % Q == 0 && (a.T / Q) % GR == 0);
 }
 
-size_t state_gemm_workspace(const SeqArgs& a) { return gemm_layout(a).end; }
+size_t state_gemm_workspace(const SeqArgs& a, int Q) { return gemm_layout(a, Q).end; }
 
-hipError_t launch_state_gemm(const SeqArgs& a, void* workspace, hipStream_t stream) {
-  const GemmLayout l = gemm_layout(a);
+hipError_t launch_state_gemm(const SeqArgs& a, int Q, float* C_out, float* n_out, float* m_out,
+                             void* workspace, hipStream_t stream) {
+  const GemmLayout l = gemm_layout(a, Q);
   char* w = static_cast<char*>(workspace);
   const int64_t BH = a.B * a.H;
   float* ev = reinterpret_cast<float*>(w + l.e);
   double* psum = reinterpret_cast<double*>(w + l.psum);
   double* pmax = reinterpret_cast<double*>(w + l.pmax);
+  float* fab = reinterpret_cast<float*>(w + l.fab);
   float* part = reinterpret_cast<float*>(w + l.part);
   float* npart = reinterpret_cast<float*>(w + l.npart);
-  const float* m0 = a.C0 ? a.m0 : nullptr;
   const unsigned ngb = static_cast<unsigned>(BH * l.nbk);
   state_gsum_kernel<<<dim3(ngb), dim3(GT), 0, stream>>>(a, psum, l.nbk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  state_gexp_kernel<<<dim3(ngb), dim3(GT), 0, stream>>>(a, psum, ev, pmax, l.nbk);
+  state_gexp_kernel<<<dim3(ngb), dim3(GT), 0, stream>>>(a, psum, ev, pmax, l.nbk, l.bps);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   GemmArgs g{};
-  g.BH = BH; g.Tp = a.T; g.Ts = a.Ts; g.dv = a.dv; g.S = l.S; g.nbk = l.nbk;
+  g.BH = BH; g.Tp = a.T; g.Ts = a.Ts; g.dv = a.dv; g.S = l.S; g.Q = Q; g.nbk = l.nbk; g.bps = l.bps;
   g.k = static_cast<const bf16_t*>(a.k);
   g.v = static_cast<const bf16_t*>(a.v);
-  g.e = ev; g.psum = psum; g.pmax = pmax; g.m0 = m0;
+  g.e = ev; g.psum = psum; g.pmax = pmax;
   g.part = part; g.npart = npart;
   const unsigned nwg = static_cast<unsigned>(BH * (a.dv / TVG) * l.S);
   state_gemm_kernel<<<dim3(nwg), dim3(NTH), 0, stream>>>(g);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t per_head = DQK * a.dv;
-  const int64_t n4 = BH * per_head / 4;
-  state_reduce_c_kernel<<<dim3(static_cast<unsigned>((n4 + 255) / 256)), dim3(256), 0, stream>>>(
-      part, a.C0, m0, psum, pmax, l.nbk, a.C1, BH, per_head, l.S);
+  state_scalars_kernel<<<dim3(static_cast<unsigned>((BH + 63) / 64)), dim3(64), 0, stream>>>(
+      psum, pmax, l.nbk, l.bps, Q, a.C0 ? a.m0 : nullptr, fab, m_out, BH, BH);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  state_reduce_n_kernel<<<dim3(static_cast<unsigned>(BH)), dim3(DQK), 0, stream>>>(
-      npart, a.C0 ? a.n0 : nullptr, m0, psum, pmax, l.nbk, a.n1, a.m1, BH, l.S);
+  const int64_t per_head = DQK * a.dv;
+  const int64_t n4 = BH * per_head / 4;
+  state_scan_c_kernel<<<dim3(static_cast<unsigned>((n4 + 255) / 256)), dim3(256), 0, stream>>>(
+      part, a.C0, fab, C_out, BH * per_head, BH, per_head, l.S, Q);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  state_scan_n_kernel<<<dim3(static_cast<unsigned>(BH)), dim3(DQK), 0, stream>>>(
+      npart, a.C0 ? a.n0 : nullptr, fab, n_out, BH * DQK, BH, l.S, Q);
   return hipGetLastError();
 }
 

@@ -94,15 +94,18 @@ def test_d256_T8192_full_sampled_heads(chunk):
     compare(gpu, run_oracle(inp, heads), TOL_BF16, heads, label=f"d256 T8192 L={chunk}")
 
 
-def test_d256x512_T65536_sampled_heads():
+@pytest.mark.parametrize("H,nsample", [(16, 2), (4, 1)])
+def test_d256x512_T65536_sampled_heads(H, nsample):
+    """16 heads: 128 workgroups, the sequence split in 2; 4 heads: 32
+    workgroups, split in 8 (states at 7 split points)."""
     cfg = workloads.CONFIGS["d256x512_T65536"]
-    log("chunkwise d256/512 T65536 full: inputs")
-    inp = workloads.make_chunkwise_inputs(cfg)
-    heads = sample_heads(cfg.B, cfg.H, 2, seed=4)
-    log("chunkwise d256/512 T65536 full: GPU")
+    log(f"chunkwise d256/512 T65536 H {H}: inputs")
+    inp = workloads.make_chunkwise_inputs(cfg, H=H)
+    heads = sample_heads(cfg.B, H, nsample, seed=4)
+    log(f"chunkwise d256/512 T65536 H {H}: GPU")
     gpu = run_gpu(inp, 128)
-    log(f"chunkwise d256/512 T65536 full: oracle on {len(heads)} heads")
-    compare(gpu, run_oracle(inp, heads), TOL_BF16, heads, label="d256/512 T65536")
+    log(f"chunkwise d256/512 T65536 H {H}: oracle on {len(heads)} heads")
+    compare(gpu, run_oracle(inp, heads), TOL_BF16, heads, label=f"d256/512 T65536 H {H}")
 
 
 # ----------------------------------------------------------------- edge cases
@@ -161,6 +164,13 @@ EDGE = [
     ("split: chunk 32, d_qk 64 d_v 192", "bf16", 1, 3, 4096, 64, 192, 32, True, True, "sigmoid"),
     ("split: d_qk 256 d_v 128 chunk 128, input-gate spikes", "bf16", 1, 1, 4096, 256, 128, 128, True,
      True, "sigmoid"),
+    # more segments when the grid is small enough: 2 workgroups -> 8 segments
+    # of 2048 tokens (states at 7 split points from 7 summary segments), 4
+    # workgroups at T 8192 -> 4 segments (3 split points)
+    ("split in 8: d_qk 256 d_v 128, T 16384, random state", "bf16", 1, 1, 16384, 256, 128, 64, True,
+     True, "sigmoid"),
+    ("split in 4: d_qk 256 d_v 256, T 8192, random state, exp gate", "bf16", 1, 1, 8192, 256, 256, 64,
+     True, True, "exp"),
 ]
 
 
