@@ -610,42 +610,46 @@ def main():
     # ------------------------------------------------------------ long context
     if not args.skip_long:
         cfg4 = workloads.CONFIGS["d256x512_T65536"]
-        log(f"bench: generating {cfg4.describe()}")
-        d4 = {k: (None if v is None else v.to(dev))
-              for k, v in workloads.make_chunkwise_inputs(cfg4).items()}
-        B4, H4, T4, dqk4, dv4, L4 = cfg4.B, cfg4.H, cfg4.T, cfg4.dqk, cfg4.dv, cfg4.chunks[0]
-        h4 = torch.empty((B4, H4, T4, dv4), dtype=torch.bfloat16, device=dev)
+        # the workload as given (16 heads: 128 workgroups, the sequence split
+        # in 2), and with 4 heads (32 workgroups, split in 8)
+        for key, heads in (("long_context", cfg4.H), ("long_context_4heads", 4)):
+            log(f"bench: generating {cfg4.describe()} with H={heads}")
+            d4 = {k: (None if v is None else v.to(dev))
+                  for k, v in workloads.make_chunkwise_inputs(cfg4, H=heads).items()}
+            B4, H4, T4, dqk4, dv4, L4 = cfg4.B, heads, cfg4.T, cfg4.dqk, cfg4.dv, cfg4.chunks[0]
+            h4 = torch.empty((B4, H4, T4, dv4), dtype=torch.bfloat16, device=dev)
 
-        def run_long():
-            M.mlstm_fwd_chunkwise(d4["q"], d4["k"], d4["v"], d4["i_pre"], d4["f_pre"],
-                                  d4["o_pre"], chunk=L4, out=h4)
+            def run_long():
+                M.mlstm_fwd_chunkwise(d4["q"], d4["k"], d4["v"], d4["i_pre"], d4["f_pre"],
+                                      d4["o_pre"], chunk=L4, out=h4)
 
-        # warm-up, then untimed passes for SETTLE_S seconds (as for the main
-        # line: the clock settles under a new sustained load)
-        for _ in range(2):
-            run_long()
-        torch.cuda.synchronize()
-        t_settle = time.perf_counter()
-        while time.perf_counter() - t_settle < SETTLE_S:
-            run_long()
+            # warm-up, then untimed passes for SETTLE_S seconds (as for the
+            # main line: the clock settles under a new sustained load)
+            for _ in range(2):
+                run_long()
             torch.cuda.synchronize()
-        ms4 = time_events(run_long, 10, stream)
-        f4, b4 = chunk_algorithmic(B4, H4, T4, dqk4, dv4, L4, 4, state_in=False)
-        gbs4 = b4 / (ms4 / 1e3) / 1e9
-        result["long_context"] = {
-            "workload": f"chunkwise forward, long context: bf16 q/k/v, fp32 gates/o-gate, B={B4} "
-                        f"H={H4} T={T4} d_qk={dqk4} d_v={dv4} chunk={L4}, zero initial state, "
-                        f"final state out",
-            "ms": ms4, "tokens_per_s": B4 * T4 / (ms4 / 1e3),
-            "roofline": {"bound": "hbm", "achieved": gbs4, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs4 / HBM_PEAK_GBS,
-                         # all launches of one call (state pass, forward, state copies)
-                         "traffic": measured_traffic("long_context")},
-            "mfma_frac": f4 / (ms4 / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-            "algorithmic_bytes": b4, "algorithmic_gflop": f4 / 1e9,
-        }
-        del d4, h4
-        torch.cuda.empty_cache()
+            t_settle = time.perf_counter()
+            while time.perf_counter() - t_settle < SETTLE_S:
+                run_long()
+                torch.cuda.synchronize()
+            ms4 = time_events(run_long, 10, stream)
+            f4, b4 = chunk_algorithmic(B4, H4, T4, dqk4, dv4, L4, 4, state_in=False)
+            gbs4 = b4 / (ms4 / 1e3) / 1e9
+            result[key] = {
+                "workload": f"chunkwise forward, long context: bf16 q/k/v, fp32 gates/o-gate, B={B4} "
+                            f"H={H4} T={T4} d_qk={dqk4} d_v={dv4} chunk={L4}, zero initial state, "
+                            f"final state out",
+                "ms": ms4, "tokens_per_s": B4 * T4 / (ms4 / 1e3),
+                "roofline": {"bound": "hbm", "achieved": gbs4, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": gbs4 / HBM_PEAK_GBS,
+                             # all launches of one call (state pass, forward, state
+                             # copies); counters taken for the 16-head workload only
+                             "traffic": measured_traffic(key) if key == "long_context" else None},
+                "mfma_frac": f4 / (ms4 / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                "algorithmic_bytes": b4, "algorithmic_gflop": f4 / 1e9,
+            }
+            del d4, h4
+            torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ parallel form
     if not args.skip_parallel:
