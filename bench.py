@@ -149,6 +149,8 @@ KERNEL_SOURCES = {
     "long_context": ["chunk_ws128.hip", "chunk_mfma.hip", "chunk_state.hip", "state_gemm.hip", "api.hip",
                      "mfma_util.hpp",
                      "common.hpp", "kernels.hpp"],
+    "long_context_4heads": ["chunk_ws128.hip", "chunk_mfma.hip", "chunk_state.hip", "state_gemm.hip",
+                            "api.hip", "mfma_util.hpp", "common.hpp", "kernels.hpp"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 
@@ -221,16 +223,19 @@ def profile_workload():
     torch.cuda.synchronize()
     del gn, cv
     torch.cuda.empty_cache()
-    # the long-context forward (chunk 128, sequence split: state pass over the
-    # first half, then both halves at once, and its state copies)
+    # the long-context forward (chunk 128, sequence split: the states at the
+    # split points, then all segments at once, and the state copies), with
+    # its 16 heads (2 segments) and with 4 heads (8 segments)
     cfg4 = workloads.CONFIGS["d256x512_T65536"]
-    d4 = {k: (None if v is None else v.to(dev)) for k, v in workloads.make_chunkwise_inputs(cfg4).items()}
-    h4 = torch.empty((cfg4.B, cfg4.H, cfg4.T, cfg4.dv), dtype=torch.bfloat16, device=dev)
-    M.mlstm_fwd_chunkwise(d4["q"], d4["k"], d4["v"], d4["i_pre"], d4["f_pre"], d4["o_pre"],
-                          chunk=cfg4.chunks[0], out=h4)
-    torch.cuda.synchronize()
-    del d4, h4
-    torch.cuda.empty_cache()
+    for heads in (cfg4.H, 4):
+        d4 = {k: (None if v is None else v.to(dev))
+              for k, v in workloads.make_chunkwise_inputs(cfg4, H=heads).items()}
+        h4 = torch.empty((cfg4.B, heads, cfg4.T, cfg4.dv), dtype=torch.bfloat16, device=dev)
+        M.mlstm_fwd_chunkwise(d4["q"], d4["k"], d4["v"], d4["i_pre"], d4["f_pre"], d4["o_pre"],
+                              chunk=cfg4.chunks[0], out=h4)
+        torch.cuda.synchronize()
+        del d4, h4
+        torch.cuda.empty_cache()
     x = torch.ones(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
     y = torch.empty_like(x)
     y.copy_(x)
@@ -642,9 +647,9 @@ def main():
                 "ms": ms4, "tokens_per_s": B4 * T4 / (ms4 / 1e3),
                 "roofline": {"bound": "hbm", "achieved": gbs4, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": gbs4 / HBM_PEAK_GBS,
-                             # all launches of one call (state pass, forward, state
-                             # copies); counters taken for the 16-head workload only
-                             "traffic": measured_traffic(key) if key == "long_context" else None},
+                             # all launches of one call (states at the split points,
+                             # forward, state copies)
+                             "traffic": measured_traffic(key)},
                 "mfma_frac": f4 / (ms4 / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                 "algorithmic_bytes": b4, "algorithmic_gflop": f4 / 1e9,
             }
