@@ -107,13 +107,13 @@ typedef struct {
  * continuing from the state the first T - T % chunk tokens leave in the
  * workspace (B*H*(d_qk*d_v + d_qk + 1) floats).  A long sequence with few
  * heads (at most 128 matrix-core workgroups of 64 value columns) is split
- * into P = 8, 4 or 2 equal segments: the largest P whose P-fold grid fits 256
+ * into P = 16, 8, 4 or 2 equal segments: the largest P whose P-fold grid fits 256
  * compute units, with T a multiple of P chunks (and of 64 P) and at least
  * 2048 tokens per segment; P above 2 needs d_qk 256 and d_v a multiple of
  * 128.  The states at the P - 1 split points are computed first, then all
  * segments run at once.  Its workspace holds (3P - 1)*B*H states and, at
  * d_qk 256 with d_v a multiple of 128, the token segments' partial sums of
- * those states (at most 16 states per head) and per-token gate weights.
+ * those states (at most 30 states per head) and per-token gate weights.
  * mlstm_fwd_chunkwise_workspace_bytes gives the size in every case.
  * Returns MLSTM_OK or an error code; on error, mlstm_last_error_detail()
  * describes it.

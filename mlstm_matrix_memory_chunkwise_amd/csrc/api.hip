@@ -313,7 +313,7 @@ bool seq_is_empty(const mlstm_problem_t* p) { return p->B * p->H == 0 || p->T ==
 // columns) through the whole sequence, so a problem with few heads leaves
 // most of the 256 compute units idle.  When that grid has at most
 // kSplitGroups workgroups and the sequence is long, the call instead splits
-// the sequence into P = 2, 4 or 8 equal segments (the most that still fit the
+// the sequence into P = 2, 4, 8 or 16 equal segments (the most that still fit the
 // compute units and leave at least kSplitMinTokens per segment):
 //   1. computes the exact states at the P - 1 split points: from weighted
 //      products over the tokens before them (state_gemm.hip) where that
@@ -377,7 +377,7 @@ FwdPlan fwd_plan(const mlstm::SeqArgs& a, int64_t chunk, size_t cap = SIZE_MAX) 
   if (f.mfma && !f.tail) {
     const int64_t unit = chunk > 64 ? chunk : 64;   // segments of whole chunks and of 64 tokens
     const int64_t grid = a.B * a.H * (a.dv / 64);
-    for (int P = 8; P >= 2 && !f.split; P /= 2) {
+    for (int P = 16; P >= 2 && !f.split; P /= 2) {
       if (grid > kSplitGroups || grid * P > kSplitCUs || a.T % (P * unit) != 0 ||
           a.T / P < kSplitMinTokens)
         continue;

@@ -171,6 +171,9 @@ EDGE = [
      True, "sigmoid"),
     ("split in 4: d_qk 256 d_v 256, T 8192, random state, exp gate", "bf16", 1, 1, 8192, 256, 256, 64,
      True, True, "exp"),
+    # 2 workgroups at T 32768 -> 16 segments (15 summary segments, 30 token segments)
+    ("split in 16: d_qk 256 d_v 128, T 32768, random state", "bf16", 1, 1, 32768, 256, 128, 64, True,
+     True, "sigmoid"),
 ]
 
 
